@@ -1,0 +1,182 @@
+"""Plain fp64 CPU oracle of the verify-and-sample step (test infrastructure).
+
+Only the test suite, the package smoke check and the CPU-baseline leg of the
+benchmark may import this module.  The product library never does; it shares no
+code with this C file.  See ``oracle.c`` for the definitions and the passages of
+the pages each one follows.
+
+The wrappers take numpy arrays (bf16 logits as ``uint16`` bit patterns) and
+return numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+FLAG_NONFINITE = 1
+FLAG_ZERO_RESIDUAL = 2
+FLAG_ZERO_WEIGHTS = 4
+FLAG_CDF_CLAMP = 8
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+def build(src: str = SRC, out: str = LIB, strict: bool = True) -> str:
+    """Compile the oracle with plain gcc (-O2, IEEE semantics, no fast-math)."""
+    warn = ["-Wall", "-Werror"] if strict else ["-w"]
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", *warn, "-o", out, src, "-lm"])
+    return out
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+
+
+def _declare(lib):
+    lib.oracle_row_stats.argtypes = [_I, _P, _I64, _D, _P, _P]
+    lib.oracle_row_stats.restype = _I
+    lib.oracle_logprob.argtypes = [_I, _P, _I64, _D, _I64]
+    lib.oracle_logprob.restype = _D
+    lib.oracle_sd_verify.argtypes = [_I, _I, _I, _I64, _D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_sd_verify.restype = _I
+    lib.oracle_sd_final_cdf.argtypes = [_I, _I, _I, _I64, _D, _P, _P, _P, _I, _P]
+    lib.oracle_sd_final_cdf.restype = _I
+    lib.oracle_smc_step.argtypes = [_I, _I, _I, _I, _I64, _D, _D] + [_P] * 8 + [_I] + [_P] * 9
+    lib.oracle_smc_step.restype = _I
+    return lib
+
+
+_lib_cache: dict = {}
+
+
+def load(path: str = LIB):
+    """Load (building first if absent) an oracle shared object."""
+    if path not in _lib_cache:
+        if not os.path.exists(path):
+            if path != LIB:
+                raise FileNotFoundError(path)
+            build()
+        _lib_cache[path] = _declare(ctypes.CDLL(path))
+    return _lib_cache[path]
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(logits: np.ndarray) -> int:
+    if logits.dtype == np.float32:
+        return DTYPE_F32
+    if logits.dtype == np.uint16:
+        return DTYPE_BF16
+    raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {logits.dtype}")
+
+
+def row_stats(row: np.ndarray, T: float, lib=None):
+    """(M, log S, bad) of one row: M = max z/T, S = sum exp(z/T - M)."""
+    lib = lib or load()
+    row = np.ascontiguousarray(row)
+    M = ctypes.c_double()
+    lS = ctypes.c_double()
+    bad = lib.oracle_row_stats(_dtype_code(row), _ptr(row), row.shape[-1], T, ctypes.byref(M), ctypes.byref(lS))
+    return M.value, lS.value, bad
+
+
+def logprob(row: np.ndarray, T: float, i: int, lib=None) -> float:
+    lib = lib or load()
+    row = np.ascontiguousarray(row)
+    return lib.oracle_logprob(_dtype_code(row), _ptr(row), row.shape[-1], T, int(i))
+
+
+def sd_verify(target, draft, tokens, uniforms, T, K=None, offsets=None, lib=None):
+    """Standard SD verify of B sequences.
+
+    Fixed K: target [B*(K+1), V], draft [B*K, V], tokens [B*K],
+    uniforms [B*(K+1)].  CSR: ``offsets`` [B+1] over draft rows; target rows
+    and uniforms of sequence b start at offsets[b] + b.
+
+    Returns dict(num_accepted, final_token, flags, accept_margin, sample_margin).
+    """
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    V = target.shape[-1]
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    uniforms = np.ascontiguousarray(uniforms, dtype=np.float32)
+    if offsets is not None:
+        offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+        B = offsets.shape[0] - 1
+        K = int(np.max(np.diff(offsets))) if B > 0 else 0
+    else:
+        B = target.shape[0] // (K + 1)
+    nd = tokens.shape[0]
+    na = np.zeros(B, np.int32)
+    ft = np.zeros(B, np.int32)
+    fl = np.zeros(1, np.uint32)
+    am = np.full(max(nd, 1), -1.0)
+    sm = np.zeros(max(B, 1))
+    lib.oracle_sd_verify(_dtype_code(target), B, K, V, T, _ptr(target), _ptr(draft), _ptr(tokens),
+                         _ptr(uniforms), _ptr(offsets), _ptr(na), _ptr(ft), _ptr(fl), _ptr(am), _ptr(sm))
+    return dict(num_accepted=na, final_token=ft, flags=int(fl[0]), accept_margin=am[:nd], sample_margin=sm[:B])
+
+
+def sd_final_cdf(target, draft, b, n, T, K=None, offsets=None, lib=None):
+    """Normalised CDF of the distribution sequence b's final token is drawn from."""
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    V = target.shape[-1]
+    if offsets is not None:
+        offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    cdf = np.zeros(V)
+    fl = lib.oracle_sd_final_cdf(_dtype_code(target), int(b), int(K or 0), V, T, _ptr(target), _ptr(draft),
+                                 _ptr(offsets), int(n), _ptr(cdf))
+    return cdf, fl
+
+
+def smc_step(target, draft, tokens, bonus_u, resample_u, logw, T, ess_frac, P, N, K, pt_in=None, lib=None):
+    """One SMC-SD reweight / ESS / systematic-resample step.
+
+    ``logw`` (float32 [P*N]) is not modified; the updated log-weights are
+    returned.  Returns dict(logw, bonus, ancestors, ess, resampled, pt_out,
+    flags, cum_weight, bonus_margin, ess_margin, resample_margin).
+    """
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    V = target.shape[-1]
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    bonus_u = np.ascontiguousarray(bonus_u, dtype=np.float32)
+    resample_u = np.ascontiguousarray(resample_u, dtype=np.float32)
+    lw = np.array(logw, dtype=np.float32, copy=True)
+    PN = P * N
+    L = 0
+    pt_out = None
+    if pt_in is not None:
+        pt_in = np.ascontiguousarray(pt_in, dtype=np.int32)
+        L = pt_in.size // max(PN, 1)
+        pt_out = np.zeros_like(pt_in)
+    bonus = np.zeros(PN, np.int32)
+    anc = np.zeros(PN, np.int32)
+    ess = np.zeros(P, np.float32)
+    res = np.zeros(P, np.int32)
+    fl = np.zeros(1, np.uint32)
+    cw = np.zeros(max(PN, 1))
+    bm = np.zeros(max(PN, 1))
+    em = np.zeros(max(P, 1))
+    rm = np.zeros(max(P, 1))
+    lib.oracle_smc_step(_dtype_code(target), P, N, K, V, T, ess_frac, _ptr(target), _ptr(draft), _ptr(tokens),
+                        _ptr(bonus_u), _ptr(resample_u), _ptr(lw), _ptr(pt_in), _ptr(pt_out), L, _ptr(bonus),
+                        _ptr(anc), _ptr(ess), _ptr(res), _ptr(fl), _ptr(cw), _ptr(bm), _ptr(em), _ptr(rm))
+    return dict(logw=lw, bonus=bonus, ancestors=anc, ess=ess, resampled=res, pt_out=pt_out, flags=int(fl[0]),
+                cum_weight=cw[:PN], bonus_margin=bm[:PN], ess_margin=em[:P], resample_margin=rm[:P])

@@ -1,0 +1,384 @@
+/*
+ * oracle.c -- plain, slow, sequential fp64 CPU reference of the
+ * verify-and-sample step of speculative decoding (SD) and of the
+ * reweight / ESS / resample step of SMC speculative decoding (SMC-SD).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, calls or
+ * reads this file.  Only the test suite, the package smoke check and the
+ * CPU-baseline leg of the benchmark may load it.  It shares no code, header,
+ * table or helper with the GPU path.
+ *
+ * Sources (pages by title and section):
+ *   [SMC]   "Faster LLM Inference via Sequential Monte Carlo"
+ *           sec. 1 (Das Problem): SD is rejection sampling and drops the rest of
+ *           the block at the first mismatch;
+ *           sec. 2 (Methodik), steps 1-4: draft K tokens per particle, score
+ *           them with the target, reweight by the target/draft probability
+ *           ratio, resample when the effective sample size falls below a
+ *           threshold; every step yields exactly K+1 tokens per particle;
+ *           sec. 3 (Schluesselbeitraege): resampling is a pointer / page-table
+ *           metadata update of a paged KV cache.
+ *   [XFAM]  "Cross-Family Speculative Decoding for Polish Language Models on
+ *           Apple Silicon", sec. 1: the target verifies k draft tokens at once.
+ *   [PACER] "PACER: Blockwise Pre-verification for Speculative Decoding with
+ *           Adaptive Length", Methodik 1-3: per-sequence draft lengths vary.
+ * The pages print no formulas.  Where they name a step without a formula the
+ * textbook definition is used and named at that function: the SD acceptance
+ * min(1, p/q) and residual max(0, p - q) (standard speculative sampling), the
+ * Kish effective sample size, and systematic resampling.
+ *
+ * Conventions fixed here (each one is a reading of a silent point):
+ *   - logits are read exactly as stored (fp32, or bf16 widened exactly);
+ *   - a_i = z_i / T, M = max_i a_i, S = sum_i exp(a_i - M) summed in index
+ *     order, log p(i) = a_i - M - log S;
+ *   - accept draft token j iff u_j < p_j(x_j) / q_j(x_j) (strict; a tie
+ *     rejects);
+ *   - inverse CDF: smallest index i (ascending token id) whose inclusive
+ *     prefix sum C_i exceeds u * Z, strictly; if rounding leaves no such i,
+ *     the last index with positive weight (flag CDF_CLAMP);
+ *   - zero residual mass at the rejected position: sample p_n instead with
+ *     the same uniform (flag ZERO_RESIDUAL);
+ *   - SD uniforms per sequence: K_b accept uniforms, then one final uniform;
+ *   - SMC: the (K+1)-th token is drawn from the target row K; its proposal is
+ *     the target itself, so it adds log p - log p = 0 to the log-weight;
+ *   - ESS = (sum w)^2 / sum w^2 with w_i = exp(logw_i - max logw);
+ *     resample iff ESS < ess_frac * N (strict);
+ *   - systematic resampling: U_k = (u + k) / N, a_k = smallest i with
+ *     C_i > U_k, C the normalised inclusive cumulative weight; after
+ *     resampling every log-weight is 0;
+ *   - page tables: row k of the output is row a_k of the input.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* status bits (same meaning as the library's device flags) */
+#define ORACLE_FLAG_NONFINITE 1u
+#define ORACLE_FLAG_ZERO_RESIDUAL 2u
+#define ORACLE_FLAG_ZERO_WEIGHTS 4u
+#define ORACLE_FLAG_CDF_CLAMP 8u
+
+/* dtype codes: 0 = fp32, 1 = bf16 (raw 16-bit patterns) */
+double oracle_logit(int dtype, const void* row, int64_t i) {
+  if (dtype == 0) return (double)((const float*)row)[i];
+  uint32_t bits = ((uint32_t)((const uint16_t*)row)[i]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static const void* row_ptr(int dtype, const void* base, int64_t row, int64_t V) {
+  size_t esz = dtype == 0 ? 4 : 2;
+  return (const char*)base + (size_t)row * (size_t)V * esz;
+}
+
+/*
+ * Temperature softmax statistics of one row [SMC sec. 2 step 3 needs
+ * normalised target and draft probabilities; the temperature scales both].
+ * Returns 1 when the row is not a distribution (NaN or +inf logit, or every
+ * logit -inf), else 0.
+ */
+int oracle_row_stats(int dtype, const void* row, int64_t V, double T, double* M_out,
+                     double* logS_out) {
+  double M = -INFINITY;
+  int bad = 0;
+  for (int64_t i = 0; i < V; i++) {
+    double z = oracle_logit(dtype, row, i);
+    if (isnan(z) || z == INFINITY) bad = 1;
+    double a = z / T;
+    if (a > M) M = a;
+  }
+  if (M == -INFINITY) bad = 1;
+  double S = 0.0;
+  for (int64_t i = 0; i < V; i++) S += exp(oracle_logit(dtype, row, i) / T - M);
+  *M_out = M;
+  *logS_out = log(S);
+  return bad;
+}
+
+/* log p(i) of a row whose statistics are (M, logS). */
+static double logprob_with(int dtype, const void* row, int64_t i, double T, double M,
+                           double logS) {
+  return oracle_logit(dtype, row, i) / T - M - logS;
+}
+
+/* Convenience: log p(i) of a row, computing its statistics. */
+double oracle_logprob(int dtype, const void* row, int64_t V, double T, int64_t i) {
+  double M, logS;
+  oracle_row_stats(dtype, row, V, T, &M, &logS);
+  return logprob_with(dtype, row, i, T, M, logS);
+}
+
+/*
+ * Inverse-CDF draw from non-negative weights w[0..n) with uniform u in [0,1).
+ * Returns the index; *margin receives the distance, in units of u, from u to
+ * the nearer edge of the chosen index's CDF interval (0 when clamped).
+ */
+static int64_t inverse_cdf(const double* w, int64_t n, double u, double* margin,
+                           uint32_t* flags) {
+  double Z = 0.0;
+  for (int64_t i = 0; i < n; i++) Z += w[i];
+  double target = u * Z;
+  double C = 0.0;
+  for (int64_t i = 0; i < n; i++) {
+    double Cprev = C;
+    C += w[i];
+    if (C > target) {
+      if (margin) {
+        double lo = u - Cprev / Z, hi = C / Z - u;
+        *margin = lo < hi ? lo : hi;
+      }
+      return i;
+    }
+  }
+  *flags |= ORACLE_FLAG_CDF_CLAMP;
+  if (margin) *margin = 0.0;
+  for (int64_t i = n - 1; i >= 0; i--)
+    if (w[i] > 0.0) return i;
+  return n - 1;
+}
+
+/*
+ * Weights of the distribution the final SD token is drawn from, for one
+ * sequence whose first rejection is at position n (n == K_b: all accepted).
+ *   residual  (n <  K_b): w_i = max(0, p_n(i) - q_n(i))   [standard SD]
+ *   bonus     (n == K_b): w_i = p_{K_b}(i)                 [K+1-th token]
+ *   fallback  (residual mass exactly 0): w_i = p_n(i), flag ZERO_RESIDUAL.
+ */
+static void final_weights(int dtype, const void* trow, const void* drow, int64_t V,
+                          double T, double* w, uint32_t* flags) {
+  double Mt, lSt;
+  if (oracle_row_stats(dtype, trow, V, T, &Mt, &lSt)) *flags |= ORACLE_FLAG_NONFINITE;
+  if (!drow) {
+    for (int64_t i = 0; i < V; i++) w[i] = exp(logprob_with(dtype, trow, i, T, Mt, lSt));
+    return;
+  }
+  double Md, lSd;
+  if (oracle_row_stats(dtype, drow, V, T, &Md, &lSd)) *flags |= ORACLE_FLAG_NONFINITE;
+  double Z = 0.0;
+  for (int64_t i = 0; i < V; i++) {
+    double p = exp(logprob_with(dtype, trow, i, T, Mt, lSt));
+    double q = exp(logprob_with(dtype, drow, i, T, Md, lSd));
+    w[i] = p - q > 0.0 ? p - q : 0.0;
+    Z += w[i];
+  }
+  if (Z == 0.0) {
+    *flags |= ORACLE_FLAG_ZERO_RESIDUAL;
+    for (int64_t i = 0; i < V; i++) w[i] = exp(logprob_with(dtype, trow, i, T, Mt, lSt));
+  }
+}
+
+/* Sequence b's draft-row base and draft length (fixed K or CSR offsets). */
+static void seq_layout(int b, int K, const int32_t* offsets, int64_t* d0, int* Kb) {
+  if (offsets) {
+    *d0 = offsets[b];
+    *Kb = offsets[b + 1] - offsets[b];
+  } else {
+    *d0 = (int64_t)b * K;
+    *Kb = K;
+  }
+}
+
+/*
+ * Standard SD verify of B sequences [SMC sec. 1; XFAM sec. 1; PACER Methodik
+ * for ragged lengths].  Sequence b has K_b draft rows starting at draft row
+ * d0 = offsets[b] (or b*K) and K_b + 1 target rows starting at target row
+ * d0 + b; its uniforms start at the same index d0 + b.
+ *
+ * accept_margin[d0 + j]: |u_j - min(1, rho_j)| for each evaluated position j,
+ *                        -1 for positions after the first rejection.
+ * sample_margin[b]:      margin of the final inverse-CDF draw.
+ * Returns 0.
+ */
+int oracle_sd_verify(int dtype, int B, int K, int64_t V, double T, const void* target,
+                     const void* draft, const int32_t* tokens, const float* uniforms,
+                     const int32_t* offsets, int32_t* num_accepted, int32_t* final_token,
+                     uint32_t* flags, double* accept_margin, double* sample_margin) {
+  double* w = (double*)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+  uint32_t fl = 0;
+  for (int b = 0; b < B; b++) {
+    int64_t d0;
+    int Kb;
+    seq_layout(b, K, offsets, &d0, &Kb);
+    int64_t t0 = d0 + b;
+    int n = Kb;
+    for (int j = 0; j < Kb; j++) {
+      const void* trow = row_ptr(dtype, target, t0 + j, V);
+      const void* drow = row_ptr(dtype, draft, d0 + j, V);
+      int32_t x = tokens[d0 + j];
+      double Mt, lSt, Md, lSd;
+      if (oracle_row_stats(dtype, trow, V, T, &Mt, &lSt)) fl |= ORACLE_FLAG_NONFINITE;
+      if (oracle_row_stats(dtype, drow, V, T, &Md, &lSd)) fl |= ORACLE_FLAG_NONFINITE;
+      double lp = logprob_with(dtype, trow, x, T, Mt, lSt);
+      double lq = logprob_with(dtype, drow, x, T, Md, lSd);
+      double rho = exp(lp - lq);
+      double u = (double)uniforms[t0 + j];
+      if (accept_margin) accept_margin[d0 + j] = fabs(u - (rho < 1.0 ? rho : 1.0));
+      if (!(u < rho)) {
+        n = j;
+        break;
+      }
+    }
+    if (accept_margin)
+      for (int j = n + 1; j < Kb; j++) accept_margin[d0 + j] = -1.0;
+    num_accepted[b] = n;
+    const void* trow = row_ptr(dtype, target, t0 + n, V);
+    const void* drow = n < Kb ? row_ptr(dtype, draft, d0 + n, V) : NULL;
+    final_weights(dtype, trow, drow, V, T, w, &fl);
+    double m = 0.0;
+    final_token[b] = (int32_t)inverse_cdf(w, V, (double)uniforms[t0 + Kb], &m, &fl);
+    if (sample_margin) sample_margin[b] = m;
+  }
+  free(w);
+  if (flags) *flags |= fl;
+  return 0;
+}
+
+/*
+ * Normalised CDF (C_i / Z, i = 0..V-1) of the distribution sequence b's final
+ * token is drawn from, given its number of accepted tokens n.  Used by the
+ * comparison to judge a differing token against the decision band.
+ */
+int oracle_sd_final_cdf(int dtype, int b, int K, int64_t V, double T, const void* target,
+                        const void* draft, const int32_t* offsets, int n, double* cdf) {
+  int64_t d0;
+  int Kb;
+  seq_layout(b, K, offsets, &d0, &Kb);
+  uint32_t fl = 0;
+  const void* trow = row_ptr(dtype, target, d0 + b + n, V);
+  const void* drow = n < Kb ? row_ptr(dtype, draft, d0 + n, V) : NULL;
+  final_weights(dtype, trow, drow, V, T, cdf, &fl);
+  double Z = 0.0;
+  for (int64_t i = 0; i < V; i++) Z += cdf[i];
+  double C = 0.0;
+  for (int64_t i = 0; i < V; i++) {
+    C += cdf[i];
+    cdf[i] = C / Z;
+  }
+  return (int)fl;
+}
+
+/*
+ * One SMC-SD step for P prompts of N particles each [SMC sec. 2 steps 3-4 and
+ * the K+1 tokens per step; sec. 3 pointer-only resampling].
+ * Particle i = p*N + n owns target rows i*(K+1) .. i*(K+1)+K and draft rows
+ * i*K .. i*K+K-1.
+ *
+ *   log-weight:   logw'_i = fp32(logw_i + sum_{j<K} (log p_ij(x_ij) - log q_ij(x_ij)))
+ *   bonus token:  inverse CDF of p_{i,K} with bonus_u[i]
+ *   ESS:          Kish, (sum w)^2 / sum w^2, w_i = exp(logw'_i - max)
+ *   resample iff ESS < ess_frac * N: systematic with resample_u[p];
+ *                 ancestors (local indices), logw_out = 0, page-table rows
+ *                 gathered by ancestor; otherwise identity and logw_out = logw'.
+ *
+ * logw is updated in place.  pt_in / pt_out may be NULL (L ignored).
+ * cum_weight[i] (optional) receives the normalised inclusive cumulative weight
+ * C_i used by the systematic draw (or -1 when the prompt did not resample);
+ * bonus_margin[i], ess_margin[p] = |ESS - ess_frac*N| / N and
+ * resample_margin[p] = min_k distance of U_k to its interval edges (optional).
+ * Returns 0.
+ */
+int oracle_smc_step(int dtype, int P, int N, int K, int64_t V, double T, double ess_frac,
+                    const void* target, const void* draft, const int32_t* tokens,
+                    const float* bonus_u, const float* resample_u, float* logw,
+                    const int32_t* pt_in, int32_t* pt_out, int L, int32_t* bonus,
+                    int32_t* ancestors, float* ess, int32_t* resampled, uint32_t* flags,
+                    double* cum_weight, double* bonus_margin, double* ess_margin,
+                    double* resample_margin) {
+  double* w = (double*)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+  double* pw = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  double* C = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  float* lw = (float*)malloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
+  uint32_t fl = 0;
+  for (int p = 0; p < P; p++) {
+    /* reweight each particle by the target/draft ratio of its K draft tokens */
+    for (int n = 0; n < N; n++) {
+      int64_t i = (int64_t)p * N + n;
+      double delta = 0.0;
+      for (int j = 0; j < K; j++) {
+        const void* trow = row_ptr(dtype, target, i * (K + 1) + j, V);
+        const void* drow = row_ptr(dtype, draft, i * K + j, V);
+        int32_t x = tokens[i * K + j];
+        double Mt, lSt, Md, lSd;
+        if (oracle_row_stats(dtype, trow, V, T, &Mt, &lSt)) fl |= ORACLE_FLAG_NONFINITE;
+        if (oracle_row_stats(dtype, drow, V, T, &Md, &lSd)) fl |= ORACLE_FLAG_NONFINITE;
+        delta += logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);
+      }
+      lw[n] = (float)((double)logw[i] + delta);
+      if (isnan(lw[n]) || lw[n] == INFINITY) fl |= ORACLE_FLAG_NONFINITE;
+      /* the (K+1)-th token, drawn from the target's row K */
+      final_weights(dtype, row_ptr(dtype, target, i * (K + 1) + K, V), NULL, V, T, w, &fl);
+      double m = 0.0;
+      bonus[i] = (int32_t)inverse_cdf(w, V, (double)bonus_u[i], &m, &fl);
+      if (bonus_margin) bonus_margin[i] = m;
+    }
+    /* effective sample size of the normalised weights */
+    double M = -INFINITY;
+    for (int n = 0; n < N; n++)
+      if ((double)lw[n] > M) M = (double)lw[n];
+    double Sw = 0.0, Sw2 = 0.0;
+    int do_resample = 0;
+    double E = 0.0;
+    if (M == -INFINITY) {
+      fl |= ORACLE_FLAG_ZERO_WEIGHTS;
+    } else {
+      for (int n = 0; n < N; n++) {
+        pw[n] = exp((double)lw[n] - M);
+        Sw += pw[n];
+        Sw2 += pw[n] * pw[n];
+      }
+      E = Sw * Sw / Sw2;
+      do_resample = E < ess_frac * N;
+    }
+    ess[p] = (float)E;
+    if (ess_margin) ess_margin[p] = fabs(E - ess_frac * N) / N;
+    resampled[p] = do_resample;
+    double rmargin = INFINITY;
+    if (do_resample) {
+      double acc = 0.0;
+      for (int n = 0; n < N; n++) {
+        acc += pw[n];
+        C[n] = acc / Sw;
+      }
+      for (int k = 0; k < N; k++) {
+        double U = ((double)resample_u[p] + k) / N;
+        int a = -1;
+        for (int n = 0; n < N; n++)
+          if (C[n] > U) {
+            a = n;
+            break;
+          }
+        if (a < 0) {
+          fl |= ORACLE_FLAG_CDF_CLAMP;
+          for (a = N - 1; a > 0 && pw[a] == 0.0; a--) {
+          }
+          rmargin = 0.0;
+        } else {
+          double lo = U - (a > 0 ? C[a - 1] : 0.0), hi = C[a] - U;
+          double mm = lo < hi ? lo : hi;
+          if (mm < rmargin) rmargin = mm;
+        }
+        ancestors[(int64_t)p * N + k] = a;
+      }
+    } else {
+      for (int k = 0; k < N; k++) ancestors[(int64_t)p * N + k] = k;
+    }
+    if (resample_margin) resample_margin[p] = rmargin;
+    for (int k = 0; k < N; k++) {
+      int64_t i = (int64_t)p * N + k;
+      if (cum_weight) cum_weight[i] = do_resample ? C[k] : -1.0;
+      logw[i] = do_resample ? 0.0f : lw[k];
+      if (pt_in && pt_out) {
+        int64_t src = (int64_t)p * N + ancestors[i];
+        for (int l = 0; l < L; l++) pt_out[i * L + l] = pt_in[src * L + l];
+      }
+    }
+  }
+  free(w);
+  free(pw);
+  free(C);
+  free(lw);
+  if (flags) *flags |= fl;
+  return 0;
+}

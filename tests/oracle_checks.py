@@ -1,0 +1,498 @@
+"""Checks that pin the oracle to facts fixed outside itself.
+
+Each ``check_*`` takes a loaded oracle library (``oracle.load()`` or a mutant
+built by the mutation test) and raises ``AssertionError`` on a violation.  The
+pins are hand-derived worked examples (``tests/golden``), closed forms,
+textbook invariants, library routines (scipy ``log_softmax``, numpy
+``searchsorted``), exact rational brute force and exact output laws obtained by
+integrating the oracle's piecewise-constant decisions over the uniforms.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+from scipy.special import log_softmax, softmax
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _logits(probs):
+    return np.log(np.asarray(probs, dtype=np.float64)).astype(np.float32)
+
+
+def rand_sd_problem(rng, B, K, V, T, delta, scale=3.0, dtype=np.float32):
+    """Random SD inputs with x_j ~ q_j (drawn here with numpy)."""
+    zt = (scale * rng.standard_normal((B * (K + 1), V))).astype(np.float32)
+    rows_t = zt.reshape(B, K + 1, V)
+    zd = (rows_t[:, :K, :] + delta * rng.standard_normal((B, K, V))).astype(np.float32).reshape(B * K, V)
+    q = softmax(zd.astype(np.float64) / T, axis=-1)
+    cq = np.cumsum(q, axis=-1)
+    r = rng.random((B * K, 1))
+    tok = np.minimum((cq < r * cq[:, -1:]).sum(axis=-1), V - 1).astype(np.int32)
+    u = rng.random(B * (K + 1)).astype(np.float32)
+    return zt, zd, tok, u
+
+
+# --------------------------------------------------------------------------
+# golden worked examples
+# --------------------------------------------------------------------------
+
+
+def check_golden_sd_fixed(lib):
+    g = _load_golden("sd_fixed_k2.json")
+    r = oracle.sd_verify(_logits(g["target_probs"]), _logits(g["draft_probs"]), g["tokens"], g["uniforms"],
+                         g["T"], K=g["K"], lib=lib)
+    assert r["num_accepted"].tolist() == g["expect"]["num_accepted"], r
+    assert r["final_token"].tolist() == g["expect"]["final_token"], r
+
+
+def check_golden_sd_csr(lib):
+    g = _load_golden("sd_csr_ragged.json")
+    r = oracle.sd_verify(_logits(g["target_probs"]), _logits(g["draft_probs"]), g["tokens"], g["uniforms"],
+                         g["T"], offsets=g["offsets"], lib=lib)
+    assert r["num_accepted"].tolist() == g["expect"]["num_accepted"], r
+    assert r["final_token"].tolist() == g["expect"]["final_token"], r
+
+
+def check_golden_smc(lib):
+    g = _load_golden("smc_step_n4.json")
+    lw = (np.array(g["logw_in_ln4_multiples"], np.float64) * math.log(4.0)).astype(np.float32)
+    r = oracle.smc_step(_logits(g["target_probs"]), _logits(g["draft_probs"]), g["tokens"], g["bonus_u"],
+                        g["resample_u"], lw, g["T"], g["ess_frac"], g["P"], g["N"], g["K"],
+                        pt_in=np.array(g["page_table_in"], np.int32), lib=lib)
+    e = g["expect"]
+    assert r["resampled"].tolist() == e["resampled"], r
+    assert r["ancestors"].tolist() == e["ancestors"], r
+    assert r["bonus"].tolist() == e["bonus"], r
+    assert r["logw"].tolist() == e["logw_out"], r
+    assert r["pt_out"].tolist() == e["page_table_out"], r
+    assert abs(float(r["ess"][0]) - e["ess"]) < 1e-6, r
+
+
+# --------------------------------------------------------------------------
+# row statistics (temperature softmax)
+# --------------------------------------------------------------------------
+
+
+def check_constant_row(lib):
+    for V in (1, 7, 32000):
+        for T in (1.0, 0.7):
+            row = np.full(V, 1.25, np.float32)
+            lp = oracle.logprob(row, T, V // 2, lib=lib)
+            assert lp == -math.log(V), (V, T, lp)
+
+
+def check_two_valued_row(lib):
+    V, k, a, b = 1000, 7, 2.5, -1.0
+    for T in (1.0, 0.7, 2.0):
+        row = np.full(V, b, np.float32)
+        row[[3, 50, 51, 400, 777, 998, 999]] = a
+        expect_a = -math.log(k + (V - k) * math.exp((b - a) / T))
+        expect_b = (b - a) / T + expect_a
+        assert abs(oracle.logprob(row, T, 50, lib=lib) - expect_a) < 1e-13
+        assert abs(oracle.logprob(row, T, 0, lib=lib) - expect_b) < 1e-13
+
+
+def _bf16_bits(x32):
+    """Round float32 to bf16 (round to nearest even); returns uint16 bits."""
+    b = np.asarray(x32, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_rows_vs_scipy(lib):
+    rng = np.random.default_rng(11)
+    for V, T in ((33, 1.0), (4096, 0.7), (151936, 1.0)):
+        z = (3 * rng.standard_normal(V)).astype(np.float32)
+        ref = log_softmax(z.astype(np.float64) / T)
+        for i in (0, V // 3, V - 1):
+            assert abs(oracle.logprob(z, T, i, lib=lib) - ref[i]) < 1e-11
+        zb = _bf16_bits(z)
+        refb = log_softmax(_bf16_to_f64(zb) / T)
+        for i in (1, V // 2, V - 2):
+            assert abs(oracle.logprob(zb, T, i, lib=lib) - refb[i]) < 1e-11
+
+
+# --------------------------------------------------------------------------
+# SD verify
+# --------------------------------------------------------------------------
+
+
+def check_accept_tie_rejects(lib):
+    """rho = p/q = 0.5 exactly and u = 0.5: the strict test rejects."""
+    target = np.array([[0.0, 0.0], [0.0, 0.0]], np.float32)  # p = (1/2, 1/2)
+    draft = np.array([[0.0, -np.inf]], np.float32)  # q = (1, 0)
+    rho = math.exp(oracle.logprob(target[0], 1.0, 0, lib=lib) - oracle.logprob(draft[0], 1.0, 0, lib=lib))
+    assert rho == 0.5, rho
+    r = oracle.sd_verify(target, draft, [0], [0.5, 0.1], 1.0, K=1, lib=lib)
+    assert r["num_accepted"].tolist() == [0], r
+    r = oracle.sd_verify(target, draft, [0], [np.nextafter(np.float32(0.5), np.float32(0)), 0.1], 1.0, K=1, lib=lib)
+    assert r["num_accepted"].tolist() == [1], r
+
+
+def check_cdf_tie(lib):
+    """Uniform p over 4 tokens has CDF (1/4, 1/2, 3/4, 1); u = 1/4 exactly picks index 1."""
+    target = np.zeros((1, 4), np.float32)
+    draft = np.zeros((0, 4), np.float32)
+    for u, want in ((0.0, 0), (0.25, 1), (0.5, 2), (0.7499, 2), (0.75, 3), (0.99999994, 3)):
+        r = oracle.sd_verify(target, draft, np.zeros(0, np.int32), [u], 1.0, K=0, lib=lib)
+        assert r["final_token"].tolist() == [want], (u, r)
+        assert r["num_accepted"].tolist() == [0]
+
+
+def _midpoints(cdf):
+    """Midpoints and lengths of the intervals [C_{i-1}, C_i) with positive length."""
+    edges = np.concatenate([[0.0], cdf])
+    lo, hi = edges[:-1], edges[1:]
+    keep = hi - lo > 1e-9
+    return (0.5 * (lo + hi))[keep], (hi - lo)[keep]
+
+
+def check_sd_exact_law(lib):
+    """K=1: integrate the oracle's decisions over (x_0 ~ q, u_0, u_1) exactly.
+
+    The first emitted token must follow p_0 and, given acceptance, the second
+    must follow p_1 (standard SD is exact).
+    """
+    rng = np.random.default_rng(5)
+    for V, T, delta in ((3, 1.0, 1.0), (5, 0.7, 2.0), (6, 1.3, 0.4)):
+        zt = (2 * rng.standard_normal((2, V))).astype(np.float32)
+        zd = (zt[:1] + delta * rng.standard_normal((1, V))).astype(np.float32)
+        p0 = softmax(zt[0].astype(np.float64) / T)
+        p1 = softmax(zt[1].astype(np.float64) / T)
+        q0 = softmax(zd[0].astype(np.float64) / T)
+        a = np.minimum(1.0, p0 / q0)
+        res = np.maximum(0.0, p0 - q0)
+        res_mid, res_len = _midpoints(np.cumsum(res / res.sum()))
+        bon_mid, bon_len = _midpoints(np.cumsum(p1))
+        law0 = np.zeros(V)
+        law1 = np.zeros(V)
+        for x in range(V):
+            # accept region u_0 in [0, a): followed by the bonus draw from p_1
+            B = len(bon_mid)
+            u = np.stack([np.full(B, a[x] / 2), bon_mid], axis=1).astype(np.float32).ravel()
+            r = oracle.sd_verify(np.tile(zt, (B, 1)), np.tile(zd, (B, 1)), np.full(B, x, np.int32), u, T, K=1, lib=lib)
+            assert (r["num_accepted"] == 1).all(), (x, r)
+            law0[x] += q0[x] * a[x]
+            for t, w in zip(r["final_token"], bon_len):
+                law1[t] += q0[x] * a[x] * w
+            if a[x] < 1.0:
+                B = len(res_mid)
+                u = np.stack([np.full(B, (1 + a[x]) / 2), res_mid], axis=1).astype(np.float32).ravel()
+                r = oracle.sd_verify(np.tile(zt, (B, 1)), np.tile(zd, (B, 1)), np.full(B, x, np.int32), u, T, K=1,
+                                     lib=lib)
+                assert (r["num_accepted"] == 0).all(), (x, r)
+                for t, w in zip(r["final_token"], res_len):
+                    law0[t] += q0[x] * (1 - a[x]) * w
+        acc = float(np.sum(np.minimum(p0, q0)))
+        assert np.abs(law0 - p0).max() < 1e-9, (law0, p0)
+        assert np.abs(law1 / acc - p1).max() < 1e-9, (law1 / acc, p1)
+
+
+def check_bonus_vs_numpy(lib):
+    """draft == target (delta = 0): every token accepted, final token is a plain
+    categorical inverse-CDF draw from p_K, i.e. numpy searchsorted."""
+    rng = np.random.default_rng(7)
+    B, K, V, T = 64, 3, 777, 0.8
+    zt, zd, tok, u = rand_sd_problem(rng, B, K, V, T, delta=0.0)
+    zd = zt.reshape(B, K + 1, V)[:, :K].reshape(B * K, V).copy()
+    r = oracle.sd_verify(zt, zd, tok, u, T, K=K, lib=lib)
+    assert (r["num_accepted"] == K).all()
+    for b in range(B):
+        p = softmax(zt[b * (K + 1) + K].astype(np.float64) / T)
+        c = np.cumsum(p)
+        uf = float(u[b * (K + 1) + K])
+        want = int(np.searchsorted(c, uf * c[-1], side="right"))
+        if np.min(np.abs(c / c[-1] - uf)) > 1e-12:
+            assert r["final_token"][b] == want, (b, r["final_token"][b], want)
+
+
+def check_residual_vs_numpy(lib):
+    rng = np.random.default_rng(8)
+    B, K, V, T = 96, 2, 500, 1.0
+    zt, zd, tok, u = rand_sd_problem(rng, B, K, V, T, delta=2.0)
+    r = oracle.sd_verify(zt, zd, tok, u, T, K=K, lib=lib)
+    seen = 0
+    for b in range(B):
+        n = int(r["num_accepted"][b])
+        if n == K:
+            continue
+        seen += 1
+        p = softmax(zt[b * (K + 1) + n].astype(np.float64) / T)
+        q = softmax(zd[b * K + n].astype(np.float64) / T)
+        c = np.cumsum(np.maximum(0.0, p - q))
+        uf = float(u[b * (K + 1) + K])
+        want = int(np.searchsorted(c, uf * c[-1], side="right"))
+        if np.min(np.abs(c / c[-1] - uf)) > 1e-12:
+            assert r["final_token"][b] == want, (b, r["final_token"][b], want)
+    assert seen > B // 2
+
+
+def check_accept_decisions_vs_scipy(lib):
+    """n = index of the first j with u_j >= p_j(x_j)/q_j(x_j) (scipy softmax)."""
+    rng = np.random.default_rng(9)
+    B, K, V, T = 128, 4, 300, 0.9
+    zt, zd, tok, u = rand_sd_problem(rng, B, K, V, T, delta=1.0)
+    r = oracle.sd_verify(zt, zd, tok, u, T, K=K, lib=lib)
+    lp = log_softmax(zt.astype(np.float64) / T, axis=-1).reshape(B, K + 1, V)
+    lq = log_softmax(zd.astype(np.float64) / T, axis=-1).reshape(B, K, V)
+    for b in range(B):
+        n = K
+        for j in range(K):
+            x = tok[b * K + j]
+            rho = math.exp(lp[b, j, x] - lq[b, j, x])
+            if abs(u[b * (K + 1) + j] - min(1.0, rho)) < 1e-12:
+                n = None
+                break
+            if not u[b * (K + 1) + j] < rho:
+                n = j
+                break
+        if n is not None:
+            assert r["num_accepted"][b] == n, (b, r["num_accepted"][b], n)
+
+
+def check_sd_statistics(lib, trials=200_000, configs=((5, 2), (3, 1), (8, 4))):
+    """Chi-square: the token emitted at position j, given it is reached, follows
+    p_j; the acceptance rate at position 0 is sum(min(p, q))."""
+    from scipy.stats import chisquare
+
+    rng = np.random.default_rng(123)
+    for V, K in configs:
+        T = 1.0
+        zt1 = (1.5 * rng.standard_normal((K + 1, V))).astype(np.float32)
+        zd1 = (zt1[:K] + 1.0 * rng.standard_normal((K, V))).astype(np.float32)
+        q = softmax(zd1.astype(np.float64) / T, axis=-1)
+        p = softmax(zt1.astype(np.float64) / T, axis=-1)
+        B = trials
+        tok = np.stack([rng.choice(V, size=B, p=q[j]) for j in range(K)], axis=1).astype(np.int32).ravel()
+        u = rng.random(B * (K + 1)).astype(np.float32)
+        r = oracle.sd_verify(np.tile(zt1, (B, 1)), np.tile(zd1, (B, 1)), tok, u, T, K=K, lib=lib)
+        n = r["num_accepted"]
+        y = r["final_token"]
+        toks = tok.reshape(B, K)
+        alpha0 = float(np.minimum(p[0], q[0]).sum())
+        rate = float(np.mean(n >= 1)) if K >= 1 else None
+        if rate is not None:
+            sd = math.sqrt(alpha0 * (1 - alpha0) / B)
+            assert abs(rate - alpha0) < 5 * sd, (rate, alpha0)
+        for j in range(K + 1):
+            reach = n >= j
+            emitted = np.where(n[reach] > j, toks[reach][:, min(j, K - 1)] if K > 0 else 0, y[reach])
+            cnt = np.bincount(emitted, minlength=V)
+            exp = p[j] * reach.sum()
+            keep = exp > 5
+            stat = chisquare(cnt[keep], exp[keep] * cnt[keep].sum() / exp[keep].sum())
+            assert stat.pvalue > 1e-4, (V, K, j, stat)
+
+
+def check_expected_length(lib, trials=200_000):
+    """Identical (p, q) at every position make the acceptance events iid with
+    alpha = sum(min(p, q)); then E[n + 1] = (1 - alpha^(K+1)) / (1 - alpha)."""
+    rng = np.random.default_rng(77)
+    V, K, T = 6, 4, 1.0
+    zt1 = (1.5 * rng.standard_normal(V)).astype(np.float32)
+    zd1 = (zt1 + 1.2 * rng.standard_normal(V)).astype(np.float32)
+    p = softmax(zt1.astype(np.float64))
+    q = softmax(zd1.astype(np.float64))
+    alpha = float(np.minimum(p, q).sum())
+    B = trials
+    tok = rng.choice(V, size=B * K, p=q).astype(np.int32)
+    u = rng.random(B * (K + 1)).astype(np.float32)
+    r = oracle.sd_verify(np.tile(zt1, (B * (K + 1), 1)), np.tile(zd1, (B * K, 1)), tok, u, T, K=K, lib=lib)
+    L = r["num_accepted"].astype(np.float64) + 1
+    want = (1 - alpha ** (K + 1)) / (1 - alpha)
+    assert abs(L.mean() - want) < 5 * L.std() / math.sqrt(B), (L.mean(), want)
+
+
+# --------------------------------------------------------------------------
+# SMC step
+# --------------------------------------------------------------------------
+
+
+def _smc_from_logw(lib, logw, u_r, ess_frac=0.5, L=3):
+    """Run the SMC step with K=0 (no draft rows), so logw' = logw exactly."""
+    N = len(logw)
+    V = 4
+    target = np.zeros((N, V), np.float32)
+    draft = np.zeros((0, V), np.float32)
+    pt = np.arange(N * L, dtype=np.int32).reshape(N, L)
+    return oracle.smc_step(target, draft, np.zeros(0, np.int32), np.full(N, 0.5, np.float32), [u_r],
+                           np.asarray(logw, np.float32), 1.0, ess_frac, 1, N, 0, pt_in=pt, lib=lib)
+
+
+def check_ess_closed_forms(lib):
+    for N in (1, 4, 16, 64):
+        r = _smc_from_logw(lib, np.full(N, -3.25), 0.3)
+        assert r["ess"][0] == N, r["ess"]
+        assert r["resampled"][0] == 0
+    lw = np.full(16, -np.inf)
+    lw[5] = 1.0
+    r = _smc_from_logw(lib, lw, 0.3)
+    assert r["ess"][0] == 1.0 and r["resampled"][0] == 1
+    assert r["ancestors"].tolist() == [5] * 16
+    # two-valued: k particles at weight 1, N-k at weight e^-2
+    N, k = 10, 3
+    lw = np.full(N, -2.0)
+    lw[:k] = 0.0
+    a, b = 1.0, math.exp(-2.0)
+    want = (k * a + (N - k) * b) ** 2 / (k * a * a + (N - k) * b * b)
+    r = _smc_from_logw(lib, lw, 0.3)
+    assert abs(float(r["ess"][0]) - want) < 1e-5, (r["ess"], want)
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        N = int(rng.integers(1, 80))
+        r = _smc_from_logw(lib, 4 * rng.standard_normal(N), float(rng.random()))
+        assert 1.0 - 1e-6 <= r["ess"][0] <= N + 1e-4
+
+
+def check_threshold_strict(lib):
+    """N=2, weights (1, 0): ESS = 1 = 0.5 * N exactly, which is not below it."""
+    r = _smc_from_logw(lib, [0.0, -np.inf], 0.3)
+    assert r["ess"][0] == 1.0 and r["resampled"][0] == 0, r
+    r = _smc_from_logw(lib, [0.0, -np.inf], 0.3, ess_frac=0.51)
+    assert r["resampled"][0] == 1 and r["ancestors"].tolist() == [0, 0], r
+
+
+def check_systematic_invariants(lib):
+    rng = np.random.default_rng(21)
+    for trial in range(60):
+        N = int(rng.integers(2, 65))
+        lw = 2.5 * rng.standard_normal(N)
+        u = float(rng.random())
+        r = _smc_from_logw(lib, lw, u, ess_frac=1.01)  # always resample
+        assert r["resampled"][0] == 1
+        a = r["ancestors"]
+        assert (np.diff(a) >= 0).all(), a
+        w = np.exp(lw.astype(np.float32).astype(np.float64) - lw.max())
+        w /= w.sum()
+        cnt = np.bincount(a, minlength=N)
+        assert cnt.sum() == N
+        lo, hi = np.floor(N * w - 1e-9), np.ceil(N * w + 1e-9)
+        assert ((cnt >= lo) & (cnt <= hi)).all(), (N * w, cnt)
+        assert (r["logw"] == 0).all()
+        pt = np.arange(N * 3).reshape(N, 3)
+        assert (r["pt_out"] == pt[a]).all()
+    for N in (1, 2, 7, 64):
+        for u in (0.0, 0.3, 0.9999999):
+            r = _smc_from_logw(lib, np.zeros(N), u, ess_frac=1.01)
+            assert r["ancestors"].tolist() == list(range(N)), (N, u, r["ancestors"])
+
+
+def check_systematic_fraction_bruteforce(lib):
+    """Exact rational systematic resampling on the oracle's own float weights."""
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        N = int(rng.integers(1, 9))
+        lw = (1.5 * rng.standard_normal(N)).astype(np.float32)
+        u = np.float32(rng.random())
+        r = _smc_from_logw(lib, lw, float(u), ess_frac=1.01)
+        M = float(lw.max())
+        w = [Fraction(math.exp(float(x) - M)) for x in lw]
+        S = sum(w)
+        C = []
+        acc = Fraction(0)
+        for x in w:
+            acc += x
+            C.append(acc / S)
+        want = []
+        for k in range(N):
+            U = (Fraction(float(u)) + k) / N
+            want.append(next(i for i in range(N) if C[i] > U))
+        near = min(abs(float(C[i] - (Fraction(float(u)) + k) / N)) for i in range(N) for k in range(N))
+        if near > 1e-12:
+            assert r["ancestors"].tolist() == want, (lw, u, r["ancestors"], want)
+
+
+def check_smc_reweight_vs_scipy(lib):
+    rng = np.random.default_rng(41)
+    P, N, K, V, T = 2, 5, 3, 257, 0.9
+    zt = (3 * rng.standard_normal((P * N * (K + 1), V))).astype(np.float32)
+    zd = (zt.reshape(P * N, K + 1, V)[:, :K] + rng.standard_normal((P * N, K, V))).astype(np.float32)
+    zd = zd.reshape(P * N * K, V)
+    tok = rng.integers(0, V, P * N * K).astype(np.int32)
+    lw0 = rng.standard_normal(P * N).astype(np.float32)
+    r = oracle.smc_step(zt, zd, tok, rng.random(P * N), rng.random(P), lw0, T, 0.0, P, N, K, lib=lib)
+    lp = log_softmax(zt.astype(np.float64) / T, axis=-1).reshape(P * N, K + 1, V)
+    lq = log_softmax(zd.astype(np.float64) / T, axis=-1).reshape(P * N, K, V)
+    for i in range(P * N):
+        d = sum(lp[i, j, tok[i * K + j]] - lq[i, j, tok[i * K + j]] for j in range(K))
+        assert abs(float(r["logw"][i]) - (float(lw0[i]) + d)) <= 1e-6 * max(1.0, abs(float(lw0[i]) + d)), i
+    assert (r["resampled"] == 0).all()
+
+
+def check_smc_delta_zero(lib):
+    """draft == target: every increment is exactly 0, so the log-weights carry over."""
+    rng = np.random.default_rng(43)
+    P, N, K, V = 1, 6, 2, 100
+    zt = (3 * rng.standard_normal((P * N * (K + 1), V))).astype(np.float32)
+    zd = zt.reshape(P * N, K + 1, V)[:, :K].reshape(P * N * K, V).copy()
+    tok = rng.integers(0, V, P * N * K).astype(np.int32)
+    lw0 = (0.01 * rng.standard_normal(P * N)).astype(np.float32)
+    r = oracle.smc_step(zt, zd, tok, rng.random(P * N), [0.5], lw0, 1.0, 0.5, P, N, K, lib=lib)
+    assert (r["logw"] == lw0).all(), (r["logw"], lw0)
+
+
+def check_smc_bonus_law(lib):
+    """The (K+1)-th token's law over its uniform is exactly p_K."""
+    rng = np.random.default_rng(45)
+    V, K, T = 7, 2, 1.1
+    zt = (2 * rng.standard_normal((K + 1, V))).astype(np.float32)
+    zd = (zt[:K] + rng.standard_normal((K, V))).astype(np.float32)
+    pK = softmax(zt[K].astype(np.float64) / T)
+    mid, ln = _midpoints(np.cumsum(pK))
+    N = len(mid)
+    tok = np.tile(rng.integers(0, V, K).astype(np.int32), N)
+    r = oracle.smc_step(np.tile(zt, (N, 1)), np.tile(zd, (N, 1)), tok, mid.astype(np.float32), [0.5],
+                        np.zeros(N, np.float32), T, 0.0, 1, N, K, lib=lib)
+    law = np.zeros(V)
+    for t, w in zip(r["bonus"], ln):
+        law[t] += w
+    assert np.abs(law - pK).max() < 1e-9, (law, pK)
+
+
+def check_smc_page_table_identity(lib):
+    rng = np.random.default_rng(47)
+    N, L = 8, 5
+    r = _smc_from_logw(lib, 0.01 * rng.standard_normal(N), 0.4, L=L)
+    assert r["resampled"][0] == 0
+    assert r["ancestors"].tolist() == list(range(N))
+    assert (r["pt_out"] == np.arange(N * L).reshape(N, L)).all()
+
+
+DETERMINISTIC_CHECKS = [
+    check_golden_sd_fixed,
+    check_golden_sd_csr,
+    check_golden_smc,
+    check_constant_row,
+    check_two_valued_row,
+    check_rows_vs_scipy,
+    check_accept_tie_rejects,
+    check_cdf_tie,
+    check_sd_exact_law,
+    check_bonus_vs_numpy,
+    check_residual_vs_numpy,
+    check_accept_decisions_vs_scipy,
+    check_ess_closed_forms,
+    check_threshold_strict,
+    check_systematic_invariants,
+    check_systematic_fraction_bruteforce,
+    check_smc_reweight_vs_scipy,
+    check_smc_delta_zero,
+    check_smc_bonus_law,
+    check_smc_page_table_identity,
+]

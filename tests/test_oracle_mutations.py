@@ -1,0 +1,70 @@
+"""The pins have power: each plausible mistake planted in a copy of the oracle
+(a dropped term, a wrong sign or index, a transposed operand, a flipped
+comparison) must make at least one pin fail.  Mutants are built on the CPU in
+a temporary directory; the real oracle is never modified."""
+import os
+
+import pytest
+
+import oracle
+import oracle_checks as oc
+
+MUTATIONS = [
+    ("temperature_dropped", "return oracle_logit(dtype, row, i) / T - M - logS;",
+     "return oracle_logit(dtype, row, i) - M - logS;"),
+    ("sum_skips_first", "for (int64_t i = 0; i < V; i++) S += exp(", "for (int64_t i = 1; i < V; i++) S += exp("),
+    ("log_of_sum_dropped", "*logS_out = log(S);", "*logS_out = S;"),
+    ("accept_tie_accepts", "if (!(u < rho)) {", "if (!(u <= rho)) {"),
+    ("ratio_inverted", "double rho = exp(lp - lq);", "double rho = exp(lq - lp);"),
+    ("residual_is_p", "w[i] = p - q > 0.0 ? p - q : 0.0;", "w[i] = p;"),
+    ("residual_transposed", "w[i] = p - q > 0.0 ? p - q : 0.0;", "w[i] = q - p > 0.0 ? q - p : 0.0;"),
+    ("cdf_non_strict", "if (C > target) {", "if (C >= target) {"),
+    ("no_first_reject_truncation", "n = j;\n        break;", "n = j;"),
+    ("final_row_off_by_one", "const void* trow = row_ptr(dtype, target, t0 + n, V);",
+     "const void* trow = row_ptr(dtype, target, t0 + (n > 0 ? n - 1 : 0), V);"),
+    ("final_uniform_index", "(double)uniforms[t0 + Kb]", "(double)uniforms[t0 + n]"),
+    ("target_base_without_b", "int64_t t0 = d0 + b;", "int64_t t0 = d0;"),
+    ("ess_formula", "E = Sw * Sw / Sw2;", "E = Sw / Sw2;"),
+    ("ess_threshold_non_strict", "do_resample = E < ess_frac * N;", "do_resample = E <= ess_frac * N;"),
+    ("systematic_stride", "double U = ((double)resample_u[p] + k) / N;",
+     "double U = ((double)resample_u[p] + k) / (N + 1);"),
+    ("systematic_non_strict", "if (C[n] > U) {", "if (C[n] >= U) {"),
+    ("logw_not_reset", "logw[i] = do_resample ? 0.0f : lw[k];", "logw[i] = lw[k];"),
+    ("page_table_scatter", "pt_out[i * L + l] = pt_in[src * L + l];", "pt_out[src * L + l] = pt_in[i * L + l];"),
+    ("increment_sign", "delta += logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);",
+     "delta += logprob_with(dtype, drow, x, T, Md, lSd) - logprob_with(dtype, trow, x, T, Mt, lSt);"),
+    ("old_weight_dropped", "lw[n] = (float)((double)logw[i] + delta);", "lw[n] = (float)delta;"),
+    ("bonus_from_first_row", "row_ptr(dtype, target, i * (K + 1) + K, V)", "row_ptr(dtype, target, i * (K + 1), V)"),
+    ("weights_not_exponentiated", "pw[n] = exp((double)lw[n] - M);", "pw[n] = (double)lw[n] - M;"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, source, name, old, new):
+    assert source.count(old) == 1, f"mutation site for {name} not unique in oracle.c"
+    src = tmp_path / f"{name}.c"
+    src.write_text(source.replace(old, new))
+    so = str(tmp_path / f"lib{name}.so")
+    oracle.build(str(src), so, strict=False)
+    lib = oracle.load(so)
+    caught = []
+    for check in oc.DETERMINISTIC_CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, ValueError, StopIteration, ZeroDivisionError, FloatingPointError) as e:
+            caught.append(check.__name__)
+            break
+    if not caught:
+        try:
+            oc.check_sd_statistics(lib, trials=100_000, configs=((5, 2),))
+            oc.check_expected_length(lib, trials=100_000)
+        except AssertionError:
+            caught.append("statistics")
+    assert caught, f"mutant {name} survived every pin"
+    os.remove(so)

@@ -1,0 +1,19 @@
+"""The oracle against what the pages and the mathematics fix (CPU only)."""
+import pytest
+
+import oracle_checks as oc
+
+
+@pytest.mark.parametrize("check", oc.DETERMINISTIC_CHECKS, ids=lambda f: f.__name__[6:])
+def test_pin(orc, check):
+    check(orc)
+
+
+def test_sd_output_law_chi_square(orc):
+    """SD's emitted tokens follow p (chi-square, 1e6 trials at V=5, K=2)."""
+    oc.check_sd_statistics(orc, trials=1_000_000, configs=((5, 2),))
+    oc.check_sd_statistics(orc, trials=200_000, configs=((2, 1), (3, 4), (8, 1)))
+
+
+def test_expected_accepted_length(orc):
+    oc.check_expected_length(orc, trials=1_000_000)
