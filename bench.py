@@ -1,0 +1,227 @@
+"""Benchmark of the verify-and-sample step on one MI355X.
+
+A step is one library call over one batch of seeded synthetic inputs: for the
+SD workloads sd_verify (row statistics, accept test with first-reject
+truncation, residual / bonus draw), for the SMC workloads
+smc_reweight_resample (reweight, bonus draw, ESS, systematic resampling,
+page-table gather).  Every step reads its own input batch, resident in HBM
+before timing starts; the batches together exceed the 256 MB Infinity Cache,
+so the timed steps stream from HBM.
+
+Prints one JSON line: verified draft positions per second (whole job), the
+roofline of the logit-streaming path against the 8 TB/s HBM peak, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload index (default: the SD B=64 K=4 V=32768 bf16 case)")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--max-batch-gb", type=float, default=24.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; --gpus N>1 is not supported (per-GPU sharding "
+                                   "is described in DESIGN.md)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import smc_resampling_amd as smcsd
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    steps = args.steps if args.steps is not None else cfg.steps
+    W = args.warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = synth.Generator(cfg, dev)
+
+    # ---------------- inputs: distinct batches, resident in HBM -------------
+    per_batch = synth.step_bytes(cfg, None if cfg.kind != "sd_ragged" else np.full(cfg.B, 7))
+    nb = min(steps + W, max(2, int(args.max_batch_gb * 1e9 // max(per_batch, 1))))
+    nb = max(nb, min(steps + W, -(-2 * MALL_BYTES // max(per_batch, 1))))
+    log(f"[bench] {cfg.name}: generating {nb} input batches of ~{per_batch / 1e6:.1f} MB")
+    batches = []
+    for b in range(nb):
+        batches.append(gen.sd_step(b) if cfg.kind != "smc" else gen.smc_step(b))
+    torch.cuda.synchronize()
+    positions = [synth.verified_positions(cfg, bt.get("Kb")) for bt in batches]
+    nbytes = [synth.step_bytes(cfg, bt.get("Kb")) for bt in batches]
+
+    # ---------------- prepared library calls ---------------------------------
+    def prepare(stream_handle):
+        calls = []
+        if cfg.kind == "smc":
+            P, N, K = cfg.P, cfg.N, cfg.K
+            logw = torch.zeros(P * N, dtype=torch.float32, device=dev)
+            pts = [torch.from_numpy(synth.initial_page_table(P, N, cfg.L)).to(dev), None]
+            pts[1] = torch.empty_like(pts[0])
+            ws = torch.empty(smcsd.smc_workspace_bytes(1, P, N, K, cfg.V) + 256, dtype=torch.uint8, device=dev)
+            outs = None
+            for s in range(steps + W):
+                bt = batches[s % nb]
+                call, o = smcsd.prepare_smc_reweight_resample(
+                    bt["target"], bt["draft"], bt["tokens"], bt["bonus_u"], bt["resample_u"], logw, cfg.T,
+                    cfg.ess_frac, P, N, K, page_table_in=pts[s % 2], page_table_out=pts[(s + 1) % 2],
+                    workspace=ws, stream=stream_handle,
+                    **({} if outs is None else {k: outs[k] for k in ("bonus_token", "ancestors", "ess", "resampled",
+                                                                    "status_flags")}))
+                outs = o
+                calls.append(call)
+        else:
+            rows_d = max(int(bt["total_draft_rows"]) for bt in batches)
+            ws = torch.empty(smcsd.sd_verify_workspace_bytes(1, cfg.B, cfg.K, cfg.V, rows_d) + 256, dtype=torch.uint8,
+                             device=dev)
+            outs = None
+            for s in range(steps + W):
+                bt = batches[s % nb]
+                call, o = smcsd.prepare_sd_verify(
+                    bt["target"], bt["draft"], bt["tokens"], bt["uniforms"], cfg.T, K=cfg.K,
+                    draft_offsets=bt["offsets"], workspace=ws, stream=stream_handle,
+                    **({} if outs is None else {k: outs[k] for k in ("num_accepted", "final_token", "status_flags")}))
+                outs = o
+                calls.append(call)
+        return calls, outs
+
+    # ---------------- timing --------------------------------------------------
+    if args.launch == "graph":
+        side = torch.cuda.Stream(device=dev)
+        calls, outs = prepare(side.cuda_stream)
+        with torch.cuda.stream(side):
+            for c in calls[:W]:
+                c()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for c in calls[W:]:
+                c()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            torch.cuda.synchronize()
+            ev0.record(side)
+            graph.replay()
+            ev1.record(side)
+        torch.cuda.synchronize()
+    else:
+        stream = torch.cuda.current_stream(dev)
+        calls, outs = prepare(stream.cuda_stream)
+        for c in calls[:W]:
+            c()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for c in calls[W:]:
+            c()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    flags = int(outs["status_flags"].item())
+    ms_per_step = ms / steps
+    timed = [(W + s) % nb for s in range(steps)]
+    pos_total = sum(positions[i] for i in timed)
+    bytes_total = sum(nbytes[i] for i in timed)
+    value = pos_total / (ms / 1e3)
+    achieved = bytes_total / steps / (ms_per_step / 1e3) / 1e9
+    log(f"[bench] {steps} steps in {ms:.3f} ms: {ms_per_step * 1e3:.2f} us/step, {value / 1e6:.2f} M positions/s, "
+        f"{achieved:.0f} GB/s algorithmic, flags={flags}")
+
+    # ---------------- CPU oracle on a bounded sample --------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from gpu_util import host_logits
+
+        done_pos, t_cpu, n_steps = 0, 0.0, 0
+        for i in range(nb):
+            bt = batches[i]
+            if cfg.kind == "smc":
+                # one prompt at a time: the oracle's unit of work
+                P, N, K = cfg.P, cfg.N, cfg.K
+                for p in range(P):
+                    rt = slice(p * N * (K + 1), (p + 1) * N * (K + 1))
+                    rd = slice(p * N * K, (p + 1) * N * K)
+                    tg, dr = host_logits(bt["target"][rt]), host_logits(bt["draft"][rd])
+                    tk = bt["tokens"][rd].cpu().numpy()
+                    ub = bt["bonus_u"][p * N:(p + 1) * N].cpu().numpy()
+                    ur = bt["resample_u"][p:p + 1].cpu().numpy()
+                    t0 = time.perf_counter()
+                    oracle.smc_step(tg, dr, tk, ub, ur, np.zeros(N, np.float32), cfg.T, cfg.ess_frac, 1, N, K)
+                    t_cpu += time.perf_counter() - t0
+                    done_pos += N * K
+                    if t_cpu > args.cpu_seconds:
+                        break
+                sample = f"{done_pos // (cfg.N * cfg.K)} prompts of {cfg.name}"
+            else:
+                tg, dr = host_logits(bt["target"]), host_logits(bt["draft"])
+                tk, u = bt["tokens"].cpu().numpy(), bt["uniforms"].cpu().numpy()
+                off = None if bt["offsets"] is None else bt["offsets"].cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.sd_verify(tg, dr, tk, u, cfg.T, K=cfg.K, offsets=off)
+                t_cpu += time.perf_counter() - t0
+                done_pos += positions[i]
+                n_steps += 1
+                sample = f"{n_steps} steps of {cfg.name}"
+            if t_cpu > args.cpu_seconds:
+                break
+        cpu = {"value": done_pos / t_cpu, "unit": "verified draft positions/s", "cores": 1, "kind": "oracle",
+               "sample": sample + f" ({t_cpu:.1f} s, single-threaded fp64 C oracle, gcc -O2)"}
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} positions/s over {sample}")
+
+    e = 4 if cfg.dtype == "f32" else 2
+    line = {
+        "metric": "verified draft positions/sec and achieved HBM GB/s (% of MI355X peak)",
+        "value": value,
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "P": cfg.P, "N": cfg.N, "K": cfg.K,
+                   "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T, "launch": args.launch,
+                   "input_batches": nb, "status_flags": flags},
+        "roofline": {"bound": "hbm", "kernel": "whole step (all kernels of one library call)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_step": bytes_total / steps,
+                     "bytes_per_element": e},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

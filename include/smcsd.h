@@ -1,0 +1,202 @@
+/*
+ * smcsd.h -- C ABI of the MI355X (gfx950) verify-and-sample library.
+ *
+ * Two operations, each one step of speculative decoding:
+ *
+ *   sd_verify              standard speculative decoding: turn the target and
+ *                          draft logits of B sequences into the number of
+ *                          accepted draft tokens and one final token per
+ *                          sequence.
+ *   smc_reweight_resample  SMC speculative decoding: reweight N particles per
+ *                          prompt by their target/draft ratio, draw each
+ *                          particle's (K+1)-th token, compute the effective
+ *                          sample size and, when it falls below the threshold,
+ *                          resample systematically and permute the particles'
+ *                          KV page-table rows.
+ *
+ * Where the operations are defined (pages by title and section):
+ *   "Faster LLM Inference via Sequential Monte Carlo"
+ *       sec. 1 Das Problem: SD is rejection sampling; the block is dropped
+ *            after the first mismatch.
+ *       sec. 2 Methodik, steps 1-4 and "Vorteil": N particles each draft K
+ *            tokens; the target scores them in one pass; particles are
+ *            reweighted by the target/draft probability ratio; they are
+ *            resampled when the effective sample size falls below a threshold;
+ *            every step yields exactly K+1 tokens per particle.
+ *       sec. 3 Schluesselbeitraege: resampling is a metadata update of a paged
+ *            KV cache (pointer operations, no data movement).
+ *   "PACER: Blockwise Pre-verification for Speculative Decoding with Adaptive
+ *    Length", Methodik 1-3: draft lengths vary per sequence (ragged CSR input).
+ *   "Cross-Family Speculative Decoding for Polish Language Models on Apple
+ *    Silicon", sec. 1: the target verifies k draft tokens in one pass.
+ * The pages print no formulas.  The acceptance min(1, p/q), the residual
+ * max(0, p - q), Kish's effective sample size and systematic resampling are
+ * the standard definitions of the steps the pages name.
+ *
+ * Conventions (all indices 0-based):
+ *   p_j = softmax(z_target[j] / T), q_j = softmax(z_draft[j] / T); the same
+ *   temperature T scales both.  Draft token j is accepted iff u_j < p_j(x_j) /
+ *   q_j(x_j) (strict).  Inverse-CDF draws pick the smallest token id i whose
+ *   inclusive prefix weight exceeds u * (total weight).
+ *
+ * Memory and ordering:
+ *   Every pointer is HIP device memory owned by the caller (for example the
+ *   storage of a torch tensor) unless stated otherwise.  The library never
+ *   allocates, frees or synchronises; it enqueues kernels on `stream` (a
+ *   hipStream_t; NULL is the default stream) and returns.  Outputs are valid
+ *   once the stream reaches that point.  Calls share no global state; two
+ *   calls may run concurrently if they use different workspaces.
+ *   Logits are row-major and contiguous: row r starts at element r * V.
+ *   bf16 logits are raw 16-bit bfloat16 patterns.
+ *
+ * Errors:
+ *   Argument errors are found on the host and returned before anything is
+ *   enqueued.  A launch failure returns SMCSD_ERR_HIP.  Conditions that
+ *   depend on the data are OR-ed as SMCSD_FLAG_* bits into *status_flags
+ *   (device memory, optional, never cleared by the library).  Uniforms must
+ *   lie in [0, 1); this is not checked.
+ */
+#ifndef SMCSD_H
+#define SMCSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMCSD_OK = 0,
+  SMCSD_ERR_INVALID_ARG = 1, /* bad shape, pointer, temperature or aliasing      */
+  SMCSD_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle       */
+  SMCSD_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned      */
+  SMCSD_ERR_HIP = 4          /* the HIP runtime refused a launch                */
+} smcsd_status;
+
+typedef enum { SMCSD_F32 = 0, SMCSD_BF16 = 1 } smcsd_dtype;
+
+/* Bits OR-ed into *status_flags. */
+enum {
+  SMCSD_FLAG_NONFINITE = 1,     /* a row held NaN or +inf, or only -inf; outputs of that
+                                   sequence / prompt are unspecified                   */
+  SMCSD_FLAG_ZERO_RESIDUAL = 2, /* residual mass 0 at the rejected position; the final
+                                   token was drawn from p_n with the same uniform      */
+  SMCSD_FLAG_ZERO_WEIGHTS = 4,  /* every particle of a prompt had log-weight -inf; no
+                                   resampling, ess = 0                                 */
+  SMCSD_FLAG_CDF_CLAMP = 8,     /* rounding left no prefix above u * total; the last
+                                   index with positive weight was taken               */
+  SMCSD_FLAG_BAD_INPUT = 16     /* a draft token outside [0, V) or malformed CSR
+                                   offsets; that sequence's outputs are unspecified   */
+};
+
+#define SMCSD_ABI_VERSION 1
+#define SMCSD_MAX_K 256    /* largest draft length per sequence / particle      */
+#define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
+#define SMCSD_WORKSPACE_ALIGN 256
+
+/* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
+int32_t smcsd_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* smcsd_status_string(int32_t status);
+
+/*
+ * Workspace bytes sd_verify needs for these sizes (0 when B == 0).
+ * total_draft_rows is B*K for fixed K, or offsets[B] for CSR input.
+ */
+size_t sd_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t K, int32_t V,
+                                 int64_t total_draft_rows);
+
+/*
+ * Standard SD verify of B sequences.
+ *
+ *   dtype            SMCSD_F32 or SMCSD_BF16 (both logit tensors).
+ *   B, K, V          sequences, largest draft length, vocabulary size.
+ *                    0 <= K <= SMCSD_MAX_K, V >= 1.
+ *   temperature      T > 0 and finite.
+ *   target_logits    [R_t, V], R_t = total_draft_rows + B.  Sequence b's K_b + 1
+ *                    target rows start at row t0_b = d0_b + b.
+ *   draft_logits     [total_draft_rows, V].  Sequence b's K_b draft rows start at
+ *                    row d0_b.
+ *   draft_tokens     int32 [total_draft_rows], the draft token of each draft row.
+ *   uniforms         fp32 [R_t].  Sequence b uses uniforms[t0_b + j] for the
+ *                    accept test at position j < K_b and uniforms[t0_b + K_b]
+ *                    for its final token.
+ *   draft_offsets    NULL: fixed K, d0_b = b*K, K_b = K.
+ *                    Else int32 [B+1] CSR offsets over draft rows: d0_b =
+ *                    offsets[b], K_b = offsets[b+1] - offsets[b] <= K,
+ *                    offsets[0] = 0, offsets[B] = total_draft_rows.  Malformed
+ *                    offsets set SMCSD_FLAG_BAD_INPUT (checked on the device).
+ *   total_draft_rows B*K when draft_offsets is NULL.
+ *   num_accepted     int32 [B] out: n_b, the number of leading accepted drafts,
+ *                    0 <= n_b <= K_b.
+ *   final_token      int32 [B] out: if n_b < K_b, the residual draw from
+ *                    max(0, p_n - q_n) at the rejected position n = n_b; if
+ *                    n_b = K_b, the bonus draw from p_{K_b}.  The sequence emits
+ *                    its first n_b draft tokens followed by this token.
+ *   status_flags     NULL or device uint32 [1]; SMCSD_FLAG_* bits are OR-ed in.
+ *   workspace        device memory of at least sd_verify_workspace_bytes(),
+ *                    aligned to SMCSD_WORKSPACE_ALIGN; contents need no
+ *                    initialisation and are scratch after the call.
+ *   stream           hipStream_t.
+ */
+int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperature,
+                  const void* target_logits, const void* draft_logits,
+                  const int32_t* draft_tokens, const float* uniforms,
+                  const int32_t* draft_offsets, int64_t total_draft_rows,
+                  int32_t* num_accepted, int32_t* final_token, uint32_t* status_flags,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes smc_reweight_resample needs for these sizes (0 when P*N == 0). */
+size_t smc_workspace_bytes(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V);
+
+/*
+ * One SMC-SD step for P prompts of N particles each.  Particle i = p*N + n owns
+ * target rows i*(K+1) .. i*(K+1)+K and draft rows i*K .. i*K+K-1.
+ *
+ *   dtype, V, temperature   as in sd_verify; 1 <= N <= SMCSD_MAX_N,
+ *                           0 <= K <= SMCSD_MAX_K.
+ *   ess_frac                resample a prompt iff ESS < ess_frac * N; 0 <= ess_frac,
+ *                           finite (0 never resamples).
+ *   target_logits           [P*N*(K+1), V].
+ *   draft_logits            [P*N*K, V].
+ *   draft_tokens            int32 [P*N*K].
+ *   bonus_uniforms          fp32 [P*N]: the uniform of each particle's (K+1)-th
+ *                           token, drawn from p_{i,K}.
+ *   resample_uniforms       fp32 [P]: the systematic-resampling uniform of each
+ *                           prompt.
+ *   log_weights             fp32 [P*N] in/out.  In: the particles' log-weights.
+ *                           Out: 0 for every particle of a prompt that resampled,
+ *                           else logw + sum_{j<K} (log p_ij(x_ij) - log q_ij(x_ij)),
+ *                           accumulated in fp64 and rounded once to fp32.  The
+ *                           (K+1)-th token adds 0: its proposal is the target.
+ *   page_table_in           NULL or int32 [P*N, L] page ids per particle.
+ *   page_table_out          int32 [P*N, L] out (ignored when page_table_in is NULL):
+ *                           row k = row ancestors[k] of the same prompt.  Must not
+ *                           overlap page_table_in.
+ *   pages_per_particle      L >= 0.
+ *   bonus_token             int32 [P*N] out, in particle order before resampling.
+ *   ancestors               int32 [P*N] out: local index (0..N-1) of the particle
+ *                           each slot descends from; the identity when the prompt
+ *                           did not resample.  Sorted ascending per prompt.
+ *   ess                     fp32 [P] out: Kish ESS (sum w)^2 / sum w^2 of the
+ *                           reweighted particles, w = exp(logw' - max logw').
+ *   resampled               int32 [P] out: 1 iff the prompt resampled.
+ *   status_flags, workspace, workspace_bytes, stream   as in sd_verify.
+ */
+int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,
+                              float temperature, float ess_frac, const void* target_logits,
+                              const void* draft_logits, const int32_t* draft_tokens,
+                              const float* bonus_uniforms, const float* resample_uniforms,
+                              float* log_weights, const int32_t* page_table_in,
+                              int32_t* page_table_out, int32_t pages_per_particle,
+                              int32_t* bonus_token, int32_t* ancestors, float* ess,
+                              int32_t* resampled, uint32_t* status_flags, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMCSD_H */

@@ -1,0 +1,223 @@
+"""smc_resampling_amd -- MI355X (gfx950) verify-and-sample step of speculative
+decoding and SMC speculative decoding.
+
+Thin binding over the C ABI in ``include/smcsd.h`` (``libsmcsd.so``): it only
+marshals arguments.  torch tensors provide device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: importing fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "sd_verify", "smc_reweight_resample", "sd_verify_workspace_bytes", "smc_workspace_bytes",
+    "prepare_sd_verify", "prepare_smc_reweight_resample", "status_string", "abi_version", "lib", "SmcsdError",
+    "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "FLAG_ZERO_WEIGHTS", "FLAG_CDF_CLAMP", "FLAG_BAD_INPUT",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsmcsd.so")
+
+SMCSD_OK, SMCSD_ERR_INVALID_ARG, SMCSD_ERR_UNSUPPORTED, SMCSD_ERR_WORKSPACE, SMCSD_ERR_HIP = range(5)
+SMCSD_F32, SMCSD_BF16 = 0, 1
+FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT = 1, 2, 4, 8, 16
+WORKSPACE_ALIGN = 256
+
+_P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "smcsd_abi_version": ([], _I32),
+    "smcsd_status_string": ([_I32], ctypes.c_char_p),
+    "sd_verify_workspace_bytes": ([_I32, _I32, _I32, _I32, _I64], _SZ),
+    "sd_verify": ([_I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
+    "smc_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
+    "smc_reweight_resample": ([_I32, _I32, _I32, _I32, _I32, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
+                               _P, _P, _P, _P, _SZ, _P], _I32),
+}
+
+
+class SmcsdError(RuntimeError):
+    pass
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"smc_resampling_amd: {path} is not built (run __graft_entry__.build()); "
+                          "there is no CPU fallback")
+    L = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    """The raw ctypes handle of libsmcsd.so."""
+    return _lib
+
+
+def abi_version() -> int:
+    return _lib.smcsd_abi_version()
+
+
+def status_string(code: int) -> str:
+    return _lib.smcsd_status_string(code).decode()
+
+
+def _check(code: int):
+    if code != SMCSD_OK:
+        raise SmcsdError(status_string(code))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SMCSD_F32
+    if t.dtype == torch.bfloat16:
+        return SMCSD_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} tensor on a HIP device")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
+    off = (-workspace.data_ptr()) % WORKSPACE_ALIGN
+    view = workspace[off:]
+    return view, view.numel()
+
+
+def sd_verify_workspace_bytes(dtype_code, B, K, V, total_draft_rows) -> int:
+    return _lib.sd_verify_workspace_bytes(dtype_code, B, K, V, total_draft_rows)
+
+
+def smc_workspace_bytes(dtype_code, P, N, K, V) -> int:
+    return _lib.smc_workspace_bytes(dtype_code, P, N, K, V)
+
+
+def prepare_sd_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, *, K=None,
+                      draft_offsets=None, num_accepted=None, final_token=None, status_flags=None, workspace=None,
+                      stream=None):
+    """Validate and marshal one sd_verify call; returns (call, outputs).
+
+    ``call()`` enqueues the step on the stream (current stream by default) and
+    raises on a non-OK status; ``outputs`` holds num_accepted, final_token and
+    status_flags.  Fixed K: target [B*(K+1), V], draft [B*K, V].  Ragged:
+    ``draft_offsets`` int32 [B+1] and ``K`` = largest draft length.
+    """
+    dev = target_logits.device
+    dt = _dtype_code(target_logits)
+    V = target_logits.shape[-1]
+    rows_t = target_logits.shape[0]
+    rows_d = draft_logits.shape[0] if draft_logits is not None else 0
+    B = rows_t - rows_d
+    if draft_offsets is None:
+        K = rows_d // B if B > 0 else (K or 0)
+    elif K is None:
+        K = int(torch.diff(draft_offsets).max().item()) if B > 0 else 0
+    for t, d, n in ((target_logits, target_logits.dtype, "target_logits"), (draft_logits, target_logits.dtype,
+                    "draft_logits"), (draft_tokens, torch.int32, "draft_tokens"), (uniforms, torch.float32,
+                    "uniforms"), (draft_offsets, torch.int32, "draft_offsets")):
+        _need(t, d, n)
+    num_accepted = num_accepted if num_accepted is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    final_token = final_token if final_token is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = sd_verify_workspace_bytes(dt, B, K, V, rows_d)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    st = stream if stream is not None else _stream(dev)
+    args = (dt, B, K, V, float(temperature), _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
+            _ptr(uniforms), _ptr(draft_offsets), rows_d, _ptr(num_accepted), _ptr(final_token), _ptr(status_flags),
+            _ptr(ws), wsb, st)
+    fn = _lib.sd_verify
+    keep = (target_logits, draft_logits, draft_tokens, uniforms, draft_offsets, ws)
+
+    def call():
+        _check(fn(*args))
+        return keep
+
+    return call, dict(num_accepted=num_accepted, final_token=final_token, status_flags=status_flags)
+
+
+def sd_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, **kw):
+    """Standard SD verify; returns (num_accepted, final_token, status_flags)."""
+    call, out = prepare_sd_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, **kw)
+    call()
+    return out["num_accepted"], out["final_token"], out["status_flags"]
+
+
+def prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms,
+                                  log_weights, temperature, ess_frac, P, N, K, *, page_table_in=None,
+                                  page_table_out=None, bonus_token=None, ancestors=None, ess=None, resampled=None,
+                                  status_flags=None, workspace=None, stream=None):
+    """Validate and marshal one SMC step; returns (call, outputs).  ``log_weights``
+    is updated in place when the call runs."""
+    dev = target_logits.device
+    dt = _dtype_code(target_logits)
+    V = target_logits.shape[-1]
+    PN = P * N
+    for t, d, n in ((target_logits, target_logits.dtype, "target_logits"), (draft_logits, target_logits.dtype,
+                    "draft_logits"), (draft_tokens, torch.int32, "draft_tokens"), (bonus_uniforms, torch.float32,
+                    "bonus_uniforms"), (resample_uniforms, torch.float32, "resample_uniforms"),
+                    (log_weights, torch.float32, "log_weights"), (page_table_in, torch.int32, "page_table_in"),
+                    (page_table_out, torch.int32, "page_table_out")):
+        _need(t, d, n)
+    L = 0
+    if page_table_in is not None:
+        L = page_table_in.numel() // max(PN, 1)
+        if page_table_out is None:
+            page_table_out = torch.empty_like(page_table_in)
+    mk = lambda n, d: torch.empty(n, dtype=d, device=dev)  # noqa: E731
+    bonus_token = bonus_token if bonus_token is not None else mk(PN, torch.int32)
+    ancestors = ancestors if ancestors is not None else mk(PN, torch.int32)
+    ess = ess if ess is not None else mk(P, torch.float32)
+    resampled = resampled if resampled is not None else mk(P, torch.int32)
+    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = smc_workspace_bytes(dt, P, N, K, V)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    st = stream if stream is not None else _stream(dev)
+    args = (dt, P, N, K, V, float(temperature), float(ess_frac), _ptr(target_logits), _ptr(draft_logits),
+            _ptr(draft_tokens), _ptr(bonus_uniforms), _ptr(resample_uniforms), _ptr(log_weights), _ptr(page_table_in),
+            _ptr(page_table_out), L, _ptr(bonus_token), _ptr(ancestors), _ptr(ess), _ptr(resampled),
+            _ptr(status_flags), _ptr(ws), wsb, st)
+    fn = _lib.smc_reweight_resample
+    keep = (target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms, log_weights,
+            page_table_in, ws)
+
+    def call():
+        _check(fn(*args))
+        return keep
+
+    return call, dict(bonus_token=bonus_token, ancestors=ancestors, ess=ess, resampled=resampled,
+                      page_table_out=page_table_out, status_flags=status_flags, log_weights=log_weights)
+
+
+def smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms, log_weights,
+                          temperature, ess_frac, P, N, K, **kw):
+    """One SMC-SD step; ``log_weights`` is updated in place.  Returns a dict of outputs."""
+    call, out = prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_uniforms,
+                                              resample_uniforms, log_weights, temperature, ess_frac, P, N, K, **kw)
+    call()
+    return out

@@ -1,0 +1,194 @@
+// api.hip -- C-ABI entry points: argument validation, workspace layout and
+// kernel launches.  No allocation, no synchronisation.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "device.h"
+#include "launch.h"
+#include "smcsd.h"
+
+namespace {
+
+constexpr size_t kAlign = SMCSD_WORKSPACE_ALIGN;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ntiles_of(int64_t V) { return (int)((V + smcsd::TILE - 1) / smcsd::TILE); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// 16-byte vector loads need aligned row starts: aligned bases and V a
+// multiple of the vector width.
+bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
+  const int64_t per = dtype == SMCSD_BF16 ? 8 : 4;
+  return V % per == 0 && aligned16(a) && (b == nullptr || aligned16(b));
+}
+
+struct SdLayout {
+  size_t part, rmass, ws_n, total;
+};
+
+SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
+  const int nt = ntiles_of(V);
+  const int64_t rows_t = rows_d + B;
+  SdLayout l;
+  l.part = 0;
+  l.rmass = align_up(l.part + sizeof(float2) * (size_t)((rows_t + rows_d) * nt));
+  l.ws_n = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
+  l.total = align_up(l.ws_n + sizeof(int32_t) * (size_t)B);
+  return l;
+}
+
+struct SmcLayout {
+  size_t part, ws_logw, total;
+};
+
+SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
+  const int nt = ntiles_of(V);
+  const int64_t PN = (int64_t)P * N;
+  SmcLayout l;
+  l.part = 0;
+  l.ws_logw = align_up(sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
+  l.total = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
+  return l;
+}
+
+bool temperature_ok(float T) { return isfinite(T) && T > 0.0f; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t smcsd_abi_version(void) { return SMCSD_ABI_VERSION; }
+
+const char* smcsd_status_string(int32_t s) {
+  switch (s) {
+    case SMCSD_OK: return "SMCSD_OK";
+    case SMCSD_ERR_INVALID_ARG: return "SMCSD_ERR_INVALID_ARG: bad shape, pointer, temperature or aliasing";
+    case SMCSD_ERR_UNSUPPORTED: return "SMCSD_ERR_UNSUPPORTED: valid but outside what the kernels handle";
+    case SMCSD_ERR_WORKSPACE: return "SMCSD_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case SMCSD_ERR_HIP: return "SMCSD_ERR_HIP: the HIP runtime refused a launch";
+    default: return "SMCSD_UNKNOWN_STATUS";
+  }
+}
+
+size_t sd_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t K, int32_t V,
+                                 int64_t total_draft_rows) {
+  (void)dtype;
+  (void)K;
+  if (B <= 0 || V <= 0 || total_draft_rows < 0) return 0;
+  return sd_layout(B, V, total_draft_rows).total;
+}
+
+int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperature,
+                  const void* target_logits, const void* draft_logits,
+                  const int32_t* draft_tokens, const float* uniforms,
+                  const int32_t* draft_offsets, int64_t total_draft_rows,
+                  int32_t* num_accepted, int32_t* final_token, uint32_t* status_flags,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
+  if (B < 0 || K < 0 || V < 1 || !temperature_ok(temperature)) return SMCSD_ERR_INVALID_ARG;
+  if (K > SMCSD_MAX_K || B > 65535) return SMCSD_ERR_UNSUPPORTED;
+  if (total_draft_rows < 0 || total_draft_rows > (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
+  if (!draft_offsets && total_draft_rows != (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
+  if (B == 0) return SMCSD_OK;
+  if (!target_logits || !uniforms || !num_accepted || !final_token) return SMCSD_ERR_INVALID_ARG;
+  if (total_draft_rows > 0 && (!draft_logits || !draft_tokens)) return SMCSD_ERR_INVALID_ARG;
+  const SdLayout l = sd_layout(B, V, total_draft_rows);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
+    return SMCSD_ERR_WORKSPACE;
+  smcsd::SdArgs a;
+  a.bf16 = dtype == SMCSD_BF16;
+  a.vec = vec_ok(dtype, V, target_logits, draft_logits);
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.rows_d = total_draft_rows;
+  a.rows_t = total_draft_rows + B;
+  a.ntiles = ntiles_of(V);
+  a.c = (float)(1.4426950408889634 / (double)temperature);
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.uniforms = uniforms;
+  a.offsets = draft_offsets;
+  a.num_accepted = num_accepted;
+  a.final_token = final_token;
+  a.flags = status_flags;
+  char* ws = static_cast<char*>(workspace);
+  a.part = reinterpret_cast<float2*>(ws + l.part);
+  a.rmass = reinterpret_cast<float*>(ws + l.rmass);
+  a.ws_n = reinterpret_cast<int32_t*>(ws + l.ws_n);
+  return smcsd::launch_sd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMCSD_OK
+                                                                               : SMCSD_ERR_HIP;
+}
+
+size_t smc_workspace_bytes(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V) {
+  (void)dtype;
+  if (P <= 0 || N <= 0 || K < 0 || V <= 0) return 0;
+  return smc_layout(P, N, K, V).total;
+}
+
+int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,
+                              float temperature, float ess_frac, const void* target_logits,
+                              const void* draft_logits, const int32_t* draft_tokens,
+                              const float* bonus_uniforms, const float* resample_uniforms,
+                              float* log_weights, const int32_t* page_table_in,
+                              int32_t* page_table_out, int32_t pages_per_particle,
+                              int32_t* bonus_token, int32_t* ancestors, float* ess,
+                              int32_t* resampled, uint32_t* status_flags, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
+  if (P < 0 || N < 1 || K < 0 || V < 1 || pages_per_particle < 0) return SMCSD_ERR_INVALID_ARG;
+  if (!temperature_ok(temperature) || !isfinite(ess_frac) || ess_frac < 0.0f)
+    return SMCSD_ERR_INVALID_ARG;
+  if (K > SMCSD_MAX_K || N > SMCSD_MAX_N) return SMCSD_ERR_UNSUPPORTED;
+  if (P == 0) return SMCSD_OK;
+  if (!target_logits || !bonus_uniforms || !resample_uniforms || !log_weights || !bonus_token ||
+      !ancestors || !ess || !resampled)
+    return SMCSD_ERR_INVALID_ARG;
+  if (K > 0 && (!draft_logits || !draft_tokens)) return SMCSD_ERR_INVALID_ARG;
+  const int64_t PN = (int64_t)P * N;
+  if (page_table_in && pages_per_particle > 0) {
+    if (!page_table_out) return SMCSD_ERR_INVALID_ARG;
+    const char* a0 = reinterpret_cast<const char*>(page_table_in);
+    const char* b0 = reinterpret_cast<const char*>(page_table_out);
+    const size_t bytes = sizeof(int32_t) * (size_t)PN * (size_t)pages_per_particle;
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return SMCSD_ERR_INVALID_ARG;
+  }
+  const SmcLayout l = smc_layout(P, N, K, V);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
+    return SMCSD_ERR_WORKSPACE;
+  smcsd::SmcArgs a;
+  a.bf16 = dtype == SMCSD_BF16;
+  a.vec = vec_ok(dtype, V, target_logits, K > 0 ? draft_logits : nullptr);
+  a.P = P;
+  a.N = N;
+  a.K = K;
+  a.L = pages_per_particle;
+  a.V = V;
+  a.ntiles = ntiles_of(V);
+  a.c = (float)(1.4426950408889634 / (double)temperature);
+  a.ess_frac = ess_frac;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.bonus_u = bonus_uniforms;
+  a.resample_u = resample_uniforms;
+  a.logw = log_weights;
+  a.pt_in = page_table_in;
+  a.pt_out = page_table_out;
+  a.bonus_token = bonus_token;
+  a.ancestors = ancestors;
+  a.ess = ess;
+  a.resampled = resampled;
+  a.flags = status_flags;
+  char* ws = static_cast<char*>(workspace);
+  a.part = reinterpret_cast<float2*>(ws + l.part);
+  a.ws_logw = reinterpret_cast<float*>(ws + l.ws_logw);
+  return smcsd::launch_smc(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMCSD_OK
+                                                                                 : SMCSD_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,252 @@
+// device.h -- device building blocks shared by the verify and SMC kernels.
+//
+// A "tile" is TILE = 2048 consecutive logits of one row, processed by one
+// 64-lane wavefront.  Lane l holds 32 values in registers, loaded with 16-byte
+// vector loads: chunk c (0..CHUNKS-1) covers elements
+// [c*64*VEC, (c+1)*64*VEC) of the tile and lane l holds the VEC consecutive
+// elements starting at c*64*VEC + l*VEC (VEC = 8 for bf16, 4 for fp32).
+// Ascending token order inside a tile is therefore (chunk, lane, element).
+//
+// Softmax statistics use base-2 exponentials: with c = log2(e) / T,
+// exp((z - m) / T) = 2^((z - m) * c).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smcsd {
+
+constexpr int WAVE = 64;
+constexpr int BLOCK = 256;  // threads per workgroup (4 wavefronts)
+constexpr int WAVES_PER_BLOCK = BLOCK / WAVE;
+constexpr int TILE = 2048;
+constexpr int PER_LANE = TILE / WAVE;  // 32 values per lane
+
+constexpr uint32_t FLAG_NONFINITE = 1, FLAG_ZERO_RESIDUAL = 2, FLAG_ZERO_WEIGHTS = 4,
+                   FLAG_CDF_CLAMP = 8, FLAG_BAD_INPUT = 16;
+
+struct Bf16 {
+  using raw = uint16_t;
+  static constexpr int VEC = 8;
+  __device__ static float to_f32(raw v) { return __uint_as_float((uint32_t)v << 16); }
+};
+struct F32 {
+  using raw = float;
+  static constexpr int VEC = 4;
+  __device__ static float to_f32(raw v) { return v; }
+};
+
+// ---------------------------------------------------------------------------
+// wavefront reductions (DPP inside 16-lane rows, then the 4 row results)
+// ---------------------------------------------------------------------------
+constexpr int DPP_QUAD_1032 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_ROR4 = 0x124;      // row_ror:4
+constexpr int DPP_ROR8 = 0x128;      // row_ror:8
+
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f32<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f32<DPP_ROR4>(v));
+  v = fmaxf(v, dpp_f32<DPP_ROR8>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+               fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+__device__ inline float wave_sum(float v) {
+  v += dpp_f32<DPP_QUAD_1032>(v);
+  v += dpp_f32<DPP_QUAD_2301>(v);
+  v += dpp_f32<DPP_ROR4>(v);
+  v += dpp_f32<DPP_ROR8>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+__device__ inline double wave_sum_f64(double v) {
+  // fixed butterfly order: deterministic for a given lane assignment
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  return v;
+}
+
+__device__ inline double wave_max_f64(double v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, WAVE));
+  return v;
+}
+
+// inclusive prefix sum over the 64 lanes (ascending lane order)
+__device__ inline float wave_incl_scan(float v, int lane) {
+  for (int off = 1; off < WAVE; off <<= 1) {
+    float o = __shfl_up(v, off, WAVE);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ inline double wave_incl_scan_f64(double v, int lane) {
+  for (int off = 1; off < WAVE; off <<= 1) {
+    double o = __shfl_up(v, off, WAVE);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// tile loads
+// ---------------------------------------------------------------------------
+// Element index (within the tile) of value e of lane `lane`.
+template <typename DT>
+__device__ inline int tile_elem(int lane, int e) {
+  return (e / DT::VEC) * (WAVE * DT::VEC) + lane * DT::VEC + (e % DT::VEC);
+}
+
+// Load tile `tile` of `row` (V logits) into v[]; elements past V read as -inf.
+// VECLOAD requires a 16-byte aligned row base and V % DT::VEC == 0.
+template <typename DT, bool VECLOAD>
+__device__ inline void load_tile(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
+                                 int lane, float (&v)[PER_LANE]) {
+  const int64_t base = tile * TILE;
+  constexpr int CHUNKS = PER_LANE / DT::VEC;
+  if constexpr (VECLOAD) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; c++) {
+      const int64_t off = base + c * (WAVE * DT::VEC) + lane * DT::VEC;
+      if (off < V) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row + off);
+        if constexpr (DT::VEC == 8) {
+          v[c * 8 + 0] = __uint_as_float(w.x << 16);
+          v[c * 8 + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+          v[c * 8 + 2] = __uint_as_float(w.y << 16);
+          v[c * 8 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+          v[c * 8 + 4] = __uint_as_float(w.z << 16);
+          v[c * 8 + 5] = __uint_as_float(w.z & 0xFFFF0000u);
+          v[c * 8 + 6] = __uint_as_float(w.w << 16);
+          v[c * 8 + 7] = __uint_as_float(w.w & 0xFFFF0000u);
+        } else {
+          v[c * 4 + 0] = __uint_as_float(w.x);
+          v[c * 4 + 1] = __uint_as_float(w.y);
+          v[c * 4 + 2] = __uint_as_float(w.z);
+          v[c * 4 + 3] = __uint_as_float(w.w);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < DT::VEC; k++) v[c * DT::VEC + k] = -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER_LANE; e++) {
+      const int64_t off = base + tile_elem<DT>(lane, e);
+      v[e] = off < V ? DT::to_f32(row[off]) : -INFINITY;
+    }
+  }
+}
+
+// Softmax partial of a loaded tile: m = max, s = sum 2^((v - m) * c).
+// An all -inf tile gives (-inf, 0).  NaN or +inf inputs make s NaN.
+__device__ inline float2 tile_partial(const float (&v)[PER_LANE], float c) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < PER_LANE; e++) m = fmaxf(m, v[e]);
+  m = wave_max(m);
+  float s = 0.0f;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int e = 0; e < PER_LANE; e++) s += __builtin_amdgcn_exp2f((v[e] - m) * c);
+  }
+  s = wave_sum(s);
+  return make_float2(m, s);
+}
+
+// ---------------------------------------------------------------------------
+// merge of per-tile partials into row statistics (one wavefront)
+// ---------------------------------------------------------------------------
+struct RowStat {
+  float M;       // max logit of the row
+  double S;      // sum over the row of 2^((z - M) * c)
+  bool ok;       // M finite and S finite and >= 1
+};
+
+__device__ inline RowStat merge_row(const float2* __restrict__ part, int ntiles, float c, int lane) {
+  float m = -INFINITY;
+  for (int t = lane; t < ntiles; t += WAVE) m = fmaxf(m, part[t].x);
+  RowStat r;
+  r.M = wave_max(m);
+  double s = 0.0;
+  if (r.M != -INFINITY) {
+    for (int t = lane; t < ntiles; t += WAVE) {
+      const float2 pt = part[t];
+      if (pt.x != -INFINITY) s += (double)pt.y * exp2(((double)pt.x - (double)r.M) * (double)c);
+    }
+  }
+  r.S = wave_sum_f64(s);
+  r.ok = (r.M > -INFINITY) && (r.M < INFINITY) && (r.S >= 1.0) && (r.S < INFINITY);
+  return r;
+}
+
+// natural-log probability of logit z under a row with statistics rs
+__device__ inline double log_prob(float z, const RowStat& rs, float c) {
+  return ((double)z - (double)rs.M) * (double)c * 0.69314718055994530942 - log(rs.S);
+}
+
+// ---------------------------------------------------------------------------
+// ordered search inside a tile
+// ---------------------------------------------------------------------------
+// Finds the first element (ascending token order) whose inclusive prefix of
+// w[] exceeds `target`.  Returns the element index within the tile, or -1 when
+// the whole tile's prefix stays <= target; *last_pos receives the last element
+// with w > 0 (or -1).  All 64 lanes must call it with the same target.
+template <typename DT>
+__device__ inline int tile_search(const float (&w)[PER_LANE], float target, int lane, int* last_pos) {
+  constexpr int CHUNKS = PER_LANE / DT::VEC;
+  float run = 0.0f;
+  int found = -1;
+  int lastp = -1;
+#pragma unroll
+  for (int c = 0; c < CHUNKS; c++) {
+    float ls = 0.0f;
+#pragma unroll
+    for (int k = 0; k < DT::VEC; k++) ls += w[c * DT::VEC + k];
+    // last positive element of this chunk (largest lane with a positive value)
+    int lp = -1;
+#pragma unroll
+    for (int k = 0; k < DT::VEC; k++)
+      if (w[c * DT::VEC + k] > 0.0f) lp = tile_elem<DT>(lane, c * DT::VEC + k);
+    for (int off = 32; off >= 1; off >>= 1) lp = max(lp, __shfl_xor(lp, off, WAVE));
+    if (lp >= 0) lastp = lp;
+    if (found < 0) {
+      const float incl = wave_incl_scan(ls, lane);
+      const float excl = incl - ls;
+      const bool cross = run + incl > target;
+      const uint64_t bal = __ballot(cross);
+      if (bal) {
+        const int src = __builtin_ctzll(bal);
+        int idx = -1;
+        if (lane == src) {
+          float acc = run + excl;
+#pragma unroll
+          for (int k = 0; k < DT::VEC; k++) {
+            acc += w[c * DT::VEC + k];
+            if (idx < 0 && acc > target) idx = tile_elem<DT>(lane, c * DT::VEC + k);
+          }
+          if (idx < 0) {  // rounding between the two sums: take the lane's last positive
+            for (int k = DT::VEC - 1; k >= 0 && idx < 0; k--)
+              if (w[c * DT::VEC + k] > 0.0f) idx = tile_elem<DT>(lane, c * DT::VEC + k);
+          }
+        }
+        found = __shfl(idx, src, WAVE);
+      }
+      if (found < 0) run += readlane_f32(incl, WAVE - 1);
+    }
+  }
+  *last_pos = lastp;
+  return found;
+}
+
+}  // namespace smcsd

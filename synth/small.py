@@ -1,0 +1,72 @@
+"""Small seeded synthetic cases built on the host with numpy (edge-case shapes).
+
+Same recipe as the GPU generator: z_t = scale * N(0,1) (+ optional rank prior),
+z_d = z_t + delta * N(0,1), rounded once to the stored dtype; draft tokens are
+Gumbel-max draws from softmax(z_d / T); uniforms are U[0,1) in fp32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (NaN kept NaN)."""
+    b = np.asarray(x32, np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x32, np.float32))
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = 0x7FC0
+    return r
+
+
+def gumbel_tokens(rng, z_draft_f64: np.ndarray, T: float) -> np.ndarray:
+    g = -np.log(-np.log(rng.random(z_draft_f64.shape).clip(1e-300, 1.0 - 1e-16)))
+    return np.argmax(z_draft_f64 / T + g, axis=-1).astype(np.int32)
+
+
+def stored(z32: np.ndarray, dtype: str):
+    """(array passed to the library/oracle, float64 view of the stored values)."""
+    if dtype == "bf16":
+        bits = to_bf16_bits(z32)
+        return bits, (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    z = np.asarray(z32, np.float32)
+    return z, z.astype(np.float64)
+
+
+def sd_case(seed, B, V, T=1.0, K=None, lengths=None, delta=1.0, dtype="f32", scale=3.0, prior=True):
+    """Fixed-K (``K``) or ragged (``lengths``) SD inputs as numpy arrays."""
+    rng = np.random.default_rng(seed)
+    Kb = np.full(B, K, np.int32) if lengths is None else np.asarray(lengths, np.int32)
+    d0 = np.concatenate([[0], np.cumsum(Kb)]).astype(np.int64)
+    rows_d = int(d0[-1])
+    rows_t = rows_d + B
+    base = -0.5 * np.log1p(rng.permutation(V)) if prior else np.zeros(V)
+    zt = (scale * rng.standard_normal((rows_t, V)) + base).astype(np.float32)
+    zd = np.zeros((rows_d, V), np.float32)
+    dl = np.broadcast_to(np.asarray(delta, np.float64), (B,))
+    for b in range(B):
+        t0 = int(d0[b]) + b
+        for j in range(int(Kb[b])):
+            zd[d0[b] + j] = (zt[t0 + j] + dl[b] * rng.standard_normal(V)).astype(np.float32)
+    tgt, _ = stored(zt, dtype)
+    drf, drf64 = stored(zd, dtype)
+    tok = gumbel_tokens(rng, drf64, T) if rows_d else np.zeros(0, np.int32)
+    u = rng.random(rows_t).astype(np.float32)
+    offsets = None if lengths is None else d0.astype(np.int32)
+    return dict(target=tgt, draft=drf, tokens=tok, uniforms=u, offsets=offsets, K=int(Kb.max()) if B else 0,
+                Kb=Kb, T=T, dtype=dtype)
+
+
+def smc_case(seed, P, N, K, V, T=1.0, delta=1.0, dtype="f32", scale=3.0, L=4, logw_scale=1.0):
+    rng = np.random.default_rng(seed)
+    PN = P * N
+    base = -0.5 * np.log1p(rng.permutation(V))
+    zt = (scale * rng.standard_normal((PN * (K + 1), V)) + base).astype(np.float32)
+    zd = (zt.reshape(PN, K + 1, V)[:, :K] + delta * rng.standard_normal((PN, K, V))).astype(np.float32)
+    zd = zd.reshape(PN * K, V)
+    tgt, _ = stored(zt, dtype)
+    drf, drf64 = stored(zd, dtype)
+    tok = gumbel_tokens(rng, drf64, T) if PN * K else np.zeros(0, np.int32)
+    return dict(target=tgt, draft=drf, tokens=tok, bonus_u=rng.random(PN).astype(np.float32),
+                resample_u=rng.random(P).astype(np.float32),
+                logw=(logw_scale * rng.standard_normal(PN)).astype(np.float32),
+                pt=np.arange(PN * L, dtype=np.int32).reshape(PN, L), P=P, N=N, K=K, T=T, dtype=dtype)

@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every function include/smcsd.h declares,
+and rejects bad arguments on the host before anything is launched (CPU only:
+no call here reaches a kernel launch)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smcsd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def s():
+    import smc_resampling_amd
+
+    return smc_resampling_amd
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("sd_verify", "smc_reweight_resample", "sd_verify_workspace_bytes", "smc_workspace_bytes",
+              "smcsd_status_string", "smcsd_abi_version"):
+        assert n in names, names
+
+
+def test_every_declared_symbol_is_exported(s):
+    L = ctypes.CDLL(s.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), f"{n} declared in smcsd.h but not exported"
+
+
+def test_abi_version_and_status_strings(s):
+    ver = int(re.search(r"#define SMCSD_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert s.abi_version() == ver
+    assert s.status_string(0) == "SMCSD_OK"
+    for code in range(1, 5):
+        assert s.status_string(code).startswith("SMCSD_ERR_")
+    assert s.status_string(99) == "SMCSD_UNKNOWN_STATUS"
+
+
+def test_workspace_sizes(s):
+    assert s.sd_verify_workspace_bytes(1, 0, 4, 32768, 0) == 0
+    a = s.sd_verify_workspace_bytes(1, 64, 4, 32768, 256)
+    b = s.sd_verify_workspace_bytes(1, 64, 4, 151936, 256)
+    assert a > 0 and b > a and a % 256 == 0
+    assert s.smc_workspace_bytes(1, 0, 16, 4, 100) == 0
+    c = s.smc_workspace_bytes(1, 32, 64, 8, 151936)
+    assert c % 256 == 0 and c >= 32 * 64 * 17 * 75 * 8
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _sd(s, **kw):
+    a = dict(dtype=1, B=4, K=2, V=1000, T=1.0, tgt=FAKE, drf=FAKE, tok=FAKE, u=FAKE, off=None, rows_d=8, na=FAKE,
+             ft=FAKE, fl=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return s.lib().sd_verify(a["dtype"], a["B"], a["K"], a["V"], a["T"], a["tgt"], a["drf"], a["tok"], a["u"],
+                             a["off"], a["rows_d"], a["na"], a["ft"], a["fl"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), 1), (dict(T=0.0), 1), (dict(T=-1.0), 1), (dict(T=math.nan), 1), (dict(T=math.inf), 1),
+    (dict(V=0), 1), (dict(B=-1), 1), (dict(K=-1), 1), (dict(K=300, rows_d=1200), 2), (dict(rows_d=7), 1),
+    (dict(rows_d=9), 1), (dict(tgt=None), 1), (dict(u=None), 1), (dict(drf=None), 1), (dict(na=None), 1),
+    (dict(ws=None), 3), (dict(wsb=16), 3), (dict(ws=FAKE + 8), 3), (dict(off=FAKE, rows_d=9), 1),
+    (dict(B=0, rows_d=0, tgt=None, drf=None), 0)])
+def test_sd_verify_host_validation(s, kw, code):
+    assert _sd(s, **kw) == code
+
+
+def _smc(s, **kw):
+    a = dict(dtype=1, P=2, N=8, K=2, V=1000, T=1.0, ess=0.5, tgt=FAKE, drf=FAKE, tok=FAKE, ub=FAKE, ur=FAKE,
+             lw=FAKE, pti=None, pto=None, L=0, bt=FAKE, anc=FAKE, es=FAKE, rs=FAKE, fl=None, ws=FAKE,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return s.lib().smc_reweight_resample(a["dtype"], a["P"], a["N"], a["K"], a["V"], a["T"], a["ess"], a["tgt"],
+                                         a["drf"], a["tok"], a["ub"], a["ur"], a["lw"], a["pti"], a["pto"], a["L"],
+                                         a["bt"], a["anc"], a["es"], a["rs"], a["fl"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), 1), (dict(N=0), 1), (dict(P=-1), 1), (dict(T=0.0), 1), (dict(ess=-0.1), 1),
+    (dict(ess=math.nan), 1), (dict(N=2000), 2), (dict(K=257), 2), (dict(lw=None), 1), (dict(ur=None), 1),
+    (dict(pti=FAKE, pto=FAKE + 64, L=4), 1), (dict(pti=FAKE, pto=None, L=4), 1), (dict(ws=None), 3),
+    (dict(wsb=100), 3), (dict(P=0, tgt=None), 0), (dict(L=-1), 1)])
+def test_smc_host_validation(s, kw, code):
+    assert _smc(s, **kw) == code

@@ -1,0 +1,115 @@
+"""sd_verify on the GPU against the oracle (element by element, decision band)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+from synth.small import sd_case  # noqa: E402
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,K,B,T", [
+    (1, 2, 3, 1.0), (2, 1, 5, 1.0), (7, 3, 4, 0.7), (9, 2, 6, 1.3), (1000, 4, 8, 1.0), (2048, 1, 3, 0.7),
+    (2049, 3, 5, 1.0), (4097, 0, 4, 1.0), (6000, 8, 3, 0.9), (32768, 4, 2, 0.7)])
+def test_sd_shapes(dtype, V, K, B, T):
+    from gpu_util import check_sd
+
+    for delta in (0.5, 2.0):
+        check_sd(sd_case(V * 31 + K * 7 + B, B, V, T=T, K=K, delta=delta, dtype=dtype), f"V={V} K={K} B={B} d={delta}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sd_ragged(dtype):
+    from gpu_util import check_sd
+
+    lengths = [0, 4, 1, 16, 0, 7, 3, 12, 8, 0, 2, 5]
+    check_sd(sd_case(5, len(lengths), 3000, T=0.8, lengths=lengths, delta=1.5, dtype=dtype), "ragged")
+    check_sd(sd_case(6, 3, 40, T=1.0, lengths=[0, 0, 0], dtype=dtype), "all-zero lengths")
+
+
+def test_sd_identical_rows_accept_all():
+    """draft == target: every draft accepted, final token is the bonus draw."""
+    from gpu_util import check_sd, run_sd_gpu
+
+    c = sd_case(9, 16, 5000, T=1.0, K=4, delta=0.0, dtype="bf16")
+    na, _, _ = run_sd_gpu(c)
+    assert (na == 4).all()
+    check_sd(c, "delta=0")
+
+
+def test_sd_uniform_and_masked_rows():
+    from gpu_util import check_sd
+
+    c = sd_case(10, 4, 4096, K=3, delta=1.0, dtype="f32", scale=0.0, prior=False)  # constant rows
+    check_sd(c, "constant rows")
+    c = sd_case(11, 4, 4096, K=3, delta=1.0, dtype="f32")
+    c["target"][:, ::3] = -np.inf  # masked tokens in the target only
+    check_sd(c, "masked")
+
+
+def test_sd_empty_batch():
+    import torch
+
+    import smc_resampling_amd as s
+
+    t = torch.empty((0, 100), dtype=torch.float32, device="cuda")
+    na, ft, fl = s.sd_verify(t, t, torch.empty(0, dtype=torch.int32, device="cuda"),
+                             torch.empty(0, dtype=torch.float32, device="cuda"), 1.0, K=2)
+    assert na.numel() == 0 and ft.numel() == 0 and int(fl.item()) == 0
+
+
+def test_sd_flags_nonfinite_and_bad_input():
+    from gpu_util import run_sd_gpu
+
+    c = sd_case(12, 3, 500, K=2, dtype="f32")
+    c["target"][1, 7] = np.nan
+    _, _, fl = run_sd_gpu(c)
+    assert fl & 1
+    c = sd_case(13, 3, 500, K=2, dtype="f32")
+    c["tokens"][2] = 500
+    _, _, fl = run_sd_gpu(c)
+    assert fl & 16
+    c = sd_case(14, 3, 500, lengths=[1, 2, 1], dtype="f32")
+    c["offsets"] = np.array([0, 2, 1, 4], np.int32)  # not monotone
+    na, _, fl = run_sd_gpu(c)
+    assert fl & 16
+
+
+def test_sd_deterministic():
+    from gpu_util import run_sd_gpu
+
+    c = sd_case(15, 32, 32768, K=4, T=0.7, delta=1.0, dtype="bf16")
+    a = run_sd_gpu(c)
+    b = run_sd_gpu(c)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+
+
+def _config_steps(idx, steps):
+    from gpu_util import check_sd, host_logits, say
+
+    import synth
+    from compare import Tally
+
+    cfg = synth.CONFIGS[idx]
+    gen = synth.Generator(cfg)
+    total = Tally()
+    for s in steps:
+        st = gen.sd_step(s)
+        case = dict(target=host_logits(st["target"]), draft=host_logits(st["draft"]),
+                    tokens=st["tokens"].cpu().numpy(), uniforms=st["uniforms"].cpu().numpy(),
+                    offsets=None if st["offsets"] is None else st["offsets"].cpu().numpy(), K=st["K"], T=cfg.T)
+        total.merge(check_sd(case, f"{cfg.name} step {s}"))
+    say(f"[{cfg.name}] total {total.summary()}")
+    total.assert_ok()
+
+
+def test_cfg0_all_steps():
+    _config_steps(0, range(64))
+
+
+def test_cfg1_full_size():
+    _config_steps(1, range(6))
+
+
+def test_cfg4_ragged_full_size():
+    _config_steps(4, range(2))

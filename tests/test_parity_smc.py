@@ -1,0 +1,110 @@
+"""smc_reweight_resample on the GPU against the oracle, in lockstep."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+from synth.small import smc_case  # noqa: E402
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,N,K,V,T,L", [
+    (1, 1, 2, 50, 1.0, 3), (2, 4, 1, 7, 1.0, 2), (1, 16, 4, 4096, 1.0, 8), (3, 64, 2, 2049, 0.8, 5),
+    (2, 5, 0, 1000, 1.0, 4), (1, 100, 3, 300, 1.2, 0)])
+def test_smc_shapes(dtype, P, N, K, V, T, L):
+    from gpu_util import check_smc_steps
+
+    c = smc_case(P * 1000 + N * 10 + K, P, N, K, V, T=T, dtype=dtype, L=L, logw_scale=2.0)
+    if L == 0:
+        c["pt"] = None
+    check_smc_steps(c, steps=1, label=f"P={P} N={N} K={K} V={V}")
+    check_smc_steps(c, steps=1, ess_frac=2.0, label="always resample")
+    check_smc_steps(c, steps=1, ess_frac=0.0, label="never resample")
+
+
+def test_smc_max_particles():
+    from gpu_util import check_smc_steps
+
+    c = smc_case(77, 1, 1024, 1, 64, dtype="bf16", L=2, logw_scale=3.0)
+    check_smc_steps(c, steps=1, ess_frac=2.0, label="N=1024")
+
+
+def test_smc_zero_weights_flag():
+    from gpu_util import run_smc_gpu
+
+    c = smc_case(78, 2, 8, 1, 100, dtype="f32", L=2)
+    logw = np.full(16, -np.inf, np.float32)
+    g = run_smc_gpu(c, logw, c["pt"])
+    assert g["flags"] & 4
+    assert (g["resampled"] == 0).all() and (g["ess"] == 0).all()
+    assert (g["ancestors"] == np.tile(np.arange(8), 2)).all()
+
+
+def test_smc_multi_step_lockstep():
+    from gpu_util import check_smc_steps
+
+    def fresh(s, case):
+        n = smc_case(500 + s, case["P"], case["N"], case["K"], 3000, dtype="bf16", L=4)
+        return n
+
+    c = smc_case(500, 2, 16, 4, 3000, dtype="bf16", L=4)
+    check_smc_steps(c, steps=6, label="6 steps", new_inputs=fresh)
+
+
+def _cfg_smc(idx, steps, prompts=None):
+    """Full-size config; the oracle checks `prompts` (all when None) in lockstep."""
+    import torch
+
+    import oracle
+    import smc_resampling_amd as s
+    import synth
+    from compare import Tally, compare_smc
+    from gpu_util import host_logits, say
+
+    cfg = synth.CONFIGS[idx]
+    gen = synth.Generator(cfg)
+    P, N, K = cfg.P, cfg.N, cfg.K
+    prompts = list(range(P)) if prompts is None else prompts
+    logw = torch.zeros(P * N, dtype=torch.float32, device="cuda")
+    pt = torch.from_numpy(synth.initial_page_table(P, N, cfg.L)).cuda()
+    total = Tally()
+    for step in steps:
+        st = gen.smc_step(step)
+        lw_in = logw.cpu().numpy()
+        pt_in = pt.cpu().numpy()
+        out = s.smc_reweight_resample(st["target"], st["draft"], st["tokens"], st["bonus_u"], st["resample_u"], logw,
+                                      cfg.T, cfg.ess_frac, P, N, K, page_table_in=pt)
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy() for k, v in out.items() if k != "log_weights"}
+        g["logw"] = logw.cpu().numpy()
+        assert int(out["status_flags"].item()) & ~8 == 0
+        # invariants on every prompt
+        anc = g["ancestors"].reshape(P, N)
+        assert (np.diff(anc, axis=1) >= 0).all()
+        assert (g["page_table_out"] == pt_in[(np.arange(P)[:, None] * N + anc).ravel()]).all()
+        for p in prompts:
+            rows_t = slice(p * N * (K + 1), (p + 1) * N * (K + 1))
+            rows_d = slice(p * N * K, (p + 1) * N * K)
+            case = dict(target=host_logits(st["target"][rows_t]), draft=host_logits(st["draft"][rows_d]),
+                        tokens=st["tokens"][rows_d].cpu().numpy(), bonus_u=st["bonus_u"][p * N:(p + 1) * N].cpu().numpy(),
+                        resample_u=st["resample_u"][p:p + 1].cpu().numpy(), P=1, N=N, K=K, T=cfg.T)
+            sl = slice(p * N, (p + 1) * N)
+            ref = oracle.smc_step(case["target"], case["draft"], case["tokens"], case["bonus_u"], case["resample_u"],
+                                  lw_in[sl], cfg.T, cfg.ess_frac, 1, N, K, pt_in=pt_in[sl])
+            gp = dict(bonus=g["bonus_token"][sl], ancestors=g["ancestors"][sl], ess=g["ess"][p:p + 1],
+                      resampled=g["resampled"][p:p + 1], logw=g["logw"][sl], pt_out=g["page_table_out"][sl])
+            t = compare_smc(case, ref, gp, lw_in[sl], pt_in[sl], f"{cfg.name} step {step} prompt {p}")
+            total.merge(t)
+            t.assert_ok()
+        say(f"[{cfg.name} step {step}] resampled {int(g['resampled'].sum())}/{P} ess[0]={g['ess'][0]:.3f} "
+            f"{total.summary()}")
+        pt = out["page_table_out"]
+    total.assert_ok()
+
+
+def test_cfg2_full_size():
+    _cfg_smc(2, range(8))
+
+
+def test_cfg3_full_size_sampled_prompts():
+    _cfg_smc(3, range(1), prompts=[0, 1, 31])
