@@ -83,7 +83,7 @@ def main():
             logw = torch.zeros(P * N, dtype=torch.float32, device=dev)
             pts = [torch.from_numpy(synth.initial_page_table(P, N, cfg.L)).to(dev), None]
             pts[1] = torch.empty_like(pts[0])
-            ws = torch.empty(smcsd.smc_workspace_bytes(1, P, N, K, cfg.V) + 256, dtype=torch.uint8, device=dev)
+            ws = smcsd.new_workspace(smcsd.smc_workspace_bytes(1, P, N, K, cfg.V), dev)
             outs = None
             for s in range(steps + W):
                 bt = batches[s % nb]
@@ -97,8 +97,7 @@ def main():
                 calls.append(call)
         else:
             rows_d = max(int(bt["total_draft_rows"]) for bt in batches)
-            ws = torch.empty(smcsd.sd_verify_workspace_bytes(1, cfg.B, cfg.K, cfg.V, rows_d) + 256, dtype=torch.uint8,
-                             device=dev)
+            ws = smcsd.new_workspace(smcsd.sd_verify_workspace_bytes(1, cfg.B, cfg.K, cfg.V, rows_d), dev)
             outs = None
             for s in range(steps + W):
                 bt = batches[s % nb]
@@ -214,7 +213,7 @@ def main():
         "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "P": cfg.P, "N": cfg.N, "K": cfg.K,
                    "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T, "launch": args.launch,
                    "input_batches": nb, "status_flags": flags},
-        "roofline": {"bound": "hbm", "kernel": "whole step (all kernels of one library call)",
+        "roofline": {"bound": "hbm", "kernel": "k_sd_fused" if cfg.kind != "smc" else "k_smc_fused",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes_per_step": bytes_total / steps,
                      "bytes_per_element": e},

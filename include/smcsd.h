@@ -42,12 +42,24 @@
  * Memory and ordering:
  *   Every pointer is HIP device memory owned by the caller (for example the
  *   storage of a torch tensor) unless stated otherwise.  The library never
- *   allocates, frees or synchronises; it enqueues kernels on `stream` (a
- *   hipStream_t; NULL is the default stream) and returns.  Outputs are valid
- *   once the stream reaches that point.  Calls share no global state; two
- *   calls may run concurrently if they use different workspaces.
- *   Logits are row-major and contiguous: row r starts at element r * V.
- *   bf16 logits are raw 16-bit bfloat16 patterns.
+ *   allocates, frees or synchronises; each call enqueues one kernel on
+ *   `stream` (a hipStream_t; NULL is the default stream) and returns.
+ *   Outputs are valid once the stream reaches that point.
+ *   The kernel is persistent: its grid is sized to what the device holds at
+ *   once and its workgroups hand work to each other through counters in the
+ *   workspace, with bounded waits.  Run one call at a time per device (other
+ *   work on the device may delay it; a wait that gives up sets
+ *   SMCSD_FLAG_SPIN_TIMEOUT).  Calls on one workspace must not overlap.
+ *
+ * Workspace:
+ *   Caller-owned device scratch of at least the size the *_workspace_bytes()
+ *   query returns, aligned to SMCSD_WORKSPACE_ALIGN.  It must be zero-filled
+ *   once before its first use; every call leaves its counters at zero again.
+ *   After a call that raised SMCSD_FLAG_BAD_INPUT or SMCSD_FLAG_SPIN_TIMEOUT,
+ *   zero-fill it again before reuse.
+ *
+ * Logits are row-major and contiguous: row r starts at element r * V.  bf16
+ * logits are raw 16-bit bfloat16 patterns.
  *
  * Errors:
  *   Argument errors are found on the host and returned before anything is
@@ -86,12 +98,14 @@ enum {
                                    resampling, ess = 0                                 */
   SMCSD_FLAG_CDF_CLAMP = 8,     /* rounding left no prefix above u * total; the last
                                    index with positive weight was taken               */
-  SMCSD_FLAG_BAD_INPUT = 16     /* a draft token outside [0, V) or malformed CSR
+  SMCSD_FLAG_BAD_INPUT = 16,    /* a draft token outside [0, V) or malformed CSR
                                    offsets; that sequence's outputs are unspecified   */
+  SMCSD_FLAG_SPIN_TIMEOUT = 32  /* a bounded in-kernel wait gave up (the launch did not
+                                   get the whole device); outputs are unspecified     */
 };
 
 #define SMCSD_ABI_VERSION 1
-#define SMCSD_MAX_K 256    /* largest draft length per sequence / particle      */
+#define SMCSD_MAX_K 128    /* largest draft length per sequence / particle      */
 #define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
 #define SMCSD_WORKSPACE_ALIGN 256
 
@@ -137,8 +151,8 @@ size_t sd_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t K, int32_t V,
  *                    its first n_b draft tokens followed by this token.
  *   status_flags     NULL or device uint32 [1]; SMCSD_FLAG_* bits are OR-ed in.
  *   workspace        device memory of at least sd_verify_workspace_bytes(),
- *                    aligned to SMCSD_WORKSPACE_ALIGN; contents need no
- *                    initialisation and are scratch after the call.
+ *                    aligned to SMCSD_WORKSPACE_ALIGN, zero-filled before its
+ *                    first use (see Workspace above).
  *   stream           hipStream_t.
  */
 int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperature,

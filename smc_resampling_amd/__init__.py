@@ -17,6 +17,7 @@ __all__ = [
     "sd_verify", "smc_reweight_resample", "sd_verify_workspace_bytes", "smc_workspace_bytes",
     "prepare_sd_verify", "prepare_smc_reweight_resample", "status_string", "abi_version", "lib", "SmcsdError",
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "FLAG_ZERO_WEIGHTS", "FLAG_CDF_CLAMP", "FLAG_BAD_INPUT",
+    "FLAG_SPIN_TIMEOUT", "new_workspace",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,7 +25,7 @@ LIB_PATH = os.path.join(HERE, "libsmcsd.so")
 
 SMCSD_OK, SMCSD_ERR_INVALID_ARG, SMCSD_ERR_UNSUPPORTED, SMCSD_ERR_WORKSPACE, SMCSD_ERR_HIP = range(5)
 SMCSD_F32, SMCSD_BF16 = 0, 1
-FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT = 1, 2, 4, 8, 16
+FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT, FLAG_SPIN_TIMEOUT = 1, 2, 4, 8, 16, 32
 WORKSPACE_ALIGN = 256
 
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -103,8 +104,8 @@ def _stream(device):
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
-    if workspace is None:
-        workspace = torch.empty(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
+    if workspace is None:  # zero-filled once: the kernels keep their counters at zero between calls
+        workspace = torch.zeros(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
     off = (-workspace.data_ptr()) % WORKSPACE_ALIGN
     view = workspace[off:]
     return view, view.numel()
@@ -116,6 +117,15 @@ def sd_verify_workspace_bytes(dtype_code, B, K, V, total_draft_rows) -> int:
 
 def smc_workspace_bytes(dtype_code, P, N, K, V) -> int:
     return _lib.smc_workspace_bytes(dtype_code, P, N, K, V)
+
+
+def new_workspace(nbytes, device):
+    """A zero-filled workspace of at least ``nbytes`` (plus alignment slack).
+
+    Reuse it across calls of the same or smaller size; calls on one workspace
+    must not overlap.  Zero it again after a call that raised FLAG_BAD_INPUT or
+    FLAG_SPIN_TIMEOUT."""
+    return torch.zeros(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
 
 
 def prepare_sd_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, *, K=None,

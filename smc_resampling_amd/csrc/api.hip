@@ -25,32 +25,38 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
   return V % per == 0 && aligned16(a) && (b == nullptr || aligned16(b));
 }
 
+// Workspace layouts.  The counters come first so that one zero-fill of the
+// start of the workspace (or of all of it) prepares it.
 struct SdLayout {
-  size_t part, rmass, ws_n, total;
+  size_t gcount, dec, rcount, rec, rmass, part, total;
 };
 
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
-  const int64_t rows_t = rows_d + B;
   SdLayout l;
-  l.part = 0;
-  l.rmass = align_up(l.part + sizeof(float2) * (size_t)((rows_t + rows_d) * nt));
-  l.ws_n = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
-  l.total = align_up(l.ws_n + sizeof(int32_t) * (size_t)B);
+  l.gcount = 0;
+  l.dec = align_up(l.gcount + sizeof(uint32_t) * (size_t)B);
+  l.rcount = align_up(l.dec + sizeof(uint32_t) * (size_t)B);
+  l.rec = align_up(l.rcount + sizeof(uint32_t) * (size_t)B);
+  l.rmass = align_up(l.rec + 24 * (size_t)B);
+  l.part = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
+  l.total = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
   return l;
 }
 
 struct SmcLayout {
-  size_t part, ws_logw, total;
+  size_t gcount, pcount, ws_logw, part, total;
 };
 
 SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   const int nt = ntiles_of(V);
   const int64_t PN = (int64_t)P * N;
   SmcLayout l;
-  l.part = 0;
-  l.ws_logw = align_up(sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
-  l.total = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
+  l.gcount = 0;
+  l.pcount = align_up(sizeof(uint32_t) * (size_t)PN);
+  l.ws_logw = align_up(l.pcount + sizeof(uint32_t) * (size_t)P);
+  l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
+  l.total = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
   return l;
 }
 
@@ -98,30 +104,34 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   const SdLayout l = sd_layout(B, V, total_draft_rows);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
-  smcsd::SdArgs a;
-  a.bf16 = dtype == SMCSD_BF16;
-  a.vec = vec_ok(dtype, V, target_logits, draft_logits);
-  a.B = B;
-  a.K = K;
-  a.V = V;
-  a.rows_d = total_draft_rows;
-  a.rows_t = total_draft_rows + B;
-  a.ntiles = ntiles_of(V);
-  a.c = (float)(1.4426950408889634 / (double)temperature);
-  a.target = target_logits;
-  a.draft = draft_logits;
+  char* ws = static_cast<char*>(workspace);
+  smcsd::SdFusedArgs a;
+  a.s.target = target_logits;
+  a.s.draft = draft_logits;
+  a.s.offsets = draft_offsets;
+  a.s.ngroups = B;
+  a.s.rows_d = total_draft_rows;
+  a.s.rows_t = total_draft_rows + B;
+  a.s.V = V;
+  a.s.K = K;
+  a.s.ntiles = ntiles_of(V);
+  a.s.total_tiles = (2 * total_draft_rows + B) * (int64_t)a.s.ntiles;
+  a.s.c = (float)(1.4426950408889634 / (double)temperature);
+  a.s.part = reinterpret_cast<float2*>(ws + l.part);
+  a.s.gcount = reinterpret_cast<uint32_t*>(ws + l.gcount);
+  a.s.flags = status_flags;
   a.tokens = draft_tokens;
   a.uniforms = uniforms;
-  a.offsets = draft_offsets;
+  a.dec = reinterpret_cast<uint32_t*>(ws + l.dec);
+  a.rcount = reinterpret_cast<uint32_t*>(ws + l.rcount);
+  a.rec = ws + l.rec;
+  a.rmass = reinterpret_cast<float*>(ws + l.rmass);
   a.num_accepted = num_accepted;
   a.final_token = final_token;
-  a.flags = status_flags;
-  char* ws = static_cast<char*>(workspace);
-  a.part = reinterpret_cast<float2*>(ws + l.part);
-  a.rmass = reinterpret_cast<float*>(ws + l.rmass);
-  a.ws_n = reinterpret_cast<int32_t*>(ws + l.ws_n);
-  return smcsd::launch_sd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMCSD_OK
-                                                                               : SMCSD_ERR_HIP;
+  const bool vec = vec_ok(dtype, V, target_logits, draft_logits);
+  return smcsd::launch_sd(a, dtype == SMCSD_BF16, vec, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SMCSD_OK
+             : SMCSD_ERR_HIP;
 }
 
 size_t smc_workspace_bytes(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V) {
@@ -160,35 +170,42 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   const SmcLayout l = smc_layout(P, N, K, V);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
-  smcsd::SmcArgs a;
-  a.bf16 = dtype == SMCSD_BF16;
-  a.vec = vec_ok(dtype, V, target_logits, K > 0 ? draft_logits : nullptr);
-  a.P = P;
+  char* ws = static_cast<char*>(workspace);
+  smcsd::SmcFusedArgs a;
+  a.s.target = target_logits;
+  a.s.draft = draft_logits;
+  a.s.offsets = nullptr;
+  a.s.ngroups = PN;
+  a.s.rows_d = PN * K;
+  a.s.rows_t = PN * (K + 1);
+  a.s.V = V;
+  a.s.K = K;
+  a.s.ntiles = ntiles_of(V);
+  a.s.total_tiles = PN * (2 * K + 1) * (int64_t)a.s.ntiles;
+  a.s.c = (float)(1.4426950408889634 / (double)temperature);
+  a.s.part = reinterpret_cast<float2*>(ws + l.part);
+  a.s.gcount = reinterpret_cast<uint32_t*>(ws + l.gcount);
+  a.s.flags = status_flags;
   a.N = N;
-  a.K = K;
   a.L = pages_per_particle;
-  a.V = V;
-  a.ntiles = ntiles_of(V);
-  a.c = (float)(1.4426950408889634 / (double)temperature);
   a.ess_frac = ess_frac;
-  a.target = target_logits;
-  a.draft = draft_logits;
   a.tokens = draft_tokens;
   a.bonus_u = bonus_uniforms;
   a.resample_u = resample_uniforms;
-  a.logw = log_weights;
+  a.logw_in = log_weights;
+  a.logw_out = log_weights;
+  a.ws_logw = reinterpret_cast<float*>(ws + l.ws_logw);
+  a.pcount = reinterpret_cast<uint32_t*>(ws + l.pcount);
   a.pt_in = page_table_in;
   a.pt_out = page_table_out;
   a.bonus_token = bonus_token;
   a.ancestors = ancestors;
   a.ess = ess;
   a.resampled = resampled;
-  a.flags = status_flags;
-  char* ws = static_cast<char*>(workspace);
-  a.part = reinterpret_cast<float2*>(ws + l.part);
-  a.ws_logw = reinterpret_cast<float*>(ws + l.ws_logw);
-  return smcsd::launch_smc(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SMCSD_OK
-                                                                                 : SMCSD_ERR_HIP;
+  const bool vec = vec_ok(dtype, V, target_logits, K > 0 ? draft_logits : nullptr);
+  return smcsd::launch_smc(a, dtype == SMCSD_BF16, vec, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SMCSD_OK
+             : SMCSD_ERR_HIP;
 }
 
 }  // extern "C"

@@ -23,7 +23,7 @@ constexpr int TILE = 2048;
 constexpr int PER_LANE = TILE / WAVE;  // 32 values per lane
 
 constexpr uint32_t FLAG_NONFINITE = 1, FLAG_ZERO_RESIDUAL = 2, FLAG_ZERO_WEIGHTS = 4,
-                   FLAG_CDF_CLAMP = 8, FLAG_BAD_INPUT = 16;
+                   FLAG_CDF_CLAMP = 8, FLAG_BAD_INPUT = 16, FLAG_SPIN_TIMEOUT = 32;
 
 struct Bf16 {
   using raw = uint16_t;
@@ -45,14 +45,14 @@ constexpr int DPP_ROR4 = 0x124;      // row_ror:4
 constexpr int DPP_ROR8 = 0x128;      // row_ror:8
 
 template <int CTRL>
-__device__ inline float dpp_f32(float v) {
+__device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ inline float readlane_f32(float v, int lane) {
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__device__ inline float wave_max(float v) {
+__device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));
   v = fmaxf(v, dpp_f32<DPP_QUAD_2301>(v));
   v = fmaxf(v, dpp_f32<DPP_ROR4>(v));
@@ -61,7 +61,7 @@ __device__ inline float wave_max(float v) {
                fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
-__device__ inline float wave_sum(float v) {
+__device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<DPP_QUAD_1032>(v);
   v += dpp_f32<DPP_QUAD_2301>(v);
   v += dpp_f32<DPP_ROR4>(v);
@@ -69,19 +69,19 @@ __device__ inline float wave_sum(float v) {
   return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
-__device__ inline double wave_sum_f64(double v) {
+__device__ __forceinline__ double wave_sum_f64(double v) {
   // fixed butterfly order: deterministic for a given lane assignment
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
   return v;
 }
 
-__device__ inline double wave_max_f64(double v) {
+__device__ __forceinline__ double wave_max_f64(double v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, WAVE));
   return v;
 }
 
 // inclusive prefix sum over the 64 lanes (ascending lane order)
-__device__ inline float wave_incl_scan(float v, int lane) {
+__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
   for (int off = 1; off < WAVE; off <<= 1) {
     float o = __shfl_up(v, off, WAVE);
     if (lane >= off) v += o;
@@ -89,7 +89,7 @@ __device__ inline float wave_incl_scan(float v, int lane) {
   return v;
 }
 
-__device__ inline double wave_incl_scan_f64(double v, int lane) {
+__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
   for (int off = 1; off < WAVE; off <<= 1) {
     double o = __shfl_up(v, off, WAVE);
     if (lane >= off) v += o;
@@ -102,14 +102,14 @@ __device__ inline double wave_incl_scan_f64(double v, int lane) {
 // ---------------------------------------------------------------------------
 // Element index (within the tile) of value e of lane `lane`.
 template <typename DT>
-__device__ inline int tile_elem(int lane, int e) {
+__device__ __forceinline__ int tile_elem(int lane, int e) {
   return (e / DT::VEC) * (WAVE * DT::VEC) + lane * DT::VEC + (e % DT::VEC);
 }
 
 // Load tile `tile` of `row` (V logits) into v[]; elements past V read as -inf.
 // VECLOAD requires a 16-byte aligned row base and V % DT::VEC == 0.
 template <typename DT, bool VECLOAD>
-__device__ inline void load_tile(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
+__device__ __forceinline__ void load_tile(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
                                  int lane, float (&v)[PER_LANE]) {
   const int64_t base = tile * TILE;
   constexpr int CHUNKS = PER_LANE / DT::VEC;
@@ -150,7 +150,7 @@ __device__ inline void load_tile(const typename DT::raw* __restrict__ row, int64
 
 // Softmax partial of a loaded tile: m = max, s = sum 2^((v - m) * c).
 // An all -inf tile gives (-inf, 0).  NaN or +inf inputs make s NaN.
-__device__ inline float2 tile_partial(const float (&v)[PER_LANE], float c) {
+__device__ __forceinline__ float2 tile_partial(const float (&v)[PER_LANE], float c) {
   float m = -INFINITY;
 #pragma unroll
   for (int e = 0; e < PER_LANE; e++) m = fmaxf(m, v[e]);
@@ -173,25 +173,8 @@ struct RowStat {
   bool ok;       // M finite and S finite and >= 1
 };
 
-__device__ inline RowStat merge_row(const float2* __restrict__ part, int ntiles, float c, int lane) {
-  float m = -INFINITY;
-  for (int t = lane; t < ntiles; t += WAVE) m = fmaxf(m, part[t].x);
-  RowStat r;
-  r.M = wave_max(m);
-  double s = 0.0;
-  if (r.M != -INFINITY) {
-    for (int t = lane; t < ntiles; t += WAVE) {
-      const float2 pt = part[t];
-      if (pt.x != -INFINITY) s += (double)pt.y * exp2(((double)pt.x - (double)r.M) * (double)c);
-    }
-  }
-  r.S = wave_sum_f64(s);
-  r.ok = (r.M > -INFINITY) && (r.M < INFINITY) && (r.S >= 1.0) && (r.S < INFINITY);
-  return r;
-}
-
 // natural-log probability of logit z under a row with statistics rs
-__device__ inline double log_prob(float z, const RowStat& rs, float c) {
+__device__ __forceinline__ double log_prob(float z, const RowStat& rs, float c) {
   return ((double)z - (double)rs.M) * (double)c * 0.69314718055994530942 - log(rs.S);
 }
 
@@ -203,7 +186,7 @@ __device__ inline double log_prob(float z, const RowStat& rs, float c) {
 // the whole tile's prefix stays <= target; *last_pos receives the last element
 // with w > 0 (or -1).  All 64 lanes must call it with the same target.
 template <typename DT>
-__device__ inline int tile_search(const float (&w)[PER_LANE], float target, int lane, int* last_pos) {
+__device__ __forceinline__ int tile_search(const float (&w)[PER_LANE], float target, int lane, int* last_pos) {
   constexpr int CHUNKS = PER_LANE / DT::VEC;
   float run = 0.0f;
   int found = -1;

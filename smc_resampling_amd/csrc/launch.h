@@ -5,61 +5,55 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <algorithm>
-
 #include "smcsd.h"
-
-#define SMCSD_MAX_K_DEV SMCSD_MAX_K
-#define SMCSD_MAX_N_DEV SMCSD_MAX_N
 
 namespace smcsd {
 
-// cap on the grid of the streaming kernels (grid-stride loops beyond it)
-constexpr int64_t kMaxStreamBlocks = 8192;
-
-struct SdArgs {
-  bool bf16, vec;
-  int B, K;
-  int64_t V, rows_t, rows_d;
-  int ntiles;
-  float c;  // log2(e) / T
+// Phase A (tile streaming) of both kernels.
+struct StreamArgs {
   const void* target;
   const void* draft;
-  const int32_t* tokens;
-  const float* uniforms;
-  const int32_t* offsets;
-  int32_t* num_accepted;
-  int32_t* final_token;
+  const int32_t* offsets;  // CSR over draft rows, or null (fixed K)
+  int64_t ngroups, rows_t, rows_d, V, total_tiles;
+  int K, ntiles;
+  float c;           // log2(e) / T
+  float2* part;      // [total_tiles] softmax partial of each tile, group-major
+  uint32_t* gcount;  // [ngroups] tiles finished per group (zero between calls)
   uint32_t* flags;
-  float2* part;   // [(rows_t + rows_d) * ntiles]
-  float* rmass;   // [B * ntiles]
-  int32_t* ws_n;  // [B]
 };
 
-struct SmcArgs {
-  bool bf16, vec;
-  int P, N, K, L;
-  int64_t V;
-  int ntiles;
-  float c, ess_frac;
-  const void* target;
-  const void* draft;
+struct SdFusedArgs {
+  StreamArgs s;
+  const int32_t* tokens;
+  const float* uniforms;
+  uint32_t* dec;     // [B] decision of each sequence (zero between calls)
+  uint32_t* rcount;  // [B] residual slots arrived (zero between calls)
+  void* rec;         // [B] statistics of the rejected pair
+  float* rmass;      // [B * ntiles] residual mass per tile
+  int32_t* num_accepted;
+  int32_t* final_token;
+};
+
+struct SmcFusedArgs {
+  StreamArgs s;
+  int N, L;
+  float ess_frac;
   const int32_t* tokens;
   const float* bonus_u;
   const float* resample_u;
-  float* logw;
+  const float* logw_in;
+  float* logw_out;    // same buffer as logw_in (each entry is read before it is written)
+  float* ws_logw;     // [P*N] reweighted log-weights
+  uint32_t* pcount;   // [P] particles finished per prompt (zero between calls)
   const int32_t* pt_in;
   int32_t* pt_out;
   int32_t* bonus_token;
   int32_t* ancestors;
   float* ess;
   int32_t* resampled;
-  uint32_t* flags;
-  float2* part;     // [P*N*(2K+1) * ntiles]
-  float* ws_logw;   // [P*N]
 };
 
-hipError_t launch_sd(const SdArgs& a, hipStream_t s);
-hipError_t launch_smc(const SmcArgs& a, hipStream_t s);
+hipError_t launch_sd(const SdFusedArgs& a, bool bf16, bool vec, hipStream_t s);
+hipError_t launch_smc(const SmcFusedArgs& a, bool bf16, bool vec, hipStream_t s);
 
 }  // namespace smcsd

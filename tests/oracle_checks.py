@@ -243,6 +243,21 @@ def check_residual_vs_numpy(lib):
     assert seen > B // 2
 
 
+def check_final_cdf_vs_numpy(lib):
+    """The normalised CDF the comparison judges differing tokens against: the
+    residual cumsum(max(0, p_n - q_n)) / Z for n < K_b, cumsum(p_K) for n = K_b."""
+    rng = np.random.default_rng(10)
+    B, K, V, T = 3, 2, 611, 0.8
+    zt, zd, tok, u = rand_sd_problem(rng, B, K, V, T, delta=1.5)
+    for b in range(B):
+        for n in range(K + 1):
+            cdf, fl = oracle.sd_final_cdf(zt, zd, b, n, T, K=K, lib=lib)
+            p = softmax(zt[b * (K + 1) + n].astype(np.float64) / T)
+            w = np.maximum(0.0, p - softmax(zd[b * K + n].astype(np.float64) / T)) if n < K else p
+            want = np.cumsum(w) / w.sum()
+            assert fl == 0 and np.abs(cdf - want).max() < 1e-12, (b, n, np.abs(cdf - want).max())
+
+
 def check_accept_decisions_vs_scipy(lib):
     """n = index of the first j with u_j >= p_j(x_j)/q_j(x_j) (scipy softmax)."""
     rng = np.random.default_rng(9)
@@ -487,6 +502,7 @@ DETERMINISTIC_CHECKS = [
     check_bonus_vs_numpy,
     check_residual_vs_numpy,
     check_accept_decisions_vs_scipy,
+    check_final_cdf_vs_numpy,
     check_ess_closed_forms,
     check_threshold_strict,
     check_systematic_invariants,

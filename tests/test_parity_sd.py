@@ -113,3 +113,26 @@ def test_cfg1_full_size():
 
 def test_cfg4_ragged_full_size():
     _config_steps(4, range(2))
+
+
+def test_sd_workspace_reuse():
+    """One zero-filled workspace across many calls of different shapes: the
+    kernel returns its counters to zero after every call."""
+    import torch
+
+    import smc_resampling_amd as s
+    from compare import compare_sd
+    from gpu_util import DEV, dev_logits, run_sd_oracle
+
+    ws = s.new_workspace(s.sd_verify_workspace_bytes(1, 40, 16, 40000, 40 * 16), DEV)
+    for i, (B, V, K, lengths) in enumerate([(40, 40000, 4, None), (7, 333, 2, None), (12, 5000, None, [3, 0, 16, 1, 2,
+                                            5, 8, 9, 0, 4, 4, 12]), (40, 40000, 16, None), (1, 10, 0, None)]):
+        c = sd_case(100 + i, B, V, T=0.9, K=K, lengths=lengths, delta=1.0, dtype="bf16")
+        off = None if c["offsets"] is None else torch.from_numpy(c["offsets"]).to(DEV)
+        na, ft, fl = s.sd_verify(dev_logits(c["target"]), dev_logits(c["draft"]), torch.from_numpy(c["tokens"]).to(DEV),
+                                 torch.from_numpy(c["uniforms"]).to(DEV), c["T"], K=c["K"], draft_offsets=off,
+                                 workspace=ws)
+        torch.cuda.synchronize()
+        t = compare_sd(c, run_sd_oracle(c), na.cpu().numpy(), ft.cpu().numpy(), f"reuse {i}")
+        t.assert_ok()
+        assert int(fl.item()) & ~8 == 0

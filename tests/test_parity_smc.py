@@ -108,3 +108,30 @@ def test_cfg2_full_size():
 
 def test_cfg3_full_size_sampled_prompts():
     _cfg_smc(3, range(1), prompts=[0, 1, 31])
+
+
+def test_smc_workspace_reuse():
+    import torch
+
+    import oracle
+    import smc_resampling_amd as s
+    from compare import compare_smc
+    from gpu_util import DEV, dev_logits
+
+    ws = s.new_workspace(s.smc_workspace_bytes(1, 4, 64, 8, 20000), DEV)
+    for i, (P, N, K, V) in enumerate([(4, 64, 8, 20000), (1, 3, 1, 50), (2, 17, 0, 2049), (4, 64, 8, 20000)]):
+        c = smc_case(200 + i, P, N, K, V, dtype="bf16", L=3, logw_scale=2.0)
+        lw = torch.from_numpy(c["logw"]).to(DEV)
+        pt = torch.from_numpy(c["pt"]).to(DEV)
+        out = s.smc_reweight_resample(dev_logits(c["target"]), dev_logits(c["draft"]),
+                                      torch.from_numpy(c["tokens"]).to(DEV), torch.from_numpy(c["bonus_u"]).to(DEV),
+                                      torch.from_numpy(c["resample_u"]).to(DEV), lw, 1.0, 0.9, P, N, K,
+                                      page_table_in=pt, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.smc_step(c["target"], c["draft"], c["tokens"], c["bonus_u"], c["resample_u"], c["logw"], 1.0, 0.9,
+                              P, N, K, pt_in=c["pt"])
+        g = dict(bonus=out["bonus_token"].cpu().numpy(), ancestors=out["ancestors"].cpu().numpy(),
+                 ess=out["ess"].cpu().numpy(), resampled=out["resampled"].cpu().numpy(), logw=lw.cpu().numpy(),
+                 pt_out=out["page_table_out"].cpu().numpy())
+        compare_smc(c, ref, g, c["logw"], c["pt"], f"reuse {i}").assert_ok()
+        assert int(out["status_flags"].item()) & ~8 == 0
