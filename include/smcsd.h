@@ -53,10 +53,12 @@
  *
  * Workspace:
  *   Caller-owned device scratch of at least the size the *_workspace_bytes()
- *   query returns, aligned to SMCSD_WORKSPACE_ALIGN.  It must be zero-filled
- *   once before its first use; every call leaves its counters at zero again.
- *   After a call that raised SMCSD_FLAG_BAD_INPUT or SMCSD_FLAG_SPIN_TIMEOUT,
- *   zero-fill it again before reuse.
+ *   query returns, aligned to SMCSD_WORKSPACE_ALIGN.  Its first
+ *   SMCSD_WORKSPACE_COUNTER_BYTES hold counters only; they must be zero before
+ *   the first call and every call leaves them at zero, so one workspace serves
+ *   any sequence of calls (of any shapes it is large enough for).  After a
+ *   call that raised SMCSD_FLAG_BAD_INPUT or SMCSD_FLAG_SPIN_TIMEOUT, zero the
+ *   counter bytes again before reuse.
  *
  * Logits are row-major and contiguous: row r starts at element r * V.  bf16
  * logits are raw 16-bit bfloat16 patterns.
@@ -108,6 +110,9 @@ enum {
 #define SMCSD_MAX_K 128    /* largest draft length per sequence / particle      */
 #define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
 #define SMCSD_WORKSPACE_ALIGN 256
+/* The first bytes of every workspace hold counters only (shape independent):
+   sd_verify needs B <= 87381, smc_reweight_resample P*N + P <= 262144. */
+#define SMCSD_WORKSPACE_COUNTER_BYTES (1u << 20)
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
 int32_t smcsd_abi_version(void);

@@ -25,11 +25,17 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
   return V % per == 0 && aligned16(a) && (b == nullptr || aligned16(b));
 }
 
-// Workspace layouts.  The counters come first so that one zero-fill of the
-// start of the workspace (or of all of it) prepares it.
+// Workspace layouts.  The first SMCSD_WORKSPACE_COUNTER_BYTES of every
+// workspace hold only counters, whatever the shape of the call, so one
+// workspace can serve calls of different shapes: the counters are zero before
+// the first call and every call leaves them at zero.  Scratch data follows.
+constexpr size_t kCounterBytes = SMCSD_WORKSPACE_COUNTER_BYTES;
+
 struct SdLayout {
   size_t gcount, dec, rcount, rec, rmass, part, total;
 };
+
+bool sd_counters_fit(int64_t B) { return 3 * align_up(sizeof(uint32_t) * (size_t)B) <= kCounterBytes; }
 
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
@@ -37,7 +43,7 @@ SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   l.gcount = 0;
   l.dec = align_up(l.gcount + sizeof(uint32_t) * (size_t)B);
   l.rcount = align_up(l.dec + sizeof(uint32_t) * (size_t)B);
-  l.rec = align_up(l.rcount + sizeof(uint32_t) * (size_t)B);
+  l.rec = kCounterBytes;
   l.rmass = align_up(l.rec + 24 * (size_t)B);
   l.part = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
   l.total = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
@@ -48,13 +54,17 @@ struct SmcLayout {
   size_t gcount, pcount, ws_logw, part, total;
 };
 
+bool smc_counters_fit(int64_t P, int64_t N) {
+  return align_up(sizeof(uint32_t) * (size_t)(P * N)) + align_up(sizeof(uint32_t) * (size_t)P) <= kCounterBytes;
+}
+
 SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   const int nt = ntiles_of(V);
   const int64_t PN = (int64_t)P * N;
   SmcLayout l;
   l.gcount = 0;
   l.pcount = align_up(sizeof(uint32_t) * (size_t)PN);
-  l.ws_logw = align_up(l.pcount + sizeof(uint32_t) * (size_t)P);
+  l.ws_logw = kCounterBytes;
   l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
   l.total = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
   return l;
@@ -95,7 +105,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
                   void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
   if (B < 0 || K < 0 || V < 1 || !temperature_ok(temperature)) return SMCSD_ERR_INVALID_ARG;
-  if (K > SMCSD_MAX_K || B > 65535) return SMCSD_ERR_UNSUPPORTED;
+  if (K > SMCSD_MAX_K || !sd_counters_fit(B)) return SMCSD_ERR_UNSUPPORTED;
   if (total_draft_rows < 0 || total_draft_rows > (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
   if (!draft_offsets && total_draft_rows != (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
   if (B == 0) return SMCSD_OK;
@@ -153,7 +163,7 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   if (P < 0 || N < 1 || K < 0 || V < 1 || pages_per_particle < 0) return SMCSD_ERR_INVALID_ARG;
   if (!temperature_ok(temperature) || !isfinite(ess_frac) || ess_frac < 0.0f)
     return SMCSD_ERR_INVALID_ARG;
-  if (K > SMCSD_MAX_K || N > SMCSD_MAX_N) return SMCSD_ERR_UNSUPPORTED;
+  if (K > SMCSD_MAX_K || N > SMCSD_MAX_N || !smc_counters_fit(P, N)) return SMCSD_ERR_UNSUPPORTED;
   if (P == 0) return SMCSD_OK;
   if (!target_logits || !bonus_uniforms || !resample_uniforms || !log_weights || !bonus_token ||
       !ancestors || !ess || !resampled)

@@ -2,6 +2,7 @@
 library through its C ABI, run the oracle on the same inputs, compare."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -14,8 +15,12 @@ DEV = torch.device("cuda:0")
 
 
 def say(msg):
+    """Progress line; also appended to $SMCSD_PARITY_LOG when set (exemption tallies)."""
     print(msg, flush=True)
-    sys.stdout.flush()
+    path = os.environ.get("SMCSD_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(msg + "\n")
 
 
 def lib():
