@@ -110,9 +110,10 @@ enum {
 #define SMCSD_MAX_K 128    /* largest draft length per sequence / particle      */
 #define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
 #define SMCSD_WORKSPACE_ALIGN 256
-/* The first bytes of every workspace hold counters only (shape independent):
-   sd_verify needs B <= 87381, smc_reweight_resample P*N + P <= 262144. */
-#define SMCSD_WORKSPACE_COUNTER_BYTES (1u << 20)
+/* The first bytes of every workspace hold counters only (shape independent),
+   one 64-byte line each: sd_verify needs B <= 21845, smc_reweight_resample
+   P*N + P <= 65536. */
+#define SMCSD_WORKSPACE_COUNTER_BYTES (4u << 20)
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
 int32_t smcsd_abi_version(void);

@@ -35,14 +35,17 @@ struct SdLayout {
   size_t gcount, dec, rcount, rec, rmass, part, total;
 };
 
-bool sd_counters_fit(int64_t B) { return 3 * align_up(sizeof(uint32_t) * (size_t)B) <= kCounterBytes; }
+// every counter occupies its own 64-byte line
+constexpr size_t kCounterLine = 64;
+
+bool sd_counters_fit(int64_t B) { return 3 * align_up(kCounterLine * (size_t)B) <= kCounterBytes; }
 
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
   SdLayout l;
   l.gcount = 0;
-  l.dec = align_up(l.gcount + sizeof(uint32_t) * (size_t)B);
-  l.rcount = align_up(l.dec + sizeof(uint32_t) * (size_t)B);
+  l.dec = align_up(l.gcount + kCounterLine * (size_t)B);
+  l.rcount = align_up(l.dec + kCounterLine * (size_t)B);
   l.rec = kCounterBytes;
   l.rmass = align_up(l.rec + 24 * (size_t)B);
   l.part = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
@@ -55,7 +58,7 @@ struct SmcLayout {
 };
 
 bool smc_counters_fit(int64_t P, int64_t N) {
-  return align_up(sizeof(uint32_t) * (size_t)(P * N)) + align_up(sizeof(uint32_t) * (size_t)P) <= kCounterBytes;
+  return align_up(kCounterLine * (size_t)(P * N)) + align_up(kCounterLine * (size_t)P) <= kCounterBytes;
 }
 
 SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
@@ -63,7 +66,7 @@ SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   const int64_t PN = (int64_t)P * N;
   SmcLayout l;
   l.gcount = 0;
-  l.pcount = align_up(sizeof(uint32_t) * (size_t)PN);
+  l.pcount = align_up(kCounterLine * (size_t)PN);
   l.ws_logw = kCounterBytes;
   l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
   l.total = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));

@@ -98,7 +98,8 @@ __device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// tile loads
+// tile loads: a tile stays packed in registers (bf16: 4 x 16 bytes per lane,
+// fp32: 8 x 16 bytes) and is unpacked one chunk at a time
 // ---------------------------------------------------------------------------
 // Element index (within the tile) of value e of lane `lane`.
 template <typename DT>
@@ -106,51 +107,77 @@ __device__ __forceinline__ int tile_elem(int lane, int e) {
   return (e / DT::VEC) * (WAVE * DT::VEC) + lane * DT::VEC + (e % DT::VEC);
 }
 
-// Load tile `tile` of `row` (V logits) into v[]; elements past V read as -inf.
+template <typename DT>
+struct Raw {
+  static constexpr int CHUNKS = PER_LANE / DT::VEC;
+  uint4 q[CHUNKS];
+};
+
+// Load tile `tile` of `row` (V logits); elements past V read as -inf.
 // VECLOAD requires a 16-byte aligned row base and V % DT::VEC == 0.
 template <typename DT, bool VECLOAD>
-__device__ __forceinline__ void load_tile(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
-                                 int lane, float (&v)[PER_LANE]) {
+__device__ __forceinline__ Raw<DT> load_raw(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
+                                            int lane) {
+  Raw<DT> r;
   const int64_t base = tile * TILE;
-  constexpr int CHUNKS = PER_LANE / DT::VEC;
-  if constexpr (VECLOAD) {
+  constexpr uint32_t NEG_INF_BITS = DT::VEC == 8 ? 0xFF80FF80u : 0xFF800000u;
 #pragma unroll
-    for (int c = 0; c < CHUNKS; c++) {
-      const int64_t off = base + c * (WAVE * DT::VEC) + lane * DT::VEC;
-      if (off < V) {
-        const uint4 w = *reinterpret_cast<const uint4*>(row + off);
+  for (int c = 0; c < Raw<DT>::CHUNKS; c++) {
+    const int64_t off = base + c * (WAVE * DT::VEC) + lane * DT::VEC;
+    if constexpr (VECLOAD) {
+      if (off < V) r.q[c] = *reinterpret_cast<const uint4*>(row + off);
+      else r.q[c] = make_uint4(NEG_INF_BITS, NEG_INF_BITS, NEG_INF_BITS, NEG_INF_BITS);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
         if constexpr (DT::VEC == 8) {
-          v[c * 8 + 0] = __uint_as_float(w.x << 16);
-          v[c * 8 + 1] = __uint_as_float(w.x & 0xFFFF0000u);
-          v[c * 8 + 2] = __uint_as_float(w.y << 16);
-          v[c * 8 + 3] = __uint_as_float(w.y & 0xFFFF0000u);
-          v[c * 8 + 4] = __uint_as_float(w.z << 16);
-          v[c * 8 + 5] = __uint_as_float(w.z & 0xFFFF0000u);
-          v[c * 8 + 6] = __uint_as_float(w.w << 16);
-          v[c * 8 + 7] = __uint_as_float(w.w & 0xFFFF0000u);
+          const uint32_t lo = off + 2 * k < V ? (uint32_t)row[off + 2 * k] : 0xFF80u;
+          const uint32_t hi = off + 2 * k + 1 < V ? (uint32_t)row[off + 2 * k + 1] : 0xFF80u;
+          w[k] = lo | (hi << 16);
         } else {
-          v[c * 4 + 0] = __uint_as_float(w.x);
-          v[c * 4 + 1] = __uint_as_float(w.y);
-          v[c * 4 + 2] = __uint_as_float(w.z);
-          v[c * 4 + 3] = __uint_as_float(w.w);
+          w[k] = off + k < V ? __float_as_uint(row[off + k]) : NEG_INF_BITS;
         }
-      } else {
-#pragma unroll
-        for (int k = 0; k < DT::VEC; k++) v[c * DT::VEC + k] = -INFINITY;
       }
+      r.q[c] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+  }
+  return r;
+}
+
+// the VEC logits of chunk c, as fp32
+template <typename DT>
+__device__ __forceinline__ void unpack(const Raw<DT>& r, int c, float (&v)[DT::VEC]) {
+  const uint4 w = r.q[c];
+  if constexpr (DT::VEC == 8) {
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    v[4] = __uint_as_float(w.z << 16);
+    v[5] = __uint_as_float(w.z & 0xFFFF0000u);
+    v[6] = __uint_as_float(w.w << 16);
+    v[7] = __uint_as_float(w.w & 0xFFFF0000u);
   } else {
-#pragma unroll
-    for (int e = 0; e < PER_LANE; e++) {
-      const int64_t off = base + tile_elem<DT>(lane, e);
-      v[e] = off < V ? DT::to_f32(row[off]) : -INFINITY;
-    }
+    v[0] = __uint_as_float(w.x);
+    v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z);
+    v[3] = __uint_as_float(w.w);
   }
 }
 
-// Softmax partial of a loaded tile: m = max, s = sum 2^((v - m) * c).
+// Softmax partial of a tile: m = max, s = sum 2^((v - m) * c).
 // An all -inf tile gives (-inf, 0).  NaN or +inf inputs make s NaN.
-__device__ __forceinline__ float2 tile_partial(const float (&v)[PER_LANE], float c) {
+template <typename DT>
+__device__ __forceinline__ float2 tile_partial(const Raw<DT>& r, float c) {
+  float v[PER_LANE];
+#pragma unroll
+  for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+    float t[DT::VEC];
+    unpack<DT>(r, ch, t);
+#pragma unroll
+    for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = t[k];
+  }
   float m = -INFINITY;
 #pragma unroll
   for (int e = 0; e < PER_LANE; e++) m = fmaxf(m, v[e]);
@@ -168,46 +195,48 @@ __device__ __forceinline__ float2 tile_partial(const float (&v)[PER_LANE], float
 // merge of per-tile partials into row statistics (one wavefront)
 // ---------------------------------------------------------------------------
 struct RowStat {
-  float M;       // max logit of the row
-  double S;      // sum over the row of 2^((z - M) * c)
-  bool ok;       // M finite and S finite and >= 1
+  float M;       // max over the row of z * c (log2 domain, c = log2(e) / T)
+  double S;      // sum over the row of 2^(z c - M)
+  bool ok;       // M finite and S finite and >= 1 (up to rounding)
 };
 
 // natural-log probability of logit z under a row with statistics rs
 __device__ __forceinline__ double log_prob(float z, const RowStat& rs, float c) {
-  return ((double)z - (double)rs.M) * (double)c * 0.69314718055994530942 - log(rs.S);
+  return ((double)z * (double)c - (double)rs.M) * 0.69314718055994530942 - log(rs.S);
 }
 
 // ---------------------------------------------------------------------------
 // ordered search inside a tile
 // ---------------------------------------------------------------------------
 // Finds the first element (ascending token order) whose inclusive prefix of
-// w[] exceeds `target`.  Returns the element index within the tile, or -1 when
+// the tile's weights exceeds `target`.  wfn(c, w) fills the DT::VEC weights of
+// this lane's chunk c.  Returns the element index within the tile, or -1 when
 // the whole tile's prefix stays <= target; *last_pos receives the last element
-// with w > 0 (or -1).  All 64 lanes must call it with the same target.
-template <typename DT>
-__device__ __forceinline__ int tile_search(const float (&w)[PER_LANE], float target, int lane, int* last_pos) {
+// with positive weight (or -1).  All 64 lanes must call it with the same target.
+template <typename DT, typename WFN>
+__device__ __forceinline__ int tile_search(WFN wfn, float target, int lane, int* last_pos) {
   constexpr int CHUNKS = PER_LANE / DT::VEC;
   float run = 0.0f;
   int found = -1;
   int lastp = -1;
 #pragma unroll
   for (int c = 0; c < CHUNKS; c++) {
+    float w[DT::VEC];
+    wfn(c, w);
     float ls = 0.0f;
 #pragma unroll
-    for (int k = 0; k < DT::VEC; k++) ls += w[c * DT::VEC + k];
+    for (int k = 0; k < DT::VEC; k++) ls += w[k];
     // last positive element of this chunk (largest lane with a positive value)
     int lp = -1;
 #pragma unroll
     for (int k = 0; k < DT::VEC; k++)
-      if (w[c * DT::VEC + k] > 0.0f) lp = tile_elem<DT>(lane, c * DT::VEC + k);
+      if (w[k] > 0.0f) lp = tile_elem<DT>(lane, c * DT::VEC + k);
     for (int off = 32; off >= 1; off >>= 1) lp = max(lp, __shfl_xor(lp, off, WAVE));
     if (lp >= 0) lastp = lp;
     if (found < 0) {
       const float incl = wave_incl_scan(ls, lane);
       const float excl = incl - ls;
-      const bool cross = run + incl > target;
-      const uint64_t bal = __ballot(cross);
+      const uint64_t bal = __ballot(run + incl > target);
       if (bal) {
         const int src = __builtin_ctzll(bal);
         int idx = -1;
@@ -215,12 +244,13 @@ __device__ __forceinline__ int tile_search(const float (&w)[PER_LANE], float tar
           float acc = run + excl;
 #pragma unroll
           for (int k = 0; k < DT::VEC; k++) {
-            acc += w[c * DT::VEC + k];
+            acc += w[k];
             if (idx < 0 && acc > target) idx = tile_elem<DT>(lane, c * DT::VEC + k);
           }
           if (idx < 0) {  // rounding between the two sums: take the lane's last positive
-            for (int k = DT::VEC - 1; k >= 0 && idx < 0; k--)
-              if (w[c * DT::VEC + k] > 0.0f) idx = tile_elem<DT>(lane, c * DT::VEC + k);
+#pragma unroll
+            for (int k = 0; k < DT::VEC; k++)
+              if (w[k] > 0.0f) idx = tile_elem<DT>(lane, c * DT::VEC + k);
           }
         }
         found = __shfl(idx, src, WAVE);

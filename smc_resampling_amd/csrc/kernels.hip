@@ -53,23 +53,59 @@ __device__ __forceinline__ void raise_flags(uint32_t* flags, uint32_t bits) {
   if (flags && bits) atomicOr(flags, bits);
 }
 
-__device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-wavefront communication.  Every value one wavefront hands to another
+// (tile partials, decisions, residual masses, log-weights, counters) is
+// written and read with agent-scope relaxed atomics, which on gfx950 are
+// write-through / read-through at the device coherence point (`sc1`) and need
+// no writeback or invalidation of the XCD-local L2.  A writer waits for its
+// stores to complete before it bumps a counter or sets a flag; a reader that
+// has seen the counter or flag then reads the values from the same point.
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float2* p, float2 v) {
+  const uint64_t b = ((uint64_t)__float_as_uint(v.y) << 32) | __float_as_uint(v.x);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __uint_as_float(
+      __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ double ld_dev(const double* p) {
+  return __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<double*>(p)),
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float2 ld_dev(const float2* p) {
+  const uint64_t b =
+      __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+}
+// wait until every memory operation this wavefront issued has completed
+__device__ __forceinline__ void stores_done() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// one acq_rel add per wavefront (lane 0), old value broadcast to every lane
+// one add per wavefront (lane 0, after the wavefront's stores completed); the
+// old value is broadcast to every lane
 __device__ __forceinline__ uint32_t wave_add(uint32_t* p, uint32_t v, int lane) {
+  stores_done();
   uint32_t old = 0;
-  if (lane == 0) old = atomic_add_acq_rel(p, v);
-  return __shfl(old, 0, WAVE);
-}
-
-__device__ __forceinline__ uint32_t load_acquire(uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_release(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) old = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, WAVE);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return old;
 }
 
 template <int CTRL>
@@ -95,7 +131,8 @@ __device__ __forceinline__ double row16_sum(double v) {
 }
 
 // Row statistics of `nrows` consecutive rows of partials (one wavefront; 16
-// lanes per row, 4 rows at a time) into the wavefront's LDS slice.
+// lanes per row, 4 rows at a time) into the wavefront's LDS slice: M = max of
+// the partials' mc (log2 domain), S = sum of s * 2^(mc - M).
 __device__ __forceinline__ void merge_group_rows(const float2* __restrict__ part, int nrows, int ntiles, float c,
                                         float* sM, double* sS, int lane) {
   const int sub = lane & 15;
@@ -105,13 +142,13 @@ __device__ __forceinline__ void merge_group_rows(const float2* __restrict__ part
     const float2* pr = part + (int64_t)(live ? r : 0) * ntiles;
     float m = -INFINITY;
     if (live)
-      for (int t = sub; t < ntiles; t += 16) m = fmaxf(m, pr[t].x);
+      for (int t = sub; t < ntiles; t += 16) m = fmaxf(m, ld_dev(pr + t).x);
     const float M = row16_max(m);
     double s = 0.0;
     if (live && M != -INFINITY) {
       for (int t = sub; t < ntiles; t += 16) {
-        const float2 pt = pr[t];
-        if (pt.x != -INFINITY) s += (double)pt.y * exp2(((double)pt.x - (double)M) * (double)c);
+        const float2 pt = ld_dev(pr + t);
+        if (pt.x != -INFINITY) s += (double)pt.y * exp2((double)pt.x - (double)M);
       }
     }
     const double S = row16_sum(s);
@@ -127,19 +164,24 @@ __device__ __forceinline__ RowStat stat_of(const float* sM, const double* sS, in
   RowStat rs;
   rs.M = sM[r];
   rs.S = sS[r];
-  rs.ok = (rs.M > -INFINITY) && (rs.M < INFINITY) && (rs.S >= 1.0) && (rs.S < INFINITY);
+  rs.ok = (rs.M > -INFINITY) && (rs.M < INFINITY) && (rs.S >= 0.5) && (rs.S < INFINITY);
   return rs;
 }
 
-// Residual weights max(0, p - q) of one tile of a (target, draft) row pair.
-__device__ __forceinline__ void residual_weights(const float (&vt)[PER_LANE], const float (&vd)[PER_LANE],
-                                        float Mt, float Md, float c, float st, float sd,
-                                        float (&r)[PER_LANE]) {
+// Residual weights max(0, p - q) of chunk ch of one tile of a (target, draft)
+// row pair, p = 2^(z_t c - Mt) * st, q = 2^(z_d c - Md) * sd (Mt, Md in the
+// log2 domain, st = 1 / S_t, sd = 1 / S_d).
+template <typename DT>
+__device__ __forceinline__ void residual_chunk(const Raw<DT>& rt, const Raw<DT>& rd, int ch, float Mt, float Md,
+                                               float c, float st, float sd, float (&r)[DT::VEC]) {
+  float vt[DT::VEC], vd[DT::VEC];
+  unpack<DT>(rt, ch, vt);
+  unpack<DT>(rd, ch, vd);
 #pragma unroll
-  for (int e = 0; e < PER_LANE; e++) {
-    const float p = __builtin_amdgcn_exp2f((vt[e] - Mt) * c) * st;
-    const float q = __builtin_amdgcn_exp2f((vd[e] - Md) * c) * sd;
-    r[e] = fmaxf(p - q, 0.0f);
+  for (int k = 0; k < DT::VEC; k++) {
+    const float p = __builtin_amdgcn_exp2f(fmaf(vt[k], c, -Mt)) * st;
+    const float q = __builtin_amdgcn_exp2f(fmaf(vd[k], c, -Md)) * sd;
+    r[k] = fmaxf(p - q, 0.0f);
   }
 }
 
@@ -187,32 +229,87 @@ __device__ __forceinline__ int draw_from_row(const typename DT::raw* __restrict_
                              const float2* __restrict__ part, int ntiles, const RowStat& rs, float c,
                              float u, int lane, uint32_t* fl) {
   auto weight = [&](int t) -> double {
-    const float2 pt = part[t];
-    return pt.x == -INFINITY ? 0.0
-                             : (double)pt.y * exp2(((double)pt.x - (double)rs.M) * (double)c);
+    const float2 pt = ld_dev(part + t);
+    return pt.x == -INFINITY ? 0.0 : (double)pt.y * exp2((double)pt.x - (double)rs.M);
   };
   double before = 0.0, total = 0.0;
   int last_tile = -1;
   const int t = locate_tile(ntiles, weight, (double)u, lane, &before, &total, &last_tile);
   const int tt = t >= 0 ? t : (last_tile >= 0 ? last_tile : ntiles - 1);
-  const float mt = part[tt].x;
-  float v[PER_LANE];
-  load_tile<DT, VL>(row, V, tt, lane, v);
+  const float mt = ld_dev(part + tt).x;
+  const Raw<DT> raw = load_raw<DT, VL>(row, V, tt, lane);
+  auto wfn = [&](int ch, float (&w)[DT::VEC]) {
+    unpack<DT>(raw, ch, w);
 #pragma unroll
-  for (int e = 0; e < PER_LANE; e++) v[e] = __builtin_amdgcn_exp2f((v[e] - mt) * c);
+    for (int k = 0; k < DT::VEC; k++) w[k] = __builtin_amdgcn_exp2f(fmaf(w[k], c, -mt));
+  };
   int last_pos = -1;
   int idx = -1;
   if (t >= 0) {
-    const double tscale = exp2(((double)mt - (double)rs.M) * (double)c);
-    idx = tile_search<DT>(v, (float)(((double)u * total - before) / tscale), lane, &last_pos);
+    const double tscale = exp2((double)mt - (double)rs.M);
+    idx = tile_search<DT>(wfn, (float)(((double)u * total - before) / tscale), lane, &last_pos);
   } else {
-    tile_search<DT>(v, INFINITY, lane, &last_pos);
+    tile_search<DT>(wfn, INFINITY, lane, &last_pos);
   }
   if (idx < 0) {
     *fl |= FLAG_CDF_CLAMP;
     idx = last_pos >= 0 ? last_pos : 0;
   }
   return tt * TILE + idx;
+}
+
+// Inverse-CDF draw from the softmax of `row` without tile partials: one pass
+// for the tile masses (kept in registers, up to 64 tiles per lane), then the
+// located tile is searched.  Used only when the residual mass is zero.
+template <typename DT, bool VL>
+__device__ __forceinline__ int draw_scan_row(const typename DT::raw* __restrict__ row, int64_t V, int ntiles,
+                                             const RowStat& rs, float c, float u, int lane, uint32_t* fl) {
+  auto wfn_for = [&](const Raw<DT>& raw) {
+    return [&raw, &rs, c](int ch, float (&w)[DT::VEC]) {
+      unpack<DT>(raw, ch, w);
+#pragma unroll
+      for (int k = 0; k < DT::VEC; k++) w[k] = __builtin_amdgcn_exp2f(fmaf(w[k], c, -rs.M));
+    };
+  };
+  auto weight = [&](int t) -> double {
+    const Raw<DT> raw = load_raw<DT, VL>(row, V, t, lane);
+    auto wfn = wfn_for(raw);
+    float s = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+      float w[DT::VEC];
+      wfn(ch, w);
+#pragma unroll
+      for (int k = 0; k < DT::VEC; k++) s += w[k];
+    }
+    return (double)wave_sum(s);
+  };
+  // tile masses, sequentially (the weight functor is wave-wide, not per lane)
+  double total = 0.0;
+  for (int t = 0; t < ntiles; t++) total += weight(t);
+  const double target = (double)u * total;
+  double run = 0.0;
+  int tt = -1, lastt = -1;
+  double before = 0.0;
+  for (int t = 0; t < ntiles; t++) {
+    const double W = weight(t);
+    if (W > 0.0) lastt = t;
+    if (run + W > target) {
+      tt = t;
+      before = run;
+      break;
+    }
+    run += W;
+  }
+  const int use = tt >= 0 ? tt : (lastt >= 0 ? lastt : ntiles - 1);
+  const Raw<DT> raw = load_raw<DT, VL>(row, V, use, lane);
+  int last_pos = -1;
+  int idx = tile_search<DT>(wfn_for(raw), tt >= 0 ? (float)(target - before) : INFINITY, lane, &last_pos);
+  if (idx < 0) {
+    *fl |= FLAG_CDF_CLAMP;
+    idx = last_pos >= 0 ? last_pos : 0;
+  }
+  return use * TILE + idx;
 }
 
 // ---------------------------------------------------------------------------
@@ -255,55 +352,146 @@ __device__ __forceinline__ int64_t find_group(int64_t fr, int64_t ngroups, int K
 
 
 
-// Phase A of wavefront w of nw.  Calls on_group(g) (wave-uniform) whenever this
-// wavefront completes group g's tile count.
+// Counters sit 64 bytes apart so that atomics on different groups do not
+// share a cache line.
+constexpr int CSTRIDE = 16;
+
+// Position of the streaming cursor: the group holding row `fr`.
+struct Cursor {
+  int64_t g, fr_end;
+  Group G;
+};
+
+__device__ __forceinline__ Cursor cursor_at(int64_t fr, const StreamArgs& a) {
+  Cursor c;
+  c.g = find_group(fr, a.ngroups, a.K, a.offsets);
+  c.G = group_of(c.g, a.K, a.offsets, a.rows_d);
+  c.fr_end = c.G.fr0 + 2 * c.G.kb + 1;
+  return c;
+}
+
+__device__ __forceinline__ Cursor cursor_advance(Cursor c, int64_t fr, const StreamArgs& a) {
+  while (fr >= c.fr_end && c.g + 1 < a.ngroups) {
+    c.g++;
+    c.G = group_of(c.g, a.K, a.offsets, a.rows_d);
+    c.fr_end = c.G.fr0 + 2 * c.G.kb + 1;
+  }
+  return c;
+}
+
+// Row `fr` of the cursor's group (null when the layout is malformed); *bonus
+// is set for the group's last target row, whose tiles keep their own partials.
+template <typename raw>
+__device__ __forceinline__ const raw* row_at(const Cursor& c, int64_t fr, const StreamArgs& a, bool* bonus) {
+  const int64_t rr = fr - c.G.fr0;
+  *bonus = rr == c.G.kb;
+  if (!c.G.ok || rr < 0 || rr > 2 * c.G.kb) return nullptr;
+  if (rr <= c.G.kb) {
+    const int64_t tr = c.G.d0 + c.g + rr;
+    return tr < a.rows_t ? static_cast<const raw*>(a.target) + tr * a.V : nullptr;
+  }
+  const int64_t dr = c.G.d0 + rr - c.G.kb - 1;
+  return dr < a.rows_d ? static_cast<const raw*>(a.draft) + dr * a.V : nullptr;
+}
+
+// Phase A of wavefront w of nw: stream tiles [f0, f1), the next tile's loads
+// in flight while the current one is reduced.  A partial is (mc, s) with
+// s = sum 2^(z c - mc) over its logits, in the log2 domain x = z c.  Each lane
+// keeps a running (max, sum) over the tiles of one row and the wavefront
+// reduces it once, into the partial slot of the segment's last tile; the other
+// tiles of the segment get an empty partial.  Tiles of a group's bonus row
+// get their own partials (the bonus draw locates its tile from them).
+// on_group(g) runs (wave-uniform) when this wavefront completes g's count.
 template <typename DT, bool VL, typename ONGROUP>
-__device__ __forceinline__ void stream_phase(const StreamArgs& a, int64_t w, int64_t nw, int lane, ONGROUP on_group) {
+__device__ __forceinline__ void stream_phase(const StreamArgs& a, int64_t w, int64_t nw, int lane,
+                                             ONGROUP on_group) {
   using raw = typename DT::raw;
   const int64_t f0 = w * a.total_tiles / nw, f1 = (w + 1) * a.total_tiles / nw;
   if (f0 >= f1) return;
-  int64_t g = find_group(f0 / a.ntiles, a.ngroups, a.K, a.offsets);
-  Group G = group_of(g, a.K, a.offsets, a.rows_d);
-  int64_t fr_end = G.fr0 + 2 * G.kb + 1;
-  uint32_t done = 0;
-  uint32_t bad = 0;
+  const int ntiles = a.ntiles;
+  const float c = a.c;
+  int64_t fr = f0 / ntiles;
+  int t = (int)(f0 - fr * ntiles);
+  Cursor cur = cursor_at(fr, a);
+  bool bonus = false;
+  const raw* row = row_at<raw>(cur, fr, a, &bonus);
+  Raw<DT> x = {};
+  if (row) x = load_raw<DT, VL>(row, a.V, t, lane);
+  uint32_t done = 0, bad = 0;
+  float m_l = -INFINITY, s_l = 0.0f;  // this lane's running max (z domain) and sum
   for (int64_t f = f0; f < f1; f++) {
-    const int64_t fr = f / a.ntiles;
-    const int64_t tile = f - fr * a.ntiles;
-    while (fr >= fr_end && g + 1 < a.ngroups) {  // next group
-      if (done) {
-        const uint32_t need = (uint32_t)((2 * G.kb + 1) * a.ntiles);
-        if (wave_add(a.gcount + g, done, lane) + done == need) on_group(g);
-        done = 0;
-      }
-      g++;
-      G = group_of(g, a.K, a.offsets, a.rows_d);
-      fr_end = G.fr0 + 2 * G.kb + 1;
+    // prefetch tile f + 1
+    const bool more = f + 1 < f1;
+    int64_t fr_n = fr;
+    int t_n = t + 1;
+    if (t_n == ntiles) {
+      t_n = 0;
+      fr_n++;
     }
-    const int64_t rr = fr - G.fr0;
-    const raw* row = nullptr;
-    if (G.ok && rr >= 0 && rr <= 2 * G.kb) {
-      if (rr <= G.kb) {
-        const int64_t tr = G.d0 + g + rr;
-        if (tr < a.rows_t) row = static_cast<const raw*>(a.target) + tr * a.V;
-      } else {
-        const int64_t dr = G.d0 + rr - G.kb - 1;
-        if (dr < a.rows_d) row = static_cast<const raw*>(a.draft) + dr * a.V;
-      }
+    Cursor nc = cur;
+    bool bonus_n = bonus;
+    const raw* row_n = row;
+    if (more && t_n == 0) {
+      nc = cursor_advance(cur, fr_n, a);
+      row_n = row_at<raw>(nc, fr_n, a, &bonus_n);
     }
-    if (row) {
-      float v[PER_LANE];
-      load_tile<DT, VL>(row, a.V, tile, lane, v);
-      const float2 pt = tile_partial(v, a.c);
-      if (lane == 0) a.part[f] = pt;
-    } else {
+    Raw<DT> xn = {};
+    if (more && row_n) xn = load_raw<DT, VL>(row_n, a.V, t_n, lane);
+    // reduce tile f
+    if (!row) {
       bad = FLAG_BAD_INPUT;
+    } else {
+      float v[PER_LANE];
+#pragma unroll
+      for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+        float q[DT::VEC];
+        unpack<DT>(x, ch, q);
+#pragma unroll
+        for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = q[k];
+      }
+      float tm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; e++) tm = fmaxf(tm, v[e]);
+      const bool seg_end = bonus || t == ntiles - 1 || f + 1 == f1;
+      if (bonus) {  // per-tile partial
+        m_l = -INFINITY;
+        s_l = 0.0f;
+      }
+      if (tm > m_l) {
+        if (m_l > -INFINITY) s_l *= __builtin_amdgcn_exp2f(m_l * c - tm * c);
+        m_l = tm;
+      }
+      if (m_l > -INFINITY) {
+        const float mc = m_l * c;
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < PER_LANE; e++) acc += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mc));
+        s_l += acc;
+      }
+      float2 pt = make_float2(-INFINITY, 0.0f);
+      if (seg_end) {
+        const float Mz = wave_max(m_l);
+        const float MC = Mz * c;
+        float sl = 0.0f;
+        if (m_l > -INFINITY) sl = s_l * __builtin_amdgcn_exp2f(m_l * c - MC);
+        pt = make_float2(Mz > -INFINITY ? MC : -INFINITY, wave_sum(sl));
+        m_l = -INFINITY;
+        s_l = 0.0f;
+      }
+      if (lane == 0) st_dev(a.part + f, pt);
     }
     done++;
-  }
-  if (done) {
-    const uint32_t need = (uint32_t)((2 * G.kb + 1) * a.ntiles);
-    if (wave_add(a.gcount + g, done, lane) + done == need) on_group(g);
+    if (!more || nc.g != cur.g) {
+      const uint32_t need = (uint32_t)((2 * cur.G.kb + 1) * ntiles);
+      if (wave_add(a.gcount + cur.g * CSTRIDE, done, lane) + done == need) on_group(cur.g);
+      done = 0;
+    }
+    x = xn;
+    cur = nc;
+    row = row_n;
+    bonus = bonus_n;
+    fr = fr_n;
+    t = t_n;
   }
   if (lane == 0) raise_flags(a.flags, bad);
 }
@@ -368,7 +556,7 @@ __global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
     }
     if (lane == 0) {
       a.num_accepted[b] = n;
-      a.s.gcount[b] = 0;  // every phase-A wavefront of b has counted
+      st_dev(a.s.gcount + b * CSTRIDE, 0u);  // every phase-A wavefront of b has counted
     }
     if (n == kb) {
       const RowStat sk = stat_of(sM[wib], sS[wib], kb);
@@ -377,17 +565,16 @@ __global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
                                           a.uniforms[t0 + kb], lane, &fl);
       if (lane == 0) {
         a.final_token[b] = y;
-        store_release(a.dec + b, DEC_BONUS);
+        st_dev(a.dec + b * CSTRIDE, DEC_BONUS);
       }
     } else {
       if (lane == 0) {
-        SdDecision d;
-        d.Mt = sM[wib][n];
-        d.St = sS[wib][n];
-        d.Md = sM[wib][kb + 1 + n];
-        d.Sd = sS[wib][kb + 1 + n];
-        rec[b] = d;
-        store_release(a.dec + b, (uint32_t)n + 1u);
+        st_dev(&rec[b].Mt, sM[wib][n]);
+        st_dev(&rec[b].St, sS[wib][n]);
+        st_dev(&rec[b].Md, sM[wib][kb + 1 + n]);
+        st_dev(&rec[b].Sd, sS[wib][kb + 1 + n]);
+        stores_done();
+        st_dev(a.dec + b * CSTRIDE, (uint32_t)n + 1u);
       }
     }
   };
@@ -403,8 +590,10 @@ __global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
     const Group G = group_of(b, a.s.K, a.s.offsets, a.s.rows_d);
     uint32_t d = 0;
     if (G.ok) {
-      while ((d = load_acquire(a.dec + b)) == 0) {
-        __builtin_amdgcn_s_sleep(4);
+      int nap = 1;  // backoff: polls of one flag by many wavefronts share a memory channel
+      while ((d = ld_dev(a.dec + b * CSTRIDE)) == 0) {
+        for (int z = 0; z < nap; z++) __builtin_amdgcn_s_sleep(2);
+        nap = min(2 * nap, 16);
         if (wall_clock64() > t_end) {
           fl |= FLAG_SPIN_TIMEOUT;
           break;
@@ -416,24 +605,34 @@ __global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
     const bool residual = d != 0 && d != DEC_BONUS;
     const int n = residual ? (int)d - 1 : 0;
     const int64_t t0 = G.d0 + b;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     SdDecision dd{};
+    float st = 0.0f, sd = 0.0f;
     if (residual) {
-      dd = rec[b];
-      float vt[PER_LANE], vd[PER_LANE], r[PER_LANE];
-      load_tile<DT, VL>(target + (t0 + n) * V, V, tile, lane, vt);
-      load_tile<DT, VL>(draft + (G.d0 + n) * V, V, tile, lane, vd);
-      residual_weights(vt, vd, dd.Mt, dd.Md, c, (float)(1.0 / dd.St), (float)(1.0 / dd.Sd), r);
+      dd.Mt = ld_dev(&rec[b].Mt);
+      dd.St = ld_dev(&rec[b].St);
+      dd.Md = ld_dev(&rec[b].Md);
+      dd.Sd = ld_dev(&rec[b].Sd);
+      st = (float)(1.0 / dd.St);
+      sd = (float)(1.0 / dd.Sd);
+      const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tile, lane);
+      const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tile, lane);
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < PER_LANE; e++) s += r[e];
+      for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+        float r[DT::VEC];
+        residual_chunk<DT>(rt, rd, ch, dd.Mt, dd.Md, c, st, sd, r);
+#pragma unroll
+        for (int k = 0; k < DT::VEC; k++) s += r[k];
+      }
       s = wave_sum(s);
-      if (lane == 0) a.rmass[slot] = s;
+      if (lane == 0) st_dev(a.rmass + slot, s);
     }
-    if (wave_add(a.rcount + b, 1u, lane) + 1u != (uint32_t)ntiles) continue;
+    if (wave_add(a.rcount + b * CSTRIDE, 1u, lane) + 1u != (uint32_t)ntiles) continue;
     // last slot of sequence b
     if (residual) {
       const float* rm = a.rmass + b * ntiles;
-      auto weight = [&](int t) -> double { return (double)rm[t]; };
+      auto weight = [&](int t) -> double { return (double)ld_dev(rm + t); };
       const float u = a.uniforms[t0 + G.kb];
       double before = 0.0, total = 0.0;
       int last_tile = -1;
@@ -442,21 +641,19 @@ __global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
       if (!(total > 0.0)) {
         // p_n and q_n agree to rounding: draw from p_n with the same uniform
         fl |= FLAG_ZERO_RESIDUAL;
-        RowStat st;
-        st.M = dd.Mt;
-        st.S = dd.St;
-        st.ok = true;
-        y = draw_from_row<DT, VL>(target + (t0 + n) * V, V, a.s.part + (G.fr0 + n) * ntiles, ntiles, st, c, u,
-                                  lane, &fl);
+        RowStat rs;
+        rs.M = dd.Mt;
+        rs.S = dd.St;
+        rs.ok = true;
+        y = draw_scan_row<DT, VL>(target + (t0 + n) * V, V, ntiles, rs, c, u, lane, &fl);
       } else {
         const int tt = t >= 0 ? t : last_tile;
-        float vt[PER_LANE], vd[PER_LANE], r[PER_LANE];
-        load_tile<DT, VL>(target + (t0 + n) * V, V, tt, lane, vt);
-        load_tile<DT, VL>(draft + (G.d0 + n) * V, V, tt, lane, vd);
-        residual_weights(vt, vd, dd.Mt, dd.Md, c, (float)(1.0 / dd.St), (float)(1.0 / dd.Sd), r);
+        const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tt, lane);
+        const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tt, lane);
+        auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, dd.Mt, dd.Md, c, st, sd, w); };
         int last_pos = -1, idx = -1;
-        if (t >= 0) idx = tile_search<DT>(r, (float)((double)u * total - before), lane, &last_pos);
-        else tile_search<DT>(r, INFINITY, lane, &last_pos);
+        if (t >= 0) idx = tile_search<DT>(wfn, (float)((double)u * total - before), lane, &last_pos);
+        else tile_search<DT>(wfn, INFINITY, lane, &last_pos);
         if (idx < 0) {
           fl |= FLAG_CDF_CLAMP;
           idx = last_pos >= 0 ? last_pos : 0;
@@ -469,8 +666,8 @@ __global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
       a.num_accepted[b] = 0;
     }
     if (lane == 0) {  // every slot of b has read its decision
-      a.rcount[b] = 0;
-      a.dec[b] = 0;
+      st_dev(a.rcount + b * CSTRIDE, 0u);
+      st_dev(a.dec + b * CSTRIDE, 0u);
     }
   }
   for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
@@ -503,7 +700,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
     const int64_t base = p * N;
     double M = -INFINITY;
     for (int k0 = 0; k0 < N; k0 += WAVE)
-      if (k0 + lane < N) M = fmax(M, (double)a.ws_logw[base + k0 + lane]);
+      if (k0 + lane < N) M = fmax(M, (double)ld_dev(a.ws_logw + base + k0 + lane));
     M = wave_max_f64(M);
     const bool zero = !(M > -INFINITY);
     if (M == INFINITY || M != M) fl |= FLAG_NONFINITE;
@@ -512,7 +709,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
     if (!zero) {
       for (int k0 = 0; k0 < N; k0 += WAVE) {
         const int k = k0 + lane;
-        const double wk = k < N ? exp((double)a.ws_logw[base + k] - M) : 0.0;
+        const double wk = k < N ? exp((double)ld_dev(a.ws_logw + base + k) - M) : 0.0;
         Sw += wave_sum_f64(wk);
         Sw2 += wave_sum_f64(wk * wk);
         int lp = wk > 0.0 ? k : -1;
@@ -531,7 +728,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
     int carry = 0;  // first slot of the chunk's first particle
     for (int k0 = 0; k0 < N; k0 += WAVE) {
       const int i = k0 + lane;
-      const float lw = i < N ? a.ws_logw[base + i] : 0.0f;
+      const float lw = i < N ? ld_dev(a.ws_logw + base + i) : 0.0f;
       int lo, hi;  // particle i supplies the slots [lo, hi)
       if (do_res) {
         // slot k descends from the first i with C_i > (u + k) / N, so particle i
@@ -574,7 +771,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
     if (lane == 0) {
       a.ess[p] = (float)E;
       a.resampled[p] = do_res ? 1 : 0;
-      a.pcount[p] = 0;
+      st_dev(a.pcount + p * CSTRIDE, 0u);
     }
   };
 
@@ -610,10 +807,10 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
                                         a.bonus_u[i], lane, &fl);
     if (lane == 0) {
       a.bonus_token[i] = y;
-      a.ws_logw[i] = lw;
-      a.s.gcount[i] = 0;
+      st_dev(a.ws_logw + i, lw);
+      st_dev(a.s.gcount + i * CSTRIDE, 0u);
     }
-    if (wave_add(a.pcount + i / N, 1u, lane) + 1u == (uint32_t)N) resample(i / N);
+    if (wave_add(a.pcount + (i / N) * CSTRIDE, 1u, lane) + 1u == (uint32_t)N) resample(i / N);
   };
 
   stream_phase<DT, VL>(a.s, w, nw, lane, particle);

@@ -136,3 +136,18 @@ def test_sd_workspace_reuse():
         t = compare_sd(c, run_sd_oracle(c), na.cpu().numpy(), ft.cpu().numpy(), f"reuse {i}")
         t.assert_ok()
         assert int(fl.item()) & ~8 == 0
+
+
+def test_sd_zero_residual_fallback():
+    """Identical rows and an accept uniform of exactly 1.0 (outside the
+    documented range, but defined on both sides): the test rejects, the residual
+    mass is exactly 0 and the final token is drawn from p_n instead."""
+    from gpu_util import check_sd, run_sd_gpu
+
+    c = sd_case(21, 6, 9000, T=1.0, K=3, delta=0.0, dtype="bf16")
+    for b in (0, 2, 5):
+        c["uniforms"][b * 4 + (b % 3)] = 1.0
+    na, _, fl = run_sd_gpu(c)
+    assert fl & 2
+    assert [int(na[b]) for b in (0, 2, 5)] == [0, 2, 2]
+    check_sd(c, "zero residual")
