@@ -109,10 +109,11 @@ enum {
 #define SMCSD_ABI_VERSION 1
 #define SMCSD_MAX_K 128    /* largest draft length per sequence / particle      */
 #define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
+#define SMCSD_MAX_V 524288 /* largest vocabulary                                 */
 #define SMCSD_WORKSPACE_ALIGN 256
 /* The first bytes of every workspace hold counters only (shape independent),
-   one 64-byte line each: sd_verify needs B <= 21845, smc_reweight_resample
-   P*N + P <= 65536. */
+   one 64-byte line each: sd_verify needs B <= 65535, smc_reweight_resample
+   P <= 65536. */
 #define SMCSD_WORKSPACE_COUNTER_BYTES (4u << 20)
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
@@ -133,7 +134,7 @@ size_t sd_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t K, int32_t V,
  *
  *   dtype            SMCSD_F32 or SMCSD_BF16 (both logit tensors).
  *   B, K, V          sequences, largest draft length, vocabulary size.
- *                    0 <= K <= SMCSD_MAX_K, V >= 1.
+ *                    0 <= K <= SMCSD_MAX_K, 1 <= V <= SMCSD_MAX_V.
  *   temperature      T > 0 and finite.
  *   target_logits    [R_t, V], R_t = total_draft_rows + B.  Sequence b's K_b + 1
  *                    target rows start at row t0_b = d0_b + b.

@@ -32,43 +32,40 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
 constexpr size_t kCounterBytes = SMCSD_WORKSPACE_COUNTER_BYTES;
 
 struct SdLayout {
-  size_t gcount, dec, rcount, rec, rmass, part, total;
+  size_t rcount, rmass, tokz, part, total;
 };
 
 // every counter occupies its own 64-byte line
 constexpr size_t kCounterLine = 64;
 
-bool sd_counters_fit(int64_t B) { return 3 * align_up(kCounterLine * (size_t)B) <= kCounterBytes; }
+// one counter per sequence; sequences are also the grid's y dimension
+bool sd_counters_fit(int64_t B) { return B <= 65535 && align_up(kCounterLine * (size_t)B) <= kCounterBytes; }
 
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
   SdLayout l;
-  l.gcount = 0;
-  l.dec = align_up(l.gcount + kCounterLine * (size_t)B);
-  l.rcount = align_up(l.dec + kCounterLine * (size_t)B);
-  l.rec = kCounterBytes;
-  l.rmass = align_up(l.rec + 24 * (size_t)B);
-  l.part = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
+  l.rcount = 0;
+  l.rmass = kCounterBytes;
+  l.tokz = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
+  l.part = align_up(l.tokz + sizeof(float) * (size_t)(2 * rows_d + B));
   l.total = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
   return l;
 }
 
 struct SmcLayout {
-  size_t gcount, pcount, ws_logw, part, total;
+  size_t pcount, ws_logw, tokz, part, total;
 };
 
-bool smc_counters_fit(int64_t P, int64_t N) {
-  return align_up(kCounterLine * (size_t)(P * N)) + align_up(kCounterLine * (size_t)P) <= kCounterBytes;
-}
+bool smc_counters_fit(int64_t P) { return align_up(kCounterLine * (size_t)P) <= kCounterBytes; }
 
 SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   const int nt = ntiles_of(V);
   const int64_t PN = (int64_t)P * N;
   SmcLayout l;
-  l.gcount = 0;
-  l.pcount = align_up(kCounterLine * (size_t)PN);
+  l.pcount = 0;
   l.ws_logw = kCounterBytes;
-  l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
+  l.tokz = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
+  l.part = align_up(l.tokz + sizeof(float) * (size_t)(PN * (2 * K + 1)));
   l.total = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
   return l;
 }
@@ -108,6 +105,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
                   void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
   if (B < 0 || K < 0 || V < 1 || !temperature_ok(temperature)) return SMCSD_ERR_INVALID_ARG;
+  if (V > SMCSD_MAX_V) return SMCSD_ERR_UNSUPPORTED;
   if (K > SMCSD_MAX_K || !sd_counters_fit(B)) return SMCSD_ERR_UNSUPPORTED;
   if (total_draft_rows < 0 || total_draft_rows > (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
   if (!draft_offsets && total_draft_rows != (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
@@ -118,7 +116,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  smcsd::SdFusedArgs a;
+  smcsd::SdTailArgs a;
   a.s.target = target_logits;
   a.s.draft = draft_logits;
   a.s.offsets = draft_offsets;
@@ -131,13 +129,11 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   a.s.total_tiles = (2 * total_draft_rows + B) * (int64_t)a.s.ntiles;
   a.s.c = (float)(1.4426950408889634 / (double)temperature);
   a.s.part = reinterpret_cast<float2*>(ws + l.part);
-  a.s.gcount = reinterpret_cast<uint32_t*>(ws + l.gcount);
+  a.s.tokz = reinterpret_cast<float*>(ws + l.tokz);
+  a.s.tokens = draft_tokens;
   a.s.flags = status_flags;
-  a.tokens = draft_tokens;
   a.uniforms = uniforms;
-  a.dec = reinterpret_cast<uint32_t*>(ws + l.dec);
   a.rcount = reinterpret_cast<uint32_t*>(ws + l.rcount);
-  a.rec = ws + l.rec;
   a.rmass = reinterpret_cast<float*>(ws + l.rmass);
   a.num_accepted = num_accepted;
   a.final_token = final_token;
@@ -166,7 +162,8 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   if (P < 0 || N < 1 || K < 0 || V < 1 || pages_per_particle < 0) return SMCSD_ERR_INVALID_ARG;
   if (!temperature_ok(temperature) || !isfinite(ess_frac) || ess_frac < 0.0f)
     return SMCSD_ERR_INVALID_ARG;
-  if (K > SMCSD_MAX_K || N > SMCSD_MAX_N || !smc_counters_fit(P, N)) return SMCSD_ERR_UNSUPPORTED;
+  if (K > SMCSD_MAX_K || N > SMCSD_MAX_N || V > SMCSD_MAX_V || !smc_counters_fit(P))
+    return SMCSD_ERR_UNSUPPORTED;
   if (P == 0) return SMCSD_OK;
   if (!target_logits || !bonus_uniforms || !resample_uniforms || !log_weights || !bonus_token ||
       !ancestors || !ess || !resampled)
@@ -184,7 +181,7 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  smcsd::SmcFusedArgs a;
+  smcsd::SmcTailArgs a;
   a.s.target = target_logits;
   a.s.draft = draft_logits;
   a.s.offsets = nullptr;
@@ -197,12 +194,12 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   a.s.total_tiles = PN * (2 * K + 1) * (int64_t)a.s.ntiles;
   a.s.c = (float)(1.4426950408889634 / (double)temperature);
   a.s.part = reinterpret_cast<float2*>(ws + l.part);
-  a.s.gcount = reinterpret_cast<uint32_t*>(ws + l.gcount);
+  a.s.tokz = reinterpret_cast<float*>(ws + l.tokz);
+  a.s.tokens = draft_tokens;
   a.s.flags = status_flags;
   a.N = N;
   a.L = pages_per_particle;
   a.ess_frac = ess_frac;
-  a.tokens = draft_tokens;
   a.bonus_u = bonus_uniforms;
   a.resample_u = resample_uniforms;
   a.logw_in = log_weights;

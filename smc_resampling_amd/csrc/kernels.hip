@@ -1,38 +1,32 @@
-// kernels.hip -- the fused HIP kernels (gfx950) of the verify-and-sample step.
+// kernels.hip -- HIP kernels (gfx950) of the verify-and-sample step.
 //
-// One launch per library call.  The grid is persistent and no larger than the
-// device holds at once, so every workgroup is resident for the whole launch.
+// Each library call launches two kernels on the caller's stream.
 //
-// Phase A (both kernels): the logit rows are laid out group by group (a group
-// is an SD sequence or an SMC particle; its rows are target rows 0..K_b, then
-// draft rows 0..K_b-1) and cut into 2048-logit tiles.  Each wavefront streams a
-// contiguous range of tiles, stores the softmax partial (max, sum of
-// exponentials) of each, and adds the number of tiles it finished to its
-// group's counter.  The wavefront that completes a group's count handles that
-// group next.
+// k_stream (both operations): the logit rows are laid out group by group (a
+// group is an SD sequence or an SMC particle; its rows are target rows
+// 0..K_b, then draft rows 0..K_b-1) and cut into 2048-logit tiles.  Each
+// wavefront streams a contiguous range of tiles with the next tiles' loads in
+// flight, and stores softmax partials (max, sum of exponentials) and the logit
+// of each row's draft token.  It is the only kernel that reads the logit
+// stream, and it holds nothing else, so it runs at full occupancy.
 //
-// sd_verify ("Faster LLM Inference via Sequential Monte Carlo", sec. 1;
-// variable lengths as in "PACER", Methodik):
-//   decider   (last phase-A wavefront of a sequence): merges the partials into
-//             row statistics, tests u_j < p_j(x_j) / q_j(x_j) up to the first
-//             rejection n.  n = K_b: draws the bonus token from p_{K_b} (tile
-//             located from the partials, then searched) and is done.
-//             n < K_b: publishes n and the statistics of the rejected pair.
-//   residual  one slot per tile of every sequence: waits (bounded) for the
-//             decision; if a draft was rejected, stores the tile's mass of
-//             max(0, p_n - q_n).  The last slot of a sequence to arrive
-//             locates u * (total mass) among the tile masses and finishes the
-//             inverse-CDF draw inside that tile.
-// smc_reweight_resample (same page, sec. 2 steps 3-4; sec. 3):
-//   particle  (last phase-A wavefront of a particle): log-weight increment
-//             sum_j log p_j(x_j) - log q_j(x_j), and the (K+1)-th token drawn
-//             from p_K.
-//   prompt    (last particle of a prompt): Kish ESS, threshold, systematic
-//             resampling, page-table rows gathered by ancestor.
-// No wavefront waits on anything in the SMC kernel.
+// k_sd_tail (sd_verify; "Faster LLM Inference via Sequential Monte Carlo",
+// sec. 1; variable lengths as in "PACER", Methodik): one workgroup per
+// (sequence, 4 tiles).  Each merges its sequence's partials into row
+// statistics and tests u_j < p_j(x_j) / q_j(x_j) up to the first rejection n
+// (every workgroup of a sequence reaches the same decision).  n = K_b: the
+// workgroup whose tiles hold u * (total mass) of p_{K_b} draws the bonus token.
+// n < K_b: each wavefront stores the mass of max(0, p_n - q_n) over its tile;
+// the last workgroup of the sequence to finish locates the tile that holds
+// u * (total mass) and draws the token inside it.
 //
-// Counters and flags live in the caller's workspace; each call returns them to
-// zero, so the workspace must be zero-filled once before its first use.
+// k_smc_tail (smc_reweight_resample; same page, sec. 2 steps 3-4; sec. 3): one
+// wavefront per particle: log-weight increment sum_j log p_j(x_j) - log
+// q_j(x_j) and the (K+1)-th token drawn from p_K; the last particle of a
+// prompt to finish computes the Kish ESS, resamples systematically when it is
+// below the threshold, and gathers the page-table rows by ancestor.
+//
+// Counters live in the caller's workspace and every call returns them to zero.
 #include <map>
 #include <mutex>
 
@@ -42,9 +36,6 @@
 namespace smcsd {
 
 constexpr int MAXR = 2 * SMCSD_MAX_K + 1;     // rows per group
-constexpr uint32_t DEC_BONUS = 0xFFFFFFFFu;   // decision: every draft accepted
-// bounded waits: give up after this many ticks of the 100 MHz wall clock
-constexpr uint64_t kSpinTicks = 50000000ull;  // 0.5 s
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -130,28 +121,39 @@ __device__ __forceinline__ double row16_sum(double v) {
   return v + dpp_f64<DPP_ROR8>(v);
 }
 
-// Row statistics of `nrows` consecutive rows of partials (one wavefront; 16
-// lanes per row, 4 rows at a time) into the wavefront's LDS slice: M = max of
-// the partials' mc (log2 domain), S = sum of s * 2^(mc - M).
-__device__ __forceinline__ void merge_group_rows(const float2* __restrict__ part, int nrows, int ntiles, float c,
-                                        float* sM, double* sS, int lane) {
-  const int sub = lane & 15;
-  for (int r0 = 0; r0 < nrows; r0 += 4) {
-    const int r = r0 + (lane >> 4);
+// reductions inside each quad of lanes; every lane receives its quad's result
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));
+  return fmaxf(v, dpp_f32<DPP_QUAD_2301>(v));
+}
+__device__ __forceinline__ double quad_sum(double v) {
+  v += dpp_f64<DPP_QUAD_1032>(v);
+  return v + dpp_f64<DPP_QUAD_2301>(v);
+}
+
+// Row statistics of `nrows` consecutive rows of partials into the
+// wavefront's LDS slice (one wavefront; 4 lanes per row, 16 rows per pass, so
+// a group of up to 16 rows is merged after a single round of loads):
+// M = max of the partials' mc (log2 domain), S = sum of s * 2^(mc - M).
+__device__ __forceinline__ void merge_group_rows(const float2* __restrict__ part, int nrows, int ntiles,
+                                                 float* sM, double* sS, int lane) {
+  const int sub = lane & 3;
+  for (int r0 = 0; r0 < nrows; r0 += WAVE / 4) {
+    const int r = r0 + (lane >> 2);
     const bool live = r < nrows;
     const float2* pr = part + (int64_t)(live ? r : 0) * ntiles;
     float m = -INFINITY;
     if (live)
-      for (int t = sub; t < ntiles; t += 16) m = fmaxf(m, ld_dev(pr + t).x);
-    const float M = row16_max(m);
-    double s = 0.0;
+      for (int t = sub; t < ntiles; t += 4) m = fmaxf(m, pr[t].x);
+    const float M = quad_max(m);
+    double acc = 0.0;
     if (live && M != -INFINITY) {
-      for (int t = sub; t < ntiles; t += 16) {
-        const float2 pt = ld_dev(pr + t);
-        if (pt.x != -INFINITY) s += (double)pt.y * exp2((double)pt.x - (double)M);
+      for (int t = sub; t < ntiles; t += 4) {
+        const float2 pt = pr[t];
+        if (pt.x != -INFINITY) acc += (double)pt.y * exp2((double)pt.x - (double)M);
       }
     }
-    const double S = row16_sum(s);
+    const double S = quad_sum(acc);
     if (live && sub == 0) {
       sM[r] = M;
       sS[r] = S;
@@ -185,58 +187,65 @@ __device__ __forceinline__ void residual_chunk(const Raw<DT>& rt, const Raw<DT>&
   }
 }
 
-// Wave-level search over per-tile weights W_t (t < ntiles) in ascending tile
-// order: the first tile whose inclusive prefix exceeds u * total, and the
+// Wave-level search over per-tile weights W_t (t < ntiles <= 256) in ascending
+// tile order: the first tile whose inclusive prefix exceeds u * total, and the
 // prefix before it; -1 (with the last tile of positive weight in *last_tile)
-// when rounding leaves no such tile.
+// when rounding leaves no such tile.  Each weight is read once.
+constexpr int kMaxTileChunks = 4;  // ntiles <= 256, i.e. V <= 524288
+
 template <typename WFN>
 __device__ __forceinline__ int locate_tile(int ntiles, WFN weight, double u, int lane, double* before,
-                                  double* total_out, int* last_tile) {
+                                           double* total_out, int* last_tile) {
+  double incl[kMaxTileChunks], W[kMaxTileChunks];
   double total = 0.0;
   int lastt = -1;
-  for (int t0 = 0; t0 < ntiles; t0 += WAVE) {
-    const int t = t0 + lane;
-    const double W = t < ntiles ? weight(t) : 0.0;
-    const double incl = wave_incl_scan_f64(W, lane);
-    total += __shfl(incl, WAVE - 1, WAVE);
-    int lt = W > 0.0 ? t : -1;
+#pragma unroll
+  for (int k = 0; k < kMaxTileChunks; k++) {
+    const int t = k * WAVE + lane;
+    W[k] = t < ntiles ? weight(t) : 0.0;
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxTileChunks; k++) {
+    incl[k] = total + wave_incl_scan_f64(W[k], lane);
+    total = __shfl(incl[k], WAVE - 1, WAVE);
+    int lt = W[k] > 0.0 ? k * WAVE + lane : -1;
     for (int off = 32; off >= 1; off >>= 1) lt = max(lt, __shfl_xor(lt, off, WAVE));
     if (lt >= 0) lastt = lt;
   }
   *total_out = total;
   *last_tile = lastt;
   const double target = u * total;
-  double run = 0.0;
-  for (int t0 = 0; t0 < ntiles; t0 += WAVE) {
-    const int t = t0 + lane;
-    const double W = t < ntiles ? weight(t) : 0.0;
-    const double incl = wave_incl_scan_f64(W, lane);
-    const uint64_t bal = __ballot(run + incl > target);
+#pragma unroll
+  for (int k = 0; k < kMaxTileChunks; k++) {
+    const uint64_t bal = __ballot(incl[k] > target);
     if (bal) {
       const int src = __builtin_ctzll(bal);
-      *before = run + __shfl(incl - W, src, WAVE);
-      return t0 + src;
+      *before = __shfl(incl[k] - W[k], src, WAVE);
+      return k * WAVE + src;
     }
-    run += __shfl(incl, WAVE - 1, WAVE);
   }
   return -1;
 }
 
 // Inverse-CDF draw from the softmax of `row` (statistics rs, tile partials
 // `part`) with uniform u.  One wavefront.
+// Inverse-CDF draw from the softmax of `row` (statistics rs, per-tile
+// partials `part`) with uniform u.  One wavefront.  Returns -1 when the
+// located tile lies outside [tb, tb + tn) (another workgroup holds it).
 template <typename DT, bool VL>
 __device__ __forceinline__ int draw_from_row(const typename DT::raw* __restrict__ row, int64_t V,
-                             const float2* __restrict__ part, int ntiles, const RowStat& rs, float c,
-                             float u, int lane, uint32_t* fl) {
+                                             const float2* __restrict__ part, int ntiles, const RowStat& rs,
+                                             float c, float u, int lane, uint32_t* fl, int tb, int tn) {
   auto weight = [&](int t) -> double {
-    const float2 pt = ld_dev(part + t);
+    const float2 pt = part[t];
     return pt.x == -INFINITY ? 0.0 : (double)pt.y * exp2((double)pt.x - (double)rs.M);
   };
   double before = 0.0, total = 0.0;
   int last_tile = -1;
   const int t = locate_tile(ntiles, weight, (double)u, lane, &before, &total, &last_tile);
   const int tt = t >= 0 ? t : (last_tile >= 0 ? last_tile : ntiles - 1);
-  const float mt = ld_dev(part + tt).x;
+  if (tt < tb || tt >= tb + tn) return -1;
+  const float mt = part[tt].x;
   const Raw<DT> raw = load_raw<DT, VL>(row, V, tt, lane);
   auto wfn = [&](int ch, float (&w)[DT::VEC]) {
     unpack<DT>(raw, ch, w);
@@ -394,60 +403,89 @@ __device__ __forceinline__ const raw* row_at(const Cursor& c, int64_t fr, const 
   return dr < a.rows_d ? static_cast<const raw*>(a.draft) + dr * a.V : nullptr;
 }
 
-// Phase A of wavefront w of nw: stream tiles [f0, f1), the next tile's loads
-// in flight while the current one is reduced.  A partial is (mc, s) with
-// s = sum 2^(z c - mc) over its logits, in the log2 domain x = z c.  Each lane
-// keeps a running (max, sum) over the tiles of one row and the wavefront
-// reduces it once, into the partial slot of the segment's last tile; the other
-// tiles of the segment get an empty partial.  Tiles of a group's bonus row
-// get their own partials (the bonus draw locates its tile from them).
-// on_group(g) runs (wave-uniform) when this wavefront completes g's count.
-template <typename DT, bool VL, typename ONGROUP>
-__device__ __forceinline__ void stream_phase(const StreamArgs& a, int64_t w, int64_t nw, int lane,
-                                             ONGROUP on_group) {
+
+// ---------------------------------------------------------------------------
+// k_stream: softmax partials and token logits of every tile
+// ---------------------------------------------------------------------------
+// Wavefront w of nw streams tiles [f0, f1) with PF tiles' loads in flight
+// while one is reduced.  A partial is (mc, s) with s = sum 2^(z c - mc) over
+// its logits, in the log2 domain x = z c.  Each lane keeps a running (max, sum)
+// over the tiles of one row and the wavefront reduces it once, into the
+// partial slot of the segment's last tile; the other tiles of the segment get
+// an empty partial.  Tiles of a group's bonus row (its last target row) get
+// their own partials, which the bonus draw uses to locate its tile.  The
+// wavefront that streams the tile holding a row's draft token also stores
+// that logit in tokz[row].
+template <typename DT, bool VL, int PF>
+__global__ __launch_bounds__(BLOCK) void k_stream(StreamArgs a) {
   using raw = typename DT::raw;
+  const int lane = threadIdx.x % WAVE;
+  const int64_t w = (int64_t)blockIdx.x * WAVES_PER_BLOCK + threadIdx.x / WAVE;
+  const int64_t nw = (int64_t)gridDim.x * WAVES_PER_BLOCK;
   const int64_t f0 = w * a.total_tiles / nw, f1 = (w + 1) * a.total_tiles / nw;
   if (f0 >= f1) return;
   const int ntiles = a.ntiles;
   const float c = a.c;
-  int64_t fr = f0 / ntiles;
-  int t = (int)(f0 - fr * ntiles);
-  Cursor cur = cursor_at(fr, a);
-  bool bonus = false;
-  const raw* row = row_at<raw>(cur, fr, a, &bonus);
-  Raw<DT> x = {};
-  if (row) x = load_raw<DT, VL>(row, a.V, t, lane);
-  uint32_t done = 0, bad = 0;
+  const int64_t fr_first = f0 / ntiles;
+  const int t_first = (int)(f0 - fr_first * ntiles);
+  // load cursor: issues the loads of tile f + PF while tile f is reduced
+  int64_t lfr = fr_first;
+  int lt = t_first;
+  Cursor lc = cursor_at(lfr, a);
+  auto fetch = [&]() {
+    if (lt == 0) lc = cursor_advance(lc, lfr, a);
+    bool bonus = false;
+    const raw* row = row_at<raw>(lc, lfr, a, &bonus);
+    Raw<DT> x = {};
+    if (row) x = load_raw<DT, VL>(row, a.V, lt, lane);
+    if (++lt == ntiles) {
+      lt = 0;
+      lfr++;
+    }
+    return x;
+  };
+  Raw<DT> q[PF + 1];
+#pragma unroll
+  for (int i = 0; i <= PF; i++) q[i] = f0 + i < f1 ? fetch() : Raw<DT>{};
+  // reduce cursor: the row of the tile being reduced
+  int64_t fr = fr_first;
+  int t = t_first;
+  Cursor rc = lc;
+  rc = cursor_at(fr, a);
+  bool bonus = false, valid = false;
+  int tok_tile = -1;  // tile of this row that holds its draft token, if this wavefront streams it
+  float tok_z = 0.0f;
+  auto enter_row = [&]() {  // row fr starts (or the range starts inside it)
+    rc = cursor_advance(rc, fr, a);
+    const raw* row = row_at<raw>(rc, fr, a, &bonus);
+    valid = row != nullptr;
+    tok_tile = -1;
+    if (valid && !bonus) {
+      const int64_t rr = fr - rc.G.fr0;
+      const int32_t tok = a.tokens[rc.G.d0 + (rr <= rc.G.kb ? rr : rr - rc.G.kb - 1)];
+      const int64_t ft = fr * ntiles + tok / TILE;
+      if (tok >= 0 && tok < a.V && ft >= f0 && ft < f1) {  // load it now, store it with its tile
+        tok_tile = tok / TILE;
+        tok_z = DT::to_f32(row[tok]);
+      }
+    }
+  };
+  enter_row();
+  uint32_t bad = 0;
   float m_l = -INFINITY, s_l = 0.0f;  // this lane's running max (z domain) and sum
   for (int64_t f = f0; f < f1; f++) {
-    // prefetch tile f + 1
-    const bool more = f + 1 < f1;
-    int64_t fr_n = fr;
-    int t_n = t + 1;
-    if (t_n == ntiles) {
-      t_n = 0;
-      fr_n++;
-    }
-    Cursor nc = cur;
-    bool bonus_n = bonus;
-    const raw* row_n = row;
-    if (more && t_n == 0) {
-      nc = cursor_advance(cur, fr_n, a);
-      row_n = row_at<raw>(nc, fr_n, a, &bonus_n);
-    }
-    Raw<DT> xn = {};
-    if (more && row_n) xn = load_raw<DT, VL>(row_n, a.V, t_n, lane);
-    // reduce tile f
-    if (!row) {
-      bad = FLAG_BAD_INPUT;
-    } else {
+    const Raw<DT> cur = q[0];
+#pragma unroll
+    for (int i = 0; i < PF; i++) q[i] = q[i + 1];
+    if (f + PF + 1 < f1) q[PF] = fetch();
+    if (valid) {
       float v[PER_LANE];
 #pragma unroll
       for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-        float q[DT::VEC];
-        unpack<DT>(x, ch, q);
+        float u8[DT::VEC];
+        unpack<DT>(cur, ch, u8);
 #pragma unroll
-        for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = q[k];
+        for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = u8[k];
       }
       float tm = -INFINITY;
 #pragma unroll
@@ -478,75 +516,71 @@ __device__ __forceinline__ void stream_phase(const StreamArgs& a, int64_t w, int
         m_l = -INFINITY;
         s_l = 0.0f;
       }
-      if (lane == 0) st_dev(a.part + f, pt);
+      if (lane == 0) {
+        a.part[f] = pt;
+        if (t == tok_tile) a.tokz[fr] = tok_z;
+      }
+    } else {
+      bad = FLAG_BAD_INPUT;
     }
-    done++;
-    if (!more || nc.g != cur.g) {
-      const uint32_t need = (uint32_t)((2 * cur.G.kb + 1) * ntiles);
-      if (wave_add(a.gcount + cur.g * CSTRIDE, done, lane) + done == need) on_group(cur.g);
-      done = 0;
+    if (++t == ntiles) {
+      t = 0;
+      fr++;
+      if (f + 1 < f1) enter_row();
     }
-    x = xn;
-    cur = nc;
-    row = row_n;
-    bonus = bonus_n;
-    fr = fr_n;
-    t = t_n;
   }
   if (lane == 0) raise_flags(a.flags, bad);
 }
 
 // ---------------------------------------------------------------------------
-// sd_verify: one fused kernel
+// k_sd_tail: decision and final token.  grid = (ceil(ntiles / 4), B)
 // ---------------------------------------------------------------------------
-struct SdDecision {  // published by the decider of a sequence that rejected a draft
-  float Mt, Md;
-  double St, Sd;
-};
-
 template <typename DT, bool VL>
-__global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
+__global__ __launch_bounds__(BLOCK) void k_sd_tail(SdTailArgs a) {
   using raw = typename DT::raw;
-  __shared__ float sM[WAVES_PER_BLOCK][MAXR];
-  __shared__ double sS[WAVES_PER_BLOCK][MAXR];
+  __shared__ float sM[MAXR];
+  __shared__ double sS[MAXR];
+  __shared__ int sN;
+  __shared__ uint32_t sFlags;
+  __shared__ int sLast;
   const int lane = threadIdx.x % WAVE;
-  const int wib = threadIdx.x / WAVE;
-  const int64_t w = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wib;
-  const int64_t nw = (int64_t)gridDim.x * WAVES_PER_BLOCK;
+  const int wave = threadIdx.x / WAVE;
+  const int64_t b = blockIdx.y;
   const raw* target = static_cast<const raw*>(a.s.target);
   const raw* draft = static_cast<const raw*>(a.s.draft);
   const int ntiles = a.s.ntiles;
   const float c = a.s.c;
   const int64_t V = a.s.V;
-  uint32_t fl = 0;
-  SdDecision* rec = reinterpret_cast<SdDecision*>(a.rec);
-
-  // ---- decider: merge, accept test, bonus draw or publish the rejection ----
-  auto decide = [&](int64_t b) {
-    const Group G = group_of(b, a.s.K, a.s.offsets, a.s.rows_d);
-    if (!G.ok) {  // malformed CSR offsets: nothing of this sequence is read
-      fl |= FLAG_BAD_INPUT;
-      return;
+  const Group G = group_of(b, a.s.K, a.s.offsets, a.s.rows_d);
+  if (!G.ok) {  // malformed CSR offsets: nothing of this sequence is read
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      raise_flags(a.s.flags, FLAG_BAD_INPUT);
+      a.num_accepted[b] = 0;
+      a.final_token[b] = 0;
     }
-    const int kb = G.kb;
-    const int64_t t0 = G.d0 + b;
-    const float2* pg = a.s.part + G.fr0 * ntiles;
-    merge_group_rows(pg, 2 * kb + 1, ntiles, c, sM[wib], sS[wib], lane);
+    return;
+  }
+  const int kb = G.kb;
+  const int64_t t0 = G.d0 + b;
+  const float2* pg = a.s.part + G.fr0 * ntiles;
+  uint32_t fl = 0;
+  if (wave == 0) {
+    merge_group_rows(pg, 2 * kb + 1, ntiles, sM, sS, lane);
     int n = kb;
     for (int j0 = 0; j0 < kb; j0 += WAVE) {
       const int j = j0 + lane;
       bool reject = false;
       if (j < kb) {
-        const int32_t x = a.tokens[G.d0 + j];
-        const RowStat st = stat_of(sM[wib], sS[wib], j);
-        const RowStat sd = stat_of(sM[wib], sS[wib], kb + 1 + j);
+        const int32_t x = a.s.tokens[G.d0 + j];
+        const RowStat st = stat_of(sM, sS, j);
+        const RowStat sd = stat_of(sM, sS, kb + 1 + j);
         if (!st.ok || !sd.ok) fl |= FLAG_NONFINITE;
         if (x < 0 || x >= V) {
           fl |= FLAG_BAD_INPUT;
           reject = true;
         } else {
-          const float zt = DT::to_f32(target[(t0 + j) * V + x]);
-          const float zd = DT::to_f32(draft[(G.d0 + j) * V + x]);
+          const float zt = a.s.tokz[G.fr0 + j];
+          const float zd = a.s.tokz[G.fr0 + kb + 1 + j];
           const double rho = exp(log_prob(zt, st, c) - log_prob(zd, sd, c));
           reject = !((double)a.uniforms[t0 + j] < rho);
         }
@@ -554,149 +588,150 @@ __global__ __launch_bounds__(BLOCK) void k_sd_fused(SdFusedArgs a) {
       const uint64_t bal = __ballot(reject);
       if (bal && n == kb) n = j0 + __builtin_ctzll(bal);
     }
+    for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
     if (lane == 0) {
-      a.num_accepted[b] = n;
-      st_dev(a.s.gcount + b * CSTRIDE, 0u);  // every phase-A wavefront of b has counted
-    }
-    if (n == kb) {
-      const RowStat sk = stat_of(sM[wib], sS[wib], kb);
-      if (!sk.ok) fl |= FLAG_NONFINITE;
-      const int y = draw_from_row<DT, VL>(target + (t0 + kb) * V, V, pg + (int64_t)kb * ntiles, ntiles, sk, c,
-                                          a.uniforms[t0 + kb], lane, &fl);
-      if (lane == 0) {
-        a.final_token[b] = y;
-        st_dev(a.dec + b * CSTRIDE, DEC_BONUS);
-      }
-    } else {
-      if (lane == 0) {
-        st_dev(&rec[b].Mt, sM[wib][n]);
-        st_dev(&rec[b].St, sS[wib][n]);
-        st_dev(&rec[b].Md, sM[wib][kb + 1 + n]);
-        st_dev(&rec[b].Sd, sS[wib][kb + 1 + n]);
-        stores_done();
-        st_dev(a.dec + b * CSTRIDE, (uint32_t)n + 1u);
-      }
-    }
-  };
-
-  stream_phase<DT, VL>(a.s, w, nw, lane, decide);
-
-  // ---- residual slots: one per (sequence, tile) ----------------------------
-  const int64_t nslots = a.s.ngroups * ntiles;
-  const uint64_t t_end = wall_clock64() + kSpinTicks;  // one deadline for every wait of this wavefront
-  for (int64_t slot = w; slot < nslots; slot += nw) {
-    const int64_t b = slot / ntiles;
-    const int tile = (int)(slot - b * ntiles);
-    const Group G = group_of(b, a.s.K, a.s.offsets, a.s.rows_d);
-    uint32_t d = 0;
-    if (G.ok) {
-      int nap = 1;  // backoff: polls of one flag by many wavefronts share a memory channel
-      while ((d = ld_dev(a.dec + b * CSTRIDE)) == 0) {
-        for (int z = 0; z < nap; z++) __builtin_amdgcn_s_sleep(2);
-        nap = min(2 * nap, 16);
-        if (wall_clock64() > t_end) {
-          fl |= FLAG_SPIN_TIMEOUT;
-          break;
-        }
-      }
-    } else {
-      fl |= FLAG_BAD_INPUT;
-    }
-    const bool residual = d != 0 && d != DEC_BONUS;
-    const int n = residual ? (int)d - 1 : 0;
-    const int64_t t0 = G.d0 + b;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    SdDecision dd{};
-    float st = 0.0f, sd = 0.0f;
-    if (residual) {
-      dd.Mt = ld_dev(&rec[b].Mt);
-      dd.St = ld_dev(&rec[b].St);
-      dd.Md = ld_dev(&rec[b].Md);
-      dd.Sd = ld_dev(&rec[b].Sd);
-      st = (float)(1.0 / dd.St);
-      sd = (float)(1.0 / dd.Sd);
-      const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tile, lane);
-      const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tile, lane);
-      float s = 0.0f;
-#pragma unroll
-      for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-        float r[DT::VEC];
-        residual_chunk<DT>(rt, rd, ch, dd.Mt, dd.Md, c, st, sd, r);
-#pragma unroll
-        for (int k = 0; k < DT::VEC; k++) s += r[k];
-      }
-      s = wave_sum(s);
-      if (lane == 0) st_dev(a.rmass + slot, s);
-    }
-    if (wave_add(a.rcount + b * CSTRIDE, 1u, lane) + 1u != (uint32_t)ntiles) continue;
-    // last slot of sequence b
-    if (residual) {
-      const float* rm = a.rmass + b * ntiles;
-      auto weight = [&](int t) -> double { return (double)ld_dev(rm + t); };
-      const float u = a.uniforms[t0 + G.kb];
-      double before = 0.0, total = 0.0;
-      int last_tile = -1;
-      const int t = locate_tile(ntiles, weight, (double)u, lane, &before, &total, &last_tile);
-      int y;
-      if (!(total > 0.0)) {
-        // p_n and q_n agree to rounding: draw from p_n with the same uniform
-        fl |= FLAG_ZERO_RESIDUAL;
-        RowStat rs;
-        rs.M = dd.Mt;
-        rs.S = dd.St;
-        rs.ok = true;
-        y = draw_scan_row<DT, VL>(target + (t0 + n) * V, V, ntiles, rs, c, u, lane, &fl);
-      } else {
-        const int tt = t >= 0 ? t : last_tile;
-        const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tt, lane);
-        const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tt, lane);
-        auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, dd.Mt, dd.Md, c, st, sd, w); };
-        int last_pos = -1, idx = -1;
-        if (t >= 0) idx = tile_search<DT>(wfn, (float)((double)u * total - before), lane, &last_pos);
-        else tile_search<DT>(wfn, INFINITY, lane, &last_pos);
-        if (idx < 0) {
-          fl |= FLAG_CDF_CLAMP;
-          idx = last_pos >= 0 ? last_pos : 0;
-        }
-        y = tt * TILE + idx;
-      }
-      if (lane == 0) a.final_token[b] = y;
-    } else if (d == 0 && lane == 0) {
-      a.final_token[b] = 0;  // malformed sequence or timeout: unspecified
-      a.num_accepted[b] = 0;
-    }
-    if (lane == 0) {  // every slot of b has read its decision
-      st_dev(a.rcount + b * CSTRIDE, 0u);
-      st_dev(a.dec + b * CSTRIDE, 0u);
+      sN = n;
+      sFlags = fl;
     }
   }
-  for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
-  if (lane == 0) raise_flags(a.s.flags, fl);
+  __syncthreads();
+  const int n = sN;
+  fl = 0;
+  const float u = a.uniforms[t0 + kb];
+  const int tile = blockIdx.x * WAVES_PER_BLOCK + wave;
+  if (n == kb) {
+    // bonus draw from p_{K_b}: only the workgroup holding the located tile draws
+    if (wave == 0) {
+      const RowStat sk = stat_of(sM, sS, kb);
+      if (!sk.ok) fl |= FLAG_NONFINITE;
+      const int y = draw_from_row<DT, VL>(target + (t0 + kb) * V, V, pg + (int64_t)kb * ntiles, ntiles, sk, c, u,
+                                          lane, &fl, (int)blockIdx.x * WAVES_PER_BLOCK, WAVES_PER_BLOCK);
+      if (lane == 0) {
+        if (y >= 0) a.final_token[b] = y;
+        if (blockIdx.x == 0) a.num_accepted[b] = n;
+        raise_flags(a.s.flags, fl | (blockIdx.x == 0 ? sFlags : 0u));
+      }
+    }
+    return;
+  }
+  // residual mass of max(0, p_n - q_n) over this wavefront's tile
+  const RowStat st = stat_of(sM, sS, n), sd = stat_of(sM, sS, kb + 1 + n);
+  const float stf = (float)(1.0 / st.S), sdf = (float)(1.0 / sd.S);
+  if (tile < ntiles) {
+    const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tile, lane);
+    const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tile, lane);
+    float s = 0.0f;
+#pragma unroll
+    for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+      float r[DT::VEC];
+      residual_chunk<DT>(rt, rd, ch, st.M, sd.M, c, stf, sdf, r);
+#pragma unroll
+      for (int k = 0; k < DT::VEC; k++) s += r[k];
+    }
+    s = wave_sum(s);
+    if (lane == 0) st_dev(a.rmass + b * ntiles + tile, s);
+  }
+  stores_done();  // every wavefront's mass is stored before the workgroup counts it
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t mine = (uint32_t)min(WAVES_PER_BLOCK, ntiles - (int)blockIdx.x * WAVES_PER_BLOCK);
+    const uint32_t old = __hip_atomic_fetch_add(a.rcount + b * CSTRIDE, mine, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    sLast = old + mine == (uint32_t)ntiles;
+    if (blockIdx.x == 0) {
+      a.num_accepted[b] = n;
+      raise_flags(a.s.flags, sFlags);
+    }
+  }
+  __syncthreads();
+  if (!sLast || wave != 0) return;
+  // last workgroup of sequence b: locate the tile, then draw inside it
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const float* rm = a.rmass + b * ntiles;
+  auto weight = [&](int t) -> double { return (double)ld_dev(rm + t); };
+  double before = 0.0, total = 0.0;
+  int last_tile = -1;
+  const int t = locate_tile(ntiles, weight, (double)u, lane, &before, &total, &last_tile);
+  int y;
+  if (!(total > 0.0)) {
+    // p_n and q_n agree to rounding: draw from p_n with the same uniform
+    fl |= FLAG_ZERO_RESIDUAL;
+    y = draw_scan_row<DT, VL>(target + (t0 + n) * V, V, ntiles, st, c, u, lane, &fl);
+  } else {
+    const int tt = t >= 0 ? t : last_tile;
+    const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tt, lane);
+    const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tt, lane);
+    auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, st.M, sd.M, c, stf, sdf, w); };
+    int last_pos = -1, idx = -1;
+    if (t >= 0) idx = tile_search<DT>(wfn, (float)((double)u * total - before), lane, &last_pos);
+    else tile_search<DT>(wfn, INFINITY, lane, &last_pos);
+    if (idx < 0) {
+      fl |= FLAG_CDF_CLAMP;
+      idx = last_pos >= 0 ? last_pos : 0;
+    }
+    y = tt * TILE + idx;
+  }
+  if (lane == 0) {
+    a.final_token[b] = y;
+    st_dev(a.rcount + b * CSTRIDE, 0u);  // every workgroup of b has counted
+    raise_flags(a.s.flags, fl);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// smc_reweight_resample: one fused kernel
+// k_smc_tail: one wavefront per particle, then per prompt.  grid = ceil(P N / 4)
 // ---------------------------------------------------------------------------
 template <typename DT, bool VL>
-__global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
+__global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcTailArgs a) {
   using raw = typename DT::raw;
   __shared__ float sM[WAVES_PER_BLOCK][MAXR];
   __shared__ double sS[WAVES_PER_BLOCK][MAXR];
   const int lane = threadIdx.x % WAVE;
   const int wib = threadIdx.x / WAVE;
-  const int64_t w = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wib;
-  const int64_t nw = (int64_t)gridDim.x * WAVES_PER_BLOCK;
+  const int64_t i = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wib;
+  if (i >= a.s.ngroups) return;
   const raw* target = static_cast<const raw*>(a.s.target);
-  const raw* draft = static_cast<const raw*>(a.s.draft);
   const int ntiles = a.s.ntiles;
   const float c = a.s.c;
   const int64_t V = a.s.V;
   const int K = a.s.K;
   const int N = a.N;
   uint32_t fl = 0;
-
-  // ---- prompt: ESS, threshold, systematic resampling, page-table gather ----
-  auto resample = [&](int64_t p) {
+  // ---- particle: reweight and the (K+1)-th token ---------------------------
+  const int64_t t0 = i * (K + 1), d0 = i * K, fr0 = i * (2 * K + 1);
+  const float2* pg = a.s.part + fr0 * ntiles;
+  merge_group_rows(pg, 2 * K + 1, ntiles, sM[wib], sS[wib], lane);
+  double delta = 0.0;
+  for (int j0 = 0; j0 < K; j0 += WAVE) {
+    const int j = j0 + lane;
+    double dj = 0.0;
+    if (j < K) {
+      const int32_t x = a.s.tokens[d0 + j];
+      const RowStat st = stat_of(sM[wib], sS[wib], j);
+      const RowStat sd = stat_of(sM[wib], sS[wib], K + 1 + j);
+      if (!st.ok || !sd.ok) fl |= FLAG_NONFINITE;
+      if (x < 0 || x >= V) {
+        fl |= FLAG_BAD_INPUT;
+      } else {
+        dj = log_prob(a.s.tokz[fr0 + j], st, c) - log_prob(a.s.tokz[fr0 + K + 1 + j], sd, c);
+      }
+    }
+    delta += wave_sum_f64(dj);
+  }
+  const RowStat sk = stat_of(sM[wib], sS[wib], K);
+  if (!sk.ok) fl |= FLAG_NONFINITE;
+  const float lw = (float)((double)a.logw_in[i] + delta);
+  if (lw != lw || lw == INFINITY) fl |= FLAG_NONFINITE;
+  const int y = draw_from_row<DT, VL>(target + (t0 + K) * V, V, pg + (int64_t)K * ntiles, ntiles, sk, c,
+                                      a.bonus_u[i], lane, &fl, 0, ntiles);
+  if (lane == 0) {
+    a.bonus_token[i] = y;
+    st_dev(a.ws_logw + i, lw);
+  }
+  const int64_t p = i / N;
+  if (wave_add(a.pcount + p * CSTRIDE, 1u, lane) + 1u == (uint32_t)N) {
+    // ---- prompt: ESS, threshold, systematic resampling, page-table gather ----
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int64_t base = p * N;
     double M = -INFINITY;
     for (int k0 = 0; k0 < N; k0 += WAVE)
@@ -727,34 +762,33 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
     double run = 0.0;
     int carry = 0;  // first slot of the chunk's first particle
     for (int k0 = 0; k0 < N; k0 += WAVE) {
-      const int i = k0 + lane;
-      const float lw = i < N ? ld_dev(a.ws_logw + base + i) : 0.0f;
-      int lo, hi;  // particle i supplies the slots [lo, hi)
+      const int ii = k0 + lane;
+      const float lwi = ii < N ? ld_dev(a.ws_logw + base + ii) : 0.0f;
+      int hi;  // particle ii supplies the slots [lo, hi)
       if (do_res) {
         // slot k descends from the first i with C_i > (u + k) / N, so particle i
         // receives k in [ceil(N C_{i-1} - u), ceil(N C_i - u)); consecutive
         // ranges share their end points, so every slot is covered exactly once
-        const double wi = i < N ? exp((double)lw - M) : 0.0;
+        const double wi = ii < N ? exp((double)lwi - M) : 0.0;
         const double incl = wave_incl_scan_f64(wi, lane);
-        const double Ci = (run + incl) / Sw;
-        double h = ceil((double)N * Ci - u);
-        if (i >= last_pos) {  // the last particle with positive weight ends at N
-          if (i == last_pos && h < (double)N) fl |= FLAG_CDF_CLAMP;
+        double h = ceil((double)N * ((run + incl) / Sw) - u);
+        if (ii >= last_pos) {  // the last particle with positive weight ends at N
+          if (ii == last_pos && h < (double)N) fl |= FLAG_CDF_CLAMP;
           h = (double)N;
         }
         hi = (int)fmin(fmax(h, 0.0), (double)N);
         run += __shfl(incl, WAVE - 1, WAVE);
       } else {
-        hi = i + 1;
+        hi = ii + 1;
       }
-      if (i >= N) hi = N;
-      int prev = __shfl_up(hi, 1, WAVE);
-      lo = lane == 0 ? carry : prev;
+      if (ii >= N) hi = N;
+      const int prev = __shfl_up(hi, 1, WAVE);
+      const int lo = lane == 0 ? carry : prev;
       hi = max(hi, lo);
       carry = __shfl(hi, WAVE - 1, WAVE);
-      if (i < N) {
-        for (int k = lo; k < hi; k++) a.ancestors[base + k] = i;
-        a.logw_out[base + i] = do_res ? 0.0f : lw;
+      if (ii < N) {
+        for (int k = lo; k < hi; k++) a.ancestors[base + k] = ii;
+        a.logw_out[base + ii] = do_res ? 0.0f : lwi;
       }
       if (gather) {
         // rows of the slots this chunk supplies, one wavefront-wide copy each
@@ -773,47 +807,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
       a.resampled[p] = do_res ? 1 : 0;
       st_dev(a.pcount + p * CSTRIDE, 0u);
     }
-  };
-
-  // ---- particle: reweight and the (K+1)-th token ---------------------------
-  auto particle = [&](int64_t i) {
-    const int64_t t0 = i * (K + 1), d0 = i * K;
-    const float2* pg = a.s.part + i * (2 * K + 1) * ntiles;
-    merge_group_rows(pg, 2 * K + 1, ntiles, c, sM[wib], sS[wib], lane);
-    double delta = 0.0;
-    for (int j0 = 0; j0 < K; j0 += WAVE) {
-      const int j = j0 + lane;
-      double dj = 0.0;
-      if (j < K) {
-        const int32_t x = a.tokens[d0 + j];
-        const RowStat st = stat_of(sM[wib], sS[wib], j);
-        const RowStat sd = stat_of(sM[wib], sS[wib], K + 1 + j);
-        if (!st.ok || !sd.ok) fl |= FLAG_NONFINITE;
-        if (x < 0 || x >= V) {
-          fl |= FLAG_BAD_INPUT;
-        } else {
-          const float zt = DT::to_f32(target[(t0 + j) * V + x]);
-          const float zd = DT::to_f32(draft[(d0 + j) * V + x]);
-          dj = log_prob(zt, st, c) - log_prob(zd, sd, c);
-        }
-      }
-      delta += wave_sum_f64(dj);
-    }
-    const RowStat sk = stat_of(sM[wib], sS[wib], K);
-    if (!sk.ok) fl |= FLAG_NONFINITE;
-    const float lw = (float)((double)a.logw_in[i] + delta);
-    if (lw != lw || lw == INFINITY) fl |= FLAG_NONFINITE;
-    const int y = draw_from_row<DT, VL>(target + (t0 + K) * V, V, pg + (int64_t)K * ntiles, ntiles, sk, c,
-                                        a.bonus_u[i], lane, &fl);
-    if (lane == 0) {
-      a.bonus_token[i] = y;
-      st_dev(a.ws_logw + i, lw);
-      st_dev(a.s.gcount + i * CSTRIDE, 0u);
-    }
-    if (wave_add(a.pcount + (i / N) * CSTRIDE, 1u, lane) + 1u == (uint32_t)N) resample(i / N);
-  };
-
-  stream_phase<DT, VL>(a.s, w, nw, lane, particle);
+  }
   for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
   if (lane == 0) raise_flags(a.s.flags, fl);
 }
@@ -822,7 +816,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_fused(SmcFusedArgs a) {
 // host launchers
 // ---------------------------------------------------------------------------
 // Workgroups of BLOCK threads the current device holds at once for `kernel`
-// (queried once per device and kernel).  The persistent grids never exceed it.
+// (queried once per device and kernel); the streaming grid is sized to it.
 static int resident_blocks(const void* kernel) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
@@ -838,35 +832,43 @@ static int resident_blocks(const void* kernel) {
   return cus * per_cu;
 }
 
-static unsigned grid_for(int64_t total_tiles, int resident) {
-  // enough wavefronts for one tile each, capped at what stays resident
-  int64_t blocks = (total_tiles + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
-  if (blocks > resident) blocks = resident;
-  return (unsigned)(blocks < 1 ? 1 : blocks);
-}
-
 template <typename DT, bool VL>
-static hipError_t launch_sd_t(const SdFusedArgs& a, hipStream_t s) {
-  const int resident = resident_blocks(reinterpret_cast<const void*>(&k_sd_fused<DT, VL>));
+static hipError_t launch_stream_t(const StreamArgs& a, hipStream_t s) {
+  constexpr int PF = DT::VEC == 8 ? 2 : 1;  // tiles in flight beyond the one being reduced
+  const void* k = reinterpret_cast<const void*>(&k_stream<DT, VL, PF>);
+  const int resident = resident_blocks(k);
   if (resident <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((k_sd_fused<DT, VL>), dim3(grid_for(a.s.total_tiles, resident)), dim3(BLOCK), 0, s, a);
+  int64_t blocks = (a.total_tiles + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
+  if (blocks > resident) blocks = resident;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((k_stream<DT, VL, PF>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_sd(const SdFusedArgs& a, bool bf16, bool vec, hipStream_t s) {
+template <typename DT, bool VL>
+static hipError_t launch_sd_t(const SdTailArgs& a, hipStream_t s) {
+  hipError_t e = launch_stream_t<DT, VL>(a.s, s);
+  if (e != hipSuccess) return e;
+  const unsigned gx = (unsigned)((a.s.ntiles + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK);
+  hipLaunchKernelGGL((k_sd_tail<DT, VL>), dim3(gx, (unsigned)a.s.ngroups), dim3(BLOCK), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sd(const SdTailArgs& a, bool bf16, bool vec, hipStream_t s) {
   if (bf16) return vec ? launch_sd_t<Bf16, true>(a, s) : launch_sd_t<Bf16, false>(a, s);
   return vec ? launch_sd_t<F32, true>(a, s) : launch_sd_t<F32, false>(a, s);
 }
 
 template <typename DT, bool VL>
-static hipError_t launch_smc_t(const SmcFusedArgs& a, hipStream_t s) {
-  const int resident = resident_blocks(reinterpret_cast<const void*>(&k_smc_fused<DT, VL>));
-  if (resident <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL((k_smc_fused<DT, VL>), dim3(grid_for(a.s.total_tiles, resident)), dim3(BLOCK), 0, s, a);
+static hipError_t launch_smc_t(const SmcTailArgs& a, hipStream_t s) {
+  hipError_t e = launch_stream_t<DT, VL>(a.s, s);
+  if (e != hipSuccess) return e;
+  const unsigned g = (unsigned)((a.s.ngroups + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK);
+  hipLaunchKernelGGL((k_smc_tail<DT, VL>), dim3(g), dim3(BLOCK), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_smc(const SmcFusedArgs& a, bool bf16, bool vec, hipStream_t s) {
+hipError_t launch_smc(const SmcTailArgs& a, bool bf16, bool vec, hipStream_t s) {
   if (bf16) return vec ? launch_smc_t<Bf16, true>(a, s) : launch_smc_t<Bf16, false>(a, s);
   return vec ? launch_smc_t<F32, true>(a, s) : launch_smc_t<F32, false>(a, s);
 }

@@ -9,42 +9,40 @@
 
 namespace smcsd {
 
-// Phase A (tile streaming) of both kernels.
+// k_stream: softmax partials of every tile and the logit of each row's
+// draft token, for groups (SD sequences / SMC particles) laid out group-major.
 struct StreamArgs {
   const void* target;
   const void* draft;
   const int32_t* offsets;  // CSR over draft rows, or null (fixed K)
+  const int32_t* tokens;   // draft token of each draft row
   int64_t ngroups, rows_t, rows_d, V, total_tiles;
   int K, ntiles;
-  float c;           // log2(e) / T
-  float2* part;      // [total_tiles] softmax partial of each tile, group-major
-  uint32_t* gcount;  // [ngroups] tiles finished per group (zero between calls)
+  float c;         // log2(e) / T
+  float2* part;    // [total_tiles] partial (mc, s) of each tile, group-major
+  float* tokz;     // [rows] logit of each row's draft token, group-major rows
   uint32_t* flags;
 };
 
-struct SdFusedArgs {
+struct SdTailArgs {
   StreamArgs s;
-  const int32_t* tokens;
   const float* uniforms;
-  uint32_t* dec;     // [B] decision of each sequence (zero between calls)
-  uint32_t* rcount;  // [B] residual slots arrived (zero between calls)
-  void* rec;         // [B] statistics of the rejected pair
+  uint32_t* rcount;  // [B] tiles of residual mass stored (zero between calls)
   float* rmass;      // [B * ntiles] residual mass per tile
   int32_t* num_accepted;
   int32_t* final_token;
 };
 
-struct SmcFusedArgs {
+struct SmcTailArgs {
   StreamArgs s;
   int N, L;
   float ess_frac;
-  const int32_t* tokens;
   const float* bonus_u;
   const float* resample_u;
   const float* logw_in;
-  float* logw_out;    // same buffer as logw_in (each entry is read before it is written)
-  float* ws_logw;     // [P*N] reweighted log-weights
-  uint32_t* pcount;   // [P] particles finished per prompt (zero between calls)
+  float* logw_out;   // same buffer as logw_in (each entry is read before it is written)
+  float* ws_logw;    // [P*N] reweighted log-weights
+  uint32_t* pcount;  // [P] particles finished per prompt (zero between calls)
   const int32_t* pt_in;
   int32_t* pt_out;
   int32_t* bonus_token;
@@ -53,7 +51,7 @@ struct SmcFusedArgs {
   int32_t* resampled;
 };
 
-hipError_t launch_sd(const SdFusedArgs& a, bool bf16, bool vec, hipStream_t s);
-hipError_t launch_smc(const SmcFusedArgs& a, bool bf16, bool vec, hipStream_t s);
+hipError_t launch_sd(const SdTailArgs& a, bool bf16, bool vec, hipStream_t s);
+hipError_t launch_smc(const SmcTailArgs& a, bool bf16, bool vec, hipStream_t s);
 
 }  // namespace smcsd

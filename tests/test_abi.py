@@ -70,7 +70,7 @@ def _sd(s, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=2), 1), (dict(B=30000, K=0, rows_d=0), 2), (dict(T=0.0), 1), (dict(T=-1.0), 1), (dict(T=math.nan), 1), (dict(T=math.inf), 1),
+    (dict(dtype=2), 1), (dict(B=70000, K=0, rows_d=0), 2), (dict(T=0.0), 1), (dict(T=-1.0), 1), (dict(T=math.nan), 1), (dict(T=math.inf), 1),
     (dict(V=0), 1), (dict(B=-1), 1), (dict(K=-1), 1), (dict(K=300, rows_d=1200), 2), (dict(rows_d=7), 1),
     (dict(rows_d=9), 1), (dict(tgt=None), 1), (dict(u=None), 1), (dict(drf=None), 1), (dict(na=None), 1),
     (dict(ws=None), 3), (dict(wsb=16), 3), (dict(ws=FAKE + 8), 3), (dict(off=FAKE, rows_d=9), 1),
@@ -90,7 +90,7 @@ def _smc(s, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=5), 1), (dict(P=70, N=1000), 2), (dict(N=0), 1), (dict(P=-1), 1), (dict(T=0.0), 1), (dict(ess=-0.1), 1),
+    (dict(dtype=5), 1), (dict(P=70000, N=1), 2), (dict(N=0), 1), (dict(P=-1), 1), (dict(T=0.0), 1), (dict(ess=-0.1), 1),
     (dict(ess=math.nan), 1), (dict(N=2000), 2), (dict(K=257), 2), (dict(lw=None), 1), (dict(ur=None), 1),
     (dict(pti=FAKE, pto=FAKE + 64, L=4), 1), (dict(pti=FAKE, pto=None, L=4), 1), (dict(ws=None), 3),
     (dict(wsb=100), 3), (dict(P=0, tgt=None), 0), (dict(L=-1), 1)])
