@@ -267,60 +267,6 @@ __device__ __forceinline__ int draw_from_row(const typename DT::raw* __restrict_
   return tt * TILE + idx;
 }
 
-// Inverse-CDF draw from the softmax of `row` without tile partials: one pass
-// for the tile masses (kept in registers, up to 64 tiles per lane), then the
-// located tile is searched.  Used only when the residual mass is zero.
-template <typename DT, bool VL>
-__device__ __forceinline__ int draw_scan_row(const typename DT::raw* __restrict__ row, int64_t V, int ntiles,
-                                             const RowStat& rs, float c, float u, int lane, uint32_t* fl) {
-  auto wfn_for = [&](const Raw<DT>& raw) {
-    return [&raw, &rs, c](int ch, float (&w)[DT::VEC]) {
-      unpack<DT>(raw, ch, w);
-#pragma unroll
-      for (int k = 0; k < DT::VEC; k++) w[k] = __builtin_amdgcn_exp2f(fmaf(w[k], c, -rs.M));
-    };
-  };
-  auto weight = [&](int t) -> double {
-    const Raw<DT> raw = load_raw<DT, VL>(row, V, t, lane);
-    auto wfn = wfn_for(raw);
-    float s = 0.0f;
-#pragma unroll
-    for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-      float w[DT::VEC];
-      wfn(ch, w);
-#pragma unroll
-      for (int k = 0; k < DT::VEC; k++) s += w[k];
-    }
-    return (double)wave_sum(s);
-  };
-  // tile masses, sequentially (the weight functor is wave-wide, not per lane)
-  double total = 0.0;
-  for (int t = 0; t < ntiles; t++) total += weight(t);
-  const double target = (double)u * total;
-  double run = 0.0;
-  int tt = -1, lastt = -1;
-  double before = 0.0;
-  for (int t = 0; t < ntiles; t++) {
-    const double W = weight(t);
-    if (W > 0.0) lastt = t;
-    if (run + W > target) {
-      tt = t;
-      before = run;
-      break;
-    }
-    run += W;
-  }
-  const int use = tt >= 0 ? tt : (lastt >= 0 ? lastt : ntiles - 1);
-  const Raw<DT> raw = load_raw<DT, VL>(row, V, use, lane);
-  int last_pos = -1;
-  int idx = tile_search<DT>(wfn_for(raw), tt >= 0 ? (float)(target - before) : INFINITY, lane, &last_pos);
-  if (idx < 0) {
-    *fl |= FLAG_CDF_CLAMP;
-    idx = last_pos >= 0 ? last_pos : 0;
-  }
-  return use * TILE + idx;
-}
-
 // ---------------------------------------------------------------------------
 // groups: layout of one SD sequence / SMC particle
 // ---------------------------------------------------------------------------
@@ -408,14 +354,13 @@ __device__ __forceinline__ const raw* row_at(const Cursor& c, int64_t fr, const 
 // k_stream: softmax partials and token logits of every tile
 // ---------------------------------------------------------------------------
 // Wavefront w of nw streams tiles [f0, f1) with PF tiles' loads in flight
-// while one is reduced.  A partial is (mc, s) with s = sum 2^(z c - mc) over
-// its logits, in the log2 domain x = z c.  Each lane keeps a running (max, sum)
-// over the tiles of one row and the wavefront reduces it once, into the
-// partial slot of the segment's last tile; the other tiles of the segment get
-// an empty partial.  Tiles of a group's bonus row (its last target row) get
-// their own partials, which the bonus draw uses to locate its tile.  The
-// wavefront that streams the tile holding a row's draft token also stores
-// that logit in tokz[row].
+// while one is reduced.  The partial of a tile is (MC, S): MC = max over the
+// tile of z c (log2 domain, c = log2(e) / T) and S = sum 2^(z c - MC), formed
+// from per-lane maxima and sums so that no exponential waits for a
+// wavefront-wide maximum.  It depends on the tile's logits alone, so equal rows
+// get bitwise equal statistics however the stream is divided.  The wavefront
+// that streams the tile holding a row's draft token also stores that logit in
+// tokz[row].
 template <typename DT, bool VL, int PF>
 __global__ __launch_bounds__(BLOCK) void k_stream(StreamArgs a) {
   using raw = typename DT::raw;
@@ -472,7 +417,6 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StreamArgs a) {
   };
   enter_row();
   uint32_t bad = 0;
-  float m_l = -INFINITY, s_l = 0.0f;  // this lane's running max (z domain) and sum
   for (int64_t f = f0; f < f1; f++) {
     const Raw<DT> cur = q[0];
 #pragma unroll
@@ -487,35 +431,20 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StreamArgs a) {
 #pragma unroll
         for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = u8[k];
       }
+      // this lane's max and sum of 2^(z c - mc_lane), then the wavefront's
+      // (MC, sum of s_lane 2^(mc_lane - MC)): a function of the tile alone
       float tm = -INFINITY;
 #pragma unroll
       for (int e = 0; e < PER_LANE; e++) tm = fmaxf(tm, v[e]);
-      const bool seg_end = bonus || t == ntiles - 1 || f + 1 == f1;
-      if (bonus) {  // per-tile partial
-        m_l = -INFINITY;
-        s_l = 0.0f;
-      }
-      if (tm > m_l) {
-        if (m_l > -INFINITY) s_l *= __builtin_amdgcn_exp2f(m_l * c - tm * c);
-        m_l = tm;
-      }
-      if (m_l > -INFINITY) {
-        const float mc = m_l * c;
-        float acc = 0.0f;
+      const float mcl = tm * c;
+      float sl = 0.0f;
+      if (tm > -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < PER_LANE; e++) acc += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mc));
-        s_l += acc;
+        for (int e = 0; e < PER_LANE; e++) sl += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mcl));
       }
-      float2 pt = make_float2(-INFINITY, 0.0f);
-      if (seg_end) {
-        const float Mz = wave_max(m_l);
-        const float MC = Mz * c;
-        float sl = 0.0f;
-        if (m_l > -INFINITY) sl = s_l * __builtin_amdgcn_exp2f(m_l * c - MC);
-        pt = make_float2(Mz > -INFINITY ? MC : -INFINITY, wave_sum(sl));
-        m_l = -INFINITY;
-        s_l = 0.0f;
-      }
+      const float MC = wave_max(mcl);
+      const float S = wave_sum(tm > -INFINITY ? sl * __builtin_amdgcn_exp2f(mcl - MC) : 0.0f);
+      const float2 pt = make_float2(MC, S);
       if (lane == 0) {
         a.part[f] = pt;
         if (t == tok_tile) a.tokz[fr] = tok_z;
@@ -656,7 +585,8 @@ __global__ __launch_bounds__(BLOCK) void k_sd_tail(SdTailArgs a) {
   if (!(total > 0.0)) {
     // p_n and q_n agree to rounding: draw from p_n with the same uniform
     fl |= FLAG_ZERO_RESIDUAL;
-    y = draw_scan_row<DT, VL>(target + (t0 + n) * V, V, ntiles, st, c, u, lane, &fl);
+    y = draw_from_row<DT, VL>(target + (t0 + n) * V, V, pg + (int64_t)n * ntiles, ntiles, st, c, u, lane, &fl, 0,
+                              ntiles);
   } else {
     const int tt = t >= 0 ? t : last_tile;
     const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tt, lane);

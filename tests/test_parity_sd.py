@@ -140,17 +140,16 @@ def test_sd_workspace_reuse():
 
 def test_sd_zero_residual_fallback():
     """Identical rows and an accept uniform of exactly 1.0 (outside the
-    documented range, but defined on both sides): the test rejects and p_n and
-    q_n agree, so the final token is drawn from p_n.  The oracle sees a residual
-    mass of exactly 0 and falls back to p_n; the kernel's row sums of two
-    identical rows may differ in the last bit (they are streamed in different
-    segments), leaving a residual that is a rounding-level multiple of p_n, or
-    exactly 0.  Both draw from p_n's shape; only the flag may differ."""
+    documented range, but defined on both sides): the test rejects, the residual
+    mass is exactly 0 (the kernel's row statistics depend on the row's logits
+    alone, so identical rows give identical probabilities) and the final token
+    is drawn from p_n instead."""
     from gpu_util import check_sd, run_sd_gpu
 
     c = sd_case(21, 6, 9000, T=1.0, K=3, delta=0.0, dtype="bf16")
     for b in (0, 2, 5):
         c["uniforms"][b * 4 + (b % 3)] = 1.0
     na, _, fl = run_sd_gpu(c)
+    assert fl & 2
     assert [int(na[b]) for b in (0, 2, 5)] == [0, 2, 2]
-    check_sd(c, "zero residual", ignore_flags=8 | 2)
+    check_sd(c, "zero residual")
