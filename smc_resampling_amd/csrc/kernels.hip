@@ -176,6 +176,9 @@ __device__ __forceinline__ RowStat stat_of(const float* sM, const double* sS, in
 template <typename DT>
 __device__ __forceinline__ void residual_chunk(const Raw<DT>& rt, const Raw<DT>& rd, int ch, float Mt, float Md,
                                                float c, float st, float sd, float (&r)[DT::VEC]) {
+  // p and q are rounded products: a fused multiply-subtract would keep one of
+  // them exact and make p - q nonzero for equal rows
+#pragma clang fp contract(off)
   float vt[DT::VEC], vd[DT::VEC];
   unpack<DT>(rt, ch, vt);
   unpack<DT>(rd, ch, vd);
