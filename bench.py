@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SLEEP_CYCLES = 100_000_000
 MALL_BYTES = 256 << 20
 
 
@@ -109,7 +110,7 @@ def main():
                 calls.append(call)
         return calls, outs
 
-    # ---------------- timing --------------------------------------------------
+    # ---------------- timing: whole calls --------------------------------------
     if args.launch == "graph":
         side = torch.cuda.Stream(device=dev)
         calls, outs = prepare(side.cuda_stream)
@@ -124,33 +125,57 @@ def main():
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(side):
-            torch.cuda.synchronize()
             ev0.record(side)
             graph.replay()
             ev1.record(side)
         torch.cuda.synchronize()
+        run_stream = side
     else:
-        stream = torch.cuda.current_stream(dev)
-        calls, outs = prepare(stream.cuda_stream)
+        run_stream = torch.cuda.current_stream(dev)
+        calls, outs = prepare(run_stream.cuda_stream)
         for c in calls[:W]:
             c()
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
+        torch.cuda._sleep(SLEEP_CYCLES)  # the host enqueues every call before the GPU reaches them
+        ev0.record(run_stream)
         for c in calls[W:]:
             c()
-        ev1.record(stream)
+        ev1.record(run_stream)
         torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
     flags = int(outs["status_flags"].item())
     ms_per_step = ms / steps
+
+    # ---------------- timing: the streaming kernel -------------------------------
+    # The same calls again, eagerly on the same stream, each bracketed by events,
+    # with an event recorded by the library between its streaming kernel and its
+    # decision kernel.  A sleep kernel first lets the host enqueue every call, so
+    # the GPU runs them back to back as in the graph.
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    with torch.cuda.stream(run_stream):
+        for e in ev_m:
+            e.record(run_stream)  # creates the event handle the library records into
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SLEEP_CYCLES)
+        for s_, c in enumerate(calls[W:]):
+            ev_a[s_].record(run_stream)
+            smcsd.mark_next_stream_phase(ev_m[s_])
+            c()
+            ev_b[s_].record(run_stream)
+    torch.cuda.synchronize()
+    stream_ms = float(np.mean([ev_a[i].elapsed_time(ev_m[i]) for i in range(steps)]))
+    tail_ms = float(np.mean([ev_m[i].elapsed_time(ev_b[i]) for i in range(steps)]))
     timed = [(W + s) % nb for s in range(steps)]
     pos_total = sum(positions[i] for i in timed)
     bytes_total = sum(nbytes[i] for i in timed)
     value = pos_total / (ms / 1e3)
-    achieved = bytes_total / steps / (ms_per_step / 1e3) / 1e9
+    achieved = bytes_total / steps / (stream_ms / 1e3) / 1e9
     log(f"[bench] {steps} steps in {ms:.3f} ms: {ms_per_step * 1e3:.2f} us/step, {value / 1e6:.2f} M positions/s, "
-        f"{achieved:.0f} GB/s algorithmic, flags={flags}")
+        f"{bytes_total / steps / (ms_per_step / 1e3) / 1e9:.0f} GB/s per call; k_stream {stream_ms * 1e3:.2f} us "
+        f"({achieved:.0f} GB/s), decision kernel {tail_ms * 1e3:.2f} us, flags={flags}")
 
     # ---------------- CPU oracle on a bounded sample --------------------------
     cpu = None
@@ -213,10 +238,11 @@ def main():
         "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "P": cfg.P, "N": cfg.N, "K": cfg.K,
                    "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T, "launch": args.launch,
                    "input_batches": nb, "status_flags": flags},
-        "roofline": {"bound": "hbm", "kernel": "k_sd_fused" if cfg.kind != "smc" else "k_smc_fused",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_step": bytes_total / steps,
-                     "bytes_per_element": e},
+        "roofline": {"bound": "hbm", "kernel": "k_stream", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": bytes_total / steps, "bytes_per_element": e,
+                     "kernel_us": stream_ms * 1e3, "decision_kernel_us": tail_ms * 1e3,
+                     "call_us": ms_per_step * 1e3},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

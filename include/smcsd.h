@@ -42,14 +42,16 @@
  * Memory and ordering:
  *   Every pointer is HIP device memory owned by the caller (for example the
  *   storage of a torch tensor) unless stated otherwise.  The library never
- *   allocates, frees or synchronises; each call enqueues one kernel on
- *   `stream` (a hipStream_t; NULL is the default stream) and returns.
+ *   allocates, frees or synchronises; each call enqueues two kernels on
+ *   `stream` (a hipStream_t; NULL is the default stream) and returns: one that
+ *   streams every logit once and one that turns the row statistics into
+ *   decisions.
  *   Outputs are valid once the stream reaches that point.
- *   The kernel is persistent: its grid is sized to what the device holds at
- *   once and its workgroups hand work to each other through counters in the
- *   workspace, with bounded waits.  Run one call at a time per device (other
- *   work on the device may delay it; a wait that gives up sets
- *   SMCSD_FLAG_SPIN_TIMEOUT).  Calls on one workspace must not overlap.
+ *   Inside the second kernel each sequence's (prompt's) last step is done by
+ *   whichever workgroup finishes its share last, counted in the workspace; no
+ *   workgroup ever waits for another, so a call completes however much of the
+ *   device it gets.  Calls on one
+ *   workspace must not overlap (on one stream they never do).
  *
  * Workspace:
  *   Caller-owned device scratch of at least the size the *_workspace_bytes()
@@ -57,8 +59,8 @@
  *   SMCSD_WORKSPACE_COUNTER_BYTES hold counters only; they must be zero before
  *   the first call and every call leaves them at zero, so one workspace serves
  *   any sequence of calls (of any shapes it is large enough for).  After a
- *   call that raised SMCSD_FLAG_BAD_INPUT or SMCSD_FLAG_SPIN_TIMEOUT, zero the
- *   counter bytes again before reuse.
+ *   call that raised SMCSD_FLAG_BAD_INPUT because of malformed CSR offsets,
+ *   zero the counter bytes again before reuse.
  *
  * Logits are row-major and contiguous: row r starts at element r * V.  bf16
  * logits are raw 16-bit bfloat16 patterns.
@@ -100,10 +102,9 @@ enum {
                                    resampling, ess = 0                                 */
   SMCSD_FLAG_CDF_CLAMP = 8,     /* rounding left no prefix above u * total; the last
                                    index with positive weight was taken               */
-  SMCSD_FLAG_BAD_INPUT = 16,    /* a draft token outside [0, V) or malformed CSR
-                                   offsets; that sequence's outputs are unspecified   */
-  SMCSD_FLAG_SPIN_TIMEOUT = 32  /* a bounded in-kernel wait gave up (the launch did not
-                                   get the whole device); outputs are unspecified     */
+  SMCSD_FLAG_BAD_INPUT = 16     /* a draft token outside [0, V) (that position is
+                                   rejected) or malformed CSR offsets (the outputs of
+                                   the sequences they describe are unspecified)       */
 };
 
 #define SMCSD_ABI_VERSION 1
@@ -112,8 +113,8 @@ enum {
 #define SMCSD_MAX_V 524288 /* largest vocabulary                                 */
 #define SMCSD_WORKSPACE_ALIGN 256
 /* The first bytes of every workspace hold counters only (shape independent),
-   one 64-byte line each: sd_verify needs B <= 65535, smc_reweight_resample
-   P <= 65536. */
+   one 64-byte line each: one per SD sequence or one per SMC prompt, so
+   sd_verify needs B <= 65535 and smc_reweight_resample P <= 65536. */
 #define SMCSD_WORKSPACE_COUNTER_BYTES (4u << 20)
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
@@ -121,6 +122,15 @@ int32_t smcsd_abi_version(void);
 
 /* Static, human-readable name of a status code. */
 const char* smcsd_status_string(int32_t status);
+
+/*
+ * Profiling aid for benchmarks: the next sd_verify or smc_reweight_resample
+ * call made by the calling thread records `event` (a hipEvent_t created by
+ * the caller, or NULL to cancel) on its stream between its logit-streaming
+ * kernel and its decision kernel, so that the streaming kernel can be timed
+ * with events.  The setting is per thread and used once.
+ */
+void smcsd_mark_next_stream_phase(void* event);
 
 /*
  * Workspace bytes sd_verify needs for these sizes (0 when B == 0).

@@ -17,7 +17,7 @@ __all__ = [
     "sd_verify", "smc_reweight_resample", "sd_verify_workspace_bytes", "smc_workspace_bytes",
     "prepare_sd_verify", "prepare_smc_reweight_resample", "status_string", "abi_version", "lib", "SmcsdError",
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "FLAG_ZERO_WEIGHTS", "FLAG_CDF_CLAMP", "FLAG_BAD_INPUT",
-    "FLAG_SPIN_TIMEOUT", "new_workspace",
+    "new_workspace", "mark_next_stream_phase",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(HERE, "libsmcsd.so")
 
 SMCSD_OK, SMCSD_ERR_INVALID_ARG, SMCSD_ERR_UNSUPPORTED, SMCSD_ERR_WORKSPACE, SMCSD_ERR_HIP = range(5)
 SMCSD_F32, SMCSD_BF16 = 0, 1
-FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT, FLAG_SPIN_TIMEOUT = 1, 2, 4, 8, 16, 32
+FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT = 1, 2, 4, 8, 16
 WORKSPACE_ALIGN = 256
 
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -33,6 +33,7 @@ _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctype
 _SIGNATURES = {
     "smcsd_abi_version": ([], _I32),
     "smcsd_status_string": ([_I32], ctypes.c_char_p),
+    "smcsd_mark_next_stream_phase": ([_P], None),
     "sd_verify_workspace_bytes": ([_I32, _I32, _I32, _I32, _I64], _SZ),
     "sd_verify": ([_I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
@@ -67,6 +68,12 @@ def lib():
 
 def abi_version() -> int:
     return _lib.smcsd_abi_version()
+
+
+def mark_next_stream_phase(event) -> None:
+    """Record ``event`` (a torch.cuda.Event) between the streaming kernel and
+    the decision kernel of this thread's next library call (benchmark aid)."""
+    _lib.smcsd_mark_next_stream_phase(None if event is None else event.cuda_event)
 
 
 def status_string(code: int) -> str:
@@ -123,8 +130,8 @@ def new_workspace(nbytes, device):
     """A zero-filled workspace of at least ``nbytes`` (plus alignment slack).
 
     Reuse it across calls of the same or smaller size; calls on one workspace
-    must not overlap.  Zero it again after a call that raised FLAG_BAD_INPUT or
-    FLAG_SPIN_TIMEOUT."""
+    must not overlap.  Zero it again after a call that raised FLAG_BAD_INPUT
+    for malformed CSR offsets."""
     return torch.zeros(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
 
 

@@ -28,55 +28,85 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
 // Workspace layouts.  The first SMCSD_WORKSPACE_COUNTER_BYTES of every
 // workspace hold only counters, whatever the shape of the call, so one
 // workspace can serve calls of different shapes: the counters are zero before
-// the first call and every call leaves them at zero.  Scratch data follows.
+// the first call and every call leaves them at zero.  Scratch data follows:
+// the segment partials (sized for one-tile segments, the most a call can
+// use) and, for SMC, the reweighted log-weights.
 constexpr size_t kCounterBytes = SMCSD_WORKSPACE_COUNTER_BYTES;
 
+// One counter line per SD sequence (the SD tail grid also has one row of
+// workgroups per sequence) or per SMC prompt.
+bool sd_counters_fit(int64_t B) { return B <= smcsd::CTR_LINES && B <= 65535; }
+bool smc_counters_fit(int64_t P) { return P <= smcsd::CTR_LINES; }
+
 struct SdLayout {
-  size_t rcount, rmass, tokz, part, total;
+  size_t rmass, part, total;
 };
-
-// every counter occupies its own 64-byte line
-constexpr size_t kCounterLine = 64;
-
-// one counter per sequence; sequences are also the grid's y dimension
-bool sd_counters_fit(int64_t B) { return B <= 65535 && align_up(kCounterLine * (size_t)B) <= kCounterBytes; }
 
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
   SdLayout l;
-  l.rcount = 0;
   l.rmass = kCounterBytes;
-  l.tokz = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
-  l.part = align_up(l.tokz + sizeof(float) * (size_t)(2 * rows_d + B));
+  l.part = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
   l.total = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
   return l;
 }
 
 struct SmcLayout {
-  size_t pcount, ws_logw, tokz, part, total;
+  size_t ws_logw, part, total;
 };
-
-bool smc_counters_fit(int64_t P) { return align_up(kCounterLine * (size_t)P) <= kCounterBytes; }
 
 SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   const int nt = ntiles_of(V);
   const int64_t PN = (int64_t)P * N;
   SmcLayout l;
-  l.pcount = 0;
   l.ws_logw = kCounterBytes;
-  l.tokz = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
-  l.part = align_up(l.tokz + sizeof(float) * (size_t)(PN * (2 * K + 1)));
+  l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
   l.total = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
   return l;
 }
 
+// Event recorded between the two kernels of this thread's next call (a
+// profiling aid; see smcsd_mark_next_stream_phase).
+thread_local hipEvent_t t_phase_mark = nullptr;
+
+hipEvent_t take_phase_mark() {
+  hipEvent_t e = t_phase_mark;
+  t_phase_mark = nullptr;
+  return e;
+}
+
 bool temperature_ok(float T) { return isfinite(T) && T > 0.0f; }
+
+void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, const void* draft,
+               const int32_t* offsets, const int32_t* tokens, int64_t ngroups, int64_t rows_t, int64_t rows_d,
+               int64_t V, int K, float T, char* ws, size_t part_off, uint32_t* flags) {
+  s->target = target;
+  s->draft = draft;
+  s->offsets = offsets;
+  s->tokens = tokens;
+  s->ngroups = ngroups;
+  s->rows_t = rows_t;
+  s->rows_d = rows_d;
+  s->V = V;
+  s->K = K;
+  s->ntiles = ntiles_of(V);
+  s->seg = plan.seg;
+  s->nseg = plan.nseg;
+  s->units = plan.units;
+  s->c = (float)(1.4426950408889634 / (double)T);
+  s->part = reinterpret_cast<float2*>(ws + part_off);
+  s->ctr = reinterpret_cast<uint32_t*>(ws);
+  s->flags = flags;
+}
+
 
 }  // namespace
 
 extern "C" {
 
 int32_t smcsd_abi_version(void) { return SMCSD_ABI_VERSION; }
+
+void smcsd_mark_next_stream_phase(void* event) { t_phase_mark = static_cast<hipEvent_t>(event); }
 
 const char* smcsd_status_string(int32_t s) {
   switch (s) {
@@ -115,30 +145,20 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   const SdLayout l = sd_layout(B, V, total_draft_rows);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
+  const bool bf16 = dtype == SMCSD_BF16;
+  const bool vec = vec_ok(dtype, V, target_logits, draft_logits);
+  const int64_t rows = 2 * total_draft_rows + B;
+  smcsd::Plan plan;
+  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
-  smcsd::SdTailArgs a;
-  a.s.target = target_logits;
-  a.s.draft = draft_logits;
-  a.s.offsets = draft_offsets;
-  a.s.ngroups = B;
-  a.s.rows_d = total_draft_rows;
-  a.s.rows_t = total_draft_rows + B;
-  a.s.V = V;
-  a.s.K = K;
-  a.s.ntiles = ntiles_of(V);
-  a.s.total_tiles = (2 * total_draft_rows + B) * (int64_t)a.s.ntiles;
-  a.s.c = (float)(1.4426950408889634 / (double)temperature);
-  a.s.part = reinterpret_cast<float2*>(ws + l.part);
-  a.s.tokz = reinterpret_cast<float*>(ws + l.tokz);
-  a.s.tokens = draft_tokens;
-  a.s.flags = status_flags;
+  smcsd::SdArgs a;
+  fill_step(&a.s, plan, target_logits, draft_logits, draft_offsets, draft_tokens, B, total_draft_rows + B,
+            total_draft_rows, V, K, temperature, ws, l.part, status_flags);
   a.uniforms = uniforms;
-  a.rcount = reinterpret_cast<uint32_t*>(ws + l.rcount);
   a.rmass = reinterpret_cast<float*>(ws + l.rmass);
   a.num_accepted = num_accepted;
   a.final_token = final_token;
-  const bool vec = vec_ok(dtype, V, target_logits, draft_logits);
-  return smcsd::launch_sd(a, dtype == SMCSD_BF16, vec, static_cast<hipStream_t>(stream)) == hipSuccess
+  return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_phase_mark()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;
 }
@@ -165,11 +185,11 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   if (K > SMCSD_MAX_K || N > SMCSD_MAX_N || V > SMCSD_MAX_V || !smc_counters_fit(P))
     return SMCSD_ERR_UNSUPPORTED;
   if (P == 0) return SMCSD_OK;
+  const int64_t PN = (int64_t)P * N;
   if (!target_logits || !bonus_uniforms || !resample_uniforms || !log_weights || !bonus_token ||
       !ancestors || !ess || !resampled)
     return SMCSD_ERR_INVALID_ARG;
   if (K > 0 && (!draft_logits || !draft_tokens)) return SMCSD_ERR_INVALID_ARG;
-  const int64_t PN = (int64_t)P * N;
   if (page_table_in && pages_per_particle > 0) {
     if (!page_table_out) return SMCSD_ERR_INVALID_ARG;
     const char* a0 = reinterpret_cast<const char*>(page_table_in);
@@ -180,40 +200,28 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   const SmcLayout l = smc_layout(P, N, K, V);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
+  const bool bf16 = dtype == SMCSD_BF16;
+  const bool vec = vec_ok(dtype, V, target_logits, K > 0 ? draft_logits : nullptr);
+  smcsd::Plan plan;
+  if (smcsd::plan_stream(PN * (2 * K + 1), ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
-  smcsd::SmcTailArgs a;
-  a.s.target = target_logits;
-  a.s.draft = draft_logits;
-  a.s.offsets = nullptr;
-  a.s.ngroups = PN;
-  a.s.rows_d = PN * K;
-  a.s.rows_t = PN * (K + 1);
-  a.s.V = V;
-  a.s.K = K;
-  a.s.ntiles = ntiles_of(V);
-  a.s.total_tiles = PN * (2 * K + 1) * (int64_t)a.s.ntiles;
-  a.s.c = (float)(1.4426950408889634 / (double)temperature);
-  a.s.part = reinterpret_cast<float2*>(ws + l.part);
-  a.s.tokz = reinterpret_cast<float*>(ws + l.tokz);
-  a.s.tokens = draft_tokens;
-  a.s.flags = status_flags;
+  smcsd::SmcArgs a;
+  fill_step(&a.s, plan, target_logits, draft_logits, nullptr, draft_tokens, PN, PN * (K + 1), PN * K, V, K,
+            temperature, ws, l.part, status_flags);
   a.N = N;
   a.L = pages_per_particle;
   a.ess_frac = ess_frac;
   a.bonus_u = bonus_uniforms;
   a.resample_u = resample_uniforms;
-  a.logw_in = log_weights;
-  a.logw_out = log_weights;
+  a.logw = log_weights;
   a.ws_logw = reinterpret_cast<float*>(ws + l.ws_logw);
-  a.pcount = reinterpret_cast<uint32_t*>(ws + l.pcount);
   a.pt_in = page_table_in;
   a.pt_out = page_table_out;
   a.bonus_token = bonus_token;
   a.ancestors = ancestors;
   a.ess = ess;
   a.resampled = resampled;
-  const bool vec = vec_ok(dtype, V, target_logits, K > 0 ? draft_logits : nullptr);
-  return smcsd::launch_smc(a, dtype == SMCSD_BF16, vec, static_cast<hipStream_t>(stream)) == hipSuccess
+  return smcsd::launch_smc(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_phase_mark()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;
 }

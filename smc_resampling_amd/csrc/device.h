@@ -23,7 +23,19 @@ constexpr int TILE = 2048;
 constexpr int PER_LANE = TILE / WAVE;  // 32 values per lane
 
 constexpr uint32_t FLAG_NONFINITE = 1, FLAG_ZERO_RESIDUAL = 2, FLAG_ZERO_WEIGHTS = 4,
-                   FLAG_CDF_CLAMP = 8, FLAG_BAD_INPUT = 16, FLAG_SPIN_TIMEOUT = 32;
+                   FLAG_CDF_CLAMP = 8, FLAG_BAD_INPUT = 16;
+
+// Index of the calling wavefront in its workgroup, as a value the compiler
+// knows to be the same across the wavefront (so branches on it stay scalar).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE); }
+
+// A 64-bit value the whole wavefront holds, as a value the compiler knows to be
+// uniform.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 struct Bf16 {
   using raw = uint16_t;
@@ -113,35 +125,71 @@ struct Raw {
   uint4 q[CHUNKS];
 };
 
-// Load tile `tile` of `row` (V logits); elements past V read as -inf.
-// VECLOAD requires a 16-byte aligned row base and V % DT::VEC == 0.
+// Load tile `tile` of `row` (V logits) without a branch: an element past the
+// row is read from a clamped address inside it, so the tile holds copies of
+// real logits there until mask_tail() turns them into -inf (only the last tile
+// of a row reaches past V).  A conditional load would make the compiler wait
+// for the data right away, which defeats loads kept in flight.  VECLOAD
+// requires a 16-byte aligned row base and V % DT::VEC == 0.
 template <typename DT, bool VECLOAD>
 __device__ __forceinline__ Raw<DT> load_raw(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
                                             int lane) {
   Raw<DT> r;
-  const int64_t base = tile * TILE;
-  constexpr uint32_t NEG_INF_BITS = DT::VEC == 8 ? 0xFF80FF80u : 0xFF800000u;
+  const int v = (int)V;  // V <= 524288
+  const int base = (int)tile * TILE;
 #pragma unroll
   for (int c = 0; c < Raw<DT>::CHUNKS; c++) {
-    const int64_t off = base + c * (WAVE * DT::VEC) + lane * DT::VEC;
+    const int off = base + c * (WAVE * DT::VEC) + lane * DT::VEC;
     if constexpr (VECLOAD) {
-      if (off < V) r.q[c] = *reinterpret_cast<const uint4*>(row + off);
-      else r.q[c] = make_uint4(NEG_INF_BITS, NEG_INF_BITS, NEG_INF_BITS, NEG_INF_BITS);
+      r.q[c] = *reinterpret_cast<const uint4*>(row + (off < v ? off : v - DT::VEC));
     } else {
       uint32_t w[4];
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         if constexpr (DT::VEC == 8) {
-          const uint32_t lo = off + 2 * k < V ? (uint32_t)row[off + 2 * k] : 0xFF80u;
-          const uint32_t hi = off + 2 * k + 1 < V ? (uint32_t)row[off + 2 * k + 1] : 0xFF80u;
+          const uint32_t lo = row[min(off + 2 * k, v - 1)];
+          const uint32_t hi = row[min(off + 2 * k + 1, v - 1)];
           w[k] = lo | (hi << 16);
         } else {
-          w[k] = off + k < V ? __float_as_uint(row[off + k]) : NEG_INF_BITS;
+          w[k] = __float_as_uint(row[min(off + k, v - 1)]);
         }
       }
       r.q[c] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
+  return r;
+}
+
+// Elements at or past V of tile `tile` become -inf; nothing happens for a tile
+// that lies inside the row (the test is the same for the whole wavefront).
+template <typename DT>
+__device__ __forceinline__ void mask_tail(Raw<DT>& r, int64_t V, int64_t tile, int lane) {
+  const int v = (int)V;
+  const int base = (int)tile * TILE;
+  if (base + TILE <= v) return;
+#pragma unroll
+  for (int c = 0; c < Raw<DT>::CHUNKS; c++) {
+    const int off = base + c * (WAVE * DT::VEC) + lane * DT::VEC;
+    uint32_t w[4] = {r.q[c].x, r.q[c].y, r.q[c].z, r.q[c].w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      if constexpr (DT::VEC == 8) {
+        if (off + 2 * k >= v) w[k] = (w[k] & 0xFFFF0000u) | 0xFF80u;
+        if (off + 2 * k + 1 >= v) w[k] = (w[k] & 0x0000FFFFu) | 0xFF800000u;
+      } else {
+        if (off + k >= v) w[k] = 0xFF800000u;
+      }
+    }
+    r.q[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// load_raw then mask_tail: a tile ready to use (waits for its data).
+template <typename DT, bool VECLOAD>
+__device__ __forceinline__ Raw<DT> load_tile(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
+                                             int lane) {
+  Raw<DT> r = load_raw<DT, VECLOAD>(row, V, tile, lane);
+  mask_tail<DT>(r, V, tile, lane);
   return r;
 }
 
@@ -166,43 +214,19 @@ __device__ __forceinline__ void unpack(const Raw<DT>& r, int c, float (&v)[DT::V
   }
 }
 
-// Softmax partial of a tile: m = max, s = sum 2^((v - m) * c).
-// An all -inf tile gives (-inf, 0).  NaN or +inf inputs make s NaN.
-template <typename DT>
-__device__ __forceinline__ float2 tile_partial(const Raw<DT>& r, float c) {
-  float v[PER_LANE];
-#pragma unroll
-  for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-    float t[DT::VEC];
-    unpack<DT>(r, ch, t);
-#pragma unroll
-    for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = t[k];
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < PER_LANE; e++) m = fmaxf(m, v[e]);
-  m = wave_max(m);
-  float s = 0.0f;
-  if (m != -INFINITY) {
-#pragma unroll
-    for (int e = 0; e < PER_LANE; e++) s += __builtin_amdgcn_exp2f((v[e] - m) * c);
-  }
-  s = wave_sum(s);
-  return make_float2(m, s);
-}
-
 // ---------------------------------------------------------------------------
-// merge of per-tile partials into row statistics (one wavefront)
+// row statistics
 // ---------------------------------------------------------------------------
 struct RowStat {
-  float M;       // max over the row of z * c (log2 domain, c = log2(e) / T)
-  double S;      // sum over the row of 2^(z c - M)
-  bool ok;       // M finite and S finite and >= 1 (up to rounding)
+  float M;    // max over the row of z * c (log2 domain, c = log2(e) / T)
+  double S;   // sum over the row of 2^(z c - M)
+  double lS;  // natural log of S
+  bool ok;    // M finite and S finite and >= 1 (up to rounding)
 };
 
 // natural-log probability of logit z under a row with statistics rs
 __device__ __forceinline__ double log_prob(float z, const RowStat& rs, float c) {
-  return ((double)z * (double)c - (double)rs.M) * 0.69314718055994530942 - log(rs.S);
+  return ((double)z * (double)c - (double)rs.M) * 0.69314718055994530942 - rs.lS;
 }
 
 // ---------------------------------------------------------------------------

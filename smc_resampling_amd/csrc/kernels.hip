@@ -2,31 +2,38 @@
 //
 // Each library call launches two kernels on the caller's stream.
 //
-// k_stream (both operations): the logit rows are laid out group by group (a
-// group is an SD sequence or an SMC particle; its rows are target rows
-// 0..K_b, then draft rows 0..K_b-1) and cut into 2048-logit tiles.  Each
-// wavefront streams a contiguous range of tiles with the next tiles' loads in
-// flight, and stores softmax partials (max, sum of exponentials) and the logit
-// of each row's draft token.  It is the only kernel that reads the logit
-// stream, and it holds nothing else, so it runs at full occupancy.
+// k_stream (both operations) reads every logit once.  The logit rows are
+// taken group by group (a group is an SD sequence or an SMC particle: its
+// target rows 0..K_b, then its draft rows 0..K_b-1), each row cut into
+// segments of `seg` consecutive 2048-logit tiles; a unit is one (row,
+// segment).  Wavefront w of W streams units [U w / W, U (w+1) / W) with the
+// next tiles' loads in flight across unit, row and group boundaries, keeps
+// per-lane running softmax statistics over a unit and stores the unit's (max,
+// sum of exponentials).  A unit's partial depends on its logits alone, so
+// equal rows get bitwise-equal statistics however the work is spread.  The
+// kernel holds nothing else, so it runs at high occupancy.
 //
 // k_sd_tail (sd_verify; "Faster LLM Inference via Sequential Monte Carlo",
-// sec. 1; variable lengths as in "PACER", Methodik): one workgroup per
-// (sequence, 4 tiles).  Each merges its sequence's partials into row
-// statistics and tests u_j < p_j(x_j) / q_j(x_j) up to the first rejection n
-// (every workgroup of a sequence reaches the same decision).  n = K_b: the
-// workgroup whose tiles hold u * (total mass) of p_{K_b} draws the bonus token.
-// n < K_b: each wavefront stores the mass of max(0, p_n - q_n) over its tile;
-// the last workgroup of the sequence to finish locates the tile that holds
-// u * (total mass) and draws the token inside it.
+// sec. 1; variable lengths as in "PACER", Methodik): workgroup (x, b) of
+// sequence b merges b's partials into row statistics and tests
+// u_j < p_j(x_j) / q_j(x_j) up to the first rejection n; every workgroup of b
+// reaches the same decision.  n = K_b: workgroup 0 draws the bonus token from
+// p_{K_b} by inverse CDF (segment, tile, token).  n < K_b: each wavefront
+// stores the mass of max(0, p_n - q_n) over one tile; the last workgroup of b
+// to finish locates the tile that holds u * (total mass) and draws inside it.
 //
-// k_smc_tail (smc_reweight_resample; same page, sec. 2 steps 3-4; sec. 3): one
-// wavefront per particle: log-weight increment sum_j log p_j(x_j) - log
-// q_j(x_j) and the (K+1)-th token drawn from p_K; the last particle of a
-// prompt to finish computes the Kish ESS, resamples systematically when it is
-// below the threshold, and gathers the page-table rows by ancestor.
+// k_smc_tail (smc_reweight_resample; same page, sec. 2 steps 3-4, sec. 3): one
+// workgroup per particle computes the log-weight increment
+// sum_j log p_j(x_j) - log q_j(x_j) and draws the (K+1)-th token from p_K; the
+// last particle of a prompt to finish computes the Kish ESS, resamples
+// systematically when it is below the threshold and gathers the page-table
+// rows by ancestor.
 //
-// Counters live in the caller's workspace and every call returns them to zero.
+// Nothing waits on another workgroup: hand-offs inside a tail kernel are
+// counters that the last arrival observes, and the values handed over
+// (residual masses, log-weights) are written and read at the device coherence
+// point (agent-scope atomics), so no XCD-local L2 holds a stale copy.  Every
+// counter is back at zero when the kernel ends.
 #include <map>
 #include <mutex>
 
@@ -35,22 +42,15 @@
 
 namespace smcsd {
 
-constexpr int MAXR = 2 * SMCSD_MAX_K + 1;     // rows per group
+constexpr int MAXR = 2 * SMCSD_MAX_K + 1;  // rows per group
+constexpr int MAX_TILES = 256;             // tiles per row (V <= 524288)
 
 // ---------------------------------------------------------------------------
-// small helpers
+// device-coherent loads and stores, counters
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void raise_flags(uint32_t* flags, uint32_t bits) {
   if (flags && bits) atomicOr(flags, bits);
 }
-
-// Cross-wavefront communication.  Every value one wavefront hands to another
-// (tile partials, decisions, residual masses, log-weights, counters) is
-// written and read with agent-scope relaxed atomics, which on gfx950 are
-// write-through / read-through at the device coherence point (`sc1`) and need
-// no writeback or invalidation of the XCD-local L2.  A writer waits for its
-// stores to complete before it bumps a counter or sets a flag; a reader that
-// has seen the counter or flag then reads the values from the same point.
 __device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -58,121 +58,488 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_dev(double* p, double v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(float2* p, float2 v) {
-  const uint64_t b = ((uint64_t)__float_as_uint(v.y) << 32) | __float_as_uint(v.x);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ float ld_dev(const float* p) {
-  return __uint_as_float(
-      __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ double ld_dev(const double* p) {
-  return __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<double*>(p)),
-                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ float2 ld_dev(const float2* p) {
-  const uint64_t b =
-      __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
 }
 // wait until every memory operation this wavefront issued has completed
 __device__ __forceinline__ void stores_done() {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-
-// one add per wavefront (lane 0, after the wavefront's stores completed); the
-// old value is broadcast to every lane
-__device__ __forceinline__ uint32_t wave_add(uint32_t* p, uint32_t v, int lane) {
-  stores_done();
-  uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0, WAVE);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return old;
+__device__ __forceinline__ uint32_t ctr_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
-  return __longlong_as_double(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+// ---------------------------------------------------------------------------
+// groups
+// ---------------------------------------------------------------------------
+struct Group {
+  int64_t d0;   // first draft row
+  int kb;       // draft length
+  int64_t fr0;  // first row in the group-major row order (= 2*d0 + g)
+  bool ok;
+};
+
+__device__ __forceinline__ Group make_group(int64_t g, int64_t a, int64_t e, int K, int64_t rows_d) {
+  Group G;
+  G.d0 = a;
+  G.kb = (int)(e - a);
+  G.ok = a >= 0 && e >= a && e - a <= K && e <= rows_d;
+  G.fr0 = 2 * a + g;
+  return G;
 }
 
-// reductions inside each 16-lane row; every lane receives its row's result
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));
-  v = fmaxf(v, dpp_f32<DPP_QUAD_2301>(v));
-  v = fmaxf(v, dpp_f32<DPP_ROR4>(v));
-  return fmaxf(v, dpp_f32<DPP_ROR8>(v));
-}
-__device__ __forceinline__ double row16_sum(double v) {
-  v += dpp_f64<DPP_QUAD_1032>(v);
-  v += dpp_f64<DPP_QUAD_2301>(v);
-  v += dpp_f64<DPP_ROR4>(v);
-  return v + dpp_f64<DPP_ROR8>(v);
+__device__ __forceinline__ Group group_of(int64_t g, int K, const int32_t* __restrict__ offsets, int64_t rows_d) {
+  if (!offsets) return make_group(g, g * K, (g + 1) * K, K, rows_d);
+  return make_group(g, offsets[g], offsets[g + 1], K, rows_d);
 }
 
-// reductions inside each quad of lanes; every lane receives its quad's result
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));
-  return fmaxf(v, dpp_f32<DPP_QUAD_2301>(v));
-}
-__device__ __forceinline__ double quad_sum(double v) {
-  v += dpp_f64<DPP_QUAD_1032>(v);
-  return v + dpp_f64<DPP_QUAD_2301>(v);
+// Logit row `rr` of group g (target rows 0..kb, then draft rows); null when
+// it falls outside the buffers (malformed offsets).
+template <typename raw>
+__device__ __forceinline__ const raw* group_row(const StepArgs& a, const Group& G, int64_t g, int64_t rr) {
+  if (!G.ok || rr < 0 || rr > 2 * G.kb) return nullptr;
+  if (rr <= G.kb) {
+    const int64_t tr = G.d0 + g + rr;
+    return tr < a.rows_t ? static_cast<const raw*>(a.target) + tr * a.V : nullptr;
+  }
+  const int64_t dr = G.d0 + rr - G.kb - 1;
+  return dr < a.rows_d ? static_cast<const raw*>(a.draft) + dr * a.V : nullptr;
 }
 
-// Row statistics of `nrows` consecutive rows of partials into the
-// wavefront's LDS slice (one wavefront; 4 lanes per row, 16 rows per pass, so
-// a group of up to 16 rows is merged after a single round of loads):
-// M = max of the partials' mc (log2 domain), S = sum of s * 2^(mc - M).
-__device__ __forceinline__ void merge_group_rows(const float2* __restrict__ part, int nrows, int ntiles,
-                                                 float* sM, double* sS, int lane) {
-  const int sub = lane & 3;
-  for (int r0 = 0; r0 < nrows; r0 += WAVE / 4) {
-    const int r = r0 + (lane >> 2);
-    const bool live = r < nrows;
-    const float2* pr = part + (int64_t)(live ? r : 0) * ntiles;
-    float m = -INFINITY;
-    if (live)
-      for (int t = sub; t < ntiles; t += 4) m = fmaxf(m, pr[t].x);
-    const float M = quad_max(m);
-    double acc = 0.0;
-    if (live && M != -INFINITY) {
-      for (int t = sub; t < ntiles; t += 4) {
-        const float2 pt = pr[t];
-        if (pt.x != -INFINITY) acc += (double)pt.y * exp2((double)pt.x - (double)M);
+// ---------------------------------------------------------------------------
+// softmax partials
+// ---------------------------------------------------------------------------
+// Per-lane running statistics over a unit's tiles: m = max of z c (log2
+// domain), s = sum 2^(z c - m), rescaled when the lane's maximum grows.
+template <typename DT>
+__device__ __forceinline__ void lane_fold_tile(const Raw<DT>& cur, float c, float& m, float& s) {
+  float v[PER_LANE];
+#pragma unroll
+  for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+    float w[DT::VEC];
+    unpack<DT>(cur, ch, w);
+#pragma unroll
+    for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = w[k];
+  }
+  float tm = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < PER_LANE; e++) tm = fmaxf(tm, v[e]);
+  const float mn = fmaxf(m, tm * c);
+  if (mn > -INFINITY) {
+    float acc = s * __builtin_amdgcn_exp2f(m - mn);  // 0 while m is -inf (NaN stays NaN)
+#pragma unroll
+    for (int e = 0; e < PER_LANE; e++) acc += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mn));
+    s = acc;
+    m = mn;
+  } else {
+    // every value so far is -inf or NaN: keep a NaN visible
+    bool nan = false;
+#pragma unroll
+    for (int e = 0; e < PER_LANE; e++) nan |= v[e] != v[e];
+    if (nan) s = __builtin_nanf("");
+  }
+}
+
+// The wavefront's (MC, S) from per-lane (m, s): MC = max m, S = sum s 2^(m - MC).
+// All -inf gives (-inf, 0); a NaN s stays NaN.
+__device__ __forceinline__ float2 wave_partial(float m, float s) {
+  const float M = wave_max(m);
+  const float sc = m > -INFINITY ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+  return make_float2(M, wave_sum(s * sc));
+}
+
+// ---------------------------------------------------------------------------
+// k_stream
+// ---------------------------------------------------------------------------
+// The group of the rows a wavefront streams.  With CSR offsets the wavefront
+// keeps offsets[g0 + l] in lane l, so moving to the next group needs no load
+// (a load inside the streaming loop would wait for every tile in flight).
+struct GroupCursor {
+  int64_t g;
+  Group G;
+  int64_t g0;   // base of the offsets window
+  int32_t win;  // offsets[g0 + lane]
+};
+
+// The group holding group-major row fr (largest g with 2*offsets[g] + g <=
+// fr): each round probes 64 candidates at once.
+__device__ __forceinline__ int64_t find_group_wave(int64_t fr, const StepArgs& a, int lane) {
+  if (!a.offsets) return fr / (2 * a.K + 1);
+  int64_t lo = 0, hi = a.ngroups;  // the answer lies in [lo, hi)
+  while (hi - lo > 1) {
+    const int64_t span = hi - lo;
+    const int64_t p = span <= WAVE + 1 ? lo + 1 + lane : lo + (span * (lane + 1)) / (WAVE + 1);
+    const bool live = p < hi;
+    const bool le = live && 2 * (int64_t)a.offsets[p] + p <= fr;
+    const uint64_t bal = __ballot(le);
+    const int j = bal ? 63 - __builtin_clzll(bal) : -1;  // last probe at or below fr
+    const int64_t pj = j >= 0 ? __shfl(p, j, WAVE) : lo;
+    const uint64_t above = __ballot(live && !le) & (j >= 0 ? ~((2ull << j) - 1) : ~0ull);
+    const int64_t pk = above ? __shfl(p, __builtin_ctzll(above), WAVE) : hi;
+    lo = uniform64(pj);
+    hi = uniform64(pk);
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void cursor_set(GroupCursor& cu, int64_t g, const StepArgs& a, int lane) {
+  cu.g = g;
+  if (!a.offsets) {
+    cu.G = make_group(g, g * a.K, (g + 1) * a.K, a.K, a.rows_d);
+    return;
+  }
+  if (g + 1 - cu.g0 >= WAVE || g < cu.g0) {  // refill the window
+    cu.g0 = g;
+    cu.win = g + lane <= a.ngroups ? a.offsets[g + lane] : 0;
+  }
+  const int i = (int)(g - cu.g0);
+  cu.G = make_group(g, __builtin_amdgcn_readlane(cu.win, i), __builtin_amdgcn_readlane(cu.win, i + 1), a.K,
+                    a.rows_d);
+}
+
+template <typename DT, bool VL, int NS>
+__global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
+  using raw = typename DT::raw;
+  const int lane = threadIdx.x % WAVE;
+  const int64_t w = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wave_id();
+  const int64_t W = (int64_t)gridDim.x * WAVES_PER_BLOCK;
+  const int64_t u0 = a.units * w / W, u1 = a.units * (w + 1) / W;
+  if (u0 >= u1) return;
+  const int nseg = a.nseg, seg = a.seg, ntiles = a.ntiles;
+  const float c = a.c;
+  uint32_t bad = 0;
+  // load cursor: unit lu of row lfr, tile lt of [.., lte)
+  int64_t lu = u0, lfr = u0 / nseg;
+  int lsg = (int)(u0 - lfr * nseg);
+  int lt = lsg * seg, lte = min(ntiles, lt + seg);
+  GroupCursor gc;
+  gc.g0 = -WAVE;
+  gc.win = 0;
+  cursor_set(gc, find_group_wave(lfr, a, lane), a, lane);
+  const raw* lrow = group_row<raw>(a, gc.G, gc.g, lfr - gc.G.fr0);
+  if (!lrow) bad = FLAG_BAD_INPUT;
+  // Issues the loads of the next tile.  A row outside the buffers (malformed
+  // offsets) is read as row 0 of the target, and its partials are not used.
+  auto fetch = [&]() {
+    const Raw<DT> x = load_raw<DT, VL>(lrow ? lrow : static_cast<const raw*>(a.target), a.V, lt, lane);
+    if (++lt == lte) {
+      if (++lu < u1) {
+        if (++lsg == nseg) {
+          lsg = 0;
+          lfr++;
+          if (lfr >= gc.G.fr0 + 2 * (int64_t)gc.G.kb + 1) cursor_set(gc, gc.g + 1, a, lane);
+          lrow = group_row<raw>(a, gc.G, gc.g, lfr - gc.G.fr0);
+          if (!lrow) bad = FLAG_BAD_INPUT;
+        }
+        lt = lsg * seg;
+        lte = min(ntiles, lt + seg);
       }
     }
-    const double S = quad_sum(acc);
-    if (live && sub == 0) {
-      sM[r] = M;
-      sS[r] = S;
+    return x;
+  };
+  // tiles in [u0, u1): seg per unit, fewer in a row's last segment
+  const int last_seg = ntiles - (nseg - 1) * seg;
+  const int64_t T = (u1 - u0) * seg - (u1 / nseg - u0 / nseg) * (int64_t)(seg - last_seg);
+  // reduce cursor: tile ct of [.., cte) of the current unit.  Finished units'
+  // partials wait in lanes (unit pbase + l in lane l) and are stored 64 at a
+  // time: a store is a memory operation the loads' wait counter also counts.
+  int csg = (int)(u0 % nseg);
+  int ct = csg * seg, cte = min(ntiles, ct + seg);
+  float m = -INFINITY, s = 0.0f;
+  float2 pb = make_float2(0.0f, 0.0f);
+  int64_t pbase = u0;
+  int pn = 0;
+  auto reduce = [&](Raw<DT>& x) {
+    mask_tail<DT>(x, a.V, ct, lane);
+    lane_fold_tile<DT>(x, c, m, s);
+    if (++ct == cte) {
+      const float2 pt = wave_partial(m, s);
+      if (lane == pn) pb = pt;
+      if (++pn == WAVE) {
+        a.part[pbase + lane] = pb;
+        pbase += WAVE;
+        pn = 0;
+      }
+      m = -INFINITY;
+      s = 0.0f;
+      if (++csg == nseg) csg = 0;
+      ct = csg * seg;
+      cte = min(ntiles, ct + seg);
     }
+  };
+  // NS tiles in flight.  Slot i always lives in the same registers (a
+  // rotating copy would wait for loads still in flight), and in the main loop
+  // every slot is refilled unconditionally, so a reduction waits only for its
+  // own tile.
+  Raw<DT> q[NS];
+  if (T >= 2 * NS) {
+#pragma unroll
+    for (int i = 0; i < NS; i++) q[i] = fetch();
+    int64_t left = T;
+    do {
+#pragma unroll
+      for (int i = 0; i < NS; i++) {
+        reduce(q[i]);
+        q[i] = fetch();
+      }
+      left -= NS;
+    } while (left >= 2 * NS);
+    // NS <= left < 2 NS: the slots hold the next NS tiles, left - NS remain
+    const int more = (int)(left - NS);
+#pragma unroll
+    for (int i = 0; i < NS; i++) {
+      reduce(q[i]);
+      if (i < more) q[i] = fetch();
+    }
+#pragma unroll
+    for (int i = 0; i < NS; i++)
+      if (i < more) reduce(q[i]);
+  } else {
+    // fewer than 2 NS tiles
+    const int t = (int)T;
+#pragma unroll
+    for (int i = 0; i < NS; i++)
+      if (i < t) q[i] = fetch();
+#pragma unroll
+    for (int i = 0; i < NS; i++) {
+      if (i < t) {
+        reduce(q[i]);
+        if (NS + i < t) q[i] = fetch();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; i++)
+      if (NS + i < t) reduce(q[i]);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");  // LDS writes done before other lanes read
+  if (lane < pn) a.part[pbase + lane] = pb;
+  if (lane == 0) raise_flags(a.flags, bad);
 }
 
-__device__ __forceinline__ RowStat stat_of(const float* sM, const double* sS, int r) {
+// ---------------------------------------------------------------------------
+// tails: workgroup-shared state
+// ---------------------------------------------------------------------------
+struct TailLds {
+  float M[MAXR];             // row max of z c (log2 domain)
+  double S[MAXR];            // row sum of 2^(z c - M)
+  double lS[MAXR];           // log S
+  float z[2 * SMCSD_MAX_K];  // logits of the draft tokens: target rows, then draft rows
+  float u[SMCSD_MAX_K];      // accept uniforms
+  int xok[SMCSD_MAX_K];      // draft token inside [0, V)
+  float2 P[MAX_TILES];       // segment partials of the row a draw uses
+  double W[MAX_TILES];       // per-tile masses of a draw
+  float Tm[MAX_TILES];       // per-tile log2 maxima of a draw
+  double before, target;
+  int sel, clamp, n, y;
+  uint32_t fl;
+};
+struct PromptLds {
+  float lw[SMCSD_MAX_N];
+  int anc[SMCSD_MAX_N];
+};
+union SharedLds {
+  TailLds t;
+  PromptLds p;
+};
+
+__device__ __forceinline__ RowStat stat_of(const TailLds& L, int r) {
   RowStat rs;
-  rs.M = sM[r];
-  rs.S = sS[r];
+  rs.M = L.M[r];
+  rs.S = L.S[r];
+  rs.lS = L.lS[r];
   rs.ok = (rs.M > -INFINITY) && (rs.M < INFINITY) && (rs.S >= 0.5) && (rs.S < INFINITY);
   return rs;
 }
 
+// fold partial (pm, ps) into running statistics (m, s) (log2 domain, fp64 sum)
+__device__ __forceinline__ void fold(float& m, double& s, float pm, double ps) {
+  if (pm > m) {
+    s = (m > -INFINITY ? s * exp2((double)m - (double)pm) : s * 0.0) + ps;
+    m = pm;
+  } else {
+    s += pm > -INFINITY ? ps * exp2((double)pm - (double)m) : ps * 0.0;
+  }
+}
+
+// Row statistics of rows [0, R) of one group from its segment partials (row
+// r's at part[r * nseg + k], written by the previous kernel) into L.M / L.S /
+// L.lS; the partials of row `keep` are copied to L.P.  Whole workgroup, `tpr`
+// threads per row, fixed combination order, so equal rows get equal
+// statistics.
+__device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, int keep, TailLds& L) {
+  int tpr = 16;
+  while (tpr > 1 && BLOCK / tpr < R) tpr >>= 1;
+  const int rpp = BLOCK / tpr;
+  const int sub = threadIdx.x & (tpr - 1);
+  for (int r0 = 0; r0 < R; r0 += rpp) {
+    const int r = r0 + (int)threadIdx.x / tpr;
+    float m = -INFINITY;
+    double s = 0.0;
+    if (r < R) {
+      for (int k = sub; k < nseg; k += tpr) {
+        const float2 pt = part[(int64_t)r * nseg + k];
+        if (r == keep) L.P[k] = pt;
+        fold(m, s, pt.x, (double)pt.y);
+      }
+    }
+    for (int off = 1; off < tpr; off <<= 1) {
+      const float mo = __shfl_xor(m, off, WAVE);
+      const double so = __shfl_xor(s, off, WAVE);
+      fold(m, s, mo, so);
+    }
+    if (r < R && sub == 0) {
+      L.M[r] = m;
+      L.S[r] = s;
+      L.lS[r] = log(s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// ordered searches
+// ---------------------------------------------------------------------------
+// Over weights W_k (k < n <= 256) in ascending order: the first k with
+// base + (inclusive prefix) > target(total), and the prefix before it; -1
+// (with the last k of positive weight in *last) when there is none.  One
+// wavefront.
+template <typename WFN, typename TFN>
+__device__ __forceinline__ int locate(int n, WFN weight, double base, TFN target_of, int lane, double* before,
+                                      double* target_out, int* last) {
+  constexpr int CH = MAX_TILES / WAVE;
+  double incl[CH], W[CH];
+  double run = base;
+  int lastk = -1;
+#pragma unroll
+  for (int k = 0; k < CH; k++) {
+    W[k] = 0.0;
+    incl[k] = run;
+    if (k * WAVE < n) {
+      const int t = k * WAVE + lane;
+      W[k] = t < n ? weight(t) : 0.0;
+      incl[k] = run + wave_incl_scan_f64(W[k], lane);
+      run = __shfl(incl[k], WAVE - 1, WAVE);
+      int lt = W[k] > 0.0 ? t : -1;
+      for (int off = 32; off >= 1; off >>= 1) lt = max(lt, __shfl_xor(lt, off, WAVE));
+      if (lt >= 0) lastk = lt;
+    }
+  }
+  const double target = target_of(run - base);
+  *target_out = target;
+  *last = lastk;
+#pragma unroll
+  for (int k = 0; k < CH; k++) {
+    if (k * WAVE < n) {
+      const uint64_t bal = __ballot(incl[k] > target && k * WAVE + lane < n);
+      if (bal) {
+        const int src = __builtin_ctzll(bal);
+        *before = __shfl(incl[k] - W[k], src, WAVE);
+        return k * WAVE + src;
+      }
+    }
+  }
+  *before = run;
+  return -1;
+}
+
+// Softmax partial (MC, S) of one tile held in registers, formed like the
+// streaming partials.
+template <typename DT>
+__device__ __forceinline__ float2 tile_partial_of(const Raw<DT>& r, float c) {
+  float m = -INFINITY, s = 0.0f;
+  lane_fold_tile<DT>(r, c, m, s);
+  return wave_partial(m, s);
+}
+
+// Inverse-CDF draw from softmax(z c) of `row` (row maximum M, log2 domain; its
+// segment partials in L.P) with uniform u.  Whole workgroup; every thread
+// gets the token.
+template <typename DT, bool VL>
+__device__ int draw_softmax(const typename DT::raw* __restrict__ row, const StepArgs& a, float M, double u,
+                            TailLds& L, uint32_t& fl) {
+  const int lane = threadIdx.x % WAVE, wave = wave_id();
+  const float c = a.c;
+  // 1. the segment
+  if (wave == 0) {
+    auto wt = [&](int k) -> double {
+      const float2 p = L.P[k];
+      return p.x > -INFINITY ? (double)p.y * exp2((double)p.x - (double)M) : 0.0;
+    };
+    double before = 0.0, target = 0.0;
+    int last = -1;
+    const int k = locate(a.nseg, wt, 0.0, [&](double tot) { return u * tot; }, lane, &before, &target, &last);
+    if (lane == 0) {
+      L.sel = k >= 0 ? k : (last >= 0 ? last : a.nseg - 1);
+      L.clamp = k < 0;
+      L.before = before;
+      L.target = target;
+    }
+  }
+  __syncthreads();
+  const int sg = L.sel;
+  const int tb = sg * a.seg, te = min(a.ntiles, tb + a.seg);
+  int tt;
+  double before_t;
+  float mt;
+  bool clamp = L.clamp;
+  if (te - tb == 1) {
+    tt = tb;
+    before_t = L.before;
+    mt = L.P[sg].x;
+  } else {
+    // 2. the tile inside the segment
+    for (int t = tb + wave; t < te; t += WAVES_PER_BLOCK) {
+      const Raw<DT> r = load_tile<DT, VL>(row, a.V, t, lane);
+      const float2 pt = tile_partial_of<DT>(r, c);
+      if (lane == 0) {
+        L.Tm[t - tb] = pt.x;
+        L.W[t - tb] = pt.x > -INFINITY ? (double)pt.y * exp2((double)pt.x - (double)M) : 0.0;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      auto wt = [&](int k) -> double { return L.W[k]; };
+      double before = 0.0, target = 0.0;
+      int last = -1;
+      const double tgt = clamp ? INFINITY : L.target;
+      const int k = locate(te - tb, wt, L.before, [&](double) { return tgt; }, lane, &before, &target, &last);
+      if (lane == 0) {
+        L.sel = tb + (k >= 0 ? k : (last >= 0 ? last : te - tb - 1));
+        L.clamp = k < 0;
+        L.before = before;
+      }
+    }
+    __syncthreads();
+    tt = L.sel;
+    clamp = L.clamp;
+    before_t = L.before;
+    mt = L.Tm[tt - tb];
+  }
+  // 3. the token inside the tile
+  if (wave == 0) {
+    const Raw<DT> raw = load_tile<DT, VL>(row, a.V, tt, lane);
+    auto wfn = [&](int ch, float (&w)[DT::VEC]) {
+      unpack<DT>(raw, ch, w);
+#pragma unroll
+      for (int k = 0; k < DT::VEC; k++) w[k] = __builtin_amdgcn_exp2f(fmaf(w[k], c, -mt));
+    };
+    int last_pos = -1;
+    const double tscale = exp2((double)mt - (double)M);
+    const float tgt = clamp ? INFINITY : (float)((L.target - before_t) / tscale);
+    int idx = tile_search<DT>(wfn, tgt, lane, &last_pos);
+    if (idx < 0) {
+      fl |= FLAG_CDF_CLAMP;
+      idx = last_pos >= 0 ? last_pos : 0;
+    }
+    if (lane == 0) L.y = tt * TILE + idx;
+  }
+  __syncthreads();
+  return L.y;
+}
+
 // Residual weights max(0, p - q) of chunk ch of one tile of a (target, draft)
-// row pair, p = 2^(z_t c - Mt) * st, q = 2^(z_d c - Md) * sd (Mt, Md in the
-// log2 domain, st = 1 / S_t, sd = 1 / S_d).
+// row pair, p = 2^(z_t c - Mt) * st, q = 2^(z_d c - Md) * sd (st = 1 / S_t,
+// sd = 1 / S_d).
 template <typename DT>
 __device__ __forceinline__ void residual_chunk(const Raw<DT>& rt, const Raw<DT>& rd, int ch, float Mt, float Md,
                                                float c, float st, float sd, float (&r)[DT::VEC]) {
@@ -190,486 +557,216 @@ __device__ __forceinline__ void residual_chunk(const Raw<DT>& rt, const Raw<DT>&
   }
 }
 
-// Wave-level search over per-tile weights W_t (t < ntiles <= 256) in ascending
-// tile order: the first tile whose inclusive prefix exceeds u * total, and the
-// prefix before it; -1 (with the last tile of positive weight in *last_tile)
-// when rounding leaves no such tile.  Each weight is read once.
-constexpr int kMaxTileChunks = 4;  // ntiles <= 256, i.e. V <= 524288
-
-template <typename WFN>
-__device__ __forceinline__ int locate_tile(int ntiles, WFN weight, double u, int lane, double* before,
-                                           double* total_out, int* last_tile) {
-  double incl[kMaxTileChunks], W[kMaxTileChunks];
-  double total = 0.0;
-  int lastt = -1;
-#pragma unroll
-  for (int k = 0; k < kMaxTileChunks; k++) {
-    const int t = k * WAVE + lane;
-    W[k] = t < ntiles ? weight(t) : 0.0;
-  }
-#pragma unroll
-  for (int k = 0; k < kMaxTileChunks; k++) {
-    incl[k] = total + wave_incl_scan_f64(W[k], lane);
-    total = __shfl(incl[k], WAVE - 1, WAVE);
-    int lt = W[k] > 0.0 ? k * WAVE + lane : -1;
-    for (int off = 32; off >= 1; off >>= 1) lt = max(lt, __shfl_xor(lt, off, WAVE));
-    if (lt >= 0) lastt = lt;
-  }
-  *total_out = total;
-  *last_tile = lastt;
-  const double target = u * total;
-#pragma unroll
-  for (int k = 0; k < kMaxTileChunks; k++) {
-    const uint64_t bal = __ballot(incl[k] > target);
-    if (bal) {
-      const int src = __builtin_ctzll(bal);
-      *before = __shfl(incl[k] - W[k], src, WAVE);
-      return k * WAVE + src;
-    }
-  }
-  return -1;
-}
-
-// Inverse-CDF draw from the softmax of `row` (statistics rs, tile partials
-// `part`) with uniform u.  One wavefront.
-// Inverse-CDF draw from the softmax of `row` (statistics rs, per-tile
-// partials `part`) with uniform u.  One wavefront.  Returns -1 when the
-// located tile lies outside [tb, tb + tn) (another workgroup holds it).
-template <typename DT, bool VL>
-__device__ __forceinline__ int draw_from_row(const typename DT::raw* __restrict__ row, int64_t V,
-                                             const float2* __restrict__ part, int ntiles, const RowStat& rs,
-                                             float c, float u, int lane, uint32_t* fl, int tb, int tn) {
-  auto weight = [&](int t) -> double {
-    const float2 pt = part[t];
-    return pt.x == -INFINITY ? 0.0 : (double)pt.y * exp2((double)pt.x - (double)rs.M);
-  };
-  double before = 0.0, total = 0.0;
-  int last_tile = -1;
-  const int t = locate_tile(ntiles, weight, (double)u, lane, &before, &total, &last_tile);
-  const int tt = t >= 0 ? t : (last_tile >= 0 ? last_tile : ntiles - 1);
-  if (tt < tb || tt >= tb + tn) return -1;
-  const float mt = part[tt].x;
-  const Raw<DT> raw = load_raw<DT, VL>(row, V, tt, lane);
-  auto wfn = [&](int ch, float (&w)[DT::VEC]) {
-    unpack<DT>(raw, ch, w);
-#pragma unroll
-    for (int k = 0; k < DT::VEC; k++) w[k] = __builtin_amdgcn_exp2f(fmaf(w[k], c, -mt));
-  };
-  int last_pos = -1;
-  int idx = -1;
-  if (t >= 0) {
-    const double tscale = exp2((double)mt - (double)rs.M);
-    idx = tile_search<DT>(wfn, (float)(((double)u * total - before) / tscale), lane, &last_pos);
-  } else {
-    tile_search<DT>(wfn, INFINITY, lane, &last_pos);
-  }
-  if (idx < 0) {
-    *fl |= FLAG_CDF_CLAMP;
-    idx = last_pos >= 0 ? last_pos : 0;
-  }
-  return tt * TILE + idx;
-}
-
 // ---------------------------------------------------------------------------
-// groups: layout of one SD sequence / SMC particle
+// tails: per-group inputs
 // ---------------------------------------------------------------------------
-struct Group {
-  int64_t d0;  // first draft row
-  int kb;      // draft length
-  int64_t fr0; // first row in the group-major row order (= 2*d0 + g)
-  bool ok;
-};
-
-__device__ __forceinline__ Group group_of(int64_t g, int K, const int32_t* __restrict__ offsets, int64_t rows_d) {
-  Group G;
-  if (!offsets) {
-    G.d0 = g * K;
-    G.kb = K;
-    G.ok = true;
-  } else {
-    const int64_t a = offsets[g], e = offsets[g + 1];
-    G.d0 = a;
-    G.kb = (int)(e - a);
-    G.ok = a >= 0 && e >= a && e - a <= K && e <= rows_d;
-  }
-  G.fr0 = 2 * G.d0 + g;
-  return G;
+// Draft token of this thread's row (threads tid < 2 kb: target row tid, then
+// draft row tid - kb, both with token x_{tid mod kb}).
+__device__ __forceinline__ int32_t token_of(const StepArgs& a, const Group& G) {
+  const int tid = threadIdx.x, kb = G.kb;
+  return tid < 2 * kb ? a.tokens[G.d0 + (tid < kb ? tid : tid - kb)] : 0;
 }
 
-// The group holding group-major row fr: largest g with 2*offsets[g] + g <= fr.
-__device__ __forceinline__ int64_t find_group(int64_t fr, int64_t ngroups, int K, const int32_t* __restrict__ offsets) {
-  if (!offsets) return fr / (2 * K + 1);
-  int64_t lo = 0, hi = ngroups - 1;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) >> 1;
-    if (2 * (int64_t)offsets[mid] + mid <= fr) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-
-
-// Counters sit 64 bytes apart so that atomics on different groups do not
-// share a cache line.
-constexpr int CSTRIDE = 16;
-
-// Position of the streaming cursor: the group holding row `fr`.
-struct Cursor {
-  int64_t g, fr_end;
-  Group G;
-};
-
-__device__ __forceinline__ Cursor cursor_at(int64_t fr, const StreamArgs& a) {
-  Cursor c;
-  c.g = find_group(fr, a.ngroups, a.K, a.offsets);
-  c.G = group_of(c.g, a.K, a.offsets, a.rows_d);
-  c.fr_end = c.G.fr0 + 2 * c.G.kb + 1;
-  return c;
-}
-
-__device__ __forceinline__ Cursor cursor_advance(Cursor c, int64_t fr, const StreamArgs& a) {
-  while (fr >= c.fr_end && c.g + 1 < a.ngroups) {
-    c.g++;
-    c.G = group_of(c.g, a.K, a.offsets, a.rows_d);
-    c.fr_end = c.G.fr0 + 2 * c.G.kb + 1;
-  }
-  return c;
-}
-
-// Row `fr` of the cursor's group (null when the layout is malformed); *bonus
-// is set for the group's last target row, whose tiles keep their own partials.
-template <typename raw>
-__device__ __forceinline__ const raw* row_at(const Cursor& c, int64_t fr, const StreamArgs& a, bool* bonus) {
-  const int64_t rr = fr - c.G.fr0;
-  *bonus = rr == c.G.kb;
-  if (!c.G.ok || rr < 0 || rr > 2 * c.G.kb) return nullptr;
-  if (rr <= c.G.kb) {
-    const int64_t tr = c.G.d0 + c.g + rr;
-    return tr < a.rows_t ? static_cast<const raw*>(a.target) + tr * a.V : nullptr;
-  }
-  const int64_t dr = c.G.d0 + rr - c.G.kb - 1;
-  return dr < a.rows_d ? static_cast<const raw*>(a.draft) + dr * a.V : nullptr;
-}
-
-
-// ---------------------------------------------------------------------------
-// k_stream: softmax partials and token logits of every tile
-// ---------------------------------------------------------------------------
-// Wavefront w of nw streams tiles [f0, f1) with PF tiles' loads in flight
-// while one is reduced.  The partial of a tile is (MC, S): MC = max over the
-// tile of z c (log2 domain, c = log2(e) / T) and S = sum 2^(z c - MC), formed
-// from per-lane maxima and sums so that no exponential waits for a
-// wavefront-wide maximum.  It depends on the tile's logits alone, so equal rows
-// get bitwise equal statistics however the stream is divided.  The wavefront
-// that streams the tile holding a row's draft token also stores that logit in
-// tokz[row].
-template <typename DT, bool VL, int PF>
-__global__ __launch_bounds__(BLOCK) void k_stream(StreamArgs a) {
+// Logit of this thread's draft token and whether the token lies in [0, V).
+template <typename DT>
+__device__ __forceinline__ float token_logit(const StepArgs& a, const Group& G, int64_t g, int32_t x, int* ok) {
   using raw = typename DT::raw;
-  const int lane = threadIdx.x % WAVE;
-  const int64_t w = (int64_t)blockIdx.x * WAVES_PER_BLOCK + threadIdx.x / WAVE;
-  const int64_t nw = (int64_t)gridDim.x * WAVES_PER_BLOCK;
-  const int64_t f0 = w * a.total_tiles / nw, f1 = (w + 1) * a.total_tiles / nw;
-  if (f0 >= f1) return;
-  const int ntiles = a.ntiles;
-  const float c = a.c;
-  const int64_t fr_first = f0 / ntiles;
-  const int t_first = (int)(f0 - fr_first * ntiles);
-  // load cursor: issues the loads of tile f + PF while tile f is reduced
-  int64_t lfr = fr_first;
-  int lt = t_first;
-  Cursor lc = cursor_at(lfr, a);
-  auto fetch = [&]() {
-    if (lt == 0) lc = cursor_advance(lc, lfr, a);
-    bool bonus = false;
-    const raw* row = row_at<raw>(lc, lfr, a, &bonus);
-    Raw<DT> x = {};
-    if (row) x = load_raw<DT, VL>(row, a.V, lt, lane);
-    if (++lt == ntiles) {
-      lt = 0;
-      lfr++;
-    }
-    return x;
-  };
-  Raw<DT> q[PF + 1];
-#pragma unroll
-  for (int i = 0; i <= PF; i++) q[i] = f0 + i < f1 ? fetch() : Raw<DT>{};
-  // reduce cursor: the row of the tile being reduced
-  int64_t fr = fr_first;
-  int t = t_first;
-  Cursor rc = lc;
-  rc = cursor_at(fr, a);
-  bool bonus = false, valid = false;
-  int tok_tile = -1;  // tile of this row that holds its draft token, if this wavefront streams it
-  float tok_z = 0.0f;
-  auto enter_row = [&]() {  // row fr starts (or the range starts inside it)
-    rc = cursor_advance(rc, fr, a);
-    const raw* row = row_at<raw>(rc, fr, a, &bonus);
-    valid = row != nullptr;
-    tok_tile = -1;
-    if (valid && !bonus) {
-      const int64_t rr = fr - rc.G.fr0;
-      const int32_t tok = a.tokens[rc.G.d0 + (rr <= rc.G.kb ? rr : rr - rc.G.kb - 1)];
-      const int64_t ft = fr * ntiles + tok / TILE;
-      if (tok >= 0 && tok < a.V && ft >= f0 && ft < f1) {  // load it now, store it with its tile
-        tok_tile = tok / TILE;
-        tok_z = DT::to_f32(row[tok]);
-      }
-    }
-  };
-  enter_row();
-  uint32_t bad = 0;
-  for (int64_t f = f0; f < f1; f++) {
-    const Raw<DT> cur = q[0];
-#pragma unroll
-    for (int i = 0; i < PF; i++) q[i] = q[i + 1];
-    if (f + PF + 1 < f1) q[PF] = fetch();
-    if (valid) {
-      float v[PER_LANE];
-#pragma unroll
-      for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-        float u8[DT::VEC];
-        unpack<DT>(cur, ch, u8);
-#pragma unroll
-        for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = u8[k];
-      }
-      // this lane's max and sum of 2^(z c - mc_lane), then the wavefront's
-      // (MC, sum of s_lane 2^(mc_lane - MC)): a function of the tile alone
-      float tm = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < PER_LANE; e++) tm = fmaxf(tm, v[e]);
-      const float mcl = tm * c;
-      float sl = 0.0f;
-      if (tm > -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < PER_LANE; e++) sl += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mcl));
-      }
-      const float MC = wave_max(mcl);
-      const float S = wave_sum(tm > -INFINITY ? sl * __builtin_amdgcn_exp2f(mcl - MC) : 0.0f);
-      const float2 pt = make_float2(MC, S);
-      if (lane == 0) {
-        a.part[f] = pt;
-        if (t == tok_tile) a.tokz[fr] = tok_z;
-      }
-    } else {
-      bad = FLAG_BAD_INPUT;
-    }
-    if (++t == ntiles) {
-      t = 0;
-      fr++;
-      if (f + 1 < f1) enter_row();
+  const int tid = threadIdx.x, kb = G.kb;
+  *ok = 1;
+  if (tid >= 2 * kb) return 0.0f;
+  *ok = x >= 0 && x < a.V;
+  const raw* row = group_row<raw>(a, G, g, tid < kb ? tid : tid + 1);
+  return *ok && row ? DT::to_f32(row[x]) : 0.0f;
+}
+
+__device__ __forceinline__ void store_tokens(float z, int ok, float u, int kb, TailLds& L) {
+  const int tid = threadIdx.x;
+  if (tid < 2 * kb) {
+    L.z[tid] = z;
+    if (tid < kb) {
+      L.u[tid] = u;
+      L.xok[tid] = ok;
     }
   }
-  if (lane == 0) raise_flags(a.flags, bad);
+}
+
+// OR of a per-thread value across the workgroup into L.fl (after a barrier).
+__device__ __forceinline__ void or_flags(uint32_t v, TailLds& L) {
+  for (int off = 32; off >= 1; off >>= 1) v |= __shfl_xor(v, off, WAVE);
+  if ((threadIdx.x % WAVE) == 0 && v) atomicOr(&L.fl, v);
 }
 
 // ---------------------------------------------------------------------------
-// k_sd_tail: decision and final token.  grid = (ceil(ntiles / 4), B)
+// k_sd_tail: grid (ceil(ntiles / 4), B)
 // ---------------------------------------------------------------------------
 template <typename DT, bool VL>
-__global__ __launch_bounds__(BLOCK) void k_sd_tail(SdTailArgs a) {
+__global__ __launch_bounds__(BLOCK) void k_sd_tail(SdArgs a) {
   using raw = typename DT::raw;
-  __shared__ float sM[MAXR];
-  __shared__ double sS[MAXR];
-  __shared__ int sN;
-  __shared__ uint32_t sFlags;
-  __shared__ int sLast;
-  const int lane = threadIdx.x % WAVE;
-  const int wave = threadIdx.x / WAVE;
+  __shared__ TailLds L;
+  __shared__ int s_last;
+  const StepArgs& s = a.s;
+  const int lane = threadIdx.x % WAVE, wave = wave_id();
+  const int x = blockIdx.x, X = gridDim.x;
   const int64_t b = blockIdx.y;
-  const raw* target = static_cast<const raw*>(a.s.target);
-  const raw* draft = static_cast<const raw*>(a.s.draft);
-  const int ntiles = a.s.ntiles;
-  const float c = a.s.c;
-  const int64_t V = a.s.V;
-  const Group G = group_of(b, a.s.K, a.s.offsets, a.s.rows_d);
-  if (!G.ok) {  // malformed CSR offsets: nothing of this sequence is read
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      raise_flags(a.s.flags, FLAG_BAD_INPUT);
-      a.num_accepted[b] = 0;
-      a.final_token[b] = 0;
-    }
-    return;
+  const int ntiles = s.ntiles;
+  const Group G = group_of(b, s.K, s.offsets, s.rows_d);
+  if (s.offsets && x == 0 && threadIdx.x == 0) {
+    uint32_t bad = G.ok ? 0u : FLAG_BAD_INPUT;
+    if (b == 0 && s.offsets[0] != 0) bad = FLAG_BAD_INPUT;
+    if (b == s.ngroups - 1 && s.offsets[s.ngroups] != s.rows_d) bad = FLAG_BAD_INPUT;
+    raise_flags(s.flags, bad);
   }
+  if (!G.ok) return;  // malformed CSR offsets: nothing of this sequence is read
   const int kb = G.kb;
   const int64_t t0 = G.d0 + b;
-  const float2* pg = a.s.part + G.fr0 * ntiles;
+  const float2* pg = s.part + G.fr0 * s.nseg;
+  if (threadIdx.x == 0) L.fl = 0;
+  const int32_t xt = token_of(s, G);
+  const float uj = (int)threadIdx.x < kb ? a.uniforms[t0 + threadIdx.x] : 0.0f;
+  const float ufin = a.uniforms[t0 + kb];
+  int ok = 1;
+  const float z = token_logit<DT>(s, G, b, xt, &ok);
+  merge_rows(pg, 2 * kb + 1, s.nseg, kb, L);
+  store_tokens(z, ok, uj, kb, L);
+  __syncthreads();
   uint32_t fl = 0;
+  // accept test up to the first rejection (the same in every workgroup of b)
   if (wave == 0) {
-    merge_group_rows(pg, 2 * kb + 1, ntiles, sM, sS, lane);
     int n = kb;
     for (int j0 = 0; j0 < kb; j0 += WAVE) {
       const int j = j0 + lane;
       bool reject = false;
       if (j < kb) {
-        const int32_t x = a.s.tokens[G.d0 + j];
-        const RowStat st = stat_of(sM, sS, j);
-        const RowStat sd = stat_of(sM, sS, kb + 1 + j);
+        const RowStat st = stat_of(L, j), sd = stat_of(L, kb + 1 + j);
         if (!st.ok || !sd.ok) fl |= FLAG_NONFINITE;
-        if (x < 0 || x >= V) {
+        if (!L.xok[j]) {
           fl |= FLAG_BAD_INPUT;
           reject = true;
         } else {
-          const float zt = a.s.tokz[G.fr0 + j];
-          const float zd = a.s.tokz[G.fr0 + kb + 1 + j];
-          const double rho = exp(log_prob(zt, st, c) - log_prob(zd, sd, c));
-          reject = !((double)a.uniforms[t0 + j] < rho);
+          const double rho = exp(log_prob(L.z[j], st, s.c) - log_prob(L.z[kb + j], sd, s.c));
+          reject = !((double)L.u[j] < rho);
         }
       }
       const uint64_t bal = __ballot(reject);
       if (bal && n == kb) n = j0 + __builtin_ctzll(bal);
     }
-    for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
-    if (lane == 0) {
-      sN = n;
-      sFlags = fl;
-    }
+    if (lane == 0) L.n = n;
   }
+  if (x != 0) fl = 0;  // workgroup 0 reports the decision's flags
   __syncthreads();
-  const int n = sN;
-  fl = 0;
-  const float u = a.uniforms[t0 + kb];
-  const int tile = blockIdx.x * WAVES_PER_BLOCK + wave;
+  const int n = L.n;
+  const raw* trow = group_row<raw>(s, G, b, n);
+  if (x == 0 && threadIdx.x == 0) a.num_accepted[b] = n;
   if (n == kb) {
-    // bonus draw from p_{K_b}: only the workgroup holding the located tile draws
-    if (wave == 0) {
-      const RowStat sk = stat_of(sM, sS, kb);
-      if (!sk.ok) fl |= FLAG_NONFINITE;
-      const int y = draw_from_row<DT, VL>(target + (t0 + kb) * V, V, pg + (int64_t)kb * ntiles, ntiles, sk, c, u,
-                                          lane, &fl, (int)blockIdx.x * WAVES_PER_BLOCK, WAVES_PER_BLOCK);
-      if (lane == 0) {
-        if (y >= 0) a.final_token[b] = y;
-        if (blockIdx.x == 0) a.num_accepted[b] = n;
-        raise_flags(a.s.flags, fl | (blockIdx.x == 0 ? sFlags : 0u));
-      }
+    // every draft accepted: workgroup 0 draws the bonus token from p_{K_b}
+    if (x != 0) return;
+    const RowStat sk = stat_of(L, kb);
+    if (!sk.ok) fl |= FLAG_NONFINITE;
+    const int y = draw_softmax<DT, VL>(trow, s, sk.M, (double)ufin, L, fl);
+    or_flags(fl, L);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      a.final_token[b] = y;
+      raise_flags(s.flags, L.fl);
     }
     return;
   }
   // residual mass of max(0, p_n - q_n) over this wavefront's tile
-  const RowStat st = stat_of(sM, sS, n), sd = stat_of(sM, sS, kb + 1 + n);
+  const raw* drow = group_row<raw>(s, G, b, kb + 1 + n);
+  const RowStat st = stat_of(L, n), sd = stat_of(L, kb + 1 + n);
   const float stf = (float)(1.0 / st.S), sdf = (float)(1.0 / sd.S);
+  const int tile = x * WAVES_PER_BLOCK + wave;
   if (tile < ntiles) {
-    const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tile, lane);
-    const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tile, lane);
-    float s = 0.0f;
+    const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tile, lane);
+    const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, tile, lane);
+    float m = 0.0f;
 #pragma unroll
     for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
       float r[DT::VEC];
-      residual_chunk<DT>(rt, rd, ch, st.M, sd.M, c, stf, sdf, r);
+      residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, r);
 #pragma unroll
-      for (int k = 0; k < DT::VEC; k++) s += r[k];
+      for (int k = 0; k < DT::VEC; k++) m += r[k];
     }
-    s = wave_sum(s);
-    if (lane == 0) st_dev(a.rmass + b * ntiles + tile, s);
+    m = wave_sum(m);
+    if (lane == 0) st_dev(a.rmass + b * ntiles + tile, m);
   }
-  stores_done();  // every wavefront's mass is stored before the workgroup counts it
+  or_flags(fl, L);
+  stores_done();  // this wavefront's mass is at the coherence point
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t mine = (uint32_t)min(WAVES_PER_BLOCK, ntiles - (int)blockIdx.x * WAVES_PER_BLOCK);
-    const uint32_t old = __hip_atomic_fetch_add(a.rcount + b * CSTRIDE, mine, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    sLast = old + mine == (uint32_t)ntiles;
-    if (blockIdx.x == 0) {
-      a.num_accepted[b] = n;
-      raise_flags(a.s.flags, sFlags);
-    }
+    raise_flags(s.flags, L.fl);
+    L.fl = 0;
+    s_last = ctr_add(s.ctr + b * CTR_STRIDE, 1u) + 1u == (uint32_t)X;
   }
   __syncthreads();
-  if (!sLast || wave != 0) return;
-  // last workgroup of sequence b: locate the tile, then draw inside it
+  if (!s_last) return;
+  // the last workgroup of sequence b: locate the tile, then draw inside it
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  const float* rm = a.rmass + b * ntiles;
-  auto weight = [&](int t) -> double { return (double)ld_dev(rm + t); };
-  double before = 0.0, total = 0.0;
-  int last_tile = -1;
-  const int t = locate_tile(ntiles, weight, (double)u, lane, &before, &total, &last_tile);
-  int y;
-  if (!(total > 0.0)) {
+  for (int k = threadIdx.x; k < ntiles; k += BLOCK) L.W[k] = (double)ld_dev(a.rmass + b * ntiles + k);
+  __syncthreads();
+  fl = 0;
+  if (wave == 0) {
+    auto wt = [&](int k) -> double { return L.W[k]; };
+    double before = 0.0, target = 0.0, total = 0.0;
+    int last = -1;
+    const int k = locate(
+        ntiles, wt, 0.0,
+        [&](double tot) {
+          total = tot;
+          return (double)ufin * tot;
+        },
+        lane, &before, &target, &last);
+    int y = -1;
+    if (total > 0.0) {
+      const int tt = k >= 0 ? k : last;
+      const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tt, lane);
+      const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, tt, lane);
+      auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, w); };
+      int last_pos = -1;
+      int idx = tile_search<DT>(wfn, k >= 0 ? (float)(target - before) : INFINITY, lane, &last_pos);
+      if (idx < 0) {
+        fl |= FLAG_CDF_CLAMP;
+        idx = last_pos >= 0 ? last_pos : 0;
+      }
+      y = tt * TILE + idx;
+    }
+    if (lane == 0) L.y = y;
+  }
+  __syncthreads();
+  int y = L.y;
+  if (y < 0) {
     // p_n and q_n agree to rounding: draw from p_n with the same uniform
     fl |= FLAG_ZERO_RESIDUAL;
-    y = draw_from_row<DT, VL>(target + (t0 + n) * V, V, pg + (int64_t)n * ntiles, ntiles, st, c, u, lane, &fl, 0,
-                              ntiles);
-  } else {
-    const int tt = t >= 0 ? t : last_tile;
-    const Raw<DT> rt = load_raw<DT, VL>(target + (t0 + n) * V, V, tt, lane);
-    const Raw<DT> rd = load_raw<DT, VL>(draft + (G.d0 + n) * V, V, tt, lane);
-    auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, st.M, sd.M, c, stf, sdf, w); };
-    int last_pos = -1, idx = -1;
-    if (t >= 0) idx = tile_search<DT>(wfn, (float)((double)u * total - before), lane, &last_pos);
-    else tile_search<DT>(wfn, INFINITY, lane, &last_pos);
-    if (idx < 0) {
-      fl |= FLAG_CDF_CLAMP;
-      idx = last_pos >= 0 ? last_pos : 0;
-    }
-    y = tt * TILE + idx;
+    for (int k = threadIdx.x; k < s.nseg; k += BLOCK) L.P[k] = pg[(int64_t)n * s.nseg + k];
+    __syncthreads();
+    y = draw_softmax<DT, VL>(trow, s, st.M, (double)ufin, L, fl);
   }
-  if (lane == 0) {
+  or_flags(fl, L);
+  __syncthreads();
+  if (threadIdx.x == 0) {
     a.final_token[b] = y;
-    st_dev(a.rcount + b * CSTRIDE, 0u);  // every workgroup of b has counted
-    raise_flags(a.s.flags, fl);
+    raise_flags(s.flags, L.fl);
+    st_dev(s.ctr + b * CTR_STRIDE, 0u);  // every workgroup of b has counted
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_smc_tail: one wavefront per particle, then per prompt.  grid = ceil(P N / 4)
+// k_smc_tail: one workgroup per particle; the last particle of a prompt runs
+// the prompt's ESS, resampling and page-table gather
 // ---------------------------------------------------------------------------
-template <typename DT, bool VL>
-__global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcTailArgs a) {
-  using raw = typename DT::raw;
-  __shared__ float sM[WAVES_PER_BLOCK][MAXR];
-  __shared__ double sS[WAVES_PER_BLOCK][MAXR];
-  const int lane = threadIdx.x % WAVE;
-  const int wib = threadIdx.x / WAVE;
-  const int64_t i = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wib;
-  if (i >= a.s.ngroups) return;
-  const raw* target = static_cast<const raw*>(a.s.target);
-  const int ntiles = a.s.ntiles;
-  const float c = a.s.c;
-  const int64_t V = a.s.V;
-  const int K = a.s.K;
+__device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
+  const StepArgs& s = a.s;
+  const int lane = threadIdx.x % WAVE, wave = wave_id();
   const int N = a.N;
+  const int64_t base = p * N;
   uint32_t fl = 0;
-  // ---- particle: reweight and the (K+1)-th token ---------------------------
-  const int64_t t0 = i * (K + 1), d0 = i * K, fr0 = i * (2 * K + 1);
-  const float2* pg = a.s.part + fr0 * ntiles;
-  merge_group_rows(pg, 2 * K + 1, ntiles, sM[wib], sS[wib], lane);
-  double delta = 0.0;
-  for (int j0 = 0; j0 < K; j0 += WAVE) {
-    const int j = j0 + lane;
-    double dj = 0.0;
-    if (j < K) {
-      const int32_t x = a.s.tokens[d0 + j];
-      const RowStat st = stat_of(sM[wib], sS[wib], j);
-      const RowStat sd = stat_of(sM[wib], sS[wib], K + 1 + j);
-      if (!st.ok || !sd.ok) fl |= FLAG_NONFINITE;
-      if (x < 0 || x >= V) {
-        fl |= FLAG_BAD_INPUT;
-      } else {
-        dj = log_prob(a.s.tokz[fr0 + j], st, c) - log_prob(a.s.tokz[fr0 + K + 1 + j], sd, c);
-      }
-    }
-    delta += wave_sum_f64(dj);
-  }
-  const RowStat sk = stat_of(sM[wib], sS[wib], K);
-  if (!sk.ok) fl |= FLAG_NONFINITE;
-  const float lw = (float)((double)a.logw_in[i] + delta);
-  if (lw != lw || lw == INFINITY) fl |= FLAG_NONFINITE;
-  const int y = draw_from_row<DT, VL>(target + (t0 + K) * V, V, pg + (int64_t)K * ntiles, ntiles, sk, c,
-                                      a.bonus_u[i], lane, &fl, 0, ntiles);
-  if (lane == 0) {
-    a.bonus_token[i] = y;
-    st_dev(a.ws_logw + i, lw);
-  }
-  const int64_t p = i / N;
-  if (wave_add(a.pcount + p * CSTRIDE, 1u, lane) + 1u == (uint32_t)N) {
-    // ---- prompt: ESS, threshold, systematic resampling, page-table gather ----
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int64_t base = p * N;
-    double M = -INFINITY;
-    for (int k0 = 0; k0 < N; k0 += WAVE)
-      if (k0 + lane < N) M = fmax(M, (double)ld_dev(a.ws_logw + base + k0 + lane));
-    M = wave_max_f64(M);
+  for (int k = threadIdx.x; k < N; k += BLOCK) Q.lw[k] = ld_dev(a.ws_logw + base + k);
+  __syncthreads();
+  if (wave == 0) {
+    float mf = -INFINITY;
+    for (int k = lane; k < N; k += WAVE) mf = fmaxf(mf, Q.lw[k]);
+    for (int off = 32; off >= 1; off >>= 1) mf = fmaxf(mf, __shfl_xor(mf, off, WAVE));
+    const double M = (double)mf;
     const bool zero = !(M > -INFINITY);
     if (M == INFINITY || M != M) fl |= FLAG_NONFINITE;
     double Sw = 0.0, Sw2 = 0.0;
@@ -677,7 +774,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcTailArgs a) {
     if (!zero) {
       for (int k0 = 0; k0 < N; k0 += WAVE) {
         const int k = k0 + lane;
-        const double wk = k < N ? exp((double)ld_dev(a.ws_logw + base + k) - M) : 0.0;
+        const double wk = k < N ? exp((double)Q.lw[k] - M) : 0.0;
         Sw += wave_sum_f64(wk);
         Sw2 += wave_sum_f64(wk * wk);
         int lp = wk > 0.0 ? k : -1;
@@ -690,19 +787,16 @@ __global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcTailArgs a) {
     const double E = zero ? 0.0 : Sw * Sw / Sw2;
     const bool do_res = !zero && E < (double)a.ess_frac * (double)N;
     const double u = (double)a.resample_u[p];
-    const bool gather = a.pt_in != nullptr && a.L > 0;
-    const int64_t L = a.L;
     double run = 0.0;
     int carry = 0;  // first slot of the chunk's first particle
     for (int k0 = 0; k0 < N; k0 += WAVE) {
       const int ii = k0 + lane;
-      const float lwi = ii < N ? ld_dev(a.ws_logw + base + ii) : 0.0f;
       int hi;  // particle ii supplies the slots [lo, hi)
       if (do_res) {
-        // slot k descends from the first i with C_i > (u + k) / N, so particle i
-        // receives k in [ceil(N C_{i-1} - u), ceil(N C_i - u)); consecutive
-        // ranges share their end points, so every slot is covered exactly once
-        const double wi = ii < N ? exp((double)lwi - M) : 0.0;
+        // slot k descends from the first i with C_i > (u + k) / N, so particle
+        // i receives k in [ceil(N C_{i-1} - u), ceil(N C_i - u)); consecutive
+        // ranges share their end points, so every slot is covered once
+        const double wi = ii < N ? exp((double)Q.lw[ii] - M) : 0.0;
         const double incl = wave_incl_scan_f64(wi, lane);
         double h = ceil((double)N * ((run + incl) / Sw) - u);
         if (ii >= last_pos) {  // the last particle with positive weight ends at N
@@ -720,36 +814,107 @@ __global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcTailArgs a) {
       hi = max(hi, lo);
       carry = __shfl(hi, WAVE - 1, WAVE);
       if (ii < N) {
-        for (int k = lo; k < hi; k++) a.ancestors[base + k] = ii;
-        a.logw_out[base + ii] = do_res ? 0.0f : lwi;
-      }
-      if (gather) {
-        // rows of the slots this chunk supplies, one wavefront-wide copy each
-        const int kbeg = __shfl(lo, 0, WAVE);
-        for (int k = kbeg; k < carry; k++) {
-          const uint64_t own = __ballot(lo <= k && k < hi);
-          const int64_t src = base + k0 + __builtin_ctzll(own);
-          const int32_t* __restrict__ from = a.pt_in + src * L;
-          int32_t* __restrict__ to = a.pt_out + (base + k) * L;
-          for (int64_t l = lane; l < L; l += WAVE) to[l] = from[l];
+        for (int k = lo; k < hi; k++) {
+          a.ancestors[base + k] = ii;
+          Q.anc[k] = ii;
         }
+        a.logw[base + ii] = do_res ? 0.0f : Q.lw[ii];
       }
     }
     if (lane == 0) {
       a.ess[p] = (float)E;
       a.resampled[p] = do_res ? 1 : 0;
-      st_dev(a.pcount + p * CSTRIDE, 0u);
+    }
+    for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
+    if (lane == 0) raise_flags(s.flags, fl);
+  }
+  __syncthreads();
+  // page-table rows by ancestor (the identity when the prompt kept its particles)
+  if (a.pt_in && a.L > 0) {
+    const int64_t L = a.L;
+    const int32_t* __restrict__ src = a.pt_in + base * L;
+    int32_t* __restrict__ dst = a.pt_out + base * L;
+    const bool v4 = (L % 4) == 0 && (((uintptr_t)src | (uintptr_t)dst) & 15) == 0;
+    if (v4) {
+      const int64_t L4 = L / 4;
+      for (int64_t e = threadIdx.x; e < (int64_t)N * L4; e += BLOCK) {
+        const int64_t k = e / L4, l = e - k * L4;
+        reinterpret_cast<int4*>(dst)[k * L4 + l] = reinterpret_cast<const int4*>(src)[Q.anc[k] * L4 + l];
+      }
+    } else {
+      for (int64_t e = threadIdx.x; e < (int64_t)N * L; e += BLOCK) {
+        const int64_t k = e / L, l = e - k * L;
+        dst[k * L + l] = src[Q.anc[k] * L + l];
+      }
     }
   }
-  for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
-  if (lane == 0) raise_flags(a.s.flags, fl);
+  if (threadIdx.x == 0) st_dev(s.ctr + p * CTR_STRIDE, 0u);  // every particle of p has counted
+}
+
+template <typename DT, bool VL>
+__global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcArgs a) {
+  using raw = typename DT::raw;
+  __shared__ SharedLds sh;
+  __shared__ int s_last;
+  TailLds& L = sh.t;
+  const StepArgs& s = a.s;
+  const int lane = threadIdx.x % WAVE, wave = wave_id();
+  const int64_t i = blockIdx.x;
+  const int K = s.K;
+  const Group G = group_of(i, K, nullptr, s.rows_d);
+  const float2* pg = s.part + G.fr0 * s.nseg;
+  if (threadIdx.x == 0) L.fl = 0;
+  const int32_t xt = token_of(s, G);
+  const float lw_in = a.logw[i];
+  const float ub = a.bonus_u[i];
+  int ok = 1;
+  const float z = token_logit<DT>(s, G, i, xt, &ok);
+  merge_rows(pg, 2 * K + 1, s.nseg, K, L);
+  store_tokens(z, ok, 0.0f, K, L);
+  __syncthreads();
+  uint32_t fl = 0;
+  float lw = 0.0f;
+  if (wave == 0) {
+    double delta = 0.0;
+    for (int j0 = 0; j0 < K; j0 += WAVE) {
+      const int j = j0 + lane;
+      double dj = 0.0;
+      if (j < K) {
+        const RowStat st = stat_of(L, j), sd = stat_of(L, K + 1 + j);
+        if (!st.ok || !sd.ok) fl |= FLAG_NONFINITE;
+        if (!L.xok[j]) fl |= FLAG_BAD_INPUT;
+        else dj = log_prob(L.z[j], st, s.c) - log_prob(L.z[K + j], sd, s.c);
+      }
+      delta += wave_sum_f64(dj);
+    }
+    lw = (float)((double)lw_in + delta);
+    if (lw != lw || lw == INFINITY) fl |= FLAG_NONFINITE;
+  }
+  const RowStat sk = stat_of(L, K);
+  if (!sk.ok) fl |= FLAG_NONFINITE;
+  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, sk.M, (double)ub, L, fl);
+  or_flags(fl, L);
+  __syncthreads();
+  const int64_t p = i / a.N;
+  if (threadIdx.x == 0) {
+    a.bonus_token[i] = y;
+    st_dev(a.ws_logw + i, lw);  // thread 0 is lane 0 of wave 0, which holds lw
+    raise_flags(s.flags, L.fl);
+    stores_done();
+    s_last = ctr_add(s.ctr + p * CTR_STRIDE, 1u) + 1u == (uint32_t)a.N;
+  }
+  __syncthreads();
+  if (s_last) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    smc_prompt_tail(a, p, sh.p);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// host launchers
+// host: plans and launches
 // ---------------------------------------------------------------------------
-// Workgroups of BLOCK threads the current device holds at once for `kernel`
-// (queried once per device and kernel); the streaming grid is sized to it.
+// Workgroups the current device holds at once for `kernel` (queried once per
+// device and kernel).
 static int resident_blocks(const void* kernel) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
@@ -765,43 +930,76 @@ static int resident_blocks(const void* kernel) {
   return cus * per_cu;
 }
 
-template <typename DT, bool VL>
-static hipError_t launch_stream_t(const StreamArgs& a, hipStream_t s) {
-  constexpr int PF = DT::VEC == 8 ? 2 : 1;  // tiles in flight beyond the one being reduced
-  const void* k = reinterpret_cast<const void*>(&k_stream<DT, VL, PF>);
-  const int resident = resident_blocks(k);
+// tiles in flight per wavefront (16 VGPRs per bf16 tile, 32 per fp32 tile)
+template <typename DT>
+constexpr int slots_of() {
+  return DT::VEC == 8 ? 3 : 2;
+}
+
+template <typename K>
+static const void* kptr(K k) {
+  return reinterpret_cast<const void*>(k);
+}
+
+static const void* stream_kernel(bool bf16, bool vec) {
+  if (bf16) return vec ? kptr(&k_stream<Bf16, true, slots_of<Bf16>()>) : kptr(&k_stream<Bf16, false, slots_of<Bf16>()>);
+  return vec ? kptr(&k_stream<F32, true, slots_of<F32>()>) : kptr(&k_stream<F32, false, slots_of<F32>()>);
+}
+
+// Segments long enough that each resident wavefront streams about 32 units
+// (fewer wavefront reductions on large calls), at most 8 tiles so that a draw
+// searches at most 8 tiles of a segment.  The streaming grid is what the
+// device holds at once, fewer when there is not one unit per wavefront.
+hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p) {
+  const int resident = resident_blocks(stream_kernel(bf16, vec));
   if (resident <= 0) return hipErrorInvalidDevice;
-  int64_t blocks = (a.total_tiles + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
-  if (blocks > resident) blocks = resident;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((k_stream<DT, VL, PF>), dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
-  return hipGetLastError();
+  const int64_t waves = (int64_t)resident * WAVES_PER_BLOCK;
+  const int64_t tiles = rows * ntiles;
+  int64_t seg = tiles / (32 * waves);
+  seg = seg < 1 ? 1 : (seg > 8 ? 8 : seg);
+  if (seg > ntiles) seg = ntiles;
+  const int nseg = (int)((ntiles + seg - 1) / seg);
+  p->seg = (ntiles + nseg - 1) / nseg;
+  p->nseg = nseg;
+  p->units = rows * nseg;
+  const int64_t want = (p->units + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
+  p->grid = (int)(want < resident ? want : resident);
+  if (p->grid < 1) p->grid = 1;
+  return hipSuccess;
+}
+
+static hipError_t launch_stream(const StepArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s,
+                                hipEvent_t mark) {
+  void* args[] = {const_cast<StepArgs*>(&a)};
+  hipError_t e = hipLaunchKernel(stream_kernel(bf16, vec), dim3(p.grid), dim3(BLOCK), args, 0, s);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
+  return e;
 }
 
 template <typename DT, bool VL>
-static hipError_t launch_sd_t(const SdTailArgs& a, hipStream_t s) {
-  hipError_t e = launch_stream_t<DT, VL>(a.s, s);
-  if (e != hipSuccess) return e;
+static hipError_t launch_sd_t(const SdArgs& a, hipStream_t s) {
   const unsigned gx = (unsigned)((a.s.ntiles + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK);
   hipLaunchKernelGGL((k_sd_tail<DT, VL>), dim3(gx, (unsigned)a.s.ngroups), dim3(BLOCK), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_sd(const SdTailArgs& a, bool bf16, bool vec, hipStream_t s) {
+hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark) {
+  hipError_t e = launch_stream(a.s, p, bf16, vec, s, mark);
+  if (e != hipSuccess) return e;
   if (bf16) return vec ? launch_sd_t<Bf16, true>(a, s) : launch_sd_t<Bf16, false>(a, s);
   return vec ? launch_sd_t<F32, true>(a, s) : launch_sd_t<F32, false>(a, s);
 }
 
 template <typename DT, bool VL>
-static hipError_t launch_smc_t(const SmcTailArgs& a, hipStream_t s) {
-  hipError_t e = launch_stream_t<DT, VL>(a.s, s);
-  if (e != hipSuccess) return e;
-  const unsigned g = (unsigned)((a.s.ngroups + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK);
-  hipLaunchKernelGGL((k_smc_tail<DT, VL>), dim3(g), dim3(BLOCK), 0, s, a);
+static hipError_t launch_smc_t(const SmcArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_smc_tail<DT, VL>), dim3((unsigned)a.s.ngroups), dim3(BLOCK), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_smc(const SmcTailArgs& a, bool bf16, bool vec, hipStream_t s) {
+hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark) {
+  hipError_t e = launch_stream(a.s, p, bf16, vec, s, mark);
+  if (e != hipSuccess) return e;
   if (bf16) return vec ? launch_smc_t<Bf16, true>(a, s) : launch_smc_t<Bf16, false>(a, s);
   return vec ? launch_smc_t<F32, true>(a, s) : launch_smc_t<F32, false>(a, s);
 }

@@ -9,40 +9,49 @@
 
 namespace smcsd {
 
-// k_stream: softmax partials of every tile and the logit of each row's
-// draft token, for groups (SD sequences / SMC particles) laid out group-major.
-struct StreamArgs {
+// Counter lines of the workspace header, 64 bytes apart: one per SD sequence
+// (tail workgroups that stored their residual masses) or one per SMC prompt
+// (particles finished).
+constexpr int CTR_STRIDE = 16;  // uint32 per 64-byte line
+constexpr int64_t CTR_LINES = SMCSD_WORKSPACE_COUNTER_BYTES / 64;
+
+// What both operations stream.  Rows are taken group by group (a group is an
+// SD sequence or an SMC particle: its target rows 0..K_b, then its draft rows
+// 0..K_b-1); each row is cut into nseg segments of `seg` tiles; a unit is one
+// (row, segment).
+struct StepArgs {
   const void* target;
   const void* draft;
   const int32_t* offsets;  // CSR over draft rows, or null (fixed K)
   const int32_t* tokens;   // draft token of each draft row
-  int64_t ngroups, rows_t, rows_d, V, total_tiles;
-  int K, ntiles;
-  float c;         // log2(e) / T
-  float2* part;    // [total_tiles] partial (mc, s) of each tile, group-major
-  float* tokz;     // [rows] logit of each row's draft token, group-major rows
+  int64_t ngroups, rows_t, rows_d, V;
+  int K;          // draft length (largest, for CSR input)
+  int ntiles;     // tiles per row
+  int seg;        // tiles per segment
+  int nseg;       // segments per row
+  int64_t units;  // rows * nseg
+  float c;        // log2(e) / T
+  float2* part;   // [units] segment partials (max of z c, sum of 2^(z c - max))
+  uint32_t* ctr;  // counter lines (zero between calls)
   uint32_t* flags;
 };
 
-struct SdTailArgs {
-  StreamArgs s;
+struct SdArgs {
+  StepArgs s;
   const float* uniforms;
-  uint32_t* rcount;  // [B] tiles of residual mass stored (zero between calls)
-  float* rmass;      // [B * ntiles] residual mass per tile
+  float* rmass;  // [B * ntiles] residual mass per tile
   int32_t* num_accepted;
   int32_t* final_token;
 };
 
-struct SmcTailArgs {
-  StreamArgs s;
+struct SmcArgs {
+  StepArgs s;
   int N, L;
   float ess_frac;
   const float* bonus_u;
   const float* resample_u;
-  const float* logw_in;
-  float* logw_out;   // same buffer as logw_in (each entry is read before it is written)
-  float* ws_logw;    // [P*N] reweighted log-weights
-  uint32_t* pcount;  // [P] particles finished per prompt (zero between calls)
+  float* logw;     // in/out (each entry is read before its prompt's particles are rewritten)
+  float* ws_logw;  // [P*N] reweighted log-weights
   const int32_t* pt_in;
   int32_t* pt_out;
   int32_t* bonus_token;
@@ -51,7 +60,17 @@ struct SmcTailArgs {
   int32_t* resampled;
 };
 
-hipError_t launch_sd(const SdTailArgs& a, bool bf16, bool vec, hipStream_t s);
-hipError_t launch_smc(const SmcTailArgs& a, bool bf16, bool vec, hipStream_t s);
+// Segment length and streaming grid of a call.
+struct Plan {
+  int seg, nseg;
+  int64_t units;
+  int grid;
+};
+
+hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p);
+// Each launches the streaming kernel, records `mark` (a hipEvent_t, may be
+// null) after it, then launches the tail kernel.
+hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark);
+hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark);
 
 }  // namespace smcsd
