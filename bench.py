@@ -32,6 +32,103 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = [os.path.join(ROOT, "include", "smcsd.h")] + sorted(
+    os.path.join(ROOT, "smc_resampling_amd", "csrc", f) for f in os.listdir(os.path.join(ROOT, "smc_resampling_amd",
+                                                                                          "csrc")))
+
+
+def kernel_sources_hash() -> str:
+    """sha256 of the library's kernel sources (the header and csrc/*)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def _csv_rows(path):
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+def summarize(dirs, copy_bytes=None, kernel="k_stream"):
+    """Text summary of rocprofv3 output directories: kernel statistics
+    (--kernel-trace --stats) and per-dispatch averages of PMC counters
+    (--pmc), with HBM traffic per launch of `kernel` when the directories
+    hold FETCH_SIZE / WRITE_SIZE and a copy of `copy_bytes` calibrates them."""
+    out = [f"kernel_sources_sha256: {kernel_sources_hash()}"]
+    avg = {}  # (kernel, counter) -> KiB per dispatch
+    peak = {}  # (kernel, counter) -> largest single dispatch
+    for d in dirs:
+        st = _find(d, "kernel_stats.csv")
+        if st:
+            out.append(f"kernel statistics ({os.path.relpath(st, ROOT)}):")
+            out.append("  name | calls | average ns | min ns | max ns")
+            for r in _csv_rows(st)[:8]:
+                out.append(f"  {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                           f"{r['MaxNs']}")
+        cc = _find(d, "counter_collection.csv")
+        if cc:
+            acc = {}
+            for r in _csv_rows(cc):
+                key = (r["Kernel_Name"], r["Counter_Name"])
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+            out.append(f"counters, average per dispatch ({os.path.relpath(cc, ROOT)}):")
+            for (k, c), v in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+                a = sum(v) / len(v)
+                avg[(k, c)] = a
+                peak[(k, c)] = max(v)
+                if len(out) < 60:
+                    out.append(f"  {k[:90]} | {c} | dispatches {len(v)} | {a:.1f}")
+    if copy_bytes:
+        def pick(table, name_part, counter):
+            vals = [v for (k, c), v in table.items() if name_part in k and c == counter]
+            return max(vals) if vals else None
+
+        res = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            # the calibration copy is the largest copy dispatch of the run
+            kv, cv = pick(avg, kernel, counter), pick(peak, "copyBuffer", counter)
+            if kv is None or cv is None:
+                continue
+            factor = cv * 1024.0 / copy_bytes  # counter KiB per byte the copy moves
+            res[counter] = kv * 1024.0 / factor
+            out.append(f"{counter}: {kernel} {kv:.1f} KiB/dispatch, copy of {copy_bytes} B reads {cv:.1f} KiB "
+                       f"(factor {factor:.4f}) -> {res[counter]:.0f} B per launch")
+        if len(res) == 2:
+            out.append(f"traffic_bytes_per_launch: {res['FETCH_SIZE'] + res['WRITE_SIZE']:.0f}")
+    return "\n".join(out)
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per k_stream launch from the committed counter summary of this
+    workload, or None when there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"k_stream_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_hash() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,11 +139,18 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--max-batch-gb", type=float, default=24.0)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many bytes (scales rocprofv3 byte counters)")
+    ap.add_argument("--summarize", nargs="+", default=None,
+                    help="print a summary of these rocprofv3 output directories and exit")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize(args.summarize, args.copy_calibration or None))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus N>1 is not supported (per-GPU sharding "
                                    "is described in DESIGN.md)"}))
@@ -177,6 +281,14 @@ def main():
         f"{bytes_total / steps / (ms_per_step / 1e3) / 1e9:.0f} GB/s per call; k_stream {stream_ms * 1e3:.2f} us "
         f"({achieved:.0f} GB/s), decision kernel {tail_ms * 1e3:.2f} us, flags={flags}")
 
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---------------- CPU oracle on a bounded sample --------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -239,7 +351,7 @@ def main():
                    "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T, "launch": args.launch,
                    "input_batches": nb, "status_flags": flags},
         "roofline": {"bound": "hbm", "kernel": "k_stream", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(cfg.name),
                      "algorithmic_bytes_per_launch": bytes_total / steps, "bytes_per_element": e,
                      "kernel_us": stream_ms * 1e3, "decision_kernel_us": tail_ms * 1e3,
                      "call_us": ms_per_step * 1e3},
