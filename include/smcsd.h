@@ -113,8 +113,8 @@ enum {
 #define SMCSD_MAX_V 524288 /* largest vocabulary                                 */
 #define SMCSD_WORKSPACE_ALIGN 256
 /* The first bytes of every workspace hold counters only (shape independent),
-   one 64-byte line each: one per SD sequence or one per SMC prompt, so
-   sd_verify needs B <= 65535 and smc_reweight_resample P <= 65536. */
+   one 64-byte line per SMC prompt, so smc_reweight_resample needs P <= 65536
+   (sd_verify keeps the same header and does not use it). */
 #define SMCSD_WORKSPACE_COUNTER_BYTES (4u << 20)
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */

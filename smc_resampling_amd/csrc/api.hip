@@ -33,20 +33,17 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
 // use) and, for SMC, the reweighted log-weights.
 constexpr size_t kCounterBytes = SMCSD_WORKSPACE_COUNTER_BYTES;
 
-// One counter line per SD sequence (the SD tail grid also has one row of
-// workgroups per sequence) or per SMC prompt.
-bool sd_counters_fit(int64_t B) { return B <= smcsd::CTR_LINES && B <= 65535; }
+// One counter line per SMC prompt.
 bool smc_counters_fit(int64_t P) { return P <= smcsd::CTR_LINES; }
 
 struct SdLayout {
-  size_t rmass, part, total;
+  size_t part, total;
 };
 
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
   SdLayout l;
-  l.rmass = kCounterBytes;
-  l.part = align_up(l.rmass + sizeof(float) * (size_t)B * nt);
+  l.part = kCounterBytes;
   l.total = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
   return l;
 }
@@ -136,7 +133,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
   if (B < 0 || K < 0 || V < 1 || !temperature_ok(temperature)) return SMCSD_ERR_INVALID_ARG;
   if (V > SMCSD_MAX_V) return SMCSD_ERR_UNSUPPORTED;
-  if (K > SMCSD_MAX_K || !sd_counters_fit(B)) return SMCSD_ERR_UNSUPPORTED;
+  if (K > SMCSD_MAX_K) return SMCSD_ERR_UNSUPPORTED;
   if (total_draft_rows < 0 || total_draft_rows > (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
   if (!draft_offsets && total_draft_rows != (int64_t)B * K) return SMCSD_ERR_INVALID_ARG;
   if (B == 0) return SMCSD_OK;
@@ -155,7 +152,6 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   fill_step(&a.s, plan, target_logits, draft_logits, draft_offsets, draft_tokens, B, total_draft_rows + B,
             total_draft_rows, V, K, temperature, ws, l.part, status_flags);
   a.uniforms = uniforms;
-  a.rmass = reinterpret_cast<float*>(ws + l.rmass);
   a.num_accepted = num_accepted;
   a.final_token = final_token;
   return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_phase_mark()) == hipSuccess

@@ -352,13 +352,16 @@ __device__ __forceinline__ RowStat stat_of(const TailLds& L, int r) {
   return rs;
 }
 
-// fold partial (pm, ps) into running statistics (m, s) (log2 domain, fp64 sum)
+// Fold partial (pm, ps) into running statistics (m, s): log2-domain maxima,
+// fp64 sums.  The rescaling factor 2^(smaller - larger) <= 1 comes from the
+// fp32 exponential (relative error about 1e-7); a factor of a -inf maximum is 0
+// and keeps a NaN sum NaN.
 __device__ __forceinline__ void fold(float& m, double& s, float pm, double ps) {
   if (pm > m) {
-    s = (m > -INFINITY ? s * exp2((double)m - (double)pm) : s * 0.0) + ps;
+    s = s * (double)(m > -INFINITY ? __builtin_amdgcn_exp2f(m - pm) : 0.0f) + ps;
     m = pm;
   } else {
-    s += pm > -INFINITY ? ps * exp2((double)pm - (double)m) : ps * 0.0;
+    s += ps * (double)(pm > -INFINITY ? __builtin_amdgcn_exp2f(pm - m) : 0.0f);
   }
 }
 
@@ -367,10 +370,11 @@ __device__ __forceinline__ void fold(float& m, double& s, float pm, double ps) {
 // L.lS; the partials of row `keep` are copied to L.P.  Whole workgroup, `tpr`
 // threads per row, fixed combination order, so equal rows get equal
 // statistics.
+template <int NT>
 __device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, int keep, TailLds& L) {
   int tpr = 16;
-  while (tpr > 1 && BLOCK / tpr < R) tpr >>= 1;
-  const int rpp = BLOCK / tpr;
+  while (tpr > 1 && NT / tpr < R) tpr >>= 1;
+  const int rpp = NT / tpr;
   const int sub = threadIdx.x & (tpr - 1);
   for (int r0 = 0; r0 < R; r0 += rpp) {
     const int r = r0 + (int)threadIdx.x / tpr;
@@ -454,7 +458,7 @@ __device__ __forceinline__ float2 tile_partial_of(const Raw<DT>& r, float c) {
 // Inverse-CDF draw from softmax(z c) of `row` (row maximum M, log2 domain; its
 // segment partials in L.P) with uniform u.  Whole workgroup; every thread
 // gets the token.
-template <typename DT, bool VL>
+template <typename DT, bool VL, int NW = WAVES_PER_BLOCK>
 __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const StepArgs& a, float M, double u,
                             TailLds& L, uint32_t& fl) {
   const int lane = threadIdx.x % WAVE, wave = wave_id();
@@ -488,7 +492,7 @@ __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const Step
     mt = L.P[sg].x;
   } else {
     // 2. the tile inside the segment
-    for (int t = tb + wave; t < te; t += WAVES_PER_BLOCK) {
+    for (int t = tb + wave; t < te; t += NW) {
       const Raw<DT> r = load_tile<DT, VL>(row, a.V, t, lane);
       const float2 pt = tile_partial_of<DT>(r, c);
       if (lane == 0) {
@@ -597,20 +601,21 @@ __device__ __forceinline__ void or_flags(uint32_t v, TailLds& L) {
 }
 
 // ---------------------------------------------------------------------------
-// k_sd_tail: grid (ceil(ntiles / 4), B)
+// k_sd_tail: one workgroup of SD_WAVES wavefronts per sequence
 // ---------------------------------------------------------------------------
+constexpr int SD_WAVES = 16;
+constexpr int SD_BLOCK = SD_WAVES * WAVE;
+
 template <typename DT, bool VL>
-__global__ __launch_bounds__(BLOCK) void k_sd_tail(SdArgs a) {
+__global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   using raw = typename DT::raw;
   __shared__ TailLds L;
-  __shared__ int s_last;
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
-  const int x = blockIdx.x, X = gridDim.x;
-  const int64_t b = blockIdx.y;
+  const int64_t b = blockIdx.x;
   const int ntiles = s.ntiles;
   const Group G = group_of(b, s.K, s.offsets, s.rows_d);
-  if (s.offsets && x == 0 && threadIdx.x == 0) {
+  if (s.offsets && threadIdx.x == 0) {
     uint32_t bad = G.ok ? 0u : FLAG_BAD_INPUT;
     if (b == 0 && s.offsets[0] != 0) bad = FLAG_BAD_INPUT;
     if (b == s.ngroups - 1 && s.offsets[s.ngroups] != s.rows_d) bad = FLAG_BAD_INPUT;
@@ -626,11 +631,11 @@ __global__ __launch_bounds__(BLOCK) void k_sd_tail(SdArgs a) {
   const float ufin = a.uniforms[t0 + kb];
   int ok = 1;
   const float z = token_logit<DT>(s, G, b, xt, &ok);
-  merge_rows(pg, 2 * kb + 1, s.nseg, kb, L);
+  merge_rows<SD_BLOCK>(pg, 2 * kb + 1, s.nseg, kb, L);
   store_tokens(z, ok, uj, kb, L);
   __syncthreads();
   uint32_t fl = 0;
-  // accept test up to the first rejection (the same in every workgroup of b)
+  // accept test up to the first rejection
   if (wave == 0) {
     int n = kb;
     for (int j0 = 0; j0 < kb; j0 += WAVE) {
@@ -652,101 +657,90 @@ __global__ __launch_bounds__(BLOCK) void k_sd_tail(SdArgs a) {
     }
     if (lane == 0) L.n = n;
   }
-  if (x != 0) fl = 0;  // workgroup 0 reports the decision's flags
   __syncthreads();
   const int n = L.n;
   const raw* trow = group_row<raw>(s, G, b, n);
-  if (x == 0 && threadIdx.x == 0) a.num_accepted[b] = n;
+  int y;
   if (n == kb) {
-    // every draft accepted: workgroup 0 draws the bonus token from p_{K_b}
-    if (x != 0) return;
+    // every draft accepted: the bonus token from p_{K_b}
     const RowStat sk = stat_of(L, kb);
     if (!sk.ok) fl |= FLAG_NONFINITE;
-    const int y = draw_softmax<DT, VL>(trow, s, sk.M, (double)ufin, L, fl);
-    or_flags(fl, L);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      a.final_token[b] = y;
-      raise_flags(s.flags, L.fl);
-    }
-    return;
-  }
-  // residual mass of max(0, p_n - q_n) over this wavefront's tile
-  const raw* drow = group_row<raw>(s, G, b, kb + 1 + n);
-  const RowStat st = stat_of(L, n), sd = stat_of(L, kb + 1 + n);
-  const float stf = (float)(1.0 / st.S), sdf = (float)(1.0 / sd.S);
-  const int tile = x * WAVES_PER_BLOCK + wave;
-  if (tile < ntiles) {
-    const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tile, lane);
-    const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, tile, lane);
-    float m = 0.0f;
+    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, sk.M, (double)ufin, L, fl);
+  } else {
+    // residual max(0, p_n - q_n): each wavefront weighs its tiles and keeps
+    // the last one in registers for the search
+    const raw* drow = group_row<raw>(s, G, b, kb + 1 + n);
+    const RowStat st = stat_of(L, n), sd = stat_of(L, kb + 1 + n);
+    const float stf = (float)(1.0 / st.S), sdf = (float)(1.0 / sd.S);
+    Raw<DT> rt, rd;
+    int held = -1;
+    for (int t = wave; t < ntiles; t += SD_WAVES) {
+      rt = load_tile<DT, VL>(trow, s.V, t, lane);
+      rd = load_tile<DT, VL>(drow, s.V, t, lane);
+      held = t;
+      float m = 0.0f;
 #pragma unroll
-    for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-      float r[DT::VEC];
-      residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, r);
+      for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+        float r[DT::VEC];
+        residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, r);
 #pragma unroll
-      for (int k = 0; k < DT::VEC; k++) m += r[k];
-    }
-    m = wave_sum(m);
-    if (lane == 0) st_dev(a.rmass + b * ntiles + tile, m);
-  }
-  or_flags(fl, L);
-  stores_done();  // this wavefront's mass is at the coherence point
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    raise_flags(s.flags, L.fl);
-    L.fl = 0;
-    s_last = ctr_add(s.ctr + b * CTR_STRIDE, 1u) + 1u == (uint32_t)X;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // the last workgroup of sequence b: locate the tile, then draw inside it
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  for (int k = threadIdx.x; k < ntiles; k += BLOCK) L.W[k] = (double)ld_dev(a.rmass + b * ntiles + k);
-  __syncthreads();
-  fl = 0;
-  if (wave == 0) {
-    auto wt = [&](int k) -> double { return L.W[k]; };
-    double before = 0.0, target = 0.0, total = 0.0;
-    int last = -1;
-    const int k = locate(
-        ntiles, wt, 0.0,
-        [&](double tot) {
-          total = tot;
-          return (double)ufin * tot;
-        },
-        lane, &before, &target, &last);
-    int y = -1;
-    if (total > 0.0) {
-      const int tt = k >= 0 ? k : last;
-      const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tt, lane);
-      const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, tt, lane);
-      auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, w); };
-      int last_pos = -1;
-      int idx = tile_search<DT>(wfn, k >= 0 ? (float)(target - before) : INFINITY, lane, &last_pos);
-      if (idx < 0) {
-        fl |= FLAG_CDF_CLAMP;
-        idx = last_pos >= 0 ? last_pos : 0;
+        for (int k = 0; k < DT::VEC; k++) m += r[k];
       }
-      y = tt * TILE + idx;
+      m = wave_sum(m);
+      if (lane == 0) L.W[t] = (double)m;
     }
-    if (lane == 0) L.y = y;
-  }
-  __syncthreads();
-  int y = L.y;
-  if (y < 0) {
-    // p_n and q_n agree to rounding: draw from p_n with the same uniform
-    fl |= FLAG_ZERO_RESIDUAL;
-    for (int k = threadIdx.x; k < s.nseg; k += BLOCK) L.P[k] = pg[(int64_t)n * s.nseg + k];
     __syncthreads();
-    y = draw_softmax<DT, VL>(trow, s, st.M, (double)ufin, L, fl);
+    if (wave == 0) {
+      auto wt = [&](int k) -> double { return L.W[k]; };
+      double before = 0.0, target = 0.0, total = 0.0;
+      int last = -1;
+      const int k = locate(
+          ntiles, wt, 0.0,
+          [&](double tot) {
+            total = tot;
+            return (double)ufin * tot;
+          },
+          lane, &before, &target, &last);
+      if (lane == 0) {
+        L.sel = total > 0.0 ? (k >= 0 ? k : last) : -1;
+        L.clamp = k < 0;
+        L.target = target - before;  // the target inside the located tile
+      }
+    }
+    __syncthreads();
+    const int tt = L.sel;
+    if (tt >= 0) {
+      // the wavefront that weighed tile tt draws inside it
+      if (wave == tt % SD_WAVES) {
+        if (held != tt) {
+          rt = load_tile<DT, VL>(trow, s.V, tt, lane);
+          rd = load_tile<DT, VL>(drow, s.V, tt, lane);
+        }
+        auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, w); };
+        int last_pos = -1;
+        int idx = tile_search<DT>(wfn, L.clamp ? INFINITY : (float)L.target, lane, &last_pos);
+        if (idx < 0) {
+          fl |= FLAG_CDF_CLAMP;
+          idx = last_pos >= 0 ? last_pos : 0;
+        }
+        if (lane == 0) L.y = tt * TILE + idx;
+      }
+      __syncthreads();
+      y = L.y;
+    } else {
+      // p_n and q_n agree to rounding: draw from p_n with the same uniform
+      fl |= FLAG_ZERO_RESIDUAL;
+      for (int k = threadIdx.x; k < s.nseg; k += SD_BLOCK) L.P[k] = pg[(int64_t)n * s.nseg + k];
+      __syncthreads();
+      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, st.M, (double)ufin, L, fl);
+    }
   }
   or_flags(fl, L);
   __syncthreads();
   if (threadIdx.x == 0) {
+    a.num_accepted[b] = n;
     a.final_token[b] = y;
     raise_flags(s.flags, L.fl);
-    st_dev(s.ctr + b * CTR_STRIDE, 0u);  // every workgroup of b has counted
   }
 }
 
@@ -869,7 +863,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcArgs a) {
   const float ub = a.bonus_u[i];
   int ok = 1;
   const float z = token_logit<DT>(s, G, i, xt, &ok);
-  merge_rows(pg, 2 * K + 1, s.nseg, K, L);
+  merge_rows<BLOCK>(pg, 2 * K + 1, s.nseg, K, L);
   store_tokens(z, ok, 0.0f, K, L);
   __syncthreads();
   uint32_t fl = 0;
@@ -979,8 +973,7 @@ static hipError_t launch_stream(const StepArgs& a, const Plan& p, bool bf16, boo
 
 template <typename DT, bool VL>
 static hipError_t launch_sd_t(const SdArgs& a, hipStream_t s) {
-  const unsigned gx = (unsigned)((a.s.ntiles + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK);
-  hipLaunchKernelGGL((k_sd_tail<DT, VL>), dim3(gx, (unsigned)a.s.ngroups), dim3(BLOCK), 0, s, a);
+  hipLaunchKernelGGL((k_sd_tail<DT, VL>), dim3((unsigned)a.s.ngroups), dim3(SD_BLOCK), 0, s, a);
   return hipGetLastError();
 }
 

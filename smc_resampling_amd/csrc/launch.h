@@ -9,8 +9,7 @@
 
 namespace smcsd {
 
-// Counter lines of the workspace header, 64 bytes apart: one per SD sequence
-// (tail workgroups that stored their residual masses) or one per SMC prompt
+// Counter lines of the workspace header, 64 bytes apart: one per SMC prompt
 // (particles finished).
 constexpr int CTR_STRIDE = 16;  // uint32 per 64-byte line
 constexpr int64_t CTR_LINES = SMCSD_WORKSPACE_COUNTER_BYTES / 64;
@@ -39,7 +38,6 @@ struct StepArgs {
 struct SdArgs {
   StepArgs s;
   const float* uniforms;
-  float* rmass;  // [B * ntiles] residual mass per tile
   int32_t* num_accepted;
   int32_t* final_token;
 };

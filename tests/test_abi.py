@@ -70,7 +70,7 @@ def _sd(s, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=2), 1), (dict(B=70000, K=0, rows_d=0), 2), (dict(T=0.0), 1), (dict(T=-1.0), 1), (dict(T=math.nan), 1), (dict(T=math.inf), 1),
+    (dict(dtype=2), 1), (dict(V=1 << 20), 2), (dict(T=0.0), 1), (dict(T=-1.0), 1), (dict(T=math.nan), 1), (dict(T=math.inf), 1),
     (dict(V=0), 1), (dict(B=-1), 1), (dict(K=-1), 1), (dict(K=300, rows_d=1200), 2), (dict(rows_d=7), 1),
     (dict(rows_d=9), 1), (dict(tgt=None), 1), (dict(u=None), 1), (dict(drf=None), 1), (dict(na=None), 1),
     (dict(ws=None), 3), (dict(wsb=16), 3), (dict(ws=FAKE + 8), 3), (dict(off=FAKE, rows_d=9), 1),
