@@ -81,32 +81,84 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
 }
 
+// 64-bit values move through DPP as two 32-bit halves
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, BANK_MASK, BOUND_ZERO);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, BANK_MASK, BOUND_ZERO);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ float dpp_f32m(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, BOUND_ZERO));
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// OR of a small flag word over the 64 lanes (one ballot per bit).
+__device__ __forceinline__ uint32_t wave_or_flags(uint32_t v) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int bit = 0; bit < 8; bit++)
+    if (__ballot((v >> bit) & 1u)) r |= 1u << bit;
+  return r;
+}
+
+// Sum and maximum over the 64 lanes in a fixed order (deterministic for a
+// given lane assignment); every lane gets the result.
 __device__ __forceinline__ double wave_sum_f64(double v) {
-  // fixed butterfly order: deterministic for a given lane assignment
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, WAVE);
-  return v;
+  v += dpp_f64<DPP_QUAD_1032>(v);
+  v += dpp_f64<DPP_QUAD_2301>(v);
+  v += dpp_f64<DPP_ROR4>(v);
+  v += dpp_f64<DPP_ROR8>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 __device__ __forceinline__ double wave_max_f64(double v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, WAVE));
-  return v;
+  v = fmax(v, dpp_f64<DPP_QUAD_1032>(v));
+  v = fmax(v, dpp_f64<DPP_QUAD_2301>(v));
+  v = fmax(v, dpp_f64<DPP_ROR4>(v));
+  v = fmax(v, dpp_f64<DPP_ROR8>(v));
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
 }
 
-// inclusive prefix sum over the 64 lanes (ascending lane order)
-__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-  for (int off = 1; off < WAVE; off <<= 1) {
-    float o = __shfl_up(v, off, WAVE);
-    if (lane >= off) v += o;
-  }
-  return v;
+// Inclusive prefix sums over the 64 lanes in ascending lane order, with DPP
+// row shifts inside 16-lane rows, then the row totals carried across rows by
+// row broadcasts (lanes a shift leaves without a source add 0).
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR3 = 0x113, DPP_ROW_SHR4 = 0x114,
+              DPP_ROW_SHR8 = 0x118, DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+__device__ __forceinline__ float wave_incl_scan(float v, int /*lane*/) {
+  float r = v + dpp_f32m<DPP_ROW_SHR1, 0xF, 0xF, true>(v);
+  r += dpp_f32m<DPP_ROW_SHR2, 0xF, 0xF, true>(v);
+  r += dpp_f32m<DPP_ROW_SHR3, 0xF, 0xF, true>(v);
+  r += dpp_f32m<DPP_ROW_SHR4, 0xF, 0xE>(r);
+  r += dpp_f32m<DPP_ROW_SHR8, 0xF, 0xC>(r);
+  r += dpp_f32m<DPP_ROW_BCAST15, 0xA, 0xF>(r);
+  r += dpp_f32m<DPP_ROW_BCAST31, 0xC, 0xF>(r);
+  return r;
 }
 
-__device__ __forceinline__ double wave_incl_scan_f64(double v, int lane) {
-  for (int off = 1; off < WAVE; off <<= 1) {
-    double o = __shfl_up(v, off, WAVE);
-    if (lane >= off) v += o;
-  }
-  return v;
+__device__ __forceinline__ double wave_incl_scan_f64(double v, int /*lane*/) {
+  double r = v + dpp_f64<DPP_ROW_SHR1, 0xF, 0xF, true>(v);
+  r += dpp_f64<DPP_ROW_SHR2, 0xF, 0xF, true>(v);
+  r += dpp_f64<DPP_ROW_SHR3, 0xF, 0xF, true>(v);
+  r += dpp_f64<DPP_ROW_SHR4, 0xF, 0xE>(r);
+  r += dpp_f64<DPP_ROW_SHR8, 0xF, 0xC>(r);
+  r += dpp_f64<DPP_ROW_BCAST15, 0xA, 0xF>(r);
+  r += dpp_f64<DPP_ROW_BCAST31, 0xC, 0xF>(r);
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -248,39 +300,34 @@ __device__ __forceinline__ int tile_search(WFN wfn, float target, int lane, int*
     float w[DT::VEC];
     wfn(c, w);
     float ls = 0.0f;
+    int lk = -1;  // this lane's last positive value in the chunk
 #pragma unroll
-    for (int k = 0; k < DT::VEC; k++) ls += w[k];
-    // last positive element of this chunk (largest lane with a positive value)
-    int lp = -1;
-#pragma unroll
-    for (int k = 0; k < DT::VEC; k++)
-      if (w[k] > 0.0f) lp = tile_elem<DT>(lane, c * DT::VEC + k);
-    for (int off = 32; off >= 1; off >>= 1) lp = max(lp, __shfl_xor(lp, off, WAVE));
-    if (lp >= 0) lastp = lp;
-    if (found < 0) {
-      const float incl = wave_incl_scan(ls, lane);
-      const float excl = incl - ls;
-      const uint64_t bal = __ballot(run + incl > target);
-      if (bal) {
-        const int src = __builtin_ctzll(bal);
-        int idx = -1;
-        if (lane == src) {
-          float acc = run + excl;
-#pragma unroll
-          for (int k = 0; k < DT::VEC; k++) {
-            acc += w[k];
-            if (idx < 0 && acc > target) idx = tile_elem<DT>(lane, c * DT::VEC + k);
-          }
-          if (idx < 0) {  // rounding between the two sums: take the lane's last positive
-#pragma unroll
-            for (int k = 0; k < DT::VEC; k++)
-              if (w[k] > 0.0f) idx = tile_elem<DT>(lane, c * DT::VEC + k);
-          }
-        }
-        found = __shfl(idx, src, WAVE);
-      }
-      if (found < 0) run += readlane_f32(incl, WAVE - 1);
+    for (int k = 0; k < DT::VEC; k++) {
+      ls += w[k];
+      if (w[k] > 0.0f) lk = k;
     }
+    // last positive element so far: the highest lane holding one
+    const uint64_t pos = __ballot(lk >= 0);
+    if (pos) {
+      const int hl = 63 - __builtin_clzll(pos);
+      lastp = tile_elem<DT>(hl, c * DT::VEC + __builtin_amdgcn_readlane(lk, hl));
+    }
+    const float incl = wave_incl_scan(ls, lane);
+    const uint64_t bal = __ballot(run + incl > target);
+    if (bal) {
+      const int src = __builtin_ctzll(bal);
+      int idx = -1;
+      float acc = run + (incl - ls);
+#pragma unroll
+      for (int k = 0; k < DT::VEC; k++) {
+        acc += w[k];
+        if (idx < 0 && acc > target) idx = k;
+      }
+      if (idx < 0) idx = lk;  // rounding between the two sums: the lane's last positive
+      found = tile_elem<DT>(src, c * DT::VEC + __builtin_amdgcn_readlane(idx, src));
+      break;
+    }
+    run += readlane_f32(incl, WAVE - 1);
   }
   *last_pos = lastp;
   return found;

@@ -175,9 +175,9 @@ __device__ __forceinline__ int64_t find_group_wave(int64_t fr, const StepArgs& a
     const bool le = live && 2 * (int64_t)a.offsets[p] + p <= fr;
     const uint64_t bal = __ballot(le);
     const int j = bal ? 63 - __builtin_clzll(bal) : -1;  // last probe at or below fr
-    const int64_t pj = j >= 0 ? __shfl(p, j, WAVE) : lo;
+    const int64_t pj = j >= 0 ? readlane_i64(p, j) : lo;
     const uint64_t above = __ballot(live && !le) & (j >= 0 ? ~((2ull << j) - 1) : ~0ull);
-    const int64_t pk = above ? __shfl(p, __builtin_ctzll(above), WAVE) : hi;
+    const int64_t pk = above ? readlane_i64(p, __builtin_ctzll(above)) : hi;
     lo = uniform64(pj);
     hi = uniform64(pk);
   }
@@ -367,31 +367,38 @@ __device__ __forceinline__ void fold(float& m, double& s, float pm, double ps) {
 
 // Row statistics of rows [0, R) of one group from its segment partials (row
 // r's at part[r * nseg + k], written by the previous kernel) into L.M / L.S /
-// L.lS; the partials of row `keep` are copied to L.P.  Whole workgroup, `tpr`
+// L.lS; the partials of row `keep` are copied to L.P.  Whole workgroup, 16
 // threads per row, fixed combination order, so equal rows get equal
 // statistics.
+template <int CTRL>
+__device__ __forceinline__ void fold_dpp(float& m, double& s) {
+  fold(m, s, dpp_f32m<CTRL>(m), dpp_f64<CTRL>(s));
+}
+
+constexpr int DPP_WAVE_SHR1 = 0x138;
+constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
+
 template <int NT>
 __device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, int keep, TailLds& L) {
-  int tpr = 16;
-  while (tpr > 1 && NT / tpr < R) tpr >>= 1;
-  const int rpp = NT / tpr;
-  const int sub = threadIdx.x & (tpr - 1);
-  for (int r0 = 0; r0 < R; r0 += rpp) {
-    const int r = r0 + (int)threadIdx.x / tpr;
+  constexpr int TPR = 16;  // threads per row: one DPP row
+  const int sub = threadIdx.x & (TPR - 1);
+  for (int r0 = 0; r0 < R; r0 += NT / TPR) {
+    const int r = r0 + (int)threadIdx.x / TPR;
     float m = -INFINITY;
     double s = 0.0;
     if (r < R) {
-      for (int k = sub; k < nseg; k += tpr) {
+      for (int k = sub; k < nseg; k += TPR) {
         const float2 pt = part[(int64_t)r * nseg + k];
         if (r == keep) L.P[k] = pt;
         fold(m, s, pt.x, (double)pt.y);
       }
     }
-    for (int off = 1; off < tpr; off <<= 1) {
-      const float mo = __shfl_xor(m, off, WAVE);
-      const double so = __shfl_xor(s, off, WAVE);
-      fold(m, s, mo, so);
-    }
+    // lanes i and 15-i, then 7-i inside each half, then the quads: lane 0 of
+    // the row ends up holding all 16 (the same order for every row)
+    fold_dpp<DPP_ROW_MIRROR>(m, s);
+    fold_dpp<DPP_ROW_HALF_MIRROR>(m, s);
+    fold_dpp<DPP_QUAD_XOR1>(m, s);
+    fold_dpp<DPP_QUAD_XOR2>(m, s);
     if (r < R && sub == 0) {
       L.M[r] = m;
       L.S[r] = s;
@@ -422,10 +429,9 @@ __device__ __forceinline__ int locate(int n, WFN weight, double base, TFN target
       const int t = k * WAVE + lane;
       W[k] = t < n ? weight(t) : 0.0;
       incl[k] = run + wave_incl_scan_f64(W[k], lane);
-      run = __shfl(incl[k], WAVE - 1, WAVE);
-      int lt = W[k] > 0.0 ? t : -1;
-      for (int off = 32; off >= 1; off >>= 1) lt = max(lt, __shfl_xor(lt, off, WAVE));
-      if (lt >= 0) lastk = lt;
+      run = readlane_f64(incl[k], WAVE - 1);
+      const uint64_t pos = __ballot(W[k] > 0.0);
+      if (pos) lastk = k * WAVE + 63 - __builtin_clzll(pos);
     }
   }
   const double target = target_of(run - base);
@@ -437,7 +443,7 @@ __device__ __forceinline__ int locate(int n, WFN weight, double base, TFN target
       const uint64_t bal = __ballot(incl[k] > target && k * WAVE + lane < n);
       if (bal) {
         const int src = __builtin_ctzll(bal);
-        *before = __shfl(incl[k] - W[k], src, WAVE);
+        *before = readlane_f64(incl[k] - W[k], src);
         return k * WAVE + src;
       }
     }
@@ -541,24 +547,30 @@ __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const Step
   return L.y;
 }
 
-// Residual weights max(0, p - q) of chunk ch of one tile of a (target, draft)
-// row pair, p = 2^(z_t c - Mt) * st, q = 2^(z_d c - Md) * sd (st = 1 / S_t,
-// sd = 1 / S_d).
+// Residual weights max(0, p - q) of one tile of a (target, draft) row pair,
+// p = 2^(z_t c - At), q = 2^(z_d c - Ad), with At = Mt + log2 S_t and
+// Ad = Md + log2 S_d (the normalisation folded into the exponent).  p and q
+// come out of the same operations, so equal rows give p - q = 0 exactly.
 template <typename DT>
-__device__ __forceinline__ void residual_chunk(const Raw<DT>& rt, const Raw<DT>& rd, int ch, float Mt, float Md,
-                                               float c, float st, float sd, float (&r)[DT::VEC]) {
-  // p and q are rounded products: a fused multiply-subtract would keep one of
-  // them exact and make p - q nonzero for equal rows
-#pragma clang fp contract(off)
-  float vt[DT::VEC], vd[DT::VEC];
-  unpack<DT>(rt, ch, vt);
-  unpack<DT>(rd, ch, vd);
+__device__ __forceinline__ void residual_weights(const Raw<DT>& rt, const Raw<DT>& rd, float At, float Ad, float c,
+                                                 float (&r)[PER_LANE]) {
 #pragma unroll
-  for (int k = 0; k < DT::VEC; k++) {
-    const float p = __builtin_amdgcn_exp2f(fmaf(vt[k], c, -Mt)) * st;
-    const float q = __builtin_amdgcn_exp2f(fmaf(vd[k], c, -Md)) * sd;
-    r[k] = fmaxf(p - q, 0.0f);
+  for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+    float vt[DT::VEC], vd[DT::VEC];
+    unpack<DT>(rt, ch, vt);
+    unpack<DT>(rd, ch, vd);
+#pragma unroll
+    for (int k = 0; k < DT::VEC; k++) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(vt[k], c, -At));
+      const float q = __builtin_amdgcn_exp2f(fmaf(vd[k], c, -Ad));
+      r[ch * DT::VEC + k] = fmaxf(p - q, 0.0f);
+    }
   }
+}
+
+// the log2-domain normalisation M + log2 S of a row
+__device__ __forceinline__ float log2_norm(const RowStat& rs) {
+  return (float)((double)rs.M + rs.lS * 1.4426950408889634);
 }
 
 // ---------------------------------------------------------------------------
@@ -596,7 +608,7 @@ __device__ __forceinline__ void store_tokens(float z, int ok, float u, int kb, T
 
 // OR of a per-thread value across the workgroup into L.fl (after a barrier).
 __device__ __forceinline__ void or_flags(uint32_t v, TailLds& L) {
-  for (int off = 32; off >= 1; off >>= 1) v |= __shfl_xor(v, off, WAVE);
+  v = wave_or_flags(v);
   if ((threadIdx.x % WAVE) == 0 && v) atomicOr(&L.fl, v);
 }
 
@@ -648,7 +660,10 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
           fl |= FLAG_BAD_INPUT;
           reject = true;
         } else {
-          const double rho = exp(log_prob(L.z[j], st, s.c) - log_prob(L.z[kb + j], sd, s.c));
+          // rho = p/q from the fp64 log difference; the fp32 exponential
+          // keeps its relative error near 1e-6
+          const double d = log_prob(L.z[j], st, s.c) - log_prob(L.z[kb + j], sd, s.c);
+          const double rho = (double)__builtin_amdgcn_exp2f((float)(d * 1.4426950408889634));
           reject = !((double)L.u[j] < rho);
         }
       }
@@ -668,24 +683,20 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     y = draw_softmax<DT, VL, SD_WAVES>(trow, s, sk.M, (double)ufin, L, fl);
   } else {
     // residual max(0, p_n - q_n): each wavefront weighs its tiles and keeps
-    // the last one in registers for the search
+    // the weights of the last one in registers for the search
     const raw* drow = group_row<raw>(s, G, b, kb + 1 + n);
     const RowStat st = stat_of(L, n), sd = stat_of(L, kb + 1 + n);
-    const float stf = (float)(1.0 / st.S), sdf = (float)(1.0 / sd.S);
-    Raw<DT> rt, rd;
+    const float At = log2_norm(st), Ad = log2_norm(sd);
+    float w[PER_LANE];
     int held = -1;
     for (int t = wave; t < ntiles; t += SD_WAVES) {
-      rt = load_tile<DT, VL>(trow, s.V, t, lane);
-      rd = load_tile<DT, VL>(drow, s.V, t, lane);
+      const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, t, lane);
+      const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, t, lane);
+      residual_weights<DT>(rt, rd, At, Ad, s.c, w);
       held = t;
       float m = 0.0f;
 #pragma unroll
-      for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-        float r[DT::VEC];
-        residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, r);
-#pragma unroll
-        for (int k = 0; k < DT::VEC; k++) m += r[k];
-      }
+      for (int e = 0; e < PER_LANE; e++) m += w[e];
       m = wave_sum(m);
       if (lane == 0) L.W[t] = (double)m;
     }
@@ -713,10 +724,14 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
       // the wavefront that weighed tile tt draws inside it
       if (wave == tt % SD_WAVES) {
         if (held != tt) {
-          rt = load_tile<DT, VL>(trow, s.V, tt, lane);
-          rd = load_tile<DT, VL>(drow, s.V, tt, lane);
+          const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tt, lane);
+          const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, tt, lane);
+          residual_weights<DT>(rt, rd, At, Ad, s.c, w);
         }
-        auto wfn = [&](int ch, float (&w)[DT::VEC]) { residual_chunk<DT>(rt, rd, ch, st.M, sd.M, s.c, stf, sdf, w); };
+        auto wfn = [&](int ch, float (&x)[DT::VEC]) {
+#pragma unroll
+          for (int k = 0; k < DT::VEC; k++) x[k] = w[ch * DT::VEC + k];
+        };
         int last_pos = -1;
         int idx = tile_search<DT>(wfn, L.clamp ? INFINITY : (float)L.target, lane, &last_pos);
         if (idx < 0) {
@@ -759,7 +774,7 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
   if (wave == 0) {
     float mf = -INFINITY;
     for (int k = lane; k < N; k += WAVE) mf = fmaxf(mf, Q.lw[k]);
-    for (int off = 32; off >= 1; off >>= 1) mf = fmaxf(mf, __shfl_xor(mf, off, WAVE));
+    mf = wave_max(mf);
     const double M = (double)mf;
     const bool zero = !(M > -INFINITY);
     if (M == INFINITY || M != M) fl |= FLAG_NONFINITE;
@@ -771,9 +786,8 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
         const double wk = k < N ? exp((double)Q.lw[k] - M) : 0.0;
         Sw += wave_sum_f64(wk);
         Sw2 += wave_sum_f64(wk * wk);
-        int lp = wk > 0.0 ? k : -1;
-        for (int off = 32; off >= 1; off >>= 1) lp = max(lp, __shfl_xor(lp, off, WAVE));
-        last_pos = max(last_pos, lp);
+        const uint64_t pos = __ballot(wk > 0.0);
+        if (pos) last_pos = k0 + 63 - __builtin_clzll(pos);
       }
     } else {
       fl |= FLAG_ZERO_WEIGHTS;
@@ -798,15 +812,15 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
           h = (double)N;
         }
         hi = (int)fmin(fmax(h, 0.0), (double)N);
-        run += __shfl(incl, WAVE - 1, WAVE);
+        run += readlane_f64(incl, WAVE - 1);
       } else {
         hi = ii + 1;
       }
       if (ii >= N) hi = N;
-      const int prev = __shfl_up(hi, 1, WAVE);
+      const int prev = __builtin_amdgcn_update_dpp(0, hi, DPP_WAVE_SHR1, 0xF, 0xF, false);  // lane - 1
       const int lo = lane == 0 ? carry : prev;
       hi = max(hi, lo);
-      carry = __shfl(hi, WAVE - 1, WAVE);
+      carry = __builtin_amdgcn_readlane(hi, WAVE - 1);
       if (ii < N) {
         for (int k = lo; k < hi; k++) {
           a.ancestors[base + k] = ii;
@@ -819,7 +833,7 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
       a.ess[p] = (float)E;
       a.resampled[p] = do_res ? 1 : 0;
     }
-    for (int off = 32; off >= 1; off >>= 1) fl |= __shfl_xor(fl, off, WAVE);
+    fl = wave_or_flags(fl);
     if (lane == 0) raise_flags(s.flags, fl);
   }
   __syncthreads();
