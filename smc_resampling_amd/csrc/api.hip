@@ -30,26 +30,28 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
 // workspace can serve calls of different shapes: the counters are zero before
 // the first call and every call leaves them at zero.  Scratch data follows:
 // the segment partials (sized for one-tile segments, the most a call can
-// use) and, for SMC, the reweighted log-weights.
+// use), the tile partials of each group's bonus row and, for SMC, the
+// reweighted log-weights.
 constexpr size_t kCounterBytes = SMCSD_WORKSPACE_COUNTER_BYTES;
 
 // One counter line per SMC prompt.
 bool smc_counters_fit(int64_t P) { return P <= smcsd::CTR_LINES; }
 
 struct SdLayout {
-  size_t part, total;
+  size_t part, tpart, total;
 };
 
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
   SdLayout l;
   l.part = kCounterBytes;
-  l.total = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
+  l.tpart = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
+  l.total = align_up(l.tpart + sizeof(float2) * (size_t)((int64_t)B * nt));
   return l;
 }
 
 struct SmcLayout {
-  size_t ws_logw, part, total;
+  size_t ws_logw, part, tpart, total;
 };
 
 SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
@@ -58,7 +60,8 @@ SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   SmcLayout l;
   l.ws_logw = kCounterBytes;
   l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
-  l.total = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
+  l.tpart = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
+  l.total = align_up(l.tpart + sizeof(float2) * (size_t)(PN * nt));
   return l;
 }
 
@@ -76,7 +79,7 @@ bool temperature_ok(float T) { return isfinite(T) && T > 0.0f; }
 
 void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, const void* draft,
                const int32_t* offsets, const int32_t* tokens, int64_t ngroups, int64_t rows_t, int64_t rows_d,
-               int64_t V, int K, float T, char* ws, size_t part_off, uint32_t* flags) {
+               int64_t V, int K, float T, char* ws, size_t part_off, size_t tpart_off, uint32_t* flags) {
   s->target = target;
   s->draft = draft;
   s->offsets = offsets;
@@ -92,6 +95,7 @@ void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, 
   s->units = plan.units;
   s->c = (float)(1.4426950408889634 / (double)T);
   s->part = reinterpret_cast<float2*>(ws + part_off);
+  s->tpart = reinterpret_cast<float2*>(ws + tpart_off);
   s->ctr = reinterpret_cast<uint32_t*>(ws);
   s->flags = flags;
 }
@@ -150,7 +154,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   char* ws = static_cast<char*>(workspace);
   smcsd::SdArgs a;
   fill_step(&a.s, plan, target_logits, draft_logits, draft_offsets, draft_tokens, B, total_draft_rows + B,
-            total_draft_rows, V, K, temperature, ws, l.part, status_flags);
+            total_draft_rows, V, K, temperature, ws, l.part, l.tpart, status_flags);
   a.uniforms = uniforms;
   a.num_accepted = num_accepted;
   a.final_token = final_token;
@@ -203,7 +207,7 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   char* ws = static_cast<char*>(workspace);
   smcsd::SmcArgs a;
   fill_step(&a.s, plan, target_logits, draft_logits, nullptr, draft_tokens, PN, PN * (K + 1), PN * K, V, K,
-            temperature, ws, l.part, status_flags);
+            temperature, ws, l.part, l.tpart, status_flags);
   a.N = N;
   a.L = pages_per_particle;
   a.ess_frac = ess_frac;

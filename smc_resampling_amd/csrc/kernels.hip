@@ -142,6 +142,19 @@ __device__ __forceinline__ void lane_fold_tile(const Raw<DT>& cur, float c, floa
   }
 }
 
+// Merge per-lane statistics (m2, s2) into (m, s).  A -inf maximum contributes
+// its sum times 0, so a NaN sum stays NaN.
+__device__ __forceinline__ void lane_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn > -INFINITY) {
+    s = s * (m > -INFINITY ? __builtin_amdgcn_exp2f(m - mn) : 0.0f) +
+        s2 * (m2 > -INFINITY ? __builtin_amdgcn_exp2f(m2 - mn) : 0.0f);
+    m = mn;
+  } else {
+    s = s + s2;
+  }
+}
+
 // The wavefront's (MC, S) from per-lane (m, s): MC = max m, S = sum s 2^(m - MC).
 // All -inf gives (-inf, 0); a NaN s stays NaN.
 __device__ __forceinline__ float2 wave_partial(float m, float s) {
@@ -199,7 +212,10 @@ __device__ __forceinline__ void cursor_set(GroupCursor& cu, int64_t g, const Ste
                     a.rows_d);
 }
 
-template <typename DT, bool VL, int NS>
+// TP: the call's segments span several tiles, so each group's bonus row also
+// gets per-tile partials (with one-tile segments the segment partials are
+// those already).
+template <typename DT, bool VL, int NS, bool TP>
 __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
   using raw = typename DT::raw;
   const int lane = threadIdx.x % WAVE;
@@ -220,10 +236,15 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
   cursor_set(gc, find_group_wave(lfr, a, lane), a, lane);
   const raw* lrow = group_row<raw>(a, gc.G, gc.g, lfr - gc.G.fr0);
   if (!lrow) bad = FLAG_BAD_INPUT;
+  // tiles of a group's last target row (its bonus row) also get a partial of
+  // their own, at tpart[lbon + tile]; lbon < 0 for every other row
+  auto bonus_base = [&]() -> int64_t { return TP && lrow && lfr - gc.G.fr0 == gc.G.kb ? gc.g * ntiles : -1; };
+  int64_t lbon = bonus_base();
   // Issues the loads of the next tile.  A row outside the buffers (malformed
   // offsets) is read as row 0 of the target, and its partials are not used.
-  auto fetch = [&]() {
+  auto fetch = [&](int64_t& dst) {
     const Raw<DT> x = load_raw<DT, VL>(lrow ? lrow : static_cast<const raw*>(a.target), a.V, lt, lane);
+    dst = lbon < 0 ? -1 : lbon + lt;
     if (++lt == lte) {
       if (++lu < u1) {
         if (++lsg == nseg) {
@@ -232,6 +253,7 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
           if (lfr >= gc.G.fr0 + 2 * (int64_t)gc.G.kb + 1) cursor_set(gc, gc.g + 1, a, lane);
           lrow = group_row<raw>(a, gc.G, gc.g, lfr - gc.G.fr0);
           if (!lrow) bad = FLAG_BAD_INPUT;
+          lbon = bonus_base();
         }
         lt = lsg * seg;
         lte = min(ntiles, lt + seg);
@@ -251,9 +273,20 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
   float2 pb = make_float2(0.0f, 0.0f);
   int64_t pbase = u0;
   int pn = 0;
-  auto reduce = [&](Raw<DT>& x) {
+  auto reduce = [&](Raw<DT>& x, int64_t dst) {
     mask_tail<DT>(x, a.V, ct, lane);
+    // a bonus-row tile is folded on its own first, then into the unit's statistics
+    const float pm = m, ps = s;
+    if (TP && dst >= 0) {
+      m = -INFINITY;
+      s = 0.0f;
+    }
     lane_fold_tile<DT>(x, c, m, s);
+    if (TP && dst >= 0) {
+      const float2 tp = wave_partial(m, s);
+      if (lane == 0) a.tpart[dst] = tp;
+      lane_merge(m, s, pm, ps);
+    }
     if (++ct == cte) {
       const float2 pt = wave_partial(m, s);
       if (lane == pn) pb = pt;
@@ -274,15 +307,16 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
   // every slot is refilled unconditionally, so a reduction waits only for its
   // own tile.
   Raw<DT> q[NS];
+  int64_t qd[NS];
   if (T >= 2 * NS) {
 #pragma unroll
-    for (int i = 0; i < NS; i++) q[i] = fetch();
+    for (int i = 0; i < NS; i++) q[i] = fetch(qd[i]);
     int64_t left = T;
     do {
 #pragma unroll
       for (int i = 0; i < NS; i++) {
-        reduce(q[i]);
-        q[i] = fetch();
+        reduce(q[i], qd[i]);
+        q[i] = fetch(qd[i]);
       }
       left -= NS;
     } while (left >= 2 * NS);
@@ -290,28 +324,28 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
     const int more = (int)(left - NS);
 #pragma unroll
     for (int i = 0; i < NS; i++) {
-      reduce(q[i]);
-      if (i < more) q[i] = fetch();
+      reduce(q[i], qd[i]);
+      if (i < more) q[i] = fetch(qd[i]);
     }
 #pragma unroll
     for (int i = 0; i < NS; i++)
-      if (i < more) reduce(q[i]);
+      if (i < more) reduce(q[i], qd[i]);
   } else {
     // fewer than 2 NS tiles
     const int t = (int)T;
 #pragma unroll
     for (int i = 0; i < NS; i++)
-      if (i < t) q[i] = fetch();
+      if (i < t) q[i] = fetch(qd[i]);
 #pragma unroll
     for (int i = 0; i < NS; i++) {
       if (i < t) {
-        reduce(q[i]);
-        if (NS + i < t) q[i] = fetch();
+        reduce(q[i], qd[i]);
+        if (NS + i < t) q[i] = fetch(qd[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < NS; i++)
-      if (NS + i < t) reduce(q[i]);
+      if (NS + i < t) reduce(q[i], qd[i]);
   }
   if (lane < pn) a.part[pbase + lane] = pb;
   if (lane == 0) raise_flags(a.flags, bad);
@@ -367,9 +401,8 @@ __device__ __forceinline__ void fold(float& m, double& s, float pm, double ps) {
 
 // Row statistics of rows [0, R) of one group from its segment partials (row
 // r's at part[r * nseg + k], written by the previous kernel) into L.M / L.S /
-// L.lS; the partials of row `keep` are copied to L.P.  Whole workgroup, 16
-// threads per row, fixed combination order, so equal rows get equal
-// statistics.
+// L.lS.  Whole workgroup, 16 threads per row, fixed combination order, so
+// equal rows get equal statistics.
 template <int CTRL>
 __device__ __forceinline__ void fold_dpp(float& m, double& s) {
   fold(m, s, dpp_f32m<CTRL>(m), dpp_f64<CTRL>(s));
@@ -379,7 +412,7 @@ constexpr int DPP_WAVE_SHR1 = 0x138;
 constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
 
 template <int NT>
-__device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, int keep, TailLds& L) {
+__device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, TailLds& L) {
   constexpr int TPR = 16;  // threads per row: one DPP row
   const int sub = threadIdx.x & (TPR - 1);
   for (int r0 = 0; r0 < R; r0 += NT / TPR) {
@@ -389,7 +422,6 @@ __device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int 
     if (r < R) {
       for (int k = sub; k < nseg; k += TPR) {
         const float2 pt = part[(int64_t)r * nseg + k];
-        if (r == keep) L.P[k] = pt;
         fold(m, s, pt.x, (double)pt.y);
       }
     }
@@ -405,6 +437,18 @@ __device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int 
       L.lS[r] = log(s);
     }
   }
+}
+
+// Per-tile partials of the bonus row kb of group g (first row fr0): the
+// segment partials when segments are one tile long.
+__device__ __forceinline__ const float2* bonus_partials(const StepArgs& s, int64_t fr0, int64_t g, int kb) {
+  return s.seg == 1 ? s.part + (fr0 + kb) * s.nseg : s.tpart + g * s.ntiles;
+}
+
+// The n partials at src into L.P.  Whole workgroup.
+template <int NT>
+__device__ __forceinline__ void stage_partials(const float2* __restrict__ src, int n, TailLds& L) {
+  for (int k = threadIdx.x; k < n; k += NT) L.P[k] = src[k];
 }
 
 // ---------------------------------------------------------------------------
@@ -461,12 +505,13 @@ __device__ __forceinline__ float2 tile_partial_of(const Raw<DT>& r, float c) {
   return wave_partial(m, s);
 }
 
-// Inverse-CDF draw from softmax(z c) of `row` (row maximum M, log2 domain; its
-// segment partials in L.P) with uniform u.  Whole workgroup; every thread
-// gets the token.
+// Inverse-CDF draw from softmax(z c) of `row` (row maximum M, log2 domain)
+// with uniform u.  L.P holds np partials of the row, each over `per` tiles (a
+// bonus row's own tile partials, or segment partials).  Whole workgroup;
+// every thread gets the token.
 template <typename DT, bool VL, int NW = WAVES_PER_BLOCK>
 __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const StepArgs& a, float M, double u,
-                            TailLds& L, uint32_t& fl) {
+                            int np, int per, TailLds& L, uint32_t& fl) {
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   const float c = a.c;
   // 1. the segment
@@ -477,9 +522,9 @@ __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const Step
     };
     double before = 0.0, target = 0.0;
     int last = -1;
-    const int k = locate(a.nseg, wt, 0.0, [&](double tot) { return u * tot; }, lane, &before, &target, &last);
+    const int k = locate(np, wt, 0.0, [&](double tot) { return u * tot; }, lane, &before, &target, &last);
     if (lane == 0) {
-      L.sel = k >= 0 ? k : (last >= 0 ? last : a.nseg - 1);
+      L.sel = k >= 0 ? k : (last >= 0 ? last : np - 1);
       L.clamp = k < 0;
       L.before = before;
       L.target = target;
@@ -487,7 +532,7 @@ __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const Step
   }
   __syncthreads();
   const int sg = L.sel;
-  const int tb = sg * a.seg, te = min(a.ntiles, tb + a.seg);
+  const int tb = sg * per, te = min(a.ntiles, tb + per);
   int tt;
   double before_t;
   float mt;
@@ -643,7 +688,8 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   const float ufin = a.uniforms[t0 + kb];
   int ok = 1;
   const float z = token_logit<DT>(s, G, b, xt, &ok);
-  merge_rows<SD_BLOCK>(pg, 2 * kb + 1, s.nseg, kb, L);
+  merge_rows<SD_BLOCK>(pg, 2 * kb + 1, s.nseg, L);
+  stage_partials<SD_BLOCK>(bonus_partials(s, G.fr0, b, kb), ntiles, L);
   store_tokens(z, ok, uj, kb, L);
   __syncthreads();
   uint32_t fl = 0;
@@ -680,7 +726,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     // every draft accepted: the bonus token from p_{K_b}
     const RowStat sk = stat_of(L, kb);
     if (!sk.ok) fl |= FLAG_NONFINITE;
-    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, sk.M, (double)ufin, L, fl);
+    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, sk.M, (double)ufin, ntiles, 1, L, fl);
   } else {
     // residual max(0, p_n - q_n): each wavefront weighs its tiles and keeps
     // the weights of the last one in registers for the search
@@ -745,9 +791,9 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     } else {
       // p_n and q_n agree to rounding: draw from p_n with the same uniform
       fl |= FLAG_ZERO_RESIDUAL;
-      for (int k = threadIdx.x; k < s.nseg; k += SD_BLOCK) L.P[k] = pg[(int64_t)n * s.nseg + k];
+      stage_partials<SD_BLOCK>(pg + (int64_t)n * s.nseg, s.nseg, L);
       __syncthreads();
-      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, st.M, (double)ufin, L, fl);
+      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, st.M, (double)ufin, s.nseg, s.seg, L, fl);
     }
   }
   or_flags(fl, L);
@@ -763,12 +809,49 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
 // k_smc_tail: one workgroup per particle; the last particle of a prompt runs
 // the prompt's ESS, resampling and page-table gather
 // ---------------------------------------------------------------------------
+// dst row k = src row anc[k], for k < N, rows of W elements.  Whole
+// workgroup: each wavefront copies GR rows at a time, two 64-element column
+// blocks per pass, with all GR x 2 loads issued before their stores.  Row and
+// column indices past the end are clamped to the last row and column, for
+// the stores too: a clamped lane writes the value that element gets anyway,
+// and with no branch around the stores the loads stay ahead of them.  (The
+// pointers are not restrict-qualified: loads from read-only memory would be
+// free to sink down to their stores.)
+using i32x4 = int __attribute__((ext_vector_type(4)));
+
+template <typename E>
+__device__ __forceinline__ void gather_rows(const E* src, E* dst, int N, int64_t W,
+                                            const int* anc) {
+  constexpr int GR = 4, GC = 2;
+  const int lane = threadIdx.x % WAVE, wave = wave_id();
+  for (int k0 = wave * GR; k0 < N; k0 += WAVES_PER_BLOCK * GR) {
+    int64_t from[GR];
+#pragma unroll
+    for (int j = 0; j < GR; j++) from[j] = (int64_t)anc[min(k0 + j, N - 1)] * W;
+    for (int64_t l0 = 0; l0 < W; l0 += GC * WAVE) {
+      E v[GR][GC];
+      int64_t col[GC];
+#pragma unroll
+      for (int h = 0; h < GC; h++) col[h] = min(l0 + h * WAVE + lane, W - 1);
+#pragma unroll
+      for (int j = 0; j < GR; j++)
+#pragma unroll
+        for (int h = 0; h < GC; h++) v[j][h] = src[from[j] + col[h]];
+#pragma unroll
+      for (int j = 0; j < GR; j++)
+#pragma unroll
+        for (int h = 0; h < GC; h++) dst[(int64_t)min(k0 + j, N - 1) * W + col[h]] = v[j][h];
+    }
+  }
+}
+
 __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   const int N = a.N;
   const int64_t base = p * N;
   uint32_t fl = 0;
+  const float ru = a.resample_u[p];  // issued early: nothing below waits on it until the slot ranges
   for (int k = threadIdx.x; k < N; k += BLOCK) Q.lw[k] = ld_dev(a.ws_logw + base + k);
   __syncthreads();
   if (wave == 0) {
@@ -794,7 +877,7 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
     }
     const double E = zero ? 0.0 : Sw * Sw / Sw2;
     const bool do_res = !zero && E < (double)a.ess_frac * (double)N;
-    const double u = (double)a.resample_u[p];
+    const double u = (double)ru;
     double run = 0.0;
     int carry = 0;  // first slot of the chunk's first particle
     for (int k0 = 0; k0 < N; k0 += WAVE) {
@@ -842,25 +925,19 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
     const int64_t L = a.L;
     const int32_t* __restrict__ src = a.pt_in + base * L;
     int32_t* __restrict__ dst = a.pt_out + base * L;
-    const bool v4 = (L % 4) == 0 && (((uintptr_t)src | (uintptr_t)dst) & 15) == 0;
-    if (v4) {
-      const int64_t L4 = L / 4;
-      for (int64_t e = threadIdx.x; e < (int64_t)N * L4; e += BLOCK) {
-        const int64_t k = e / L4, l = e - k * L4;
-        reinterpret_cast<int4*>(dst)[k * L4 + l] = reinterpret_cast<const int4*>(src)[Q.anc[k] * L4 + l];
-      }
-    } else {
-      for (int64_t e = threadIdx.x; e < (int64_t)N * L; e += BLOCK) {
-        const int64_t k = e / L, l = e - k * L;
-        dst[k * L + l] = src[Q.anc[k] * L + l];
-      }
-    }
+    if ((L % 4) == 0 && (((uintptr_t)src | (uintptr_t)dst) & 15) == 0)
+      gather_rows(reinterpret_cast<const i32x4*>(src), reinterpret_cast<i32x4*>(dst), N, L / 4, Q.anc);
+    else
+      gather_rows(src, dst, N, L, Q.anc);
   }
   if (threadIdx.x == 0) st_dev(s.ctr + p * CTR_STRIDE, 0u);  // every particle of p has counted
 }
 
+// With vector loads, at most 64 VGPRs (8 wavefronts per SIMD), so that 8
+// workgroups fit on a compute unit and a launch of 2048 particles is resident
+// at once (the element-wise loads need more registers than that).
 template <typename DT, bool VL>
-__global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcArgs a) {
+__global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   using raw = typename DT::raw;
   __shared__ SharedLds sh;
   __shared__ int s_last;
@@ -877,7 +954,8 @@ __global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcArgs a) {
   const float ub = a.bonus_u[i];
   int ok = 1;
   const float z = token_logit<DT>(s, G, i, xt, &ok);
-  merge_rows<BLOCK>(pg, 2 * K + 1, s.nseg, K, L);
+  merge_rows<BLOCK>(pg, 2 * K + 1, s.nseg, L);
+  stage_partials<BLOCK>(bonus_partials(s, G.fr0, i, K), s.ntiles, L);
   store_tokens(z, ok, 0.0f, K, L);
   __syncthreads();
   uint32_t fl = 0;
@@ -900,7 +978,7 @@ __global__ __launch_bounds__(BLOCK) void k_smc_tail(SmcArgs a) {
   }
   const RowStat sk = stat_of(L, K);
   if (!sk.ok) fl |= FLAG_NONFINITE;
-  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, sk.M, (double)ub, L, fl);
+  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, sk.M, (double)ub, s.ntiles, 1, L, fl);
   or_flags(fl, L);
   __syncthreads();
   const int64_t p = i / a.N;
@@ -949,9 +1027,14 @@ static const void* kptr(K k) {
   return reinterpret_cast<const void*>(k);
 }
 
-static const void* stream_kernel(bool bf16, bool vec) {
-  if (bf16) return vec ? kptr(&k_stream<Bf16, true, slots_of<Bf16>()>) : kptr(&k_stream<Bf16, false, slots_of<Bf16>()>);
-  return vec ? kptr(&k_stream<F32, true, slots_of<F32>()>) : kptr(&k_stream<F32, false, slots_of<F32>()>);
+template <typename DT, bool TP>
+static const void* stream_kernel_t(bool vec) {
+  return vec ? kptr(&k_stream<DT, true, slots_of<DT>(), TP>) : kptr(&k_stream<DT, false, slots_of<DT>(), TP>);
+}
+
+static const void* stream_kernel(bool bf16, bool vec, bool tp) {
+  if (bf16) return tp ? stream_kernel_t<Bf16, true>(vec) : stream_kernel_t<Bf16, false>(vec);
+  return tp ? stream_kernel_t<F32, true>(vec) : stream_kernel_t<F32, false>(vec);
 }
 
 // Segments long enough that each resident wavefront streams about 32 units
@@ -959,7 +1042,7 @@ static const void* stream_kernel(bool bf16, bool vec) {
 // searches at most 8 tiles of a segment.  The streaming grid is what the
 // device holds at once, fewer when there is not one unit per wavefront.
 hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p) {
-  const int resident = resident_blocks(stream_kernel(bf16, vec));
+  const int resident = resident_blocks(stream_kernel(bf16, vec, false));
   if (resident <= 0) return hipErrorInvalidDevice;
   const int64_t waves = (int64_t)resident * WAVES_PER_BLOCK;
   const int64_t tiles = rows * ntiles;
@@ -979,7 +1062,7 @@ hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p) {
 static hipError_t launch_stream(const StepArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s,
                                 hipEvent_t mark) {
   void* args[] = {const_cast<StepArgs*>(&a)};
-  hipError_t e = hipLaunchKernel(stream_kernel(bf16, vec), dim3(p.grid), dim3(BLOCK), args, 0, s);
+  hipError_t e = hipLaunchKernel(stream_kernel(bf16, vec, p.seg > 1), dim3(p.grid), dim3(BLOCK), args, 0, s);
   if (e == hipSuccess) e = hipGetLastError();
   if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
   return e;

@@ -31,6 +31,7 @@ struct StepArgs {
   int64_t units;  // rows * nseg
   float c;        // log2(e) / T
   float2* part;   // [units] segment partials (max of z c, sum of 2^(z c - max))
+  float2* tpart;  // [ngroups * ntiles] tile partials of each group's bonus row
   uint32_t* ctr;  // counter lines (zero between calls)
   uint32_t* flags;
 };
