@@ -251,27 +251,25 @@ def main():
     flags = int(outs["status_flags"].item())
     ms_per_step = ms / steps
 
-    # ---------------- timing: the streaming kernel -------------------------------
-    # The same calls again, eagerly on the same stream, each bracketed by events,
-    # with an event recorded by the library between its streaming kernel and its
-    # decision kernel.  A sleep kernel first lets the host enqueue every call, so
-    # the GPU runs them back to back as in the graph.
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # ---------------- timing: each kernel ----------------------------------------
+    # The same calls again, eagerly on the same stream, each call's two kernels
+    # launched with HIP events attached to their own start and stop (the
+    # library's timing aid), so an event pair times one kernel's execution, as
+    # a kernel trace does.  A sleep kernel first lets the host enqueue every
+    # call, so the GPU runs them back to back as in the graph.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     with torch.cuda.stream(run_stream):
-        for e in ev_m:
-            e.record(run_stream)  # creates the event handle the library records into
+        for quad in ev:
+            for e in quad:
+                e.record(run_stream)  # creates the event handles the library attaches
         torch.cuda.synchronize()
         torch.cuda._sleep(SLEEP_CYCLES)
         for s_, c in enumerate(calls[W:]):
-            ev_a[s_].record(run_stream)
-            smcsd.mark_next_stream_phase(ev_m[s_])
+            smcsd.time_next_call(*ev[s_])
             c()
-            ev_b[s_].record(run_stream)
     torch.cuda.synchronize()
-    stream_ms = float(np.mean([ev_a[i].elapsed_time(ev_m[i]) for i in range(steps)]))
-    tail_ms = float(np.mean([ev_m[i].elapsed_time(ev_b[i]) for i in range(steps)]))
+    stream_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]))
+    tail_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(steps)]))
     timed = [(W + s) % nb for s in range(steps)]
     pos_total = sum(positions[i] for i in timed)
     bytes_total = sum(nbytes[i] for i in timed)

@@ -125,12 +125,16 @@ const char* smcsd_status_string(int32_t status);
 
 /*
  * Profiling aid for benchmarks: the next sd_verify or smc_reweight_resample
- * call made by the calling thread records `event` (a hipEvent_t created by
- * the caller, or NULL to cancel) on its stream between its logit-streaming
- * kernel and its decision kernel, so that the streaming kernel can be timed
- * with events.  The setting is per thread and used once.
+ * call made by the calling thread launches its two kernels so that the given
+ * events take the start and stop times of the kernels themselves:
+ * stream_start / stream_stop for the logit-streaming kernel, tail_start /
+ * tail_stop for the decision kernel.  hipEventElapsedTime of a pair is then
+ * that kernel's execution time, without the dispatch gaps around it.  Each
+ * argument is a hipEvent_t created by the caller with timing enabled, or
+ * NULL.  The setting is per thread and used once; not for calls under
+ * stream capture.
  */
-void smcsd_mark_next_stream_phase(void* event);
+void smcsd_time_next_call(void* stream_start, void* stream_stop, void* tail_start, void* tail_stop);
 
 /*
  * Workspace bytes sd_verify needs for these sizes (0 when B == 0).

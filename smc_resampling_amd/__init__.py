@@ -17,7 +17,7 @@ __all__ = [
     "sd_verify", "smc_reweight_resample", "sd_verify_workspace_bytes", "smc_workspace_bytes",
     "prepare_sd_verify", "prepare_smc_reweight_resample", "status_string", "abi_version", "lib", "SmcsdError",
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "FLAG_ZERO_WEIGHTS", "FLAG_CDF_CLAMP", "FLAG_BAD_INPUT",
-    "new_workspace", "mark_next_stream_phase",
+    "new_workspace", "time_next_call",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,7 @@ _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctype
 _SIGNATURES = {
     "smcsd_abi_version": ([], _I32),
     "smcsd_status_string": ([_I32], ctypes.c_char_p),
-    "smcsd_mark_next_stream_phase": ([_P], None),
+    "smcsd_time_next_call": ([_P, _P, _P, _P], None),
     "sd_verify_workspace_bytes": ([_I32, _I32, _I32, _I32, _I64], _SZ),
     "sd_verify": ([_I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
@@ -70,10 +70,13 @@ def abi_version() -> int:
     return _lib.smcsd_abi_version()
 
 
-def mark_next_stream_phase(event) -> None:
-    """Record ``event`` (a torch.cuda.Event) between the streaming kernel and
-    the decision kernel of this thread's next library call (benchmark aid)."""
-    _lib.smcsd_mark_next_stream_phase(None if event is None else event.cuda_event)
+def time_next_call(stream_start=None, stream_stop=None, tail_start=None, tail_stop=None) -> None:
+    """Have this thread's next library call attach the given events (timing
+    torch.cuda.Event objects whose handles exist, i.e. recorded once, or None)
+    to the start and stop of its streaming kernel and its decision kernel
+    (benchmark aid)."""
+    h = [None if e is None else e.cuda_event for e in (stream_start, stream_stop, tail_start, tail_stop)]
+    _lib.smcsd_time_next_call(*h)
 
 
 def status_string(code: int) -> str:

@@ -65,14 +65,14 @@ SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   return l;
 }
 
-// Event recorded between the two kernels of this thread's next call (a
-// profiling aid; see smcsd_mark_next_stream_phase).
-thread_local hipEvent_t t_phase_mark = nullptr;
+// Kernel timers of this thread's next call (a profiling aid; see
+// smcsd_time_next_call).
+thread_local smcsd::KernelTimers t_timers = {};
 
-hipEvent_t take_phase_mark() {
-  hipEvent_t e = t_phase_mark;
-  t_phase_mark = nullptr;
-  return e;
+smcsd::KernelTimers take_timers() {
+  const smcsd::KernelTimers t = t_timers;
+  t_timers = {};
+  return t;
 }
 
 bool temperature_ok(float T) { return isfinite(T) && T > 0.0f; }
@@ -107,7 +107,10 @@ extern "C" {
 
 int32_t smcsd_abi_version(void) { return SMCSD_ABI_VERSION; }
 
-void smcsd_mark_next_stream_phase(void* event) { t_phase_mark = static_cast<hipEvent_t>(event); }
+void smcsd_time_next_call(void* stream_start, void* stream_stop, void* tail_start, void* tail_stop) {
+  t_timers = {static_cast<hipEvent_t>(stream_start), static_cast<hipEvent_t>(stream_stop),
+              static_cast<hipEvent_t>(tail_start), static_cast<hipEvent_t>(tail_stop)};
+}
 
 const char* smcsd_status_string(int32_t s) {
   switch (s) {
@@ -158,7 +161,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   a.uniforms = uniforms;
   a.num_accepted = num_accepted;
   a.final_token = final_token;
-  return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_phase_mark()) == hipSuccess
+  return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;
 }
@@ -221,7 +224,7 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   a.ancestors = ancestors;
   a.ess = ess;
   a.resampled = resampled;
-  return smcsd::launch_smc(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_phase_mark()) == hipSuccess
+  return smcsd::launch_smc(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;
 }

@@ -34,6 +34,8 @@
 // (residual masses, log-weights) are written and read at the device coherence
 // point (agent-scope atomics), so no XCD-local L2 holds a stale copy.  Every
 // counter is back at zero when the kernel ends.
+#include <hip/hip_ext.h>
+
 #include <map>
 #include <mutex>
 
@@ -1059,39 +1061,43 @@ hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p) {
   return hipSuccess;
 }
 
-static hipError_t launch_stream(const StepArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s,
-                                hipEvent_t mark) {
-  void* args[] = {const_cast<StepArgs*>(&a)};
-  hipError_t e = hipLaunchKernel(stream_kernel(bf16, vec, p.seg > 1), dim3(p.grid), dim3(BLOCK), args, 0, s);
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e == hipSuccess && mark) e = hipEventRecord(mark, s);
-  return e;
+// One kernel launch; with a start or stop event, through the launch that
+// attaches them to the dispatch itself.
+template <typename A>
+static hipError_t launch(const void* kernel, unsigned grid, unsigned block, const A& arg, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop) {
+  void* args[] = {const_cast<A*>(&arg)};
+  hipError_t e = start || stop ? hipExtLaunchKernel(kernel, dim3(grid), dim3(block), args, 0, s, start, stop, 0)
+                               : hipLaunchKernel(kernel, dim3(grid), dim3(block), args, 0, s);
+  return e == hipSuccess ? hipGetLastError() : e;
 }
 
 template <typename DT, bool VL>
-static hipError_t launch_sd_t(const SdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_sd_tail<DT, VL>), dim3((unsigned)a.s.ngroups), dim3(SD_BLOCK), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark) {
-  hipError_t e = launch_stream(a.s, p, bf16, vec, s, mark);
-  if (e != hipSuccess) return e;
-  if (bf16) return vec ? launch_sd_t<Bf16, true>(a, s) : launch_sd_t<Bf16, false>(a, s);
-  return vec ? launch_sd_t<F32, true>(a, s) : launch_sd_t<F32, false>(a, s);
+static const void* sd_tail_kernel() {
+  return kptr(&k_sd_tail<DT, VL>);
 }
 
 template <typename DT, bool VL>
-static hipError_t launch_smc_t(const SmcArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_smc_tail<DT, VL>), dim3((unsigned)a.s.ngroups), dim3(BLOCK), 0, s, a);
-  return hipGetLastError();
+static const void* smc_tail_kernel() {
+  return kptr(&k_smc_tail<DT, VL>);
 }
 
-hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark) {
-  hipError_t e = launch_stream(a.s, p, bf16, vec, s, mark);
+hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
+  hipError_t e = launch(stream_kernel(bf16, vec, p.seg > 1), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
+                        t.stream_stop);
   if (e != hipSuccess) return e;
-  if (bf16) return vec ? launch_smc_t<Bf16, true>(a, s) : launch_smc_t<Bf16, false>(a, s);
-  return vec ? launch_smc_t<F32, true>(a, s) : launch_smc_t<F32, false>(a, s);
+  const void* k = bf16 ? (vec ? sd_tail_kernel<Bf16, true>() : sd_tail_kernel<Bf16, false>())
+                       : (vec ? sd_tail_kernel<F32, true>() : sd_tail_kernel<F32, false>());
+  return launch(k, (unsigned)a.s.ngroups, SD_BLOCK, a, s, t.tail_start, t.tail_stop);
+}
+
+hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
+  hipError_t e = launch(stream_kernel(bf16, vec, p.seg > 1), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
+                        t.stream_stop);
+  if (e != hipSuccess) return e;
+  const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())
+                       : (vec ? smc_tail_kernel<F32, true>() : smc_tail_kernel<F32, false>());
+  return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
 }
 
 }  // namespace smcsd

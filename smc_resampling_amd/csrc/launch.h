@@ -66,10 +66,16 @@ struct Plan {
   int grid;
 };
 
+// Events that take the start and stop times of a call's two kernels (any may
+// be null).
+struct KernelTimers {
+  hipEvent_t stream_start, stream_stop, tail_start, tail_stop;
+};
+
 hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p);
-// Each launches the streaming kernel, records `mark` (a hipEvent_t, may be
-// null) after it, then launches the tail kernel.
-hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark);
-hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, hipEvent_t mark);
+// Each launches the streaming kernel, then the tail kernel; with timers, the
+// launches carry the events.
+hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);
+hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);
 
 }  // namespace smcsd

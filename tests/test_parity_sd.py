@@ -153,3 +153,45 @@ def test_sd_zero_residual_fallback():
     assert fl & 2
     assert [int(na[b]) for b in (0, 2, 5)] == [0, 2, 2]
     check_sd(c, "zero residual")
+
+
+def test_sd_multi_tile_segments_sampled():
+    """A batch large enough (2048 sequences, K=8, V=32768: 557056 tiles) that
+    every streamed segment spans at least two tiles whatever the occupancy
+    (at most 8192 wavefronts, 32 tiles each per segment step), so a bonus draw
+    locates its tile through the bonus row's own tile partials.  The batch is
+    32 replicas of a 64-sequence case (every other sequence with draft ==
+    target, so all of its drafts are accepted) with fresh uniforms; a sample
+    of the sequences is checked against the oracle."""
+    import torch
+
+    import smc_resampling_amd as s
+    from compare import compare_sd
+    from gpu_util import DEV, dev_logits, run_sd_oracle, say
+
+    B0, R, K, V, T = 64, 32, 8, 32768, 0.7
+    c = sd_case(4242, B0, V, T=T, K=K, delta=np.where(np.arange(B0) % 2 == 0, 0.0, 1.0), dtype="bf16")
+    B = B0 * R
+    rng = np.random.default_rng(4243)
+    u = rng.random(B * (K + 1)).astype(np.float32)
+    tgt = dev_logits(c["target"]).repeat(R, 1)
+    drf = dev_logits(c["draft"]).repeat(R, 1)
+    tok = torch.from_numpy(np.tile(c["tokens"], R)).to(DEV)
+    na, ft, fl = s.sd_verify(tgt, drf, tok, torch.from_numpy(u).to(DEV), T, K=K)
+    torch.cuda.synchronize()
+    na, ft = na.cpu().numpy(), ft.cpu().numpy()
+    del tgt, drf
+    pick = np.array(sorted(set([0, 1, 62, 63, 64, 1001, B - 2, B - 1]) | set(rng.choice(B, 24, replace=False).tolist())))
+    src = pick % B0
+    sub = dict(target=np.concatenate([c["target"][b * (K + 1):(b + 1) * (K + 1)] for b in src]),
+               draft=np.concatenate([c["draft"][b * K:(b + 1) * K] for b in src]),
+               tokens=np.concatenate([c["tokens"][b * K:(b + 1) * K] for b in src]),
+               uniforms=np.concatenate([u[b * (K + 1):(b + 1) * (K + 1)] for b in pick]),
+               offsets=None, K=K, Kb=np.full(len(pick), K, np.int32), T=T, dtype="bf16")
+    ref = run_sd_oracle(sub)
+    t = compare_sd(sub, ref, na[pick], ft[pick], "multi-tile segments")
+    say(f"[sd multi-tile segments B={B}] {t.summary()} all-accepted={int((na[pick] == K).sum())}/{len(pick)} "
+        f"flags gpu={int(fl.item())}")
+    t.assert_ok()
+    assert (na[pick] == K).sum() >= 4  # the picked even sequences (draft == target) take the bonus draw
+    assert int(fl.item()) & ~8 == 0
