@@ -171,42 +171,64 @@ __device__ __forceinline__ int tile_elem(int lane, int e) {
   return (e / DT::VEC) * (WAVE * DT::VEC) + lane * DT::VEC + (e % DT::VEC);
 }
 
+// 16 bytes of raw logits in four 32-bit words (a native vector, so loads land
+// in place).
+using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+
 template <typename DT>
 struct Raw {
   static constexpr int CHUNKS = PER_LANE / DT::VEC;
-  uint4 q[CHUNKS];
+  u32x4 q[CHUNKS];
 };
 
-// Load tile `tile` of `row` (V logits) without a branch: an element past the
-// row is read from a clamped address inside it, so the tile holds copies of
-// real logits there until mask_tail() turns them into -inf (only the last tile
-// of a row reaches past V).  A conditional load would make the compiler wait
-// for the data right away, which defeats loads kept in flight.  VECLOAD
-// requires a 16-byte aligned row base and V % DT::VEC == 0.
+// Buffer resource over the n bytes at p (a raw buffer: loads at byte offsets
+// of n or more return 0 instead of touching memory).  p and n must be the
+// same across the wavefront.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uint32_t n) {
+  constexpr int GFX9_RAW_BUFFER_WORD3 = 0x00020000;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)n, GFX9_RAW_BUFFER_WORD3);
+}
+
+// Load tile `tile` of `row` (V logits; row and tile the same across the
+// wavefront) through a buffer resource that ends where the row does: an
+// element past the row reads as 0 until mask_tail() turns it into -inf (only
+// the last tile of a row reaches past V).  No load sits behind a branch (a
+// conditional load would make the compiler wait for the data right away, which
+// defeats loads kept in flight), and every lane's offsets are the same for
+// every tile, so a tile costs its loads and a few scalar instructions.
+// VECLOAD (one 16-byte load per chunk) requires a 16-byte aligned row base and
+// V % DT::VEC == 0; otherwise each element is loaded on its own.  The loads
+// are non-temporal (logits are streamed, not reused from cache: measured
+// faster for the streaming and the decision kernels alike).
 template <typename DT, bool VECLOAD>
 __device__ __forceinline__ Raw<DT> load_raw(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
                                             int lane) {
+  using raw = typename DT::raw;
   Raw<DT> r;
-  const int v = (int)V;  // V <= 524288
-  const int base = (int)tile * TILE;
+  const int64_t t0 = tile * TILE;
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_over(reinterpret_cast<const void*>(uniform64(reinterpret_cast<int64_t>(row + t0))),
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)((V - t0) * (int64_t)sizeof(raw))));
+  const int lane_bytes = lane * DT::VEC * (int)sizeof(raw);  // 16
+  constexpr int pol = 2;                                      // cache policy: non-temporal
 #pragma unroll
   for (int c = 0; c < Raw<DT>::CHUNKS; c++) {
-    const int off = base + c * (WAVE * DT::VEC) + lane * DT::VEC;
+    const int off = lane_bytes + c * WAVE * 16;
     if constexpr (VECLOAD) {
-      r.q[c] = *reinterpret_cast<const uint4*>(row + (off < v ? off : v - DT::VEC));
+      r.q[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, pol);
     } else {
       uint32_t w[4];
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         if constexpr (DT::VEC == 8) {
-          const uint32_t lo = row[min(off + 2 * k, v - 1)];
-          const uint32_t hi = row[min(off + 2 * k + 1, v - 1)];
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4 * k, 0, pol);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4 * k + 2, 0, pol);
           w[k] = lo | (hi << 16);
         } else {
-          w[k] = __float_as_uint(row[min(off + k, v - 1)]);
+          w[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * k, 0, pol);
         }
       }
-      r.q[c] = make_uint4(w[0], w[1], w[2], w[3]);
+      r.q[c] = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
   return r;
@@ -232,7 +254,7 @@ __device__ __forceinline__ void mask_tail(Raw<DT>& r, int64_t V, int64_t tile, i
         if (off + k >= v) w[k] = 0xFF800000u;
       }
     }
-    r.q[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    r.q[c] = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -248,7 +270,7 @@ __device__ __forceinline__ Raw<DT> load_tile(const typename DT::raw* __restrict_
 // the VEC logits of chunk c, as fp32
 template <typename DT>
 __device__ __forceinline__ void unpack(const Raw<DT>& r, int c, float (&v)[DT::VEC]) {
-  const uint4 w = r.q[c];
+  const u32x4 w = r.q[c];
   if constexpr (DT::VEC == 8) {
     v[0] = __uint_as_float(w.x << 16);
     v[1] = __uint_as_float(w.x & 0xFFFF0000u);
