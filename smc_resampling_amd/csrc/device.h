@@ -174,6 +174,7 @@ __device__ __forceinline__ int tile_elem(int lane, int e) {
 // 16 bytes of raw logits in four 32-bit words (a native vector, so loads land
 // in place).
 using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+using u32x2 = unsigned int __attribute__((ext_vector_type(2)));
 
 template <typename DT>
 struct Raw {

@@ -205,13 +205,23 @@ __device__ __forceinline__ void cursor_set(GroupCursor& cu, int64_t g, const Ste
     cu.G = make_group(g, g * a.K, (g + 1) * a.K, a.K, a.rows_d);
     return;
   }
+  int32_t o0, o1;
   if (g + 1 - cu.g0 >= WAVE || g < cu.g0) {  // refill the window
     cu.g0 = g;
-    cu.win = g + lane <= a.ngroups ? a.offsets[g + lane] : 0;
+    cu.win = a.offsets[min(g + lane, a.ngroups)];
+    // read it here: the wait for the load (and for every tile load issued
+    // before it) then stays in this rare branch instead of following every
+    // group change (the empty asm keeps the reads from being merged with the
+    // other branch's)
+    o0 = __builtin_amdgcn_readlane(cu.win, 0);
+    o1 = __builtin_amdgcn_readlane(cu.win, 1);
+    asm volatile("" ::"s"(o0), "s"(o1));
+  } else {
+    const int i = (int)(g - cu.g0);
+    o0 = __builtin_amdgcn_readlane(cu.win, i);
+    o1 = __builtin_amdgcn_readlane(cu.win, i + 1);
   }
-  const int i = (int)(g - cu.g0);
-  cu.G = make_group(g, __builtin_amdgcn_readlane(cu.win, i), __builtin_amdgcn_readlane(cu.win, i + 1), a.K,
-                    a.rows_d);
+  cu.G = make_group(g, o0, o1, a.K, a.rows_d);
 }
 
 // TP: the call's segments span several tiles, so each group's bonus row also
@@ -417,14 +427,32 @@ template <int NT>
 __device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, TailLds& L) {
   constexpr int TPR = 16;  // threads per row: one DPP row
   const int sub = threadIdx.x & (TPR - 1);
+  // the group's partials through a buffer resource: 32-bit offsets
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(part, (uint32_t)(R * nseg * (int)sizeof(float2)));
   for (int r0 = 0; r0 < R; r0 += NT / TPR) {
     const int r = r0 + (int)threadIdx.x / TPR;
     float m = -INFINITY;
     double s = 0.0;
     if (r < R) {
-      for (int k = sub; k < nseg; k += TPR) {
-        const float2 pt = part[(int64_t)r * nseg + k];
-        fold(m, s, pt.x, (double)pt.y);
+      // at most MAX_TILES / 16 = 16 partials per thread, in batches of GB
+      // loads in flight (8, or 4 in the smaller workgroups that keep fewer
+      // registers; indices past the row clamped, so the loads need no branch;
+      // straight-line code, so loads issued before the call are not waited
+      // for here), folded in ascending k
+      constexpr int GB = NT >= 1024 ? 8 : 4;
+      constexpr int NB = MAX_TILES / (GB * TPR);
+      const int row0 = r * nseg;
+#pragma unroll
+      for (int h = 0; h < NB; h++) {
+        const int k0 = sub + h * GB * TPR;
+        if (h > 0 && nseg <= h * GB * TPR) break;
+        u32x2 v[GB];
+#pragma unroll
+        for (int j = 0; j < GB; j++)
+          v[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (row0 + min(k0 + j * TPR, nseg - 1)) * 8, 0, 0);
+#pragma unroll
+        for (int j = 0; j < GB; j++)
+          if (k0 + j * TPR < nseg) fold(m, s, __uint_as_float(v[j][0]), (double)__uint_as_float(v[j][1]));
       }
     }
     // lanes i and 15-i, then 7-i inside each half, then the quads: lane 0 of
@@ -688,10 +716,12 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   const int32_t xt = token_of(s, G);
   const float uj = (int)threadIdx.x < kb ? a.uniforms[t0 + threadIdx.x] : 0.0f;
   const float ufin = a.uniforms[t0 + kb];
-  int ok = 1;
-  const float z = token_logit<DT>(s, G, b, xt, &ok);
+  // the partials' loads go out before the token logits', which wait for the
+  // tokens
   merge_rows<SD_BLOCK>(pg, 2 * kb + 1, s.nseg, L);
   stage_partials<SD_BLOCK>(bonus_partials(s, G.fr0, b, kb), ntiles, L);
+  int ok = 1;
+  const float z = token_logit<DT>(s, G, b, xt, &ok);
   store_tokens(z, ok, uj, kb, L);
   __syncthreads();
   uint32_t fl = 0;
@@ -954,10 +984,10 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   const int32_t xt = token_of(s, G);
   const float lw_in = a.logw[i];
   const float ub = a.bonus_u[i];
-  int ok = 1;
-  const float z = token_logit<DT>(s, G, i, xt, &ok);
   merge_rows<BLOCK>(pg, 2 * K + 1, s.nseg, L);
   stage_partials<BLOCK>(bonus_partials(s, G.fr0, i, K), s.ntiles, L);
+  int ok = 1;
+  const float z = token_logit<DT>(s, G, i, xt, &ok);
   store_tokens(z, ok, 0.0f, K, L);
   __syncthreads();
   uint32_t fl = 0;
