@@ -382,6 +382,7 @@ struct TailLds {
 };
 struct PromptLds {
   float lw[SMCSD_MAX_N];
+  int hi[SMCSD_MAX_N];   // particle i supplies the slots [hi[i-1], hi[i])
   int anc[SMCSD_MAX_N];
 };
 union SharedLds {
@@ -638,7 +639,9 @@ __device__ __forceinline__ void residual_weights(const Raw<DT>& rt, const Raw<DT
     for (int k = 0; k < DT::VEC; k++) {
       const float p = __builtin_amdgcn_exp2f(fmaf(vt[k], c, -At));
       const float q = __builtin_amdgcn_exp2f(fmaf(vd[k], c, -Ad));
-      r[ch * DT::VEC + k] = fmaxf(p - q, 0.0f);
+      // p, q <= 1, so max(p - q, 0) is p - q clamped to [0, 1]: the
+      // subtraction's own output clamp
+      r[ch * DT::VEC + k] = __builtin_amdgcn_fmed3f(p - q, 0.0f, 1.0f);
     }
   }
 }
@@ -937,10 +940,7 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
       hi = max(hi, lo);
       carry = __builtin_amdgcn_readlane(hi, WAVE - 1);
       if (ii < N) {
-        for (int k = lo; k < hi; k++) {
-          a.ancestors[base + k] = ii;
-          Q.anc[k] = ii;
-        }
+        Q.hi[ii] = hi;
         a.logw[base + ii] = do_res ? 0.0f : Q.lw[ii];
       }
     }
@@ -950,6 +950,20 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
     }
     fl = wave_or_flags(fl);
     if (lane == 0) raise_flags(s.flags, fl);
+  }
+  __syncthreads();
+  // slot k's ancestor: the first particle whose range ends past k (the range
+  // ends never decrease and the last one is N), found by bisection, one
+  // thread per slot
+  for (int k = threadIdx.x; k < N; k += BLOCK) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (Q.hi[mid] > k) hi = mid;
+      else lo = mid + 1;
+    }
+    a.ancestors[base + k] = lo;
+    Q.anc[k] = lo;
   }
   __syncthreads();
   // page-table rows by ancestor (the identity when the prompt kept its particles)
