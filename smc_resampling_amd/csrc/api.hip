@@ -92,6 +92,7 @@ void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, 
   s->ntiles = ntiles_of(V);
   s->seg = plan.seg;
   s->nseg = plan.nseg;
+  s->tp = plan.tp ? 1 : 0;
   s->units = plan.units;
   s->c = (float)(1.4426950408889634 / (double)T);
   s->part = reinterpret_cast<float2*>(ws + part_off);

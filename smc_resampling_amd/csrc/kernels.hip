@@ -470,10 +470,14 @@ __device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int 
   }
 }
 
-// Per-tile partials of the bonus row kb of group g (first row fr0): the
-// segment partials when segments are one tile long.
-__device__ __forceinline__ const float2* bonus_partials(const StepArgs& s, int64_t fr0, int64_t g, int kb) {
-  return s.seg == 1 ? s.part + (fr0 + kb) * s.nseg : s.tpart + g * s.ntiles;
+// Partials of the bonus row kb of group g (first row fr0): its tile partials
+// when the call keeps them, else its segment partials.  *np entries of *per
+// tiles each.
+__device__ __forceinline__ const float2* bonus_partials(const StepArgs& s, int64_t fr0, int64_t g, int kb, int* np,
+                                                        int* per) {
+  *np = s.tp ? s.ntiles : s.nseg;
+  *per = s.tp ? 1 : s.seg;
+  return s.tp ? s.tpart + g * s.ntiles : s.part + (fr0 + kb) * s.nseg;
 }
 
 // The n partials at src into L.P.  Whole workgroup.
@@ -722,7 +726,9 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   // the partials' loads go out before the token logits', which wait for the
   // tokens
   merge_rows<SD_BLOCK>(pg, 2 * kb + 1, s.nseg, L);
-  stage_partials<SD_BLOCK>(bonus_partials(s, G.fr0, b, kb), ntiles, L);
+  int bnp, bper;
+  const float2* bp = bonus_partials(s, G.fr0, b, kb, &bnp, &bper);
+  stage_partials<SD_BLOCK>(bp, bnp, L);
   int ok = 1;
   const float z = token_logit<DT>(s, G, b, xt, &ok);
   store_tokens(z, ok, uj, kb, L);
@@ -761,7 +767,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     // every draft accepted: the bonus token from p_{K_b}
     const RowStat sk = stat_of(L, kb);
     if (!sk.ok) fl |= FLAG_NONFINITE;
-    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, sk.M, (double)ufin, ntiles, 1, L, fl);
+    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, sk.M, (double)ufin, bnp, bper, L, fl);
   } else {
     // residual max(0, p_n - q_n): each wavefront weighs its tiles and keeps
     // the weights of the last one in registers for the search
@@ -999,7 +1005,9 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   const float lw_in = a.logw[i];
   const float ub = a.bonus_u[i];
   merge_rows<BLOCK>(pg, 2 * K + 1, s.nseg, L);
-  stage_partials<BLOCK>(bonus_partials(s, G.fr0, i, K), s.ntiles, L);
+  int bnp, bper;
+  const float2* bp = bonus_partials(s, G.fr0, i, K, &bnp, &bper);
+  stage_partials<BLOCK>(bp, bnp, L);
   int ok = 1;
   const float z = token_logit<DT>(s, G, i, xt, &ok);
   store_tokens(z, ok, 0.0f, K, L);
@@ -1024,7 +1032,7 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   }
   const RowStat sk = stat_of(L, K);
   if (!sk.ok) fl |= FLAG_NONFINITE;
-  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, sk.M, (double)ub, s.ntiles, 1, L, fl);
+  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, sk.M, (double)ub, bnp, bper, L, fl);
   or_flags(fl, L);
   __syncthreads();
   const int64_t p = i / a.N;
@@ -1084,21 +1092,26 @@ static const void* stream_kernel(bool bf16, bool vec, bool tp) {
 }
 
 // Segments long enough that each resident wavefront streams about 32 units
-// (fewer wavefront reductions on large calls), at most 8 tiles so that a draw
-// searches at most 8 tiles of a segment.  The streaming grid is what the
-// device holds at once, fewer when there is not one unit per wavefront.
+// (fewer wavefront reductions on large calls), at least SEG_MIN and at most 8
+// tiles.  From TP_MIN_SEG tiles on, the bonus rows also get tile partials, so
+// a draw re-reads one tile rather than its segment.  The streaming grid is
+// what the device holds at once, fewer when there is not one unit per
+// wavefront.
+constexpr int SEG_MIN = 1, TP_MIN_SEG = 2;
+
 hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p) {
   const int resident = resident_blocks(stream_kernel(bf16, vec, false));
   if (resident <= 0) return hipErrorInvalidDevice;
   const int64_t waves = (int64_t)resident * WAVES_PER_BLOCK;
   const int64_t tiles = rows * ntiles;
   int64_t seg = tiles / (32 * waves);
-  seg = seg < 1 ? 1 : (seg > 8 ? 8 : seg);
+  seg = seg < SEG_MIN ? SEG_MIN : (seg > 8 ? 8 : seg);
   if (seg > ntiles) seg = ntiles;
   const int nseg = (int)((ntiles + seg - 1) / seg);
   p->seg = (ntiles + nseg - 1) / nseg;
   p->nseg = nseg;
   p->units = rows * nseg;
+  p->tp = p->seg >= TP_MIN_SEG;
   const int64_t want = (p->units + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   p->grid = (int)(want < resident ? want : resident);
   if (p->grid < 1) p->grid = 1;
@@ -1127,7 +1140,7 @@ static const void* smc_tail_kernel() {
 }
 
 hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
-  hipError_t e = launch(stream_kernel(bf16, vec, p.seg > 1), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
+  hipError_t e = launch(stream_kernel(bf16, vec, p.tp), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
                         t.stream_stop);
   if (e != hipSuccess) return e;
   const void* k = bf16 ? (vec ? sd_tail_kernel<Bf16, true>() : sd_tail_kernel<Bf16, false>())
@@ -1136,7 +1149,7 @@ hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStr
 }
 
 hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
-  hipError_t e = launch(stream_kernel(bf16, vec, p.seg > 1), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
+  hipError_t e = launch(stream_kernel(bf16, vec, p.tp), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
                         t.stream_stop);
   if (e != hipSuccess) return e;
   const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())

@@ -28,6 +28,7 @@ struct StepArgs {
   int ntiles;     // tiles per row
   int seg;        // tiles per segment
   int nseg;       // segments per row
+  int tp;         // 1: each group's bonus row also has tile partials in tpart
   int64_t units;  // rows * nseg
   float c;        // log2(e) / T
   float2* part;   // [units] segment partials (max of z c, sum of 2^(z c - max))
@@ -62,6 +63,7 @@ struct SmcArgs {
 // Segment length and streaming grid of a call.
 struct Plan {
   int seg, nseg;
+  bool tp;  // bonus-row tile partials (segments long enough that a re-read would cost)
   int64_t units;
   int grid;
 };

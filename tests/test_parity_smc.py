@@ -29,6 +29,22 @@ def test_smc_max_particles():
     check_smc_steps(c, steps=1, ess_frac=2.0, label="N=1024")
 
 
+def test_smc_dominant_particle():
+    """One particle holds all the weight (first, middle or last of its prompt):
+    every slot descends from it, the other particles' slot ranges are empty."""
+    from gpu_util import check_smc_steps, run_smc_gpu
+
+    c = smc_case(90, 3, 64, 2, 500, dtype="bf16", L=3)
+    lw = np.zeros(3 * 64, np.float32)
+    lw[0], lw[64 + 37], lw[2 * 64 + 63] = 90.0, 90.0, 90.0
+    c["logw"] = lw
+    g = run_smc_gpu(c, lw, c["pt"])
+    assert (g["resampled"] == 1).all()
+    anc = g["ancestors"].reshape(3, 64)
+    assert (anc[0] == 0).all() and (anc[1] == 37).all() and (anc[2] == 63).all()
+    check_smc_steps(c, steps=1, label="dominant particle")
+
+
 def test_smc_zero_weights_flag():
     from gpu_util import run_smc_gpu
 
