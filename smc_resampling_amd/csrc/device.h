@@ -73,6 +73,21 @@ __device__ __forceinline__ float wave_max(float v) {
                fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
+// Maximum over the 64 lanes of values that are never NaN, through order-
+// preserving integer keys: an unsigned max needs no NaN quieting and fuses
+// with its DPP move, and the four row results combine in scalar registers.
+__device__ __forceinline__ float wave_max_nonnan(float v) {
+  const uint32_t b = __float_as_uint(v);
+  uint32_t k = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, DPP_QUAD_1032, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, DPP_QUAD_2301, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, DPP_ROR4, 0xF, 0xF, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, DPP_ROR8, 0xF, 0xF, false));
+  const uint32_t r = max(max((uint32_t)__builtin_amdgcn_readlane((int)k, 0), (uint32_t)__builtin_amdgcn_readlane((int)k, 16)),
+                         max((uint32_t)__builtin_amdgcn_readlane((int)k, 32), (uint32_t)__builtin_amdgcn_readlane((int)k, 48)));
+  return __uint_as_float(r ^ ((r & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<DPP_QUAD_1032>(v);
   v += dpp_f32<DPP_QUAD_2301>(v);

@@ -160,7 +160,7 @@ __device__ __forceinline__ void lane_merge(float& m, float& s, float m2, float s
 // The wavefront's (MC, S) from per-lane (m, s): MC = max m, S = sum s 2^(m - MC).
 // All -inf gives (-inf, 0); a NaN s stays NaN.
 __device__ __forceinline__ float2 wave_partial(float m, float s) {
-  const float M = wave_max(m);
+  const float M = wave_max_nonnan(m);  // m comes from fmaxf: never NaN
   const float sc = m > -INFINITY ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
   return make_float2(M, wave_sum(s * sc));
 }
