@@ -53,6 +53,8 @@ def _declare(lib):
     lib.oracle_sd_final_cdf.restype = _I
     lib.oracle_smc_step.argtypes = [_I, _I, _I, _I, _I64, _D, _D] + [_P] * 8 + [_I] + [_P] * 9
     lib.oracle_smc_step.restype = _I
+    lib.oracle_smc_step_power.argtypes = [_I, _I, _I, _I, _I64, _D, _D, _D] + [_P] * 8 + [_I] + [_P] * 9
+    lib.oracle_smc_step_power.restype = _I
     return lib
 
 
@@ -144,8 +146,10 @@ def sd_final_cdf(target, draft, b, n, T, K=None, offsets=None, lib=None):
     return cdf, fl
 
 
-def smc_step(target, draft, tokens, bonus_u, resample_u, logw, T, ess_frac, P, N, K, pt_in=None, lib=None):
-    """One SMC-SD reweight / ESS / systematic-resample step.
+def smc_step(target, draft, tokens, bonus_u, resample_u, logw, T, ess_frac, P, N, K, pt_in=None, lib=None,
+             beta=None):
+    """One SMC-SD reweight / ESS / systematic-resample step (with ``beta``, the
+    power target: increments beta log p - log q, bonus from softmax(beta z/T)).
 
     ``logw`` (float32 [P*N]) is not modified; the updated log-weights are
     returned.  Returns dict(logw, bonus, ancestors, ess, resampled, pt_out,
@@ -175,8 +179,12 @@ def smc_step(target, draft, tokens, bonus_u, resample_u, logw, T, ess_frac, P, N
     bm = np.zeros(max(PN, 1))
     em = np.zeros(max(P, 1))
     rm = np.zeros(max(P, 1))
-    lib.oracle_smc_step(_dtype_code(target), P, N, K, V, T, ess_frac, _ptr(target), _ptr(draft), _ptr(tokens),
-                        _ptr(bonus_u), _ptr(resample_u), _ptr(lw), _ptr(pt_in), _ptr(pt_out), L, _ptr(bonus),
-                        _ptr(anc), _ptr(ess), _ptr(res), _ptr(fl), _ptr(cw), _ptr(bm), _ptr(em), _ptr(rm))
+    tail = (_ptr(target), _ptr(draft), _ptr(tokens), _ptr(bonus_u), _ptr(resample_u), _ptr(lw), _ptr(pt_in),
+            _ptr(pt_out), L, _ptr(bonus), _ptr(anc), _ptr(ess), _ptr(res), _ptr(fl), _ptr(cw), _ptr(bm), _ptr(em),
+            _ptr(rm))
+    if beta is None:
+        lib.oracle_smc_step(_dtype_code(target), P, N, K, V, T, ess_frac, *tail)
+    else:
+        lib.oracle_smc_step_power(_dtype_code(target), P, N, K, V, T, float(beta), ess_frac, *tail)
     return dict(logw=lw, bonus=bonus, ancestors=anc, ess=ess, resampled=res, pt_out=pt_out, flags=int(fl[0]),
                 cum_weight=cw[:PN], bonus_margin=bm[:PN], ess_margin=em[:P], resample_margin=rm[:P])

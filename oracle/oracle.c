@@ -46,7 +46,13 @@
  *   - systematic resampling: U_k = (u + k) / N, a_k = smallest i with
  *     C_i > U_k, C the normalised inclusive cumulative weight; after
  *     resampling every log-weight is 0;
- *   - page tables: row k of the output is row a_k of the input.
+ *   - page tables: row k of the output is row a_k of the input;
+ *   - power target ([SMC] sec. 3, Flexibilitaet: the framework also targets
+ *     modified distributions such as power sampling, without retraining): the
+ *     target is proportional to p^beta, so a draft token adds
+ *     beta * log p - log q to the log-weight, and the (K+1)-th token comes
+ *     from softmax(beta * z / T), i.e. temperature T / beta; beta = 1 is the
+ *     plain step above.
  */
 #include <math.h>
 #include <stdint.h>
@@ -265,8 +271,9 @@ int oracle_sd_final_cdf(int dtype, int b, int K, int64_t V, double T, const void
  * Particle i = p*N + n owns target rows i*(K+1) .. i*(K+1)+K and draft rows
  * i*K .. i*K+K-1.
  *
- *   log-weight:   logw'_i = fp32(logw_i + sum_{j<K} (log p_ij(x_ij) - log q_ij(x_ij)))
- *   bonus token:  inverse CDF of p_{i,K} with bonus_u[i]
+ *   log-weight:   logw'_i = fp32(logw_i + sum_{j<K} (beta log p_ij(x_ij) - log q_ij(x_ij)))
+ *   bonus token:  inverse CDF of softmax(beta z_{i,K} / T) with bonus_u[i]
+ *                 (beta = 1 for the plain step: p_{i,K})
  *   ESS:          Kish, (sum w)^2 / sum w^2, w_i = exp(logw'_i - max)
  *   resample iff ESS < ess_frac * N: systematic with resample_u[p];
  *                 ancestors (local indices), logw_out = 0, page-table rows
@@ -279,13 +286,13 @@ int oracle_sd_final_cdf(int dtype, int b, int K, int64_t V, double T, const void
  * resample_margin[p] = min_k distance of U_k to its interval edges (optional).
  * Returns 0.
  */
-int oracle_smc_step(int dtype, int P, int N, int K, int64_t V, double T, double ess_frac,
-                    const void* target, const void* draft, const int32_t* tokens,
-                    const float* bonus_u, const float* resample_u, float* logw,
-                    const int32_t* pt_in, int32_t* pt_out, int L, int32_t* bonus,
-                    int32_t* ancestors, float* ess, int32_t* resampled, uint32_t* flags,
-                    double* cum_weight, double* bonus_margin, double* ess_margin,
-                    double* resample_margin) {
+int oracle_smc_step_power(int dtype, int P, int N, int K, int64_t V, double T, double beta,
+                          double ess_frac, const void* target, const void* draft,
+                          const int32_t* tokens, const float* bonus_u, const float* resample_u,
+                          float* logw, const int32_t* pt_in, int32_t* pt_out, int L,
+                          int32_t* bonus, int32_t* ancestors, float* ess, int32_t* resampled,
+                          uint32_t* flags, double* cum_weight, double* bonus_margin,
+                          double* ess_margin, double* resample_margin) {
   double* w = (double*)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
   double* pw = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
   double* C = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
@@ -303,12 +310,12 @@ int oracle_smc_step(int dtype, int P, int N, int K, int64_t V, double T, double 
         double Mt, lSt, Md, lSd;
         if (oracle_row_stats(dtype, trow, V, T, &Mt, &lSt)) fl |= ORACLE_FLAG_NONFINITE;
         if (oracle_row_stats(dtype, drow, V, T, &Md, &lSd)) fl |= ORACLE_FLAG_NONFINITE;
-        delta += logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);
+        delta += beta * logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);
       }
       lw[n] = (float)((double)logw[i] + delta);
       if (isnan(lw[n]) || lw[n] == INFINITY) fl |= ORACLE_FLAG_NONFINITE;
-      /* the (K+1)-th token, drawn from the target's row K */
-      final_weights(dtype, row_ptr(dtype, target, i * (K + 1) + K, V), NULL, V, T, w, &fl);
+      /* the (K+1)-th token, drawn from the target's row K (power: at T / beta) */
+      final_weights(dtype, row_ptr(dtype, target, i * (K + 1) + K, V), NULL, V, T / beta, w, &fl);
       double m = 0.0;
       bonus[i] = (int32_t)inverse_cdf(w, V, (double)bonus_u[i], &m, &fl);
       if (bonus_margin) bonus_margin[i] = m;
@@ -381,4 +388,18 @@ int oracle_smc_step(int dtype, int P, int N, int K, int64_t V, double T, double 
   free(lw);
   if (flags) *flags |= fl;
   return 0;
+}
+
+/* The plain SMC-SD step: the power step with beta = 1 (1 * x and T / 1 are
+ * exact, so the arithmetic is the same). */
+int oracle_smc_step(int dtype, int P, int N, int K, int64_t V, double T, double ess_frac,
+                    const void* target, const void* draft, const int32_t* tokens,
+                    const float* bonus_u, const float* resample_u, float* logw,
+                    const int32_t* pt_in, int32_t* pt_out, int L, int32_t* bonus,
+                    int32_t* ancestors, float* ess, int32_t* resampled, uint32_t* flags,
+                    double* cum_weight, double* bonus_margin, double* ess_margin,
+                    double* resample_margin) {
+  return oracle_smc_step_power(dtype, P, N, K, V, T, 1.0, ess_frac, target, draft, tokens, bonus_u,
+                               resample_u, logw, pt_in, pt_out, L, bonus, ancestors, ess, resampled,
+                               flags, cum_weight, bonus_margin, ess_margin, resample_margin);
 }

@@ -489,6 +489,60 @@ def check_smc_page_table_identity(lib):
     assert (r["pt_out"] == np.arange(N * L).reshape(N, L)).all()
 
 
+def check_power_bonus_law(lib):
+    """Power target: the (K+1)-th token's law over its uniform is exactly
+    softmax(beta z_K / T) (scipy), for a sharpening and a flattening beta."""
+    rng = np.random.default_rng(49)
+    V, K, T = 6, 1, 0.9
+    zt = (2 * rng.standard_normal((K + 1, V))).astype(np.float32)
+    zd = (zt[:K] + rng.standard_normal((K, V))).astype(np.float32)
+    for beta in (2.5, 0.4):
+        law_ref = softmax(beta * zt[K].astype(np.float64) / T)
+        mid, ln = _midpoints(np.cumsum(law_ref))
+        N = len(mid)
+        tok = np.tile(rng.integers(0, V, K).astype(np.int32), N)
+        r = oracle.smc_step(np.tile(zt, (N, 1)), np.tile(zd, (N, 1)), tok, mid.astype(np.float32), [0.5],
+                            np.zeros(N, np.float32), T, 0.0, 1, N, K, lib=lib, beta=beta)
+        law = np.zeros(V)
+        for t, w in zip(r["bonus"], ln):
+            law[t] += w
+        assert np.abs(law - law_ref).max() < 1e-9, (beta, law, law_ref)
+
+
+def check_power_increment(lib):
+    """Power target with draft == target: each draft token adds
+    beta log p - log p = (beta - 1) log p (scipy log_softmax)."""
+    rng = np.random.default_rng(51)
+    P, N, K, V, T = 1, 4, 3, 64, 1.2
+    zt = (3 * rng.standard_normal((P * N * (K + 1), V))).astype(np.float32)
+    zd = zt.reshape(P * N, K + 1, V)[:, :K].reshape(P * N * K, V).copy()
+    tok = rng.integers(0, V, P * N * K).astype(np.int32)
+    lw0 = (0.1 * rng.standard_normal(P * N)).astype(np.float32)
+    lp = log_softmax(zt.astype(np.float64) / T, axis=-1).reshape(P * N, K + 1, V)
+    for beta in (3.0, 0.5):
+        r = oracle.smc_step(zt, zd, tok, rng.random(P * N), [0.5], lw0, T, 0.0, P, N, K, lib=lib, beta=beta)
+        for i in range(P * N):
+            d = (beta - 1.0) * sum(lp[i, j, tok[i * K + j]] for j in range(K))
+            want = float(lw0[i]) + d
+            assert abs(float(r["logw"][i]) - want) <= 1e-6 * max(1.0, abs(want)), (beta, i)
+
+
+def check_power_one_is_plain(lib):
+    """beta = 1 is the plain step, output for output."""
+    rng = np.random.default_rng(53)
+    P, N, K, V = 2, 8, 2, 300
+    zt = (3 * rng.standard_normal((P * N * (K + 1), V))).astype(np.float32)
+    zd = (zt.reshape(P * N, K + 1, V)[:, :K] + rng.standard_normal((P * N, K, V))).astype(np.float32)
+    zd = zd.reshape(P * N * K, V)
+    tok = rng.integers(0, V, P * N * K).astype(np.int32)
+    args = (zt, zd, tok, rng.random(P * N).astype(np.float32), rng.random(P).astype(np.float32),
+            rng.standard_normal(P * N).astype(np.float32), 0.8, 0.7, P, N, K)
+    a = oracle.smc_step(*args, pt_in=np.arange(P * N * 3, dtype=np.int32).reshape(P * N, 3), lib=lib)
+    b = oracle.smc_step(*args, pt_in=np.arange(P * N * 3, dtype=np.int32).reshape(P * N, 3), lib=lib, beta=1.0)
+    for k in ("logw", "bonus", "ancestors", "ess", "resampled", "pt_out"):
+        assert (a[k] == b[k]).all(), k
+
+
 DETERMINISTIC_CHECKS = [
     check_golden_sd_fixed,
     check_golden_sd_csr,
@@ -511,4 +565,7 @@ DETERMINISTIC_CHECKS = [
     check_smc_delta_zero,
     check_smc_bonus_law,
     check_smc_page_table_identity,
+    check_power_bonus_law,
+    check_power_increment,
+    check_power_one_is_plain,
 ]

@@ -31,8 +31,17 @@ MUTATIONS = [
     ("systematic_non_strict", "if (C[n] > U) {", "if (C[n] >= U) {"),
     ("logw_not_reset", "logw[i] = do_resample ? 0.0f : lw[k];", "logw[i] = lw[k];"),
     ("page_table_scatter", "pt_out[i * L + l] = pt_in[src * L + l];", "pt_out[src * L + l] = pt_in[i * L + l];"),
-    ("increment_sign", "delta += logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);",
-     "delta += logprob_with(dtype, drow, x, T, Md, lSd) - logprob_with(dtype, trow, x, T, Mt, lSt);"),
+    ("increment_sign",
+     "delta += beta * logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);",
+     "delta += beta * logprob_with(dtype, drow, x, T, Md, lSd) - logprob_with(dtype, trow, x, T, Mt, lSt);"),
+    ("power_on_draft",
+     "delta += beta * logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);",
+     "delta += logprob_with(dtype, trow, x, T, Mt, lSt) - beta * logprob_with(dtype, drow, x, T, Md, lSd);"),
+    ("power_dropped_from_weight",
+     "delta += beta * logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);",
+     "delta += logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);"),
+    ("power_bonus_temperature", "V, T / beta, w, &fl);", "V, T * beta, w, &fl);"),
+    ("power_bonus_plain", "V, T / beta, w, &fl);", "V, T, w, &fl);"),
     ("old_weight_dropped", "lw[n] = (float)((double)logw[i] + delta);", "lw[n] = (float)delta;"),
     ("bonus_from_first_row", "row_ptr(dtype, target, i * (K + 1) + K, V)", "row_ptr(dtype, target, i * (K + 1), V)"),
     ("weights_not_exponentiated", "pw[n] = exp((double)lw[n] - M);", "pw[n] = (double)lw[n] - M;"),
