@@ -230,6 +230,33 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
                               int32_t* resampled, uint32_t* status_flags, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * The same step for a power-sampling target proportional to p^beta (the
+ * flexibility of "Faster LLM Inference via Sequential Monte Carlo", sec. 3:
+ * modified targets such as power sampling, without retraining).  Arguments
+ * as in smc_reweight_resample, plus:
+ *
+ *   beta                    > 0, finite, with beta / temperature finite.
+ *   log_weights             Out: logw + sum_{j<K} (beta * log p_ij(x_ij)
+ *                           - log q_ij(x_ij)) (or 0 after resampling), p and q
+ *                           at the given temperature.
+ *   bonus_token             drawn from softmax(beta * z_{i,K} / temperature).
+ *
+ * beta = 1 gives exactly smc_reweight_resample's results.  Same workspace size
+ * (smc_workspace_bytes) and error codes; an invalid beta is
+ * SMCSD_ERR_INVALID_ARG.
+ */
+int32_t smc_reweight_resample_power(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,
+                                    float temperature, float beta, float ess_frac,
+                                    const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* bonus_uniforms,
+                                    const float* resample_uniforms, float* log_weights,
+                                    const int32_t* page_table_in, int32_t* page_table_out,
+                                    int32_t pages_per_particle, int32_t* bonus_token,
+                                    int32_t* ancestors, float* ess, int32_t* resampled,
+                                    uint32_t* status_flags, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,8 @@ _SIGNATURES = {
     "smc_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
     "smc_reweight_resample": ([_I32, _I32, _I32, _I32, _I32, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P,
                                _P, _P, _P, _P, _SZ, _P], _I32),
+    "smc_reweight_resample_power": ([_I32, _I32, _I32, _I32, _I32, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                     _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
 }
 
 
@@ -191,9 +193,10 @@ def sd_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, 
 def prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms,
                                   log_weights, temperature, ess_frac, P, N, K, *, page_table_in=None,
                                   page_table_out=None, bonus_token=None, ancestors=None, ess=None, resampled=None,
-                                  status_flags=None, workspace=None, stream=None):
+                                  status_flags=None, workspace=None, stream=None, beta=None):
     """Validate and marshal one SMC step; returns (call, outputs).  ``log_weights``
-    is updated in place when the call runs."""
+    is updated in place when the call runs.  With ``beta``, the power-sampling
+    target (``smc_reweight_resample_power``)."""
     dev = target_logits.device
     dt = _dtype_code(target_logits)
     V = target_logits.shape[-1]
@@ -218,11 +221,12 @@ def prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bon
     nbytes = smc_workspace_bytes(dt, P, N, K, V)
     ws, wsb = _workspace(nbytes, dev, workspace)
     st = stream if stream is not None else _stream(dev)
-    args = (dt, P, N, K, V, float(temperature), float(ess_frac), _ptr(target_logits), _ptr(draft_logits),
+    scal = (float(temperature), float(ess_frac)) if beta is None else (float(temperature), float(beta), float(ess_frac))
+    args = (dt, P, N, K, V, *scal, _ptr(target_logits), _ptr(draft_logits),
             _ptr(draft_tokens), _ptr(bonus_uniforms), _ptr(resample_uniforms), _ptr(log_weights), _ptr(page_table_in),
             _ptr(page_table_out), L, _ptr(bonus_token), _ptr(ancestors), _ptr(ess), _ptr(resampled),
             _ptr(status_flags), _ptr(ws), wsb, st)
-    fn = _lib.smc_reweight_resample
+    fn = _lib.smc_reweight_resample if beta is None else _lib.smc_reweight_resample_power
     keep = (target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms, log_weights,
             page_table_in, ws)
 
@@ -236,7 +240,8 @@ def prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bon
 
 def smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms, log_weights,
                           temperature, ess_frac, P, N, K, **kw):
-    """One SMC-SD step; ``log_weights`` is updated in place.  Returns a dict of outputs."""
+    """One SMC-SD step (``beta=...``: power-sampling target); ``log_weights`` is
+    updated in place.  Returns a dict of outputs."""
     call, out = prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_uniforms,
                                               resample_uniforms, log_weights, temperature, ess_frac, P, N, K, **kw)
     call()

@@ -95,6 +95,7 @@ void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, 
   s->tp = plan.tp ? 1 : 0;
   s->units = plan.units;
   s->c = (float)(1.4426950408889634 / (double)T);
+  s->cb = s->c;
   s->part = reinterpret_cast<float2*>(ws + part_off);
   s->tpart = reinterpret_cast<float2*>(ws + tpart_off);
   s->ctr = reinterpret_cast<uint32_t*>(ws);
@@ -173,19 +174,24 @@ size_t smc_workspace_bytes(int32_t dtype, int32_t P, int32_t N, int32_t K, int32
   return smc_layout(P, N, K, V).total;
 }
 
-int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,
-                              float temperature, float ess_frac, const void* target_logits,
-                              const void* draft_logits, const int32_t* draft_tokens,
-                              const float* bonus_uniforms, const float* resample_uniforms,
-                              float* log_weights, const int32_t* page_table_in,
-                              int32_t* page_table_out, int32_t pages_per_particle,
-                              int32_t* bonus_token, int32_t* ancestors, float* ess,
-                              int32_t* resampled, uint32_t* status_flags, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+static int32_t smc_step(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V, float temperature,
+                        float beta, float ess_frac, const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const float* bonus_uniforms,
+                        const float* resample_uniforms, float* log_weights, const int32_t* page_table_in,
+                        int32_t* page_table_out, int32_t pages_per_particle, int32_t* bonus_token,
+                        int32_t* ancestors, float* ess, int32_t* resampled, uint32_t* status_flags,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
   if (P < 0 || N < 1 || K < 0 || V < 1 || pages_per_particle < 0) return SMCSD_ERR_INVALID_ARG;
   if (!temperature_ok(temperature) || !isfinite(ess_frac) || ess_frac < 0.0f)
     return SMCSD_ERR_INVALID_ARG;
+  // the bonus row's scale beta * log2(e) / T must be a positive finite number
+  const double cb = (double)beta * 1.4426950408889634 / (double)temperature;
+  if (!isfinite(beta) || !(beta > 0.0f) || !isfinite((float)cb) || !((float)cb > 0.0f)) return SMCSD_ERR_INVALID_ARG;
   if (K > SMCSD_MAX_K || N > SMCSD_MAX_N || V > SMCSD_MAX_V || !smc_counters_fit(P))
     return SMCSD_ERR_UNSUPPORTED;
   if (P == 0) return SMCSD_OK;
@@ -212,6 +218,8 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   smcsd::SmcArgs a;
   fill_step(&a.s, plan, target_logits, draft_logits, nullptr, draft_tokens, PN, PN * (K + 1), PN * K, V, K,
             temperature, ws, l.part, l.tpart, status_flags);
+  a.s.cb = (float)cb;
+  a.beta = beta;
   a.N = N;
   a.L = pages_per_particle;
   a.ess_frac = ess_frac;
@@ -228,6 +236,41 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
   return smcsd::launch_smc(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,
+                              float temperature, float ess_frac, const void* target_logits,
+                              const void* draft_logits, const int32_t* draft_tokens,
+                              const float* bonus_uniforms, const float* resample_uniforms,
+                              float* log_weights, const int32_t* page_table_in,
+                              int32_t* page_table_out, int32_t pages_per_particle,
+                              int32_t* bonus_token, int32_t* ancestors, float* ess,
+                              int32_t* resampled, uint32_t* status_flags, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return smc_step(dtype, P, N, K, V, temperature, 1.0f, ess_frac, target_logits, draft_logits, draft_tokens,
+                  bonus_uniforms, resample_uniforms, log_weights, page_table_in, page_table_out,
+                  pages_per_particle, bonus_token, ancestors, ess, resampled, status_flags, workspace,
+                  workspace_bytes, stream);
+}
+
+int32_t smc_reweight_resample_power(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,
+                                    float temperature, float beta, float ess_frac,
+                                    const void* target_logits, const void* draft_logits,
+                                    const int32_t* draft_tokens, const float* bonus_uniforms,
+                                    const float* resample_uniforms, float* log_weights,
+                                    const int32_t* page_table_in, int32_t* page_table_out,
+                                    int32_t pages_per_particle, int32_t* bonus_token,
+                                    int32_t* ancestors, float* ess, int32_t* resampled,
+                                    uint32_t* status_flags, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return smc_step(dtype, P, N, K, V, temperature, beta, ess_frac, target_logits, draft_logits, draft_tokens,
+                  bonus_uniforms, resample_uniforms, log_weights, page_table_in, page_table_out,
+                  pages_per_particle, bonus_token, ancestors, ess, resampled, status_flags, workspace,
+                  workspace_bytes, stream);
 }
 
 }  // extern "C"

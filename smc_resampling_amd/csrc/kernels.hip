@@ -281,6 +281,13 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
   // time: a store is a memory operation the loads' wait counter also counts.
   int csg = (int)(u0 % nseg);
   int ct = csg * seg, cte = min(ntiles, ct + seg);
+  // the scale of the row being reduced: c, or cb for a group's bonus row when
+  // the call gives that row its own (SMC, whose groups are all 2K+1 rows: the
+  // row within its group is the row index modulo 2K+1)
+  const bool split = a.cb != c;
+  const int grows = 2 * a.K + 1;
+  int crr = split ? (int)((u0 / nseg) % grows) : 0;
+  float cc = split && crr == a.K ? a.cb : c;
   float m = -INFINITY, s = 0.0f;
   float2 pb = make_float2(0.0f, 0.0f);
   int64_t pbase = u0;
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
       m = -INFINITY;
       s = 0.0f;
     }
-    lane_fold_tile<DT>(x, c, m, s);
+    lane_fold_tile<DT>(x, cc, m, s);
     if (TP && dst >= 0) {
       const float2 tp = wave_partial(m, s);
       if (lane == 0) a.tpart[dst] = tp;
@@ -309,7 +316,13 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
       }
       m = -INFINITY;
       s = 0.0f;
-      if (++csg == nseg) csg = 0;
+      if (++csg == nseg) {
+        csg = 0;
+        if (split) {
+          if (++crr == grows) crr = 0;
+          cc = crr == a.K ? a.cb : c;
+        }
+      }
       ct = csg * seg;
       cte = min(ntiles, ct + seg);
     }
@@ -545,10 +558,9 @@ __device__ __forceinline__ float2 tile_partial_of(const Raw<DT>& r, float c) {
 // bonus row's own tile partials, or segment partials).  Whole workgroup;
 // every thread gets the token.
 template <typename DT, bool VL, int NW = WAVES_PER_BLOCK>
-__device__ int draw_softmax(const typename DT::raw* __restrict__ row, const StepArgs& a, float M, double u,
+__device__ int draw_softmax(const typename DT::raw* __restrict__ row, const StepArgs& a, float c, float M, double u,
                             int np, int per, TailLds& L, uint32_t& fl) {
   const int lane = threadIdx.x % WAVE, wave = wave_id();
-  const float c = a.c;
   // 1. the segment
   if (wave == 0) {
     auto wt = [&](int k) -> double {
@@ -767,7 +779,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     // every draft accepted: the bonus token from p_{K_b}
     const RowStat sk = stat_of(L, kb);
     if (!sk.ok) fl |= FLAG_NONFINITE;
-    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, sk.M, (double)ufin, bnp, bper, L, fl);
+    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, sk.M, (double)ufin, bnp, bper, L, fl);
   } else {
     // residual max(0, p_n - q_n): each wavefront weighs its tiles and keeps
     // the weights of the last one in registers for the search
@@ -834,7 +846,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
       fl |= FLAG_ZERO_RESIDUAL;
       stage_partials<SD_BLOCK>(pg + (int64_t)n * s.nseg, s.nseg, L);
       __syncthreads();
-      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, st.M, (double)ufin, s.nseg, s.seg, L, fl);
+      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, st.M, (double)ufin, s.nseg, s.seg, L, fl);
     }
   }
   or_flags(fl, L);
@@ -1023,7 +1035,7 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
         const RowStat st = stat_of(L, j), sd = stat_of(L, K + 1 + j);
         if (!st.ok || !sd.ok) fl |= FLAG_NONFINITE;
         if (!L.xok[j]) fl |= FLAG_BAD_INPUT;
-        else dj = log_prob(L.z[j], st, s.c) - log_prob(L.z[K + j], sd, s.c);
+        else dj = (double)a.beta * log_prob(L.z[j], st, s.c) - log_prob(L.z[K + j], sd, s.c);
       }
       delta += wave_sum_f64(dj);
     }
@@ -1032,7 +1044,8 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   }
   const RowStat sk = stat_of(L, K);
   if (!sk.ok) fl |= FLAG_NONFINITE;
-  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, sk.M, (double)ub, bnp, bper, L, fl);
+  // the bonus row's statistics and draw are at its own scale (beta / T)
+  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, s.cb, sk.M, (double)ub, bnp, bper, L, fl);
   or_flags(fl, L);
   __syncthreads();
   const int64_t p = i / a.N;

@@ -31,6 +31,7 @@ struct StepArgs {
   int tp;         // 1: each group's bonus row also has tile partials in tpart
   int64_t units;  // rows * nseg
   float c;        // log2(e) / T
+  float cb;       // scale of each group's bonus row: c, or beta * log2(e) / T for a power target
   float2* part;   // [units] segment partials (max of z c, sum of 2^(z c - max))
   float2* tpart;  // [ngroups * ntiles] tile partials of each group's bonus row
   uint32_t* ctr;  // counter lines (zero between calls)
@@ -46,6 +47,7 @@ struct SdArgs {
 
 struct SmcArgs {
   StepArgs s;
+  float beta;  // power target: draft tokens add beta log p - log q
   int N, L;
   float ess_frac;
   const float* bonus_u;

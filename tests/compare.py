@@ -107,18 +107,19 @@ def bonus_cdf(target, p_row, T):
 
 def compare_smc(inp, ref, out_g, logw_in, pt_in, label="") -> Tally:
     """Lockstep check of one SMC step.  inp: numpy inputs (target, draft, tokens,
-    bonus_u, resample_u, P, N, K, T); ref: oracle.smc_step(...) run from the same
+    bonus_u, resample_u, P, N, K, T, optional beta); ref: oracle.smc_step(...) run from the same
     logw_in / pt_in as the GPU; out_g: numpy GPU outputs (bonus, ancestors, ess,
     resampled, logw, pt_out)."""
     t = Tally()
     P, N, K, T = inp["P"], inp["N"], inp["K"], inp["T"]
+    Tb = T / inp["beta"] if inp.get("beta") is not None else T  # the bonus row's temperature
     for i in range(P * N):
         yg, yo = int(out_g["bonus"][i]), int(ref["bonus"][i])
         if yg == yo:
             t.equal += 1
             t.exempt_equal += int(ref["bonus_margin"][i] < BAND)
         else:
-            _token_diff(t, float(inp["bonus_u"][i]), bonus_cdf(inp["target"], i * (K + 1) + K, T), yg,
+            _token_diff(t, float(inp["bonus_u"][i]), bonus_cdf(inp["target"], i * (K + 1) + K, Tb), yg,
                         f"{label} particle {i} bonus")
     for p in range(P):
         sl = slice(p * N, (p + 1) * N)

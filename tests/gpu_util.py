@@ -76,7 +76,7 @@ def run_smc_gpu(case, logw, pt, ess_frac=0.5):
     out = s.smc_reweight_resample(dev_logits(case["target"]), dev_logits(case["draft"]),
                                   torch.from_numpy(case["tokens"]).to(DEV), torch.from_numpy(case["bonus_u"]).to(DEV),
                                   torch.from_numpy(case["resample_u"]).to(DEV), lw, case["T"], ess_frac, case["P"],
-                                  case["N"], case["K"], page_table_in=ptd)
+                                  case["N"], case["K"], page_table_in=ptd, beta=case.get("beta"))
     torch.cuda.synchronize()
     return dict(bonus=out["bonus_token"].cpu().numpy(), ancestors=out["ancestors"].cpu().numpy(),
                 ess=out["ess"].cpu().numpy(), resampled=out["resampled"].cpu().numpy(), logw=lw.cpu().numpy(),
@@ -93,7 +93,8 @@ def check_smc_steps(case, steps=1, ess_frac=0.5, label="", new_inputs=None):
             case = new_inputs(s, case)
         g = run_smc_gpu(case, logw, pt, ess_frac)
         ref = oracle.smc_step(case["target"], case["draft"], case["tokens"], case["bonus_u"], case["resample_u"],
-                              logw, case["T"], ess_frac, case["P"], case["N"], case["K"], pt_in=pt)
+                              logw, case["T"], ess_frac, case["P"], case["N"], case["K"], pt_in=pt,
+                              beta=case.get("beta"))
         t = compare_smc(case, ref, g, logw, pt, f"{label} step {s}")
         say(f"[smc {label} step {s}] {t.summary()} resampled={int(g['resampled'].sum())}/{case['P']} "
             f"flags gpu={g['flags']} oracle={ref['flags']}")

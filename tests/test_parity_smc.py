@@ -45,6 +45,32 @@ def test_smc_dominant_particle():
     check_smc_steps(c, steps=1, label="dominant particle")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta", [0.5, 2.0, 4.0])
+def test_smc_power_target(dtype, beta):
+    """Power-sampling target p^beta against the oracle: increments
+    beta log p - log q, bonus from softmax(beta z / T)."""
+    from gpu_util import check_smc_steps
+
+    for P, N, K, V, T, L in ((2, 16, 3, 3000, 1.0, 4), (1, 64, 2, 2049, 0.8, 3), (3, 5, 0, 700, 1.1, 2)):
+        c = smc_case(int(beta * 10) + P * 100 + K, P, N, K, V, T=T, dtype=dtype, L=L, logw_scale=1.0)
+        c["beta"] = beta
+        check_smc_steps(c, steps=1, label=f"power beta={beta} P={P} N={N} K={K} V={V}")
+        check_smc_steps(c, steps=1, ess_frac=2.0, label=f"power beta={beta} always resample")
+
+
+def test_smc_power_one_is_plain():
+    """beta = 1 through the power entry point gives the plain step's outputs bit for bit."""
+    from gpu_util import run_smc_gpu
+
+    for dtype in ("f32", "bf16"):
+        c = smc_case(91, 2, 32, 3, 5000, dtype=dtype, L=3, logw_scale=2.0)
+        a = run_smc_gpu(c, c["logw"], c["pt"])
+        b = run_smc_gpu(dict(c, beta=1.0), c["logw"], c["pt"])
+        for k in ("bonus", "ancestors", "ess", "resampled", "logw", "pt_out", "flags"):
+            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+
+
 def test_smc_zero_weights_flag():
     from gpu_util import run_smc_gpu
 
@@ -67,8 +93,9 @@ def test_smc_multi_step_lockstep():
     check_smc_steps(c, steps=6, label="6 steps", new_inputs=fresh)
 
 
-def _cfg_smc(idx, steps, prompts=None):
-    """Full-size config; the oracle checks `prompts` (all when None) in lockstep."""
+def _cfg_smc(idx, steps, prompts=None, beta=None):
+    """Full-size config; the oracle checks `prompts` (all when None) in lockstep
+    (with ``beta``, the power-sampling target)."""
     import torch
 
     import oracle
@@ -89,7 +116,7 @@ def _cfg_smc(idx, steps, prompts=None):
         lw_in = logw.cpu().numpy()
         pt_in = pt.cpu().numpy()
         out = s.smc_reweight_resample(st["target"], st["draft"], st["tokens"], st["bonus_u"], st["resample_u"], logw,
-                                      cfg.T, cfg.ess_frac, P, N, K, page_table_in=pt)
+                                      cfg.T, cfg.ess_frac, P, N, K, page_table_in=pt, beta=beta)
         torch.cuda.synchronize()
         g = {k: v.cpu().numpy() for k, v in out.items() if k != "log_weights"}
         g["logw"] = logw.cpu().numpy()
@@ -103,10 +130,10 @@ def _cfg_smc(idx, steps, prompts=None):
             rows_d = slice(p * N * K, (p + 1) * N * K)
             case = dict(target=host_logits(st["target"][rows_t]), draft=host_logits(st["draft"][rows_d]),
                         tokens=st["tokens"][rows_d].cpu().numpy(), bonus_u=st["bonus_u"][p * N:(p + 1) * N].cpu().numpy(),
-                        resample_u=st["resample_u"][p:p + 1].cpu().numpy(), P=1, N=N, K=K, T=cfg.T)
+                        resample_u=st["resample_u"][p:p + 1].cpu().numpy(), P=1, N=N, K=K, T=cfg.T, beta=beta)
             sl = slice(p * N, (p + 1) * N)
             ref = oracle.smc_step(case["target"], case["draft"], case["tokens"], case["bonus_u"], case["resample_u"],
-                                  lw_in[sl], cfg.T, cfg.ess_frac, 1, N, K, pt_in=pt_in[sl])
+                                  lw_in[sl], cfg.T, cfg.ess_frac, 1, N, K, pt_in=pt_in[sl], beta=beta)
             gp = dict(bonus=g["bonus_token"][sl], ancestors=g["ancestors"][sl], ess=g["ess"][p:p + 1],
                       resampled=g["resampled"][p:p + 1], logw=g["logw"][sl], pt_out=g["page_table_out"][sl])
             t = compare_smc(case, ref, gp, lw_in[sl], pt_in[sl], f"{cfg.name} step {step} prompt {p}")
@@ -124,6 +151,16 @@ def test_cfg2_full_size():
 
 def test_cfg3_full_size_sampled_prompts():
     _cfg_smc(3, range(1), prompts=[0, 1, 31])
+
+
+def test_cfg2_power_full_size():
+    _cfg_smc(2, range(2), beta=2.0)
+
+
+def test_cfg3_power_sampled_prompts():
+    """cfg3 shape (multi-tile segments: bonus rows with their own tile partials,
+    at their own scale) with the power target."""
+    _cfg_smc(3, range(1), prompts=[0, 17], beta=3.0)
 
 
 def test_smc_workspace_reuse():
