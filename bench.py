@@ -139,6 +139,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--max-batch-gb", type=float, default=24.0)
+    ap.add_argument("--beta", type=float, default=None,
+                    help="SMC workloads: power-sampling target p^beta (smc_reweight_resample_power)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many bytes (scales rocprofv3 byte counters)")
     ap.add_argument("--summarize", nargs="+", default=None,
@@ -152,8 +154,7 @@ def main():
         print(summarize(args.summarize, args.copy_calibration or None))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this library runs on one GPU; --gpus N>1 is not supported (per-GPU sharding "
-                                   "is described in DESIGN.md)"}))
+        print(json.dumps({"error": "this library runs on one GPU: --gpus N > 1 is not supported"}))
         sys.exit(2)
     import numpy as np
     import torch
@@ -195,7 +196,7 @@ def main():
                 call, o = smcsd.prepare_smc_reweight_resample(
                     bt["target"], bt["draft"], bt["tokens"], bt["bonus_u"], bt["resample_u"], logw, cfg.T,
                     cfg.ess_frac, P, N, K, page_table_in=pts[s % 2], page_table_out=pts[(s + 1) % 2],
-                    workspace=ws, stream=stream_handle,
+                    workspace=ws, stream=stream_handle, beta=args.beta,
                     **({} if outs is None else {k: outs[k] for k in ("bonus_token", "ancestors", "ess", "resampled",
                                                                     "status_flags")}))
                 outs = o
@@ -309,7 +310,8 @@ def main():
                     ub = bt["bonus_u"][p * N:(p + 1) * N].cpu().numpy()
                     ur = bt["resample_u"][p:p + 1].cpu().numpy()
                     t0 = time.perf_counter()
-                    oracle.smc_step(tg, dr, tk, ub, ur, np.zeros(N, np.float32), cfg.T, cfg.ess_frac, 1, N, K)
+                    oracle.smc_step(tg, dr, tk, ub, ur, np.zeros(N, np.float32), cfg.T, cfg.ess_frac, 1, N, K,
+                                    beta=args.beta)
                     t_cpu += time.perf_counter() - t0
                     done_pos += N * K
                     if t_cpu > args.cpu_seconds:
@@ -347,9 +349,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "P": cfg.P, "N": cfg.N, "K": cfg.K,
                    "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T, "launch": args.launch,
-                   "input_batches": nb, "status_flags": flags},
+                   "input_batches": nb, "status_flags": flags,
+                   **({} if args.beta is None else {"power_beta": args.beta})},
         "roofline": {"bound": "hbm", "kernel": "k_stream", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(cfg.name),
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles(cfg.name) if args.beta is None else None,
                      "algorithmic_bytes_per_launch": bytes_total / steps, "bytes_per_element": e,
                      "kernel_us": stream_ms * 1e3, "decision_kernel_us": tail_ms * 1e3,
                      "call_us": ms_per_step * 1e3},
