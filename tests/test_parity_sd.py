@@ -27,6 +27,19 @@ def test_sd_ragged(dtype):
     check_sd(sd_case(6, 3, 40, T=1.0, lengths=[0, 0, 0], dtype=dtype), "all-zero lengths")
 
 
+def test_sd_max_vocab_and_max_k():
+    """Rows of the largest vocabulary (524288 logits: 256 tiles, so the
+    statistics merge takes more than one batch of partials) and the largest
+    draft length (K = 128: 257 rows per sequence, several merge passes)."""
+    from gpu_util import check_sd
+
+    for dtype in ("bf16", "f32"):
+        check_sd(sd_case(4100, 2, 524288, T=1.0, K=2, delta=1.0, dtype=dtype), f"V=524288 {dtype}")
+        check_sd(sd_case(4101, 3, 524288, T=0.8, K=1, delta=0.0, dtype=dtype), f"V=524288 accept-all {dtype}")
+    check_sd(sd_case(4102, 2, 3000, T=1.0, K=128, delta=0.3, dtype="bf16"), "K=128")
+    check_sd(sd_case(4103, 1, 2048, T=1.0, K=128, delta=0.0, dtype="f32"), "K=128 accept-all")
+
+
 def test_sd_identical_rows_accept_all():
     """draft == target: every draft accepted, final token is the bonus draw."""
     from gpu_util import check_sd, run_sd_gpu

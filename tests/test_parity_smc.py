@@ -29,6 +29,18 @@ def test_smc_max_particles():
     check_smc_steps(c, steps=1, ess_frac=2.0, label="N=1024")
 
 
+def test_smc_max_vocab_and_max_k():
+    """SMC rows of 524288 logits (256 tiles: four batches of partials in the
+    256-thread merge) and K = 128 draft rows per particle."""
+    from gpu_util import check_smc_steps
+
+    for dtype in ("bf16", "f32"):
+        c = smc_case(4200, 1, 3, 2, 524288, dtype=dtype, L=2, logw_scale=1.0)
+        check_smc_steps(c, steps=1, ess_frac=2.0, label=f"V=524288 {dtype}")
+    c = smc_case(4201, 1, 2, 128, 1500, dtype="bf16", L=2, logw_scale=1.0)
+    check_smc_steps(c, steps=1, ess_frac=2.0, label="K=128")
+
+
 def test_smc_dominant_particle():
     """One particle holds all the weight (first, middle or last of its prompt):
     every slot descends from it, the other particles' slot ranges are empty."""
