@@ -55,6 +55,10 @@ def _declare(lib):
     lib.oracle_smc_step.restype = _I
     lib.oracle_smc_step_power.argtypes = [_I, _I, _I, _I, _I64, _D, _D, _D] + [_P] * 8 + [_I] + [_P] * 9
     lib.oracle_smc_step_power.restype = _I
+    lib.oracle_pages_append.argtypes = [_I, _I, _I, _I, _I64] + [_P] * 8
+    lib.oracle_pages_append.restype = _I
+    lib.oracle_pages_resample.argtypes = [_I, _I, _I, _I, _I64] + [_P] * 8
+    lib.oracle_pages_resample.restype = _I
     return lib
 
 
@@ -188,3 +192,41 @@ def smc_step(target, draft, tokens, bonus_u, resample_u, logw, T, ess_frac, P, N
         lib.oracle_smc_step_power(_dtype_code(target), P, N, K, V, T, float(beta), ess_frac, *tail)
     return dict(logw=lw, bonus=bonus, ancestors=anc, ess=ess, resampled=res, pt_out=pt_out, flags=int(fl[0]),
                 cum_weight=cw[:PN], bonus_margin=bm[:PN], ess_margin=em[:P], resample_margin=rm[:P])
+
+
+def pages_append(table, lens, ref, free_pages, free_count, S, A, lib=None):
+    """Paged-KV append of A tokens per particle (copy-on-write of shared tail
+    pages, new pages from the free stack).  Inputs are not modified; returns
+    dict(status, table, len, ref, free_pages, free_count, slots, cow)."""
+    lib = lib or load()
+    table = np.array(table, np.int32, copy=True)
+    R, L = table.shape
+    lens = np.array(lens, np.int32, copy=True)
+    ref = np.array(ref, np.int32, copy=True)
+    free_pages = np.array(free_pages, np.int32, copy=True)
+    fc = np.array([free_count], np.int32)
+    slots = np.zeros(max(R * A, 1), np.int32)
+    cow = np.zeros(max(3 * R, 3), np.int32)
+    nc = np.zeros(1, np.int32)
+    st = lib.oracle_pages_append(R, L, S, A, ref.size, _ptr(table), _ptr(lens), _ptr(ref), _ptr(free_pages),
+                                 _ptr(fc), _ptr(slots), _ptr(cow), _ptr(nc))
+    return dict(status=int(st), table=table, len=lens, ref=ref, free_pages=free_pages, free_count=int(fc[0]),
+                slots=slots[:R * A].reshape(R, A), cow=cow[:3 * int(nc[0])].reshape(-1, 3))
+
+
+def pages_resample(P, N, ancestors, table_old, table_new, lens, ref, free_pages, free_count, S, lib=None):
+    """Paged-KV bookkeeping of a resampling: lengths by ancestor, reference
+    counts, freed pages pushed.  Returns dict(len, ref, free_pages, free_count)."""
+    lib = lib or load()
+    table_old = np.ascontiguousarray(table_old, np.int32)
+    table_new = np.ascontiguousarray(table_new, np.int32)
+    L = table_old.shape[1]
+    anc = np.ascontiguousarray(ancestors, np.int32)
+    lens = np.ascontiguousarray(lens, np.int32)
+    len_out = np.zeros_like(lens)
+    ref = np.array(ref, np.int32, copy=True)
+    free_pages = np.array(free_pages, np.int32, copy=True)
+    fc = np.array([free_count], np.int32)
+    lib.oracle_pages_resample(P, N, L, S, ref.size, _ptr(anc), _ptr(table_old), _ptr(table_new), _ptr(lens),
+                              _ptr(len_out), _ptr(ref), _ptr(free_pages), _ptr(fc))
+    return dict(len=len_out, ref=ref, free_pages=free_pages, free_count=int(fc[0]))

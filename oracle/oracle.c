@@ -403,3 +403,139 @@ int oracle_smc_step(int dtype, int P, int N, int K, int64_t V, double T, double 
                                resample_u, logw, pt_in, pt_out, L, bonus, ancestors, ess, resampled,
                                flags, cum_weight, bonus_margin, ess_margin, resample_margin);
 }
+
+/* ---------------------------------------------------------------------------
+ * Paged-KV bookkeeping around SMC resampling ([SMC] sec. 3: resampling is a
+ * pointer / metadata update of a page-based KV cache, no data movement; sec. 2:
+ * every step adds exactly K+1 tokens per particle).  The pages give no data
+ * structure; the reading fixed here:
+ *   - a pool of M pages of S token slots; particle r (r = p*N + n) has a
+ *     page-table row of L entries and a length len[r]; its first
+ *     ceil(len[r] / S) entries are page ids, the others -1;
+ *   - ref[page] = number of page-table entries (of used positions) naming it;
+ *     a page with ref 0 is free, and the free pages are a stack
+ *     free_pages[0 .. free_count-1] (top = free_count-1);
+ *   - a partially filled page is named only as the last used entry (the tail)
+ *     of rows of equal length (what resampling produces); a state that breaks
+ *     this is rejected.
+ * Append (A = K+1 new tokens per particle), particles in index order:
+ *   if the tail page is partially filled and ref > 1, copy on write: pop a page,
+ *   list the copy (source page, destination page, tokens to copy = len % S),
+ *   ref[source] -= 1, ref[new] = 1, and the row names the new page; then pop one
+ *   page (ref 1) per further position the A tokens reach; slot t of particle r
+ *   is page * S + offset of position len + t; len += A.  Pops take the top of
+ *   the stack.  If some row would exceed L pages, or the pops exceed the free
+ *   pages, nothing changes (status 1 or 2).
+ * Resample (ancestors a_k of each prompt, new rows already gathered):
+ *   len_out[k] = len_in[a_k]; every entry of a new row adds 1 to its page's ref,
+ *   every entry of an old row subtracts 1; the pages whose ref reaches 0 are
+ *   pushed in the order of their first entry in the old rows (row, then
+ *   position).
+ * ------------------------------------------------------------------------- */
+static int64_t used_pages(int32_t len, int S) { return ((int64_t)len + S - 1) / S; }
+
+/* Returns 0, or 1 (a row would exceed L pages), 2 (not enough free pages),
+ * 3 (the state breaks the sharing rule); on a non-zero return nothing changes. */
+int oracle_pages_append(int R, int L, int S, int A, int64_t M, int32_t* table, int32_t* len,
+                        int32_t* ref, int32_t* free_pages, int32_t* free_count, int32_t* slots,
+                        int32_t* cow, int32_t* n_cow) {
+  /* check the sharing rule: a partially filled page is only ever a tail, and
+   * its ref equals the number of rows whose tail it is */
+  int32_t* tails = (int32_t*)calloc((size_t)(M > 0 ? M : 1), sizeof(int32_t));
+  int bad = 0;
+  for (int r = 0; r < R; r++) {
+    if (len[r] % S) tails[table[(int64_t)r * L + used_pages(len[r], S) - 1]]++;
+  }
+  for (int r = 0; r < R && !bad; r++) {
+    int64_t u = used_pages(len[r], S);
+    for (int64_t j = 0; j < u; j++) {
+      int32_t pg = table[(int64_t)r * L + j];
+      if (pg < 0 || pg >= M) bad = 1;
+      else if (tails[pg] && (j != u - 1 || len[r] % S == 0)) bad = 1;
+      else if (tails[pg] && tails[pg] != ref[pg]) bad = 1;
+    }
+  }
+  free(tails);
+  if (bad) return 3;
+  /* dry run on a copy of the ref counts: capacity and pages needed */
+  int32_t* rc = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1));
+  memcpy(rc, ref, sizeof(int32_t) * (size_t)M);
+  int64_t need = 0;
+  for (int r = 0; r < R; r++) {
+    int64_t u0 = used_pages(len[r], S), u1 = used_pages(len[r] + A, S);
+    if (u1 > L) {
+      free(rc);
+      return 1;
+    }
+    if (len[r] % S) {
+      int32_t tail = table[(int64_t)r * L + u0 - 1];
+      if (rc[tail] > 1) {
+        rc[tail]--;
+        need++;
+      }
+    }
+    need += u1 - u0;
+  }
+  free(rc);
+  if (need > *free_count) return 2;
+  /* apply */
+  int32_t top = *free_count, nc = 0;
+  for (int r = 0; r < R; r++) {
+    int32_t* row = table + (int64_t)r * L;
+    int64_t u0 = used_pages(len[r], S), u1 = used_pages(len[r] + A, S);
+    if (len[r] % S) {
+      int32_t tail = row[u0 - 1];
+      if (ref[tail] > 1) {
+        int32_t q = free_pages[--top];
+        cow[3 * nc] = tail;
+        cow[3 * nc + 1] = q;
+        cow[3 * nc + 2] = len[r] % S;
+        nc++;
+        ref[tail]--;
+        ref[q] = 1;
+        row[u0 - 1] = q;
+      }
+    }
+    for (int64_t j = u0; j < u1; j++) {
+      int32_t q = free_pages[--top];
+      ref[q] = 1;
+      row[j] = q;
+    }
+    for (int t = 0; t < A; t++) {
+      int64_t pos = (int64_t)len[r] + t;
+      slots[(int64_t)r * A + t] = row[pos / S] * S + (int32_t)(pos % S);
+    }
+    len[r] += A;
+  }
+  *free_count = top;
+  *n_cow = nc;
+  return 0;
+}
+
+/* ancestors: local indices per prompt (P prompts of N).  table_old / len_in:
+ * the rows before resampling; table_new: the gathered rows.  Returns 0. */
+int oracle_pages_resample(int P, int N, int L, int S, int64_t M, const int32_t* ancestors,
+                          const int32_t* table_old, const int32_t* table_new,
+                          const int32_t* len_in, int32_t* len_out, int32_t* ref,
+                          int32_t* free_pages, int32_t* free_count) {
+  int64_t R = (int64_t)P * N;
+  for (int64_t k = 0; k < R; k++) len_out[k] = len_in[(k / N) * N + ancestors[k]];
+  for (int64_t k = 0; k < R; k++) {
+    for (int64_t j = 0; j < used_pages(len_out[k], S); j++) ref[table_new[k * L + j]]++;
+    for (int64_t j = 0; j < used_pages(len_in[k], S); j++) ref[table_old[k * L + j]]--;
+  }
+  unsigned char* pushed = (unsigned char*)calloc((size_t)(M > 0 ? M : 1), 1);
+  int32_t top = *free_count;
+  for (int64_t k = 0; k < R; k++) {
+    for (int64_t j = 0; j < used_pages(len_in[k], S); j++) {
+      int32_t pg = table_old[k * L + j];
+      if (ref[pg] == 0 && !pushed[pg]) {
+        pushed[pg] = 1;
+        free_pages[top++] = pg;
+      }
+    }
+  }
+  free(pushed);
+  *free_count = top;
+  return 0;
+}

@@ -70,3 +70,39 @@ def smc_case(seed, P, N, K, V, T=1.0, delta=1.0, dtype="f32", scale=3.0, L=4, lo
                 resample_u=rng.random(P).astype(np.float32),
                 logw=(logw_scale * rng.standard_normal(PN)).astype(np.float32),
                 pt=np.arange(PN * L, dtype=np.int32).reshape(PN, L), P=P, N=N, K=K, T=T, dtype=dtype)
+
+
+def pages_state(seed, P, N, L, S, M, max_len=None):
+    """A paged-KV state to start from: every particle owns distinct pages for a
+    random length (at most max_len tokens, default half the row), reference
+    count 1 on them, every other page on the free stack (shuffled).  Returns
+    dict(table [P*N, L] with -1 past the used entries, len, ref [M],
+    free_pages [M], free_count)."""
+    rng = np.random.default_rng(seed)
+    R = P * N
+    max_len = L * S // 2 if max_len is None else max_len
+    lens = rng.integers(0, max_len + 1, R).astype(np.int32)
+    perm = rng.permutation(M).astype(np.int32)
+    table = np.full((R, L), -1, np.int32)
+    ref = np.zeros(M, np.int32)
+    nxt = 0
+    for r in range(R):
+        u = (int(lens[r]) + S - 1) // S
+        table[r, :u] = perm[nxt:nxt + u]
+        ref[perm[nxt:nxt + u]] = 1
+        nxt += u
+    assert nxt <= M, "pool too small for the lengths drawn"
+    free = np.zeros(M, np.int32)
+    free[:M - nxt] = perm[nxt:]
+    return dict(table=table, len=lens, ref=ref, free_pages=free, free_count=M - nxt)
+
+
+def sorted_ancestors(seed, P, N, concentrate=0.0):
+    """Ancestor indices per prompt, ascending (as systematic resampling gives),
+    drawn with replacement; concentrate in [0, 1) favours low indices."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(P):
+        w = (1.0 - concentrate) ** np.arange(N) if concentrate else np.ones(N)
+        out.append(np.sort(rng.choice(N, N, p=w / w.sum())))
+    return np.concatenate(out).astype(np.int32)

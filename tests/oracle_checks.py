@@ -543,6 +543,91 @@ def check_power_one_is_plain(lib):
         assert (a[k] == b[k]).all(), k
 
 
+def _pages_invariants(table, lens, ref, free, fc, S, M):
+    """Reference counts equal the entries naming each page; the free stack holds
+    exactly the pages nobody names, once each."""
+    count = np.zeros(M, np.int64)
+    for r in range(table.shape[0]):
+        u = (int(lens[r]) + S - 1) // S
+        assert u <= table.shape[1]
+        assert (table[r, :u] >= 0).all() and (table[r, :u] < M).all(), r
+        np.add.at(count, table[r, :u], 1)
+    assert (count == ref).all(), np.nonzero(count != ref)[0][:8]
+    stack = free[:fc]
+    assert len(set(stack.tolist())) == fc, "a page is on the free stack twice"
+    assert set(stack.tolist()) == set(np.nonzero(count == 0)[0].tolist()), "leaked or live page on the free stack"
+
+
+def _read_kv(phys, table, lens, S):
+    return [[int(phys[table[r, t // S], t % S]) for t in range(int(lens[r]))] for r in range(table.shape[0])]
+
+
+def check_pages_content_model(lib):
+    """The bookkeeping against what it is for: a physical page pool that the
+    copy list and the new-token slots are applied to must read back, through
+    each particle's row, exactly the particle's logical token sequence, over
+    appends and resamplings (with heavy duplication); reference counts and
+    the free stack stay exact."""
+    from synth.small import pages_state, sorted_ancestors
+
+    P, N, L, S, M, A = 2, 6, 14, 4, 160, 3
+    st = pages_state(61, P, N, L, S, M, max_len=9)
+    rng = np.random.default_rng(62)
+    R = P * N
+    table, lens, ref, free, fc = st["table"], st["len"], st["ref"], st["free_pages"], st["free_count"]
+    phys = np.full((M, S), -1, np.int64)
+    logical = []
+    for r in range(R):
+        seq = rng.integers(0, 1000, int(lens[r])).tolist()
+        for t, v in enumerate(seq):
+            phys[table[r, t // S], t % S] = v
+        logical.append(seq)
+    n_cow = 0
+    for step in range(6):
+        out = oracle.pages_append(table, lens, ref, free, fc, S, A, lib=lib)
+        assert out["status"] == 0, out["status"]
+        for src, dst, n in out["cow"]:
+            phys[dst, :n] = phys[src, :n]
+        n_cow += len(out["cow"])
+        new = rng.integers(1000, 2000, (R, A))
+        for r in range(R):
+            for t in range(A):
+                sl = int(out["slots"][r, t])
+                phys[sl // S, sl % S] = new[r, t]
+            logical[r] = logical[r] + new[r].tolist()
+        table, lens, ref, free, fc = out["table"], out["len"], out["ref"], out["free_pages"], out["free_count"]
+        _pages_invariants(table, lens, ref, free, fc, S, M)
+        assert _read_kv(phys, table, lens, S) == logical, f"append {step}"
+        anc = sorted_ancestors(70 + step, P, N, concentrate=0.5)
+        src = (np.arange(R) // N) * N + anc
+        table_new = table[src].copy()
+        res = oracle.pages_resample(P, N, anc, table, table_new, lens, ref, free, fc, S, lib=lib)
+        logical = [list(logical[k]) for k in src]
+        table, lens, ref, free, fc = table_new, res["len"], res["ref"], res["free_pages"], res["free_count"]
+        _pages_invariants(table, lens, ref, free, fc, S, M)
+        assert _read_kv(phys, table, lens, S) == logical, f"resample {step}"
+    assert n_cow > 0, "the scenario never shared a partially filled page"
+
+
+def check_pages_errors(lib):
+    """Capacity, an exhausted pool and a broken sharing rule leave the state
+    unchanged with their status."""
+    from synth.small import pages_state
+
+    st = pages_state(63, 1, 4, 4, 4, 40, max_len=10)
+    args = (st["table"], st["len"], st["ref"], st["free_pages"], st["free_count"])
+    full = oracle.pages_append(*args, 4, 7, lib=lib)   # 10 + 7 tokens > 4 pages of 4
+    assert full["status"] == 1 and (full["table"] == st["table"]).all() and (full["len"] == st["len"]).all()
+    dry = oracle.pages_append(st["table"], st["len"], st["ref"], st["free_pages"], 1, 4, 5, lib=lib)
+    assert dry["status"] == 2 and (dry["ref"] == st["ref"]).all() and dry["free_count"] == 1
+    bad_ref = st["ref"].copy()
+    r0 = int(np.argmax(st["len"] % 4 != 0))
+    tail = st["table"][r0, (int(st["len"][r0]) + 3) // 4 - 1]
+    bad_ref[tail] = 2  # a partially filled page counted twice, named once
+    bad = oracle.pages_append(st["table"], st["len"], bad_ref, st["free_pages"], st["free_count"], 4, 2, lib=lib)
+    assert bad["status"] == 3 and (bad["table"] == st["table"]).all()
+
+
 DETERMINISTIC_CHECKS = [
     check_golden_sd_fixed,
     check_golden_sd_csr,
@@ -568,4 +653,6 @@ DETERMINISTIC_CHECKS = [
     check_power_bonus_law,
     check_power_increment,
     check_power_one_is_plain,
+    check_pages_content_model,
+    check_pages_errors,
 ]
