@@ -216,7 +216,7 @@ def pages_append(table, lens, ref, free_pages, free_count, S, A, lib=None):
 
 def pages_resample(P, N, ancestors, table_old, table_new, lens, ref, free_pages, free_count, S, lib=None):
     """Paged-KV bookkeeping of a resampling: lengths by ancestor, reference
-    counts, freed pages pushed.  Returns dict(len, ref, free_pages, free_count)."""
+    counts, freed pages pushed.  Returns dict(status, len, ref, free_pages, free_count)."""
     lib = lib or load()
     table_old = np.ascontiguousarray(table_old, np.int32)
     table_new = np.ascontiguousarray(table_new, np.int32)
@@ -227,6 +227,6 @@ def pages_resample(P, N, ancestors, table_old, table_new, lens, ref, free_pages,
     ref = np.array(ref, np.int32, copy=True)
     free_pages = np.array(free_pages, np.int32, copy=True)
     fc = np.array([free_count], np.int32)
-    lib.oracle_pages_resample(P, N, L, S, ref.size, _ptr(anc), _ptr(table_old), _ptr(table_new), _ptr(lens),
-                              _ptr(len_out), _ptr(ref), _ptr(free_pages), _ptr(fc))
-    return dict(len=len_out, ref=ref, free_pages=free_pages, free_count=int(fc[0]))
+    st = lib.oracle_pages_resample(P, N, L, S, ref.size, _ptr(anc), _ptr(table_old), _ptr(table_new), _ptr(lens),
+                                   _ptr(len_out), _ptr(ref), _ptr(free_pages), _ptr(fc))
+    return dict(status=int(st), len=len_out, ref=ref, free_pages=free_pages, free_count=int(fc[0]))

@@ -415,9 +415,10 @@ int oracle_smc_step(int dtype, int P, int N, int K, int64_t V, double T, double 
  *   - ref[page] = number of page-table entries (of used positions) naming it;
  *     a page with ref 0 is free, and the free pages are a stack
  *     free_pages[0 .. free_count-1] (top = free_count-1);
- *   - a partially filled page is named only as the last used entry (the tail)
- *     of rows of equal length (what resampling produces); a state that breaks
- *     this is rejected.
+ *   - the reference counts equal the entries naming each page (assumed, not
+ *     checked), and a partially filled page is named only as the last used
+ *     entry (the tail) of rows (what resampling produces): its count must equal
+ *     the number of rows whose tail it is, else the state is rejected.
  * Append (A = K+1 new tokens per particle), particles in index order:
  *   if the tail page is partially filled and ref > 1, copy on write: pop a page,
  *   list the copy (source page, destination page, tokens to copy = len % S),
@@ -439,20 +440,22 @@ static int64_t used_pages(int32_t len, int S) { return ((int64_t)len + S - 1) / 
 int oracle_pages_append(int R, int L, int S, int A, int64_t M, int32_t* table, int32_t* len,
                         int32_t* ref, int32_t* free_pages, int32_t* free_count, int32_t* slots,
                         int32_t* cow, int32_t* n_cow) {
-  /* check the sharing rule: a partially filled page is only ever a tail, and
-   * its ref equals the number of rows whose tail it is */
+  /* check the sharing rule: the count of a partially filled tail page equals
+   * the number of rows whose tail it is (tail ids must be pages of the pool) */
   int32_t* tails = (int32_t*)calloc((size_t)(M > 0 ? M : 1), sizeof(int32_t));
   int bad = 0;
   for (int r = 0; r < R; r++) {
-    if (len[r] % S) tails[table[(int64_t)r * L + used_pages(len[r], S) - 1]]++;
+    if (len[r] < 0 || used_pages(len[r], S) > L) bad = 1;
+    else if (len[r] % S) {
+      int32_t pg = table[(int64_t)r * L + used_pages(len[r], S) - 1];
+      if (pg < 0 || pg >= M) bad = 1;
+      else tails[pg]++;
+    }
   }
   for (int r = 0; r < R && !bad; r++) {
-    int64_t u = used_pages(len[r], S);
-    for (int64_t j = 0; j < u; j++) {
-      int32_t pg = table[(int64_t)r * L + j];
-      if (pg < 0 || pg >= M) bad = 1;
-      else if (tails[pg] && (j != u - 1 || len[r] % S == 0)) bad = 1;
-      else if (tails[pg] && tails[pg] != ref[pg]) bad = 1;
+    if (len[r] % S) {
+      int32_t pg = table[(int64_t)r * L + used_pages(len[r], S) - 1];
+      if (tails[pg] != ref[pg]) bad = 1;
     }
   }
   free(tails);
@@ -513,12 +516,25 @@ int oracle_pages_append(int R, int L, int S, int A, int64_t M, int32_t* table, i
 }
 
 /* ancestors: local indices per prompt (P prompts of N).  table_old / len_in:
- * the rows before resampling; table_new: the gathered rows.  Returns 0. */
+ * the rows before resampling; table_new: the gathered rows.  Returns 0, or 3
+ * (an ancestor outside 0..N-1, a length outside 0..L*S or a page id outside
+ * the pool), changing nothing. */
 int oracle_pages_resample(int P, int N, int L, int S, int64_t M, const int32_t* ancestors,
                           const int32_t* table_old, const int32_t* table_new,
                           const int32_t* len_in, int32_t* len_out, int32_t* ref,
                           int32_t* free_pages, int32_t* free_count) {
   int64_t R = (int64_t)P * N;
+  for (int64_t k = 0; k < R; k++) {
+    if (ancestors[k] < 0 || ancestors[k] >= N) return 3;
+    if (len_in[k] < 0 || used_pages(len_in[k], S) > L) return 3;
+  }
+  for (int64_t k = 0; k < R; k++) {
+    int32_t ln = len_in[(k / N) * N + ancestors[k]];
+    for (int64_t j = 0; j < used_pages(ln, S); j++)
+      if (table_new[k * L + j] < 0 || table_new[k * L + j] >= M) return 3;
+    for (int64_t j = 0; j < used_pages(len_in[k], S); j++)
+      if (table_old[k * L + j] < 0 || table_old[k * L + j] >= M) return 3;
+  }
   for (int64_t k = 0; k < R; k++) len_out[k] = len_in[(k / N) * N + ancestors[k]];
   for (int64_t k = 0; k < R; k++) {
     for (int64_t j = 0; j < used_pages(len_out[k], S); j++) ref[table_new[k * L + j]]++;

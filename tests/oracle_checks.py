@@ -602,6 +602,7 @@ def check_pages_content_model(lib):
         src = (np.arange(R) // N) * N + anc
         table_new = table[src].copy()
         res = oracle.pages_resample(P, N, anc, table, table_new, lens, ref, free, fc, S, lib=lib)
+        assert res["status"] == 0
         logical = [list(logical[k]) for k in src]
         table, lens, ref, free, fc = table_new, res["len"], res["ref"], res["free_pages"], res["free_count"]
         _pages_invariants(table, lens, ref, free, fc, S, M)
@@ -626,6 +627,10 @@ def check_pages_errors(lib):
     bad_ref[tail] = 2  # a partially filled page counted twice, named once
     bad = oracle.pages_append(st["table"], st["len"], bad_ref, st["free_pages"], st["free_count"], 4, 2, lib=lib)
     assert bad["status"] == 3 and (bad["table"] == st["table"]).all()
+    anc = np.array([0, 1, 4, 3], np.int32)  # 4 is outside the prompt's 0..3
+    res = oracle.pages_resample(1, 4, anc, st["table"], st["table"], st["len"], st["ref"], st["free_pages"],
+                                st["free_count"], 4, lib=lib)
+    assert res["status"] == 3 and (res["ref"] == st["ref"]).all() and res["free_count"] == st["free_count"]
 
 
 DETERMINISTIC_CHECKS = [
