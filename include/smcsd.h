@@ -102,9 +102,14 @@ enum {
                                    resampling, ess = 0                                 */
   SMCSD_FLAG_CDF_CLAMP = 8,     /* rounding left no prefix above u * total; the last
                                    index with positive weight was taken               */
-  SMCSD_FLAG_BAD_INPUT = 16     /* a draft token outside [0, V) (that position is
+  SMCSD_FLAG_BAD_INPUT = 16,    /* a draft token outside [0, V) (that position is
                                    rejected) or malformed CSR offsets (the outputs of
-                                   the sequences they describe are unspecified)       */
+                                   the sequences they describe are unspecified); for
+                                   the page bookkeeping, a state it rejects           */
+  SMCSD_FLAG_PAGES_FULL = 32,   /* smc_pages_append: a row would exceed its L pages;
+                                   nothing changed                                    */
+  SMCSD_FLAG_PAGES_EXHAUSTED = 64 /* smc_pages_append: fewer free pages than the step
+                                   needs; nothing changed                             */
 };
 
 #define SMCSD_ABI_VERSION 1
@@ -256,6 +261,73 @@ int32_t smc_reweight_resample_power(int32_t dtype, int32_t P, int32_t N, int32_t
                                     int32_t* ancestors, float* ess, int32_t* resampled,
                                     uint32_t* status_flags, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * Paged-KV bookkeeping around SMC resampling: the metadata update that makes
+ * resampling a pointer operation on a page-based KV cache ("Faster LLM
+ * Inference via Sequential Monte Carlo", sec. 3), with the K+1 tokens every
+ * step adds per particle (sec. 2).  All arrays are device memory owned by the
+ * caller; calls on one stream run in order.
+ *
+ * State.  A pool of num_pages (M) pages of page_size (S) token slots.
+ *   page_table   int32 [P*N, L]: particle r = p*N + n; its first
+ *                ceil(seq_len[r] / S) entries are page ids in [0, M).
+ *   seq_len      int32 [P*N]: tokens per particle, 0 <= len <= L*S.
+ *   ref_count    int32 [M]: entries naming each page; it must equal the table
+ *                (not checked).  A partially filled page is named only as the
+ *                last used entry (tail) of rows, so its count is the number of
+ *                rows whose tail it is (checked by smc_pages_append).
+ *   free_pages   int32 [M], free_count int32 [1]: the pages with count 0, a
+ *                stack whose top is free_pages[free_count - 1].
+ * Both calls need a workspace of smc_pages_workspace_bytes(P, N, L, M),
+ * SMCSD_WORKSPACE_ALIGN aligned, zero-filled before its first use; every call
+ * leaves it as it found it, so one workspace serves every call of those sizes.
+ * Requirements: N >= 1, L >= 1, S >= 1, M >= 1, (P*N)*L and L*S and M below
+ * 2^31; otherwise SMCSD_ERR_INVALID_ARG.
+ */
+size_t smc_pages_workspace_bytes(int32_t P, int32_t N, int32_t L, int64_t num_pages);
+
+/*
+ * Adds new_tokens (A = K+1) token slots to every particle, particles in index
+ * order: a partially filled tail page that other rows also name is copied on
+ * write (a fresh page from the top of the stack; the copy is listed; the row
+ * names the fresh page, the old page's count drops by one) unless this row is
+ * the last (highest index) of its sharers, which keeps it; then one fresh page
+ * per further position the A tokens reach (count 1).
+ *   slots        int32 [P*N, A] out: page * S + offset of each new token.
+ *   cow_list     int32 [P*N, 3] out: (source page, destination page, tokens to
+ *                copy = old len % S) per copy, in particle order; *cow_count
+ *                (int32 [1]) out: their number.  The caller copies the KV data.
+ * page_table, seq_len (len += A), ref_count and free_count are updated in
+ * place; free_pages is only read.  A row that would exceed L pages
+ * (SMCSD_FLAG_PAGES_FULL), too few free pages (SMCSD_FLAG_PAGES_EXHAUSTED) or a
+ * rejected state (SMCSD_FLAG_BAD_INPUT) change nothing.
+ */
+int32_t smc_pages_append(int32_t P, int32_t N, int32_t L, int32_t page_size, int32_t new_tokens,
+                         int64_t num_pages, int32_t* page_table, int32_t* seq_len, int32_t* ref_count,
+                         const int32_t* free_pages, int32_t* free_count, int32_t* slots, int32_t* cow_list,
+                         int32_t* cow_count, uint32_t* status_flags, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * The bookkeeping of a resampling step, after smc_reweight_resample.
+ *   ancestors       int32 [P*N]: local ancestor (0..N-1) of each slot.
+ *   page_table_old  the rows before resampling (page_table_in of the step).
+ *   page_table_new  the gathered rows (its page_table_out).
+ *   seq_len_in      lengths before; seq_len_out (out, must not overlap it):
+ *                   seq_len_out[r] = seq_len_in[p*N + ancestors[r]].
+ * Every entry of a new row counts its page once more and every entry of an old
+ * row once less (only where the two rows differ); the pages that reach zero
+ * are pushed on the free stack in the order of their first entry in the old
+ * rows (row, then position).  ref_count, free_pages and free_count are updated
+ * in place.  An ancestor, length or page id out of range raises
+ * SMCSD_FLAG_BAD_INPUT (the state is then unspecified).
+ */
+int32_t smc_pages_resample(int32_t P, int32_t N, int32_t L, int32_t page_size, int64_t num_pages,
+                           const int32_t* ancestors, const int32_t* page_table_old, const int32_t* page_table_new,
+                           const int32_t* seq_len_in, int32_t* seq_len_out, int32_t* ref_count, int32_t* free_pages,
+                           int32_t* free_count, uint32_t* status_flags, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 #ifdef __cplusplus
 }

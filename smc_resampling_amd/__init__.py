@@ -17,7 +17,8 @@ __all__ = [
     "sd_verify", "smc_reweight_resample", "sd_verify_workspace_bytes", "smc_workspace_bytes",
     "prepare_sd_verify", "prepare_smc_reweight_resample", "status_string", "abi_version", "lib", "SmcsdError",
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "FLAG_ZERO_WEIGHTS", "FLAG_CDF_CLAMP", "FLAG_BAD_INPUT",
-    "new_workspace", "time_next_call",
+    "FLAG_PAGES_FULL", "FLAG_PAGES_EXHAUSTED",
+    "new_workspace", "time_next_call", "smc_pages_workspace_bytes", "smc_pages_append", "smc_pages_resample",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +27,7 @@ LIB_PATH = os.path.join(HERE, "libsmcsd.so")
 SMCSD_OK, SMCSD_ERR_INVALID_ARG, SMCSD_ERR_UNSUPPORTED, SMCSD_ERR_WORKSPACE, SMCSD_ERR_HIP = range(5)
 SMCSD_F32, SMCSD_BF16 = 0, 1
 FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT = 1, 2, 4, 8, 16
+FLAG_PAGES_FULL, FLAG_PAGES_EXHAUSTED = 32, 64
 WORKSPACE_ALIGN = 256
 
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -41,6 +43,9 @@ _SIGNATURES = {
                                _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_reweight_resample_power": ([_I32, _I32, _I32, _I32, _I32, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
                                      _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "smc_pages_workspace_bytes": ([_I32, _I32, _I32, _I64], _SZ),
+    "smc_pages_append": ([_I32, _I32, _I32, _I32, _I32, _I64] + [_P] * 10 + [_SZ, _P], _I32),
+    "smc_pages_resample": ([_I32, _I32, _I32, _I32, _I64] + [_P] * 10 + [_SZ, _P], _I32),
 }
 
 
@@ -246,3 +251,53 @@ def smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_unifo
                                               resample_uniforms, log_weights, temperature, ess_frac, P, N, K, **kw)
     call()
     return out
+
+
+def smc_pages_workspace_bytes(P, N, L, num_pages) -> int:
+    return _lib.smc_pages_workspace_bytes(P, N, L, num_pages)
+
+
+def smc_pages_append(page_table, seq_len, ref_count, free_pages, free_count, P, N, page_size, new_tokens, *,
+                     workspace=None, status_flags=None, stream=None):
+    """Paged-KV append of ``new_tokens`` slots per particle (see
+    ``smc_pages_append`` in include/smcsd.h); page_table, seq_len, ref_count
+    and free_count (int32 [1]) are updated in place.  Returns dict(slots,
+    cow_list, cow_count, status_flags)."""
+    for t, n in ((page_table, "page_table"), (seq_len, "seq_len"), (ref_count, "ref_count"),
+                 (free_pages, "free_pages"), (free_count, "free_count")):
+        _need(t, torch.int32, n)
+    dev = page_table.device
+    R, L = P * N, page_table.shape[-1]
+    M = ref_count.numel()
+    slots = torch.empty((R, new_tokens), dtype=torch.int32, device=dev)
+    cow = torch.empty((max(R, 1), 3), dtype=torch.int32, device=dev)
+    cow_count = torch.zeros(1, dtype=torch.int32, device=dev)
+    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
+    _check(_lib.smc_pages_append(P, N, L, page_size, new_tokens, M, _ptr(page_table), _ptr(seq_len),
+                                 _ptr(ref_count), _ptr(free_pages), _ptr(free_count), _ptr(slots), _ptr(cow),
+                                 _ptr(cow_count), _ptr(status_flags), _ptr(ws), wsb,
+                                 stream if stream is not None else _stream(dev)))
+    return dict(slots=slots, cow_list=cow, cow_count=cow_count, status_flags=status_flags)
+
+
+def smc_pages_resample(ancestors, page_table_old, page_table_new, seq_len_in, ref_count, free_pages, free_count, P,
+                       N, page_size, *, seq_len_out=None, workspace=None, status_flags=None, stream=None):
+    """Paged-KV bookkeeping of a resampling (see ``smc_pages_resample`` in
+    include/smcsd.h); ref_count, free_pages and free_count are updated in
+    place.  Returns dict(seq_len_out, status_flags)."""
+    for t, n in ((ancestors, "ancestors"), (page_table_old, "page_table_old"), (page_table_new, "page_table_new"),
+                 (seq_len_in, "seq_len_in"), (ref_count, "ref_count"), (free_pages, "free_pages"),
+                 (free_count, "free_count"), (seq_len_out, "seq_len_out")):
+        _need(t, torch.int32, n)
+    dev = page_table_old.device
+    L = page_table_old.shape[-1]
+    M = ref_count.numel()
+    seq_len_out = seq_len_out if seq_len_out is not None else torch.empty_like(seq_len_in)
+    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
+    _check(_lib.smc_pages_resample(P, N, L, page_size, M, _ptr(ancestors), _ptr(page_table_old),
+                                   _ptr(page_table_new), _ptr(seq_len_in), _ptr(seq_len_out), _ptr(ref_count),
+                                   _ptr(free_pages), _ptr(free_count), _ptr(status_flags), _ptr(ws), wsb,
+                                   stream if stream is not None else _stream(dev)))
+    return dict(seq_len_out=seq_len_out, status_flags=status_flags)
