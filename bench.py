@@ -139,6 +139,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--max-batch-gb", type=float, default=24.0)
+    ap.add_argument("--with-pages", action="store_true",
+                    help="SMC workloads: each step also does the paged-KV bookkeeping (append K+1 tokens "
+                         "before, resample after), 16-token pages")
     ap.add_argument("--beta", type=float, default=None,
                     help="SMC workloads: power-sampling target p^beta (smc_reweight_resample_power)")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -165,6 +168,13 @@ def main():
     cfg = synth.CONFIGS[args.config]
     steps = args.steps if args.steps is not None else cfg.steps
     W = args.warmup
+    if args.with_pages:
+        if cfg.kind != "smc":
+            sys.exit("--with-pages applies to the SMC workloads")
+        # the page tables alternate between two buffers: even counts keep every
+        # pass on the buffer the previous one ended on
+        steps += steps % 2
+        W += W % 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     gen = synth.Generator(cfg, dev)
@@ -191,6 +201,24 @@ def main():
             pts[1] = torch.empty_like(pts[0])
             ws = smcsd.new_workspace(smcsd.smc_workspace_bytes(1, P, N, K, cfg.V), dev)
             outs = None
+            pg = None
+            if args.with_pages:
+                # every particle starts with the same length, on pages of its own, with room for all steps
+                from synth.small import pages_state
+
+                S, A, R = 16, K + 1, P * N
+                M = R * cfg.L + R
+                # room for the warm-up, the graph replay and the eager timing pass
+                st0 = pages_state(0, P, N, cfg.L, S, M, fixed_len=max(0, cfg.L * S - (W + 2 * steps + 1) * A - S))
+                i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+                pts = [i32(st0["table"]), torch.empty_like(i32(st0["table"]))]
+                pg = dict(S=S, A=A, lens=[i32(st0["len"]), i32(st0["len"])], ref=i32(st0["ref"]),
+                          free=i32(st0["free_pages"]), fc=i32([st0["free_count"]]),
+                          ws=smcsd.new_workspace(smcsd.smc_pages_workspace_bytes(P, N, cfg.L, M), dev),
+                          slots=torch.empty((R, A), dtype=torch.int32, device=dev),
+                          cow=torch.empty((R, 3), dtype=torch.int32, device=dev),
+                          ncow=torch.zeros(1, dtype=torch.int32, device=dev),
+                          flags=torch.zeros(1, dtype=torch.int32, device=dev))
             for s in range(steps + W):
                 bt = batches[s % nb]
                 call, o = smcsd.prepare_smc_reweight_resample(
@@ -200,7 +228,21 @@ def main():
                     **({} if outs is None else {k: outs[k] for k in ("bonus_token", "ancestors", "ess", "resampled",
                                                                     "status_flags")}))
                 outs = o
-                calls.append(call)
+                if pg is not None:
+                    def step(call=call, o=o, cur=s % 2, nxt=(s + 1) % 2):
+                        smcsd.smc_pages_append(pts[cur], pg["lens"][cur], pg["ref"], pg["free"], pg["fc"], P, N,
+                                               pg["S"], pg["A"], workspace=pg["ws"], status_flags=pg["flags"],
+                                               stream=stream_handle, slots=pg["slots"], cow_list=pg["cow"],
+                                               cow_count=pg["ncow"])
+                        call()
+                        smcsd.smc_pages_resample(o["ancestors"], pts[cur], pts[nxt], pg["lens"][cur], pg["ref"],
+                                                 pg["free"], pg["fc"], P, N, pg["S"], seq_len_out=pg["lens"][nxt],
+                                                 workspace=pg["ws"], status_flags=pg["flags"], stream=stream_handle)
+                    calls.append(step)
+                else:
+                    calls.append(call)
+            if pg is not None:
+                outs = dict(outs, page_flags=pg["flags"])
         else:
             rows_d = max(int(bt["total_draft_rows"]) for bt in batches)
             ws = smcsd.new_workspace(smcsd.sd_verify_workspace_bytes(1, cfg.B, cfg.K, cfg.V, rows_d), dev)
@@ -249,7 +291,7 @@ def main():
         ev1.record(run_stream)
         torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
-    flags = int(outs["status_flags"].item())
+    flags = int(outs["status_flags"].item()) | (int(outs["page_flags"].item()) if "page_flags" in outs else 0)
     ms_per_step = ms / steps
 
     # ---------------- timing: each kernel ----------------------------------------
@@ -350,7 +392,8 @@ def main():
         "config": {"workload": cfg.name, "kind": cfg.kind, "B": cfg.B, "P": cfg.P, "N": cfg.N, "K": cfg.K,
                    "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T, "launch": args.launch,
                    "input_batches": nb, "status_flags": flags,
-                   **({} if args.beta is None else {"power_beta": args.beta})},
+                   **({} if args.beta is None else {"power_beta": args.beta}),
+                   **({"paged_kv_bookkeeping": True, "page_size": 16} if args.with_pages else {})},
         "roofline": {"bound": "hbm", "kernel": "k_stream", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic_from_profiles(cfg.name) if args.beta is None else None,

@@ -258,7 +258,7 @@ def smc_pages_workspace_bytes(P, N, L, num_pages) -> int:
 
 
 def smc_pages_append(page_table, seq_len, ref_count, free_pages, free_count, P, N, page_size, new_tokens, *,
-                     workspace=None, status_flags=None, stream=None):
+                     workspace=None, status_flags=None, stream=None, slots=None, cow_list=None, cow_count=None):
     """Paged-KV append of ``new_tokens`` slots per particle (see
     ``smc_pages_append`` in include/smcsd.h); page_table, seq_len, ref_count
     and free_count (int32 [1]) are updated in place.  Returns dict(slots,
@@ -269,9 +269,11 @@ def smc_pages_append(page_table, seq_len, ref_count, free_pages, free_count, P, 
     dev = page_table.device
     R, L = P * N, page_table.shape[-1]
     M = ref_count.numel()
-    slots = torch.empty((R, new_tokens), dtype=torch.int32, device=dev)
-    cow = torch.empty((max(R, 1), 3), dtype=torch.int32, device=dev)
-    cow_count = torch.zeros(1, dtype=torch.int32, device=dev)
+    slots = slots if slots is not None else torch.empty((R, new_tokens), dtype=torch.int32, device=dev)
+    cow = cow_list if cow_list is not None else torch.empty((max(R, 1), 3), dtype=torch.int32, device=dev)
+    cow_count = cow_count if cow_count is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    for t, n in ((slots, "slots"), (cow, "cow_list"), (cow_count, "cow_count")):
+        _need(t, torch.int32, n)
     status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
     ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
     _check(_lib.smc_pages_append(P, N, L, page_size, new_tokens, M, _ptr(page_table), _ptr(seq_len),

@@ -72,16 +72,17 @@ def smc_case(seed, P, N, K, V, T=1.0, delta=1.0, dtype="f32", scale=3.0, L=4, lo
                 pt=np.arange(PN * L, dtype=np.int32).reshape(PN, L), P=P, N=N, K=K, T=T, dtype=dtype)
 
 
-def pages_state(seed, P, N, L, S, M, max_len=None):
+def pages_state(seed, P, N, L, S, M, max_len=None, fixed_len=None):
     """A paged-KV state to start from: every particle owns distinct pages for a
-    random length (at most max_len tokens, default half the row), reference
+    random length (at most max_len tokens, default half the row; or
+    fixed_len for all), reference
     count 1 on them, every other page on the free stack (shuffled).  Returns
     dict(table [P*N, L] with -1 past the used entries, len, ref [M],
     free_pages [M], free_count)."""
     rng = np.random.default_rng(seed)
     R = P * N
     max_len = L * S // 2 if max_len is None else max_len
-    lens = rng.integers(0, max_len + 1, R).astype(np.int32)
+    lens = rng.integers(0, max_len + 1, R).astype(np.int32) if fixed_len is None else np.full(R, fixed_len, np.int32)
     perm = rng.permutation(M).astype(np.int32)
     table = np.full((R, L), -1, np.int32)
     ref = np.zeros(M, np.int32)
