@@ -235,7 +235,7 @@ def main():
                                                stream=stream_handle, slots=pg["slots"], cow_list=pg["cow"],
                                                cow_count=pg["ncow"])
                         call()
-                        smcsd.smc_pages_resample(o["ancestors"], pts[cur], pts[nxt], pg["lens"][cur], pg["ref"],
+                        smcsd.smc_pages_resample(o["ancestors"], pts[cur], pg["lens"][cur], pg["ref"],
                                                  pg["free"], pg["fc"], P, N, pg["S"], seq_len_out=pg["lens"][nxt],
                                                  workspace=pg["ws"], status_flags=pg["flags"], stream=stream_handle)
                     calls.append(step)

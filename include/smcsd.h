@@ -281,7 +281,8 @@ int32_t smc_reweight_resample_power(int32_t dtype, int32_t P, int32_t N, int32_t
  *                stack whose top is free_pages[free_count - 1].
  * Both calls need a workspace of smc_pages_workspace_bytes(P, N, L, M),
  * SMCSD_WORKSPACE_ALIGN aligned, zero-filled before its first use; every call
- * leaves it as it found it, so one workspace serves every call of those sizes.
+ * leaves at zero what has to start there, so one workspace serves every call
+ * of those sizes (not two calls at once).
  * Requirements: N >= 1, L >= 1, S >= 1, M >= 1, (P*N)*L and L*S and M below
  * 2^31; otherwise SMCSD_ERR_INVALID_ARG.
  */
@@ -312,22 +313,25 @@ int32_t smc_pages_append(int32_t P, int32_t N, int32_t L, int32_t page_size, int
 /*
  * The bookkeeping of a resampling step, after smc_reweight_resample.
  *   ancestors       int32 [P*N]: local ancestor (0..N-1) of each slot.
- *   page_table_old  the rows before resampling (page_table_in of the step).
- *   page_table_new  the gathered rows (its page_table_out).
+ *   page_table_old  the rows before resampling (page_table_in of the step);
+ *                   the new rows are the ancestors' old rows (its
+ *                   page_table_out: row r = old row p*N + ancestors[r]), which
+ *                   is all the call assumes of them; it does not read them.
  *   seq_len_in      lengths before; seq_len_out (out, must not overlap it):
  *                   seq_len_out[r] = seq_len_in[p*N + ancestors[r]].
  * Every entry of a new row counts its page once more and every entry of an old
- * row once less (only where the two rows differ); the pages that reach zero
- * are pushed on the free stack in the order of their first entry in the old
- * rows (row, then position).  ref_count, free_pages and free_count are updated
- * in place.  An ancestor, length or page id out of range raises
+ * row once less, so a page's count changes by the sum of (copies - 1) over the
+ * old rows naming it, copies = the slots whose ancestor the row is; the pages
+ * that reach zero are pushed on the free stack in the order of their first
+ * entry in the old rows (row, then position).  ref_count, free_pages and
+ * free_count are updated in place.  An ancestor or length out of range, or a
+ * page id out of range in a row that is dropped or copied, raises
  * SMCSD_FLAG_BAD_INPUT (the state is then unspecified).
  */
 int32_t smc_pages_resample(int32_t P, int32_t N, int32_t L, int32_t page_size, int64_t num_pages,
-                           const int32_t* ancestors, const int32_t* page_table_old, const int32_t* page_table_new,
-                           const int32_t* seq_len_in, int32_t* seq_len_out, int32_t* ref_count, int32_t* free_pages,
-                           int32_t* free_count, uint32_t* status_flags, void* workspace, size_t workspace_bytes,
-                           void* stream);
+                           const int32_t* ancestors, const int32_t* page_table_old, const int32_t* seq_len_in,
+                           int32_t* seq_len_out, int32_t* ref_count, int32_t* free_pages, int32_t* free_count,
+                           uint32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

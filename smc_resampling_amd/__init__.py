@@ -45,7 +45,7 @@ _SIGNATURES = {
                                      _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_pages_workspace_bytes": ([_I32, _I32, _I32, _I64], _SZ),
     "smc_pages_append": ([_I32, _I32, _I32, _I32, _I32, _I64] + [_P] * 10 + [_SZ, _P], _I32),
-    "smc_pages_resample": ([_I32, _I32, _I32, _I32, _I64] + [_P] * 10 + [_SZ, _P], _I32),
+    "smc_pages_resample": ([_I32, _I32, _I32, _I32, _I64] + [_P] * 9 + [_SZ, _P], _I32),
 }
 
 
@@ -283,14 +283,14 @@ def smc_pages_append(page_table, seq_len, ref_count, free_pages, free_count, P, 
     return dict(slots=slots, cow_list=cow, cow_count=cow_count, status_flags=status_flags)
 
 
-def smc_pages_resample(ancestors, page_table_old, page_table_new, seq_len_in, ref_count, free_pages, free_count, P,
-                       N, page_size, *, seq_len_out=None, workspace=None, status_flags=None, stream=None):
+def smc_pages_resample(ancestors, page_table_old, seq_len_in, ref_count, free_pages, free_count, P, N, page_size, *,
+                       seq_len_out=None, workspace=None, status_flags=None, stream=None):
     """Paged-KV bookkeeping of a resampling (see ``smc_pages_resample`` in
     include/smcsd.h); ref_count, free_pages and free_count are updated in
     place.  Returns dict(seq_len_out, status_flags)."""
-    for t, n in ((ancestors, "ancestors"), (page_table_old, "page_table_old"), (page_table_new, "page_table_new"),
-                 (seq_len_in, "seq_len_in"), (ref_count, "ref_count"), (free_pages, "free_pages"),
-                 (free_count, "free_count"), (seq_len_out, "seq_len_out")):
+    for t, n in ((ancestors, "ancestors"), (page_table_old, "page_table_old"), (seq_len_in, "seq_len_in"),
+                 (ref_count, "ref_count"), (free_pages, "free_pages"), (free_count, "free_count"),
+                 (seq_len_out, "seq_len_out")):
         _need(t, torch.int32, n)
     dev = page_table_old.device
     L = page_table_old.shape[-1]
@@ -298,8 +298,8 @@ def smc_pages_resample(ancestors, page_table_old, page_table_new, seq_len_in, re
     seq_len_out = seq_len_out if seq_len_out is not None else torch.empty_like(seq_len_in)
     status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
     ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
-    _check(_lib.smc_pages_resample(P, N, L, page_size, M, _ptr(ancestors), _ptr(page_table_old),
-                                   _ptr(page_table_new), _ptr(seq_len_in), _ptr(seq_len_out), _ptr(ref_count),
-                                   _ptr(free_pages), _ptr(free_count), _ptr(status_flags), _ptr(ws), wsb,
+    _check(_lib.smc_pages_resample(P, N, L, page_size, M, _ptr(ancestors), _ptr(page_table_old), _ptr(seq_len_in),
+                                   _ptr(seq_len_out), _ptr(ref_count), _ptr(free_pages), _ptr(free_count),
+                                   _ptr(status_flags), _ptr(ws), wsb,
                                    stream if stream is not None else _stream(dev)))
     return dict(seq_len_out=seq_len_out, status_flags=status_flags)

@@ -17,7 +17,14 @@ def _host(t):
     return t.cpu().numpy()
 
 
-def _lockstep(P, N, L, S, M, A, steps, seed, max_len=None, concentrate=0.5):
+def _scratch_bytes(P, N, L, M):
+    """Bytes at the start of the workspace that every call leaves at zero: two
+    per-page arrays, then a row of entry marks per particle."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return 2 * al(4 * M) + al(4 * P * N * ((L + 31) // 32))
+
+
+def _lockstep(P, N, L, S, M, A, steps, seed, max_len=None, concentrate=0.5, shuffle=False, identity_every=0):
     import torch
 
     import oracle
@@ -34,7 +41,7 @@ def _lockstep(P, N, L, S, M, A, steps, seed, max_len=None, concentrate=0.5):
         o = oracle.pages_append(table, lens, ref, free, fc, S, A)
         g = s.smc_pages_append(g_table, g_len, g_ref, g_free, g_fc, P, N, S, A, workspace=ws)
         torch.cuda.synchronize()
-        assert o["status"] == 0 and int(g["status_flags"].item()) == 0, (o["status"], int(g["status_flags"].item()))
+        assert o["status"] == 0 and int(g["status_flags"].item()) == 0, (step, o["status"], int(g["status_flags"].item()))
         nc = int(g["cow_count"].item())
         assert nc == len(o["cow"]), (nc, len(o["cow"]))
         assert (_host(g["cow_list"])[:nc] == o["cow"]).all(), "copy list"
@@ -46,15 +53,20 @@ def _lockstep(P, N, L, S, M, A, steps, seed, max_len=None, concentrate=0.5):
         table, lens, ref = o["table"], o["len"], o["ref"]
         n_cow += nc
         anc = sorted_ancestors(seed * 100 + step, P, N, concentrate=concentrate)
+        if shuffle:  # copies no longer neighbours: runs of a shared page split
+            rng = np.random.default_rng(seed * 100 + step)
+            anc = np.concatenate([rng.permutation(anc[p * N:(p + 1) * N]) for p in range(P)]).astype(np.int32)
+        if identity_every and step % identity_every == 0:  # a step that did not resample
+            anc = np.tile(np.arange(N, dtype=np.int32), P)
         src = (np.arange(R) // N) * N + anc
         table_new = table[src].copy()
         o = oracle.pages_resample(P, N, anc, table, table_new, lens, ref, free, fc, S)
         g_new = _dev(table_new)
         g_out = torch.empty_like(g_len)
-        r = s.smc_pages_resample(_dev(anc), g_table, g_new, g_len, g_ref, g_free, g_fc, P, N, S, seq_len_out=g_out,
+        r = s.smc_pages_resample(_dev(anc), g_table, g_len, g_ref, g_free, g_fc, P, N, S, seq_len_out=g_out,
                                  workspace=ws)
         torch.cuda.synchronize()
-        assert o["status"] == 0 and int(r["status_flags"].item()) == 0
+        assert o["status"] == 0 and int(r["status_flags"].item()) == 0, (step, o["status"], int(r["status_flags"].item()))
         fc = o["free_count"]
         assert int(g_fc.item()) == fc, (int(g_fc.item()), fc)
         assert (_host(g_out) == o["len"]).all(), "lengths after resampling"
@@ -63,8 +75,7 @@ def _lockstep(P, N, L, S, M, A, steps, seed, max_len=None, concentrate=0.5):
         table, lens, ref, free = table_new, o["len"], o["ref"], o["free_pages"]
         g_table, g_len = g_new, g_out
     # the calls leave the scratch as they found it (the staging area aside)
-    l_scratch = 2 * ((4 * M + 255) // 256 * 256)
-    assert int(ws[:l_scratch].count_nonzero().item()) == 0, "page scratch not cleared"
+    assert int(ws[:_scratch_bytes(P, N, L, M)].count_nonzero().item()) == 0, "page scratch not cleared"
     say(f"[pages P={P} N={N} L={L} S={S} M={M} A={A}] {steps} steps, {n_cow} copies, free {fc}")
     return n_cow
 
@@ -80,8 +91,18 @@ def test_pages_odd_sizes():
 
 
 def test_pages_chunked_particles():
-    """More particles than the bookkeeping workgroup's threads (chunked scans)."""
+    """More particles than the append workgroup's threads (several particles
+    per thread), and more than it holds in registers at once (chunks)."""
     _lockstep(5, 300, 12, 8, 30000, 9, steps=3, seed=15, max_len=40, concentrate=0.3)
+    _lockstep(3, 3000, 6, 4, 3 * 3000 * 8, 3, steps=3, seed=18, max_len=10, concentrate=0.3)
+
+
+def test_pages_unsorted_ancestors():
+    """Ancestors in any order (copies of a row not adjacent) and steps that did
+    not resample (every row its own ancestor)."""
+    _lockstep(2, 6, 14, 4, 160, 3, steps=6, seed=19, max_len=9, shuffle=True)
+    _lockstep(4, 70, 20, 4, 4 * 70 * 25, 5, steps=6, seed=20, max_len=40, concentrate=0.6, shuffle=True,
+              identity_every=2)
 
 
 def test_pages_batched_smc_shape():
