@@ -59,6 +59,10 @@ def _declare(lib):
     lib.oracle_pages_append.restype = _I
     lib.oracle_pages_resample.argtypes = [_I, _I, _I, _I, _I64] + [_P] * 8
     lib.oracle_pages_resample.restype = _I
+    lib.oracle_draft_sample.argtypes = [_I, _I64, _I64, _D, _P, _P, _P, _P]
+    lib.oracle_draft_sample.restype = _I
+    lib.oracle_pacer_lengths.argtypes = [_I, _I, _I, _D, _D, _P, _P, _P]
+    lib.oracle_pacer_lengths.restype = None
     return lib
 
 
@@ -230,3 +234,30 @@ def pages_resample(P, N, ancestors, table_old, table_new, lens, ref, free_pages,
     st = lib.oracle_pages_resample(P, N, L, S, ref.size, _ptr(anc), _ptr(table_old), _ptr(table_new), _ptr(lens),
                                    _ptr(len_out), _ptr(ref), _ptr(free_pages), _ptr(fc))
     return dict(status=int(st), len=len_out, ref=ref, free_pages=free_pages, free_count=int(fc[0]))
+
+
+def draft_sample(logits, uniforms, T, lib=None):
+    """One token per row from softmax(z / T) by inverse CDF with the row's
+    uniform.  Returns dict(tokens, margin, flags)."""
+    lib = lib or load()
+    logits = np.ascontiguousarray(logits)
+    R, V = logits.shape
+    u = np.ascontiguousarray(uniforms, np.float32)
+    assert u.size == R
+    tokens = np.zeros(R, np.int32)
+    margin = np.zeros(R, np.float64)
+    fl = lib.oracle_draft_sample(_dtype_code(logits), R, V, T, _ptr(logits), _ptr(u), _ptr(tokens), _ptr(margin))
+    return dict(tokens=tokens, margin=margin, flags=int(fl))
+
+
+def pacer_lengths(scores, block, max_blocks, t0, rho, lib=None):
+    """PACER draft lengths from scores [B, max_blocks * block].  Returns
+    (lengths [B], offsets [B + 1])."""
+    lib = lib or load()
+    scores = np.ascontiguousarray(scores, np.float32)
+    B = scores.shape[0]
+    assert scores.shape == (B, max_blocks * block)
+    lengths = np.zeros(B, np.int32)
+    offsets = np.zeros(B + 1, np.int32)
+    lib.oracle_pacer_lengths(B, block, max_blocks, t0, rho, _ptr(scores), _ptr(lengths), _ptr(offsets))
+    return lengths, offsets

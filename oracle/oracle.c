@@ -555,3 +555,63 @@ int oracle_pages_resample(int P, int N, int L, int S, int64_t M, const int32_t* 
   *free_count = top;
   return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Draft side: the steps just before verification.
+ *   [SMC] sec. 2 step 1: the draft model extends every particle (or sequence)
+ *         by one token per draft position, a draw from the draft
+ *         distribution q.
+ *   [PACER] Methodik 1-3: drafting goes in blocks of b tokens; after each
+ *         block a pre-verifier estimates the acceptance of its tokens, and the
+ *         drafting stops when the block's mean estimate falls below a
+ *         threshold t; otherwise t grows by a factor rho and another block is
+ *         drafted.
+ * ------------------------------------------------------------------------- */
+
+/*
+ * One token per row r of logits [R, V], drawn from softmax(z_r / T) by inverse
+ * CDF with uniforms[r] (the conventions at the top of this file).  margin[r]
+ * (optional): the draw's distance to the nearer edge of its CDF interval.
+ * Returns the status bits (NONFINITE, CDF_CLAMP) of all rows.
+ */
+int oracle_draft_sample(int dtype, int64_t R, int64_t V, double T, const void* logits,
+                        const float* uniforms, int32_t* tokens, double* margin) {
+  double* w = (double*)malloc(sizeof(double) * (size_t)(V > 0 ? V : 1));
+  uint32_t flags = 0;
+  for (int64_t r = 0; r < R; r++) {
+    final_weights(dtype, row_ptr(dtype, logits, r, V), NULL, V, T, w, &flags);
+    tokens[r] = (int32_t)inverse_cdf(w, V, (double)uniforms[r], margin ? &margin[r] : NULL, &flags);
+  }
+  free(w);
+  return (int)flags;
+}
+
+/*
+ * PACER draft lengths of B sequences.  scores [B, max_blocks * block]: the
+ * pre-verifier's estimated acceptance of each drafted token, block after
+ * block.  Per sequence the threshold starts at t0; after block m (m = 1, 2,
+ * ...) the block's mean score -- its scores summed in index order in double,
+ * divided by block -- is compared with t: if it is below t (strictly), or m ==
+ * max_blocks, the sequence stops with K_b = block * m tokens; otherwise
+ * t = t * rho.  Scores after a sequence's stopping block are not read.
+ * offsets[B + 1]: offsets[0] = 0, offsets[b + 1] = offsets[b] + K_b (the
+ * packed draft rows of a ragged verify).
+ */
+void oracle_pacer_lengths(int B, int block, int max_blocks, double t0, double rho,
+                          const float* scores, int32_t* lengths, int32_t* offsets) {
+  offsets[0] = 0;
+  for (int b = 0; b < B; b++) {
+    const float* s = scores + (int64_t)b * max_blocks * block;
+    double t = t0;
+    int m = 1;
+    for (;; m++) {
+      double sum = 0.0;
+      for (int k = 0; k < block; k++) sum += (double)s[(int64_t)(m - 1) * block + k];
+      double mean = sum / block;
+      if (mean < t || m == max_blocks) break;
+      t = t * rho;
+    }
+    lengths[b] = block * m;
+    offsets[b + 1] = offsets[b] + lengths[b];
+  }
+}

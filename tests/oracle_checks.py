@@ -28,7 +28,8 @@ def _load_golden(name):
 
 
 def _logits(probs):
-    return np.log(np.asarray(probs, dtype=np.float64)).astype(np.float32)
+    with np.errstate(divide="ignore"):  # probability 0 is logit -inf
+        return np.log(np.asarray(probs, dtype=np.float64)).astype(np.float32)
 
 
 def rand_sd_problem(rng, B, K, V, T, delta, scale=3.0, dtype=np.float32):
@@ -633,6 +634,113 @@ def check_pages_errors(lib):
     assert res["status"] == 3 and (res["ref"] == st["ref"]).all() and res["free_count"] == st["free_count"]
 
 
+# --------------------------------------------------------------------------
+# draft side: token draws from q, PACER lengths
+# --------------------------------------------------------------------------
+
+
+def check_golden_draft_sample(lib):
+    g = _load_golden("draft_sample.json")
+    z = _logits(np.array(g["weights"])[None, :])
+    for case in g["cases"]:
+        u = np.array(case["uniforms"], np.float32)
+        r = oracle.draft_sample(np.repeat(z, len(u), axis=0), u, case["T"], lib=lib)
+        assert r["tokens"].tolist() == case["tokens"], (case, r["tokens"])
+
+
+def check_draft_sample_vs_numpy(lib):
+    """A categorical inverse-CDF draw per row: numpy searchsorted on the
+    cumulative softmax (scipy), away from interval edges."""
+    rng = np.random.default_rng(71)
+    R, V, T = 48, 777, 0.8
+    z = (3 * rng.standard_normal((R, V))).astype(np.float32)
+    u = rng.random(R).astype(np.float32)
+    r = oracle.draft_sample(z, u, T, lib=lib)
+    for i in range(R):
+        c = np.cumsum(softmax(z[i].astype(np.float64) / T))
+        want = int(np.searchsorted(c, float(u[i]) * c[-1], side="right"))
+        if np.min(np.abs(c / c[-1] - float(u[i]))) > 1e-12:
+            assert r["tokens"][i] == want, (i, r["tokens"][i], want)
+
+
+def check_draft_sample_law(lib):
+    """The draw's law over its uniform is exactly softmax(z / T): each CDF
+    interval's midpoint yields that interval's token, masked (-inf) tokens
+    never appear, and the rows are drawn independently of one another."""
+    rng = np.random.default_rng(73)
+    for V, T in ((3, 1.0), (6, 0.6), (9, 2.5)):
+        z = (2 * rng.standard_normal(V)).astype(np.float32)
+        z[rng.integers(0, V)] = -np.inf
+        p = softmax(z.astype(np.float64) / T)
+        mid, length = _midpoints(np.cumsum(p))
+        r = oracle.draft_sample(np.tile(z, (len(mid), 1)), mid.astype(np.float32), T, lib=lib)
+        law = np.zeros(V)
+        for t, w in zip(r["tokens"], length):
+            law[t] += w
+        assert np.abs(law - p).max() < 1e-7, (law, p)
+    # rows are independent: row i's token depends on row i and uniform i only
+    z = (2 * rng.standard_normal((5, 40))).astype(np.float32)
+    u = rng.random(5).astype(np.float32)
+    both = oracle.draft_sample(z, u, 1.0, lib=lib)["tokens"]
+    alone = [int(oracle.draft_sample(z[i:i + 1], u[i:i + 1], 1.0, lib=lib)["tokens"][0]) for i in range(5)]
+    assert both.tolist() == alone, (both, alone)
+
+
+def check_golden_pacer(lib):
+    g = _load_golden("pacer_lengths.json")
+    scores = np.array([[float(x) for x in row] for row in g["scores"]], np.float32)
+    lengths, offsets = oracle.pacer_lengths(scores, g["block"], g["max_blocks"], g["t0"], g["rho"], lib=lib)
+    assert lengths.tolist() == g["expect"]["lengths"], lengths
+    assert offsets.tolist() == g["expect"]["offsets"], offsets
+
+
+def check_pacer_special_cases(lib):
+    """A threshold no mean can fall below drafts every block; one no mean can
+    reach stops after the first; one block is always the last; offsets are the
+    exclusive prefix sums of the lengths."""
+    rng = np.random.default_rng(79)
+    B, blk, mb = 200, 3, 5
+    s = rng.random((B, blk * mb)).astype(np.float32)
+    lens, offs = oracle.pacer_lengths(s, blk, mb, 0.0, 1.3, lib=lib)
+    assert (lens == blk * mb).all()
+    lens, offs = oracle.pacer_lengths(s, blk, mb, 1.0, 1.3, lib=lib)  # scores < 1
+    assert (lens == blk).all()
+    lens, _ = oracle.pacer_lengths(s[:, :blk], blk, 1, 0.9, 1.3, lib=lib)
+    assert (lens == blk).all()
+    lens, offs = oracle.pacer_lengths(s, blk, mb, 0.5, 1.1, lib=lib)
+    assert offs[0] == 0 and (np.diff(offs) == lens).all() and set(np.unique(lens)) <= {blk * m for m in range(1, 6)}
+    # a constant threshold (rho = 1): the number of blocks is the first block
+    # whose mean falls below t0, counted directly
+    lens, _ = oracle.pacer_lengths(s, blk, mb, 0.45, 1.0, lib=lib)
+    means = s.astype(np.float64).reshape(B, mb, blk).sum(axis=2) / blk
+    below = means < 0.45
+    first = np.where(below.any(axis=1), below.argmax(axis=1) + 1, mb)
+    assert (lens == blk * np.minimum(first, mb)).all()
+
+
+def _irwin_hall_cdf(x, n):
+    return sum((-1) ** k * math.comb(n, k) * (x - k) ** n for k in range(int(math.floor(x)) + 1)) / math.factorial(n)
+
+
+def check_pacer_law(lib):
+    """With scores ~ U(0,1) the chance of stopping after block m is the
+    Irwin-Hall CDF of n = block scores at n * t0 * rho^(m-1): the length law of
+    the rule, against 100k sequences (5-sigma bands; numpy's seeded stream)."""
+    rng = np.random.default_rng(83)
+    B, blk, mb, t0, rho = 102400, 4, 4, 0.5, 1.1
+    s = rng.random((B, blk * mb)).astype(np.float32)
+    lens, _ = oracle.pacer_lengths(s, blk, mb, t0, rho, lib=lib)
+    stop = [_irwin_hall_cdf(blk * t0 * rho ** m, blk) for m in range(mb - 1)]
+    p, go = [], 1.0
+    for m in range(mb - 1):
+        p.append(go * stop[m])
+        go *= 1 - stop[m]
+    p.append(go)
+    for m in range(mb):
+        f = float(np.mean(lens == blk * (m + 1)))
+        assert abs(f - p[m]) < 5 * math.sqrt(p[m] * (1 - p[m]) / B), (m, f, p[m])
+
+
 DETERMINISTIC_CHECKS = [
     check_golden_sd_fixed,
     check_golden_sd_csr,
@@ -660,4 +768,10 @@ DETERMINISTIC_CHECKS = [
     check_power_one_is_plain,
     check_pages_content_model,
     check_pages_errors,
+    check_golden_draft_sample,
+    check_draft_sample_vs_numpy,
+    check_draft_sample_law,
+    check_golden_pacer,
+    check_pacer_special_cases,
+    check_pacer_law,
 ]

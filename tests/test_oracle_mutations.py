@@ -56,6 +56,14 @@ MUTATIONS = [
      "for (int64_t j = 0; j < used_pages(len_in[k], S); j++) ref[table_old[k * L + j]]--;", ""),
     ("pages_length_not_gathered", "len_out[k] = len_in[(k / N) * N + ancestors[k]];", "len_out[k] = len_in[k];"),
     ("pages_freed_twice", "if (ref[pg] == 0 && !pushed[pg]) {", "if (ref[pg] == 0) {"),
+    ("draft_sample_uniform_index", "(double)uniforms[r]", "(double)uniforms[0]"),
+    ("draft_sample_row_index", "row_ptr(dtype, logits, r, V)", "row_ptr(dtype, logits, 0, V)"),
+    ("pacer_not_strict", "if (mean < t || m == max_blocks) break;", "if (mean <= t || m == max_blocks) break;"),
+    ("pacer_threshold_not_grown", "t = t * rho;", "t = t * 1.0;"),
+    ("pacer_mean_not_divided", "double mean = sum / block;", "double mean = sum;"),
+    ("pacer_stopping_block_dropped", "lengths[b] = block * m;", "lengths[b] = block * (m - 1);"),
+    ("pacer_offsets_not_accumulated", "offsets[b + 1] = offsets[b] + lengths[b];", "offsets[b + 1] = lengths[b];"),
+    ("pacer_block_offset", "sum += (double)s[(int64_t)(m - 1) * block + k];", "sum += (double)s[(int64_t)m * block + k];"),
 ]
 
 
