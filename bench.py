@@ -142,6 +142,9 @@ def parse():
     ap.add_argument("--with-pages", action="store_true",
                     help="SMC workloads: each step also does the paged-KV bookkeeping (append K+1 tokens "
                          "before, resample after), 16-token pages")
+    ap.add_argument("--draft-sample", action="store_true",
+                    help="time the draft-side draw instead: one token per row of one draft position "
+                         "(B sequences or P*N particles) of the workload")
     ap.add_argument("--beta", type=float, default=None,
                     help="SMC workloads: power-sampling target p^beta (smc_reweight_resample_power)")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -168,6 +171,8 @@ def main():
     cfg = synth.CONFIGS[args.config]
     steps = args.steps if args.steps is not None else cfg.steps
     W = args.warmup
+    if args.draft_sample and (args.with_pages or args.beta is not None):
+        sys.exit("--draft-sample times the draft-side draw alone")
     if args.with_pages:
         if cfg.kind != "smc":
             sys.exit("--with-pages applies to the SMC workloads")
@@ -177,7 +182,12 @@ def main():
         W += W % 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    gen = synth.Generator(cfg, dev)
+    def lib_lengths(scores, block, max_blocks, t0, rho):
+        # the ragged workload's draft lengths by the library's PACER rule
+        out = smcsd.pacer_lengths(torch.from_numpy(scores).to(dev), block, max_blocks, t0, rho)
+        return out["lengths"].cpu().numpy()
+
+    gen = synth.Generator(cfg, dev, lengths=lib_lengths)
 
     # ---------------- inputs: distinct batches, resident in HBM -------------
     per_batch = synth.step_bytes(cfg, None if cfg.kind != "sd_ragged" else np.full(cfg.B, 7))
@@ -190,10 +200,28 @@ def main():
     torch.cuda.synchronize()
     positions = [synth.verified_positions(cfg, bt.get("Kb")) for bt in batches]
     nbytes = [synth.step_bytes(cfg, bt.get("Kb")) for bt in batches]
+    R_draw = cfg.B if cfg.kind != "smc" else cfg.P * cfg.N  # rows of one draft position
+    if args.draft_sample:
+        positions = [R_draw] * nb
+        nbytes = [R_draw * cfg.V * (4 if cfg.dtype == "f32" else 2)] * nb
 
     # ---------------- prepared library calls ---------------------------------
     def prepare(stream_handle):
         calls = []
+        if args.draft_sample:
+            # one draft position: the first R_draw draft rows of each batch, one
+            # uniform per row
+            ws = smcsd.new_workspace(smcsd.draft_sample_workspace_bytes(int(cfg.dtype == "bf16"), R_draw, cfg.V), dev)
+            outs = None
+            for s in range(steps + W):
+                bt = batches[s % nb]
+                u = bt["bonus_u"] if cfg.kind == "smc" else bt["uniforms"]
+                call, o = smcsd.prepare_draft_sample(
+                    bt["draft"][:R_draw], u[:R_draw], cfg.T, workspace=ws, stream=stream_handle,
+                    **({} if outs is None else {k: outs[k] for k in ("tokens", "status_flags")}))
+                outs = o
+                calls.append(call)
+            return calls, outs
         if cfg.kind == "smc":
             P, N, K = cfg.P, cfg.N, cfg.K
             logw = torch.zeros(P * N, dtype=torch.float32, device=dev)
@@ -341,7 +369,18 @@ def main():
         done_pos, t_cpu, n_steps = 0, 0.0, 0
         for i in range(nb):
             bt = batches[i]
-            if cfg.kind == "smc":
+            if args.draft_sample:
+                u = (bt["bonus_u"] if cfg.kind == "smc" else bt["uniforms"])[:R_draw].cpu().numpy()
+                for r0 in range(0, R_draw, 8):  # a few rows at a time: the sample stays bounded
+                    z = host_logits(bt["draft"][r0:min(r0 + 8, R_draw)])
+                    t0 = time.perf_counter()
+                    oracle.draft_sample(z, u[r0:r0 + len(z)], cfg.T)
+                    t_cpu += time.perf_counter() - t0
+                    done_pos += len(z)
+                    if t_cpu > args.cpu_seconds:
+                        break
+                sample = f"{done_pos} draft rows of {cfg.name}"
+            elif cfg.kind == "smc":
                 # one prompt at a time: the oracle's unit of work
                 P, N, K = cfg.P, cfg.N, cfg.K
                 for p in range(P):
@@ -362,7 +401,15 @@ def main():
             else:
                 tg, dr = host_logits(bt["target"]), host_logits(bt["draft"])
                 tk, u = bt["tokens"].cpu().numpy(), bt["uniforms"].cpu().numpy()
-                off = None if bt["offsets"] is None else bt["offsets"].cpu().numpy()
+                off = None
+                if bt["offsets"] is not None:
+                    # the oracle's own lengths for this step's scores (they equal the
+                    # library's, which laid out the batch)
+                    pc = cfg.pacer
+                    _, off = oracle.pacer_lengths(synth.pacer_scores(cfg.B, cfg.seed, i, pc["block"], pc["max_blocks"]),
+                                                  pc["block"], pc["max_blocks"], pc["t0"], pc["rho"])
+                    if not np.array_equal(off, bt["offsets"].cpu().numpy()):
+                        sys.exit("PACER lengths of the library and the oracle differ")
                 t0 = time.perf_counter()
                 oracle.sd_verify(tg, dr, tk, u, cfg.T, K=cfg.K, offsets=off)
                 t_cpu += time.perf_counter() - t0
@@ -371,15 +418,17 @@ def main():
                 sample = f"{n_steps} steps of {cfg.name}"
             if t_cpu > args.cpu_seconds:
                 break
-        cpu = {"value": done_pos / t_cpu, "unit": "verified draft positions/s", "cores": 1, "kind": "oracle",
+        unit = "sampled draft tokens/s" if args.draft_sample else "verified draft positions/s"
+        cpu = {"value": done_pos / t_cpu, "unit": unit, "cores": 1, "kind": "oracle",
                "sample": sample + f" ({t_cpu:.1f} s, single-threaded fp64 C oracle, gcc -O2)"}
         log(f"[bench] cpu oracle: {cpu['value']:.1f} positions/s over {sample}")
 
     e = 4 if cfg.dtype == "f32" else 2
     line = {
-        "metric": "verified draft positions/sec and achieved HBM GB/s (% of MI355X peak)",
+        "metric": ("sampled draft tokens/sec and achieved HBM GB/s (% of MI355X peak)" if args.draft_sample else
+                   "verified draft positions/sec and achieved HBM GB/s (% of MI355X peak)"),
         "value": value,
-        "unit": "verified draft positions/s",
+        "unit": "sampled draft tokens/s" if args.draft_sample else "verified draft positions/s",
         "n_gpus": 1,
         "steps": steps,
         "warmup": W,
@@ -393,10 +442,12 @@ def main():
                    "V": cfg.V, "logits": cfg.dtype, "temperature": cfg.T, "launch": args.launch,
                    "input_batches": nb, "status_flags": flags,
                    **({} if args.beta is None else {"power_beta": args.beta}),
-                   **({"paged_kv_bookkeeping": True, "page_size": 16} if args.with_pages else {})},
+                   **({"paged_kv_bookkeeping": True, "page_size": 16} if args.with_pages else {}),
+                   **({"draft_sample_rows": R_draw} if args.draft_sample else {})},
         "roofline": {"bound": "hbm", "kernel": "k_stream", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_from_profiles(cfg.name) if args.beta is None else None,
+                     "traffic": (traffic_from_profiles(cfg.name) if args.beta is None and not args.draft_sample
+                                 else None),
                      "algorithmic_bytes_per_launch": bytes_total / steps, "bytes_per_element": e,
                      "kernel_us": stream_ms * 1e3, "decision_kernel_us": tail_ms * 1e3,
                      "call_us": ms_per_step * 1e3},

@@ -333,6 +333,56 @@ int32_t smc_pages_resample(int32_t P, int32_t N, int32_t L, int32_t page_size, i
                            int32_t* seq_len_out, int32_t* ref_count, int32_t* free_pages, int32_t* free_count,
                            uint32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Draft side: the steps just before verification.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * One token per row drawn from the draft distribution ("Faster LLM Inference
+ * via Sequential Monte Carlo", sec. 2 step 1: the draft model extends every
+ * particle, or sequence, by one token per draft position).
+ *   logits    [R, V] fp32 or bf16 (dtype as for sd_verify), row-major, device.
+ *   uniforms  float [R] in [0, 1), device, one per row.
+ *   tokens    int32 [R] out, device: the smallest token id whose inclusive
+ *             prefix sum of softmax(z / T) exceeds uniforms[r] times the row
+ *             total (strict comparison, ascending token id); if rounding
+ *             leaves none, the last token of positive probability
+ *             (SMCSD_FLAG_CDF_CLAMP).  This is the convention of every draw
+ *             in this library: the call is sd_verify's final draw with no
+ *             draft tokens, on the same kernels.
+ * Workspace: draft_sample_workspace_bytes(dtype, R, V) bytes, aligned and
+ * zero-filled before the first use as for sd_verify (the same workspace may
+ * serve both).  Errors and flags as for sd_verify (SMCSD_FLAG_NONFINITE for a
+ * row that is not a distribution; its token is then unspecified).
+ */
+size_t draft_sample_workspace_bytes(int32_t dtype, int32_t R, int32_t V);
+int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, const void* logits,
+                     const float* uniforms, int32_t* tokens, uint32_t* status_flags, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * PACER draft lengths ("PACER: Blockwise Pre-verification for Speculative
+ * Decoding with Adaptive Length", Methodik 1-3: drafting in blocks; after each
+ * block the pre-verifier's mean estimated acceptance of its tokens is compared
+ * with a threshold t; below it the drafting stops, otherwise t grows by the
+ * factor rho and another block follows).
+ *   scores   float [B, max_blocks * block], device: the estimated acceptance of
+ *            each drafted token, block after block.  Scores after a
+ *            sequence's stopping block are not read.
+ *   lengths  int32 [B] out, device: K_b = block * m, m the first block whose
+ *            mean (its scores summed in index order in double, divided by
+ *            block) is below t (strictly), or max_blocks; t starts at t0 and
+ *            is multiplied by rho (in double) after every block that goes on.
+ *            A NaN mean never stops a sequence.
+ *   offsets  int32 [B + 1] out, device: 0, then the running sums of lengths
+ *            (the draft_offsets of a ragged sd_verify).
+ * One workgroup; no workspace.  Requirements: B >= 0, block >= 1,
+ * max_blocks >= 1, B * max_blocks * block <= 2^31 - 1, t0 and rho finite;
+ * otherwise SMCSD_ERR_INVALID_ARG.
+ */
+int32_t pacer_lengths(int32_t B, int32_t block, int32_t max_blocks, double t0, double rho, const float* scores,
+                      int32_t* lengths, int32_t* offsets, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ __all__ = [
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "FLAG_ZERO_WEIGHTS", "FLAG_CDF_CLAMP", "FLAG_BAD_INPUT",
     "FLAG_PAGES_FULL", "FLAG_PAGES_EXHAUSTED",
     "new_workspace", "time_next_call", "smc_pages_workspace_bytes", "smc_pages_append", "smc_pages_resample",
+    "draft_sample_workspace_bytes", "prepare_draft_sample", "draft_sample", "pacer_lengths",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,6 +44,9 @@ _SIGNATURES = {
                                _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_reweight_resample_power": ([_I32, _I32, _I32, _I32, _I32, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
                                      _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "draft_sample_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+    "draft_sample": ([_I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "pacer_lengths": ([_I32, _I32, _I32, ctypes.c_double, ctypes.c_double, _P, _P, _P, _P], _I32),
     "smc_pages_workspace_bytes": ([_I32, _I32, _I32, _I64], _SZ),
     "smc_pages_append": ([_I32, _I32, _I32, _I32, _I32, _I64] + [_P] * 10 + [_SZ, _P], _I32),
     "smc_pages_resample": ([_I32, _I32, _I32, _I32, _I64] + [_P] * 9 + [_SZ, _P], _I32),
@@ -303,3 +307,59 @@ def smc_pages_resample(ancestors, page_table_old, seq_len_in, ref_count, free_pa
                                    _ptr(status_flags), _ptr(ws), wsb,
                                    stream if stream is not None else _stream(dev)))
     return dict(seq_len_out=seq_len_out, status_flags=status_flags)
+
+
+def draft_sample_workspace_bytes(dtype_code, R, V) -> int:
+    return int(_lib.draft_sample_workspace_bytes(dtype_code, R, V))
+
+
+def prepare_draft_sample(logits, uniforms, temperature, *, tokens=None, status_flags=None, workspace=None,
+                         stream=None):
+    """Validate and marshal one draft_sample call (one token per row of
+    ``logits`` [R, V] from softmax(z / T) by inverse CDF with ``uniforms``
+    [R]); returns (call, outputs) with outputs tokens and status_flags."""
+    dev = logits.device
+    dt = _dtype_code(logits)
+    R, V = logits.shape
+    _need(logits, logits.dtype, "logits")
+    _need(uniforms, torch.float32, "uniforms")
+    if uniforms.numel() != R:
+        raise ValueError(f"uniforms: {uniforms.numel()} values for {R} rows")
+    tokens = tokens if tokens is not None else torch.empty(R, dtype=torch.int32, device=dev)
+    _need(tokens, torch.int32, "tokens")
+    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    ws, wsb = _workspace(draft_sample_workspace_bytes(dt, R, V), dev, workspace)
+    st = stream if stream is not None else _stream(dev)
+    args = (dt, R, V, float(temperature), _ptr(logits), _ptr(uniforms), _ptr(tokens), _ptr(status_flags), _ptr(ws),
+            wsb, st)
+    fn = _lib.draft_sample
+    keep = (logits, uniforms, ws)
+
+    def call():
+        _check(fn(*args))
+        return keep
+
+    return call, dict(tokens=tokens, status_flags=status_flags)
+
+
+def draft_sample(logits, uniforms, temperature, **kw):
+    call, out = prepare_draft_sample(logits, uniforms, temperature, **kw)
+    call()
+    return out
+
+
+def pacer_lengths(scores, block, max_blocks, t0, rho, *, lengths=None, offsets=None, stream=None):
+    """PACER draft lengths from ``scores`` [B, max_blocks * block] (see
+    ``pacer_lengths`` in include/smcsd.h).  Returns dict(lengths, offsets)."""
+    _need(scores, torch.float32, "scores")
+    dev = scores.device
+    B = scores.shape[0]
+    if scores.dim() != 2 or scores.shape[1] != max_blocks * block:
+        raise ValueError(f"scores must be [B, {max_blocks * block}], got {tuple(scores.shape)}")
+    lengths = lengths if lengths is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    offsets = offsets if offsets is not None else torch.empty(B + 1, dtype=torch.int32, device=dev)
+    _need(lengths, torch.int32, "lengths")
+    _need(offsets, torch.int32, "offsets")
+    _check(_lib.pacer_lengths(B, block, max_blocks, float(t0), float(rho), _ptr(scores), _ptr(lengths),
+                              _ptr(offsets), stream if stream is not None else _stream(dev)))
+    return dict(lengths=lengths, offsets=offsets)

@@ -168,6 +168,41 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
              : SMCSD_ERR_HIP;
 }
 
+size_t draft_sample_workspace_bytes(int32_t dtype, int32_t R, int32_t V) {
+  (void)dtype;
+  if (R <= 0 || V <= 0) return 0;
+  return sd_layout(R, V, 0).total;
+}
+
+// One draw per row: the verify step's final draw with no draft tokens (each
+// row a sequence whose draft length is 0, so its "bonus" row is the row).
+int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, const void* logits,
+                     const float* uniforms, int32_t* tokens, uint32_t* status_flags, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
+  if (R < 0 || V < 1 || !temperature_ok(temperature)) return SMCSD_ERR_INVALID_ARG;
+  if (V > SMCSD_MAX_V) return SMCSD_ERR_UNSUPPORTED;
+  if (R == 0) return SMCSD_OK;
+  if (!logits || !uniforms || !tokens) return SMCSD_ERR_INVALID_ARG;
+  const SdLayout l = sd_layout(R, V, 0);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
+    return SMCSD_ERR_WORKSPACE;
+  const bool bf16 = dtype == SMCSD_BF16;
+  const bool vec = vec_ok(dtype, V, logits, nullptr);
+  smcsd::Plan plan;
+  if (smcsd::plan_stream(R, ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  char* ws = static_cast<char*>(workspace);
+  smcsd::SdArgs a;
+  fill_step(&a.s, plan, logits, nullptr, nullptr, nullptr, R, R, 0, V, 0, temperature, ws, l.part, l.tpart,
+            status_flags);
+  a.uniforms = uniforms;
+  a.num_accepted = nullptr;
+  a.final_token = tokens;
+  return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
+             ? SMCSD_OK
+             : SMCSD_ERR_HIP;
+}
+
 size_t smc_workspace_bytes(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V) {
   (void)dtype;
   if (P <= 0 || N <= 0 || K < 0 || V <= 0) return 0;

@@ -852,7 +852,40 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   or_flags(fl, L);
   __syncthreads();
   if (threadIdx.x == 0) {
-    a.num_accepted[b] = n;
+    if (a.num_accepted) a.num_accepted[b] = n;  // absent for a plain draw (no draft tokens)
+    a.final_token[b] = y;
+    raise_flags(s.flags, L.fl);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_draw_tail: the final draw alone, when no sequence has draft tokens (fixed
+// K = 0: every group is one row and n = K_b = 0).  The same merge and the same
+// draw as k_sd_tail, at a quarter of its threads, so that thousands of rows
+// (one draft position of many particles) run as resident small workgroups.
+// ---------------------------------------------------------------------------
+template <typename DT, bool VL>
+__global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_draw_tail(SdArgs a) {
+  using raw = typename DT::raw;
+  __shared__ TailLds L;
+  const StepArgs& s = a.s;
+  const int64_t b = blockIdx.x;
+  const Group G = group_of(b, 0, nullptr, 0);
+  if (threadIdx.x == 0) L.fl = 0;
+  const float u = a.uniforms[b];
+  merge_rows<BLOCK>(s.part + G.fr0 * s.nseg, 1, s.nseg, L);
+  int bnp, bper;
+  const float2* bp = bonus_partials(s, G.fr0, b, 0, &bnp, &bper);
+  stage_partials<BLOCK>(bp, bnp, L);
+  __syncthreads();
+  uint32_t fl = 0;
+  const RowStat sk = stat_of(L, 0);
+  if (!sk.ok) fl |= FLAG_NONFINITE;
+  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, b, 0), s, s.c, sk.M, (double)u, bnp, bper, L, fl);
+  or_flags(fl, L);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (a.num_accepted) a.num_accepted[b] = 0;
     a.final_token[b] = y;
     raise_flags(s.flags, L.fl);
   }
@@ -1146,6 +1179,10 @@ template <typename DT, bool VL>
 static const void* sd_tail_kernel() {
   return kptr(&k_sd_tail<DT, VL>);
 }
+template <typename DT, bool VL>
+static const void* draw_tail_kernel() {
+  return kptr(&k_draw_tail<DT, VL>);
+}
 
 template <typename DT, bool VL>
 static const void* smc_tail_kernel() {
@@ -1156,6 +1193,11 @@ hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStr
   hipError_t e = launch(stream_kernel(bf16, vec, p.tp), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
                         t.stream_stop);
   if (e != hipSuccess) return e;
+  if (a.s.K == 0 && !a.s.offsets) {  // draws only
+    const void* k = bf16 ? (vec ? draw_tail_kernel<Bf16, true>() : draw_tail_kernel<Bf16, false>())
+                         : (vec ? draw_tail_kernel<F32, true>() : draw_tail_kernel<F32, false>());
+    return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
+  }
   const void* k = bf16 ? (vec ? sd_tail_kernel<Bf16, true>() : sd_tail_kernel<Bf16, false>())
                        : (vec ? sd_tail_kernel<F32, true>() : sd_tail_kernel<F32, false>());
   return launch(k, (unsigned)a.s.ngroups, SD_BLOCK, a, s, t.tail_start, t.tail_stop);

@@ -1,10 +1,12 @@
 """Seeded synthetic inputs for the verify-and-sample step (test / bench infrastructure).
 
 Both the GPU library (through its tests and benchmark) and the CPU oracle
-consume what this module produces; it contains none of the verify or resample
-arithmetic.  Logits, draft tokens and uniforms are generated on the GPU by
-``libsmcsd_synth.so`` (Philox4x32-10 streams); the rank prior, the PACER-style
-ragged lengths and the page tables are built on the host.
+consume what this module produces; it contains none of the verify, resample or
+drafting arithmetic.  Logits, draft tokens and uniforms are generated on the
+GPU by ``libsmcsd_synth.so`` (Philox4x32-10 streams); the rank prior, the PACER
+pre-verifier scores and the page tables are built on the host.  Draft tokens are
+drawn by the Gumbel-max method, not by the inverse CDF that the library and the
+oracle use for their own draws.
 
 The five workloads stand in for the pages' model families and draft lengths:
 vocabulary widths 32000 / 32768 (Mistral-family ~32k tokenizer), 128256 and
@@ -52,7 +54,7 @@ def lib():
         P, I32, I64, U32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
         L.synth_philox4x32_10.argtypes = [P, P, P]
         L.synth_rank_base.argtypes = [I64, U32, P, P]
-        L.synth_pacer_lengths.argtypes = [I32, I32, I32, ctypes.c_double, ctypes.c_double, U32, U32, P]
+        L.synth_pacer_scores.argtypes = [I32, I32, I32, U32, U32, P]
         L.synth_logits.argtypes = [I32, I64, I64, P, P, P, U32, U32, P, P, P]
         L.synth_logits.restype = I32
         L.synth_draft_tokens.argtypes = [I32, I64, I64, F, P, U32, U32, P, P]
@@ -82,9 +84,10 @@ def rank_base(V: int, seed: int):
     return rank, base
 
 
-def pacer_lengths(B, seed, step, block=4, max_blocks=4, t0=0.5, rho=1.1):
-    out = np.zeros(B, np.int32)
-    lib().synth_pacer_lengths(B, block, max_blocks, t0, rho, seed, step, _np_ptr(out))
+def pacer_scores(B, seed, step, block=4, max_blocks=4):
+    """Pre-verifier stand-in scores [B, max_blocks * block] ~ U(0,1) of one step."""
+    out = np.zeros((B, max_blocks * block), np.float32)
+    lib().synth_pacer_scores(B, block, max_blocks, seed, step, _np_ptr(out))
     return out
 
 
@@ -132,11 +135,17 @@ def _torch():
 
 
 class Generator:
-    """Builds one step of inputs for a config on a torch device."""
+    """Builds one step of inputs for a config on a torch device.
 
-    def __init__(self, cfg: Config, device="cuda"):
+    ``lengths(scores, block, max_blocks, t0, rho) -> int32 [B]`` turns a ragged
+    workload's PACER scores into draft lengths; the caller supplies it (the
+    oracle in tests, the library in the benchmark), so this module holds no
+    part of the rule."""
+
+    def __init__(self, cfg: Config, device="cuda", lengths=None):
         torch = _torch()
         self.cfg = cfg
+        self.lengths = lengths
         self.device = torch.device(device)
         _, base = rank_base(cfg.V, cfg.seed)
         self.base = torch.from_numpy(base).to(self.device)
@@ -154,7 +163,11 @@ class Generator:
             delta = np.array([c.deltas[b % len(c.deltas)] for b in range(G)], np.float32)
         elif c.kind == "sd_ragged":
             G = c.B
-            Kb = pacer_lengths(c.B, c.seed, step, **c.pacer)
+            if self.lengths is None:
+                raise ValueError("a ragged workload needs a lengths function (PACER rule)")
+            pc = c.pacer
+            scores = pacer_scores(c.B, c.seed, step, pc["block"], pc["max_blocks"])
+            Kb = np.asarray(self.lengths(scores, pc["block"], pc["max_blocks"], pc["t0"], pc["rho"]), np.int32)
             delta = np.array([c.deltas[b % len(c.deltas)] for b in range(G)], np.float32)
         else:
             G, Kb = c.P * c.N, np.full(c.P * c.N, c.K, np.int32)

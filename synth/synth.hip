@@ -197,26 +197,21 @@ void synth_rank_base(int64_t V, uint32_t seed, int32_t* rank, float* base) {
   for (int64_t i = 0; i < V; i++) base[i] = (float)(-0.5 * log(1.0 + (double)rank[i]));
 }
 
-// PACER-style blockwise draft lengths (host).  Per sequence: t = t0; for block
-// m = 1..max_blocks the pre-verifier stand-in gives `block` scores
-// s ~ U(0,1) (stream 6, counter (step, b, m-1, 0)); drafting stops after block m
-// when m == max_blocks or mean(s) < t, else t *= rho.  K_b = block * m.
-void synth_pacer_lengths(int32_t B, int32_t block, int32_t max_blocks, double t0, double rho,
-                         uint32_t seed, uint32_t step, int32_t* lengths) {
+// PACER pre-verifier stand-in scores (host): scores[b, (m-1) * block + k] ~
+// U(0,1) from stream 6 at counter (step, b, m-1, k / 4), element k % 4, for
+// blocks m = 1..max_blocks.  The draft lengths follow from them by the PACER
+// rule, which the library and the oracle each implement.
+void synth_pacer_scores(int32_t B, int32_t block, int32_t max_blocks, uint32_t seed, uint32_t step,
+                        float* scores) {
   for (int32_t b = 0; b < B; b++) {
-    double t = t0;
-    int32_t m = 1;
-    for (;; m++) {
-      double sum = 0.0;
+    for (int32_t m = 1; m <= max_blocks; m++) {
+      float* out = scores + ((int64_t)b * max_blocks + (m - 1)) * block;
       for (int32_t k = 0; k < block; k += 4) {
         const U4 r = philox(U4{step, (uint32_t)b, (uint32_t)(m - 1), (uint32_t)(k / 4)}, seed, 6u);
         const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
-        for (int32_t e = 0; e < 4 && k + e < block; e++) sum += (double)u01(rr[e]);
+        for (int32_t e = 0; e < 4 && k + e < block; e++) out[k + e] = u01(rr[e]);
       }
-      if (m == max_blocks || sum / block < t) break;
-      t *= rho;
     }
-    lengths[b] = block * m;
   }
 }
 

@@ -105,6 +105,20 @@ def bonus_cdf(target, p_row, T):
     return cdf
 
 
+def compare_draft(logits, uniforms, T, ref, tokens_g, label="") -> Tally:
+    """Draft draws: tokens_g (GPU) against ref = oracle.draft_sample(logits,
+    uniforms, T), row by row, with the CDF band."""
+    t = Tally()
+    for r in range(len(tokens_g)):
+        yg, yo = int(tokens_g[r]), int(ref["tokens"][r])
+        if yg == yo:
+            t.equal += 1
+            t.exempt_equal += int(ref["margin"][r] < BAND)
+        else:
+            _token_diff(t, float(uniforms[r]), bonus_cdf(logits, r, T), yg, f"{label} row {r}")
+    return t
+
+
 def compare_smc(inp, ref, out_g, logw_in, pt_in, label="") -> Tally:
     """Lockstep check of one SMC step.  inp: numpy inputs (target, draft, tokens,
     bonus_u, resample_u, P, N, K, T, optional beta); ref: oracle.smc_step(...) run from the same

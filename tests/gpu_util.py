@@ -29,6 +29,12 @@ def lib():
     return s
 
 
+def oracle_lengths(scores, block, max_blocks, t0, rho):
+    """PACER draft lengths of a ragged workload, by the oracle (the lengths a
+    parity test feeds both sides come from the oracle, never the library)."""
+    return oracle.pacer_lengths(scores, block, max_blocks, t0, rho)[0]
+
+
 def dev_logits(a: np.ndarray):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)

@@ -98,13 +98,13 @@ def test_sd_deterministic():
 
 
 def _config_steps(idx, steps):
-    from gpu_util import check_sd, host_logits, say
+    from gpu_util import check_sd, host_logits, oracle_lengths, say
 
     import synth
     from compare import Tally
 
     cfg = synth.CONFIGS[idx]
-    gen = synth.Generator(cfg)
+    gen = synth.Generator(cfg, lengths=oracle_lengths)
     total = Tally()
     for s in steps:
         st = gen.sd_step(s)

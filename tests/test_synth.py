@@ -29,23 +29,20 @@ def test_rank_prior(synth):
     assert (rank != rank2).any()
 
 
-def _irwin_hall_cdf(x, n):
-    return sum((-1) ** k * math.comb(n, k) * (x - k) ** n for k in range(int(math.floor(x)) + 1)) / math.factorial(n)
-
-
-def test_pacer_length_law(synth):
-    """Blockwise lengths: stop after block m when mean(4 scores) < t, t = 0.5 * 1.1^(m-1)."""
-    stop = [_irwin_hall_cdf(4 * 0.5 * 1.1 ** (m - 1), 4) for m in range(1, 4)]
-    p = [stop[0], (1 - stop[0]) * stop[1], (1 - stop[0]) * (1 - stop[1]) * stop[2],
-         (1 - stop[0]) * (1 - stop[1]) * (1 - stop[2])]
-    assert abs(p[1] - 0.31543) < 1e-4 and abs(p[2] - 0.14012) < 1e-4 and abs(p[3] - 0.04444) < 1e-4
-    lens = np.concatenate([synth.pacer_lengths(256, 4, s) for s in range(400)])
-    assert set(np.unique(lens).tolist()) <= {4, 8, 12, 16}
-    n = lens.size
-    for m in range(4):
-        f = np.mean(lens == 4 * (m + 1))
-        assert abs(f - p[m]) < 5 * math.sqrt(p[m] * (1 - p[m]) / n), (m, f, p[m])
-    assert abs(lens.mean() - 4 * sum((m + 1) * p[m] for m in range(4))) < 0.05
+def test_pacer_scores(synth):
+    """The pre-verifier stand-in: U(0,1) scores, reproducible, one Philox block
+    per 4 scores of a block (counter (step, b, block, k / 4), stream 6), so a
+    sequence's scores do not depend on the batch size."""
+    a = synth.pacer_scores(256, 4, 7)
+    b = synth.pacer_scores(256, 4, 7)
+    assert a.shape == (256, 16) and a.dtype == np.float32 and (a == b).all()
+    assert (a >= 0).all() and (a < 1).all() and abs(float(a.mean()) - 0.5) < 0.02
+    assert (synth.pacer_scores(3, 4, 7) == a[:3]).all()
+    assert not (synth.pacer_scores(256, 4, 8) == a).all()
+    ctr = np.array([7, 5, 2, 0], np.uint32)
+    key = np.array([4, 6], np.uint32)
+    out = np.asarray(synth.philox4x32_10(ctr, key), np.uint32)
+    assert np.allclose(a[5, 8:12], (out >> 8).astype(np.float64) / 2 ** 24)
 
 
 def test_config_table(synth):
