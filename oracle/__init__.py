@@ -63,6 +63,10 @@ def _declare(lib):
     lib.oracle_draft_sample.restype = _I
     lib.oracle_pacer_lengths.argtypes = [_I, _I, _I, _D, _D, _P, _P, _P]
     lib.oracle_pacer_lengths.restype = None
+    lib.oracle_tree_verify.argtypes = [_I, _I, _I64, _D] + [_P] * 13
+    lib.oracle_tree_verify.restype = _I
+    lib.oracle_tree_final_cdf.argtypes = [_I, _I, _I64, _D] + [_P] * 5 + [_I, _P]
+    lib.oracle_tree_final_cdf.restype = _I
     return lib
 
 
@@ -261,3 +265,54 @@ def pacer_lengths(scores, block, max_blocks, t0, rho, lib=None):
     offsets = np.zeros(B + 1, np.int32)
     lib.oracle_pacer_lengths(B, block, max_blocks, t0, rho, _ptr(scores), _ptr(lengths), _ptr(offsets))
     return lengths, offsets
+
+
+def tree_verify(target, draft, node_off, draft_off, parent, tokens, uniforms, T, lib=None):
+    """Multi-draft speculative sampling over B token trees.
+
+    node_off [B+1] CSR over nodes (one target row, one uniform, one parent and
+    one token per node); draft_off [B+1] CSR over the draft rows (one per node
+    with children, in node order); parent: local parent index (-1 at the root);
+    uniforms[node_off[b] + n]: acceptance uniform of node n >= 1, the root's
+    slot holding the final draw's uniform.
+
+    Returns dict(num_accepted, last_node, final_token, flags, accept_margin,
+    sample_margin, status) -- status -1 when a tree is malformed.
+    """
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    V = target.shape[-1]
+    node_off = np.ascontiguousarray(node_off, dtype=np.int32)
+    draft_off = np.ascontiguousarray(draft_off, dtype=np.int32)
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    uniforms = np.ascontiguousarray(uniforms, dtype=np.float32)
+    B = node_off.shape[0] - 1
+    nn = int(node_off[-1]) if B >= 0 else 0
+    na = np.zeros(max(B, 1), np.int32)
+    ln = np.zeros(max(B, 1), np.int32)
+    ft = np.zeros(max(B, 1), np.int32)
+    fl = np.zeros(1, np.uint32)
+    am = np.full(max(nn, 1), -1.0)
+    sm = np.zeros(max(B, 1))
+    st = lib.oracle_tree_verify(_dtype_code(target), B, V, T, _ptr(node_off), _ptr(draft_off), _ptr(parent),
+                                _ptr(tokens), _ptr(target), _ptr(draft), _ptr(uniforms), _ptr(na), _ptr(ln),
+                                _ptr(ft), _ptr(fl), _ptr(am), _ptr(sm))
+    return dict(num_accepted=na[:B], last_node=ln[:B], final_token=ft[:B], flags=int(fl[0]), accept_margin=am[:nn],
+                sample_margin=sm[:B], status=st)
+
+
+def tree_final_cdf(target, draft, node_off, draft_off, parent, b, u, T, lib=None):
+    """Normalised CDF of tree b's final draw when the walk stops at node u."""
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    V = target.shape[-1]
+    node_off = np.ascontiguousarray(node_off, dtype=np.int32)
+    draft_off = np.ascontiguousarray(draft_off, dtype=np.int32)
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    cdf = np.zeros(V)
+    fl = lib.oracle_tree_final_cdf(_dtype_code(target), int(b), V, T, _ptr(node_off), _ptr(draft_off),
+                                   _ptr(parent), _ptr(target), _ptr(draft), int(u), _ptr(cdf))
+    return cdf, fl

@@ -615,3 +615,198 @@ void oracle_pacer_lengths(int B, int block, int max_blocks, double t0, double rh
     offsets[b + 1] = offsets[b] + lengths[b];
   }
 }
+
+/* ---------------------------------------------------------------------------
+ * Tree verification.  [SMC] sec. 4 (Ergebnisse) compares SMC-SD with
+ * tree-based speculative decoding but gives no algorithm for verifying a
+ * token tree.  Reading (multi-draft speculative sampling, the textbook way to
+ * verify several draft continuations against one target distribution):
+ *   - tree b has M_b = node_off[b+1] - node_off[b] nodes; node 0 is the root
+ *     (the last committed token), every other node n has a parent
+ *     parent[n] < n (local index) and a draft token x_n proposed as a child of
+ *     its parent; children of a node are tried in increasing node index;
+ *   - target row of node n: global row node_off[b] + n (the target's logits
+ *     for the token after the path root..n); draft row of node n, for nodes
+ *     with at least one child: draft_off[b] + (number of such nodes of tree b
+ *     with a smaller index) (the draft logits the children were drawn from);
+ *   - at node u the running distribution r starts as p_u; child c (token x)
+ *     is accepted iff u_c < r(x) / q_u(x) (strict), and the walk moves to c;
+ *     after a rejection, r becomes max(0, r - q_u) / Z with Z its total mass
+ *     (if Z is 0, r stays, flag ZERO_RESIDUAL);
+ *   - the walk stops at a leaf (final token from p_leaf) or at a node all of
+ *     whose children were rejected (final token from the last residual
+ *     max(0, r - q_u), drawn from the unnormalised weights as in plain SD);
+ *   - uniforms[node_off[b] + n], n >= 1: acceptance uniform of node n;
+ *     uniforms[node_off[b]] (the root's slot): the final draw's uniform.
+ * A chain (every node has one child) is plain SD with K_b = M_b - 1.
+ * ------------------------------------------------------------------------ */
+
+/* Draft row of each node of tree b (-1 for leaves); returns the number of
+ * nodes with children, or -1 when the parents are not a tree in this order. */
+static int64_t tree_draft_rows(const int32_t* par, int M, int64_t d0, int64_t* drow) {
+  for (int n = 0; n < M; n++) drow[n] = -1;
+  for (int n = 1; n < M; n++) {
+    if (par[n] < 0 || par[n] >= n) return -1;
+    drow[par[n]] = 0;
+  }
+  if (M > 0 && par[0] != -1) return -1;
+  int64_t k = 0;
+  for (int n = 0; n < M; n++)
+    if (drow[n] == 0) drow[n] = d0 + k++;
+  return k;
+}
+
+/*
+ * One rejection: w = max(0, r - q) elementwise, Z = its total (index order),
+ * r <- w / Z.  When Z is 0 (r and q agree), r stays, w = r and ZERO_RESIDUAL
+ * is raised.
+ */
+static void residual_step(double* r, const double* q, double* w, int64_t V, uint32_t* fl) {
+  double Z = 0.0;
+  for (int64_t i = 0; i < V; i++) {
+    w[i] = r[i] - q[i] > 0.0 ? r[i] - q[i] : 0.0;
+    Z += w[i];
+  }
+  if (Z > 0.0) {
+    for (int64_t i = 0; i < V; i++) r[i] = w[i] / Z;
+  } else {
+    *fl |= ORACLE_FLAG_ZERO_RESIDUAL;
+    for (int64_t i = 0; i < V; i++) w[i] = r[i];
+  }
+}
+
+/*
+ * The residual chain at node u: r starts as p_u (and q as q_u when u has a
+ * draft row); then the first nrej children of u in order (nrej < 0: all of
+ * them) are rejected, each turning r into max(0, r - q_u) / Z.  Leaves w = the
+ * weights of the final draw if the walk stops at u after those rejections
+ * (p_u before any; then the last rejection's max(0, r - q_u), or r when its
+ * mass is 0) and r = the running distribution.
+ */
+static void tree_residual(int dtype, int64_t V, double T, const void* trow, const void* drow,
+                          const int32_t* par, int M, int u, int nrej, double* r, double* q, double* w,
+                          uint32_t* fl) {
+  double Mt, lSt;
+  if (oracle_row_stats(dtype, trow, V, T, &Mt, &lSt)) *fl |= ORACLE_FLAG_NONFINITE;
+  for (int64_t i = 0; i < V; i++) r[i] = exp(logprob_with(dtype, trow, i, T, Mt, lSt));
+  for (int64_t i = 0; i < V; i++) w[i] = r[i];
+  if (!drow) return;
+  double Md, lSd;
+  if (oracle_row_stats(dtype, drow, V, T, &Md, &lSd)) *fl |= ORACLE_FLAG_NONFINITE;
+  for (int64_t i = 0; i < V; i++) q[i] = exp(logprob_with(dtype, drow, i, T, Md, lSd));
+  int done = 0;
+  for (int c = u + 1; c < M && (nrej < 0 || done < nrej); c++) {
+    if (par[c] != u) continue;
+    residual_step(r, q, w, V, fl);
+    done++;
+  }
+}
+
+/*
+ * Verify B token trees.  Outputs per tree: num_accepted (depth of the node
+ * where the walk stopped), last_node (its local index) and final_token.
+ * accept_margin[node_off[b] + n] (optional): |u_n - min(1, ratio)| for every
+ * child n that was tested, -1 for the others (and the root);
+ * sample_margin[b] (optional): margin of the final draw.
+ * Returns 0, or -1 (nothing written for that tree) when a tree's parents are
+ * not in tree order or its number of nodes with children differs from
+ * draft_off[b+1] - draft_off[b].
+ */
+int oracle_tree_verify(int dtype, int B, int64_t V, double T, const int32_t* node_off,
+                       const int32_t* draft_off, const int32_t* parent, const int32_t* tokens,
+                       const void* target, const void* draft, const float* uniforms,
+                       int32_t* num_accepted, int32_t* last_node, int32_t* final_token, uint32_t* flags,
+                       double* accept_margin, double* sample_margin) {
+  size_t nv = (size_t)(V > 0 ? V : 1);
+  double* r = (double*)malloc(sizeof(double) * nv);
+  double* q = (double*)malloc(sizeof(double) * nv);
+  double* w = (double*)malloc(sizeof(double) * nv);
+  uint32_t fl = 0;
+  int ret = 0;
+  for (int b = 0; b < B; b++) {
+    int64_t n0 = node_off[b];
+    int M = node_off[b + 1] - node_off[b];
+    const int32_t* par = parent + n0;
+    int64_t* drow = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    if (M < 1 || tree_draft_rows(par, M, draft_off[b], drow) != draft_off[b + 1] - draft_off[b]) {
+      free(drow);
+      ret = -1;
+      continue;
+    }
+    if (accept_margin)
+      for (int n = 0; n < M; n++) accept_margin[n0 + n] = -1.0;
+    int u = 0, depth = 0;
+    for (;;) {
+      const void* trow = row_ptr(dtype, target, n0 + u, V);
+      const void* dr = drow[u] >= 0 ? row_ptr(dtype, draft, drow[u], V) : NULL;
+      /* start of the residual chain at u: r = p_u, q = q_u */
+      tree_residual(dtype, V, T, trow, dr, par, M, u, 0, r, q, w, &fl);
+      if (!dr) break; /* a leaf: the final token comes from p_u (w) */
+      int next = -1;
+      for (int c = u + 1; c < M; c++) {
+        if (par[c] != u) continue;
+        int32_t x = tokens[n0 + c];
+        /* a token outside the vocabulary is rejected */
+        double ratio = x >= 0 && x < V ? r[x] / q[x] : 0.0;
+        double uc = (double)uniforms[n0 + c];
+        if (accept_margin) accept_margin[n0 + c] = fabs(uc - (ratio < 1.0 ? ratio : 1.0));
+        if (uc < ratio) {
+          next = c;
+          break;
+        }
+        residual_step(r, q, w, V, &fl);
+      }
+      if (next < 0) break; /* every child rejected: final token from w */
+      u = next;
+      depth++;
+    }
+    num_accepted[b] = depth;
+    last_node[b] = u;
+    double m = 0.0;
+    final_token[b] = (int32_t)inverse_cdf(w, V, (double)uniforms[n0], &m, &fl);
+    if (sample_margin) sample_margin[b] = m;
+    free(drow);
+  }
+  free(r);
+  free(q);
+  free(w);
+  if (flags) *flags |= fl;
+  return ret;
+}
+
+/*
+ * Normalised CDF of the distribution tree b's final token is drawn from when
+ * the walk stops at node u (every child of u rejected, or u a leaf).  Used by
+ * the comparison to judge a differing token against the decision band.
+ * Returns the flags raised, or -1 for a malformed tree.
+ */
+int oracle_tree_final_cdf(int dtype, int b, int64_t V, double T, const int32_t* node_off,
+                          const int32_t* draft_off, const int32_t* parent, const void* target,
+                          const void* draft, int u, double* cdf) {
+  int64_t n0 = node_off[b];
+  int M = node_off[b + 1] - node_off[b];
+  const int32_t* par = parent + n0;
+  if (M < 1 || u < 0 || u >= M) return -1;
+  int64_t* drow = (int64_t*)malloc(sizeof(int64_t) * (size_t)M);
+  if (tree_draft_rows(par, M, draft_off[b], drow) != draft_off[b + 1] - draft_off[b]) {
+    free(drow);
+    return -1;
+  }
+  size_t nv = (size_t)(V > 0 ? V : 1);
+  double* r = (double*)malloc(sizeof(double) * nv);
+  double* q = (double*)malloc(sizeof(double) * nv);
+  uint32_t fl = 0;
+  const void* dr = drow[u] >= 0 ? row_ptr(dtype, draft, drow[u], V) : NULL;
+  tree_residual(dtype, V, T, row_ptr(dtype, target, n0 + u, V), dr, par, M, u, -1, r, q, cdf, &fl);
+  double Z = 0.0;
+  for (int64_t i = 0; i < V; i++) Z += cdf[i];
+  double C = 0.0;
+  for (int64_t i = 0; i < V; i++) {
+    C += cdf[i];
+    cdf[i] = C / Z;
+  }
+  free(drow);
+  free(r);
+  free(q);
+  return (int)fl;
+}

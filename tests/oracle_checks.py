@@ -741,7 +741,294 @@ def check_pacer_law(lib):
         assert abs(f - p[m]) < 5 * math.sqrt(p[m] * (1 - p[m]) / B), (m, f, p[m])
 
 
+# --------------------------------------------------------------------------
+# tree verification (multi-draft speculative sampling over a token tree)
+# --------------------------------------------------------------------------
+
+
+def _pack_trees(trees):
+    """Concatenate per-tree dicts (parent, tokens, target [M, V], draft [D, V],
+    uniforms [M]) into the CSR layout of oracle.tree_verify."""
+    node_off, draft_off = [0], [0]
+    for t in trees:
+        node_off.append(node_off[-1] + len(t["parent"]))
+        draft_off.append(draft_off[-1] + len(t["draft"]))
+    V = trees[0]["target"].shape[-1]
+    dt = trees[0]["target"].dtype
+    cat = lambda k, w: np.concatenate([np.asarray(t[k]) for t in trees]) if trees else np.zeros((0,) * w)
+    draft = np.concatenate([t["draft"] for t in trees]) if draft_off[-1] else np.zeros((0, V), dt)
+    return dict(node_off=np.array(node_off, np.int32), draft_off=np.array(draft_off, np.int32),
+                parent=cat("parent", 1).astype(np.int32), tokens=cat("tokens", 1).astype(np.int32),
+                target=np.concatenate([t["target"] for t in trees]), draft=draft,
+                uniforms=cat("uniforms", 1).astype(np.float32))
+
+
+def _tree_run(lib, packed, T):
+    return oracle.tree_verify(packed["target"], packed["draft"], packed["node_off"], packed["draft_off"],
+                              packed["parent"], packed["tokens"], packed["uniforms"], T, lib=lib)
+
+
+def check_golden_tree(lib):
+    g = _load_golden("tree_verify.json")
+    trees = []
+    for case in g["cases"]:
+        t = g["trees"][case["tree"]]
+        trees.append(dict(parent=t["parent"], tokens=t["tokens"], target=_logits(t["target_probs"]),
+                          draft=_logits(t["draft_probs"]), uniforms=case["uniforms"]))
+    r = _tree_run(lib, _pack_trees(trees), g["T"])
+    got = np.stack([r["num_accepted"], r["last_node"], r["final_token"]], axis=1).tolist()
+    assert r["status"] == 0 and got == [c["expect"] for c in g["cases"]], got
+
+
+def check_tree_chain_is_sd(lib):
+    """A chain (every node one child) is plain SD with K_b = M_b - 1: same
+    accepted counts and final tokens, bit for bit, for every chain length."""
+    rng = np.random.default_rng(41)
+    for K, V, T, delta in ((1, 50, 1.0, 1.0), (3, 300, 0.8, 1.5), (6, 97, 1.2, 0.7), (0, 40, 1.0, 1.0)):
+        B = 64
+        zt, zd, tok, u = rand_sd_problem(rng, B, K, V, T, delta)
+        ref = oracle.sd_verify(zt, zd, tok, u, T, K=K, lib=lib)
+        trees = []
+        for b in range(B):
+            ub = u[b * (K + 1):(b + 1) * (K + 1)]
+            trees.append(dict(parent=np.arange(-1, K), tokens=np.concatenate([[0], tok[b * K:(b + 1) * K]]),
+                              target=zt[b * (K + 1):(b + 1) * (K + 1)], draft=zd[b * K:(b + 1) * K],
+                              uniforms=np.concatenate([[ub[K]], ub[:K]])))
+        r = _tree_run(lib, _pack_trees(trees), T)
+        assert r["status"] == 0
+        assert (r["num_accepted"] == ref["num_accepted"]).all(), (K, r["num_accepted"], ref["num_accepted"])
+        assert (r["last_node"] == ref["num_accepted"]).all()
+        assert (r["final_token"] == ref["final_token"]).all(), (K, r["final_token"], ref["final_token"])
+
+
+def check_tree_star_exact_law(lib):
+    """A root with k children drawn iid from q (k = 2, 3), each child a leaf
+    whose row depends only on its token.  Integrating the oracle's decisions
+    exactly over the child tokens and all uniforms: the first emitted token
+    follows p_root, and after an accepted child with token x the next token
+    follows that child's row -- multi-draft speculative sampling is exact
+    only with the residual renormalised after every rejection."""
+    import itertools
+
+    rng = np.random.default_rng(43)
+    for V, k, T, delta in ((3, 2, 1.0, 1.5), (4, 3, 0.8, 1.0), (4, 2, 1.0, 0.3)):
+        zt0 = (2 * rng.standard_normal(V)).astype(np.float32)
+        zd0 = (zt0 + delta * rng.standard_normal(V)).astype(np.float32)
+        child_rows = (2 * rng.standard_normal((V, V))).astype(np.float32)  # row of a child with token x
+        p0 = softmax(zt0.astype(np.float64) / T)
+        q0 = softmax(zd0.astype(np.float64) / T)
+        pc = softmax(child_rows.astype(np.float64) / T, axis=-1)
+        # Breakpoints of the uniforms: for child tokens xs, the acceptance
+        # thresholds of the children and every CDF edge of every final
+        # distribution; between consecutive breakpoints the oracle's decisions
+        # are constant, so one midpoint per interval, weighted by its length,
+        # integrates them exactly.  (The thresholds are computed here only to
+        # place the midpoints; the assertions are the laws below.)
+        def chains(xs):
+            rr = p0.copy()
+            out = []
+            for x in xs:
+                out.append(min(1.0, rr[x] / q0[x]))
+                w = np.maximum(0.0, rr - q0)
+                rr = w / w.sum() if w.sum() > 0 else rr
+            return out, np.cumsum(rr)
+        law0 = np.zeros(V)
+        law1 = np.zeros((V, V))
+        acc_mass = np.zeros(V)
+        for xs in itertools.product(range(V), repeat=k):
+            wx = float(np.prod([q0[x] for x in xs]))
+            thr, cres = chains(xs)
+            grids = []
+            for j in range(k):
+                e = sorted({0.0, 1.0, thr[j]})
+                grids.append([(0.5 * (a + b), b - a) for a, b in zip(e[:-1], e[1:]) if b - a > 1e-12])
+            fe = sorted(set(np.concatenate([[0.0], cres, np.cumsum(pc, axis=-1).ravel(), [1.0]]).tolist()))
+            fgrid = [(0.5 * (a + b), b - a) for a, b in zip(fe[:-1], fe[1:]) if b - a > 1e-9]
+            trees, weights = [], []
+            for combo in itertools.product(*grids):
+                for uf, lf in fgrid:
+                    trees.append(dict(parent=[-1] + [0] * k, tokens=[0] + list(xs),
+                                      target=np.concatenate([zt0[None], child_rows[list(xs)]]), draft=zd0[None],
+                                      uniforms=[uf] + [c[0] for c in combo]))
+                    weights.append(wx * lf * float(np.prod([c[1] for c in combo])))
+            res = _tree_run(lib, _pack_trees(trees), T)
+            assert res["status"] == 0
+            for t, w_, (na, ln, ft) in zip(trees, weights, zip(res["num_accepted"], res["last_node"],
+                                                              res["final_token"])):
+                if na == 0:
+                    law0[ft] += w_
+                else:
+                    x = t["tokens"][ln]
+                    law0[x] += w_
+                    law1[x, ft] += w_
+                    acc_mass[x] += w_
+        assert abs(law0.sum() - 1.0) < 1e-9, law0.sum()
+        assert np.abs(law0 - p0).max() < 1e-7, (V, k, law0, p0)
+        for x in range(V):
+            if acc_mass[x] > 1e-6:
+                assert np.abs(law1[x] / acc_mass[x] - pc[x]).max() < 1e-7, (V, k, x, law1[x] / acc_mass[x], pc[x])
+
+
+def check_tree_accept_tie(lib):
+    """r(x)/q(x) = 0.5 exactly for the first child (p = (1/2, 1/2), q = (1, 0))
+    and u = 0.5: the strict test rejects it, the residual (0, 1) then accepts
+    the second child; just below 0.5 the first child is accepted."""
+    target = np.zeros((3, 2), np.float32)
+    draft = np.array([[0.0, -np.inf]], np.float32)
+    for u1, want in ((0.5, 2), (float(np.nextafter(np.float32(0.5), np.float32(0))), 1)):
+        r = _tree_run(lib, _pack_trees([dict(parent=[-1, 0, 0], tokens=[0, 0, 1], target=target, draft=draft,
+                                             uniforms=[0.3, u1, 0.9])]), 1.0)
+        assert r["last_node"].tolist() == [want], (u1, r)
+
+
+def check_tree_identical_rows(lib):
+    """Draft rows equal to the target rows make every ratio 1: the first child
+    is always accepted, so the walk follows first children to a leaf and the
+    final token is the inverse-CDF draw from that leaf's row (numpy)."""
+    rng = np.random.default_rng(47)
+    V, T = 211, 0.9
+    trees = []
+    for b in range(40):
+        M = int(rng.integers(1, 12))
+        par = [-1] + [int(rng.integers(0, n)) for n in range(1, M)]
+        zt = (3 * rng.standard_normal((M, V))).astype(np.float32)
+        internal = sorted({p for p in par[1:]})
+        trees.append(dict(parent=par, tokens=[0] + rng.integers(0, V, M - 1).tolist(), target=zt,
+                          draft=zt[internal] if internal else np.zeros((0, V), np.float32),
+                          uniforms=rng.random(M).astype(np.float32)))
+    r = _tree_run(lib, _pack_trees(trees), T)
+    assert r["status"] == 0
+    for b, t in enumerate(trees):
+        u, depth = 0, 0
+        while True:
+            kids = [c for c in range(len(t["parent"])) if t["parent"][c] == u]
+            if not kids:
+                break
+            u, depth = kids[0], depth + 1
+        assert r["last_node"][b] == u and r["num_accepted"][b] == depth, (b, r["last_node"][b], u)
+        p = softmax(t["target"][u].astype(np.float64) / T)
+        c = np.cumsum(p)
+        uf = float(t["uniforms"][0])
+        if np.min(np.abs(c / c[-1] - uf)) > 1e-12:
+            assert r["final_token"][b] == int(np.searchsorted(c, uf * c[-1], side="right"))
+
+
+def check_tree_root_only(lib):
+    """Trees of one node: the final token is the inverse-CDF draw from the root's
+    row (numpy searchsorted), nothing is accepted."""
+    rng = np.random.default_rng(53)
+    V, T = 333, 1.1
+    zt = (3 * rng.standard_normal((30, V))).astype(np.float32)
+    u = rng.random(30).astype(np.float32)
+    trees = [dict(parent=[-1], tokens=[0], target=zt[i:i + 1], draft=np.zeros((0, V), np.float32), uniforms=[u[i]])
+             for i in range(30)]
+    r = _tree_run(lib, _pack_trees(trees), T)
+    assert (r["num_accepted"] == 0).all() and (r["last_node"] == 0).all()
+    for i in range(30):
+        c = np.cumsum(softmax(zt[i].astype(np.float64) / T))
+        if np.min(np.abs(c / c[-1] - u[i])) > 1e-12:
+            assert r["final_token"][i] == int(np.searchsorted(c, u[i] * c[-1], side="right"))
+
+
+def check_tree_malformed(lib):
+    """Parents out of tree order, or a draft-row count that disagrees with the
+    nodes that have children, are refused."""
+    V = 8
+    z = np.zeros((3, V), np.float32)
+    for par, nd in (([-1, 1, 0], 1), ([0, 0, 0], 1), ([-1, 0, 0], 2), ([-1, 0, 1], 1)):
+        r = _tree_run(lib, _pack_trees([dict(parent=par, tokens=[0, 1, 2], target=z, draft=z[:nd],
+                                             uniforms=[0.5, 0.5, 0.5])]), 1.0)
+        assert r["status"] == -1, (par, nd)
+
+
+def check_tree_final_cdf(lib):
+    """The CDF the comparison judges a differing final token against: p_u at a
+    leaf; after every child of u is rejected, the last max(0, r - q) of the
+    chain r <- max(0, r - q) / Z (numpy)."""
+    rng = np.random.default_rng(59)
+    V, T = 97, 0.8
+    par = [-1, 0, 0, 0, 1, 1]
+    zt = (2 * rng.standard_normal((6, V))).astype(np.float32)
+    zd = (zt[[0, 1]] + rng.standard_normal((2, V))).astype(np.float32)
+    pk = _pack_trees([dict(parent=par, tokens=[0, 1, 2, 3, 4, 5], target=zt, draft=zd, uniforms=np.zeros(6))])
+    for u, drow, k in ((0, 0, 3), (1, 1, 2), (2, None, 0), (5, None, 0)):
+        cdf, fl = oracle.tree_final_cdf(pk["target"], pk["draft"], pk["node_off"], pk["draft_off"], pk["parent"],
+                                        0, u, T, lib=lib)
+        r = softmax(zt[u].astype(np.float64) / T)
+        w = r
+        if drow is not None:
+            q = softmax(zd[drow].astype(np.float64) / T)
+            for _ in range(k):
+                w = np.maximum(0.0, r - q)
+                r = w / w.sum()
+        want = np.cumsum(w) / w.sum()
+        assert fl == 0 and np.abs(cdf - want).max() < 1e-12, (u, np.abs(cdf - want).max())
+
+
+def check_tree_statistics(lib, trials=100_000):
+    """Chi-square on a depth-2 tree (root with 2 children, each with 2
+    children), children drawn iid from their parent's draft row and every
+    row a function of its token path: the first emitted token follows p_root,
+    and after an accepted first-level child with token x the second emitted
+    token follows that child's row."""
+    from scipy.stats import chisquare
+
+    rng = np.random.default_rng(61)
+    V, T = 5, 1.0
+    root = (1.5 * rng.standard_normal(V)).astype(np.float32)
+    lvl1 = (1.5 * rng.standard_normal((V, V))).astype(np.float32)     # row after token x
+    lvl2 = (1.5 * rng.standard_normal((V, V, V))).astype(np.float32)  # row after tokens x, y
+    droot = (root + rng.standard_normal(V)).astype(np.float32)
+    dl1 = (lvl1 + rng.standard_normal((V, V))).astype(np.float32)
+    B = trials
+    qr = softmax(droot.astype(np.float64) / T)
+    x = rng.choice(V, size=(B, 2), p=qr)
+    ql1 = softmax(dl1.astype(np.float64) / T, axis=-1)
+    u2 = rng.random((B, 2, 2))  # second-level children: inverse CDF of q at their parent
+    y = np.empty((B, 2, 2), np.int64)
+    for a in range(2):
+        c = np.cumsum(ql1[x[:, a]], axis=-1)
+        for s2 in range(2):
+            y[:, a, s2] = np.minimum((c < u2[:, a, s2:s2 + 1] * c[:, -1:]).sum(-1), V - 1)
+    par = np.array([-1, 0, 0, 1, 1, 2, 2], np.int32)
+    tok = np.stack([np.zeros(B, np.int64), x[:, 0], x[:, 1], y[:, 0, 0], y[:, 0, 1], y[:, 1, 0], y[:, 1, 1]], 1)
+    target = np.stack([np.broadcast_to(root, (B, V)), lvl1[x[:, 0]], lvl1[x[:, 1]], lvl2[x[:, 0], y[:, 0, 0]],
+                       lvl2[x[:, 0], y[:, 0, 1]], lvl2[x[:, 1], y[:, 1, 0]], lvl2[x[:, 1], y[:, 1, 1]]], 1)
+    draft = np.stack([np.broadcast_to(droot, (B, V)), dl1[x[:, 0]], dl1[x[:, 1]]], 1)
+    pk = dict(node_off=np.arange(0, 7 * B + 1, 7, dtype=np.int32), draft_off=np.arange(0, 3 * B + 1, 3, dtype=np.int32),
+              parent=np.tile(par, B), tokens=tok.astype(np.int32).ravel(), target=target.reshape(7 * B, V),
+              draft=draft.reshape(3 * B, V), uniforms=rng.random(7 * B).astype(np.float32))
+    r = _tree_run(lib, pk, T)
+    assert r["status"] == 0
+    ln, na, ft = r["last_node"], r["num_accepted"], r["final_token"]
+    first = np.where(na >= 1, tok[np.arange(B), np.where(ln >= 3, par[ln], ln)], ft)
+    pr = softmax(root.astype(np.float64) / T)
+    stat = chisquare(np.bincount(first, minlength=V), pr * B)
+    assert stat.pvalue > 1e-4, stat
+    # the second emitted token after an accepted first-level child with token x0
+    reach = na >= 1
+    x0 = tok[np.arange(B), np.where(ln >= 3, par[ln], ln)]
+    second = np.where(na >= 2, tok[np.arange(B), ln], ft)
+    for xv in range(V):
+        sel = reach & (x0 == xv)
+        if sel.sum() < 2000:
+            continue
+        pxv = softmax(lvl1[xv].astype(np.float64) / T)
+        cnt = np.bincount(second[sel], minlength=V)
+        keep = pxv * sel.sum() > 5
+        st = chisquare(cnt[keep], pxv[keep] * cnt[keep].sum() / pxv[keep].sum())
+        assert st.pvalue > 1e-4, (xv, st)
+
+
 DETERMINISTIC_CHECKS = [
+    check_golden_tree,
+    check_tree_chain_is_sd,
+    check_tree_star_exact_law,
+    check_tree_accept_tie,
+    check_tree_identical_rows,
+    check_tree_root_only,
+    check_tree_malformed,
+    check_tree_final_cdf,
     check_golden_sd_fixed,
     check_golden_sd_csr,
     check_golden_smc,

@@ -64,6 +64,18 @@ MUTATIONS = [
     ("pacer_stopping_block_dropped", "lengths[b] = block * m;", "lengths[b] = block * (m - 1);"),
     ("pacer_offsets_not_accumulated", "offsets[b + 1] = offsets[b] + lengths[b];", "offsets[b + 1] = lengths[b];"),
     ("pacer_block_offset", "sum += (double)s[(int64_t)(m - 1) * block + k];", "sum += (double)s[(int64_t)m * block + k];"),
+    ("tree_residual_not_renormalised", "for (int64_t i = 0; i < V; i++) r[i] = w[i] / Z;",
+     "for (int64_t i = 0; i < V; i++) r[i] = w[i];"),
+    ("tree_residual_is_r", "w[i] = r[i] - q[i] > 0.0 ? r[i] - q[i] : 0.0;", "w[i] = r[i];"),
+    ("tree_ratio_inverted", "double ratio = x >= 0 && x < V ? r[x] / q[x] : 0.0;",
+     "double ratio = x >= 0 && x < V ? q[x] / r[x] : 0.0;"),
+    ("tree_accept_non_strict", "if (uc < ratio) {", "if (uc <= ratio) {"),
+    ("tree_keeps_testing_after_accept", "          next = c;\n          break;", "          next = c;"),
+    ("tree_final_uniform_of_node", "(double)uniforms[n0], &m, &fl);", "(double)uniforms[n0 + u], &m, &fl);"),
+    ("tree_draft_row_not_advanced", "if (drow[n] == 0) drow[n] = d0 + k++;", "if (drow[n] == 0) { drow[n] = d0; k++; }"),
+    ("tree_depth_not_counted", "      u = next;\n      depth++;", "      u = next;"),
+    ("tree_row_of_root", "const void* trow = row_ptr(dtype, target, n0 + u, V);",
+     "const void* trow = row_ptr(dtype, target, n0, V);"),
 ]
 
 

@@ -17,3 +17,8 @@ def test_sd_output_law_chi_square(orc):
 
 def test_expected_accepted_length(orc):
     oc.check_expected_length(orc, trials=1_000_000)
+
+
+def test_tree_output_law_chi_square(orc):
+    """Tree verification's emitted tokens follow the target (chi-square, depth-2 tree)."""
+    oc.check_tree_statistics(orc, trials=200_000)
