@@ -383,6 +383,64 @@ int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, con
 int32_t pacer_lengths(int32_t B, int32_t block, int32_t max_blocks, double t0, double rho, const float* scores,
                       int32_t* lengths, int32_t* offsets, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Tree verification.
+ * ------------------------------------------------------------------------ */
+
+#define SMCSD_TREE_MAX_NODES 256 /* largest token tree (nodes, root included) */
+
+/*
+ * Verify B token trees ("Faster LLM Inference via Sequential Monte Carlo",
+ * sec. 4: SMC-SD is measured against tree-based speculative decoding; the
+ * pages give no algorithm for verifying a tree, and this is multi-draft
+ * speculative sampling, the textbook way to check several draft
+ * continuations against one target distribution):
+ *   at node u the running distribution r starts as p_u; the children of u
+ *   are tried in increasing node index, child c (token x_c) accepted iff
+ *   u_c < r(x_c) / q_u(x_c) (strict), and the walk moves to c; a rejection
+ *   turns r into max(0, r - q_u) / Z, Z its total (if Z is 0, r stays and
+ *   SMCSD_FLAG_ZERO_RESIDUAL is raised).  The walk stops at a leaf (final
+ *   token drawn from p_leaf) or at a node whose children were all rejected
+ *   (final token drawn from the last max(0, r - q_u)).  A chain of K+1 nodes
+ *   is sd_verify with K draft tokens, decision for decision.
+ * Layout (all device memory, caller-owned):
+ *   node_offsets   int32 [B+1]: tree b owns nodes node_offsets[b] ..
+ *                  node_offsets[b+1]-1 (1 <= M_b <= SMCSD_TREE_MAX_NODES),
+ *                  node_offsets[0] = 0, node_offsets[B] = num_nodes.
+ *   parent         int32 [num_nodes]: local index of each node's parent;
+ *                  -1 for node 0 (the root, the last committed token), and
+ *                  0 <= parent < n for every other node n.
+ *   tokens         int32 [num_nodes]: the draft token of each node (the
+ *                  root's entry is not read).
+ *   target_logits  [num_nodes, V]: row node_offsets[b] + n holds the target's
+ *                  logits after the path root .. n.
+ *   draft_offsets  int32 [B+1]: tree b owns draft rows draft_offsets[b] ..
+ *                  draft_offsets[b+1]-1, one per node with at least one
+ *                  child, in node order (the draft logits its children were
+ *                  drawn from); draft_offsets[B] = num_draft_rows.
+ *   draft_logits   [num_draft_rows, V].
+ *   uniforms       float [num_nodes]: entry node_offsets[b] + n (n >= 1) is
+ *                  node n's acceptance uniform; the root's entry is the final
+ *                  draw's uniform.
+ *   num_accepted   int32 [B] out: depth of the node where the walk stopped
+ *                  (the accepted tokens are those of the path root .. it).
+ *   last_node      int32 [B] out: local index of that node.
+ *   final_token    int32 [B] out: the token drawn there.
+ * Workspace: tree_verify_workspace_bytes(...) bytes, as for sd_verify.
+ * Errors: SMCSD_ERR_INVALID_ARG for bad sizes, pointers or temperature;
+ * SMCSD_ERR_UNSUPPORTED for V > SMCSD_MAX_V.  A tree whose offsets, parents
+ * or draft-row count disagree with the rules above raises
+ * SMCSD_FLAG_BAD_INPUT and its outputs are unspecified; a token outside
+ * [0, V) is a rejection and raises SMCSD_FLAG_BAD_INPUT; flags otherwise as
+ * for sd_verify.
+ */
+size_t tree_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t V, int64_t num_nodes, int64_t num_draft_rows);
+int32_t tree_verify(int32_t dtype, int32_t B, int32_t V, float temperature, const int32_t* node_offsets,
+                    const int32_t* parent, const int32_t* tokens, int64_t num_nodes, const void* target_logits,
+                    const int32_t* draft_offsets, int64_t num_draft_rows, const void* draft_logits,
+                    const float* uniforms, int32_t* num_accepted, int32_t* last_node, int32_t* final_token,
+                    uint32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

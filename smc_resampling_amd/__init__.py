@@ -20,6 +20,7 @@ __all__ = [
     "FLAG_PAGES_FULL", "FLAG_PAGES_EXHAUSTED",
     "new_workspace", "time_next_call", "smc_pages_workspace_bytes", "smc_pages_append", "smc_pages_resample",
     "draft_sample_workspace_bytes", "prepare_draft_sample", "draft_sample", "pacer_lengths",
+    "tree_verify_workspace_bytes", "prepare_tree_verify", "tree_verify", "TREE_MAX_NODES",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ SMCSD_F32, SMCSD_BF16 = 0, 1
 FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT = 1, 2, 4, 8, 16
 FLAG_PAGES_FULL, FLAG_PAGES_EXHAUSTED = 32, 64
 WORKSPACE_ALIGN = 256
+TREE_MAX_NODES = 256
 
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -47,6 +49,9 @@ _SIGNATURES = {
     "draft_sample_workspace_bytes": ([_I32, _I32, _I32], _SZ),
     "draft_sample": ([_I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "pacer_lengths": ([_I32, _I32, _I32, ctypes.c_double, ctypes.c_double, _P, _P, _P, _P], _I32),
+    "tree_verify_workspace_bytes": ([_I32, _I32, _I32, _I64, _I64], _SZ),
+    "tree_verify": ([_I32, _I32, _I32, _F, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+                    _I32),
     "smc_pages_workspace_bytes": ([_I32, _I32, _I32, _I64], _SZ),
     "smc_pages_append": ([_I32, _I32, _I32, _I32, _I32, _I64] + [_P] * 10 + [_SZ, _P], _I32),
     "smc_pages_resample": ([_I32, _I32, _I32, _I32, _I64] + [_P] * 9 + [_SZ, _P], _I32),
@@ -363,3 +368,58 @@ def pacer_lengths(scores, block, max_blocks, t0, rho, *, lengths=None, offsets=N
     _check(_lib.pacer_lengths(B, block, max_blocks, float(t0), float(rho), _ptr(scores), _ptr(lengths),
                               _ptr(offsets), stream if stream is not None else _stream(dev)))
     return dict(lengths=lengths, offsets=offsets)
+
+
+def tree_verify_workspace_bytes(dtype_code, B, V, num_nodes, num_draft_rows) -> int:
+    return _lib.tree_verify_workspace_bytes(dtype_code, B, V, num_nodes, num_draft_rows)
+
+
+def prepare_tree_verify(target_logits, draft_logits, node_offsets, draft_offsets, parent, tokens, uniforms,
+                        temperature, *, num_accepted=None, last_node=None, final_token=None, status_flags=None,
+                        workspace=None, stream=None):
+    """Validate and marshal one tree_verify call; returns (call, outputs).
+
+    target [num_nodes, V] (one row per tree node), draft [num_draft_rows, V]
+    (one row per node with children, node order), node_offsets / draft_offsets
+    int32 [B+1], parent / tokens int32 [num_nodes] (local parent, -1 at the
+    root), uniforms float32 [num_nodes] (the root's slot: the final draw)."""
+    dev = target_logits.device
+    dt = _dtype_code(target_logits)
+    V = target_logits.shape[-1]
+    nodes = target_logits.shape[0]
+    rows_d = draft_logits.shape[0] if draft_logits is not None else 0
+    B = node_offsets.numel() - 1
+    for t, d, n in ((target_logits, target_logits.dtype, "target_logits"), (draft_logits, target_logits.dtype,
+                    "draft_logits"), (node_offsets, torch.int32, "node_offsets"), (draft_offsets, torch.int32,
+                    "draft_offsets"), (parent, torch.int32, "parent"), (tokens, torch.int32, "tokens"),
+                    (uniforms, torch.float32, "uniforms")):
+        _need(t, d, n)
+    mk = lambda n, d: torch.empty(n, dtype=d, device=dev)  # noqa: E731
+    num_accepted = num_accepted if num_accepted is not None else mk(B, torch.int32)
+    last_node = last_node if last_node is not None else mk(B, torch.int32)
+    final_token = final_token if final_token is not None else mk(B, torch.int32)
+    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+    nbytes = tree_verify_workspace_bytes(dt, B, V, nodes, rows_d)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    st = stream if stream is not None else _stream(dev)
+    args = (dt, B, V, float(temperature), _ptr(node_offsets), _ptr(parent), _ptr(tokens), nodes, _ptr(target_logits),
+            _ptr(draft_offsets), rows_d, _ptr(draft_logits), _ptr(uniforms), _ptr(num_accepted), _ptr(last_node),
+            _ptr(final_token), _ptr(status_flags), _ptr(ws), wsb, st)
+    fn = _lib.tree_verify
+    keep = (target_logits, draft_logits, node_offsets, draft_offsets, parent, tokens, uniforms, ws)
+
+    def call():
+        _check(fn(*args))
+        return keep
+
+    return call, dict(num_accepted=num_accepted, last_node=last_node, final_token=final_token,
+                      status_flags=status_flags)
+
+
+def tree_verify(target_logits, draft_logits, node_offsets, draft_offsets, parent, tokens, uniforms, temperature,
+                **kw):
+    """Tree verification; returns dict(num_accepted, last_node, final_token, status_flags)."""
+    call, out = prepare_tree_verify(target_logits, draft_logits, node_offsets, draft_offsets, parent, tokens,
+                                    uniforms, temperature, **kw)
+    call()
+    return out

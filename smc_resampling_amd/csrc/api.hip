@@ -50,6 +50,17 @@ SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   return l;
 }
 
+// Token trees: every target row (node) and draft row is a group of its own,
+// so each has segment partials and, with multi-tile segments, tile partials.
+SdLayout tree_layout(int64_t rows, int64_t V) {
+  const int nt = ntiles_of(V);
+  SdLayout l;
+  l.part = kCounterBytes;
+  l.tpart = align_up(l.part + sizeof(float2) * (size_t)(rows * nt));
+  l.total = align_up(l.tpart + sizeof(float2) * (size_t)(rows * nt));
+  return l;
+}
+
 struct SmcLayout {
   size_t ws_logw, part, tpart, total;
 };
@@ -100,6 +111,7 @@ void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, 
   s->tpart = reinterpret_cast<float2*>(ws + tpart_off);
   s->ctr = reinterpret_cast<uint32_t*>(ws);
   s->flags = flags;
+  s->flat = 0;
 }
 
 
@@ -199,6 +211,57 @@ int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, con
   a.num_accepted = nullptr;
   a.final_token = tokens;
   return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
+             ? SMCSD_OK
+             : SMCSD_ERR_HIP;
+}
+
+size_t tree_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t V, int64_t num_nodes, int64_t num_draft_rows) {
+  (void)dtype;
+  if (B <= 0 || V <= 0 || num_nodes < B || num_draft_rows < 0) return 0;
+  return tree_layout(num_nodes + num_draft_rows, V).total;
+}
+
+int32_t tree_verify(int32_t dtype, int32_t B, int32_t V, float temperature, const int32_t* node_offsets,
+                    const int32_t* parent, const int32_t* tokens, int64_t num_nodes, const void* target_logits,
+                    const int32_t* draft_offsets, int64_t num_draft_rows, const void* draft_logits,
+                    const float* uniforms, int32_t* num_accepted, int32_t* last_node, int32_t* final_token,
+                    uint32_t* status_flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_INVALID_ARG;
+  if (B < 0 || V < 1 || !temperature_ok(temperature)) return SMCSD_ERR_INVALID_ARG;
+  if (V > SMCSD_MAX_V) return SMCSD_ERR_UNSUPPORTED;
+  // every tree has a root and at most SMCSD_TREE_MAX_NODES nodes, fewer
+  // nodes with children than nodes
+  if (num_nodes < B || num_nodes > (int64_t)B * SMCSD_TREE_MAX_NODES) return SMCSD_ERR_INVALID_ARG;
+  if (num_draft_rows < 0 || num_draft_rows > num_nodes - B) return SMCSD_ERR_INVALID_ARG;
+  if (B == 0) return SMCSD_OK;
+  if (!node_offsets || !parent || !tokens || !target_logits || !draft_offsets || !uniforms || !num_accepted ||
+      !last_node || !final_token)
+    return SMCSD_ERR_INVALID_ARG;
+  if (num_draft_rows > 0 && !draft_logits) return SMCSD_ERR_INVALID_ARG;
+  const int64_t rows = num_nodes + num_draft_rows;
+  const SdLayout l = tree_layout(rows, V);
+  if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
+    return SMCSD_ERR_WORKSPACE;
+  const bool bf16 = dtype == SMCSD_BF16;
+  const bool vec = vec_ok(dtype, V, target_logits, num_draft_rows > 0 ? draft_logits : nullptr);
+  smcsd::Plan plan;
+  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  char* ws = static_cast<char*>(workspace);
+  smcsd::TreeArgs a;
+  // flat streaming: group g is target row g, then draft row g - num_nodes
+  fill_step(&a.s, plan, target_logits, draft_logits, nullptr, nullptr, rows, num_nodes, num_draft_rows, V, 0,
+            temperature, ws, l.part, l.tpart, status_flags);
+  a.s.flat = 1;
+  a.node_off = node_offsets;
+  a.draft_off = draft_offsets;
+  a.parent = parent;
+  a.tokens = tokens;
+  a.uniforms = uniforms;
+  a.num_accepted = num_accepted;
+  a.last_node = last_node;
+  a.final_token = final_token;
+  a.B = B;
+  return smcsd::launch_tree(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;
 }

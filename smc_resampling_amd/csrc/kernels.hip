@@ -98,12 +98,17 @@ __device__ __forceinline__ Group group_of(int64_t g, int K, const int32_t* __res
 }
 
 // Logit row `rr` of group g (target rows 0..kb, then draft rows); null when
-// it falls outside the buffers (malformed offsets).
+// it falls outside the buffers (malformed offsets).  In flat mode group g is
+// target row g, and draft row g - rows_t past the target rows.
 template <typename raw>
 __device__ __forceinline__ const raw* group_row(const StepArgs& a, const Group& G, int64_t g, int64_t rr) {
   if (!G.ok || rr < 0 || rr > 2 * G.kb) return nullptr;
   if (rr <= G.kb) {
     const int64_t tr = G.d0 + g + rr;
+    if (a.flat && tr >= a.rows_t) {
+      const int64_t dr = tr - a.rows_t;
+      return dr < a.rows_d ? static_cast<const raw*>(a.draft) + dr * a.V : nullptr;
+    }
     return tr < a.rows_t ? static_cast<const raw*>(a.target) + tr * a.V : nullptr;
   }
   const int64_t dr = G.d0 + rr - G.kb - 1;
@@ -438,7 +443,8 @@ constexpr int DPP_WAVE_SHR1 = 0x138;
 constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
 
 template <int NT>
-__device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, TailLds& L) {
+__device__ __forceinline__ void merge_rows_to(const float2* __restrict__ part, int R, int nseg, float* Mo,
+                                              double* So, double* lSo) {
   constexpr int TPR = 16;  // threads per row: one DPP row
   const int sub = threadIdx.x & (TPR - 1);
   // the group's partials through a buffer resource: 32-bit offsets
@@ -476,11 +482,15 @@ __device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int 
     fold_dpp<DPP_QUAD_XOR1>(m, s);
     fold_dpp<DPP_QUAD_XOR2>(m, s);
     if (r < R && sub == 0) {
-      L.M[r] = m;
-      L.S[r] = s;
-      L.lS[r] = log(s);
+      Mo[r] = m;
+      So[r] = s;
+      lSo[r] = log(s);
     }
   }
+}
+template <int NT>
+__device__ __forceinline__ void merge_rows(const float2* __restrict__ part, int R, int nseg, TailLds& L) {
+  merge_rows_to<NT>(part, R, nseg, L.M, L.S, L.lS);
 }
 
 // Partials of the bonus row kb of group g (first row fr0): its tile partials
@@ -892,6 +902,328 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_draw_tail(SdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_tree_tail: one workgroup of SD_WAVES wavefronts per token tree
+// ("Faster LLM Inference via Sequential Monte Carlo", sec. 4: tree-based SD;
+// multi-draft speculative sampling over the tree).  The workgroup merges the
+// statistics of every target and draft row of the tree and gathers each
+// node's token logits in its parent's rows, then walks from the root: at
+// node u, child c is accepted iff u_c < r(x_c) / q_u(x_c) with r the running
+// distribution (p_u, then max(0, r - q_u) / Z after each rejected child).  A
+// rejection costs one pass of the whole workgroup over u's row pair: the
+// residual chain is rebuilt elementwise from p_u and q_u with the masses Z of
+// the earlier rejections, and the tile masses of max(0, r - q_u) give the new
+// Z.  The walk ends at a leaf (bonus draw from p_leaf, as in sd_verify) or
+// when every child of u is rejected (inverse-CDF draw from the last pass's
+// weights: the tile is located from the pass's tile masses, then reloaded and
+// searched).
+// ---------------------------------------------------------------------------
+constexpr int TREE_MAX = SMCSD_TREE_MAX_NODES;
+
+struct TreeLds {
+  TailLds t;  // draw scratch: staged partials, tile masses, located tile
+  float Mt[TREE_MAX], Md[TREE_MAX];      // row maxima (log2 domain): target row of node n, local draft row k
+  double St[TREE_MAX], Sd[TREE_MAX];     // row sums of 2^(z c - M)
+  double lSt[TREE_MAX], lSd[TREE_MAX];   // their natural logs
+  int par[TREE_MAX];                     // local parent of node n (-1 at the root)
+  int drow[TREE_MAX];                    // local draft row of node n, -1 for a leaf
+  float zt[TREE_MAX], zd[TREE_MAX];      // node n's token logit in its parent's target / draft row
+  int xok[TREE_MAX];                     // node n's token lies in [0, V)
+  float ut[TREE_MAX];                    // uniforms (the root's slot: the final draw)
+  uint64_t kids[TREE_MAX / WAVE];        // children of the current node, as bits
+  int wcnt[SD_WAVES];                    // nodes with children per wavefront (draft-row scan)
+  double Z[TREE_MAX];                    // masses of the current node's rejections
+  float iz[TREE_MAX];                    // 1 / Z (0: that rejection left r unchanged)
+  int bad, accept;
+};
+
+__device__ __forceinline__ RowStat stat_at(const float* M, const double* S, const double* lS, int r) {
+  RowStat rs;
+  rs.M = M[r];
+  rs.S = S[r];
+  rs.lS = lS[r];
+  rs.ok = (rs.M > -INFINITY) && (rs.M < INFINITY) && (rs.S >= 0.5) && (rs.S < INFINITY);
+  return rs;
+}
+
+// Weights of one tile of node u's row pair after `nrej` earlier rejections at
+// u: r = p, then r <- max(0, r - q) * iz[j] for each earlier rejection j (r
+// unchanged where iz[j] = 0); w = max(0, r - q) (sub) or w = r (!sub).  With
+// no earlier rejection this is exactly residual_weights, as in sd_verify.
+template <typename DT>
+__device__ __forceinline__ void tree_weights(const Raw<DT>& rt, const Raw<DT>& rd, float At, float Ad, float c,
+                                             const float* iz, int nrej, bool sub, float (&w)[PER_LANE]) {
+  if (nrej == 0 && sub) {
+    residual_weights<DT>(rt, rd, At, Ad, c, w);
+    return;
+  }
+#pragma unroll
+  for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+    float r[DT::VEC], q[DT::VEC];
+    unpack<DT>(rt, ch, r);
+    unpack<DT>(rd, ch, q);
+#pragma unroll
+    for (int k = 0; k < DT::VEC; k++) {
+      r[k] = __builtin_amdgcn_exp2f(fmaf(r[k], c, -At));
+      q[k] = __builtin_amdgcn_exp2f(fmaf(q[k], c, -Ad));
+    }
+    // the earlier rejections, one chunk at a time
+    for (int j = 0; j < nrej; j++) {
+      const float z = iz[j];
+      if (z > 0.0f) {
+#pragma unroll
+        for (int k = 0; k < DT::VEC; k++) r[k] = fmaxf(r[k] - q[k], 0.0f) * z;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < DT::VEC; k++) w[ch * DT::VEC + k] = sub ? fmaxf(r[k] - q[k], 0.0f) : r[k];
+  }
+}
+
+template <typename DT, bool VL>
+__global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
+  using raw = typename DT::raw;
+  __shared__ TreeLds L;
+  const StepArgs& s = a.s;
+  const int lane = threadIdx.x % WAVE, wave = wave_id();
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int ntiles = s.ntiles;
+  const int64_t n0 = a.node_off[b], d0 = a.draft_off[b];
+  const int64_t M64 = a.node_off[b + 1] - n0, D64 = a.draft_off[b + 1] - d0;
+  // offsets that do not describe a tree inside the buffers: nothing is read
+  bool ok = M64 >= 1 && M64 <= TREE_MAX && D64 >= 0 && D64 < M64 && n0 >= 0 && n0 + M64 <= s.rows_t && d0 >= 0 &&
+            d0 + D64 <= s.rows_d;
+  if (b == 0) ok = ok && n0 == 0 && d0 == 0;
+  if (b == a.B - 1) ok = ok && n0 + M64 == s.rows_t && d0 + D64 == s.rows_d;
+  if (!ok) {
+    if (tid == 0) raise_flags(s.flags, FLAG_BAD_INPUT);
+    return;
+  }
+  const int M = (int)M64, D = (int)D64;
+  if (tid == 0) {
+    L.t.fl = 0;
+    L.bad = 0;
+  }
+  // parents, tokens and uniforms, one thread per node
+  int pn = -1;
+  int32_t xn = 0;
+  float un = 0.0f;
+  if (tid < M) {
+    pn = a.parent[n0 + tid];
+    xn = a.tokens[n0 + tid];
+    un = a.uniforms[n0 + tid];
+  }
+  // statistics of the tree's target rows (flat rows n0 ..) and draft rows
+  // (flat rows rows_t + d0 ..)
+  merge_rows_to<SD_BLOCK>(s.part + n0 * s.nseg, M, s.nseg, L.Mt, L.St, L.lSt);
+  merge_rows_to<SD_BLOCK>(s.part + (s.rows_t + d0) * s.nseg, D, s.nseg, L.Md, L.Sd, L.lSd);
+  if (tid < M) {
+    L.par[tid] = pn;
+    L.drow[tid] = 0;
+    L.ut[tid] = un;
+  }
+  __syncthreads();
+  // tree order: the root's parent is -1, every other parent comes earlier;
+  // mark the nodes that have children
+  bool badn = false;
+  if (tid < M) {
+    if (tid == 0) {
+      badn = pn != -1;
+    } else {
+      badn = pn < 0 || pn >= tid;
+      if (!badn) L.drow[pn] = 1;
+    }
+  }
+  __syncthreads();
+  const int has = tid < M ? L.drow[tid] : 0;
+  const uint64_t hb = __ballot(has != 0);
+  if (lane == 0) L.wcnt[wave] = __builtin_popcountll(hb);
+  const uint64_t anyb = __ballot(badn);
+  if (lane == 0 && anyb) atomicOr(&L.bad, 1);
+  __syncthreads();
+  // draft row of a node with children: its rank among them (node order)
+  int before = 0, total = 0;
+  for (int w = 0; w < SD_WAVES; w++) {
+    const int cnt = L.wcnt[w];
+    before += w < wave ? cnt : 0;
+    total += cnt;
+  }
+  const int rank = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)hb, 0));
+  if (tid < M) L.drow[tid] = has ? rank : -1;
+  if (total != D && tid == 0) L.bad = 1;
+  __syncthreads();
+  if (L.bad) {
+    if (tid == 0) raise_flags(s.flags, FLAG_BAD_INPUT);
+    return;
+  }
+  // each node's token logit in its parent's target row and draft row
+  if (tid >= 1 && tid < M) {
+    const int pp = L.par[tid];
+    const bool xv = xn >= 0 && xn < s.V;
+    const raw* tr = static_cast<const raw*>(s.target) + (n0 + pp) * s.V;
+    const raw* dr = static_cast<const raw*>(s.draft) + (d0 + L.drow[pp]) * s.V;
+    L.zt[tid] = xv ? DT::to_f32(tr[xn]) : 0.0f;
+    L.zd[tid] = xv ? DT::to_f32(dr[xn]) : 0.0f;
+    L.xok[tid] = xv;
+  }
+  __syncthreads();
+  uint32_t fl = 0;
+  const double ufin = (double)L.ut[0];
+  int u = 0, depth = 0, y = 0;
+  for (;;) {
+    // the children of u, as bits of node indices (M <= TREE_MAX = 4 wavefronts of nodes)
+    const uint64_t kb = __ballot(tid < M && L.par[tid] == u);
+    if (lane == 0 && wave < TREE_MAX / WAVE) L.kids[wave] = kb;
+    __syncthreads();
+    const int dr = L.drow[u];
+    const RowStat st = stat_at(L.Mt, L.St, L.lSt, u);
+    if (!st.ok) fl |= FLAG_NONFINITE;
+    const raw* trow = static_cast<const raw*>(s.target) + (n0 + u) * s.V;
+    if (dr < 0) {
+      // a leaf: the bonus token from p_u (its tile or segment partials)
+      int bnp, bper;
+      const float2* bp = bonus_partials(s, n0 + u, n0 + u, 0, &bnp, &bper);
+      stage_partials<SD_BLOCK>(bp, bnp, L.t);
+      __syncthreads();
+      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, st.M, ufin, bnp, bper, L.t, fl);
+      break;
+    }
+    const RowStat sd = stat_at(L.Md, L.Sd, L.lSd, dr);
+    if (!sd.ok) fl |= FLAG_NONFINITE;
+    const raw* drw = static_cast<const raw*>(s.draft) + (d0 + dr) * s.V;
+    const float At = log2_norm(st), Ad = log2_norm(sd);
+    int nrej = 0, next = -1;
+    for (int kw = 0; kw < TREE_MAX / WAVE && next < 0; kw++) {
+      uint64_t bits = L.kids[kw];
+      while (bits && next < 0) {
+        const int cnode = kw * WAVE + __builtin_ctzll(bits);
+        bits &= bits - 1;
+        if (tid == 0) {
+          // the ratio r(x) / q(x) of this child's token
+          bool acc = false;
+          if (!L.xok[cnode]) {
+            fl |= FLAG_BAD_INPUT;
+          } else {
+            // p(x) / q(x) as in sd_verify (the fp32 exponential of the fp64
+            // log difference); each earlier rejection j turns r(x) / q(x)
+            // into max(0, r(x) / q(x) - 1) / Z_j
+            const double lp = log_prob(L.zt[cnode], st, s.c), lq = log_prob(L.zd[cnode], sd, s.c);
+            double ratio = (double)__builtin_amdgcn_exp2f((float)((lp - lq) * 1.4426950408889634));
+            for (int j = 0; j < nrej; j++)
+              if (L.Z[j] > 0.0) ratio = fmax(ratio - 1.0, 0.0) / L.Z[j];
+            acc = (double)L.ut[cnode] < ratio;
+          }
+          L.accept = acc;
+        }
+        __syncthreads();
+        if (L.accept) {
+          next = cnode;
+          break;
+        }
+        // rejected: one pass over u's row pair for the mass of max(0, r - q)
+        for (int t = wave; t < ntiles; t += SD_WAVES) {
+          const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, t, lane);
+          const Raw<DT> rd = load_tile<DT, VL>(drw, s.V, t, lane);
+          float w[PER_LANE];
+          tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, nrej, true, w);
+          float m = 0.0f;
+#pragma unroll
+          for (int e = 0; e < PER_LANE; e++) m += w[e];
+          m = wave_sum(m);
+          if (lane == 0) L.t.W[t] = (double)m;
+        }
+        __syncthreads();
+        if (wave == 0) {
+          double z = 0.0;
+          for (int t = lane; t < ntiles; t += WAVE) z += L.t.W[t];
+          z = wave_sum_f64(z);
+          if (lane == 0) {
+            L.Z[nrej] = z;
+            L.iz[nrej] = z > 0.0 ? (float)(1.0 / z) : 0.0f;
+            if (!(z > 0.0)) fl |= FLAG_ZERO_RESIDUAL;  // r and q agree: r stays
+          }
+        }
+        __syncthreads();
+        nrej++;
+      }
+    }
+    if (next >= 0) {
+      u = next;
+      depth++;
+      __syncthreads();  // L.kids is rewritten for the next node
+      continue;
+    }
+    // every child rejected: the final token from the last pass's weights, or,
+    // when that pass left no mass, from r itself (sd_verify's p_n fallback
+    // for the first rejection)
+    const int last = nrej - 1;
+    const bool zero = !(L.Z[last] > 0.0);
+    if (zero) {
+      for (int t = wave; t < ntiles; t += SD_WAVES) {
+        const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, t, lane);
+        const Raw<DT> rd = load_tile<DT, VL>(drw, s.V, t, lane);
+        float w[PER_LANE];
+        tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, last, false, w);
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < PER_LANE; e++) m += w[e];
+        m = wave_sum(m);
+        if (lane == 0) L.t.W[t] = (double)m;
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+      auto wt = [&](int k) -> double { return L.t.W[k]; };
+      double bef = 0.0, target = 0.0, tot = 0.0;
+      int lastk = -1;
+      const int k = locate(
+          ntiles, wt, 0.0,
+          [&](double tt) {
+            tot = tt;
+            return ufin * tt;
+          },
+          lane, &bef, &target, &lastk);
+      if (lane == 0) {
+        L.t.sel = k >= 0 ? k : (lastk >= 0 ? lastk : 0);
+        L.t.clamp = k < 0;
+        L.t.target = target - bef;  // the target inside the located tile
+      }
+    }
+    __syncthreads();
+    const int tt = L.t.sel;
+    if (wave == 0) {
+      // the located tile's weights, recomputed exactly as its pass did
+      float w[PER_LANE];
+      const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tt, lane);
+      const Raw<DT> rd = load_tile<DT, VL>(drw, s.V, tt, lane);
+      tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, last, !zero, w);
+      auto wfn = [&](int ch, float (&x)[DT::VEC]) {
+#pragma unroll
+        for (int k = 0; k < DT::VEC; k++) x[k] = w[ch * DT::VEC + k];
+      };
+      int last_pos = -1;
+      int idx = tile_search<DT>(wfn, L.t.clamp ? INFINITY : (float)L.t.target, lane, &last_pos);
+      if (idx < 0) {
+        fl |= FLAG_CDF_CLAMP;
+        idx = last_pos >= 0 ? last_pos : 0;
+      }
+      if (lane == 0) L.t.y = tt * TILE + idx;
+    }
+    __syncthreads();
+    y = L.t.y;
+    break;
+  }
+  or_flags(fl, L.t);
+  __syncthreads();
+  if (tid == 0) {
+    a.num_accepted[b] = depth;
+    a.last_node[b] = u;
+    a.final_token[b] = y;
+    raise_flags(s.flags, L.t.fl);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_smc_tail: one workgroup per particle; the last particle of a prompt runs
 // the prompt's ESS, resampling and page-table gather
 // ---------------------------------------------------------------------------
@@ -1210,6 +1542,20 @@ hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipS
   const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())
                        : (vec ? smc_tail_kernel<F32, true>() : smc_tail_kernel<F32, false>());
   return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
+}
+
+template <typename DT, bool VL>
+static const void* tree_tail_kernel() {
+  return kptr(&k_tree_tail<DT, VL>);
+}
+
+hipError_t launch_tree(const TreeArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
+  hipError_t e = launch(stream_kernel(bf16, vec, p.tp), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
+                        t.stream_stop);
+  if (e != hipSuccess) return e;
+  const void* k = bf16 ? (vec ? tree_tail_kernel<Bf16, true>() : tree_tail_kernel<Bf16, false>())
+                       : (vec ? tree_tail_kernel<F32, true>() : tree_tail_kernel<F32, false>());
+  return launch(k, (unsigned)a.B, SD_BLOCK, a, s, t.tail_start, t.tail_stop);
 }
 
 }  // namespace smcsd

@@ -36,6 +36,7 @@ struct StepArgs {
   float2* tpart;  // [ngroups * ntiles] tile partials of each group's bonus row
   uint32_t* ctr;  // counter lines (zero between calls)
   uint32_t* flags;
+  int flat;       // 1: every row is a group of its own, the target rows then the draft rows (K = 0)
 };
 
 struct SdArgs {
@@ -62,6 +63,21 @@ struct SmcArgs {
   int32_t* resampled;
 };
 
+// Token trees: one workgroup per tree decides by walking it (the streaming
+// kernel runs in flat mode over the trees' target rows, then their draft rows).
+struct TreeArgs {
+  StepArgs s;
+  const int32_t* node_off;   // [B+1] CSR over nodes (= target rows)
+  const int32_t* draft_off;  // [B+1] CSR over draft rows (one per node with children)
+  const int32_t* parent;     // [nodes] local parent index, -1 at the root
+  const int32_t* tokens;     // [nodes] draft token of each node
+  const float* uniforms;     // [nodes] acceptance uniforms; the root's slot: final draw
+  int32_t* num_accepted;
+  int32_t* last_node;
+  int32_t* final_token;
+  int B;
+};
+
 // Segment length and streaming grid of a call.
 struct Plan {
   int seg, nseg;
@@ -81,5 +97,6 @@ hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p);
 // launches carry the events.
 hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);
 hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);
+hipError_t launch_tree(const TreeArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);
 
 }  // namespace smcsd

@@ -107,3 +107,70 @@ def sorted_ancestors(seed, P, N, concentrate=0.0):
         w = (1.0 - concentrate) ** np.arange(N) if concentrate else np.ones(N)
         out.append(np.sort(rng.choice(N, N, p=w / w.sum())))
     return np.concatenate(out).astype(np.int32)
+
+
+def tree_parents(kind, rng=None, M=None, width=2, depth=3):
+    """Parent lists (local indices, -1 at the root) of token-tree shapes:
+    "root" (one node), "chain" (M nodes), "star" (a root with M-1 children),
+    "full" (complete `width`-ary tree of `depth` levels below the root, nodes
+    numbered level by level) and "random" (M nodes, each parent drawn
+    uniformly from the earlier nodes)."""
+    if kind == "root":
+        return [-1]
+    if kind == "chain":
+        return list(range(-1, M - 1))
+    if kind == "star":
+        return [-1] + [0] * (M - 1)
+    if kind == "full":
+        par, level = [-1], [0]
+        for _ in range(depth):
+            nxt = []
+            for p in level:
+                for _ in range(width):
+                    par.append(p)
+                    nxt.append(len(par) - 1)
+            level = nxt
+        return par
+    if kind == "random":
+        return [-1] + [int(rng.integers(0, n)) for n in range(1, M)]
+    raise ValueError(kind)
+
+
+def tree_case(seed, parents_list, V, T=1.0, delta=1.0, dtype="f32", scale=3.0, prior=True):
+    """Token trees as numpy arrays in the layout of tree_verify.
+
+    Each node has a target row z_t = scale * N(0,1) (+ rank prior); each node
+    with children has a draft row z_d = z_t + delta * N(0,1) of its own target
+    row; every child's token is a Gumbel-max draw from its parent's draft
+    distribution (iid across siblings); uniforms U[0,1) per node.  ``delta``
+    may be one value or one per tree."""
+    rng = np.random.default_rng(seed)
+    B = len(parents_list)
+    base = -0.5 * np.log1p(rng.permutation(V)) if prior else np.zeros(V)
+    dl = np.broadcast_to(np.asarray(delta, np.float64), (B,))
+    node_off, draft_off = [0], [0]
+    zt_rows, zd_rows, par_all, internal_of = [], [], [], []
+    for b, par in enumerate(parents_list):
+        M = len(par)
+        zt = (scale * rng.standard_normal((M, V)) + base).astype(np.float32)
+        internal = sorted({p for p in par[1:]})
+        zd = (zt[internal] + dl[b] * rng.standard_normal((len(internal), V))).astype(np.float32)
+        zt_rows.append(zt)
+        zd_rows.append(zd)
+        par_all.extend(par)
+        internal_of.append(internal)
+        node_off.append(node_off[-1] + M)
+        draft_off.append(draft_off[-1] + len(internal))
+    tgt, _ = stored(np.concatenate(zt_rows) if zt_rows else np.zeros((0, V), np.float32), dtype)
+    zd_all = np.concatenate(zd_rows) if draft_off[-1] else np.zeros((0, V), np.float32)
+    drf, drf64 = stored(zd_all, dtype)
+    tokens = np.zeros(node_off[-1], np.int32)
+    for b, par in enumerate(parents_list):
+        rank = {p: i for i, p in enumerate(internal_of[b])}
+        kids = list(range(1, len(par)))
+        if kids:
+            rows = np.stack([drf64[draft_off[b] + rank[par[n]]] for n in kids])
+            tokens[node_off[b] + 1:node_off[b + 1]] = gumbel_tokens(rng, rows, T)
+    u = rng.random(node_off[-1]).astype(np.float32)
+    return dict(target=tgt, draft=drf, node_off=np.array(node_off, np.int32), draft_off=np.array(draft_off, np.int32),
+                parent=np.array(par_all, np.int32), tokens=tokens, uniforms=u, T=T, dtype=dtype)

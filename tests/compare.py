@@ -188,3 +188,57 @@ def compare_smc(inp, ref, out_g, logw_in, pt_in, label="") -> Tally:
                 t.nonexempt_diff += 1
                 t.failures.append(f"{label} prompt {p}: page table is not the ancestor gather")
     return t
+
+
+def _depth_path(parent, n0, node):
+    """Nodes root .. node (local indices) of a tree whose parents start at n0."""
+    path = [node]
+    while path[-1] > 0:
+        path.append(int(parent[n0 + path[-1]]))
+    return path[::-1]
+
+
+def compare_tree(inp, ref, na_g, ln_g, ft_g, label="") -> Tally:
+    """Tree verification: the GPU's stopping node, depth and final token against
+    the oracle's.  When the walks part, the first child tested differently at
+    the deepest common node must have its uniform within BAND of its ratio."""
+    t = Tally()
+    noff, par = inp["node_off"], inp["parent"]
+    for b in range(len(na_g)):
+        n0, M = int(noff[b]), int(noff[b + 1] - noff[b])
+        lo, yo = int(ref["last_node"][b]), int(ref["final_token"][b])
+        lg, yg, ng = int(ln_g[b]), int(ft_g[b]), int(na_g[b])
+        if not (0 <= lg < M) or ng != len(_depth_path(par, n0, lg)) - 1:
+            t.nonexempt_diff += 1
+            t.failures.append(f"{label} tree {b}: gpu stop node {lg} / depth {ng} is not a node and its depth")
+            continue
+        po, pg = _depth_path(par, n0, lo), _depth_path(par, n0, lg)
+        am = ref["accept_margin"][n0:n0 + M]
+        tested = am[am >= 0]
+        near = (len(tested) and tested.min() < BAND) or ref["sample_margin"][b] < BAND
+        if lg == lo and yg == yo:
+            t.equal += 1
+            t.exempt_equal += int(bool(near))
+            continue
+        if lg != lo:
+            k = 0
+            while k + 1 < min(len(po), len(pg)) and po[k + 1] == pg[k + 1]:
+                k += 1
+            co = po[k + 1] if k + 1 < len(po) else None
+            cg = pg[k + 1] if k + 1 < len(pg) else None
+            first = cg if co is None else co if cg is None else min(co, cg)
+            m = float(am[first])
+            if 0 <= m <= BAND:
+                t.exempt_diff += 1
+            else:
+                t.nonexempt_diff += 1
+                t.failures.append(f"{label} tree {b}: walks part at node {po[k]} (gpu stop {lg}, oracle {lo}); "
+                                  f"test of node {first} margin {m}")
+            if 0 <= m <= BAND_TIGHT:
+                t.tight_exempt_diff += 1
+            else:
+                t.tight_nonexempt_diff += 1
+            continue
+        cdf, _ = oracle.tree_final_cdf(inp["target"], inp["draft"], noff, inp["draft_off"], par, b, lo, inp["T"])
+        _token_diff(t, float(inp["uniforms"][n0]), cdf, yg, f"{label} tree {b} final")
+    return t

@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 import oracle
-from compare import compare_sd, compare_smc
+from compare import compare_sd, compare_smc, compare_tree
 
 DEV = torch.device("cuda:0")
 
@@ -109,3 +109,29 @@ def check_smc_steps(case, steps=1, ess_frac=0.5, label="", new_inputs=None):
         total = t if total is None else (total.merge(t) or total)
         logw, pt = g["logw"], g["pt_out"]
     return total
+
+
+def run_tree_gpu(case):
+    s = lib()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    out = s.tree_verify(dev_logits(case["target"]), dev_logits(case["draft"]), t(case["node_off"]),
+                        t(case["draft_off"]), t(case["parent"]), t(case["tokens"]), t(case["uniforms"]), case["T"])
+    torch.cuda.synchronize()
+    return (out["num_accepted"].cpu().numpy(), out["last_node"].cpu().numpy(), out["final_token"].cpu().numpy(),
+            int(out["status_flags"].item()))
+
+
+def run_tree_oracle(case):
+    return oracle.tree_verify(case["target"], case["draft"], case["node_off"], case["draft_off"], case["parent"],
+                              case["tokens"], case["uniforms"], case["T"])
+
+
+def check_tree(case, label="", ignore_flags=8):
+    na, ln, ft, fl = run_tree_gpu(case)
+    ref = run_tree_oracle(case)
+    assert ref["status"] == 0
+    t = compare_tree(case, ref, na, ln, ft, label)
+    say(f"[tree {label}] {t.summary()} accepted={int(na.sum())} flags gpu={fl} oracle={ref['flags']}")
+    t.assert_ok()
+    assert (fl & ~ignore_flags) == (ref["flags"] & ~ignore_flags), (fl, ref["flags"])
+    return t

@@ -96,3 +96,28 @@ def _smc(s, **kw):
     (dict(wsb=100), 3), (dict(P=0, tgt=None), 0), (dict(L=-1), 1)])
 def test_smc_host_validation(s, kw, code):
     assert _smc(s, **kw) == code
+
+
+def _tree(s, **kw):
+    a = dict(dtype=1, B=4, V=1000, T=1.0, noff=FAKE, par=FAKE, tok=FAKE, nodes=28, tgt=FAKE, doff=FAKE, rows_d=12,
+             drf=FAKE, u=FAKE, na=FAKE, ln=FAKE, ft=FAKE, fl=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return s.lib().tree_verify(a["dtype"], a["B"], a["V"], a["T"], a["noff"], a["par"], a["tok"], a["nodes"],
+                               a["tgt"], a["doff"], a["rows_d"], a["drf"], a["u"], a["na"], a["ln"], a["ft"],
+                               a["fl"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), 1), (dict(V=1 << 20), 2), (dict(V=0), 1), (dict(T=0.0), 1), (dict(T=math.nan), 1),
+    (dict(B=-1), 1), (dict(nodes=3), 1), (dict(nodes=4 * 256 + 1), 1), (dict(rows_d=-1), 1), (dict(rows_d=25), 1),
+    (dict(noff=None), 1), (dict(par=None), 1), (dict(tok=None), 1), (dict(doff=None), 1), (dict(u=None), 1),
+    (dict(ln=None), 1), (dict(drf=None), 1), (dict(ws=None), 3), (dict(wsb=1000), 3), (dict(ws=FAKE + 4), 3),
+    (dict(B=0, nodes=0, rows_d=0, tgt=None, drf=None), 0)])
+def test_tree_verify_host_validation(s, kw, code):
+    assert _tree(s, **kw) == code
+
+
+def test_tree_workspace_sizes(s):
+    assert s.tree_verify_workspace_bytes(1, 0, 100, 0, 0) == 0
+    a = s.tree_verify_workspace_bytes(1, 64, 32768, 64 * 15, 64 * 7)
+    assert a % 256 == 0 and a >= 2 * (64 * 22) * 16 * 8 + (4 << 20)
