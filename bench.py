@@ -173,6 +173,8 @@ def main():
     W = args.warmup
     if args.draft_sample and (args.with_pages or args.beta is not None):
         sys.exit("--draft-sample times the draft-side draw alone")
+    if cfg.kind == "tree" and (args.draft_sample or args.with_pages or args.beta is not None):
+        sys.exit("the tree workload runs tree_verify alone")
     if args.with_pages:
         if cfg.kind != "smc":
             sys.exit("--with-pages applies to the SMC workloads")
@@ -196,7 +198,8 @@ def main():
     log(f"[bench] {cfg.name}: generating {nb} input batches of ~{per_batch / 1e6:.1f} MB")
     batches = []
     for b in range(nb):
-        batches.append(gen.sd_step(b) if cfg.kind != "smc" else gen.smc_step(b))
+        batches.append(gen.tree_step(b) if cfg.kind == "tree" else gen.sd_step(b) if cfg.kind != "smc"
+                       else gen.smc_step(b))
     torch.cuda.synchronize()
     positions = [synth.verified_positions(cfg, bt.get("Kb")) for bt in batches]
     nbytes = [synth.step_bytes(cfg, bt.get("Kb")) for bt in batches]
@@ -219,6 +222,21 @@ def main():
                 call, o = smcsd.prepare_draft_sample(
                     bt["draft"][:R_draw], u[:R_draw], cfg.T, workspace=ws, stream=stream_handle,
                     **({} if outs is None else {k: outs[k] for k in ("tokens", "status_flags")}))
+                outs = o
+                calls.append(call)
+            return calls, outs
+        if cfg.kind == "tree":
+            bt0 = batches[0]
+            ws = smcsd.new_workspace(smcsd.tree_verify_workspace_bytes(1, cfg.B, cfg.V, bt0["target"].shape[0],
+                                                                       bt0["draft"].shape[0]), dev)
+            outs = None
+            for s in range(steps + W):
+                bt = batches[s % nb]
+                call, o = smcsd.prepare_tree_verify(
+                    bt["target"], bt["draft"], bt["node_off"], bt["draft_off"], bt["parent"], bt["tokens"],
+                    bt["uniforms"], cfg.T, workspace=ws, stream=stream_handle,
+                    **({} if outs is None else {k: outs[k] for k in ("num_accepted", "last_node", "final_token",
+                                                                    "status_flags")}))
                 outs = o
                 calls.append(call)
             return calls, outs
@@ -380,6 +398,16 @@ def main():
                     if t_cpu > args.cpu_seconds:
                         break
                 sample = f"{done_pos} draft rows of {cfg.name}"
+            elif cfg.kind == "tree":
+                tg, dr = host_logits(bt["target"]), host_logits(bt["draft"])
+                host = {k: bt[k].cpu().numpy() for k in ("node_off", "draft_off", "parent", "tokens", "uniforms")}
+                t0 = time.perf_counter()
+                oracle.tree_verify(tg, dr, host["node_off"], host["draft_off"], host["parent"], host["tokens"],
+                                   host["uniforms"], cfg.T)
+                t_cpu += time.perf_counter() - t0
+                done_pos += positions[i]
+                n_steps += 1
+                sample = f"{n_steps} steps of {cfg.name}"
             elif cfg.kind == "smc":
                 # one prompt at a time: the oracle's unit of work
                 P, N, K = cfg.P, cfg.N, cfg.K
@@ -443,7 +471,9 @@ def main():
                    "input_batches": nb, "status_flags": flags,
                    **({} if args.beta is None else {"power_beta": args.beta}),
                    **({"paged_kv_bookkeeping": True, "page_size": 16} if args.with_pages else {}),
-                   **({"draft_sample_rows": R_draw} if args.draft_sample else {})},
+                   **({"draft_sample_rows": R_draw} if args.draft_sample else {}),
+                   **({"tree": dict(cfg.tree, nodes=len(synth.full_tree_parents(**cfg.tree)))}
+                      if cfg.kind == "tree" else {})},
         "roofline": {"bound": "hbm", "kernel": "k_stream", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (traffic_from_profiles(cfg.name) if args.beta is None and not args.draft_sample

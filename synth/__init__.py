@@ -59,6 +59,8 @@ def lib():
         L.synth_logits.restype = I32
         L.synth_draft_tokens.argtypes = [I32, I64, I64, F, P, U32, U32, P, P]
         L.synth_draft_tokens.restype = I32
+        L.synth_draft_tokens_rows.argtypes = [I32, I64, I64, F, P, P, U32, U32, P, P]
+        L.synth_draft_tokens_rows.restype = I32
         L.synth_uniforms.argtypes = [I64, U32, U32, U32, P, P]
         L.synth_uniforms.restype = I32
         _lib = L
@@ -94,7 +96,7 @@ def pacer_scores(B, seed, step, block=4, max_blocks=4):
 @dataclass
 class Config:
     name: str
-    kind: str  # "sd" | "sd_ragged" | "smc"
+    kind: str  # "sd" | "sd_ragged" | "smc" | "tree"
     V: int
     dtype: str  # "f32" | "bf16"
     T: float
@@ -109,6 +111,7 @@ class Config:
     page_tokens: int = 16
     context: int = 0
     pacer: dict = field(default_factory=dict)
+    tree: dict = field(default_factory=dict)  # complete tree shape: width, depth
 
     @property
     def L(self):
@@ -125,7 +128,25 @@ CONFIGS = [
            N=64, K=8, deltas=(0.5, 2.0), context=8192),
     Config("cfg4_sd_ragged_b256_v32000_bf16", "sd_ragged", V=32000, dtype="bf16", T=1.0, steps=128, seed=4, B=256,
            K=16, pacer=dict(block=4, max_blocks=4, t0=0.5, rho=1.1)),
+    # token trees in the shape of the batched SD workload: 64 complete binary
+    # trees of depth 3 (15 nodes, 14 draft tokens, 7 draft rows each)
+    Config("tree_b64_binary_d3_v32768_bf16", "tree", V=32768, dtype="bf16", T=0.7, steps=256, seed=5, B=64,
+           deltas=(0.5, 1.0, 2.0), tree=dict(width=2, depth=3)),
 ]
+
+
+def full_tree_parents(width, depth):
+    """Parents of a complete width-ary tree with depth levels below the root,
+    numbered level by level (-1 at the root)."""
+    par, level = [-1], [0]
+    for _ in range(depth):
+        nxt = []
+        for p in level:
+            for _ in range(width):
+                par.append(p)
+                nxt.append(len(par) - 1)
+        level = nxt
+    return par
 
 
 def _torch():
@@ -207,6 +228,44 @@ class Generator:
         assert rc == 0, rc
         return out
 
+    def tree_step(self, step):
+        """dict(target, draft, node_off, draft_off, parent, tokens, uniforms, M): B
+        trees of the config's shape; each node with children has a draft row
+        made from its own target row, and every child's token is drawn from
+        its parent's draft row."""
+        torch = _torch()
+        c = self.cfg
+        par = full_tree_parents(c.tree["width"], c.tree["depth"])
+        M = len(par)
+        internal = sorted({p for p in par[1:]})
+        rank = {n: i for i, n in enumerate(internal)}
+        D = len(internal)
+        B = c.B
+        draft_row = np.full(B * M, -1, np.int32)
+        delta_row = np.zeros(B * M, np.float32)
+        rowmap = np.zeros(B * M, np.int32)  # the draft row each node's token is drawn from
+        for b in range(B):
+            delta_row[b * M:(b + 1) * M] = c.deltas[b % len(c.deltas)]
+            for n in internal:
+                draft_row[b * M + n] = b * D + rank[n]
+            for n in range(1, M):
+                rowmap[b * M + n] = b * D + rank[par[n]]
+            rowmap[b * M] = b * D  # the root's token is not read
+        target = torch.empty((B * M, c.V), dtype=self.tdtype, device=self.device)
+        draft = torch.empty((B * D, c.V), dtype=self.tdtype, device=self.device)
+        dr, dl, rm = (torch.from_numpy(a).to(self.device) for a in (draft_row, delta_row, rowmap))
+        rc = lib().synth_logits(self.bf16, B * M, c.V, self.base.data_ptr(), dr.data_ptr(), dl.data_ptr(), c.seed,
+                                step, target.data_ptr(), draft.data_ptr(), self._stream())
+        assert rc == 0, rc
+        tokens = torch.empty(B * M, dtype=torch.int32, device=self.device)
+        rc = lib().synth_draft_tokens_rows(self.bf16, B * M, c.V, c.T, draft.data_ptr(), rm.data_ptr(), c.seed, step,
+                                           tokens.data_ptr(), self._stream())
+        assert rc == 0, rc
+        i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(self.device)  # noqa: E731
+        return dict(target=target, draft=draft, node_off=i32(np.arange(0, B * M + 1, M)),
+                    draft_off=i32(np.arange(0, B * D + 1, D)), parent=i32(np.tile(par, B)), tokens=tokens,
+                    uniforms=self.uniforms(B * M, STREAM_UNIFORM, step), M=M, D=D, _keep=(dr, dl, rm))
+
     def sd_step(self, step):
         """dict(target, draft, tokens, uniforms, offsets or None, total_draft_rows, K, Kb)."""
         torch = _torch()
@@ -237,6 +296,9 @@ def initial_page_table(P, N, L):
 def step_bytes(cfg: Config, Kb=None) -> int:
     """Algorithmic logit bytes of one step: every target and draft row read once."""
     e = 4 if cfg.dtype == "f32" else 2
+    if cfg.kind == "tree":
+        par = full_tree_parents(cfg.tree["width"], cfg.tree["depth"])
+        return cfg.B * (len(par) + len(set(par[1:]))) * cfg.V * e
     if cfg.kind == "smc":
         rows = cfg.P * cfg.N * (2 * cfg.K + 1)
     elif Kb is not None:
@@ -250,6 +312,8 @@ def verified_positions(cfg: Config, Kb=None) -> int:
     """Draft positions submitted for verification in one step."""
     if cfg.kind == "smc":
         return cfg.P * cfg.N * cfg.K
+    if cfg.kind == "tree":
+        return cfg.B * (len(full_tree_parents(cfg.tree["width"], cfg.tree["depth"])) - 1)
     if Kb is not None:
         return int(np.sum(Kb))
     return cfg.B * cfg.K

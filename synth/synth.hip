@@ -107,12 +107,15 @@ __global__ void k_logits(int bf16, int64_t rows_t, int64_t V, const float* __res
   }
 }
 
-// Gumbel-max draw from softmax(z / T) of each stored draft row; one block per row.
+// Gumbel-max draw d from softmax(z / T) of draft row rowmap[d] (row d without
+// a map); one block per draw.
 __global__ void k_draft_tokens(int bf16, int64_t rows_d, int64_t V, float inv_t, const void* draft,
-                               uint32_t seed, uint32_t step, int32_t* __restrict__ tokens) {
+                               const int32_t* __restrict__ rowmap, uint32_t seed, uint32_t step,
+                               int32_t* __restrict__ tokens) {
   __shared__ float sv[1024];
   __shared__ int si[1024];
   for (int64_t d = blockIdx.x; d < rows_d; d += gridDim.x) {
+    const int64_t src = rowmap ? (int64_t)rowmap[d] : d;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
     const int64_t nblk = (V + 3) / 4;
@@ -124,9 +127,9 @@ __global__ void k_draft_tokens(int bf16, int64_t rows_d, int64_t V, float inv_t,
         if (i >= V) break;
         float z;
         if (bf16)
-          z = __uint_as_float((uint32_t) static_cast<const uint16_t*>(draft)[d * V + i] << 16);
+          z = __uint_as_float((uint32_t) static_cast<const uint16_t*>(draft)[src * V + i] << 16);
         else
-          z = static_cast<const float*>(draft)[d * V + i];
+          z = static_cast<const float*>(draft)[src * V + i];
         const float s = z * inv_t - logf(-logf(u01_open(rr[k])));
         if (s > best) {  // ascending i within a thread: strict keeps the smallest
           best = s;
@@ -230,7 +233,18 @@ int32_t synth_draft_tokens(int32_t bf16, int64_t rows_d, int64_t V, float temper
                            void* stream) {
   if (rows_d > 0)
     hipLaunchKernelGGL(k_draft_tokens, dim3(grid_for(rows_d, 1)), dim3(1024), 0, (hipStream_t)stream,
-                       bf16, rows_d, V, 1.0f / temperature, draft, seed, step, tokens);
+                       bf16, rows_d, V, 1.0f / temperature, draft, nullptr, seed, step, tokens);
+  return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// n draws, draw d from draft row rowmap[d] (several draws may share a row:
+// the children of one tree node), counter (step, d, ...) as above.
+int32_t synth_draft_tokens_rows(int32_t bf16, int64_t n, int64_t V, float temperature, const void* draft,
+                                const int32_t* rowmap, uint32_t seed, uint32_t step, int32_t* tokens,
+                                void* stream) {
+  if (n > 0)
+    hipLaunchKernelGGL(k_draft_tokens, dim3(grid_for(n, 1)), dim3(1024), 0, (hipStream_t)stream, bf16, n, V,
+                       1.0f / temperature, draft, rowmap, seed, step, tokens);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

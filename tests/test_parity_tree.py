@@ -156,3 +156,19 @@ def test_tree_workloads_full_size():
     c = tree_case(20, [tree_parents("random", rng, M=64) for _ in range(16)], 151936, T=1.0, delta=1.0,
                   dtype="bf16")
     check_tree(c, "16 x random 64 nodes, V=151936")
+
+
+def test_tree_generated_workload_steps():
+    """Two steps of the benchmark's tree workload as the GPU generator makes
+    them (64 binary trees of depth 3, V=32768 bf16): the library against the
+    oracle on host copies of the same bytes."""
+    import synth
+    from gpu_util import DEV, check_tree, host_logits
+
+    cfg = synth.CONFIGS[5]
+    gen = synth.Generator(cfg, DEV)
+    for step in (0, 1):
+        bt = gen.tree_step(step)
+        case = dict(target=host_logits(bt["target"]), draft=host_logits(bt["draft"]), T=cfg.T,
+                    **{k: bt[k].cpu().numpy() for k in ("node_off", "draft_off", "parent", "tokens", "uniforms")})
+        check_tree(case, f"{cfg.name} step {step}")

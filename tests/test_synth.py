@@ -47,7 +47,9 @@ def test_pacer_scores(synth):
 
 def test_config_table(synth):
     c = synth.CONFIGS
-    assert [x.kind for x in c] == ["sd", "sd", "smc", "smc", "sd_ragged"]
+    assert [x.kind for x in c] == ["sd", "sd", "smc", "smc", "sd_ragged", "tree"]
+    assert synth.full_tree_parents(2, 3) == [-1, 0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5, 6, 6]
+    assert synth.step_bytes(c[5]) == 64 * (15 + 7) * 32768 * 2 and synth.verified_positions(c[5]) == 64 * 14
     assert synth.step_bytes(c[1]) == 37748736 and synth.verified_positions(c[1]) == 256
     assert synth.step_bytes(c[2]) == 36937728 and c[2].L == 256
     assert synth.step_bytes(c[3]) == 10579607552 and c[3].L == 512
