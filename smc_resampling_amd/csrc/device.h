@@ -213,10 +213,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uin
 // defeats loads kept in flight), and every lane's offsets are the same for
 // every tile, so a tile costs its loads and a few scalar instructions.
 // VECLOAD (one 16-byte load per chunk) requires a 16-byte aligned row base and
-// V % DT::VEC == 0; otherwise each element is loaded on its own.  The loads
-// are non-temporal (logits are streamed, not reused from cache: measured
-// faster for the streaming and the decision kernels alike).
-template <typename DT, bool VECLOAD>
+// V % DT::VEC == 0; otherwise each element is loaded on its own.  By default
+// the loads are non-temporal (logits are streamed, not reused from cache:
+// measured faster for the streaming and the decision kernels alike); POL = 0
+// keeps them in cache for a kernel that reads the same tiles again.
+template <typename DT, bool VECLOAD, int POL = 2>
 __device__ __forceinline__ Raw<DT> load_raw(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
                                             int lane) {
   using raw = typename DT::raw;
@@ -226,7 +227,7 @@ __device__ __forceinline__ Raw<DT> load_raw(const typename DT::raw* __restrict__
       buffer_over(reinterpret_cast<const void*>(uniform64(reinterpret_cast<int64_t>(row + t0))),
                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((V - t0) * (int64_t)sizeof(raw))));
   const int lane_bytes = lane * DT::VEC * (int)sizeof(raw);  // 16
-  constexpr int pol = 2;                                      // cache policy: non-temporal
+  constexpr int pol = POL;                                    // cache policy
 #pragma unroll
   for (int c = 0; c < Raw<DT>::CHUNKS; c++) {
     const int off = lane_bytes + c * WAVE * 16;
@@ -275,10 +276,10 @@ __device__ __forceinline__ void mask_tail(Raw<DT>& r, int64_t V, int64_t tile, i
 }
 
 // load_raw then mask_tail: a tile ready to use (waits for its data).
-template <typename DT, bool VECLOAD>
+template <typename DT, bool VECLOAD, int POL = 2>
 __device__ __forceinline__ Raw<DT> load_tile(const typename DT::raw* __restrict__ row, int64_t V, int64_t tile,
                                              int lane) {
-  Raw<DT> r = load_raw<DT, VECLOAD>(row, V, tile, lane);
+  Raw<DT> r = load_raw<DT, VECLOAD, POL>(row, V, tile, lane);
   mask_tail<DT>(r, V, tile, lane);
   return r;
 }

@@ -902,7 +902,7 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_draw_tail(SdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_tree_tail: one workgroup of SD_WAVES wavefronts per token tree
+// k_tree_tail: one workgroup of TREE_WAVES wavefronts per token tree
 // ("Faster LLM Inference via Sequential Monte Carlo", sec. 4: tree-based SD;
 // multi-draft speculative sampling over the tree).  The workgroup merges the
 // statistics of every target and draft row of the tree and gathers each
@@ -918,6 +918,18 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_draw_tail(SdArgs a) {
 // searched).
 // ---------------------------------------------------------------------------
 constexpr int TREE_MAX = SMCSD_TREE_MAX_NODES;
+// 8 wavefronts: with 2 waves per SIMD the walk keeps its state in registers
+// (no scratch spills, whose stores every barrier would wait for)
+constexpr int TREE_WAVES = 8;
+constexpr int TREE_BLOCK = TREE_WAVES * WAVE;
+// Workgroup barrier that orders LDS accesses only (no wait for global
+// memory operations still in flight), for code whose waves share nothing but
+// LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 struct TreeLds {
   TailLds t;  // draw scratch: staged partials, tile masses, located tile
@@ -930,11 +942,60 @@ struct TreeLds {
   int xok[TREE_MAX];                     // node n's token lies in [0, V)
   float ut[TREE_MAX];                    // uniforms (the root's slot: the final draw)
   uint64_t kids[TREE_MAX / WAVE];        // children of the current node, as bits
-  int wcnt[SD_WAVES];                    // nodes with children per wavefront (draft-row scan)
+  int wcnt[TREE_WAVES];                    // nodes with children per wavefront (draft-row scan)
   double Z[TREE_MAX];                    // masses of the current node's rejections
   float iz[TREE_MAX];                    // 1 / Z (0: that rejection left r unchanged)
   int bad, accept;
 };
+
+// Row statistics of the RA rows at partA (into Mt/St/lSt) and the RB rows at
+// partB (into Md/Sd/lSd), each row's nseg partials folded exactly as
+// merge_rows_to folds them (16 threads per row, ascending partial index per
+// thread, the same DPP fold), so a row gets the statistics it would get there;
+// the loads of both sets are issued before any is folded.
+template <int NT>
+__device__ __forceinline__ void merge_tree_rows(const float2* __restrict__ partA, int RA,
+                                                const float2* __restrict__ partB, int RB, int nseg, TreeLds& L) {
+  constexpr int TPR = 16;
+  constexpr int GB = 4;
+  constexpr int NB = MAX_TILES / (GB * TPR);
+  const int sub = threadIdx.x & (TPR - 1);
+  const int R = RA + RB;
+  for (int r0 = 0; r0 < R; r0 += NT / TPR) {
+    const int r = r0 + (int)threadIdx.x / TPR;
+    float m = -INFINITY;
+    double s = 0.0;
+    if (r < R) {
+      const float2* row = r < RA ? partA + (int64_t)r * nseg : partB + (int64_t)(r - RA) * nseg;
+#pragma unroll
+      for (int h = 0; h < NB; h++) {
+        const int k0 = sub + h * GB * TPR;
+        if (h > 0 && nseg <= h * GB * TPR) break;
+        float2 v[GB];
+#pragma unroll
+        for (int j = 0; j < GB; j++) v[j] = row[min(k0 + j * TPR, nseg - 1)];
+#pragma unroll
+        for (int j = 0; j < GB; j++)
+          if (k0 + j * TPR < nseg) fold(m, s, v[j].x, (double)v[j].y);
+      }
+    }
+    fold_dpp<DPP_ROW_MIRROR>(m, s);
+    fold_dpp<DPP_ROW_HALF_MIRROR>(m, s);
+    fold_dpp<DPP_QUAD_XOR1>(m, s);
+    fold_dpp<DPP_QUAD_XOR2>(m, s);
+    if (r < R && sub == 0) {
+      if (r < RA) {
+        L.Mt[r] = m;
+        L.St[r] = s;
+        L.lSt[r] = log(s);
+      } else {
+        L.Md[r - RA] = m;
+        L.Sd[r - RA] = s;
+        L.lSd[r - RA] = log(s);
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ RowStat stat_at(const float* M, const double* S, const double* lS, int r) {
   RowStat rs;
@@ -980,7 +1041,7 @@ __device__ __forceinline__ void tree_weights(const Raw<DT>& rt, const Raw<DT>& r
 }
 
 template <typename DT, bool VL>
-__global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
+__global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
   using raw = typename DT::raw;
   __shared__ TreeLds L;
   const StepArgs& s = a.s;
@@ -1014,9 +1075,8 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
     un = a.uniforms[n0 + tid];
   }
   // statistics of the tree's target rows (flat rows n0 ..) and draft rows
-  // (flat rows rows_t + d0 ..)
-  merge_rows_to<SD_BLOCK>(s.part + n0 * s.nseg, M, s.nseg, L.Mt, L.St, L.lSt);
-  merge_rows_to<SD_BLOCK>(s.part + (s.rows_t + d0) * s.nseg, D, s.nseg, L.Md, L.Sd, L.lSd);
+  // (flat rows rows_t + d0 ..), all partial loads in one round trip
+  merge_tree_rows<TREE_BLOCK>(s.part + n0 * s.nseg, M, s.part + (s.rows_t + d0) * s.nseg, D, s.nseg, L);
   if (tid < M) {
     L.par[tid] = pn;
     L.drow[tid] = 0;
@@ -1043,7 +1103,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
   __syncthreads();
   // draft row of a node with children: its rank among them (node order)
   int before = 0, total = 0;
-  for (int w = 0; w < SD_WAVES; w++) {
+  for (int w = 0; w < TREE_WAVES; w++) {
     const int cnt = L.wcnt[w];
     before += w < wave ? cnt : 0;
     total += cnt;
@@ -1083,15 +1143,37 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
       // a leaf: the bonus token from p_u (its tile or segment partials)
       int bnp, bper;
       const float2* bp = bonus_partials(s, n0 + u, n0 + u, 0, &bnp, &bper);
-      stage_partials<SD_BLOCK>(bp, bnp, L.t);
+      stage_partials<TREE_BLOCK>(bp, bnp, L.t);
       __syncthreads();
-      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, st.M, ufin, bnp, bper, L.t, fl);
+      y = draw_softmax<DT, VL, TREE_WAVES>(trow, s, s.c, st.M, ufin, bnp, bper, L.t, fl);
       break;
     }
     const RowStat sd = stat_at(L.Md, L.Sd, L.lSd, dr);
     if (!sd.ok) fl |= FLAG_NONFINITE;
     const raw* drw = static_cast<const raw*>(s.draft) + (d0 + dr) * s.V;
     const float At = log2_norm(st), Ad = log2_norm(sd);
+    // weights of tile t of u's row pair after nr earlier rejections (cached
+    // loads: a second pass at u reads the same tiles again)
+    auto tile_w = [&](int t, int nr, bool sub, float (&w)[PER_LANE]) {
+      const Raw<DT> rt = load_tile<DT, VL, 0>(trow, s.V, t, lane);
+      const Raw<DT> rd = load_tile<DT, VL, 0>(drw, s.V, t, lane);
+      tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, nr, sub, w);
+    };
+    auto store_mass = [&](int t, const float (&w)[PER_LANE]) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < PER_LANE; e++) m += w[e];
+      m = wave_sum(m);
+      if (lane == 0) L.t.W[t] = (double)m;
+    };
+    // one pass over u's row pair: every tile's mass into L.t.W
+    auto pass = [&](int nr, bool sub) {
+      for (int t = wave; t < ntiles; t += TREE_WAVES) {
+        float w[PER_LANE];
+        tile_w(t, nr, sub, w);
+        store_mass(t, w);
+      }
+    };
     int nrej = 0, next = -1;
     for (int kw = 0; kw < TREE_MAX / WAVE && next < 0; kw++) {
       uint64_t bits = L.kids[kw];
@@ -1115,24 +1197,14 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
           }
           L.accept = acc;
         }
-        __syncthreads();
+        lds_barrier();
         if (L.accept) {
           next = cnode;
           break;
         }
-        // rejected: one pass over u's row pair for the mass of max(0, r - q)
-        for (int t = wave; t < ntiles; t += SD_WAVES) {
-          const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, t, lane);
-          const Raw<DT> rd = load_tile<DT, VL>(drw, s.V, t, lane);
-          float w[PER_LANE];
-          tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, nrej, true, w);
-          float m = 0.0f;
-#pragma unroll
-          for (int e = 0; e < PER_LANE; e++) m += w[e];
-          m = wave_sum(m);
-          if (lane == 0) L.t.W[t] = (double)m;
-        }
-        __syncthreads();
+        // rejected: one pass for the mass of max(0, r - q)
+        pass(nrej, true);
+        lds_barrier();
         if (wave == 0) {
           double z = 0.0;
           for (int t = lane; t < ntiles; t += WAVE) z += L.t.W[t];
@@ -1143,14 +1215,14 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
             if (!(z > 0.0)) fl |= FLAG_ZERO_RESIDUAL;  // r and q agree: r stays
           }
         }
-        __syncthreads();
+        lds_barrier();
         nrej++;
       }
     }
     if (next >= 0) {
       u = next;
       depth++;
-      __syncthreads();  // L.kids is rewritten for the next node
+      lds_barrier();  // L.kids is rewritten for the next node
       continue;
     }
     // every child rejected: the final token from the last pass's weights, or,
@@ -1159,18 +1231,8 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
     const int last = nrej - 1;
     const bool zero = !(L.Z[last] > 0.0);
     if (zero) {
-      for (int t = wave; t < ntiles; t += SD_WAVES) {
-        const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, t, lane);
-        const Raw<DT> rd = load_tile<DT, VL>(drw, s.V, t, lane);
-        float w[PER_LANE];
-        tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, last, false, w);
-        float m = 0.0f;
-#pragma unroll
-        for (int e = 0; e < PER_LANE; e++) m += w[e];
-        m = wave_sum(m);
-        if (lane == 0) L.t.W[t] = (double)m;
-      }
-      __syncthreads();
+      pass(last, false);
+      lds_barrier();
     }
     if (wave == 0) {
       auto wt = [&](int k) -> double { return L.t.W[k]; };
@@ -1189,14 +1251,13 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
         L.t.target = target - bef;  // the target inside the located tile
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int tt = L.t.sel;
-    if (wave == 0) {
-      // the located tile's weights, recomputed exactly as its pass did
+    if (wave == tt % TREE_WAVES) {
+      // the located tile's weights, recomputed exactly as its pass did (the
+      // wavefront that weighed it reads it again, likely from its cache)
       float w[PER_LANE];
-      const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tt, lane);
-      const Raw<DT> rd = load_tile<DT, VL>(drw, s.V, tt, lane);
-      tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, last, !zero, w);
+      tile_w(tt, last, !zero, w);
       auto wfn = [&](int ch, float (&x)[DT::VEC]) {
 #pragma unroll
         for (int k = 0; k < DT::VEC; k++) x[k] = w[ch * DT::VEC + k];
@@ -1209,7 +1270,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_tree_tail(TreeArgs a) {
       }
       if (lane == 0) L.t.y = tt * TILE + idx;
     }
-    __syncthreads();
+    lds_barrier();
     y = L.t.y;
     break;
   }
@@ -1555,7 +1616,7 @@ hipError_t launch_tree(const TreeArgs& a, const Plan& p, bool bf16, bool vec, hi
   if (e != hipSuccess) return e;
   const void* k = bf16 ? (vec ? tree_tail_kernel<Bf16, true>() : tree_tail_kernel<Bf16, false>())
                        : (vec ? tree_tail_kernel<F32, true>() : tree_tail_kernel<F32, false>());
-  return launch(k, (unsigned)a.B, SD_BLOCK, a, s, t.tail_start, t.tail_stop);
+  return launch(k, (unsigned)a.B, TREE_BLOCK, a, s, t.tail_start, t.tail_stop);
 }
 
 }  // namespace smcsd
