@@ -1,7 +1,7 @@
 /*
  * smcsd.h -- C ABI of the MI355X (gfx950) verify-and-sample library.
  *
- * Two operations, each one step of speculative decoding:
+ * The verify-and-sample step of speculative decoding:
  *
  *   sd_verify              standard speculative decoding: turn the target and
  *                          draft logits of B sequences into the number of
@@ -13,6 +13,13 @@
  *                          sample size and, when it falls below the threshold,
  *                          resample systematically and permute the particles'
  *                          KV page-table rows.
+ * and the steps around it:
+ *   smc_reweight_resample_power  the same SMC step for a power target p^beta;
+ *   smc_pages_append / smc_pages_resample  paged-KV bookkeeping (reference
+ *                          counts, free list, copy-on-write) around it;
+ *   draft_sample, pacer_lengths  the draft side: token draws from q and PACER
+ *                          draft lengths;
+ *   tree_verify            verification of token trees.
  *
  * Where the operations are defined (pages by title and section):
  *   "Faster LLM Inference via Sequential Monte Carlo"
@@ -129,8 +136,9 @@ int32_t smcsd_abi_version(void);
 const char* smcsd_status_string(int32_t status);
 
 /*
- * Profiling aid for benchmarks: the next sd_verify or smc_reweight_resample
- * call made by the calling thread launches its two kernels so that the given
+ * Profiling aid for benchmarks: the next sd_verify, smc_reweight_resample,
+ * draft_sample or tree_verify call made by the calling thread launches its
+ * two kernels so that the given
  * events take the start and stop times of the kernels themselves:
  * stream_start / stream_stop for the logit-streaming kernel, tail_start /
  * tail_stop for the decision kernel.  hipEventElapsedTime of a pair is then
