@@ -37,6 +37,15 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for global memory operations still in flight (stores of
+// outputs, loads issued ahead).  For code whose waves share nothing but LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 struct Bf16 {
   using raw = uint16_t;
   static constexpr int VEC = 8;

@@ -922,14 +922,6 @@ constexpr int TREE_MAX = SMCSD_TREE_MAX_NODES;
 // (no scratch spills, whose stores every barrier would wait for)
 constexpr int TREE_WAVES = 8;
 constexpr int TREE_BLOCK = TREE_WAVES * WAVE;
-// Workgroup barrier that orders LDS accesses only (no wait for global
-// memory operations still in flight), for code whose waves share nothing but
-// LDS.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 struct TreeLds {
   TailLds t;  // draw scratch: staged partials, tile masses, located tile
