@@ -81,7 +81,8 @@ struct TreeArgs {
 // Segment length and streaming grid of a call.
 struct Plan {
   int seg, nseg;
-  bool tp;  // bonus-row tile partials (segments long enough that a re-read would cost)
+  bool tp;    // bonus-row tile partials (segments long enough that a re-read would cost)
+  bool wide;  // k_stream_wide (bf16, one-tile segments)
   int64_t units;
   int grid;
 };
