@@ -474,7 +474,8 @@ def main():
                    **({"draft_sample_rows": R_draw} if args.draft_sample else {}),
                    **({"tree": dict(cfg.tree, nodes=len(synth.full_tree_parents(**cfg.tree)))}
                       if cfg.kind == "tree" else {})},
-        "roofline": {"bound": "hbm", "kernel": "k_stream", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "logit streaming (k_stream, or k_stream_wide for one-tile segments)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (traffic_from_profiles(cfg.name) if args.beta is None and not args.draft_sample
                                  else None),
