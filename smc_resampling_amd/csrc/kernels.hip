@@ -696,18 +696,28 @@ __device__ __forceinline__ float log2_norm(const RowStat& rs) {
 // ---------------------------------------------------------------------------
 // tails: per-group inputs
 // ---------------------------------------------------------------------------
-// Draft token of this thread's row (threads tid < 2 kb: target row tid, then
-// draft row tid - kb, both with token x_{tid mod kb}).
+// The token work of a workgroup of NT threads runs on its highest threads
+// (slot NT - 1 - threadIdx.x), which the statistics merge (on the lowest
+// threads) leaves idle: the two dependent round trips of the token logits
+// (token, then its logit) overlap the merge's round trip and fold.
+template <int NT>
+__device__ __forceinline__ int token_slot() {
+  return NT - 1 - (int)threadIdx.x;
+}
+
+// Draft token of this thread's row (slots t < 2 kb: target row t, then draft
+// row t - kb, both with token x_{t mod kb}).
+template <int NT>
 __device__ __forceinline__ int32_t token_of(const StepArgs& a, const Group& G) {
-  const int tid = threadIdx.x, kb = G.kb;
+  const int tid = token_slot<NT>(), kb = G.kb;
   return tid < 2 * kb ? a.tokens[G.d0 + (tid < kb ? tid : tid - kb)] : 0;
 }
 
 // Logit of this thread's draft token and whether the token lies in [0, V).
-template <typename DT>
+template <typename DT, int NT>
 __device__ __forceinline__ float token_logit(const StepArgs& a, const Group& G, int64_t g, int32_t x, int* ok) {
   using raw = typename DT::raw;
-  const int tid = threadIdx.x, kb = G.kb;
+  const int tid = token_slot<NT>(), kb = G.kb;
   *ok = 1;
   if (tid >= 2 * kb) return 0.0f;
   *ok = x >= 0 && x < a.V;
@@ -715,8 +725,9 @@ __device__ __forceinline__ float token_logit(const StepArgs& a, const Group& G, 
   return *ok && row ? DT::to_f32(row[x]) : 0.0f;
 }
 
+template <int NT>
 __device__ __forceinline__ void store_tokens(float z, int ok, float u, int kb, TailLds& L) {
-  const int tid = threadIdx.x;
+  const int tid = token_slot<NT>();
   if (tid < 2 * kb) {
     L.z[tid] = z;
     if (tid < kb) {
@@ -758,18 +769,19 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   const int64_t t0 = G.d0 + b;
   const float2* pg = s.part + G.fr0 * s.nseg;
   if (threadIdx.x == 0) L.fl = 0;
-  const int32_t xt = token_of(s, G);
-  const float uj = (int)threadIdx.x < kb ? a.uniforms[t0 + threadIdx.x] : 0.0f;
+  const int32_t xt = token_of<SD_BLOCK>(s, G);
+  const int slot = token_slot<SD_BLOCK>();
+  const float uj = slot < kb ? a.uniforms[t0 + slot] : 0.0f;
   const float ufin = a.uniforms[t0 + kb];
-  // the partials' loads go out before the token logits', which wait for the
-  // tokens
+  // the merge runs on the lowest threads while the highest ones wait for the
+  // tokens, then for their logits
   merge_rows<SD_BLOCK>(pg, 2 * kb + 1, s.nseg, L);
   int bnp, bper;
   const float2* bp = bonus_partials(s, G.fr0, b, kb, &bnp, &bper);
   stage_partials<SD_BLOCK>(bp, bnp, L);
   int ok = 1;
-  const float z = token_logit<DT>(s, G, b, xt, &ok);
-  store_tokens(z, ok, uj, kb, L);
+  const float z = token_logit<DT, SD_BLOCK>(s, G, b, xt, &ok);
+  store_tokens<SD_BLOCK>(z, ok, uj, kb, L);
   __syncthreads();
   uint32_t fl = 0;
   // accept test up to the first rejection
@@ -1447,7 +1459,7 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   const Group G = group_of(i, K, nullptr, s.rows_d);
   const float2* pg = s.part + G.fr0 * s.nseg;
   if (threadIdx.x == 0) L.fl = 0;
-  const int32_t xt = token_of(s, G);
+  const int32_t xt = token_of<BLOCK>(s, G);
   const float lw_in = a.logw[i];
   const float ub = a.bonus_u[i];
   merge_rows<BLOCK>(pg, 2 * K + 1, s.nseg, L);
@@ -1455,8 +1467,8 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   const float2* bp = bonus_partials(s, G.fr0, i, K, &bnp, &bper);
   stage_partials<BLOCK>(bp, bnp, L);
   int ok = 1;
-  const float z = token_logit<DT>(s, G, i, xt, &ok);
-  store_tokens(z, ok, 0.0f, K, L);
+  const float z = token_logit<DT, BLOCK>(s, G, i, xt, &ok);
+  store_tokens<BLOCK>(z, ok, 0.0f, K, L);
   __syncthreads();
   uint32_t fl = 0;
   float lw = 0.0f;
