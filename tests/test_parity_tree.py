@@ -172,3 +172,39 @@ def test_tree_generated_workload_steps():
         case = dict(target=host_logits(bt["target"]), draft=host_logits(bt["draft"]), T=cfg.T,
                     **{k: bt[k].cpu().numpy() for k in ("node_off", "draft_off", "parent", "tokens", "uniforms")})
         check_tree(case, f"{cfg.name} step {step}")
+
+
+def test_tree_workspace_shared_with_sd_verify():
+    """One workspace serves tree calls of different shapes interleaved with
+    sd_verify calls: the tree call uses no counters, and the partials each
+    call reads are the ones it wrote."""
+    import torch
+
+    import oracle
+    import smc_resampling_amd as s
+    from compare import compare_sd, compare_tree
+    from gpu_util import DEV, dev_logits
+    from synth.small import sd_case
+
+    rng = np.random.default_rng(23)
+    nbytes = max(s.tree_verify_workspace_bytes(1, 40, 20000, 40 * 64, 40 * 63),
+                 s.sd_verify_workspace_bytes(1, 40, 8, 20000, 40 * 8))
+    ws = s.new_workspace(nbytes, DEV)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    for i, (B, V) in enumerate([(40, 20000), (3, 50), (17, 2049), (40, 20000)]):
+        trees = [tree_parents("random", rng, M=int(m)) for m in rng.integers(1, 65, B)]
+        c = tree_case(300 + i, trees, V, T=0.8, delta=1.0, dtype="bf16")
+        out = s.tree_verify(dev_logits(c["target"]), dev_logits(c["draft"]), t(c["node_off"]), t(c["draft_off"]),
+                            t(c["parent"]), t(c["tokens"]), t(c["uniforms"]), c["T"], workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.tree_verify(c["target"], c["draft"], c["node_off"], c["draft_off"], c["parent"], c["tokens"],
+                                 c["uniforms"], c["T"])
+        compare_tree(c, ref, out["num_accepted"].cpu().numpy(), out["last_node"].cpu().numpy(),
+                     out["final_token"].cpu().numpy(), f"shared workspace tree {i}").assert_ok()
+        assert int(out["status_flags"].item()) & ~8 == 0
+        sc = sd_case(310 + i, min(B, 40), V, T=1.0, K=int(rng.integers(0, 9)), delta=1.0, dtype="bf16")
+        na, ft, fl = s.sd_verify(dev_logits(sc["target"]), dev_logits(sc["draft"]), t(sc["tokens"]),
+                                 t(sc["uniforms"]), sc["T"], K=sc["K"], workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.sd_verify(sc["target"], sc["draft"], sc["tokens"], sc["uniforms"], sc["T"], K=sc["K"])
+        compare_sd(sc, ref, na.cpu().numpy(), ft.cpu().numpy(), f"shared workspace sd {i}").assert_ok()
