@@ -208,3 +208,34 @@ def test_sd_multi_tile_segments_sampled():
     t.assert_ok()
     assert (na[pick] == K).sum() >= 4  # the picked even sequences (draft == target) take the bonus draw
     assert int(fl.item()) & ~8 == 0
+
+
+def test_sd_decisions_do_not_depend_on_segmentation():
+    """The same 64 sequences decided in a small call (one-tile segments) and
+    as 40 identical replicas in one large call (multi-tile segments, where the
+    bonus rows keep tile partials): every replica decides alike, and the two
+    calls agree on every decision whose uniform is not within the band of a
+    boundary (the row statistics then differ only in rounding)."""
+    import torch
+
+    import smc_resampling_amd as s
+    from compare import BAND
+    from gpu_util import DEV, dev_logits, run_sd_oracle
+
+    B0, R, K, V, T = 64, 40, 4, 32768, 0.7
+    c = sd_case(4300, B0, V, T=T, K=K, delta=np.array([(0.5, 1.0, 2.0)[b % 3] for b in range(B0)]), dtype="bf16")
+    tok = torch.from_numpy(c["tokens"]).to(DEV)
+    u = torch.from_numpy(c["uniforms"]).to(DEV)
+    na1, ft1, _ = s.sd_verify(dev_logits(c["target"]), dev_logits(c["draft"]), tok, u, T, K=K)
+    naR, ftR, flR = s.sd_verify(dev_logits(c["target"]).repeat(R, 1), dev_logits(c["draft"]).repeat(R, 1),
+                                tok.repeat(R), u.repeat(R), T, K=K)
+    torch.cuda.synchronize()
+    na1, ft1 = na1.cpu().numpy(), ft1.cpu().numpy()
+    naR, ftR = naR.cpu().numpy().reshape(R, B0), ftR.cpu().numpy().reshape(R, B0)
+    assert (naR == naR[0]).all() and (ftR == ftR[0]).all()  # replicas alike
+    ref = run_sd_oracle(c)
+    am = ref["accept_margin"].reshape(B0, K)
+    near = (np.where(am >= 0, am, np.inf).min(axis=1) < BAND) | (ref["sample_margin"] < BAND)
+    differ = (naR[0] != na1) | (ftR[0] != ft1)
+    assert not (differ & ~near).any(), np.nonzero(differ & ~near)
+    assert int(flR.item()) & ~8 == 0

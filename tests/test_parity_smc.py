@@ -200,3 +200,14 @@ def test_smc_workspace_reuse():
                  pt_out=out["page_table_out"].cpu().numpy())
         compare_smc(c, ref, g, c["logw"], c["pt"], f"reuse {i}").assert_ok()
         assert int(out["status_flags"].item()) & ~8 == 0
+
+
+def test_smc_deterministic():
+    """Two runs of the same SMC step give bitwise-equal outputs."""
+    from gpu_util import run_smc_gpu
+
+    c = smc_case(4400, 4, 64, 4, 20000, dtype="bf16", L=8, logw_scale=2.0)
+    a = run_smc_gpu(c, c["logw"], c["pt"], 0.9)
+    b = run_smc_gpu(c, c["logw"], c["pt"], 0.9)
+    for k in ("bonus", "ancestors", "ess", "resampled", "logw", "pt_out"):
+        assert (a[k] == b[k]).all(), k

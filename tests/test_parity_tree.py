@@ -208,3 +208,16 @@ def test_tree_workspace_shared_with_sd_verify():
         torch.cuda.synchronize()
         ref = oracle.sd_verify(sc["target"], sc["draft"], sc["tokens"], sc["uniforms"], sc["T"], K=sc["K"])
         compare_sd(sc, ref, na.cpu().numpy(), ft.cpu().numpy(), f"shared workspace sd {i}").assert_ok()
+
+
+def test_tree_deterministic():
+    """Two runs of the same tree call give bitwise-equal outputs."""
+    from gpu_util import run_tree_gpu
+
+    rng = np.random.default_rng(29)
+    c = tree_case(4500, [tree_parents("random", rng, M=int(m)) for m in rng.integers(1, 80, 32)], 20000, T=0.8,
+                  delta=1.5, dtype="bf16")
+    a = run_tree_gpu(c)
+    b = run_tree_gpu(c)
+    for x, y in zip(a, b):
+        assert np.array_equal(np.asarray(x), np.asarray(y))
