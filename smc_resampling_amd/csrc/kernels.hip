@@ -579,13 +579,19 @@ __device__ __forceinline__ float2 tile_partial_of(const Raw<DT>& r, float c) {
   return wave_partial(m, s);
 }
 
+struct NoIdleWork {
+  __device__ void operator()() const {}
+};
+
 // Inverse-CDF draw from softmax(z c) of `row` (row maximum M, log2 domain)
 // with uniform u.  L.P holds np partials of the row, each over `per` tiles (a
 // bonus row's own tile partials, or segment partials).  Whole workgroup;
-// every thread gets the token.
-template <typename DT, bool VL, int NW = WAVES_PER_BLOCK>
+// every thread gets the token.  While wavefront 0 reloads and searches the
+// located tile, the other wavefronts run `idle` (memory operations it leaves
+// in flight do not hold up the closing barrier, which orders LDS only).
+template <typename DT, bool VL, int NW = WAVES_PER_BLOCK, typename Idle = NoIdleWork>
 __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const StepArgs& a, float c, float M, double u,
-                            int np, int per, TailLds& L, uint32_t& fl) {
+                            int np, int per, TailLds& L, uint32_t& fl, Idle idle = Idle()) {
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   // 1. the segment
   if (wave == 0) {
@@ -660,8 +666,10 @@ __device__ int draw_softmax(const typename DT::raw* __restrict__ row, const Step
       idx = last_pos >= 0 ? last_pos : 0;
     }
     if (lane == 0) L.y = tt * TILE + idx;
+  } else {
+    idle();
   }
-  __syncthreads();
+  lds_barrier();
   return L.y;
 }
 
@@ -1472,7 +1480,10 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   __syncthreads();
   uint32_t fl = 0;
   float lw = 0.0f;
-  if (wave == 0) {
+  // wavefront 1 forms the new log-weight while wavefront 0 locates the bonus
+  // draw's tile, and publishes it while wavefront 0 reloads and searches that
+  // tile: the prompt's resampling needs the log-weights, not the bonus tokens
+  if (wave == 1) {
     double delta = 0.0;
     for (int j0 = 0; j0 < K; j0 += WAVE) {
       const int j = j0 + lane;
@@ -1490,20 +1501,28 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   }
   const RowStat sk = stat_of(L, K);
   if (!sk.ok) fl |= FLAG_NONFINITE;
-  // the bonus row's statistics and draw are at its own scale (beta / T)
-  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, s.cb, sk.M, (double)ub, bnp, bper, L, fl);
-  or_flags(fl, L);
-  __syncthreads();
   const int64_t p = i / a.N;
+  uint32_t before = 0;
+  // the log-weight is visible before the count that announces it
+  auto publish = [&]() {
+    if (wave == 1 && lane == 0) {
+      st_dev(a.ws_logw + i, lw);
+      stores_done();
+      before = ctr_add(s.ctr + p * CTR_STRIDE, 1u);
+    }
+  };
+  // the bonus row's statistics and draw are at its own scale (beta / T)
+  const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, s.cb, sk.M, (double)ub, bnp, bper, L, fl,
+                                     publish);
+  or_flags(fl, L);
+  if (wave == 1 && lane == 0) s_last = before + 1u == (uint32_t)a.N;
+  __syncthreads();
   if (threadIdx.x == 0) {
     a.bonus_token[i] = y;
-    st_dev(a.ws_logw + i, lw);  // thread 0 is lane 0 of wave 0, which holds lw
     raise_flags(s.flags, L.fl);
-    stores_done();
-    s_last = ctr_add(s.ctr + p * CTR_STRIDE, 1u) + 1u == (uint32_t)a.N;
   }
-  __syncthreads();
   if (s_last) {
+    lds_barrier();  // thread 0 has read L.fl: the prompt's LDS overlays it
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     smc_prompt_tail(a, p, sh.p);
   }
