@@ -28,6 +28,10 @@
 //                    whose page reached zero are staged per row in entry
 //                    order, the last workgroup to finish lays the rows out on
 //                    the stack by a scan, and a third launch pushes them.
+//                    Calls of at most 16 rows of at most 256 entries run in
+//                    one workgroup instead: each wavefront keeps the entries
+//                    it marks in registers and, after a barrier, pushes the
+//                    freed ones itself (no marks, no staging).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -439,20 +443,15 @@ __device__ __forceinline__ uint32_t entry_key(const ResampleArgs& a, int64_t k, 
   return (uint32_t)(a.R * a.L - (k * a.L + j));  // larger for earlier entries; 0 = none
 }
 
-// Workgroup (row block x, position block y): 64 rows as the lanes of every
-// wavefront, 16 positions per wavefront.
-__global__ __launch_bounds__(BLOCK) void k_pages_delta(ResampleArgs a) {
-  __shared__ int32_t copies[WAVE];
-  const int lane = threadIdx.x % WAVE;
-  const int64_t rb = (int64_t)blockIdx.x * WAVE;
-  const int N = a.N;
-  if (threadIdx.x < WAVE) copies[threadIdx.x] = 0;
-  __syncthreads();
+// Copies of each of the 64 rows of block rb: the slots of their prompts that
+// name them (NT threads; copies[] zeroed before).  Returns bad-input bits.
+template <int NT>
+__device__ uint32_t delta_copies(const ResampleArgs& a, int64_t rb, int32_t* copies) {
   uint32_t bad = 0;
-  // copies of each of the 64 rows: the slots of their prompts naming them
+  const int N = a.N;
   const int64_t rl = (rb + WAVE < a.R ? rb + WAVE : a.R) - 1;
   const int64_t s1 = (rl / N + 1) * N < a.R ? (rl / N + 1) * N : a.R;
-  for (int64_t r = (rb / N) * N + threadIdx.x; r < s1; r += BLOCK) {
+  for (int64_t r = (rb / N) * N + threadIdx.x; r < s1; r += NT) {
     const int32_t anc = a.ancestors[r];
     if (anc < 0 || anc >= N) {
       bad = FLAG_BAD_INPUT;
@@ -461,16 +460,30 @@ __global__ __launch_bounds__(BLOCK) void k_pages_delta(ResampleArgs a) {
     const int64_t t = (r / N) * N + anc - rb;
     if (t >= 0 && t < WAVE) atomicAdd(&copies[t], 1);
   }
-  __syncthreads();
+  return bad;
+}
+
+constexpr int JW = PB / WAVES_PER_BLOCK;  // positions per wavefront
+
+// One wavefront: rows rb .. rb+63 as the lanes (c = this lane's row's
+// copies), positions j0 .. j0+JW-1.  With write_len, also the rows' new
+// lengths.  An entry that starts a run of dying rows offers its key as the
+// page's first and is marked: in the marks array (MARKS), or in bit i of
+// `held` with its page id left in pv[i].  Returns bad-input bits.
+template <bool MARKS>
+__device__ __forceinline__ uint32_t delta_positions(const ResampleArgs& a, int64_t rb, int j0, int32_t c,
+                                                    bool write_len, int32_t (&pv)[JW], uint32_t& held) {
+  const int lane = threadIdx.x % WAVE;
+  const int N = a.N;
+  uint32_t bad = 0;
   const int64_t k = rb + lane;
   const bool in = k < a.R;
-  const int32_t c = copies[lane];
   int32_t ln = in ? a.len_in[k] : 0;
   if (ln < 0 || ln > (int64_t)a.L * a.S) {
     bad = FLAG_BAD_INPUT;
     ln = 0;
   }
-  if (blockIdx.y == 0 && wave_id() == 0 && in) {
+  if (write_len && in) {
     const int32_t anc = a.ancestors[k];
     if (anc >= 0 && anc < N) {
       const int32_t la = a.len_in[(k / N) * N + anc];
@@ -479,113 +492,122 @@ __global__ __launch_bounds__(BLOCK) void k_pages_delta(ResampleArgs a) {
     }
   }
   const int32_t used = (int32_t)used_pages(ln, a.S);
-  const int j0 = blockIdx.y * PB + wave_id() * (PB / WAVES_PER_BLOCK);
   // nothing to do where every row is copied exactly once
-  if (__ballot(in && c != 1 && used > j0)) {
-    constexpr int JW = PB / WAVES_PER_BLOCK;
-    int32_t pv[JW];
+  held = 0;
+  if (!__ballot(in && c != 1 && used > j0)) return bad;
 #pragma unroll
-    for (int i = 0; i < JW; i++) pv[i] = in && j0 + i < used ? a.table_old[k * a.L + j0 + i] : -1;
-    // A run of lanes naming one page holds valid entries only, so its sum of
-    // (copies - 1) is a difference of two prefixes over the lanes, the same
-    // at every position.
-    const int32_t v = in ? c - 1 : 0;
-    int32_t pre = v;  // inclusive prefix of v over the lanes
+  for (int i = 0; i < JW; i++) pv[i] = in && j0 + i < used ? a.table_old[k * a.L + j0 + i] : -1;
+  // A run of lanes naming one page holds valid entries only, so its sum of
+  // (copies - 1) is a difference of two prefixes over the lanes, the same
+  // at every position.
+  const int32_t v = in ? c - 1 : 0;
+  int32_t pre = v;  // inclusive prefix of v over the lanes
 #pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-      const int32_t y = __shfl_up(pre, d);
-      if (lane >= d) pre += y;
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int32_t y = __shfl_up(pre, d);
+    if (lane >= d) pre += y;
+  }
+  const uint64_t dying_rows = __ballot(in && c == 0);
+  // runs at every position first (no branches: the positions interleave) ...
+  bool head[JW];
+  int32_t end[JW], pre_end[JW];
+#pragma unroll
+  for (int i = 0; i < JW; i++) {
+    bool valid = in && j0 + i < used;
+    if (valid && (pv[i] < 0 || pv[i] >= a.M)) {
+      bad = FLAG_BAD_INPUT;
+      valid = false;
     }
-    const uint64_t dying_rows = __ballot(in && c == 0);
-    // runs at every position first (no branches: the positions interleave) ...
-    bool head[JW];
-    int32_t end[JW], pre_end[JW];
+    pv[i] = valid ? pv[i] : -1;
+    const int32_t pp = __shfl_up(pv[i], 1);
+    const bool starts = lane == 0 || pp != pv[i];
+    head[i] = starts && valid;
+    const uint64_t heads = __ballot(starts);
+    const uint64_t later = lane == WAVE - 1 ? 0 : heads & (~0ull << (lane + 1));
+    end[i] = later ? __builtin_ctzll(later) - 1 : WAVE - 1;
+    pre_end[i] = __shfl(pre, end[i]);
+  }
+  // ... then one update per run
 #pragma unroll
-    for (int i = 0; i < JW; i++) {
-      bool valid = in && j0 + i < used;
-      if (valid && (pv[i] < 0 || pv[i] >= a.M)) {
-        bad = FLAG_BAD_INPUT;
-        valid = false;
-      }
-      pv[i] = valid ? pv[i] : -1;
-      const int32_t pp = __shfl_up(pv[i], 1);
-      const bool starts = lane == 0 || pp != pv[i];
-      head[i] = starts && valid;
-      const uint64_t heads = __ballot(starts);
-      const uint64_t later = lane == WAVE - 1 ? 0 : heads & (~0ull << (lane + 1));
-      end[i] = later ? __builtin_ctzll(later) - 1 : WAVE - 1;
-      pre_end[i] = __shfl(pre, end[i]);
-    }
-    // ... then one update per run
-#pragma unroll
-    for (int i = 0; i < JW; i++) {
-      if (!head[i]) continue;
-      const int32_t p = pv[i];
-      const int32_t sum = pre_end[i] - pre + v;  // over lanes lane .. end
-      if (sum) atomicAdd(&a.ref[p], sum);
-      const int n = end[i] - lane + 1;
-      const uint64_t run = (n == WAVE ? ~0ull : (1ull << n) - 1) << lane;
-      if ((dying_rows & run) == run) {
-        // every row of the run dies: its first entry may be the page's first
-        const int64_t j = j0 + i;
-        atomicMax(&a.first[p], entry_key(a, k, j));
-        atomicOr(&a.marks[k * a.W + j / 32], 1u << (j % 32));
-      }
+  for (int i = 0; i < JW; i++) {
+    if (!head[i]) continue;
+    const int32_t p = pv[i];
+    const int32_t sum = pre_end[i] - pre + v;  // over lanes lane .. end
+    if (sum) atomicAdd(&a.ref[p], sum);
+    const int n = end[i] - lane + 1;
+    const uint64_t run = (n == WAVE ? ~0ull : (1ull << n) - 1) << lane;
+    if ((dying_rows & run) == run) {
+      // every row of the run dies: its first entry may be the page's first
+      const int64_t j = j0 + i;
+      atomicMax(&a.first[p], entry_key(a, k, j));
+      if (MARKS) atomicOr(&a.marks[k * a.W + j / 32], 1u << (j % 32));
+      else held |= 1u << i;
     }
   }
+  return bad;
+}
+
+// Workgroup (row block x, position block y): 64 rows as the lanes of every
+// wavefront, JW positions per wavefront.
+__global__ __launch_bounds__(BLOCK) void k_pages_delta(ResampleArgs a) {
+  __shared__ int32_t copies[WAVE];
+  const int lane = threadIdx.x % WAVE;
+  const int64_t rb = (int64_t)blockIdx.x * WAVE;
+  if (threadIdx.x < WAVE) copies[threadIdx.x] = 0;
+  __syncthreads();
+  uint32_t bad = delta_copies<BLOCK>(a, rb, copies);
+  __syncthreads();
+  int32_t pv[JW];
+  uint32_t held;
+  bad |= delta_positions<true>(a, rb, blockIdx.y * PB + wave_id() * JW, copies[lane],
+                               blockIdx.y == 0 && wave_id() == 0, pv, held);
   if (bad) raise_flags(a.flags, bad);
 }
 
-// One wavefront per row: the marked entries whose page reached zero and whose
+// One wavefront, row k: the marked entries whose page reached zero and whose
 // entry is that page's first, staged in entry order; the marks and keys are
-// cleared.  The last workgroup to finish lays the rows' pages out on the stack.
-__global__ __launch_bounds__(BLOCK) void k_pages_stage(ResampleArgs a) {
-  __shared__ int64_t lds[WAVES_PER_BLOCK + 1];
-  __shared__ bool s_last;
+// cleared, and the row's count stored.
+__device__ void stage_row(const ResampleArgs& a, int64_t k) {
   const int lane = threadIdx.x % WAVE;
-  const int64_t k = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wave_id();
-  if (k < a.R) {
-    int32_t n = 0;
-    for (int w0 = 0; w0 < a.W; w0 += WAVE) {
-      uint32_t* mk = a.marks + k * a.W + w0;
-      const uint32_t word = w0 + lane < a.W ? mk[lane] : 0u;
-      if (!__ballot(word != 0)) continue;
-      const int nw = a.W - w0 < WAVE ? a.W - w0 : WAVE;
-      for (int w = 0; w < nw; w += 2) {
-        const uint32_t lo = __builtin_amdgcn_readlane(word, w);
-        const uint32_t hi = w + 1 < nw ? __builtin_amdgcn_readlane(word, w + 1) : 0u;
-        if (!(lo | hi)) continue;
-        const int64_t j = (int64_t)(w0 + w) * 32 + lane;
-        const bool marked = ((lane < 32 ? lo >> lane : hi >> (lane - 32)) & 1u) != 0;
-        bool freed = false;
-        int32_t p = -1;
-        if (marked) {
-          p = a.table_old[k * a.L + j];
-          if (ld_agent(&a.first[p]) == entry_key(a, k, j)) {
-            a.first[p] = 0;
-            freed = ld_agent(&a.ref[p]) == 0;
-          }
+  int32_t n = 0;
+  for (int w0 = 0; w0 < a.W; w0 += WAVE) {
+    uint32_t* mk = a.marks + k * a.W + w0;
+    const uint32_t word = w0 + lane < a.W ? ld_agent(mk + lane) : 0u;
+    if (!__ballot(word != 0)) continue;
+    const int nw = a.W - w0 < WAVE ? a.W - w0 : WAVE;
+    for (int w = 0; w < nw; w += 2) {
+      const uint32_t lo = __builtin_amdgcn_readlane(word, w);
+      const uint32_t hi = w + 1 < nw ? __builtin_amdgcn_readlane(word, w + 1) : 0u;
+      if (!(lo | hi)) continue;
+      const int64_t j = (int64_t)(w0 + w) * 32 + lane;
+      const bool marked = ((lane < 32 ? lo >> lane : hi >> (lane - 32)) & 1u) != 0;
+      bool freed = false;
+      int32_t p = -1;
+      if (marked) {
+        p = a.table_old[k * a.L + j];
+        if (ld_agent(&a.first[p]) == entry_key(a, k, j)) {
+          a.first[p] = 0;
+          freed = ld_agent(&a.ref[p]) == 0;
         }
-        const uint64_t bal = __ballot(freed);
-        if (freed) a.staged[k * a.L + n + __builtin_popcountll(bal & ((1ull << lane) - 1))] = p;
-        n += __builtin_popcountll(bal);
       }
-      if (word) mk[lane] = 0;
+      const uint64_t bal = __ballot(freed);
+      if (freed) a.staged[k * a.L + n + __builtin_popcountll(bal & ((1ull << lane) - 1))] = p;
+      n += __builtin_popcountll(bal);
     }
-    if (lane == 0) st_agent(&a.counts[k], n);
+    if (word) mk[lane] = 0;
   }
-  // the last workgroup: stack positions of each row's pages
-  mem_done();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(a.arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  // each thread takes SCAN_RPT consecutive rows: one trip to memory per
-  // BLOCK * SCAN_RPT rows
+  if (lane == 0) st_agent(&a.counts[k], n);
+}
+
+// Whole workgroup of NT threads, after every row's count is stored: the stack
+// position of each row's pages (an exclusive scan of the counts, NT * 8 rows
+// per trip to memory); thread 0 records the stack height before the push and
+// raises it.  lds holds NT / WAVE + 1 values.
+template <int NT>
+__device__ void scan_offsets(const ResampleArgs& a, int64_t* lds) {
   constexpr int SCAN_RPT = 8;
   int64_t carry = 0;
-  for (int64_t r0 = 0; r0 < a.R; r0 += (int64_t)BLOCK * SCAN_RPT) {
+  for (int64_t r0 = 0; r0 < a.R; r0 += (int64_t)NT * SCAN_RPT) {
     const int64_t r = r0 + (int64_t)threadIdx.x * SCAN_RPT;
     int32_t n[SCAN_RPT];
     int64_t v = 0;
@@ -594,32 +616,138 @@ __global__ __launch_bounds__(BLOCK) void k_pages_stage(ResampleArgs a) {
 #pragma unroll
     for (int i = 0; i < SCAN_RPT; i++) v += n[i];
     int64_t t;
-    int64_t off = carry + block_excl_scan<BLOCK>(v, lds, &t);
+    int64_t off = carry + block_excl_scan<NT>(v, lds, &t);
 #pragma unroll
     for (int i = 0; i < SCAN_RPT; i++) {
-      if (r + i < a.R) a.offsets[r + i] = (int32_t)off;
+      if (r + i < a.R) st_agent(&a.offsets[r + i], (int32_t)off);
       off += n[i];
     }
     carry += t;
   }
   if (threadIdx.x == 0) {
-    __hip_atomic_store(a.arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int32_t fc = *a.free_count;
-    *a.base = fc;
+    st_agent(a.base, fc);
     if ((int64_t)fc + carry > a.M) raise_flags(a.flags, FLAG_BAD_INPUT);  // the counts were not consistent
     *a.free_count = (int32_t)((int64_t)fc + carry < a.M ? (int64_t)fc + carry : a.M);
   }
 }
 
+// One wavefront, row k: push the row's staged pages.
+__device__ void push_row(const ResampleArgs& a, int64_t k) {
+  const int lane = threadIdx.x % WAVE;
+  const int64_t base = (int64_t)ld_agent(a.base) + ld_agent(&a.offsets[k]);
+  const int32_t n = ld_agent(&a.counts[k]);
+  for (int i = lane; i < n; i += WAVE)
+    if (base + i < a.M) a.free_pages[base + i] = ld_agent(&a.staged[k * a.L + i]);
+}
+
+// One wavefront per row stages; the last workgroup to finish lays the rows'
+// pages out on the stack.
+__global__ __launch_bounds__(BLOCK) void k_pages_stage(ResampleArgs a) {
+  __shared__ int64_t lds[WAVES_PER_BLOCK + 1];
+  __shared__ bool s_last;
+  const int64_t k = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wave_id();
+  if (k < a.R) stage_row(a, k);
+  mem_done();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  scan_offsets<BLOCK>(a, lds);
+  if (threadIdx.x == 0) __hip_atomic_store(a.arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One wavefront per row: push the staged pages.
 __global__ __launch_bounds__(BLOCK) void k_pages_push(ResampleArgs a) {
-  const int lane = threadIdx.x % WAVE;
   const int64_t k = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wave_id();
-  if (k >= a.R) return;
-  const int64_t base = (int64_t)*a.base + a.offsets[k];
-  const int32_t n = a.counts[k];
-  for (int i = lane; i < n; i += WAVE)
-    if (base + i < a.M) a.free_pages[base + i] = a.staged[k * a.L + i];
+  if (k < a.R) push_row(a, k);
+}
+
+// Small calls (at most 16 rows of at most 256 entries): the whole resample in
+// one workgroup.  Wavefront w takes positions JW w .. JW w + JW-1 of every row
+// (rows as lanes) and keeps the entries it marks, with their page ids, in
+// registers.  After one barrier the counts are final: each such entry reads
+// its page's count and first key together, and the entries whose page reached
+// zero and that are the page's first go straight onto the stack, in row order
+// and entry order within a row (a scan over (row, wavefront) in LDS).  No marks,
+// no staging.
+constexpr int PG_SMALL_ROWS = PG_BLOCK / WAVE;
+constexpr int PG_SMALL_L = PG_SMALL_ROWS * JW;
+
+__global__ __launch_bounds__(PG_BLOCK) void k_pages_resample_small(ResampleArgs a) {
+  constexpr int NW = PG_BLOCK / WAVE;
+  static_assert(NW * JW == PG_SMALL_L && NW <= WAVE, "one slice of positions per wavefront");
+  __shared__ int32_t copies[WAVE];
+  __shared__ int32_t off[NW][PG_SMALL_ROWS];  // freed entries of (wavefront, row), then their stack offsets
+  __shared__ int32_t s_total;
+  const int lane = threadIdx.x % WAVE, wave = wave_id();
+  const int64_t fc = *a.free_count;
+  if (threadIdx.x < WAVE) copies[threadIdx.x] = 0;
+  __syncthreads();
+  uint32_t bad = delta_copies<PG_BLOCK>(a, 0, copies);
+  __syncthreads();
+  const int j0 = wave * JW;
+  int32_t pv[JW];
+  uint32_t held;
+  bad |= delta_positions<false>(a, 0, j0, copies[lane], wave == 0, pv, held);
+  mem_done();
+  __syncthreads();
+  // the page counts and first keys are final
+  int32_t first_key[JW], count[JW];
+#pragma unroll
+  for (int i = 0; i < JW; i++) {
+    const bool h = (held >> i) & 1u;
+    first_key[i] = h ? (int32_t)ld_agent(&a.first[pv[i]]) : 0;
+    count[i] = h ? ld_agent(&a.ref[pv[i]]) : -1;
+  }
+  uint32_t freed = 0;
+#pragma unroll
+  for (int i = 0; i < JW; i++) {
+    if (((held >> i) & 1u) && (uint32_t)first_key[i] == entry_key(a, lane, j0 + i)) {
+      a.first[pv[i]] = 0;  // the scratch goes back to zero
+      if (count[i] == 0) freed |= 1u << i;
+    }
+  }
+  if (lane < PG_SMALL_ROWS) off[wave][lane] = __builtin_popcount(freed);
+  __syncthreads();
+  if (wave == 0) {
+    // lane = row: exclusive over the wavefronts, then over the rows
+    int32_t run = 0;
+    if (lane < PG_SMALL_ROWS) {
+      for (int w = 0; w < NW; w++) {
+        const int32_t t = off[w][lane];
+        off[w][lane] = run;
+        run += t;
+      }
+    }
+    int32_t pre = run;
+#pragma unroll
+    for (int d = 1; d < PG_SMALL_ROWS; d <<= 1) {
+      const int32_t y = __shfl_up(pre, d);
+      if (lane >= d) pre += y;
+    }
+    if (lane < PG_SMALL_ROWS)
+      for (int w = 0; w < NW; w++) off[w][lane] += pre - run;
+    if (lane == PG_SMALL_ROWS - 1) s_total = pre;
+  }
+  __syncthreads();
+  if (freed) {
+    int64_t pos = fc + off[wave][lane];
+#pragma unroll
+    for (int i = 0; i < JW; i++) {
+      if ((freed >> i) & 1u) {
+        if (pos < a.M) a.free_pages[pos] = pv[i];
+        pos++;
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    const int64_t total = s_total;
+    if (fc + total > a.M) bad |= FLAG_BAD_INPUT;  // the counts were not consistent
+    *a.free_count = (int32_t)(fc + total < a.M ? fc + total : a.M);
+  }
+  if (bad) raise_flags(a.flags, bad);
 }
 
 // ---------------------------------------------------------------------------
@@ -748,6 +876,10 @@ int32_t smc_pages_resample(int32_t P, int32_t N, int32_t L, int32_t page_size, i
   a.base = reinterpret_cast<int32_t*>(ws + l.base);
   a.arrived = reinterpret_cast<uint32_t*>(ws + l.base + 4);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (R <= PG_SMALL_ROWS && L <= PG_SMALL_L) {
+    hipLaunchKernelGGL(k_pages_resample_small, dim3(1), dim3(PG_BLOCK), 0, s, a);
+    return hipGetLastError() == hipSuccess ? SMCSD_OK : SMCSD_ERR_HIP;
+  }
   const unsigned rows = (unsigned)((R + WAVE - 1) / WAVE), cols = (unsigned)((L + PB - 1) / PB);
   hipLaunchKernelGGL(k_pages_delta, dim3(rows, cols), dim3(BLOCK), 0, s, a);
   if (hipGetLastError() != hipSuccess) return SMCSD_ERR_HIP;

@@ -90,6 +90,18 @@ def test_pages_odd_sizes():
     _lockstep(2, 7, 30, 1, 800, 1, steps=4, seed=14, max_len=5)     # one-token pages
 
 
+def test_pages_single_workgroup_bounds():
+    """Calls of at most 16 rows of at most 256 entries resample in one
+    workgroup; the sizes at and just past those bounds, and the 1 x 16-particle
+    SMC workload's shape (16-token pages, K+1 = 5 tokens a step, 256-entry rows)."""
+    _lockstep(1, 16, 256, 16, 16 * 300, 5, steps=4, seed=21, max_len=3000, concentrate=0.4)
+    _lockstep(16, 1, 256, 4, 16 * 300, 7, steps=3, seed=22, max_len=1000)    # every particle a prompt
+    _lockstep(2, 8, 256, 2, 16 * 300, 3, steps=4, seed=23, max_len=500, concentrate=0.3, shuffle=True)
+    _lockstep(4, 4, 256, 1, 16 * 300, 2, steps=6, seed=26, max_len=250, concentrate=0.2, identity_every=3)
+    _lockstep(1, 17, 64, 4, 17 * 80, 5, steps=3, seed=24, max_len=200, concentrate=0.4)    # one row too many
+    _lockstep(1, 16, 257, 2, 16 * 300, 3, steps=3, seed=25, max_len=500, concentrate=0.4)  # rows too long
+
+
 def test_pages_chunked_particles():
     """More particles than the append workgroup's threads (several particles
     per thread), and more than it holds in registers at once (chunks)."""
