@@ -316,6 +316,39 @@ def check_sd_statistics(lib, trials=200_000, configs=((5, 2), (3, 1), (8, 4))):
             assert stat.pvalue > 1e-4, (V, K, j, stat)
 
 
+def check_particle_l1_trend(lib, reps=300, Ns=(32, 128, 512, 2048)):
+    """The weighted particles' error shrinks like 1/sqrt(N) ("Faster LLM
+    Inference via Sequential Monte Carlo", sec. 3: the L1 bias falls as
+    O(1/sqrt(N)); the constants, set by the draft/target chi-square divergence,
+    are not given, so only the trend is checked).  One SMC step with K = 1 and
+    no resampling: particle i drafts x_i ~ q and carries log p(x_i) - log q(x_i);
+    the weighted histogram of the x_i against p, mean L1 distance over `reps`
+    independent prompts, must halve (within [1.6, 2.5]) each time N
+    quadruples.  A weight that is not log p - log q (a flipped sign, a dropped
+    term) leaves a bias that does not shrink."""
+    rng = np.random.default_rng(2604)
+    V, K, T = 6, 1, 1.0
+    zt = (1.5 * rng.standard_normal((K + 1, V))).astype(np.float32)
+    zd = (zt[:K] + 1.0 * rng.standard_normal((K, V))).astype(np.float32)
+    p = softmax(zt[0].astype(np.float64) / T)
+    q = softmax(zd[0].astype(np.float64) / T)
+    means = []
+    for N in Ns:
+        P = reps
+        x = rng.choice(V, size=P * N, p=q).astype(np.int32)
+        r = oracle.smc_step(np.tile(zt, (P * N, 1)), np.tile(zd, (P * N, 1)), x,
+                            rng.random(P * N).astype(np.float32), rng.random(P).astype(np.float32),
+                            np.zeros(P * N, np.float32), T, 0.0, P, N, K, lib=lib)
+        assert r["resampled"].sum() == 0 and r["flags"] == 0
+        lw = r["logw"].astype(np.float64).reshape(P, N)
+        w = np.exp(lw - lw.max(axis=1, keepdims=True))
+        l1 = [np.abs(np.bincount(x.reshape(P, N)[i], weights=w[i], minlength=V) / w[i].sum() - p).sum()
+              for i in range(P)]
+        means.append(float(np.mean(l1)))
+    ratios = [a / b for a, b in zip(means, means[1:])]
+    assert all(1.6 < t < 2.5 for t in ratios), (means, ratios)
+
+
 def check_expected_length(lib, trials=200_000):
     """Identical (p, q) at every position make the acceptance events iid with
     alpha = sum(min(p, q)); then E[n + 1] = (1 - alpha^(K+1)) / (1 - alpha)."""

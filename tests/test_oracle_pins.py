@@ -22,3 +22,8 @@ def test_expected_accepted_length(orc):
 def test_tree_output_law_chi_square(orc):
     """Tree verification's emitted tokens follow the target (chi-square, depth-2 tree)."""
     oc.check_tree_statistics(orc, trials=200_000)
+
+
+def test_particle_error_shrinks_like_inverse_sqrt_n(orc):
+    """Weighted particles converge to the target at the 1/sqrt(N) rate."""
+    oc.check_particle_l1_trend(orc)
