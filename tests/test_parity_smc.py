@@ -211,3 +211,15 @@ def test_smc_deterministic():
     b = run_smc_gpu(c, c["logw"], c["pt"], 0.9)
     for k in ("bonus", "ancestors", "ess", "resampled", "logw", "pt_out"):
         assert (a[k] == b[k]).all(), k
+
+
+def test_smc_many_small_prompts():
+    """Thousands of workgroups handing their prompts' log-weights to the last
+    particle to count: 1024 prompts of 2 particles, and 300 prompts of 7 with
+    resampling at almost every prompt, over two lockstep steps."""
+    from gpu_util import check_smc_steps
+
+    c = smc_case(4600, 1024, 2, 2, 3000, dtype="bf16", L=3, logw_scale=2.0)
+    check_smc_steps(c, steps=2, ess_frac=0.9, label="1024x2")
+    c = smc_case(4601, 300, 7, 3, 1500, T=0.8, dtype="f32", L=5, logw_scale=3.0)
+    check_smc_steps(c, steps=2, ess_frac=1.0, label="300x7")
