@@ -49,10 +49,14 @@
  *   - page tables: row k of the output is row a_k of the input;
  *   - power target ([SMC] sec. 3, Flexibilitaet: the framework also targets
  *     modified distributions such as power sampling, without retraining): the
- *     target is proportional to p^beta, so a draft token adds
- *     beta * log p - log q to the log-weight, and the (K+1)-th token comes
- *     from softmax(beta * z / T), i.e. temperature T / beta; beta = 1 is the
- *     plain step above.
+ *     target of a particle's tokens is proportional to the product of
+ *     p_j(x_j)^beta over them.  A draft token (proposal q) adds
+ *     beta * log p - log q to the log-weight.  The (K+1)-th token comes from
+ *     the normalised softmax(beta * z / T) = p_K^beta / Z_beta, i.e.
+ *     temperature T / beta, so its importance weight is
+ *     p_K(y)^beta / (p_K(y)^beta / Z_beta) = Z_beta = sum_y p_K(y)^beta, the
+ *     same for every y: it adds log Z_beta.  beta = 1 is the plain step above
+ *     (Z_1 = 1).
  */
 #include <math.h>
 #include <stdint.h>
@@ -271,9 +275,10 @@ int oracle_sd_final_cdf(int dtype, int b, int K, int64_t V, double T, const void
  * Particle i = p*N + n owns target rows i*(K+1) .. i*(K+1)+K and draft rows
  * i*K .. i*K+K-1.
  *
- *   log-weight:   logw'_i = fp32(logw_i + sum_{j<K} (beta log p_ij(x_ij) - log q_ij(x_ij)))
+ *   log-weight:   logw'_i = fp32(logw_i + sum_{j<K} (beta log p_ij(x_ij) - log q_ij(x_ij))
+ *                                   + log sum_y p_{i,K}(y)^beta)
  *   bonus token:  inverse CDF of softmax(beta z_{i,K} / T) with bonus_u[i]
- *                 (beta = 1 for the plain step: p_{i,K})
+ *                 (beta = 1 for the plain step: p_{i,K}, and the last term is 0)
  *   ESS:          Kish, (sum w)^2 / sum w^2, w_i = exp(logw'_i - max)
  *   resample iff ESS < ess_frac * N: systematic with resample_u[p];
  *                 ancestors (local indices), logw_out = 0, page-table rows
@@ -312,10 +317,23 @@ int oracle_smc_step_power(int dtype, int P, int N, int K, int64_t V, double T, d
         if (oracle_row_stats(dtype, drow, V, T, &Md, &lSd)) fl |= ORACLE_FLAG_NONFINITE;
         delta += beta * logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);
       }
+      /* the (K+1)-th token's weight Z_beta = sum_y p_K(y)^beta.  With
+       * p_K(y) = exp(a_y - M - log S), a_y = z_y / T:
+       *   Z_beta = exp(-beta log S) * sum_y exp(beta (a_y - M)),
+       * so log Z_beta = log S_beta - beta log S, S_beta the second sum.  At
+       * beta = 1, Z_1 = 1 (p_K sums to one) and nothing is added. */
+      const void* brow = row_ptr(dtype, target, i * (K + 1) + K, V);
+      if (beta != 1.0) {
+        double Mk, lSk;
+        if (oracle_row_stats(dtype, brow, V, T, &Mk, &lSk)) fl |= ORACLE_FLAG_NONFINITE;
+        double Sb = 0.0;
+        for (int64_t y = 0; y < V; y++) Sb += exp(beta * (oracle_logit(dtype, brow, y) / T - Mk));
+        delta += log(Sb) - beta * lSk;
+      }
       lw[n] = (float)((double)logw[i] + delta);
       if (isnan(lw[n]) || lw[n] == INFINITY) fl |= ORACLE_FLAG_NONFINITE;
       /* the (K+1)-th token, drawn from the target's row K (power: at T / beta) */
-      final_weights(dtype, row_ptr(dtype, target, i * (K + 1) + K, V), NULL, V, T / beta, w, &fl);
+      final_weights(dtype, brow, NULL, V, T / beta, w, &fl);
       double m = 0.0;
       bonus[i] = (int32_t)inverse_cdf(w, V, (double)bonus_u[i], &m, &fl);
       if (bonus_margin) bonus_margin[i] = m;

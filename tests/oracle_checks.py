@@ -205,6 +205,56 @@ def check_sd_exact_law(lib):
         assert np.abs(law1 / acc - p1).max() < 1e-9, (law1 / acc, p1)
 
 
+def check_zero_residual_fallback(lib):
+    """Reading: a rejection whose residual max(0, p_n - q_n) has no mass
+    (p_n equal to q_n) draws the final token from p_n with the same final
+    uniform, and raises ZERO_RESIDUAL.  Identical target and draft rows make
+    rho = 1 exactly, and an accept uniform of 1.0 (outside the documented
+    [0, 1), but defined) then rejects.  The residual is exactly 0, and the
+    final token must be numpy's searchsorted on cumsum(p_n)."""
+    rng = np.random.default_rng(57)
+    V, K, T = 9, 2, 0.8
+    zt = (2 * rng.standard_normal((K + 1, V))).astype(np.float32)
+    zd = zt[:K].copy()
+    tok = rng.integers(0, V, K).astype(np.int32)
+    for n in range(K):
+        p = softmax(zt[n].astype(np.float64) / T)
+        c = np.cumsum(p)
+        for uf in (0.05, 0.3, 0.61, 0.93):
+            u = np.full(K + 1, 0.5, np.float32)
+            u[n], u[K] = 1.0, uf
+            r = oracle.sd_verify(zt, zd, tok, u, T, K=K, lib=lib)
+            assert r["num_accepted"].tolist() == [n], (n, r)
+            assert r["flags"] & oracle.FLAG_ZERO_RESIDUAL, r
+            want = int(np.searchsorted(c, np.float64(np.float32(uf)) * c[-1], side="right"))
+            if np.min(np.abs(c / c[-1] - np.float32(uf))) > 1e-9:
+                assert r["final_token"].tolist() == [want], (n, uf, r["final_token"], want)
+
+
+def check_cdf_clamp_last_positive(lib):
+    """Reading: when no inclusive prefix exceeds u * Z (u = 1.0 here, where the
+    last prefix equals Z), the draw takes the last index with positive weight
+    and raises CDF_CLAMP.  Rows whose trailing (and some inner) logits are
+    -inf: the answer is the last finite logit, neither index 0 nor V - 1.
+    Checked on the bonus draw (draft = target, all accepted) and on the
+    residual draw (a rejection)."""
+    ninf = -np.inf
+    for row, last in (([1.0, 2.0, ninf, 0.5, ninf, ninf], 3), ([ninf, 0.25, 3.0, ninf], 2),
+                      ([0.0, 0.0, 0.0, 0.0, 0.0, ninf, ninf, ninf], 4)):
+        z = np.asarray([row], np.float32)
+        r = oracle.sd_verify(z, np.zeros((0, z.shape[1]), np.float32), np.zeros(0, np.int32), [1.0], 1.0, K=0,
+                             lib=lib)
+        assert r["final_token"].tolist() == [last], (row, r)
+        assert r["flags"] & oracle.FLAG_CDF_CLAMP, r
+    # residual: p puts mass on tokens 0..3, q on token 0 only; max(0, p - q)
+    # is positive on 1..3 (trailing tokens -inf in both rows); token 0 rejects
+    zt = np.asarray([[0.0, 0.0, 0.0, 0.0, ninf, ninf], [0.0] * 6], np.float32)
+    zd = np.asarray([[0.0, ninf, ninf, ninf, ninf, ninf]], np.float32)
+    r = oracle.sd_verify(zt, zd, np.zeros(1, np.int32), [0.5, 1.0], 1.0, K=1, lib=lib)
+    assert r["num_accepted"].tolist() == [0] and r["final_token"].tolist() == [3], r
+    assert r["flags"] & oracle.FLAG_CDF_CLAMP, r
+
+
 def check_bonus_vs_numpy(lib):
     """draft == target (delta = 0): every token accepted, final token is a plain
     categorical inverse-CDF draw from p_K, i.e. numpy searchsorted."""
@@ -442,6 +492,32 @@ def check_systematic_invariants(lib):
             assert r["ancestors"].tolist() == list(range(N)), (N, u, r["ancestors"])
 
 
+def check_systematic_clamp_last_positive(lib):
+    """Reading: a systematic point U_k that no normalised prefix C_i exceeds
+    (resample uniform 1.0 puts U_{N-1} = 1.0, and the last prefix equals 1)
+    goes to the last particle with positive weight, and CDF_CLAMP is raised.
+    Particles with weight 0 (log-weight -inf) at the end: the last slot's
+    ancestor is the last live particle, not particle 0 or N - 1; the other
+    slots follow the exact rational rule."""
+    ninf = -np.inf
+    for lw, last in (([0.3, -1.0, 0.5, ninf, ninf], 2), ([ninf, 0.0, ninf, 1.5, -0.5, ninf], 4),
+                     ([0.0, 0.0, 0.0, ninf], 2)):
+        N = len(lw)
+        r = _smc_from_logw(lib, lw, 1.0, ess_frac=1.01)
+        a = r["ancestors"].tolist()
+        assert r["resampled"][0] == 1 and a[-1] == last, (lw, a)
+        assert r["flags"] & oracle.FLAG_CDF_CLAMP, r
+        M = max(x for x in lw if x > ninf)
+        w = [Fraction(math.exp(float(np.float32(x)) - M)) if x > ninf else Fraction(0) for x in lw]
+        C, acc = [], Fraction(0)
+        for x in w:
+            acc += x
+            C.append(acc / sum(w))
+        for k in range(N - 1):
+            U = Fraction(1 + k, N)
+            assert a[k] == next(i for i in range(N) if C[i] > U), (lw, k, a)
+
+
 def check_systematic_fraction_bruteforce(lib):
     """Exact rational systematic resampling on the oracle's own float weights."""
     rng = np.random.default_rng(31)
@@ -543,22 +619,115 @@ def check_power_bonus_law(lib):
         assert np.abs(law - law_ref).max() < 1e-9, (beta, law, law_ref)
 
 
-def check_power_increment(lib):
-    """Power target with draft == target: each draft token adds
-    beta log p - log p = (beta - 1) log p (scipy log_softmax)."""
-    rng = np.random.default_rng(51)
-    P, N, K, V, T = 1, 4, 3, 64, 1.2
-    zt = (3 * rng.standard_normal((P * N * (K + 1), V))).astype(np.float32)
-    zd = zt.reshape(P * N, K + 1, V)[:, :K].reshape(P * N * K, V).copy()
-    tok = rng.integers(0, V, P * N * K).astype(np.int32)
-    lw0 = (0.1 * rng.standard_normal(P * N)).astype(np.float32)
-    lp = log_softmax(zt.astype(np.float64) / T, axis=-1).reshape(P * N, K + 1, V)
-    for beta in (3.0, 0.5):
-        r = oracle.smc_step(zt, zd, tok, rng.random(P * N), [0.5], lw0, T, 0.0, P, N, K, lib=lib, beta=beta)
-        for i in range(P * N):
-            d = (beta - 1.0) * sum(lp[i, j, tok[i * K + j]] for j in range(K))
-            want = float(lw0[i]) + d
-            assert abs(float(r["logw"][i]) - want) <= 1e-6 * max(1.0, abs(want)), (beta, i)
+def _power_paths(rng, V, K, T, spread=2.5):
+    """Rows of a K-token draft whose later rows depend on the tokens drafted
+    before them: target row j and draft row j of path (x_0 .. x_{j-1}), and
+    the bonus row K of each full path (indexed by the path's base-V number)."""
+    tgt = [(spread * rng.standard_normal((V ** j, V))).astype(np.float32) for j in range(K + 1)]
+    drf = [(tgt[j] + 1.0 * rng.standard_normal((V ** j, V))).astype(np.float32) for j in range(K)]
+    return tgt, drf
+
+
+def _path_index(path, V):
+    h = 0
+    for x in path:
+        h = h * V + int(x)
+    return h
+
+
+def check_power_weighted_law(lib):
+    """Power target p^beta: the weights make the proposal exact.
+
+    The target of one step's K+1 tokens is gamma(x) = prod_j p_j(x_j)^beta
+    (unnormalised), p_j the target's conditional at row j, which depends on
+    the tokens before it.  For importance weights of a proposal r, r(x) w(x) =
+    gamma(x) up to one constant per step; with log-weights starting at 0 that
+    constant is 1.  The oracle's decisions are integrated exactly: every draft
+    path x_0..x_{K-1} (probability prod_j q_j(x_j), scipy), and for the
+    (K+1)-th token every interval of its uniform (midpoints; the token is the
+    one the oracle draws, the interval length its probability).  Summed per
+    cell (path, drawn token), r * exp(logw) must equal gamma (scipy softmax)
+    to the fp32 rounding of the log-weight.  A dropped or misscaled weight of
+    the (K+1)-th token, beta on the wrong side, or a bonus drawn at the wrong
+    temperature all break it."""
+    rng = np.random.default_rng(55)
+    for V, K, T, beta in ((4, 1, 0.9, 2.0), (4, 1, 1.1, 0.5), (3, 2, 1.0, 3.0), (3, 0, 0.8, 2.5)):
+        tgt, drf = _power_paths(rng, V, K, T, spread=1.2)
+        sm = lambda z, b=1.0: softmax(b * z.astype(np.float64) / T)  # noqa: E731
+        cells_zt, cells_zd, cells_tok, cells_u, cells_r, cells_key = [], [], [], [], [], []
+        for path in np.ndindex(*([V] * K)):
+            r_path = 1.0
+            rows_t, rows_d = [], []
+            for j in range(K):
+                h = _path_index(path[:j], V)
+                rows_t.append(tgt[j][h])
+                rows_d.append(drf[j][h])
+                r_path *= sm(drf[j][h])[path[j]]
+            hb = _path_index(path, V)
+            rows_t.append(tgt[K][hb])
+            mid, ln = _midpoints(np.cumsum(sm(tgt[K][hb], beta)))
+            assert len(mid) == V and ln.min() > 1e-5  # every interval holds fp32 uniforms
+            for m, w in zip(mid, ln):
+                cells_zt.append(np.stack(rows_t))
+                cells_zd.append(np.stack(rows_d) if K else np.zeros((0, V), np.float32))
+                cells_tok.append(np.asarray(path, np.int32))
+                cells_u.append(m)
+                cells_r.append(r_path * w)
+                cells_key.append(path)
+        N = len(cells_u)
+        r = oracle.smc_step(np.concatenate(cells_zt), np.concatenate(cells_zd), np.concatenate(cells_tok),
+                            np.asarray(cells_u, np.float32), [0.5], np.zeros(N, np.float32), T, 0.0, 1, N, K,
+                            lib=lib, beta=beta)
+        assert r["resampled"][0] == 0 and r["flags"] == 0, r["flags"]
+        got = {}
+        for key, y, rr, lw in zip(cells_key, r["bonus"], cells_r, r["logw"]):
+            got[key + (int(y),)] = got.get(key + (int(y),), 0.0) + rr * math.exp(float(lw))
+        for path in np.ndindex(*([V] * (K + 1))):
+            g = 1.0
+            for j in range(K + 1):
+                g *= sm(tgt[j][_path_index(path[:j], V)])[path[j]] ** beta
+            have = got.get(tuple(int(x) for x in path), 0.0)
+            assert abs(have - g) <= 1e-6 * g, (V, K, beta, path, have, g)
+
+
+def check_power_particle_trend(lib, reps=300, Ns=(32, 128, 512, 2048)):
+    """Power target: weighted particles approach the normalised target at the
+    1/sqrt(N) rate ("Faster LLM Inference via Sequential Monte Carlo", sec. 3:
+    the L1 bias falls as O(1/sqrt(N))).  K = 1, V = 4, beta = 2: particle i
+    drafts x_0 ~ q_0 (numpy), its bonus row depends on x_0, and the oracle
+    draws x_1 and weighs the particle.  The mean L1 distance of the weighted
+    (x_0, x_1) histogram to gamma / sum(gamma), gamma = p_0^beta p_1(.|x_0)^beta,
+    over `reps` prompts must halve (ratio in [1.6, 2.5]) each time N
+    quadruples.  A weight that leaves out the bonus token's Z_beta has a bias
+    that does not shrink, and ratios near 1."""
+    rng = np.random.default_rng(2605)
+    V, K, T, beta = 4, 1, 1.0, 2.0
+    tgt, drf = _power_paths(rng, V, K, T, spread=1.0)
+    # bonus rows from nearly flat to sharply peaked, so Z_beta(x_0) spans a factor of about 3
+    tgt[1] = (tgt[1] * np.array([[0.1], [0.8], [2.5], [4.0]])).astype(np.float32)
+    sm = lambda z, b=1.0: softmax(b * z.astype(np.float64) / T)  # noqa: E731
+    q0, p0 = sm(drf[0][0]), sm(tgt[0][0])
+    gamma = np.array([[p0[a] ** beta * sm(tgt[1][a])[b] ** beta for b in range(V)] for a in range(V)])
+    gamma /= gamma.sum()
+    means = []
+    for N in Ns:
+        P = reps
+        x0 = rng.choice(V, size=P * N, p=q0).astype(np.int32)
+        zt = np.empty((P * N * 2, V), np.float32)
+        zt[0::2] = tgt[0][0]
+        zt[1::2] = tgt[1][x0]
+        r = oracle.smc_step(zt, np.tile(drf[0][0], (P * N, 1)), x0, rng.random(P * N).astype(np.float32),
+                            rng.random(P).astype(np.float32), np.zeros(P * N, np.float32), T, 0.0, P, N, K,
+                            lib=lib, beta=beta)
+        assert r["resampled"].sum() == 0 and r["flags"] == 0
+        lw = r["logw"].astype(np.float64).reshape(P, N)
+        w = np.exp(lw - lw.max(axis=1, keepdims=True))
+        cell = (x0 * V + r["bonus"]).reshape(P, N)
+        l1 = [np.abs(np.bincount(cell[i], weights=w[i], minlength=V * V) / w[i].sum() - gamma.ravel()).sum()
+              for i in range(P)]
+        means.append(float(np.mean(l1)))
+    ratios = [a / b for a, b in zip(means, means[1:])]
+    assert all(1.6 < t < 2.5 for t in ratios), (means, ratios)
 
 
 def check_power_one_is_plain(lib):
@@ -1071,6 +1240,8 @@ DETERMINISTIC_CHECKS = [
     check_accept_tie_rejects,
     check_cdf_tie,
     check_sd_exact_law,
+    check_zero_residual_fallback,
+    check_cdf_clamp_last_positive,
     check_bonus_vs_numpy,
     check_residual_vs_numpy,
     check_accept_decisions_vs_scipy,
@@ -1078,13 +1249,14 @@ DETERMINISTIC_CHECKS = [
     check_ess_closed_forms,
     check_threshold_strict,
     check_systematic_invariants,
+    check_systematic_clamp_last_positive,
     check_systematic_fraction_bruteforce,
     check_smc_reweight_vs_scipy,
     check_smc_delta_zero,
     check_smc_bonus_law,
     check_smc_page_table_identity,
     check_power_bonus_law,
-    check_power_increment,
+    check_power_weighted_law,
     check_power_one_is_plain,
     check_pages_content_model,
     check_pages_errors,

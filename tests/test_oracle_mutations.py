@@ -43,6 +43,21 @@ MUTATIONS = [
      "delta += logprob_with(dtype, trow, x, T, Mt, lSt) - logprob_with(dtype, drow, x, T, Md, lSd);"),
     ("power_bonus_temperature", "V, T / beta, w, &fl);", "V, T * beta, w, &fl);"),
     ("power_bonus_plain", "V, T / beta, w, &fl);", "V, T, w, &fl);"),
+    ("power_bonus_weight_dropped", "        delta += log(Sb) - beta * lSk;\n", ""),
+    ("power_bonus_weight_unscaled", "delta += log(Sb) - beta * lSk;", "delta += log(Sb) - lSk;"),
+    ("power_bonus_weight_sign", "delta += log(Sb) - beta * lSk;", "delta -= log(Sb) - beta * lSk;"),
+    ("power_bonus_weight_plain_scale", "Sb += exp(beta * (oracle_logit(dtype, brow, y) / T - Mk));",
+     "Sb += exp(oracle_logit(dtype, brow, y) / T - Mk);"),
+    ("zero_residual_fallback_uniform",
+     "    *flags |= ORACLE_FLAG_ZERO_RESIDUAL;\n    for (int64_t i = 0; i < V; i++) w[i] = exp(logprob_with(dtype, trow, i, T, Mt, lSt));",
+     "    *flags |= ORACLE_FLAG_ZERO_RESIDUAL;\n    for (int64_t i = 0; i < V; i++) w[i] = 1.0;"),
+    ("cdf_clamp_to_first", "  for (int64_t i = n - 1; i >= 0; i--)\n    if (w[i] > 0.0) return i;\n  return n - 1;",
+     "  return 0;"),
+    ("cdf_clamp_to_end", "  for (int64_t i = n - 1; i >= 0; i--)\n    if (w[i] > 0.0) return i;\n  return n - 1;",
+     "  return n - 1;"),
+    ("systematic_clamp_to_first", "          for (a = N - 1; a > 0 && pw[a] == 0.0; a--) {\n          }", "          a = 0;"),
+    ("systematic_clamp_to_end", "          for (a = N - 1; a > 0 && pw[a] == 0.0; a--) {\n          }",
+     "          a = N - 1;"),
     ("old_weight_dropped", "lw[n] = (float)((double)logw[i] + delta);", "lw[n] = (float)delta;"),
     ("bonus_from_first_row", "row_ptr(dtype, target, i * (K + 1) + K, V)", "row_ptr(dtype, target, i * (K + 1), V)"),
     ("weights_not_exponentiated", "pw[n] = exp((double)lw[n] - M);", "pw[n] = (double)lw[n] - M;"),

@@ -27,3 +27,8 @@ def test_tree_output_law_chi_square(orc):
 def test_particle_error_shrinks_like_inverse_sqrt_n(orc):
     """Weighted particles converge to the target at the 1/sqrt(N) rate."""
     oc.check_particle_l1_trend(orc)
+
+
+def test_power_particles_converge_to_power_target(orc):
+    """Power target: weighted (x_0, x_1) particles converge to p^beta at the 1/sqrt(N) rate."""
+    oc.check_power_particle_trend(orc)
