@@ -150,6 +150,26 @@ const char* smcsd_status_string(int32_t status);
 void smcsd_time_next_call(void* stream_start, void* stream_stop, void* tail_start, void* tail_stop);
 
 /*
+ * Measurement aid: the plain-read ceiling of the streaming kernel's access
+ * pattern.  Reads every byte of a[0 .. a_bytes) and b[0 .. b_bytes) once with
+ * the loads the logit-streaming kernel uses (16-byte non-temporal loads, 4 KiB
+ * per wavefront per step, three steps in flight, the grid the device holds at
+ * once) and no arithmetic, so its duration at a call's logit bytes is the
+ * time those bytes take to stream with nothing else to do.
+ *   a, b          device buffers, 16-byte aligned (b may be NULL with
+ *                 b_bytes = 0); byte counts even.
+ *   sink          device uint32 [64]: written only when the folded words hit
+ *                 one fixed value (keeps the loads); contents unspecified.
+ *   start_event, stop_event  hipEvent_t (timing enabled) attached to the
+ *                 kernel's own start and stop, or NULL.
+ * Returns SMCSD_ERR_INVALID_ARG on a NULL buffer with a nonzero size, an odd
+ * size or a misaligned buffer, SMCSD_ERR_HIP when the launch fails.  One
+ * kernel on `stream`; nothing allocated.
+ */
+int32_t smcsd_read_ceiling(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink,
+                           void* start_event, void* stop_event, void* stream);
+
+/*
  * Workspace bytes sd_verify needs for these sizes (0 when B == 0).
  * total_draft_rows is B*K for fixed K, or offsets[B] for CSR input.
  */
@@ -244,19 +264,25 @@ int32_t smc_reweight_resample(int32_t dtype, int32_t P, int32_t N, int32_t K, in
                               size_t workspace_bytes, void* stream);
 
 /*
- * The same step for a power-sampling target proportional to p^beta (the
- * flexibility of "Faster LLM Inference via Sequential Monte Carlo", sec. 3:
- * modified targets such as power sampling, without retraining).  Arguments
- * as in smc_reweight_resample, plus:
+ * The same step for a power-sampling target (the flexibility of "Faster LLM
+ * Inference via Sequential Monte Carlo", sec. 3: modified targets such as
+ * power sampling, without retraining): the target of a particle's tokens is
+ * proportional to the product of p_j(x_j)^beta over them, p at the given
+ * temperature.  Arguments as in smc_reweight_resample, plus:
  *
  *   beta                    > 0, finite, with beta / temperature finite.
  *   log_weights             Out: logw + sum_{j<K} (beta * log p_ij(x_ij)
- *                           - log q_ij(x_ij)) (or 0 after resampling), p and q
- *                           at the given temperature.
+ *                           - log q_ij(x_ij)) + log Z_i (or 0 after
+ *                           resampling), p and q at the given temperature, and
+ *                           Z_i = sum_y p_{i,K}(y)^beta: the (K+1)-th token is
+ *                           drawn from the normalised p_{i,K}^beta / Z_i, so
+ *                           its importance weight is Z_i whatever token it is.
  *   bonus_token             drawn from softmax(beta * z_{i,K} / temperature).
  *
- * beta = 1 gives exactly smc_reweight_resample's results.  Same workspace size
- * (smc_workspace_bytes) and error codes; an invalid beta is
+ * beta = 1 gives exactly smc_reweight_resample's results (Z = 1, nothing
+ * added).  For beta != 1 the streaming kernel also reduces every bonus row at
+ * the plain scale (one more exponential per logit of those rows).  Same
+ * workspace size (smc_workspace_bytes) and error codes; an invalid beta is
  * SMCSD_ERR_INVALID_ARG.
  */
 int32_t smc_reweight_resample_power(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,

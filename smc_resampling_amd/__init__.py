@@ -8,6 +8,7 @@ There is no CPU fallback: importing fails loudly when the library is missing.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -20,7 +21,7 @@ __all__ = [
     "FLAG_PAGES_FULL", "FLAG_PAGES_EXHAUSTED",
     "new_workspace", "time_next_call", "smc_pages_workspace_bytes", "smc_pages_append", "smc_pages_resample",
     "draft_sample_workspace_bytes", "prepare_draft_sample", "draft_sample", "pacer_lengths",
-    "tree_verify_workspace_bytes", "prepare_tree_verify", "tree_verify", "TREE_MAX_NODES",
+    "tree_verify_workspace_bytes", "prepare_tree_verify", "tree_verify", "TREE_MAX_NODES", "read_ceiling",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +40,7 @@ _SIGNATURES = {
     "smcsd_abi_version": ([], _I32),
     "smcsd_status_string": ([_I32], ctypes.c_char_p),
     "smcsd_time_next_call": ([_P, _P, _P, _P], None),
+    "smcsd_read_ceiling": ([_P, _SZ, _P, _SZ, _P, _P, _P, _P], _I32),
     "sd_verify_workspace_bytes": ([_I32, _I32, _I32, _I32, _I64], _SZ),
     "sd_verify": ([_I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
@@ -95,6 +97,22 @@ def time_next_call(stream_start=None, stream_stop=None, tail_start=None, tail_st
     _lib.smcsd_time_next_call(*h)
 
 
+def read_ceiling(a, b=None, *, sink=None, start=None, stop=None, stream=None):
+    """Launch the plain-read ceiling kernel over the bytes of tensors ``a``
+    and ``b`` (``smcsd_read_ceiling``): the streaming kernel's loads with no
+    arithmetic.  ``start`` / ``stop``: torch.cuda.Event objects whose handles
+    exist (recorded once), attached to the kernel itself (measurement aid)."""
+    dev = a.device
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        sink = sink if sink is not None else torch.empty(64, dtype=torch.int32, device=dev)
+    nb = lambda t: 0 if t is None else t.numel() * t.element_size()  # noqa: E731
+    _check(_lib.smcsd_read_ceiling(_ptr(a), nb(a), _ptr(b), nb(b), _ptr(sink),
+                                   None if start is None else start.cuda_event,
+                                   None if stop is None else stop.cuda_event, st))
+    return sink
+
+
 def status_string(code: int) -> str:
     return _lib.smcsd_status_string(code).decode()
 
@@ -125,6 +143,18 @@ def _need(t, dtype, name):
 
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _on_stream(stream, device):
+    """(context, handle) for one call on ``stream`` (a HIP stream handle, or
+    None for the current stream).  The binding makes its own tensors (outputs,
+    zeroed status flags, a temporary workspace) inside the context, so their
+    allocation and zero-fill are ordered on the stream the kernels run on, and
+    the caching allocator hands a temporary freed after the call only to later
+    work on that same stream."""
+    if stream is None:
+        return contextlib.nullcontext(), _stream(device)
+    return torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)), stream
 
 
 def _workspace(nbytes, device, workspace):
@@ -162,7 +192,8 @@ def prepare_sd_verify(target_logits, draft_logits, draft_tokens, uniforms, tempe
     ``call()`` enqueues the step on the stream (current stream by default) and
     raises on a non-OK status; ``outputs`` holds num_accepted, final_token and
     status_flags.  Fixed K: target [B*(K+1), V], draft [B*K, V].  Ragged:
-    ``draft_offsets`` int32 [B+1] and ``K`` = largest draft length.
+    ``draft_offsets`` int32 [B+1] and ``K`` = largest draft length (required:
+    the binding reads nothing back from the device).
     """
     dev = target_logits.device
     dt = _dtype_code(target_logits)
@@ -173,17 +204,18 @@ def prepare_sd_verify(target_logits, draft_logits, draft_tokens, uniforms, tempe
     if draft_offsets is None:
         K = rows_d // B if B > 0 else (K or 0)
     elif K is None:
-        K = int(torch.diff(draft_offsets).max().item()) if B > 0 else 0
+        raise ValueError("draft_offsets needs K, the largest draft length")
     for t, d, n in ((target_logits, target_logits.dtype, "target_logits"), (draft_logits, target_logits.dtype,
                     "draft_logits"), (draft_tokens, torch.int32, "draft_tokens"), (uniforms, torch.float32,
                     "uniforms"), (draft_offsets, torch.int32, "draft_offsets")):
         _need(t, d, n)
-    num_accepted = num_accepted if num_accepted is not None else torch.empty(B, dtype=torch.int32, device=dev)
-    final_token = final_token if final_token is not None else torch.empty(B, dtype=torch.int32, device=dev)
-    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    nbytes = sd_verify_workspace_bytes(dt, B, K, V, rows_d)
-    ws, wsb = _workspace(nbytes, dev, workspace)
-    st = stream if stream is not None else _stream(dev)
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        num_accepted = num_accepted if num_accepted is not None else torch.empty(B, dtype=torch.int32, device=dev)
+        final_token = final_token if final_token is not None else torch.empty(B, dtype=torch.int32, device=dev)
+        status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        nbytes = sd_verify_workspace_bytes(dt, B, K, V, rows_d)
+        ws, wsb = _workspace(nbytes, dev, workspace)
     args = (dt, B, K, V, float(temperature), _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens),
             _ptr(uniforms), _ptr(draft_offsets), rows_d, _ptr(num_accepted), _ptr(final_token), _ptr(status_flags),
             _ptr(ws), wsb, st)
@@ -222,19 +254,20 @@ def prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bon
                     (page_table_out, torch.int32, "page_table_out")):
         _need(t, d, n)
     L = 0
-    if page_table_in is not None:
-        L = page_table_in.numel() // max(PN, 1)
-        if page_table_out is None:
-            page_table_out = torch.empty_like(page_table_in)
-    mk = lambda n, d: torch.empty(n, dtype=d, device=dev)  # noqa: E731
-    bonus_token = bonus_token if bonus_token is not None else mk(PN, torch.int32)
-    ancestors = ancestors if ancestors is not None else mk(PN, torch.int32)
-    ess = ess if ess is not None else mk(P, torch.float32)
-    resampled = resampled if resampled is not None else mk(P, torch.int32)
-    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    nbytes = smc_workspace_bytes(dt, P, N, K, V)
-    ws, wsb = _workspace(nbytes, dev, workspace)
-    st = stream if stream is not None else _stream(dev)
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        if page_table_in is not None:
+            L = page_table_in.numel() // max(PN, 1)
+            if page_table_out is None:
+                page_table_out = torch.empty_like(page_table_in)
+        mk = lambda n, d: torch.empty(n, dtype=d, device=dev)  # noqa: E731
+        bonus_token = bonus_token if bonus_token is not None else mk(PN, torch.int32)
+        ancestors = ancestors if ancestors is not None else mk(PN, torch.int32)
+        ess = ess if ess is not None else mk(P, torch.float32)
+        resampled = resampled if resampled is not None else mk(P, torch.int32)
+        status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        nbytes = smc_workspace_bytes(dt, P, N, K, V)
+        ws, wsb = _workspace(nbytes, dev, workspace)
     scal = (float(temperature), float(ess_frac)) if beta is None else (float(temperature), float(beta), float(ess_frac))
     args = (dt, P, N, K, V, *scal, _ptr(target_logits), _ptr(draft_logits),
             _ptr(draft_tokens), _ptr(bonus_uniforms), _ptr(resample_uniforms), _ptr(log_weights), _ptr(page_table_in),
@@ -278,17 +311,18 @@ def smc_pages_append(page_table, seq_len, ref_count, free_pages, free_count, P, 
     dev = page_table.device
     R, L = P * N, page_table.shape[-1]
     M = ref_count.numel()
-    slots = slots if slots is not None else torch.empty((R, new_tokens), dtype=torch.int32, device=dev)
-    cow = cow_list if cow_list is not None else torch.empty((max(R, 1), 3), dtype=torch.int32, device=dev)
-    cow_count = cow_count if cow_count is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    for t, n in ((slots, "slots"), (cow, "cow_list"), (cow_count, "cow_count")):
-        _need(t, torch.int32, n)
-    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        slots = slots if slots is not None else torch.empty((R, new_tokens), dtype=torch.int32, device=dev)
+        cow = cow_list if cow_list is not None else torch.empty((max(R, 1), 3), dtype=torch.int32, device=dev)
+        cow_count = cow_count if cow_count is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        for t, n in ((slots, "slots"), (cow, "cow_list"), (cow_count, "cow_count")):
+            _need(t, torch.int32, n)
+        status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
     _check(_lib.smc_pages_append(P, N, L, page_size, new_tokens, M, _ptr(page_table), _ptr(seq_len),
                                  _ptr(ref_count), _ptr(free_pages), _ptr(free_count), _ptr(slots), _ptr(cow),
-                                 _ptr(cow_count), _ptr(status_flags), _ptr(ws), wsb,
-                                 stream if stream is not None else _stream(dev)))
+                                 _ptr(cow_count), _ptr(status_flags), _ptr(ws), wsb, st))
     return dict(slots=slots, cow_list=cow, cow_count=cow_count, status_flags=status_flags)
 
 
@@ -304,13 +338,14 @@ def smc_pages_resample(ancestors, page_table_old, seq_len_in, ref_count, free_pa
     dev = page_table_old.device
     L = page_table_old.shape[-1]
     M = ref_count.numel()
-    seq_len_out = seq_len_out if seq_len_out is not None else torch.empty_like(seq_len_in)
-    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        seq_len_out = seq_len_out if seq_len_out is not None else torch.empty_like(seq_len_in)
+        status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        ws, wsb = _workspace(smc_pages_workspace_bytes(P, N, L, M), dev, workspace)
     _check(_lib.smc_pages_resample(P, N, L, page_size, M, _ptr(ancestors), _ptr(page_table_old), _ptr(seq_len_in),
                                    _ptr(seq_len_out), _ptr(ref_count), _ptr(free_pages), _ptr(free_count),
-                                   _ptr(status_flags), _ptr(ws), wsb,
-                                   stream if stream is not None else _stream(dev)))
+                                   _ptr(status_flags), _ptr(ws), wsb, st))
     return dict(seq_len_out=seq_len_out, status_flags=status_flags)
 
 
@@ -330,11 +365,12 @@ def prepare_draft_sample(logits, uniforms, temperature, *, tokens=None, status_f
     _need(uniforms, torch.float32, "uniforms")
     if uniforms.numel() != R:
         raise ValueError(f"uniforms: {uniforms.numel()} values for {R} rows")
-    tokens = tokens if tokens is not None else torch.empty(R, dtype=torch.int32, device=dev)
-    _need(tokens, torch.int32, "tokens")
-    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    ws, wsb = _workspace(draft_sample_workspace_bytes(dt, R, V), dev, workspace)
-    st = stream if stream is not None else _stream(dev)
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        tokens = tokens if tokens is not None else torch.empty(R, dtype=torch.int32, device=dev)
+        _need(tokens, torch.int32, "tokens")
+        status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        ws, wsb = _workspace(draft_sample_workspace_bytes(dt, R, V), dev, workspace)
     args = (dt, R, V, float(temperature), _ptr(logits), _ptr(uniforms), _ptr(tokens), _ptr(status_flags), _ptr(ws),
             wsb, st)
     fn = _lib.draft_sample
@@ -361,12 +397,14 @@ def pacer_lengths(scores, block, max_blocks, t0, rho, *, lengths=None, offsets=N
     B = scores.shape[0]
     if scores.dim() != 2 or scores.shape[1] != max_blocks * block:
         raise ValueError(f"scores must be [B, {max_blocks * block}], got {tuple(scores.shape)}")
-    lengths = lengths if lengths is not None else torch.empty(B, dtype=torch.int32, device=dev)
-    offsets = offsets if offsets is not None else torch.empty(B + 1, dtype=torch.int32, device=dev)
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        lengths = lengths if lengths is not None else torch.empty(B, dtype=torch.int32, device=dev)
+        offsets = offsets if offsets is not None else torch.empty(B + 1, dtype=torch.int32, device=dev)
     _need(lengths, torch.int32, "lengths")
     _need(offsets, torch.int32, "offsets")
     _check(_lib.pacer_lengths(B, block, max_blocks, float(t0), float(rho), _ptr(scores), _ptr(lengths),
-                              _ptr(offsets), stream if stream is not None else _stream(dev)))
+                              _ptr(offsets), st))
     return dict(lengths=lengths, offsets=offsets)
 
 
@@ -394,14 +432,15 @@ def prepare_tree_verify(target_logits, draft_logits, node_offsets, draft_offsets
                     "draft_offsets"), (parent, torch.int32, "parent"), (tokens, torch.int32, "tokens"),
                     (uniforms, torch.float32, "uniforms")):
         _need(t, d, n)
-    mk = lambda n, d: torch.empty(n, dtype=d, device=dev)  # noqa: E731
-    num_accepted = num_accepted if num_accepted is not None else mk(B, torch.int32)
-    last_node = last_node if last_node is not None else mk(B, torch.int32)
-    final_token = final_token if final_token is not None else mk(B, torch.int32)
-    status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-    nbytes = tree_verify_workspace_bytes(dt, B, V, nodes, rows_d)
-    ws, wsb = _workspace(nbytes, dev, workspace)
-    st = stream if stream is not None else _stream(dev)
+    ctx, st = _on_stream(stream, dev)
+    with ctx:
+        mk = lambda n, d: torch.empty(n, dtype=d, device=dev)  # noqa: E731
+        num_accepted = num_accepted if num_accepted is not None else mk(B, torch.int32)
+        last_node = last_node if last_node is not None else mk(B, torch.int32)
+        final_token = final_token if final_token is not None else mk(B, torch.int32)
+        status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
+        nbytes = tree_verify_workspace_bytes(dt, B, V, nodes, rows_d)
+        ws, wsb = _workspace(nbytes, dev, workspace)
     args = (dt, B, V, float(temperature), _ptr(node_offsets), _ptr(parent), _ptr(tokens), nodes, _ptr(target_logits),
             _ptr(draft_offsets), rows_d, _ptr(draft_logits), _ptr(uniforms), _ptr(num_accepted), _ptr(last_node),
             _ptr(final_token), _ptr(status_flags), _ptr(ws), wsb, st)

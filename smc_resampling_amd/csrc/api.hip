@@ -71,7 +71,9 @@ SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   SmcLayout l;
   l.ws_logw = kCounterBytes;
   l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
-  l.tpart = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 1) * nt));
+  // the segment partials of every row, then (power target) those of each
+  // particle's bonus row at the plain scale: 2K+2 rows per particle
+  l.tpart = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 2) * nt));
   l.total = align_up(l.tpart + sizeof(float2) * (size_t)(PN * nt));
   return l;
 }
@@ -108,6 +110,7 @@ void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, 
   s->c = (float)(1.4426950408889634 / (double)T);
   s->cb = s->c;
   s->part = reinterpret_cast<float2*>(ws + part_off);
+  s->part1 = nullptr;
   s->tpart = reinterpret_cast<float2*>(ws + tpart_off);
   s->ctr = reinterpret_cast<uint32_t*>(ws);
   s->flags = flags;
@@ -167,7 +170,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   const bool vec = vec_ok(dtype, V, target_logits, draft_logits);
   const int64_t rows = 2 * total_draft_rows + B;
   smcsd::Plan plan;
-  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, false, &plan) != hipSuccess) return SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::SdArgs a;
   fill_step(&a.s, plan, target_logits, draft_logits, draft_offsets, draft_tokens, B, total_draft_rows + B,
@@ -202,7 +205,7 @@ int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, con
   const bool bf16 = dtype == SMCSD_BF16;
   const bool vec = vec_ok(dtype, V, logits, nullptr);
   smcsd::Plan plan;
-  if (smcsd::plan_stream(R, ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  if (smcsd::plan_stream(R, ntiles_of(V), bf16, vec, false, &plan) != hipSuccess) return SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::SdArgs a;
   fill_step(&a.s, plan, logits, nullptr, nullptr, nullptr, R, R, 0, V, 0, temperature, ws, l.part, l.tpart,
@@ -245,7 +248,7 @@ int32_t tree_verify(int32_t dtype, int32_t B, int32_t V, float temperature, cons
   const bool bf16 = dtype == SMCSD_BF16;
   const bool vec = vec_ok(dtype, V, target_logits, num_draft_rows > 0 ? draft_logits : nullptr);
   smcsd::Plan plan;
-  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, false, &plan) != hipSuccess) return SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::TreeArgs a;
   // flat streaming: group g is target row g, then draft row g - num_nodes
@@ -310,14 +313,19 @@ static int32_t smc_step(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t 
     return SMCSD_ERR_WORKSPACE;
   const bool bf16 = dtype == SMCSD_BF16;
   const bool vec = vec_ok(dtype, V, target_logits, K > 0 ? draft_logits : nullptr);
+  // a power target (beta != 1) also reduces every bonus row at the plain scale
+  const bool power = beta != 1.0f;
   smcsd::Plan plan;
-  if (smcsd::plan_stream(PN * (2 * K + 1), ntiles_of(V), bf16, vec, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  const int64_t rows = PN * (2 * K + 1);
+  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, power, &plan) != hipSuccess) return SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::SmcArgs a;
   fill_step(&a.s, plan, target_logits, draft_logits, nullptr, draft_tokens, PN, PN * (K + 1), PN * K, V, K,
             temperature, ws, l.part, l.tpart, status_flags);
   a.s.cb = (float)cb;
+  a.s.part1 = power ? a.s.part + rows * plan.nseg : nullptr;  // after the call's own partials
   a.beta = beta;
+  a.power = power ? 1 : 0;
   a.N = N;
   a.L = pages_per_particle;
   a.ess_frac = ess_frac;

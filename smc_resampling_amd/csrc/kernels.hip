@@ -30,9 +30,10 @@
 // rows by ancestor.
 //
 // Nothing waits on another workgroup: hand-offs inside a tail kernel are
-// counters that the last arrival observes, and the values handed over
-// (residual masses, log-weights) are written and read at the device coherence
-// point (agent-scope atomics), so no XCD-local L2 holds a stale copy.  Every
+// counters that the last arrival observes.  Each arrival is a device-scope
+// release that follows the values it hands over (log-weights), and the last
+// arrival's workgroup acquires before reading them; the values themselves are
+// written and read at the device coherence point (agent-scope atomics).  Every
 // counter is back at zero when the kernel ends.
 #include <hip/hip_ext.h>
 
@@ -64,14 +65,15 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT));
 }
-// wait until every memory operation this wavefront issued has completed
-__device__ __forceinline__ void stores_done() {
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+// Arrival at a counter: a release at device scope, so every store this thread
+// made before it (the values it hands over) is visible to a thread that
+// acquires after reading the count.
+__device__ __forceinline__ uint32_t ctr_arrive(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t ctr_add(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// The acquire that pairs with every earlier arrival, for the whole workgroup
+// of the last arrival.
+__device__ __forceinline__ void acquire_arrivals() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // ---------------------------------------------------------------------------
 // groups
@@ -231,8 +233,10 @@ __device__ __forceinline__ void cursor_set(GroupCursor& cu, int64_t g, const Ste
 
 // TP: the call's segments span several tiles, so each group's bonus row also
 // gets per-tile partials (with one-tile segments the segment partials are
-// those already).
-template <typename DT, bool VL, int NS, bool TP>
+// those already).  PW (SMC with a power target, whose groups are all 2K+1
+// rows): each group's bonus row is reduced at its own scale cb, and also at
+// the plain scale c into part1 (segment partials, group-major).
+template <typename DT, bool VL, int NS, bool TP, bool PW>
 __device__ __forceinline__ void stream_body(const StepArgs& a) {
   using raw = typename DT::raw;
   const int lane = threadIdx.x % WAVE;
@@ -286,14 +290,14 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   // time: a store is a memory operation the loads' wait counter also counts.
   int csg = (int)(u0 % nseg);
   int ct = csg * seg, cte = min(ntiles, ct + seg);
-  // the scale of the row being reduced: c, or cb for a group's bonus row when
-  // the call gives that row its own (SMC, whose groups are all 2K+1 rows: the
-  // row within its group is the row index modulo 2K+1)
-  const bool split = a.cb != c;
+  // the scale of the row being reduced: c, or cb for a group's bonus row with
+  // a power target (the row within its group is the row index modulo 2K+1)
   const int grows = 2 * a.K + 1;
-  int crr = split ? (int)((u0 / nseg) % grows) : 0;
-  float cc = split && crr == a.K ? a.cb : c;
+  int crr = PW ? (int)((u0 / nseg) % grows) : 0;
+  int64_t cgrp = PW ? (u0 / nseg) / grows : 0;  // group of the row being reduced
+  float cc = PW && crr == a.K ? a.cb : c;
   float m = -INFINITY, s = 0.0f;
+  float m1 = -INFINITY, s1 = 0.0f;  // PW: the bonus row's unit at scale c
   float2 pb = make_float2(0.0f, 0.0f);
   int64_t pbase = u0;
   int pn = 0;
@@ -306,6 +310,8 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
       s = 0.0f;
     }
     lane_fold_tile<DT>(x, cc, m, s);
+    const bool bon1 = PW && crr == a.K;
+    if (bon1) lane_fold_tile<DT>(x, c, m1, s1);
     if (TP && dst >= 0) {
       const float2 tp = wave_partial(m, s);
       if (lane == 0) a.tpart[dst] = tp;
@@ -321,10 +327,19 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
       }
       m = -INFINITY;
       s = 0.0f;
+      if (bon1) {
+        const float2 p1 = wave_partial(m1, s1);
+        if (lane == 0) a.part1[cgrp * nseg + csg] = p1;
+        m1 = -INFINITY;
+        s1 = 0.0f;
+      }
       if (++csg == nseg) {
         csg = 0;
-        if (split) {
-          if (++crr == grows) crr = 0;
+        if (PW) {
+          if (++crr == grows) {
+            crr = 0;
+            cgrp++;
+          }
           cc = crr == a.K ? a.cb : c;
         }
       }
@@ -382,9 +397,9 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
 }
 
 // NS tiles in flight per wavefront, at the occupancy the registers allow.
-template <typename DT, bool VL, int NS, bool TP>
+template <typename DT, bool VL, int NS, bool TP, bool PW>
 __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
-  stream_body<DT, VL, NS, TP>(a);
+  stream_body<DT, VL, NS, TP, PW>(a);
 }
 
 // Calls with one-tile segments (a few tiles per wavefront; bf16 rows that
@@ -394,16 +409,18 @@ __global__ __launch_bounds__(BLOCK) void k_stream(StepArgs a) {
 // 10.6 GB call, where the deeper pipeline wins).
 template <typename DT, bool VL>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(6, 6))) void k_stream_wide(StepArgs a) {
-  stream_body<DT, VL, 2, false>(a);
+  stream_body<DT, VL, 2, false, false>(a);
 }
 
 // ---------------------------------------------------------------------------
 // tails: workgroup-shared state
 // ---------------------------------------------------------------------------
 struct TailLds {
-  float M[MAXR];             // row max of z c (log2 domain)
-  double S[MAXR];            // row sum of 2^(z c - M)
-  double lS[MAXR];           // log S
+  // per row of the group (and, for a power target, the bonus row at the
+  // plain scale as row 2K+1)
+  float M[MAXR + 1];         // row max of z c (log2 domain)
+  double S[MAXR + 1];        // row sum of 2^(z c - M)
+  double lS[MAXR + 1];       // log S
   float z[2 * SMCSD_MAX_K];  // logits of the draft tokens: target rows, then draft rows
   float u[SMCSD_MAX_K];      // accept uniforms
   int xok[SMCSD_MAX_K];      // draft token inside [0, V)
@@ -448,8 +465,9 @@ __device__ __forceinline__ void fold(float& m, double& s, float pm, double ps) {
 
 // Row statistics of rows [0, R) of one group from its segment partials (row
 // r's at part[r * nseg + k], written by the previous kernel) into L.M / L.S /
-// L.lS.  Whole workgroup, 16 threads per row, fixed combination order, so
-// equal rows get equal statistics.
+// L.lS, and with `extra` one more row, row R, whose nseg partials lie at extra
+// (further on in the same workspace).  Whole workgroup, 16 threads per row,
+// fixed combination order, so equal rows get equal statistics.
 template <int CTRL>
 __device__ __forceinline__ void fold_dpp(float& m, double& s) {
   fold(m, s, dpp_f32m<CTRL>(m), dpp_f64<CTRL>(s));
@@ -460,16 +478,20 @@ constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_MIRROR = 0x140
 
 template <int NT>
 __device__ __forceinline__ void merge_rows_to(const float2* __restrict__ part, int R, int nseg, float* Mo,
-                                              double* So, double* lSo) {
+                                              double* So, double* lSo, const float2* extra = nullptr) {
   constexpr int TPR = 16;  // threads per row: one DPP row
   const int sub = threadIdx.x & (TPR - 1);
-  // the group's partials through a buffer resource: 32-bit offsets
-  const __amdgpu_buffer_rsrc_t rs = buffer_over(part, (uint32_t)(R * nseg * (int)sizeof(float2)));
-  for (int r0 = 0; r0 < R; r0 += NT / TPR) {
+  // the group's partials (and the extra row's) through one buffer resource:
+  // 32-bit offsets
+  const int xoff = extra ? (int)(extra - part) : 0;  // in partials
+  const int RR = extra ? R + 1 : R;
+  const __amdgpu_buffer_rsrc_t rs =
+      buffer_over(part, (uint32_t)((extra ? xoff + nseg : R * nseg) * (int)sizeof(float2)));
+  for (int r0 = 0; r0 < RR; r0 += NT / TPR) {
     const int r = r0 + (int)threadIdx.x / TPR;
     float m = -INFINITY;
     double s = 0.0;
-    if (r < R) {
+    if (r < RR) {
       // at most MAX_TILES / 16 = 16 partials per thread, in batches of GB
       // loads in flight (8, or 4 in the smaller workgroups that keep fewer
       // registers; indices past the row clamped, so the loads need no branch;
@@ -477,7 +499,7 @@ __device__ __forceinline__ void merge_rows_to(const float2* __restrict__ part, i
       // for here), folded in ascending k
       constexpr int GB = NT >= 1024 ? 8 : 4;
       constexpr int NB = MAX_TILES / (GB * TPR);
-      const int row0 = r * nseg;
+      const int row0 = r < R ? r * nseg : xoff;
 #pragma unroll
       for (int h = 0; h < NB; h++) {
         const int k0 = sub + h * GB * TPR;
@@ -497,7 +519,7 @@ __device__ __forceinline__ void merge_rows_to(const float2* __restrict__ part, i
     fold_dpp<DPP_ROW_HALF_MIRROR>(m, s);
     fold_dpp<DPP_QUAD_XOR1>(m, s);
     fold_dpp<DPP_QUAD_XOR2>(m, s);
-    if (r < R && sub == 0) {
+    if (r < RR && sub == 0) {
       Mo[r] = m;
       So[r] = s;
       lSo[r] = log(s);
@@ -1470,7 +1492,8 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   const int32_t xt = token_of<BLOCK>(s, G);
   const float lw_in = a.logw[i];
   const float ub = a.bonus_u[i];
-  merge_rows<BLOCK>(pg, 2 * K + 1, s.nseg, L);
+  // power target: the bonus row at the plain scale too, as row 2K+1
+  merge_rows_to<BLOCK>(pg, 2 * K + 1, s.nseg, L.M, L.S, L.lS, a.power ? s.part1 + i * s.nseg : nullptr);
   int bnp, bper;
   const float2* bp = bonus_partials(s, G.fr0, i, K, &bnp, &bper);
   stage_partials<BLOCK>(bp, bnp, L);
@@ -1496,6 +1519,17 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
       }
       delta += wave_sum_f64(dj);
     }
+    if (a.power) {
+      // the (K+1)-th token comes from the normalised p_K^beta, so its weight
+      // is Z_beta = sum_y p_K(y)^beta = exp(LSE(beta a) - beta LSE(a)), with
+      // LSE(beta a) = M ln 2 + ln S from the bonus row's statistics at its own
+      // scale and LSE(a) from those at the plain scale (row 2K+1); beta is
+      // taken as the ratio of the two scales the statistics were formed with
+      const RowStat sb = stat_of(L, K), s1 = stat_of(L, 2 * K + 1);
+      if (!s1.ok) fl |= FLAG_NONFINITE;
+      const double bb = (double)s.cb / (double)s.c;
+      delta += ((double)sb.M - bb * (double)s1.M) * 0.69314718055994530942 + (sb.lS - bb * s1.lS);
+    }
     lw = (float)((double)lw_in + delta);
     if (lw != lw || lw == INFINITY) fl |= FLAG_NONFINITE;
   }
@@ -1503,12 +1537,11 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   if (!sk.ok) fl |= FLAG_NONFINITE;
   const int64_t p = i / a.N;
   uint32_t before = 0;
-  // the log-weight is visible before the count that announces it
+  // the log-weight, then the count that announces it (a release)
   auto publish = [&]() {
     if (wave == 1 && lane == 0) {
       st_dev(a.ws_logw + i, lw);
-      stores_done();
-      before = ctr_add(s.ctr + p * CTR_STRIDE, 1u);
+      before = ctr_arrive(s.ctr + p * CTR_STRIDE);
     }
   };
   // the bonus row's statistics and draw are at its own scale (beta / T)
@@ -1523,7 +1556,7 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   }
   if (s_last) {
     lds_barrier();  // thread 0 has read L.fl: the prompt's LDS overlays it
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    acquire_arrivals();  // every particle's log-weight, released with its count
     smc_prompt_tail(a, p, sh.p);
   }
 }
@@ -1559,28 +1592,33 @@ static const void* kptr(K k) {
   return reinterpret_cast<const void*>(k);
 }
 
-template <typename DT, bool TP>
+template <typename DT, bool TP, bool PW>
 static const void* stream_kernel_t(bool vec) {
-  return vec ? kptr(&k_stream<DT, true, slots_of<DT>(), TP>) : kptr(&k_stream<DT, false, slots_of<DT>(), TP>);
+  return vec ? kptr(&k_stream<DT, true, slots_of<DT>(), TP, PW>) : kptr(&k_stream<DT, false, slots_of<DT>(), TP, PW>);
 }
 
-static const void* stream_kernel(bool bf16, bool vec, bool tp, bool wide = false) {
-  if (bf16 && vec && wide) return kptr(&k_stream_wide<Bf16, true>);
-  if (bf16) return tp ? stream_kernel_t<Bf16, true>(vec) : stream_kernel_t<Bf16, false>(vec);
-  return tp ? stream_kernel_t<F32, true>(vec) : stream_kernel_t<F32, false>(vec);
+template <bool PW>
+static const void* stream_kernel_p(bool bf16, bool vec, bool tp) {
+  if (bf16) return tp ? stream_kernel_t<Bf16, true, PW>(vec) : stream_kernel_t<Bf16, false, PW>(vec);
+  return tp ? stream_kernel_t<F32, true, PW>(vec) : stream_kernel_t<F32, false, PW>(vec);
+}
+
+static const void* stream_kernel(bool bf16, bool vec, bool tp, bool wide, bool pw) {
+  if (bf16 && vec && wide && !pw) return kptr(&k_stream_wide<Bf16, true>);
+  return pw ? stream_kernel_p<true>(bf16, vec, tp) : stream_kernel_p<false>(bf16, vec, tp);
 }
 
 // Segments long enough that each resident wavefront streams about 32 units
 // (fewer wavefront reductions on large calls), at least SEG_MIN and at most 8
 // tiles.  From TP_MIN_SEG tiles on, the bonus rows also get tile partials, so
 // a draw re-reads one tile rather than its segment.  bf16 calls with 16-byte
-// loads whose segments are single tiles use k_stream_wide.  The streaming grid is what the
-// device holds at once of the chosen kernel, fewer when there is not one unit
-// per wavefront.
+// loads whose segments are single tiles use k_stream_wide (not with a power
+// target).  The streaming grid is what the device holds at once of the chosen
+// kernel, fewer when there is not one unit per wavefront.
 constexpr int SEG_MIN = 1, TP_MIN_SEG = 2;
 
-hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p) {
-  const int resident = resident_blocks(stream_kernel(bf16, vec, false));
+hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, bool pw, Plan* p) {
+  const int resident = resident_blocks(stream_kernel(bf16, vec, false, false, pw));
   if (resident <= 0) return hipErrorInvalidDevice;
   const int64_t waves = (int64_t)resident * WAVES_PER_BLOCK;
   const int64_t tiles = rows * ntiles;
@@ -1592,8 +1630,9 @@ hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p) {
   p->nseg = nseg;
   p->units = rows * nseg;
   p->tp = p->seg >= TP_MIN_SEG;
-  p->wide = bf16 && vec && p->seg == 1;
-  const int held = p->wide ? resident_blocks(stream_kernel(bf16, vec, false, true)) : resident;
+  p->pw = pw;
+  p->wide = bf16 && vec && p->seg == 1 && !pw;
+  const int held = p->wide ? resident_blocks(stream_kernel(bf16, vec, false, true, false)) : resident;
   if (held <= 0) return hipErrorInvalidDevice;
   const int64_t want = (p->units + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   p->grid = (int)(want < held ? want : held);
@@ -1627,8 +1666,8 @@ static const void* smc_tail_kernel() {
 }
 
 hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
-  hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
-                        t.stream_stop);
+  hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide, p.pw), (unsigned)p.grid, BLOCK, a.s, s,
+                        t.stream_start, t.stream_stop);
   if (e != hipSuccess) return e;
   if (a.s.K == 0 && !a.s.offsets) {  // draws only
     const void* k = bf16 ? (vec ? draw_tail_kernel<Bf16, true>() : draw_tail_kernel<Bf16, false>())
@@ -1641,8 +1680,8 @@ hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStr
 }
 
 hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
-  hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
-                        t.stream_stop);
+  hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide, p.pw), (unsigned)p.grid, BLOCK, a.s, s,
+                        t.stream_start, t.stream_stop);
   if (e != hipSuccess) return e;
   const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())
                        : (vec ? smc_tail_kernel<F32, true>() : smc_tail_kernel<F32, false>());
@@ -1655,8 +1694,8 @@ static const void* tree_tail_kernel() {
 }
 
 hipError_t launch_tree(const TreeArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
-  hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide), (unsigned)p.grid, BLOCK, a.s, s, t.stream_start,
-                        t.stream_stop);
+  hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide, p.pw), (unsigned)p.grid, BLOCK, a.s, s,
+                        t.stream_start, t.stream_stop);
   if (e != hipSuccess) return e;
   const void* k = bf16 ? (vec ? tree_tail_kernel<Bf16, true>() : tree_tail_kernel<Bf16, false>())
                        : (vec ? tree_tail_kernel<F32, true>() : tree_tail_kernel<F32, false>());

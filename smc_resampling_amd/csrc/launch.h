@@ -33,6 +33,7 @@ struct StepArgs {
   float c;        // log2(e) / T
   float cb;       // scale of each group's bonus row: c, or beta * log2(e) / T for a power target
   float2* part;   // [units] segment partials (max of z c, sum of 2^(z c - max))
+  float2* part1;  // power target: [ngroups * nseg] segment partials of each group's bonus row at scale c
   float2* tpart;  // [ngroups * ntiles] tile partials of each group's bonus row
   uint32_t* ctr;  // counter lines (zero between calls)
   uint32_t* flags;
@@ -49,6 +50,7 @@ struct SdArgs {
 struct SmcArgs {
   StepArgs s;
   float beta;  // power target: draft tokens add beta log p - log q
+  int power;   // beta != 1: the bonus token also adds log sum_y p_K(y)^beta
   int N, L;
   float ess_frac;
   const float* bonus_u;
@@ -83,6 +85,7 @@ struct Plan {
   int seg, nseg;
   bool tp;    // bonus-row tile partials (segments long enough that a re-read would cost)
   bool wide;  // k_stream_wide (bf16, one-tile segments)
+  bool pw;    // power target: the bonus rows also at the plain scale
   int64_t units;
   int grid;
 };
@@ -93,7 +96,7 @@ struct KernelTimers {
   hipEvent_t stream_start, stream_stop, tail_start, tail_stop;
 };
 
-hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, Plan* p);
+hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, bool pw, Plan* p);
 // Each launches the streaming kernel, then the tail kernel; with timers, the
 // launches carry the events.
 hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);

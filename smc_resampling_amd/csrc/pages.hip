@@ -650,10 +650,13 @@ __global__ __launch_bounds__(BLOCK) void k_pages_stage(ResampleArgs a) {
   if (k < a.R) stage_row(a, k);
   mem_done();
   __syncthreads();
+  // the workgroup's stores are complete; the arrival releases them at device
+  // scope, and the last workgroup to arrive acquires every earlier arrival's
   if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(a.arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    s_last = __hip_atomic_fetch_add(a.arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   scan_offsets<BLOCK>(a, lds);
   if (threadIdx.x == 0) __hip_atomic_store(a.arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

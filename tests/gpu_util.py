@@ -75,6 +75,37 @@ def check_sd(case, label="", ignore_flags=8):
     return t
 
 
+def oracle_threads():
+    """Host threads for oracle calls that run side by side (the oracle's C
+    calls release the GIL): one per available core, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def check_sd_many(cases, labels, ignore_flags=8):
+    """check_sd over many cases: every GPU call first, then the oracle on a
+    pool of host threads, then the comparisons in order.  Returns the merged
+    tally."""
+    import concurrent.futures as cf
+
+    from compare import Tally
+
+    gpu = [run_sd_gpu(c) for c in cases]
+    total = Tally()
+    with cf.ThreadPoolExecutor(max_workers=oracle_threads()) as ex:
+        refs = ex.map(run_sd_oracle, cases)
+        for c, lab, (na, ft, fl), ref in zip(cases, labels, gpu, refs):
+            t = compare_sd(c, ref, na, ft, lab)
+            say(f"[sd {lab}] {t.summary()} flags gpu={fl} oracle={ref['flags']}")
+            t.assert_ok()
+            assert (fl & ~ignore_flags) == (ref["flags"] & ~ignore_flags), (fl, ref["flags"])
+            total.merge(t)
+    return total
+
+
 def run_smc_gpu(case, logw, pt, ess_frac=0.5):
     s = lib()
     lw = torch.from_numpy(np.array(logw, np.float32)).to(DEV)

@@ -121,3 +121,25 @@ def test_tree_workspace_sizes(s):
     assert s.tree_verify_workspace_bytes(1, 0, 100, 0, 0) == 0
     a = s.tree_verify_workspace_bytes(1, 64, 32768, 64 * 15, 64 * 7)
     assert a % 256 == 0 and a >= 2 * (64 * 22) * 16 * 8 + (4 << 20)
+
+
+def test_csr_call_needs_k(s):
+    """A ragged (CSR) sd_verify call must name K, its largest draft length: the
+    binding never reads a device value back to find it (checked before any
+    tensor reaches the device, so host tensors do here)."""
+    import torch
+
+    t = torch.zeros((5, 16), dtype=torch.float32)
+    d = torch.zeros((3, 16), dtype=torch.float32)
+    off = torch.tensor([0, 1, 3], dtype=torch.int32)
+    with pytest.raises(ValueError, match="needs K"):
+        s.prepare_sd_verify(t, d, torch.zeros(3, dtype=torch.int32), torch.zeros(5), 1.0, draft_offsets=off)
+
+
+def test_read_ceiling_rejects_bad_buffers(s):
+    L = s.lib()
+    sink = ctypes.c_void_p(1 << 40)
+    assert L.smcsd_read_ceiling(None, 64, None, 0, sink, None, None, None) == 1  # NULL with a size
+    assert L.smcsd_read_ceiling(ctypes.c_void_p(1 << 40), 63, None, 0, sink, None, None, None) == 1  # odd size
+    assert L.smcsd_read_ceiling(ctypes.c_void_p((1 << 40) + 8), 64, None, 0, sink, None, None, None) == 1  # align
+    assert L.smcsd_read_ceiling(ctypes.c_void_p(1 << 40), 64, None, 0, None, None, None, None) == 1  # no sink

@@ -97,8 +97,10 @@ def test_sd_deterministic():
     assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
 
 
-def _config_steps(idx, steps):
-    from gpu_util import check_sd, host_logits, oracle_lengths, say
+def _config_steps(idx, steps, chunk=16):
+    """Full-size steps of a workload, element by element against the oracle
+    (the oracle's calls side by side on host threads, `chunk` steps at a time)."""
+    from gpu_util import check_sd_many, host_logits, oracle_lengths, say
 
     import synth
     from compare import Tally
@@ -106,13 +108,18 @@ def _config_steps(idx, steps):
     cfg = synth.CONFIGS[idx]
     gen = synth.Generator(cfg, lengths=oracle_lengths)
     total = Tally()
-    for s in steps:
-        st = gen.sd_step(s)
-        case = dict(target=host_logits(st["target"]), draft=host_logits(st["draft"]),
-                    tokens=st["tokens"].cpu().numpy(), uniforms=st["uniforms"].cpu().numpy(),
-                    offsets=None if st["offsets"] is None else st["offsets"].cpu().numpy(), K=st["K"], T=cfg.T)
-        total.merge(check_sd(case, f"{cfg.name} step {s}"))
-    say(f"[{cfg.name}] total {total.summary()}")
+    steps = list(steps)
+    for c0 in range(0, len(steps), chunk):
+        cases, labels = [], []
+        for s in steps[c0:c0 + chunk]:
+            st = gen.sd_step(s)
+            cases.append(dict(target=host_logits(st["target"]), draft=host_logits(st["draft"]),
+                              tokens=st["tokens"].cpu().numpy(), uniforms=st["uniforms"].cpu().numpy(),
+                              offsets=None if st["offsets"] is None else st["offsets"].cpu().numpy(), K=st["K"],
+                              T=cfg.T))
+            labels.append(f"{cfg.name} step {s}")
+        total.merge(check_sd_many(cases, labels))
+    say(f"[{cfg.name}] {len(steps)} steps, total {total.summary()}")
     total.assert_ok()
 
 
@@ -121,11 +128,38 @@ def test_cfg0_all_steps():
 
 
 def test_cfg1_full_size():
-    _config_steps(1, range(6))
+    """32 of the 256 steps of the 64-sequence workload."""
+    _config_steps(1, range(32))
 
 
 def test_cfg4_ragged_full_size():
-    _config_steps(4, range(2))
+    """16 of the 128 steps of the ragged 256-sequence workload."""
+    _config_steps(4, range(16), chunk=8)
+
+
+def test_sd_side_stream_without_workspace():
+    """A call on a stream other than the current one, with no workspace or
+    outputs given: the binding allocates and zero-fills them on that stream,
+    so the kernels see zeroed counters and flags (the current stream is kept
+    busy meanwhile, so an unordered fill would land late)."""
+    import torch
+
+    import smc_resampling_amd as s
+    from compare import compare_sd
+    from gpu_util import DEV, dev_logits, run_sd_oracle
+
+    side = torch.cuda.Stream(device=DEV)
+    for i in range(3):
+        c = sd_case(300 + i, 48, 20000, T=0.9, K=4, delta=1.0, dtype="bf16")
+        args = [dev_logits(c["target"]), dev_logits(c["draft"]), torch.from_numpy(c["tokens"]).to(DEV),
+                torch.from_numpy(c["uniforms"]).to(DEV)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)  # the current stream is busy
+        na, ft, fl = s.sd_verify(*args, c["T"], K=c["K"], stream=side.cuda_stream)
+        side.synchronize()
+        torch.cuda.synchronize()
+        compare_sd(c, run_sd_oracle(c), na.cpu().numpy(), ft.cpu().numpy(), f"side stream {i}").assert_ok()
+        assert int(fl.item()) & ~8 == 0
 
 
 def test_sd_workspace_reuse():

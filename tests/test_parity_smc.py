@@ -106,15 +106,19 @@ def test_smc_multi_step_lockstep():
 
 
 def _cfg_smc(idx, steps, prompts=None, beta=None):
-    """Full-size config; the oracle checks `prompts` (all when None) in lockstep
-    (with ``beta``, the power-sampling target)."""
+    """Full-size workload in lockstep: every step runs on the GPU for all
+    prompts; the oracle checks `prompts` (all when None) from the GPU's state
+    before the step (with ``beta``, the power-sampling target).  The oracle's
+    per-prompt calls run side by side on host threads."""
+    import concurrent.futures as cf
+
     import torch
 
     import oracle
     import smc_resampling_amd as s
     import synth
     from compare import Tally, compare_smc
-    from gpu_util import host_logits, say
+    from gpu_util import host_logits, oracle_threads, say
 
     cfg = synth.CONFIGS[idx]
     gen = synth.Generator(cfg)
@@ -123,37 +127,47 @@ def _cfg_smc(idx, steps, prompts=None, beta=None):
     logw = torch.zeros(P * N, dtype=torch.float32, device="cuda")
     pt = torch.from_numpy(synth.initial_page_table(P, N, cfg.L)).cuda()
     total = Tally()
-    for step in steps:
-        st = gen.smc_step(step)
-        lw_in = logw.cpu().numpy()
-        pt_in = pt.cpu().numpy()
-        out = s.smc_reweight_resample(st["target"], st["draft"], st["tokens"], st["bonus_u"], st["resample_u"], logw,
-                                      cfg.T, cfg.ess_frac, P, N, K, page_table_in=pt, beta=beta)
-        torch.cuda.synchronize()
-        g = {k: v.cpu().numpy() for k, v in out.items() if k != "log_weights"}
-        g["logw"] = logw.cpu().numpy()
-        assert int(out["status_flags"].item()) & ~8 == 0
-        # invariants on every prompt
-        anc = g["ancestors"].reshape(P, N)
-        assert (np.diff(anc, axis=1) >= 0).all()
-        assert (g["page_table_out"] == pt_in[(np.arange(P)[:, None] * N + anc).ravel()]).all()
-        for p in prompts:
-            rows_t = slice(p * N * (K + 1), (p + 1) * N * (K + 1))
-            rows_d = slice(p * N * K, (p + 1) * N * K)
-            case = dict(target=host_logits(st["target"][rows_t]), draft=host_logits(st["draft"][rows_d]),
-                        tokens=st["tokens"][rows_d].cpu().numpy(), bonus_u=st["bonus_u"][p * N:(p + 1) * N].cpu().numpy(),
-                        resample_u=st["resample_u"][p:p + 1].cpu().numpy(), P=1, N=N, K=K, T=cfg.T, beta=beta)
-            sl = slice(p * N, (p + 1) * N)
-            ref = oracle.smc_step(case["target"], case["draft"], case["tokens"], case["bonus_u"], case["resample_u"],
-                                  lw_in[sl], cfg.T, cfg.ess_frac, 1, N, K, pt_in=pt_in[sl], beta=beta)
-            gp = dict(bonus=g["bonus_token"][sl], ancestors=g["ancestors"][sl], ess=g["ess"][p:p + 1],
-                      resampled=g["resampled"][p:p + 1], logw=g["logw"][sl], pt_out=g["page_table_out"][sl])
-            t = compare_smc(case, ref, gp, lw_in[sl], pt_in[sl], f"{cfg.name} step {step} prompt {p}")
-            total.merge(t)
-            t.assert_ok()
-        say(f"[{cfg.name} step {step}] resampled {int(g['resampled'].sum())}/{P} ess[0]={g['ess'][0]:.3f} "
-            f"{total.summary()}")
-        pt = out["page_table_out"]
+    with cf.ThreadPoolExecutor(max_workers=oracle_threads()) as ex:
+        for step in steps:
+            st = gen.smc_step(step)
+            lw_in = logw.cpu().numpy()
+            pt_in = pt.cpu().numpy()
+            out = s.smc_reweight_resample(st["target"], st["draft"], st["tokens"], st["bonus_u"], st["resample_u"],
+                                          logw, cfg.T, cfg.ess_frac, P, N, K, page_table_in=pt, beta=beta)
+            torch.cuda.synchronize()
+            g = {k: v.cpu().numpy() for k, v in out.items() if k != "log_weights"}
+            g["logw"] = logw.cpu().numpy()
+            assert int(out["status_flags"].item()) & ~8 == 0
+            # invariants on every prompt
+            anc = g["ancestors"].reshape(P, N)
+            assert (np.diff(anc, axis=1) >= 0).all()
+            assert (g["page_table_out"] == pt_in[(np.arange(P)[:, None] * N + anc).ravel()]).all()
+            cases = []
+            for p in prompts:
+                rows_t = slice(p * N * (K + 1), (p + 1) * N * (K + 1))
+                rows_d = slice(p * N * K, (p + 1) * N * K)
+                cases.append(dict(target=host_logits(st["target"][rows_t]), draft=host_logits(st["draft"][rows_d]),
+                                  tokens=st["tokens"][rows_d].cpu().numpy(),
+                                  bonus_u=st["bonus_u"][p * N:(p + 1) * N].cpu().numpy(),
+                                  resample_u=st["resample_u"][p:p + 1].cpu().numpy(), P=1, N=N, K=K, T=cfg.T,
+                                  beta=beta))
+
+            def ref_of(pc):
+                p, c = pc
+                sl = slice(p * N, (p + 1) * N)
+                return oracle.smc_step(c["target"], c["draft"], c["tokens"], c["bonus_u"], c["resample_u"], lw_in[sl],
+                                       cfg.T, cfg.ess_frac, 1, N, K, pt_in=pt_in[sl], beta=beta)
+
+            for (p, case), ref in zip(zip(prompts, cases), ex.map(ref_of, zip(prompts, cases))):
+                sl = slice(p * N, (p + 1) * N)
+                gp = dict(bonus=g["bonus_token"][sl], ancestors=g["ancestors"][sl], ess=g["ess"][p:p + 1],
+                          resampled=g["resampled"][p:p + 1], logw=g["logw"][sl], pt_out=g["page_table_out"][sl])
+                t = compare_smc(case, ref, gp, lw_in[sl], pt_in[sl], f"{cfg.name} step {step} prompt {p}")
+                total.merge(t)
+                t.assert_ok()
+            say(f"[{cfg.name} step {step}] {len(prompts)} prompts checked, resampled {int(g['resampled'].sum())}/{P} "
+                f"ess[0]={g['ess'][0]:.3f} {total.summary()}")
+            pt = out["page_table_out"]
     total.assert_ok()
 
 
@@ -161,8 +175,14 @@ def test_cfg2_full_size():
     _cfg_smc(2, range(8))
 
 
-def test_cfg3_full_size_sampled_prompts():
-    _cfg_smc(3, range(1), prompts=[0, 1, 31])
+def test_cfg3_full_size_all_prompts():
+    """Steps 0-3 of the 32-prompt x 64-particle workload, every prompt."""
+    _cfg_smc(3, range(4))
+
+
+def test_cfg3_full_size_two_prompts_16_steps():
+    """Steps 0-15 in lockstep, prompts 0 (delta 0.5) and 31 (delta 2) checked."""
+    _cfg_smc(3, range(16), prompts=[0, 31])
 
 
 def test_cfg2_power_full_size():
@@ -173,6 +193,39 @@ def test_cfg3_power_sampled_prompts():
     """cfg3 shape (multi-tile segments: bonus rows with their own tile partials,
     at their own scale) with the power target."""
     _cfg_smc(3, range(1), prompts=[0, 17], beta=3.0)
+
+
+def test_smc_side_stream_without_workspace():
+    """An SMC call on a stream other than the current one, with no workspace
+    or outputs given: the binding zero-fills the workspace (whose counters
+    decide which particle runs its prompt's resampling) on the call's own
+    stream, while the current stream is kept busy."""
+    import torch
+
+    import oracle
+    import smc_resampling_amd as s
+    from compare import compare_smc
+    from gpu_util import DEV, dev_logits
+
+    side = torch.cuda.Stream(device=DEV)
+    for i in range(3):
+        c = smc_case(700 + i, 6, 32, 3, 9000, dtype="bf16", L=4, logw_scale=2.0)
+        lw = torch.from_numpy(c["logw"]).to(DEV)
+        pt = torch.from_numpy(c["pt"]).to(DEV)
+        args = [dev_logits(c["target"]), dev_logits(c["draft"]), torch.from_numpy(c["tokens"]).to(DEV),
+                torch.from_numpy(c["bonus_u"]).to(DEV), torch.from_numpy(c["resample_u"]).to(DEV), lw]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)  # the current stream is busy
+        out = s.smc_reweight_resample(*args, 1.0, 0.9, 6, 32, 3, page_table_in=pt, stream=side.cuda_stream)
+        side.synchronize()
+        torch.cuda.synchronize()
+        ref = oracle.smc_step(c["target"], c["draft"], c["tokens"], c["bonus_u"], c["resample_u"], c["logw"], 1.0, 0.9,
+                              6, 32, 3, pt_in=c["pt"])
+        g = dict(bonus=out["bonus_token"].cpu().numpy(), ancestors=out["ancestors"].cpu().numpy(),
+                 ess=out["ess"].cpu().numpy(), resampled=out["resampled"].cpu().numpy(), logw=lw.cpu().numpy(),
+                 pt_out=out["page_table_out"].cpu().numpy())
+        compare_smc(c, ref, g, c["logw"], c["pt"], f"side stream {i}").assert_ok()
+        assert int(out["status_flags"].item()) & ~8 == 0
 
 
 def test_smc_workspace_reuse():
