@@ -9,8 +9,12 @@ before timing starts; the batches together exceed the 256 MB Infinity Cache,
 so the timed steps stream from HBM.
 
 Prints one JSON line: verified draft positions per second (whole job), the
-roofline of the logit-streaming path against the 8 TB/s HBM peak, and the CPU
-oracle timed on a bounded sample of the same workload.
+roofline of the logit-streaming kernel against the 8 TB/s HBM peak and against
+the plain-read ceiling measured here at the call's byte count, the decision
+kernel's time and the whole call's bandwidth, and the CPU oracle timed on a
+bounded sample of the same workload (one thread, and one thread per host core
+up to 16).  The default workload is the largest, the 32-prompt x 64-particle
+SMC step at V = 151936.
 """
 from __future__ import annotations
 
@@ -63,11 +67,17 @@ def _find(d, suffix):
     return None
 
 
-def summarize(dirs, copy_bytes=None, kernel="k_stream"):
+# kernels of a call: the logit stream, and the decision path (one kernel, or
+# for SMC the particle kernel and the prompt kernel), by name part
+CALL_KERNELS = {"k_stream": ("k_stream",), "decision": ("_tail", "k_smc_prompt")}
+
+
+def summarize(dirs, copy_bytes=None):
     """Text summary of rocprofv3 output directories: kernel statistics
     (--kernel-trace --stats) and per-dispatch averages of PMC counters
-    (--pmc), with HBM traffic per launch of `kernel` when the directories
-    hold FETCH_SIZE / WRITE_SIZE and a copy of `copy_bytes` calibrates them."""
+    (--pmc), with HBM traffic per call of the streaming kernel and of the
+    decision path (CALL_KERNELS) when the directories hold FETCH_SIZE /
+    WRITE_SIZE and a copy of `copy_bytes` calibrates them."""
     out = [f"kernel_sources_sha256: {kernel_sources_hash()}"]
     avg = {}  # (kernel, counter) -> KiB per dispatch
     peak = {}  # (kernel, counter) -> largest single dispatch
@@ -93,40 +103,61 @@ def summarize(dirs, copy_bytes=None, kernel="k_stream"):
                 if len(out) < 60:
                     out.append(f"  {k[:90]} | {c} | dispatches {len(v)} | {a:.1f}")
     if copy_bytes:
-        def pick(table, name_part, counter):
-            vals = [v for (k, c), v in table.items() if name_part in k and c == counter]
-            return max(vals) if vals else None
-
-        res = {}
-        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            # the calibration copy is the largest copy dispatch of the run
-            kv, cv = pick(avg, kernel, counter), pick(peak, "copyBuffer", counter)
-            if kv is None or cv is None:
-                continue
-            factor = cv * 1024.0 / copy_bytes  # counter KiB per byte the copy moves
-            res[counter] = kv * 1024.0 / factor
-            out.append(f"{counter}: {kernel} {kv:.1f} KiB/dispatch, copy of {copy_bytes} B reads {cv:.1f} KiB "
-                       f"(factor {factor:.4f}) -> {res[counter]:.0f} B per launch")
-        if len(res) == 2:
-            out.append(f"traffic_bytes_per_launch: {res['FETCH_SIZE'] + res['WRITE_SIZE']:.0f}")
+        for role, parts in CALL_KERNELS.items():
+            res = {}
+            for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                # the calibration copy is the largest copy dispatch of the run
+                cv = max([v for (k, c), v in peak.items() if "copyBuffer" in k and c == counter] or [0.0]) or None
+                names = sorted(k for (k, c) in avg if c == counter and any(p in k for p in parts) and "k_read" not in k)
+                if not names or cv is None:
+                    continue
+                factor = cv * 1024.0 / copy_bytes  # counter KiB per byte the copy moves
+                res[counter] = 0.0
+                for k in names:  # one dispatch of each per call
+                    kv = avg[(k, counter)]
+                    res[counter] += kv * 1024.0 / factor
+                    out.append(f"{counter}: {k[:60]} {kv:.1f} KiB/dispatch, copy of {copy_bytes} B reads {cv:.1f} "
+                               f"KiB (factor {factor:.4f}) -> {kv * 1024.0 / factor:.0f} B per launch")
+            if len(res) == 2:
+                out.append(f"traffic_bytes_per_call {role}: {res['FETCH_SIZE'] + res['WRITE_SIZE']:.0f}")
     return "\n".join(out)
 
 
 def traffic_from_profiles(workload):
-    """HBM bytes per k_stream launch from the committed counter summary of this
-    workload, or None when there is none or the kernels changed since."""
+    """HBM bytes per launch of the streaming kernel and of the decision kernel
+    from the committed counter summary of this workload: (stream, decision), each
+    None when there is no summary or the kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"k_stream_{workload}_traffic.txt")
     if not os.path.exists(path):
-        return None
+        return None, None
     fields = {}
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_sources_sha256") != kernel_sources_hash() or "traffic_bytes_per_launch" not in fields:
-        return None
-    return float(fields["traffic_bytes_per_launch"])
+    if fields.get("kernel_sources_sha256") != kernel_sources_hash():
+        return None, None
+    get = lambda k: float(fields[k]) if k in fields else None  # noqa: E731
+    return get("traffic_bytes_per_call k_stream"), get("traffic_bytes_per_call decision")
+
+
+def host_description():
+    """CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, avail
 
 
 def parse():
@@ -134,9 +165,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1, help="workload index (default: the SD B=64 K=4 V=32768 bf16 case)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload index (default: the largest, SMC 32 prompts x 64 particles, K=8, V=151936 bf16)")
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's CPU sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="bound on each leg (one thread, all threads) of the oracle's CPU sample")
+    ap.add_argument("--cpu-threads", type=int, default=16, help="most host threads for the all-cores oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--max-batch-gb", type=float, default=24.0)
     ap.add_argument("--with-pages", action="store_true",
@@ -152,6 +186,121 @@ def parse():
     ap.add_argument("--summarize", nargs="+", default=None,
                     help="print a summary of these rocprofv3 output directories and exit")
     return ap.parse_args()
+
+
+def cpu_baseline(args, cfg, batches, nb, positions, R_draw):
+    """The oracle as it stands on a bounded sample of the workload's own
+    inputs: its unit of work (an SMC prompt, an SD or tree step, eight draft
+    rows) on host copies made before timing.  Two legs of about
+    --cpu-seconds each: one thread, then a pool of threads (one per host core
+    up to --cpu-threads; the oracle's C calls release the GIL), each worker
+    taking the next unit of the sample in turn.  Returns the baseline record."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    import synth
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import host_logits
+
+    model, avail = host_description()
+    threads = max(1, min(args.cpu_threads, avail))
+    units = []  # (callable, positions), at most `threads` of them (host memory bound)
+    if args.draft_sample:
+        for i in range(nb):
+            bt = batches[i]
+            u = (bt["bonus_u"] if cfg.kind == "smc" else bt["uniforms"])[:R_draw].cpu().numpy()
+            for r0 in range(0, R_draw, 8):
+                z = host_logits(bt["draft"][r0:min(r0 + 8, R_draw)])
+                units.append((lambda z=z, uu=u[r0:r0 + len(z)]: oracle.draft_sample(z, uu, cfg.T), len(z)))
+                if len(units) >= threads:
+                    break
+            if len(units) >= threads:
+                break
+        what = "blocks of 8 draft rows"
+    elif cfg.kind == "smc":
+        P, N, K = cfg.P, cfg.N, cfg.K
+        for i in range(nb):
+            bt = batches[i]
+            for p in range(P):
+                rt = slice(p * N * (K + 1), (p + 1) * N * (K + 1))
+                rd = slice(p * N * K, (p + 1) * N * K)
+                tg, dr = host_logits(bt["target"][rt]), host_logits(bt["draft"][rd])
+                tk = bt["tokens"][rd].cpu().numpy()
+                ub = bt["bonus_u"][p * N:(p + 1) * N].cpu().numpy()
+                ur = bt["resample_u"][p:p + 1].cpu().numpy()
+                units.append((lambda tg=tg, dr=dr, tk=tk, ub=ub, ur=ur: oracle.smc_step(
+                    tg, dr, tk, ub, ur, np.zeros(N, np.float32), cfg.T, cfg.ess_frac, 1, N, K, beta=args.beta),
+                    N * K))
+                if len(units) >= threads:
+                    break
+            if len(units) >= threads:
+                break
+        what = "prompts"
+    else:
+        for i in range(min(nb, threads)):
+            bt = batches[i]
+            tg, dr = host_logits(bt["target"]), host_logits(bt["draft"])
+            if cfg.kind == "tree":
+                host = {k: bt[k].cpu().numpy() for k in ("node_off", "draft_off", "parent", "tokens", "uniforms")}
+                units.append((lambda tg=tg, dr=dr, h=host: oracle.tree_verify(
+                    tg, dr, h["node_off"], h["draft_off"], h["parent"], h["tokens"], h["uniforms"], cfg.T),
+                    positions[i]))
+            else:
+                tk, u = bt["tokens"].cpu().numpy(), bt["uniforms"].cpu().numpy()
+                off = None
+                if bt["offsets"] is not None:
+                    # the oracle's own lengths for this step's scores (they equal the
+                    # library's, which laid out the batch)
+                    pc = cfg.pacer
+                    _, off = oracle.pacer_lengths(synth.pacer_scores(cfg.B, cfg.seed, i, pc["block"],
+                                                                     pc["max_blocks"]),
+                                                  pc["block"], pc["max_blocks"], pc["t0"], pc["rho"])
+                    if not np.array_equal(off, bt["offsets"].cpu().numpy()):
+                        sys.exit("PACER lengths of the library and the oracle differ")
+                units.append((lambda tg=tg, dr=dr, tk=tk, u=u, off=off: oracle.sd_verify(
+                    tg, dr, tk, u, cfg.T, K=cfg.K, offsets=off), positions[i]))
+        what = "steps"
+
+    def leg(workers):
+        done, n_units = 0, 0
+        t0 = time.perf_counter()
+        if workers == 1:
+            while time.perf_counter() - t0 < args.cpu_seconds:
+                fn, pos = units[n_units % len(units)]
+                fn()
+                done += pos
+                n_units += 1
+        else:
+            with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+                pending = set()
+                k = 0
+                while True:
+                    while len(pending) < workers and time.perf_counter() - t0 < args.cpu_seconds:
+                        fn, pos = units[k % len(units)]
+                        pending.add(ex.submit(lambda fn=fn, pos=pos: (fn(), pos)[1]))
+                        k += 1
+                    if not pending:
+                        break
+                    fin, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+                    for f in fin:
+                        done += f.result()
+                        n_units += 1
+        return done / (time.perf_counter() - t0), n_units
+
+    v1, n1 = leg(1)
+    log(f"[bench] cpu oracle, 1 thread: {v1:.1f} positions/s over {n1} {what}")
+    vn, nn = leg(threads)
+    log(f"[bench] cpu oracle, {threads} threads: {vn:.1f} positions/s over {nn} {what}")
+    unit = "sampled draft tokens/s" if args.draft_sample else "verified draft positions/s"
+    return {"value": vn, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{nn} {what} of {cfg.name} ({len(units)} distinct, host copies made before timing) in "
+                      f"about {args.cpu_seconds:.0f} s wall on {threads} threads; fp64 C oracle, gcc -O2, one call "
+                      f"per {what[:-1]}",
+            "single_thread_value": v1, "single_thread_sample": f"{n1} {what} in about {args.cpu_seconds:.0f} s",
+            "host_cpu": model, "host_cores_available": avail}
 
 
 def main():
@@ -368,6 +517,34 @@ def main():
         f"{bytes_total / steps / (ms_per_step / 1e3) / 1e9:.0f} GB/s per call; k_stream {stream_ms * 1e3:.2f} us "
         f"({achieved:.0f} GB/s), decision kernel {tail_ms * 1e3:.2f} us, flags={flags}")
 
+    # ---------------- the plain-read ceiling at the call's byte count -------------
+    # The library's read-only kernel (the streaming kernel's loads, no
+    # arithmetic) over the same batches, in the same order, with events on
+    # its own dispatches: the time these bytes take to stream with nothing
+    # else to do.
+    rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    sink = torch.empty(64, dtype=torch.int32, device=dev)
+    read_bytes = []
+    with torch.cuda.stream(run_stream):
+        for pair in rev:
+            for e_ in pair:
+                e_.record(run_stream)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SLEEP_CYCLES)
+        for s_ in range(steps):
+            bt = batches[(W + s_) % nb]
+            if args.draft_sample:
+                a_, b_ = bt["draft"][:R_draw], None
+            else:
+                a_, b_ = bt["target"], bt["draft"]
+            read_bytes.append(sum(0 if t is None else t.numel() * t.element_size() for t in (a_, b_)))
+            smcsd.read_ceiling(a_, b_, sink=sink, start=rev[s_][0], stop=rev[s_][1], stream=run_stream.cuda_stream)
+    torch.cuda.synchronize()
+    read_ms = float(np.mean([rev[i][0].elapsed_time(rev[i][1]) for i in range(steps)]))
+    read_gbs = float(np.mean(read_bytes)) / (read_ms / 1e3) / 1e9
+    log(f"[bench] plain read of the same {np.mean(read_bytes) / 1e6:.1f} MB: {read_ms * 1e3:.2f} us "
+        f"({read_gbs:.0f} GB/s)")
+
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -379,79 +556,12 @@ def main():
     # ---------------- CPU oracle on a bounded sample --------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from gpu_util import host_logits
-
-        done_pos, t_cpu, n_steps = 0, 0.0, 0
-        for i in range(nb):
-            bt = batches[i]
-            if args.draft_sample:
-                u = (bt["bonus_u"] if cfg.kind == "smc" else bt["uniforms"])[:R_draw].cpu().numpy()
-                for r0 in range(0, R_draw, 8):  # a few rows at a time: the sample stays bounded
-                    z = host_logits(bt["draft"][r0:min(r0 + 8, R_draw)])
-                    t0 = time.perf_counter()
-                    oracle.draft_sample(z, u[r0:r0 + len(z)], cfg.T)
-                    t_cpu += time.perf_counter() - t0
-                    done_pos += len(z)
-                    if t_cpu > args.cpu_seconds:
-                        break
-                sample = f"{done_pos} draft rows of {cfg.name}"
-            elif cfg.kind == "tree":
-                tg, dr = host_logits(bt["target"]), host_logits(bt["draft"])
-                host = {k: bt[k].cpu().numpy() for k in ("node_off", "draft_off", "parent", "tokens", "uniforms")}
-                t0 = time.perf_counter()
-                oracle.tree_verify(tg, dr, host["node_off"], host["draft_off"], host["parent"], host["tokens"],
-                                   host["uniforms"], cfg.T)
-                t_cpu += time.perf_counter() - t0
-                done_pos += positions[i]
-                n_steps += 1
-                sample = f"{n_steps} steps of {cfg.name}"
-            elif cfg.kind == "smc":
-                # one prompt at a time: the oracle's unit of work
-                P, N, K = cfg.P, cfg.N, cfg.K
-                for p in range(P):
-                    rt = slice(p * N * (K + 1), (p + 1) * N * (K + 1))
-                    rd = slice(p * N * K, (p + 1) * N * K)
-                    tg, dr = host_logits(bt["target"][rt]), host_logits(bt["draft"][rd])
-                    tk = bt["tokens"][rd].cpu().numpy()
-                    ub = bt["bonus_u"][p * N:(p + 1) * N].cpu().numpy()
-                    ur = bt["resample_u"][p:p + 1].cpu().numpy()
-                    t0 = time.perf_counter()
-                    oracle.smc_step(tg, dr, tk, ub, ur, np.zeros(N, np.float32), cfg.T, cfg.ess_frac, 1, N, K,
-                                    beta=args.beta)
-                    t_cpu += time.perf_counter() - t0
-                    done_pos += N * K
-                    if t_cpu > args.cpu_seconds:
-                        break
-                sample = f"{done_pos // (cfg.N * cfg.K)} prompts of {cfg.name}"
-            else:
-                tg, dr = host_logits(bt["target"]), host_logits(bt["draft"])
-                tk, u = bt["tokens"].cpu().numpy(), bt["uniforms"].cpu().numpy()
-                off = None
-                if bt["offsets"] is not None:
-                    # the oracle's own lengths for this step's scores (they equal the
-                    # library's, which laid out the batch)
-                    pc = cfg.pacer
-                    _, off = oracle.pacer_lengths(synth.pacer_scores(cfg.B, cfg.seed, i, pc["block"], pc["max_blocks"]),
-                                                  pc["block"], pc["max_blocks"], pc["t0"], pc["rho"])
-                    if not np.array_equal(off, bt["offsets"].cpu().numpy()):
-                        sys.exit("PACER lengths of the library and the oracle differ")
-                t0 = time.perf_counter()
-                oracle.sd_verify(tg, dr, tk, u, cfg.T, K=cfg.K, offsets=off)
-                t_cpu += time.perf_counter() - t0
-                done_pos += positions[i]
-                n_steps += 1
-                sample = f"{n_steps} steps of {cfg.name}"
-            if t_cpu > args.cpu_seconds:
-                break
-        unit = "sampled draft tokens/s" if args.draft_sample else "verified draft positions/s"
-        cpu = {"value": done_pos / t_cpu, "unit": unit, "cores": 1, "kind": "oracle",
-               "sample": sample + f" ({t_cpu:.1f} s, single-threaded fp64 C oracle, gcc -O2)"}
-        log(f"[bench] cpu oracle: {cpu['value']:.1f} positions/s over {sample}")
+        cpu = cpu_baseline(args, cfg, batches, nb, positions, R_draw)
 
     e = 4 if cfg.dtype == "f32" else 2
+    t_stream, t_tail = (traffic_from_profiles(cfg.name) if args.beta is None and not args.draft_sample
+                        else (None, None))
+    call_gbs = bytes_total / steps / (ms_per_step / 1e3) / 1e9
     line = {
         "metric": ("sampled draft tokens/sec and achieved HBM GB/s (% of MI355X peak)" if args.draft_sample else
                    "verified draft positions/sec and achieved HBM GB/s (% of MI355X peak)"),
@@ -477,11 +587,14 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "logit streaming (k_stream, or k_stream_wide for one-tile segments)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (traffic_from_profiles(cfg.name) if args.beta is None and not args.draft_sample
-                                 else None),
+                     "traffic": t_stream,
                      "algorithmic_bytes_per_launch": bytes_total / steps, "bytes_per_element": e,
-                     "kernel_us": stream_ms * 1e3, "decision_kernel_us": tail_ms * 1e3,
-                     "call_us": ms_per_step * 1e3},
+                     "kernel_us": stream_ms * 1e3,
+                     "read_ceiling": read_gbs, "read_ceiling_frac": read_gbs / HBM_PEAK_GBS,
+                     "frac_of_read_ceiling": achieved / read_gbs,
+                     "decision_kernel_us": tail_ms * 1e3, "decision_kernel_traffic": t_tail,
+                     "call_us": ms_per_step * 1e3, "call_achieved": call_gbs, "call_frac": call_gbs / HBM_PEAK_GBS,
+                     "call_traffic": (t_stream + t_tail) if t_stream is not None and t_tail is not None else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -49,25 +49,23 @@
  * Memory and ordering:
  *   Every pointer is HIP device memory owned by the caller (for example the
  *   storage of a torch tensor) unless stated otherwise.  The library never
- *   allocates, frees or synchronises; each call enqueues two kernels on
+ *   allocates, frees or synchronises; each call enqueues its kernels on
  *   `stream` (a hipStream_t; NULL is the default stream) and returns: one that
  *   streams every logit once and one that turns the row statistics into
- *   decisions.
- *   Outputs are valid once the stream reaches that point.
- *   Inside the second kernel each sequence's (prompt's) last step is done by
- *   whichever workgroup finishes its share last, counted in the workspace; no
- *   workgroup ever waits for another, so a call completes however much of the
- *   device it gets.  Calls on one
- *   workspace must not overlap (on one stream they never do).
+ *   decisions (for smc_reweight_resample a third, one workgroup per prompt,
+ *   for the effective sample size, the resampling and the page tables).
+ *   Outputs are valid once the stream reaches that point.  No workgroup ever
+ *   waits for another, so a call completes however much of the device it
+ *   gets; what one kernel reads from other workgroups the kernel before it
+ *   wrote.  Calls on one workspace must not overlap (on one stream they never
+ *   do).
  *
  * Workspace:
  *   Caller-owned device scratch of at least the size the *_workspace_bytes()
- *   query returns, aligned to SMCSD_WORKSPACE_ALIGN.  Its first
- *   SMCSD_WORKSPACE_COUNTER_BYTES hold counters only; they must be zero before
- *   the first call and every call leaves them at zero, so one workspace serves
- *   any sequence of calls (of any shapes it is large enough for).  After a
- *   call that raised SMCSD_FLAG_BAD_INPUT because of malformed CSR offsets,
- *   zero the counter bytes again before reuse.
+ *   query returns, aligned to SMCSD_WORKSPACE_ALIGN.  A call writes every
+ *   workspace byte it reads, so a workspace needs no initial contents and one
+ *   workspace serves any sequence of calls of the shapes it is large enough
+ *   for (the paged-KV calls' workspace is the exception: see there).
  *
  * Logits are row-major and contiguous: row r starts at element r * V.  bf16
  * logits are raw 16-bit bfloat16 patterns.
@@ -119,15 +117,11 @@ enum {
                                    needs; nothing changed                             */
 };
 
-#define SMCSD_ABI_VERSION 1
+#define SMCSD_ABI_VERSION 2
 #define SMCSD_MAX_K 128    /* largest draft length per sequence / particle      */
 #define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
 #define SMCSD_MAX_V 524288 /* largest vocabulary                                 */
 #define SMCSD_WORKSPACE_ALIGN 256
-/* The first bytes of every workspace hold counters only (shape independent),
-   one 64-byte line per SMC prompt, so smc_reweight_resample needs P <= 65536
-   (sd_verify keeps the same header and does not use it). */
-#define SMCSD_WORKSPACE_COUNTER_BYTES (4u << 20)
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
 int32_t smcsd_abi_version(void);
@@ -205,8 +199,8 @@ size_t sd_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t K, int32_t V,
  *                    its first n_b draft tokens followed by this token.
  *   status_flags     NULL or device uint32 [1]; SMCSD_FLAG_* bits are OR-ed in.
  *   workspace        device memory of at least sd_verify_workspace_bytes(),
- *                    aligned to SMCSD_WORKSPACE_ALIGN, zero-filled before its
- *                    first use (see Workspace above).
+ *                    aligned to SMCSD_WORKSPACE_ALIGN (any contents; see
+ *                    Workspace above).
  *   stream           hipStream_t.
  */
 int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperature,
@@ -384,9 +378,8 @@ int32_t smc_pages_resample(int32_t P, int32_t N, int32_t L, int32_t page_size, i
  *             (SMCSD_FLAG_CDF_CLAMP).  This is the convention of every draw
  *             in this library: the call is sd_verify's final draw with no
  *             draft tokens, on the same kernels.
- * Workspace: draft_sample_workspace_bytes(dtype, R, V) bytes, aligned and
- * zero-filled before the first use as for sd_verify (the same workspace may
- * serve both).  Errors and flags as for sd_verify (SMCSD_FLAG_NONFINITE for a
+ * Workspace: draft_sample_workspace_bytes(dtype, R, V) bytes, aligned as for
+ * sd_verify (the same workspace may serve both).  Errors and flags as for sd_verify (SMCSD_FLAG_NONFINITE for a
  * row that is not a distribution; its token is then unspecified).
  */
 size_t draft_sample_workspace_bytes(int32_t dtype, int32_t R, int32_t V);

@@ -160,7 +160,7 @@ def _on_stream(stream, device):
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
-    if workspace is None:  # zero-filled once: the kernels keep their counters at zero between calls
+    if workspace is None:  # zero-filled: the paged-KV calls need zeros on first use (the others any contents)
         workspace = torch.zeros(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
     off = (-workspace.data_ptr()) % WORKSPACE_ALIGN
     view = workspace[off:]
@@ -179,8 +179,9 @@ def new_workspace(nbytes, device):
     """A zero-filled workspace of at least ``nbytes`` (plus alignment slack).
 
     Reuse it across calls of the same or smaller size; calls on one workspace
-    must not overlap.  Zero it again after a call that raised FLAG_BAD_INPUT
-    for malformed CSR offsets."""
+    must not overlap.  The verify, SMC, draft and tree calls write every
+    workspace byte they read; the paged-KV calls need zeros on first use and
+    leave them."""
     return torch.zeros(nbytes + WORKSPACE_ALIGN, dtype=torch.uint8, device=device)
 
 

@@ -25,17 +25,11 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
   return V % per == 0 && aligned16(a) && (b == nullptr || aligned16(b));
 }
 
-// Workspace layouts.  The first SMCSD_WORKSPACE_COUNTER_BYTES of every
-// workspace hold only counters, whatever the shape of the call, so one
-// workspace can serve calls of different shapes: the counters are zero before
-// the first call and every call leaves them at zero.  Scratch data follows:
-// the segment partials (sized for one-tile segments, the most a call can
-// use), the tile partials of each group's bonus row and, for SMC, the
-// reweighted log-weights.
-constexpr size_t kCounterBytes = SMCSD_WORKSPACE_COUNTER_BYTES;
-
-// One counter line per SMC prompt.
-bool smc_counters_fit(int64_t P) { return P <= smcsd::CTR_LINES; }
+// Workspace layouts: scratch that each call writes before it reads it, so a
+// workspace needs no initial contents and serves calls of any shapes it is
+// large enough for.  The segment partials (sized for one-tile segments, the
+// most a call can use), the tile partials of each group's bonus row and, for
+// SMC, the reweighted log-weights.
 
 struct SdLayout {
   size_t part, tpart, total;
@@ -44,7 +38,7 @@ struct SdLayout {
 SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
   const int nt = ntiles_of(V);
   SdLayout l;
-  l.part = kCounterBytes;
+  l.part = 0;
   l.tpart = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
   l.total = align_up(l.tpart + sizeof(float2) * (size_t)((int64_t)B * nt));
   return l;
@@ -55,7 +49,7 @@ SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
 SdLayout tree_layout(int64_t rows, int64_t V) {
   const int nt = ntiles_of(V);
   SdLayout l;
-  l.part = kCounterBytes;
+  l.part = 0;
   l.tpart = align_up(l.part + sizeof(float2) * (size_t)(rows * nt));
   l.total = align_up(l.tpart + sizeof(float2) * (size_t)(rows * nt));
   return l;
@@ -69,7 +63,7 @@ SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   const int nt = ntiles_of(V);
   const int64_t PN = (int64_t)P * N;
   SmcLayout l;
-  l.ws_logw = kCounterBytes;
+  l.ws_logw = 0;
   l.part = align_up(l.ws_logw + sizeof(float) * (size_t)PN);
   // the segment partials of every row, then (power target) those of each
   // particle's bonus row at the plain scale: 2K+2 rows per particle
@@ -112,7 +106,6 @@ void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, 
   s->part = reinterpret_cast<float2*>(ws + part_off);
   s->part1 = nullptr;
   s->tpart = reinterpret_cast<float2*>(ws + tpart_off);
-  s->ctr = reinterpret_cast<uint32_t*>(ws);
   s->flags = flags;
   s->flat = 0;
 }
@@ -293,7 +286,7 @@ static int32_t smc_step(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t 
   // the bonus row's scale beta * log2(e) / T must be a positive finite number
   const double cb = (double)beta * 1.4426950408889634 / (double)temperature;
   if (!isfinite(beta) || !(beta > 0.0f) || !isfinite((float)cb) || !((float)cb > 0.0f)) return SMCSD_ERR_INVALID_ARG;
-  if (K > SMCSD_MAX_K || N > SMCSD_MAX_N || V > SMCSD_MAX_V || !smc_counters_fit(P))
+  if (K > SMCSD_MAX_K || N > SMCSD_MAX_N || V > SMCSD_MAX_V)
     return SMCSD_ERR_UNSUPPORTED;
   if (P == 0) return SMCSD_OK;
   const int64_t PN = (int64_t)P * N;

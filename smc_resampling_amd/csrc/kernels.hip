@@ -1,8 +1,9 @@
 // kernels.hip -- HIP kernels (gfx950) of the verify-and-sample step.
 //
-// Each library call launches two kernels on the caller's stream.
+// sd_verify, draft_sample and tree_verify launch two kernels on the caller's
+// stream, smc_reweight_resample three.
 //
-// k_stream (both operations) reads every logit once.  The logit rows are
+// k_stream (every operation) reads every logit once.  The logit rows are
 // taken group by group (a group is an SD sequence or an SMC particle: its
 // target rows 0..K_b, then its draft rows 0..K_b-1), each row cut into
 // segments of `seg` consecutive 2048-logit tiles; a unit is one (row,
@@ -14,27 +15,26 @@
 // kernel holds nothing else, so it runs at high occupancy.
 //
 // k_sd_tail (sd_verify; "Faster LLM Inference via Sequential Monte Carlo",
-// sec. 1; variable lengths as in "PACER", Methodik): workgroup (x, b) of
-// sequence b merges b's partials into row statistics and tests
-// u_j < p_j(x_j) / q_j(x_j) up to the first rejection n; every workgroup of b
-// reaches the same decision.  n = K_b: workgroup 0 draws the bonus token from
-// p_{K_b} by inverse CDF (segment, tile, token).  n < K_b: each wavefront
-// stores the mass of max(0, p_n - q_n) over one tile; the last workgroup of b
-// to finish locates the tile that holds u * (total mass) and draws inside it.
+// sec. 1; variable lengths as in "PACER", Methodik): one workgroup per
+// sequence merges its partials into row statistics, tests
+// u_j < p_j(x_j) / q_j(x_j) up to the first rejection n and draws the final
+// token by inverse CDF: from p_{K_b} when n = K_b (tile located from the bonus
+// row's partials, then searched), else from max(0, p_n - q_n) (every tile's
+// mass, then the located tile searched).
 //
-// k_smc_tail (smc_reweight_resample; same page, sec. 2 steps 3-4, sec. 3): one
+// k_smc_tail (smc_reweight_resample; same page, sec. 2 steps 3-4): one
 // workgroup per particle computes the log-weight increment
-// sum_j log p_j(x_j) - log q_j(x_j) and draws the (K+1)-th token from p_K; the
-// last particle of a prompt to finish computes the Kish ESS, resamples
-// systematically when it is below the threshold and gathers the page-table
-// rows by ancestor.
+// sum_j log p_j(x_j) - log q_j(x_j) (and, for a power target, the bonus
+// token's weight) and draws the (K+1)-th token.  k_smc_prompt, one workgroup
+// per prompt, then computes the Kish ESS, resamples systematically when it is
+// below the threshold and gathers the page-table rows by ancestor (sec. 3).
 //
-// Nothing waits on another workgroup: hand-offs inside a tail kernel are
-// counters that the last arrival observes.  Each arrival is a device-scope
-// release that follows the values it hands over (log-weights), and the last
-// arrival's workgroup acquires before reading them; the values themselves are
-// written and read at the device coherence point (agent-scope atomics).  Every
-// counter is back at zero when the kernel ends.
+// k_tree_tail (tree_verify): one workgroup per token tree walks it from the
+// root.  k_draw_tail (draft_sample): one workgroup per row draws its token.
+//
+// No workgroup waits for, or hands data to, another: what a kernel needs from
+// other workgroups was written by an earlier kernel, and the kernel boundary
+// orders it.
 #include <hip/hip_ext.h>
 
 #include <map>
@@ -49,32 +49,11 @@ constexpr int MAXR = 2 * SMCSD_MAX_K + 1;  // rows per group
 constexpr int MAX_TILES = 256;             // tiles per row (V <= 524288)
 
 // ---------------------------------------------------------------------------
-// device-coherent loads and stores, counters
+// status flags
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void raise_flags(uint32_t* flags, uint32_t bits) {
   if (flags && bits) atomicOr(flags, bits);
 }
-__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-// Arrival at a counter: a release at device scope, so every store this thread
-// made before it (the values it hands over) is visible to a thread that
-// acquires after reading the count.
-__device__ __forceinline__ uint32_t ctr_arrive(uint32_t* p) {
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-// The acquire that pairs with every earlier arrival, for the whole workgroup
-// of the last arrival.
-__device__ __forceinline__ void acquire_arrivals() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
 // ---------------------------------------------------------------------------
 // groups
 // ---------------------------------------------------------------------------
@@ -290,14 +269,17 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   // time: a store is a memory operation the loads' wait counter also counts.
   int csg = (int)(u0 % nseg);
   int ct = csg * seg, cte = min(ntiles, ct + seg);
-  // the scale of the row being reduced: c, or cb for a group's bonus row with
-  // a power target (the row within its group is the row index modulo 2K+1)
+  // the scale of the row being reduced: c, or cb for a group's bonus row when
+  // the call gives that row its own (SMC with a power target, whose groups are
+  // all 2K+1 rows: the row within its group is the row index modulo 2K+1)
+  const bool split = PW || a.cb != c;
   const int grows = 2 * a.K + 1;
-  int crr = PW ? (int)((u0 / nseg) % grows) : 0;
-  int64_t cgrp = PW ? (u0 / nseg) / grows : 0;  // group of the row being reduced
-  float cc = PW && crr == a.K ? a.cb : c;
+  int crr = split ? (int)((u0 / nseg) % grows) : 0;
+  float cc = split && crr == a.K ? a.cb : c;
   float m = -INFINITY, s = 0.0f;
-  float m1 = -INFINITY, s1 = 0.0f;  // PW: the bonus row's unit at scale c
+  // PW: the group of the row being reduced, and the bonus row's unit at scale c
+  int64_t cgrp = PW ? (u0 / nseg) / grows : 0;
+  float m1 = -INFINITY, s1 = 0.0f;
   float2 pb = make_float2(0.0f, 0.0f);
   int64_t pbase = u0;
   int pn = 0;
@@ -310,8 +292,9 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
       s = 0.0f;
     }
     lane_fold_tile<DT>(x, cc, m, s);
-    const bool bon1 = PW && crr == a.K;
-    if (bon1) lane_fold_tile<DT>(x, c, m1, s1);
+    if constexpr (PW) {
+      if (crr == a.K) lane_fold_tile<DT>(x, c, m1, s1);
+    }
     if (TP && dst >= 0) {
       const float2 tp = wave_partial(m, s);
       if (lane == 0) a.tpart[dst] = tp;
@@ -327,18 +310,20 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
       }
       m = -INFINITY;
       s = 0.0f;
-      if (bon1) {
-        const float2 p1 = wave_partial(m1, s1);
-        if (lane == 0) a.part1[cgrp * nseg + csg] = p1;
-        m1 = -INFINITY;
-        s1 = 0.0f;
+      if constexpr (PW) {
+        if (crr == a.K) {
+          const float2 p1 = wave_partial(m1, s1);
+          if (lane == 0) a.part1[cgrp * nseg + csg] = p1;
+          m1 = -INFINITY;
+          s1 = 0.0f;
+        }
       }
       if (++csg == nseg) {
         csg = 0;
-        if (PW) {
+        if (split) {
           if (++crr == grows) {
             crr = 0;
-            cgrp++;
+            if constexpr (PW) cgrp++;
           }
           cc = crr == a.K ? a.cb : c;
         }
@@ -435,10 +420,6 @@ struct PromptLds {
   float lw[SMCSD_MAX_N];
   int hi[SMCSD_MAX_N];   // particle i supplies the slots [hi[i-1], hi[i])
   int anc[SMCSD_MAX_N];
-};
-union SharedLds {
-  TailLds t;
-  PromptLds p;
 };
 
 __device__ __forceinline__ RowStat stat_of(const TailLds& L, int r) {
@@ -1381,7 +1362,7 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
   const int64_t base = p * N;
   uint32_t fl = 0;
   const float ru = a.resample_u[p];  // issued early: nothing below waits on it until the slot ranges
-  for (int k = threadIdx.x; k < N; k += BLOCK) Q.lw[k] = ld_dev(a.ws_logw + base + k);
+  for (int k = threadIdx.x; k < N; k += BLOCK) Q.lw[k] = a.ws_logw[base + k];
   __syncthreads();
   if (wave == 0) {
     float mf = -INFINITY;
@@ -1470,7 +1451,6 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
     else
       gather_rows(src, dst, N, L, Q.anc);
   }
-  if (threadIdx.x == 0) st_dev(s.ctr + p * CTR_STRIDE, 0u);  // every particle of p has counted
 }
 
 // With vector loads, at most 64 VGPRs (8 wavefronts per SIMD), so that 8
@@ -1479,9 +1459,7 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
 template <typename DT, bool VL>
 __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   using raw = typename DT::raw;
-  __shared__ SharedLds sh;
-  __shared__ int s_last;
-  TailLds& L = sh.t;
+  __shared__ TailLds L;
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   const int64_t i = blockIdx.x;
@@ -1504,8 +1482,7 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   uint32_t fl = 0;
   float lw = 0.0f;
   // wavefront 1 forms the new log-weight while wavefront 0 locates the bonus
-  // draw's tile, and publishes it while wavefront 0 reloads and searches that
-  // tile: the prompt's resampling needs the log-weights, not the bonus tokens
+  // draw's tile, and stores it while wavefront 0 reloads and searches that tile
   if (wave == 1) {
     double delta = 0.0;
     for (int j0 = 0; j0 < K; j0 += WAVE) {
@@ -1535,30 +1512,25 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   }
   const RowStat sk = stat_of(L, K);
   if (!sk.ok) fl |= FLAG_NONFINITE;
-  const int64_t p = i / a.N;
-  uint32_t before = 0;
-  // the log-weight, then the count that announces it (a release)
-  auto publish = [&]() {
-    if (wave == 1 && lane == 0) {
-      st_dev(a.ws_logw + i, lw);
-      before = ctr_arrive(s.ctr + p * CTR_STRIDE);
-    }
+  auto store_lw = [&]() {
+    if (wave == 1 && lane == 0) a.ws_logw[i] = lw;
   };
   // the bonus row's statistics and draw are at its own scale (beta / T)
   const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, s.cb, sk.M, (double)ub, bnp, bper, L, fl,
-                                     publish);
+                                     store_lw);
   or_flags(fl, L);
-  if (wave == 1 && lane == 0) s_last = before + 1u == (uint32_t)a.N;
   __syncthreads();
   if (threadIdx.x == 0) {
     a.bonus_token[i] = y;
     raise_flags(s.flags, L.fl);
   }
-  if (s_last) {
-    lds_barrier();  // thread 0 has read L.fl: the prompt's LDS overlays it
-    acquire_arrivals();  // every particle's log-weight, released with its count
-    smc_prompt_tail(a, p, sh.p);
-  }
+}
+
+// One workgroup per prompt, after every particle's log-weight is stored (the
+// kernel boundary orders them): ESS, systematic resampling, page-table gather.
+__global__ __launch_bounds__(BLOCK) void k_smc_prompt(SmcArgs a) {
+  __shared__ PromptLds Q;
+  smc_prompt_tail(a, blockIdx.x, Q);
 }
 
 // ---------------------------------------------------------------------------
@@ -1685,7 +1657,9 @@ hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipS
   if (e != hipSuccess) return e;
   const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())
                        : (vec ? smc_tail_kernel<F32, true>() : smc_tail_kernel<F32, false>());
-  return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
+  e = launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, nullptr);
+  if (e != hipSuccess) return e;
+  return launch(kptr(&k_smc_prompt), (unsigned)(a.s.ngroups / a.N), BLOCK, a, s, nullptr, t.tail_stop);
 }
 
 template <typename DT, bool VL>

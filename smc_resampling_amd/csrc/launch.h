@@ -9,11 +9,6 @@
 
 namespace smcsd {
 
-// Counter lines of the workspace header, 64 bytes apart: one per SMC prompt
-// (particles finished).
-constexpr int CTR_STRIDE = 16;  // uint32 per 64-byte line
-constexpr int64_t CTR_LINES = SMCSD_WORKSPACE_COUNTER_BYTES / 64;
-
 // What both operations stream.  Rows are taken group by group (a group is an
 // SD sequence or an SMC particle: its target rows 0..K_b, then its draft rows
 // 0..K_b-1); each row is cut into nseg segments of `seg` tiles; a unit is one
@@ -33,11 +28,10 @@ struct StepArgs {
   float c;        // log2(e) / T
   float cb;       // scale of each group's bonus row: c, or beta * log2(e) / T for a power target
   float2* part;   // [units] segment partials (max of z c, sum of 2^(z c - max))
-  float2* part1;  // power target: [ngroups * nseg] segment partials of each group's bonus row at scale c
   float2* tpart;  // [ngroups * ntiles] tile partials of each group's bonus row
-  uint32_t* ctr;  // counter lines (zero between calls)
   uint32_t* flags;
   int flat;       // 1: every row is a group of its own, the target rows then the draft rows (K = 0)
+  float2* part1;  // power target: [ngroups * nseg] segment partials of each group's bonus row at scale c
 };
 
 struct SdArgs {

@@ -17,7 +17,7 @@
 //                    a run of consecutive particles in registers through the
 //                    phases, so the kernel makes a handful of dependent trips
 //                    to memory, not a handful per particle.
-// smc_pages_resample three launches.  The new rows are the ancestors' old
+// smc_pages_resample four launches.  The new rows are the ancestors' old
 //                    rows, so a page's count changes by the sum of (copies - 1)
 //                    over the old rows that name it: one wavefront takes 64
 //                    rows at a time, one position at a time, and adds that sum
@@ -26,8 +26,10 @@
 //                    so shared prefixes cost one atomic or none).  A run whose
 //                    rows all die marks its first entry; the marked entries
 //                    whose page reached zero are staged per row in entry
-//                    order, the last workgroup to finish lays the rows out on
-//                    the stack by a scan, and a third launch pushes them.
+//                    order, one workgroup lays the rows out on the stack by a
+//                    scan, and a fourth launch pushes them (each launch reads
+//                    what the one before wrote: the kernel boundaries order
+//                    it, and no workgroup hands data to another).
 //                    Calls of at most 16 rows of at most 256 entries run in
 //                    one workgroup instead: each wavefront keeps the entries
 //                    it marks in registers and, after a barrier, pushes the
@@ -81,7 +83,6 @@ struct ResampleArgs {
   int32_t* offsets;  // [R] exclusive scan of counts
   int32_t* staged;   // [R * L] freed pages of each row, in entry order
   int32_t* base;     // [1] the stack height before the push
-  uint32_t* arrived; // [1] workgroups of the staging launch done (0 between calls)
 };
 
 __device__ __forceinline__ int64_t used_pages(int64_t len, int S) { return (len + S - 1) / S; }
@@ -641,24 +642,17 @@ __device__ void push_row(const ResampleArgs& a, int64_t k) {
     if (base + i < a.M) a.free_pages[base + i] = ld_agent(&a.staged[k * a.L + i]);
 }
 
-// One wavefront per row stages; the last workgroup to finish lays the rows'
-// pages out on the stack.
+// One wavefront per row stages its freed pages and stores its count.
 __global__ __launch_bounds__(BLOCK) void k_pages_stage(ResampleArgs a) {
-  __shared__ int64_t lds[WAVES_PER_BLOCK + 1];
-  __shared__ bool s_last;
   const int64_t k = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wave_id();
   if (k < a.R) stage_row(a, k);
-  mem_done();
-  __syncthreads();
-  // the workgroup's stores are complete; the arrival releases them at device
-  // scope, and the last workgroup to arrive acquires every earlier arrival's
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(a.arrived, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// One workgroup, after every row's count is stored (the kernel boundary
+// orders them): the rows' stack positions.
+__global__ __launch_bounds__(BLOCK) void k_pages_scan(ResampleArgs a) {
+  __shared__ int64_t lds[WAVES_PER_BLOCK + 1];
   scan_offsets<BLOCK>(a, lds);
-  if (threadIdx.x == 0) __hip_atomic_store(a.arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One wavefront per row: push the staged pages.
@@ -877,7 +871,6 @@ int32_t smc_pages_resample(int32_t P, int32_t N, int32_t L, int32_t page_size, i
   a.offsets = reinterpret_cast<int32_t*>(ws + l.offsets);
   a.staged = reinterpret_cast<int32_t*>(ws + l.staged);
   a.base = reinterpret_cast<int32_t*>(ws + l.base);
-  a.arrived = reinterpret_cast<uint32_t*>(ws + l.base + 4);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (R <= PG_SMALL_ROWS && L <= PG_SMALL_L) {
     hipLaunchKernelGGL(k_pages_resample_small, dim3(1), dim3(PG_BLOCK), 0, s, a);
@@ -888,6 +881,8 @@ int32_t smc_pages_resample(int32_t P, int32_t N, int32_t L, int32_t page_size, i
   if (hipGetLastError() != hipSuccess) return SMCSD_ERR_HIP;
   const unsigned grid = (unsigned)((R + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK);
   hipLaunchKernelGGL(k_pages_stage, dim3(grid), dim3(BLOCK), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return SMCSD_ERR_HIP;
+  hipLaunchKernelGGL(k_pages_scan, dim3(1), dim3(BLOCK), 0, s, a);
   if (hipGetLastError() != hipSuccess) return SMCSD_ERR_HIP;
   hipLaunchKernelGGL(k_pages_push, dim3(grid), dim3(BLOCK), 0, s, a);
   return hipGetLastError() == hipSuccess ? SMCSD_OK : SMCSD_ERR_HIP;
