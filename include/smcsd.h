@@ -122,6 +122,8 @@ enum {
 #define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
 #define SMCSD_MAX_V 524288 /* largest vocabulary                                 */
 #define SMCSD_WORKSPACE_ALIGN 256
+/* Size of the static scratch of smc_reweight_resample_noalloc (one per GPU). */
+#define SMCSD_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
 int32_t smcsd_abi_version(void);
@@ -289,6 +291,31 @@ int32_t smc_reweight_resample_power(int32_t dtype, int32_t P, int32_t N, int32_t
                                     int32_t* ancestors, float* ess, int32_t* resampled,
                                     uint32_t* status_flags, void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * smc_reweight_resample for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, results and errors as smc_reweight_resample,
+ * without the workspace: the kernels use a static device array of
+ * SMCSD_NOALLOC_SCRATCH_BYTES (32 MiB) instead, one per GPU, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no library
+ * allocation); the caller still passes every input and output.
+ *   A call whose workspace would exceed the array (smc_workspace_bytes(dtype,
+ *   P, N, K, V) > SMCSD_NOALLOC_SCRATCH_BYTES) returns SMCSD_ERR_UNSUPPORTED
+ *   before anything is enqueued; the 32-prompt x 64-particle step at K = 8,
+ *   V = 151936 needs 23.5 MB.
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's
+ *   contents (nothing in it has to start at zero): calls that overlap on one
+ *   GPU (two streams, two threads) race.  Calls in order on one stream do not.
+ */
+int32_t smc_reweight_resample_noalloc(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t V,
+                                      float temperature, float ess_frac, const void* target_logits,
+                                      const void* draft_logits, const int32_t* draft_tokens,
+                                      const float* bonus_uniforms, const float* resample_uniforms,
+                                      float* log_weights, const int32_t* page_table_in,
+                                      int32_t* page_table_out, int32_t pages_per_particle,
+                                      int32_t* bonus_token, int32_t* ancestors, float* ess,
+                                      int32_t* resampled, uint32_t* status_flags, void* stream);
 
 /*
  * Paged-KV bookkeeping around SMC resampling: the metadata update that makes

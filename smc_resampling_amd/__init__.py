@@ -22,6 +22,7 @@ __all__ = [
     "new_workspace", "time_next_call", "smc_pages_workspace_bytes", "smc_pages_append", "smc_pages_resample",
     "draft_sample_workspace_bytes", "prepare_draft_sample", "draft_sample", "pacer_lengths",
     "tree_verify_workspace_bytes", "prepare_tree_verify", "tree_verify", "TREE_MAX_NODES", "read_ceiling",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,7 @@ FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_
 FLAG_PAGES_FULL, FLAG_PAGES_EXHAUSTED = 32, 64
 WORKSPACE_ALIGN = 256
 TREE_MAX_NODES = 256
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -48,6 +50,8 @@ _SIGNATURES = {
                                _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_reweight_resample_power": ([_I32, _I32, _I32, _I32, _I32, _F, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
                                      _P, _P, _P, _P, _P, _P, _SZ, _P], _I32),
+    "smc_reweight_resample_noalloc": ([_I32, _I32, _I32, _I32, _I32, _F, _F, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                                       _P, _P, _P, _P, _P], _I32),
     "draft_sample_workspace_bytes": ([_I32, _I32, _I32], _SZ),
     "draft_sample": ([_I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P], _I32),
     "pacer_lengths": ([_I32, _I32, _I32, ctypes.c_double, ctypes.c_double, _P, _P, _P, _P], _I32),
@@ -240,10 +244,14 @@ def sd_verify(target_logits, draft_logits, draft_tokens, uniforms, temperature, 
 def prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms,
                                   log_weights, temperature, ess_frac, P, N, K, *, page_table_in=None,
                                   page_table_out=None, bonus_token=None, ancestors=None, ess=None, resampled=None,
-                                  status_flags=None, workspace=None, stream=None, beta=None):
+                                  status_flags=None, workspace=None, stream=None, beta=None, noalloc=False):
     """Validate and marshal one SMC step; returns (call, outputs).  ``log_weights``
     is updated in place when the call runs.  With ``beta``, the power-sampling
-    target (``smc_reweight_resample_power``)."""
+    target (``smc_reweight_resample_power``).  With ``noalloc``, the entry point
+    that allocates nothing (``smc_reweight_resample_noalloc``: its scratch is a
+    static device array; no workspace is made or passed)."""
+    if noalloc and (beta is not None or workspace is not None):
+        raise ValueError("noalloc takes neither beta nor a workspace")
     dev = target_logits.device
     dt = _dtype_code(target_logits)
     V = target_logits.shape[-1]
@@ -267,14 +275,14 @@ def prepare_smc_reweight_resample(target_logits, draft_logits, draft_tokens, bon
         ess = ess if ess is not None else mk(P, torch.float32)
         resampled = resampled if resampled is not None else mk(P, torch.int32)
         status_flags = status_flags if status_flags is not None else torch.zeros(1, dtype=torch.int32, device=dev)
-        nbytes = smc_workspace_bytes(dt, P, N, K, V)
-        ws, wsb = _workspace(nbytes, dev, workspace)
+        ws, wsb = (None, 0) if noalloc else _workspace(smc_workspace_bytes(dt, P, N, K, V), dev, workspace)
     scal = (float(temperature), float(ess_frac)) if beta is None else (float(temperature), float(beta), float(ess_frac))
     args = (dt, P, N, K, V, *scal, _ptr(target_logits), _ptr(draft_logits),
             _ptr(draft_tokens), _ptr(bonus_uniforms), _ptr(resample_uniforms), _ptr(log_weights), _ptr(page_table_in),
             _ptr(page_table_out), L, _ptr(bonus_token), _ptr(ancestors), _ptr(ess), _ptr(resampled),
-            _ptr(status_flags), _ptr(ws), wsb, st)
-    fn = _lib.smc_reweight_resample if beta is None else _lib.smc_reweight_resample_power
+            _ptr(status_flags), *(() if noalloc else (_ptr(ws), wsb)), st)
+    fn = (_lib.smc_reweight_resample_noalloc if noalloc else
+          _lib.smc_reweight_resample if beta is None else _lib.smc_reweight_resample_power)
     keep = (target_logits, draft_logits, draft_tokens, bonus_uniforms, resample_uniforms, log_weights,
             page_table_in, ws)
 

@@ -143,3 +143,15 @@ def test_read_ceiling_rejects_bad_buffers(s):
     assert L.smcsd_read_ceiling(ctypes.c_void_p(1 << 40), 63, None, 0, sink, None, None, None) == 1  # odd size
     assert L.smcsd_read_ceiling(ctypes.c_void_p((1 << 40) + 8), 64, None, 0, sink, None, None, None) == 1  # align
     assert L.smcsd_read_ceiling(ctypes.c_void_p(1 << 40), 64, None, 0, None, None, None, None) == 1  # no sink
+
+
+def test_noalloc_validates_on_the_host(s):
+    """The allocation-free SMC entry point checks its arguments before it looks
+    up its scratch or plans a launch (so no device is touched here)."""
+    L = s.lib()
+    F = ctypes.c_void_p(1 << 40)
+    args = lambda **kw: [kw.get("dtype", 1), kw.get("P", 2), 4, 2, 1000, kw.get("T", 1.0), 0.5, F, F, F, F, F, F,  # noqa
+                         None, None, 0, F, F, F, F, None, None]
+    assert L.smc_reweight_resample_noalloc(*args(dtype=5)) == 1
+    assert L.smc_reweight_resample_noalloc(*args(T=0.0)) == 1
+    assert L.smc_reweight_resample_noalloc(*args(P=0)) == 0
