@@ -26,7 +26,9 @@ __all__ = [
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsmcsd.so")
+# SMCSD_LIBRARY names another build of the same library (a measurement build
+# with different compile options); by default the one built here
+LIB_PATH = os.environ.get("SMCSD_LIBRARY") or os.path.join(HERE, "libsmcsd.so")
 
 SMCSD_OK, SMCSD_ERR_INVALID_ARG, SMCSD_ERR_UNSUPPORTED, SMCSD_ERR_WORKSPACE, SMCSD_ERR_HIP = range(5)
 SMCSD_F32, SMCSD_BF16 = 0, 1

@@ -45,6 +45,11 @@
 
 namespace smcsd {
 
+// Measurement knob, 0 in the library's build: see the streaming kernel's loads.
+#ifndef SMCSD_TEMPORAL_ROWS
+#define SMCSD_TEMPORAL_ROWS 0
+#endif
+
 constexpr int MAXR = 2 * SMCSD_MAX_K + 1;  // rows per group
 constexpr int MAX_TILES = 256;             // tiles per row (V <= 524288)
 
@@ -243,7 +248,19 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   // Issues the loads of the next tile.  A row outside the buffers (malformed
   // offsets) is read as row 0 of the target, and its partials are not used.
   auto fetch = [&](int64_t& dst) {
+#if SMCSD_TEMPORAL_ROWS > 0
+    // build-time measurement knob: SD rows at the first draft positions
+    // (target and draft row j < SMCSD_TEMPORAL_ROWS) loaded with the temporal
+    // policy, so that a rejection's re-read might find them cached
+    const int64_t rr = lfr - gc.G.fr0;
+    const bool keep = !a.flat && a.cb == a.c &&
+                      ((rr < SMCSD_TEMPORAL_ROWS) || (rr > gc.G.kb && rr <= gc.G.kb + SMCSD_TEMPORAL_ROWS));
+    Raw<DT> x;
+    if (keep) x = load_raw<DT, VL, 0>(lrow ? lrow : static_cast<const raw*>(a.target), a.V, lt, lane);
+    else x = load_raw<DT, VL>(lrow ? lrow : static_cast<const raw*>(a.target), a.V, lt, lane);
+#else
     const Raw<DT> x = load_raw<DT, VL>(lrow ? lrow : static_cast<const raw*>(a.target), a.V, lt, lane);
+#endif
     dst = lbon < 0 ? -1 : lbon + lt;
     if (++lt == lte) {
       if (++lu < u1) {
