@@ -1597,14 +1597,17 @@ static const void* stream_kernel(bool bf16, bool vec, bool tp, bool wide, bool p
   return pw ? stream_kernel_p<true>(bf16, vec, tp) : stream_kernel_p<false>(bf16, vec, tp);
 }
 
-// Segments long enough that each resident wavefront streams about 32 units
-// (fewer wavefront reductions on large calls), at least SEG_MIN and at most 8
-// tiles.  From TP_MIN_SEG tiles on, the bonus rows also get tile partials, so
-// a draw re-reads one tile rather than its segment.  bf16 calls with 16-byte
-// loads whose segments are single tiles use k_stream_wide (not with a power
-// target).  The streaming grid is what the device holds at once of the chosen
-// kernel, fewer when there is not one unit per wavefront.
-constexpr int SEG_MIN = 1, TP_MIN_SEG = 2;
+// Segments long enough that each resident wavefront streams about 32 units;
+// on large calls, where that would give units of 8 tiles or more, about 16
+// (each unit ends in a wavefront reduction: on the 32 x 64-particle
+// V = 151936 call, 85 units of 8 tiles per wavefront streamed at 6.65 TB/s,
+// 17 units of 38 tiles at 6.73).  From TP_MIN_SEG tiles on, the bonus rows
+// also get tile partials, so a draw re-reads one tile rather than its segment.
+// bf16 calls with 16-byte loads whose segments are single tiles use
+// k_stream_wide (not with a power target).  The streaming grid is what the
+// device holds at once of the chosen kernel, fewer when there is not one unit
+// per wavefront.
+constexpr int SEG_MIN = 1, TP_MIN_SEG = 2, LONG_SEG = 8;
 
 hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, bool pw, Plan* p) {
   const int resident = resident_blocks(stream_kernel(bf16, vec, false, false, pw));
@@ -1612,7 +1615,8 @@ hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, bool pw, P
   const int64_t waves = (int64_t)resident * WAVES_PER_BLOCK;
   const int64_t tiles = rows * ntiles;
   int64_t seg = tiles / (32 * waves);
-  seg = seg < SEG_MIN ? SEG_MIN : (seg > 8 ? 8 : seg);
+  if (seg >= LONG_SEG) seg = tiles / (16 * waves);
+  seg = seg < SEG_MIN ? SEG_MIN : seg;
   if (seg > ntiles) seg = ntiles;
   const int nseg = (int)((ntiles + seg - 1) / seg);
   p->seg = (ntiles + nseg - 1) / nseg;
