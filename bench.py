@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+OTHER_WORKLOADS = (0, 1, 2, 4, 5)
 SLEEP_CYCLES = 100_000_000
 MALL_BYTES = 256 << 20
 
@@ -165,13 +166,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3,
-                    help="workload index (default: the largest, SMC 32 prompts x 64 particles, K=8, V=151936 bf16)")
+    ap.add_argument("--config", type=int, default=None,
+                    help="workload index; by default the largest (SMC 32 prompts x 64 particles, K=8, V=151936 "
+                         "bf16) is the line's headline and the others follow in other_workloads")
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on each leg (one thread, all threads) of the oracle's CPU sample")
     ap.add_argument("--cpu-threads", type=int, default=16, help="most host threads for the all-cores oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="without --config the run also measures the smaller workloads (0, 1, 2, 4 and the token "
+                         "trees) into other_workloads; this skips them")
     ap.add_argument("--max-batch-gb", type=float, default=24.0)
     ap.add_argument("--with-pages", action="store_true",
                     help="SMC workloads: each step also does the paged-KV bookkeeping (append K+1 tokens "
@@ -303,22 +308,16 @@ def cpu_baseline(args, cfg, batches, nb, positions, R_draw):
             "host_cpu": model, "host_cores_available": avail}
 
 
-def main():
-    args = parse()
-    if args.summarize:
-        print(summarize(args.summarize, args.copy_calibration or None))
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this library runs on one GPU: --gpus N > 1 is not supported"}))
-        sys.exit(2)
+def run_workload(args, config, steps_arg, with_cpu):
+    """Measure one workload (index into synth.CONFIGS) and return its JSON record."""
     import numpy as np
     import torch
 
     import smc_resampling_amd as smcsd
     import synth
 
-    cfg = synth.CONFIGS[args.config]
-    steps = args.steps if args.steps is not None else cfg.steps
+    cfg = synth.CONFIGS[config]
+    steps = steps_arg if steps_arg is not None else cfg.steps
     W = args.warmup
     if args.draft_sample and (args.with_pages or args.beta is not None):
         sys.exit("--draft-sample times the draft-side draw alone")
@@ -555,7 +554,7 @@ def main():
 
     # ---------------- CPU oracle on a bounded sample --------------------------
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         cpu = cpu_baseline(args, cfg, batches, nb, positions, R_draw)
 
     e = 4 if cfg.dtype == "f32" else 2
@@ -597,6 +596,37 @@ def main():
                      "call_traffic": (t_stream + t_tail) if t_stream is not None and t_tail is not None else None},
         "cpu_baseline": cpu,
     }
+    return line
+
+
+def main():
+    args = parse()
+    if args.summarize:
+        print(summarize(args.summarize, args.copy_calibration or None))
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU: --gpus N > 1 is not supported"}))
+        sys.exit(2)
+    import torch
+
+    default_run = args.config is None
+    line = run_workload(args, 3 if default_run else args.config, args.steps, not args.no_cpu_baseline)
+    if default_run and not args.no_others and not (args.draft_sample or args.with_pages or args.beta is not None):
+        # the smaller workloads, each with its own inputs (those of the one
+        # before freed first), at their default step counts, no CPU leg
+        others = []
+        for c in OTHER_WORKLOADS:
+            torch.cuda.empty_cache()
+            o = run_workload(args, c, None, False)
+            r = o["roofline"]
+            others.append({"workload": o["config"]["workload"], "value": o["value"], "unit": o["unit"],
+                           "ms_per_step": o["ms_per_step"], "steps": o["steps"], "kernel_us": r["kernel_us"],
+                           "frac": r["frac"], "read_ceiling": r["read_ceiling"],
+                           "frac_of_read_ceiling": r["frac_of_read_ceiling"],
+                           "decision_kernel_us": r["decision_kernel_us"], "call_frac": r["call_frac"],
+                           "traffic": r["traffic"], "call_traffic": r["call_traffic"],
+                           "status_flags": o["config"]["status_flags"]})
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
 
