@@ -28,6 +28,9 @@ FLAG_CDF_CLAMP = 8
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
+# value the wrappers fill output buffers with before a call
+UNWRITTEN = -7
+
 
 def build(src: str = SRC, out: str = LIB, strict: bool = True) -> str:
     """Compile the oracle with plain gcc (-O2, IEEE semantics, no fast-math)."""
@@ -134,11 +137,12 @@ def sd_verify(target, draft, tokens, uniforms, T, K=None, offsets=None, lib=None
     else:
         B = target.shape[0] // (K + 1)
     nd = tokens.shape[0]
-    na = np.zeros(B, np.int32)
-    ft = np.zeros(B, np.int32)
+    # outputs start at a sentinel (not 0), so an output left unwritten shows
+    na = np.full(B, UNWRITTEN, np.int32)
+    ft = np.full(B, UNWRITTEN, np.int32)
     fl = np.zeros(1, np.uint32)
-    am = np.full(max(nd, 1), -1.0)
-    sm = np.zeros(max(B, 1))
+    am = np.full(max(nd, 1), float(UNWRITTEN))
+    sm = np.full(max(B, 1), float(UNWRITTEN))
     lib.oracle_sd_verify(_dtype_code(target), B, K, V, T, _ptr(target), _ptr(draft), _ptr(tokens),
                          _ptr(uniforms), _ptr(offsets), _ptr(na), _ptr(ft), _ptr(fl), _ptr(am), _ptr(sm))
     return dict(num_accepted=na, final_token=ft, flags=int(fl[0]), accept_margin=am[:nd], sample_margin=sm[:B])
@@ -181,16 +185,16 @@ def smc_step(target, draft, tokens, bonus_u, resample_u, logw, T, ess_frac, P, N
     if pt_in is not None:
         pt_in = np.ascontiguousarray(pt_in, dtype=np.int32)
         L = pt_in.size // max(PN, 1)
-        pt_out = np.zeros_like(pt_in)
-    bonus = np.zeros(PN, np.int32)
-    anc = np.zeros(PN, np.int32)
-    ess = np.zeros(P, np.float32)
-    res = np.zeros(P, np.int32)
+        pt_out = np.full_like(pt_in, UNWRITTEN)
+    bonus = np.full(PN, UNWRITTEN, np.int32)
+    anc = np.full(PN, UNWRITTEN, np.int32)
+    ess = np.full(P, UNWRITTEN, np.float32)
+    res = np.full(P, UNWRITTEN, np.int32)
     fl = np.zeros(1, np.uint32)
-    cw = np.zeros(max(PN, 1))
-    bm = np.zeros(max(PN, 1))
-    em = np.zeros(max(P, 1))
-    rm = np.zeros(max(P, 1))
+    cw = np.full(max(PN, 1), float(UNWRITTEN))
+    bm = np.full(max(PN, 1), float(UNWRITTEN))
+    em = np.full(max(P, 1), float(UNWRITTEN))
+    rm = np.full(max(P, 1), float(UNWRITTEN))
     tail = (_ptr(target), _ptr(draft), _ptr(tokens), _ptr(bonus_u), _ptr(resample_u), _ptr(lw), _ptr(pt_in),
             _ptr(pt_out), L, _ptr(bonus), _ptr(anc), _ptr(ess), _ptr(res), _ptr(fl), _ptr(cw), _ptr(bm), _ptr(em),
             _ptr(rm))
@@ -213,8 +217,8 @@ def pages_append(table, lens, ref, free_pages, free_count, S, A, lib=None):
     ref = np.array(ref, np.int32, copy=True)
     free_pages = np.array(free_pages, np.int32, copy=True)
     fc = np.array([free_count], np.int32)
-    slots = np.zeros(max(R * A, 1), np.int32)
-    cow = np.zeros(max(3 * R, 3), np.int32)
+    slots = np.full(max(R * A, 1), UNWRITTEN, np.int32)
+    cow = np.full(max(3 * R, 3), UNWRITTEN, np.int32)
     nc = np.zeros(1, np.int32)
     st = lib.oracle_pages_append(R, L, S, A, ref.size, _ptr(table), _ptr(lens), _ptr(ref), _ptr(free_pages),
                                  _ptr(fc), _ptr(slots), _ptr(cow), _ptr(nc))
@@ -231,7 +235,7 @@ def pages_resample(P, N, ancestors, table_old, table_new, lens, ref, free_pages,
     L = table_old.shape[1]
     anc = np.ascontiguousarray(ancestors, np.int32)
     lens = np.ascontiguousarray(lens, np.int32)
-    len_out = np.zeros_like(lens)
+    len_out = np.full_like(lens, UNWRITTEN)
     ref = np.array(ref, np.int32, copy=True)
     free_pages = np.array(free_pages, np.int32, copy=True)
     fc = np.array([free_count], np.int32)
@@ -248,8 +252,8 @@ def draft_sample(logits, uniforms, T, lib=None):
     R, V = logits.shape
     u = np.ascontiguousarray(uniforms, np.float32)
     assert u.size == R
-    tokens = np.zeros(R, np.int32)
-    margin = np.zeros(R, np.float64)
+    tokens = np.full(R, UNWRITTEN, np.int32)
+    margin = np.full(R, float(UNWRITTEN), np.float64)
     fl = lib.oracle_draft_sample(_dtype_code(logits), R, V, T, _ptr(logits), _ptr(u), _ptr(tokens), _ptr(margin))
     return dict(tokens=tokens, margin=margin, flags=int(fl))
 
@@ -261,8 +265,8 @@ def pacer_lengths(scores, block, max_blocks, t0, rho, lib=None):
     scores = np.ascontiguousarray(scores, np.float32)
     B = scores.shape[0]
     assert scores.shape == (B, max_blocks * block)
-    lengths = np.zeros(B, np.int32)
-    offsets = np.zeros(B + 1, np.int32)
+    lengths = np.full(B, UNWRITTEN, np.int32)
+    offsets = np.full(B + 1, UNWRITTEN, np.int32)
     lib.oracle_pacer_lengths(B, block, max_blocks, t0, rho, _ptr(scores), _ptr(lengths), _ptr(offsets))
     return lengths, offsets
 
@@ -290,12 +294,12 @@ def tree_verify(target, draft, node_off, draft_off, parent, tokens, uniforms, T,
     uniforms = np.ascontiguousarray(uniforms, dtype=np.float32)
     B = node_off.shape[0] - 1
     nn = int(node_off[-1]) if B >= 0 else 0
-    na = np.zeros(max(B, 1), np.int32)
-    ln = np.zeros(max(B, 1), np.int32)
-    ft = np.zeros(max(B, 1), np.int32)
+    na = np.full(max(B, 1), UNWRITTEN, np.int32)
+    ln = np.full(max(B, 1), UNWRITTEN, np.int32)
+    ft = np.full(max(B, 1), UNWRITTEN, np.int32)
     fl = np.zeros(1, np.uint32)
-    am = np.full(max(nn, 1), -1.0)
-    sm = np.zeros(max(B, 1))
+    am = np.full(max(nn, 1), float(UNWRITTEN))
+    sm = np.full(max(B, 1), float(UNWRITTEN))
     st = lib.oracle_tree_verify(_dtype_code(target), B, V, T, _ptr(node_off), _ptr(draft_off), _ptr(parent),
                                 _ptr(tokens), _ptr(target), _ptr(draft), _ptr(uniforms), _ptr(na), _ptr(ln),
                                 _ptr(ft), _ptr(fl), _ptr(am), _ptr(sm))

@@ -234,10 +234,10 @@ def check_zero_residual_fallback(lib):
 def check_cdf_clamp_last_positive(lib):
     """Reading: when no inclusive prefix exceeds u * Z (u = 1.0 here, where the
     last prefix equals Z), the draw takes the last index with positive weight
-    and raises CDF_CLAMP.  Rows whose trailing (and some inner) logits are
-    -inf: the answer is the last finite logit, neither index 0 nor V - 1.
-    Checked on the bonus draw (draft = target, all accepted) and on the
-    residual draw (a rejection)."""
+    and raises CDF_CLAMP, its margin 0 (no interval holds u).  Rows whose
+    trailing (and some inner) logits are -inf: the answer is the last finite
+    logit, neither index 0 nor V - 1.  Checked on the bonus draw (draft =
+    target, all accepted) and on the residual draw (a rejection)."""
     ninf = -np.inf
     for row, last in (([1.0, 2.0, ninf, 0.5, ninf, ninf], 3), ([ninf, 0.25, 3.0, ninf], 2),
                       ([0.0, 0.0, 0.0, 0.0, 0.0, ninf, ninf, ninf], 4)):
@@ -245,14 +245,14 @@ def check_cdf_clamp_last_positive(lib):
         r = oracle.sd_verify(z, np.zeros((0, z.shape[1]), np.float32), np.zeros(0, np.int32), [1.0], 1.0, K=0,
                              lib=lib)
         assert r["final_token"].tolist() == [last], (row, r)
-        assert r["flags"] & oracle.FLAG_CDF_CLAMP, r
+        assert r["flags"] & oracle.FLAG_CDF_CLAMP and r["sample_margin"][0] == 0.0, r
     # residual: p puts mass on tokens 0..3, q on token 0 only; max(0, p - q)
     # is positive on 1..3 (trailing tokens -inf in both rows); token 0 rejects
     zt = np.asarray([[0.0, 0.0, 0.0, 0.0, ninf, ninf], [0.0] * 6], np.float32)
     zd = np.asarray([[0.0, ninf, ninf, ninf, ninf, ninf]], np.float32)
     r = oracle.sd_verify(zt, zd, np.zeros(1, np.int32), [0.5, 1.0], 1.0, K=1, lib=lib)
     assert r["num_accepted"].tolist() == [0] and r["final_token"].tolist() == [3], r
-    assert r["flags"] & oracle.FLAG_CDF_CLAMP, r
+    assert r["flags"] & oracle.FLAG_CDF_CLAMP and r["sample_margin"][0] == 0.0, r
 
 
 def check_bonus_vs_numpy(lib):
@@ -495,7 +495,8 @@ def check_systematic_invariants(lib):
 def check_systematic_clamp_last_positive(lib):
     """Reading: a systematic point U_k that no normalised prefix C_i exceeds
     (resample uniform 1.0 puts U_{N-1} = 1.0, and the last prefix equals 1)
-    goes to the last particle with positive weight, and CDF_CLAMP is raised.
+    goes to the last particle with positive weight, CDF_CLAMP is raised and
+    the resampling margin is 0.
     Particles with weight 0 (log-weight -inf) at the end: the last slot's
     ancestor is the last live particle, not particle 0 or N - 1; the other
     slots follow the exact rational rule."""
@@ -506,7 +507,7 @@ def check_systematic_clamp_last_positive(lib):
         r = _smc_from_logw(lib, lw, 1.0, ess_frac=1.01)
         a = r["ancestors"].tolist()
         assert r["resampled"][0] == 1 and a[-1] == last, (lw, a)
-        assert r["flags"] & oracle.FLAG_CDF_CLAMP, r
+        assert r["flags"] & oracle.FLAG_CDF_CLAMP and r["resample_margin"][0] == 0.0, r
         M = max(x for x in lw if x > ninf)
         w = [Fraction(math.exp(float(np.float32(x)) - M)) if x > ninf else Fraction(0) for x in lw]
         C, acc = [], Fraction(0)
@@ -836,6 +837,234 @@ def check_pages_errors(lib):
     assert res["status"] == 3 and (res["ref"] == st["ref"]).all() and res["free_count"] == st["free_count"]
 
 
+def _interval_margin(cdf, y, u):
+    """Distance from u to the nearer edge of [cdf[y-1], cdf[y]) (normalised cdf)."""
+    lo = cdf[y - 1] if y > 0 else 0.0
+    return min(u - lo, cdf[y] - u)
+
+
+def check_margins_vs_numpy(lib):
+    """The decision margins the GPU comparison uses to excuse boundary cases,
+    recomputed here from scipy / numpy: SD accept margins |u_j - min(1, rho_j)|
+    for the tested positions and -1 after the first rejection, the final
+    draw's distance to its CDF interval edges; SMC bonus margins, the ESS
+    margin |ESS - ess_frac N| / N, the systematic margins and the cumulative
+    weights the draw used (-1 when a prompt keeps its particles)."""
+    rng = np.random.default_rng(59)
+    B, K, V, T = 24, 3, 40, 0.9
+    zt, zd, tok, u = rand_sd_problem(rng, B, K, V, T, delta=1.5)
+    r = oracle.sd_verify(zt, zd, tok, u, T, K=K, lib=lib)
+    lp = log_softmax(zt.astype(np.float64) / T, axis=-1)
+    lq = log_softmax(zd.astype(np.float64) / T, axis=-1)
+    for b in range(B):
+        n = int(r["num_accepted"][b])
+        for j in range(K):
+            got = r["accept_margin"][b * K + j]
+            if j <= n and j < K:
+                rho = math.exp(lp[b * (K + 1) + j, tok[b * K + j]] - lq[b * K + j, tok[b * K + j]])
+                assert abs(got - abs(float(u[b * (K + 1) + j]) - min(1.0, rho))) < 1e-9, (b, j, got)
+            else:
+                assert got == -1.0, (b, j, got)
+        p = np.exp(lp[b * (K + 1) + n])
+        w = np.maximum(0.0, p - np.exp(lq[b * K + n])) if n < K else p
+        cdf = np.cumsum(w) / w.sum()
+        uf = float(u[b * (K + 1) + K])
+        assert abs(r["sample_margin"][b] - _interval_margin(cdf, int(r["final_token"][b]), uf)) < 1e-9, b
+    P, N, K, V, T = 3, 8, 2, 30, 1.1
+    zt = (2 * rng.standard_normal((P * N * (K + 1), V))).astype(np.float32)
+    zd = (zt.reshape(P * N, K + 1, V)[:, :K] + rng.standard_normal((P * N, K, V))).astype(np.float32)
+    zd = zd.reshape(P * N * K, V)
+    tok = rng.integers(0, V, P * N * K).astype(np.int32)
+    ub, ur = rng.random(P * N).astype(np.float32), rng.random(P).astype(np.float32)
+    lw0 = (1.5 * rng.standard_normal(P * N)).astype(np.float32)
+    for ess_frac in (2.0, 0.0):
+        r = oracle.smc_step(zt, zd, tok, ub, ur, lw0, T, ess_frac, P, N, K, lib=lib)
+        for i in range(P * N):
+            cdf = np.cumsum(softmax(zt[i * (K + 1) + K].astype(np.float64) / T))
+            assert abs(r["bonus_margin"][i] - _interval_margin(cdf, int(r["bonus"][i]), float(ub[i]))) < 1e-9, i
+        lp = log_softmax(zt.astype(np.float64) / T, axis=-1).reshape(P * N, K + 1, V)
+        lq = log_softmax(zd.astype(np.float64) / T, axis=-1).reshape(P * N, K, V)
+        for p in range(P):
+            lw = np.array([np.float32(float(lw0[p * N + n]) + sum(
+                lp[p * N + n, j, tok[(p * N + n) * K + j]] - lq[p * N + n, j, tok[(p * N + n) * K + j]]
+                for j in range(K))) for n in range(N)], np.float64)
+            w = np.exp(lw - lw.max())
+            E = w.sum() ** 2 / (w * w).sum()
+            assert abs(r["ess_margin"][p] - abs(E - ess_frac * N) / N) < 1e-9, p
+            C = np.cumsum(w) / w.sum()
+            cw = r["cum_weight"][p * N:(p + 1) * N]
+            if ess_frac == 2.0:
+                assert np.abs(cw - C).max() < 1e-12, p
+                a = r["ancestors"][p * N:(p + 1) * N]
+                m = min(min((float(ur[p]) + k) / N - (C[a[k] - 1] if a[k] > 0 else 0.0), C[a[k]] - (float(ur[p]) + k) / N)
+                        for k in range(N))
+                assert abs(r["resample_margin"][p] - m) < 1e-12, p
+            else:
+                assert (cw == -1.0).all() and r["resample_margin"][p] == np.inf, p
+
+
+def check_nonfinite_and_zero_weight_flags(lib):
+    """NONFINITE for a NaN or +inf logit and for a row of -inf logits (SD and
+    SMC rows), and for a NaN or +inf log-weight; a row with some -inf logits
+    (masked tokens) is no error.  Every log-weight -inf: ZERO_WEIGHTS, ESS 0,
+    no resampling, identity ancestors, log-weights carried over."""
+    ninf = -np.inf
+    t = np.array([[0.5, 1.0, -0.5], [0.1, 0.2, 0.3]], np.float32)
+    d = np.array([[0.4, 1.1, -0.2]], np.float32)
+    assert oracle.sd_verify(t, d, [1], [0.3, 0.6], 1.0, K=1, lib=lib)["flags"] == 0
+    for bad in (np.nan, np.inf):
+        for which in ("t", "d"):
+            tt, dd = t.copy(), d.copy()
+            (tt if which == "t" else dd)[0, 2] = bad
+            assert oracle.sd_verify(tt, dd, [1], [0.3, 0.6], 1.0, K=1, lib=lib)["flags"] & oracle.FLAG_NONFINITE, (bad,
+                                                                                                                     which)
+    masked = t.copy()
+    masked[0, 2] = ninf
+    assert oracle.sd_verify(masked, d, [1], [0.3, 0.6], 1.0, K=1, lib=lib)["flags"] == 0
+    dead = d.copy()
+    dead[0, :] = ninf
+    assert oracle.sd_verify(t, dead, [1], [0.3, 0.6], 1.0, K=1, lib=lib)["flags"] & oracle.FLAG_NONFINITE
+    N, V = 4, 3
+    zt = np.tile(t[:1], (N * 2, 1))
+    zd = np.tile(d, (N, 1))
+    args = (zt, zd, np.ones(N, np.int32), np.full(N, 0.5, np.float32), [0.3])
+    assert oracle.smc_step(*args, np.zeros(N, np.float32), 1.0, 0.5, 1, N, 1, lib=lib)["flags"] == 0
+    for bad in (np.nan, np.inf):
+        lw = np.zeros(N, np.float32)
+        lw[2] = bad
+        assert oracle.smc_step(*args, lw, 1.0, 0.5, 1, N, 1, lib=lib)["flags"] & oracle.FLAG_NONFINITE, bad
+    zb = zt.copy()
+    zb[1, 0] = np.nan  # a bonus row (row K = 1 of particle 0)
+    assert oracle.smc_step(zb, *args[1:], np.zeros(N, np.float32), 1.0, 0.5, 1, N, 1, lib=lib)["flags"] & 1
+    r = _smc_from_logw(lib, np.full(5, ninf), 0.4, ess_frac=2.0)
+    assert r["flags"] & oracle.FLAG_ZERO_WEIGHTS and r["ess"][0] == 0.0 and r["resampled"][0] == 0, r
+    assert r["ancestors"].tolist() == list(range(5)) and np.isneginf(r["logw"]).all(), r
+
+
+def _pages_used_entries(table, lens, S):
+    return [int(table[r, j]) for r in range(table.shape[0]) for j in range((int(lens[r]) + S - 1) // S)]
+
+
+def check_pages_exact_capacity(lib):
+    """An append that needs exactly the free pages succeeds and empties the
+    stack; one page short it fails (status 2) and changes nothing.  A shared
+    partially filled tail costs a copy (the highest-index sharer keeps the
+    page); a tail named by one row costs none."""
+    S, L, M = 4, 4, 8
+    # rows 0 and 1 share page 5 as their tail (2 tokens), pages 0, 1, 3 free
+    table = np.full((2, L), -1, np.int32)
+    table[:, 0] = 5
+    lens = np.array([2, 2], np.int32)
+    ref = np.zeros(M, np.int32)
+    ref[5] = 2
+    free = np.array([0, 1, 3, 0, 0, 0, 0, 0], np.int32)
+    # 6 more tokens: each row reaches a second page, row 0 also copies its tail
+    ok = oracle.pages_append(table, lens, ref, free, 3, S, 6, lib=lib)
+    assert ok["status"] == 0 and ok["free_count"] == 0, ok
+    assert ok["cow"].tolist() == [[5, 3, 2]] and ok["table"][1, 0] == 5 and ok["table"][0, 0] == 3, ok
+    assert ok["ref"][5] == 1 and sorted(_pages_used_entries(ok["table"], ok["len"], S)) == [0, 1, 3, 5]
+    short = oracle.pages_append(table, lens, ref, free, 2, S, 6, lib=lib)
+    assert short["status"] == 2 and (short["table"] == table).all() and (short["ref"] == ref).all(), short
+    assert short["free_count"] == 2 and (short["len"] == lens).all()
+    # a tail named once (page 2, 2 tokens) and a full page (page 4): one token
+    # each needs one new page (row 1's), no copy
+    table = np.array([[2, -1, -1, -1], [4, -1, -1, -1]], np.int32)
+    lens = np.array([2, 4], np.int32)
+    ref = np.zeros(M, np.int32)
+    ref[2] = ref[4] = 1
+    one = oracle.pages_append(table, lens, ref, np.array([6] + [0] * 7, np.int32), 1, S, 1, lib=lib)
+    assert one["status"] == 0 and one["free_count"] == 0 and one["cow"].size == 0, one
+    assert one["table"].tolist() == [[2, -1, -1, -1], [4, 6, -1, -1]] and one["slots"].tolist() == [[10], [24]], one
+
+
+def check_pages_invalid_states(lib):
+    """States the bookkeeping cannot take change nothing and return status 3:
+    for an append, a negative length, a length past L pages, a tail page id
+    outside the pool (-1 or M); for a resampling, an ancestor outside 0..N-1,
+    a length outside 0..L*S, a page id outside the pool in a used entry of an
+    old or a gathered row."""
+    S, L, M = 4, 2, 6
+    table = np.array([[1, -1], [2, 3]], np.int32)
+    lens = np.array([3, 6], np.int32)
+    ref = np.array([0, 1, 1, 1, 0, 0], np.int32)
+    free = np.array([0, 4, 5, 0, 0, 0], np.int32)
+    assert oracle.pages_append(table, lens, ref, free, 3, S, 1, lib=lib)["status"] == 0
+    cases = []
+    for r, v in ((0, -1), (1, 9)):
+        ll = lens.copy()
+        ll[r] = v
+        cases.append((table, ll, ref))
+    for pg in (-1, M):
+        tt = table.copy()
+        tt[0, 0] = pg
+        cases.append((tt, lens, ref))
+    for tt, ll, rr in cases:
+        res = oracle.pages_append(tt, ll, rr, free, 3, S, 1, lib=lib)
+        assert res["status"] == 3 and (res["table"] == tt).all() and (res["len"] == ll).all(), (tt, ll, res)
+        assert (res["ref"] == rr).all() and res["free_count"] == 3
+    N = 2
+    good = oracle.pages_resample(1, N, [1, 1], table, table[[1, 1]], lens, ref, free, 3, S, lib=lib)
+    assert good["status"] == 0 and good["len"].tolist() == [6, 6], good
+    bad = [([-1, 1], table, table[[1, 1]], lens), ([1, 2], table, table[[1, 1]], lens),
+           ([1, 1], table, table[[1, 1]], np.array([-2, 6], np.int32)),
+           ([1, 1], table, table[[1, 1]], np.array([3, 9], np.int32))]
+    for pg in (-1, M):
+        tn = table[[1, 1]].copy()
+        tn[0, 1] = pg
+        bad.append(([1, 1], table, tn, lens))
+        to = table.copy()
+        to[1, 1] = pg
+        bad.append(([0, 0], to, to[[0, 0]], lens))
+    for anc, told, tnew, ll in bad:
+        res = oracle.pages_resample(1, N, np.array(anc, np.int32), told, tnew, ll, ref, free, 3, S, lib=lib)
+        assert res["status"] == 3 and (res["ref"] == ref).all() and res["free_count"] == 3, (anc, told, tnew, ll)
+
+
+def check_pages_empty_rows_and_page_zero(lib):
+    """Length 0 is a valid row (no used entry, no tail) for an append and for
+    a resampling; page 0 is a page of the pool like any other, also as a
+    shared tail."""
+    S, L, M = 4, 2, 6
+    table = np.array([[0, -1], [-1, -1], [0, -1]], np.int32)
+    lens = np.array([1, 0, 1], np.int32)
+    ref = np.array([2, 0, 0, 0, 0, 0], np.int32)
+    free = np.array([5, 4, 3, 2, 1, 0], np.int32)
+    r = oracle.pages_append(table, lens, ref, free, 5, S, 2, lib=lib)
+    # rows in order pop the stack's top: row 0 copies its shared tail (page 0,
+    # 1 token) into page 1; row 1 takes page 2; row 2, the highest-index
+    # sharer, keeps page 0
+    assert r["status"] == 0 and r["len"].tolist() == [3, 2, 3], r
+    assert r["table"][:, 0].tolist() == [1, 2, 0] and r["cow"].tolist() == [[0, 1, 1]], r
+    assert r["slots"].tolist() == [[5, 6], [8, 9], [1, 2]] and r["free_count"] == 3, r
+    assert r["ref"].tolist() == [1, 1, 1, 0, 0, 0], r
+    rs = oracle.pages_resample(1, 3, np.array([1, 1, 0], np.int32), table, table[[1, 1, 0]], lens, ref, free, 5, S,
+                               lib=lib)
+    # rows 0 and 2 named page 0; only the new row 2 does: count 1, no page freed
+    assert rs["status"] == 0 and rs["len"].tolist() == [0, 0, 1] and rs["ref"].tolist() == [1, 0, 0, 0, 0, 0], rs
+    assert rs["free_count"] == 5
+
+
+def check_pages_full_rows(lib):
+    """A resampling over rows filled to their last page: every page's count
+    equals the used entries naming it in the gathered rows, and the free stack
+    gains exactly the pages no gathered row names."""
+    S, L, M = 4, 2, 12
+    table = np.array([[0, 1], [2, 3], [4, -1], [5, 6]], np.int32)
+    lens = np.array([8, 8, 3, 8], np.int32)  # rows 0, 1 and 3 full
+    ref = np.zeros(M, np.int32)
+    for pg in (0, 1, 2, 3, 4, 5, 6):
+        ref[pg] = 1
+    free = np.array(list(range(7, 12)) + [0] * 7, np.int32)
+    anc = np.array([0, 0, 3, 3], np.int32)
+    r = oracle.pages_resample(1, 4, anc, table, table[anc], lens, ref, free, 5, S, lib=lib)
+    assert r["status"] == 0 and r["len"].tolist() == [8, 8, 8, 8], r
+    want = np.zeros(M, np.int32)
+    for pg in _pages_used_entries(table[anc], r["len"], S):
+        want[pg] += 1
+    assert (r["ref"] == want).all(), (r["ref"], want)
+    assert sorted(r["free_pages"][5:r["free_count"]].tolist()) == [2, 3, 4], r
+
+
 # --------------------------------------------------------------------------
 # draft side: token draws from q, PACER lengths
 # --------------------------------------------------------------------------
@@ -1143,6 +1372,109 @@ def check_tree_malformed(lib):
         assert r["status"] == -1, (par, nd)
 
 
+def _residual_chain(p, q, rejections):
+    """numpy: r = p, then `rejections` times r <- max(0, r - q) / Z (r kept when
+    Z is 0); returns (r, weights of the final draw after them)."""
+    r, w = p.copy(), p.copy()
+    for _ in range(rejections):
+        w = np.maximum(0.0, r - q)
+        if w.sum() > 0:
+            r = w / w.sum()
+        else:
+            w = r.copy()
+    return r, w
+
+
+def check_tree_zero_residual_and_bad_tokens(lib):
+    """A rejection whose residual has no mass (the node's draft row equal to
+    its target row, accept uniform 1.0) keeps r and raises ZERO_RESIDUAL: the
+    next child's ratio is still 1, so it is accepted with u < 1, and when it
+    is rejected too the final token is drawn from r = p_root (numpy
+    searchsorted).  A child whose token lies outside the vocabulary has ratio
+    0 and is rejected even with u = 0; the final token then follows the
+    numpy residual chain."""
+    rng = np.random.default_rng(61)
+    V, T, uf = 9, 1.0, 0.4321
+    zr = (2 * rng.standard_normal(V)).astype(np.float32)
+    z1, z2 = (2 * rng.standard_normal((2, V))).astype(np.float32)
+    zq = (zr + rng.standard_normal(V)).astype(np.float32)
+    mk = lambda d, toks, us: dict(parent=[-1, 0, 0], tokens=toks, target=np.stack([zr, z1, z2]),  # noqa: E731
+                                  draft=d[None, :], uniforms=[uf] + us)
+    trees = [mk(zr, [0, 3, 5], [1.0, 0.3]), mk(zr, [0, 3, 5], [1.0, 1.0]), mk(zq, [0, V, -1], [0.0, 0.0])]
+    r = _tree_run(lib, _pack_trees(trees), T)
+    assert r["status"] == 0 and r["flags"] & oracle.FLAG_ZERO_RESIDUAL, r
+    assert r["num_accepted"].tolist() == [1, 0, 0] and r["last_node"].tolist() == [2, 0, 0], r
+    sm = lambda z: softmax(z.astype(np.float64) / T)  # noqa: E731
+    p_root, q_root = sm(zr), sm(zq)
+    _, w = _residual_chain(p_root, q_root, 2)
+    for b, wt in ((0, sm(z2)), (1, p_root), (2, w)):
+        c = np.cumsum(wt)
+        assert np.min(np.abs(c / c[-1] - uf)) > 1e-9
+        assert r["final_token"][b] == int(np.searchsorted(c, uf * c[-1], side="right")), (b, r["final_token"])
+
+
+def check_tree_margins_vs_numpy(lib):
+    """Tree margins against numpy: each tested child's |u - min(1, r(x)/q(x))|
+    with r the residual chain at its parent, -1 for untested nodes and the
+    root, and the final draw's distance to its CDF interval edges."""
+    rng = np.random.default_rng(67)
+    V, T = 12, 0.8
+    trees = []
+    for b in range(30):
+        zt = (2 * rng.standard_normal((4, V))).astype(np.float32)
+        zd = (zt[:1] + 1.5 * rng.standard_normal((1, V))).astype(np.float32)
+        trees.append(dict(parent=[-1, 0, 0, 0], tokens=[0] + rng.integers(0, V, 3).tolist(), target=zt, draft=zd,
+                          uniforms=rng.random(4).astype(np.float32)))
+    r = _tree_run(lib, _pack_trees(trees), T)
+    assert r["status"] == 0
+    sm = lambda z: softmax(z.astype(np.float64) / T)  # noqa: E731
+    for b, t in enumerate(trees):
+        am = r["accept_margin"][4 * b:4 * b + 4]
+        p, q = sm(t["target"][0]), sm(t["draft"][0])
+        rr, w = p.copy(), p.copy()
+        assert am[0] == -1.0
+        stop = None
+        for c in (1, 2, 3):
+            if stop is not None:
+                assert am[c] == -1.0, (b, c, am)
+                continue
+            x, uc = t["tokens"][c], float(t["uniforms"][c])
+            ratio = rr[x] / q[x]
+            assert abs(am[c] - abs(uc - min(1.0, ratio))) < 1e-9, (b, c, am[c])
+            if uc < ratio:
+                stop = c
+            else:
+                rr, w = _residual_chain(rr, q, 1)
+        wt = sm(t["target"][stop]) if stop is not None else w
+        cdf = np.cumsum(wt) / wt.sum()
+        assert r["last_node"][b] == (stop or 0)
+        assert abs(r["sample_margin"][b] - _interval_margin(cdf, int(r["final_token"][b]), float(t["uniforms"][0]))) \
+            < 1e-9, b
+
+
+def check_tree_malformed_orders(lib):
+    """A node that is its own parent, or whose parent comes after it, is
+    refused even when the count of nodes with children matches the draft
+    rows; and the final-draw CDF refuses a node outside the tree (a tree of
+    one node, the root alone, has the root's softmax as its CDF)."""
+    V = 8
+    z = np.zeros((3, V), np.float32)
+    for par, nd in (([-1, 1], 1), ([-1, 2, 0], 2), ([-1, 0, 2], 1)):
+        r = _tree_run(lib, _pack_trees([dict(parent=par, tokens=[0] * len(par), target=z[:len(par)], draft=z[:nd],
+                                             uniforms=[0.5] * len(par))]), 1.0)
+        assert r["status"] == -1, (par, nd)
+    one = np.asarray([[0.5, -1.0, 2.0, 0.0, 0.0, 1.0, -2.0, 0.25]], np.float32)
+    pk = _pack_trees([dict(parent=[-1], tokens=[0], target=one, draft=z[:0], uniforms=[0.5])])
+    cdf, fl = oracle.tree_final_cdf(pk["target"], pk["draft"], pk["node_off"], pk["draft_off"], pk["parent"], 0, 0,
+                                    1.0, lib=lib)
+    assert fl == 0 and np.allclose(cdf, np.cumsum(softmax(one[0].astype(np.float64))), rtol=0, atol=1e-12), cdf
+    pk = _pack_trees([dict(parent=[-1, 0], tokens=[0, 1], target=z[:2], draft=z[:1], uniforms=[0.5, 0.5])])
+    for u in (-1, 2):
+        _, fl = oracle.tree_final_cdf(pk["target"], pk["draft"], pk["node_off"], pk["draft_off"], pk["parent"], 0, u,
+                                      1.0, lib=lib)
+        assert fl == -1, u
+
+
 def check_tree_final_cdf(lib):
     """The CDF the comparison judges a differing final token against: p_u at a
     leaf; after every child of u is rejected, the last max(0, r - q) of the
@@ -1230,6 +1562,9 @@ DETERMINISTIC_CHECKS = [
     check_tree_identical_rows,
     check_tree_root_only,
     check_tree_malformed,
+    check_tree_malformed_orders,
+    check_tree_zero_residual_and_bad_tokens,
+    check_tree_margins_vs_numpy,
     check_tree_final_cdf,
     check_golden_sd_fixed,
     check_golden_sd_csr,
@@ -1246,6 +1581,8 @@ DETERMINISTIC_CHECKS = [
     check_residual_vs_numpy,
     check_accept_decisions_vs_scipy,
     check_final_cdf_vs_numpy,
+    check_margins_vs_numpy,
+    check_nonfinite_and_zero_weight_flags,
     check_ess_closed_forms,
     check_threshold_strict,
     check_systematic_invariants,
@@ -1260,6 +1597,10 @@ DETERMINISTIC_CHECKS = [
     check_power_one_is_plain,
     check_pages_content_model,
     check_pages_errors,
+    check_pages_exact_capacity,
+    check_pages_invalid_states,
+    check_pages_full_rows,
+    check_pages_empty_rows_and_page_zero,
     check_golden_draft_sample,
     check_draft_sample_vs_numpy,
     check_draft_sample_law,

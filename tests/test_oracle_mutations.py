@@ -91,6 +91,23 @@ MUTATIONS = [
     ("tree_depth_not_counted", "      u = next;\n      depth++;", "      u = next;"),
     ("tree_row_of_root", "const void* trow = row_ptr(dtype, target, n0 + u, V);",
      "const void* trow = row_ptr(dtype, target, n0, V);"),
+    ("accept_margin_unclamped", "fabs(u - (rho < 1.0 ? rho : 1.0))", "fabs(u - rho)"),
+    ("sample_margin_on_clamp", "  if (margin) *margin = 0.0;\n", "  if (margin) *margin = 1.0;\n"),
+    ("resample_margin_on_clamp", "          rmargin = 0.0;\n", "          rmargin = 1.0;\n"),
+    ("nonfinite_weight_unflagged", "      if (isnan(lw[n]) || lw[n] == INFINITY) fl |= ORACLE_FLAG_NONFINITE;\n", ""),
+    ("zero_weights_unflagged", "      fl |= ORACLE_FLAG_ZERO_WEIGHTS;\n", ""),
+    ("pages_empty_row_refused", "if (len[r] < 0 || used_pages(len[r], S) > L) bad = 1;",
+     "if (len[r] <= 0 || used_pages(len[r], S) > L) bad = 1;"),
+    ("pages_page_zero_refused", "if (pg < 0 || pg >= M) bad = 1;", "if (pg <= 0 || pg >= M) bad = 1;"),
+    ("pages_resample_empty_row_refused", "if (len_in[k] < 0 || used_pages(len_in[k], S) > L) return 3;",
+     "if (len_in[k] <= 0 || used_pages(len_in[k], S) > L) return 3;"),
+    ("tree_bad_token_accepted", "double ratio = x >= 0 && x < V ? r[x] / q[x] : 0.0;",
+     "double ratio = x >= 0 && x < V ? r[x] / q[x] : 1.0;"),
+    ("tree_zero_residual_uniform", "    *fl |= ORACLE_FLAG_ZERO_RESIDUAL;\n    for (int64_t i = 0; i < V; i++) w[i] = r[i];",
+     "    *fl |= ORACLE_FLAG_ZERO_RESIDUAL;\n    for (int64_t i = 0; i < V; i++) w[i] = 1.0;"),
+    ("tree_accept_margin_unclamped", "fabs(uc - (ratio < 1.0 ? ratio : 1.0))", "fabs(uc - ratio)"),
+    ("tree_self_parent_accepted", "if (par[n] < 0 || par[n] >= n) return -1;", "if (par[n] < 0 || par[n] > n) return -1;"),
+    ("tree_single_node_refused", "if (M < 1 || u < 0 || u >= M) return -1;", "if (M <= 1 || u < 0 || u >= M) return -1;"),
 ]
 
 
