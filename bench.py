@@ -73,6 +73,9 @@ def _find(d, suffix):
 CALL_KERNELS = {"k_stream": ("k_stream",), "decision": ("_tail", "k_smc_prompt")}
 
 
+VALU_CUS, VALU_XCDS = 256, 8  # MI355X
+
+
 def summarize(dirs, copy_bytes=None):
     """Text summary of rocprofv3 output directories: kernel statistics
     (--kernel-trace --stats) and per-dispatch averages of PMC counters
@@ -121,6 +124,20 @@ def summarize(dirs, copy_bytes=None):
                                f"KiB (factor {factor:.4f}) -> {kv * 1024.0 / factor:.0f} B per launch")
             if len(res) == 2:
                 out.append(f"traffic_bytes_per_call {role}: {res['FETCH_SIZE'] + res['WRITE_SIZE']:.0f}")
+    valu = sorted({k for (k, c) in avg if c == "SQ_ACTIVE_INST_VALU" and "smcsd" in k})
+    if valu and all((k, c) in avg for k in valu for c in ("GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")):
+        # SQ_ACTIVE_INST_VALU and SQ_BUSY_CU_CYCLES are quad-cycles summed over
+        # SIMDs and CUs, GRBM_GUI_ACTIVE is summed over the XCDs: device-wide
+        # VALU busy = VALU / CUs / (GUI active / XCDs) (the VALUBusy metric);
+        # per busy CU = VALU / busy-CU cycles
+        out.append(f"VALU activity ({VALU_CUS} CUs, {VALU_XCDS} XCDs):")
+        for k in valu:
+            v, g, b = avg[(k, "SQ_ACTIVE_INST_VALU")], avg[(k, "GRBM_GUI_ACTIVE")], avg[(k, "SQ_BUSY_CU_CYCLES")]
+            extra = ""
+            if (k, "SQ_INSTS_VALU_TRANS_F32") in avg and (k, "SQ_INSTS_VALU") in avg:
+                extra = f" | transcendental share {avg[(k, 'SQ_INSTS_VALU_TRANS_F32')] / avg[(k, 'SQ_INSTS_VALU')]:.2f}"
+            out.append(f"  {k[:70]} | VALU busy {100 * v / VALU_CUS / (g / VALU_XCDS):.1f} % of the device | "
+                       f"{100 * v / b:.1f} % of its busy CUs' time{extra}")
     return "\n".join(out)
 
 

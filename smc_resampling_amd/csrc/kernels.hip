@@ -1214,12 +1214,38 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
       m = wave_sum(m);
       if (lane == 0) L.t.W[t] = (double)m;
     };
-    // one pass over u's row pair: every tile's mass into L.t.W
+    // one pass over u's row pair: every tile's mass into L.t.W; with bf16
+    // 16-byte loads (registers to spare) a wavefront issues the loads of two
+    // of its tiles before weighing either, so a 16-tile pair costs one round
+    // trip to memory, not two
+    constexpr bool PAIR = DT::VEC == 8 && VL;
     auto pass = [&](int nr, bool sub) {
-      for (int t = wave; t < ntiles; t += TREE_WAVES) {
+      if constexpr (!PAIR) {
+        for (int t = wave; t < ntiles; t += TREE_WAVES) {
+          float w[PER_LANE];
+          tile_w(t, nr, sub, w);
+          store_mass(t, w);
+        }
+        return;
+      }
+      for (int t0 = wave; t0 < ntiles; t0 += 2 * TREE_WAVES) {
+        const int t1 = t0 + TREE_WAVES;
+        const int t1c = min(t1, ntiles - 1);  // a tile of the row either way
+        Raw<DT> rt0 = load_raw<DT, VL, 0>(trow, s.V, t0, lane);
+        Raw<DT> rd0 = load_raw<DT, VL, 0>(drw, s.V, t0, lane);
+        Raw<DT> rt1 = load_raw<DT, VL, 0>(trow, s.V, t1c, lane);
+        Raw<DT> rd1 = load_raw<DT, VL, 0>(drw, s.V, t1c, lane);
         float w[PER_LANE];
-        tile_w(t, nr, sub, w);
-        store_mass(t, w);
+        mask_tail<DT>(rt0, s.V, t0, lane);
+        mask_tail<DT>(rd0, s.V, t0, lane);
+        tree_weights<DT>(rt0, rd0, At, Ad, s.c, L.iz, nr, sub, w);
+        store_mass(t0, w);
+        if (t1 < ntiles) {
+          mask_tail<DT>(rt1, s.V, t1, lane);
+          mask_tail<DT>(rd1, s.V, t1, lane);
+          tree_weights<DT>(rt1, rd1, At, Ad, s.c, L.iz, nr, sub, w);
+          store_mass(t1, w);
+        }
       }
     };
     int nrej = 0, next = -1;
