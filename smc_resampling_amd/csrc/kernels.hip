@@ -37,9 +37,6 @@
 // orders it.
 #include <hip/hip_ext.h>
 
-#include <map>
-#include <mutex>
-
 #include "device.h"
 #include "launch.h"
 
@@ -1579,20 +1576,14 @@ __global__ __launch_bounds__(BLOCK) void k_smc_prompt(SmcArgs a) {
 // ---------------------------------------------------------------------------
 // host: plans and launches
 // ---------------------------------------------------------------------------
-// Workgroups the current device holds at once for `kernel` (queried once per
-// device and kernel).
+// Workgroups the current device holds at once for `kernel`, queried on every
+// call (the runtime answers both queries in about 0.1 us of host time, so the
+// library keeps no state for them).
 static int resident_blocks(const void* kernel) {
-  static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
-  int dev = 0;
+  int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find({dev, kernel});
-  if (it != cache.end()) return it->second;
-  int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, BLOCK, 0) != hipSuccess) return 0;
-  cache[{dev, kernel}] = cus * per_cu;
   return cus * per_cu;
 }
 
