@@ -19,6 +19,7 @@ SMC step at V = 151936.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -158,6 +159,24 @@ def traffic_from_profiles(workload):
         return None, None
     get = lambda k: float(fields[k]) if k in fields else None  # noqa: E731
     return get("traffic_bytes_per_call k_stream"), get("traffic_bytes_per_call decision")
+
+
+def environment():
+    """The GPU and software the line was measured on."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    env = {"device": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+           "hip": torch.version.hip, "torch": torch.__version__}
+    try:  # the shader clock the runtime reports (kHz)
+        lib = ctypes.CDLL("libamdhip64.so")
+        for key, attr in (("clock_mhz", 5), ("memory_clock_mhz", 60)):  # hipDeviceAttribute{,Memory}ClockRate
+            khz = ctypes.c_int(0)
+            if lib.hipDeviceGetAttribute(ctypes.byref(khz), attr, 0) == 0:
+                env[key] = khz.value / 1000.0
+    except OSError:
+        pass
+    return env
 
 
 def host_description():
@@ -522,8 +541,12 @@ def run_workload(args, config, steps_arg, with_cpu):
             smcsd.time_next_call(*ev[s_])
             c()
     torch.cuda.synchronize()
-    stream_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]))
-    tail_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(steps)]))
+    stream_each = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    tail_each = [ev[i][2].elapsed_time(ev[i][3]) for i in range(steps)]
+    call_each = [ev[i][0].elapsed_time(ev[i][3]) for i in range(steps)]  # first kernel's start to last one's stop
+    stream_ms = float(np.mean(stream_each))
+    tail_ms = float(np.mean(tail_each))
+    spread = lambda x: [round(float(v) * 1e3, 3) for v in np.percentile(x, [10, 50, 90])]  # noqa: E731  us
     timed = [(W + s) % nb for s in range(steps)]
     pos_total = sum(positions[i] for i in timed)
     bytes_total = sum(nbytes[i] for i in timed)
@@ -610,7 +633,13 @@ def run_workload(args, config, steps_arg, with_cpu):
                      "frac_of_read_ceiling": achieved / read_gbs,
                      "decision_kernel_us": tail_ms * 1e3, "decision_kernel_traffic": t_tail,
                      "call_us": ms_per_step * 1e3, "call_achieved": call_gbs, "call_frac": call_gbs / HBM_PEAK_GBS,
-                     "call_traffic": (t_stream + t_tail) if t_stream is not None and t_tail is not None else None},
+                     "call_traffic": (t_stream + t_tail) if t_stream is not None and t_tail is not None else None,
+                     # per-step spread of the event-timed eager pass (us: p10, median, p90); the
+                     # eager call span runs from the streaming kernel's start to the last decision
+                     # kernel's stop, without the graph
+                     "kernel_us_p10_p50_p90": spread(stream_each),
+                     "decision_kernel_us_p10_p50_p90": spread(tail_each),
+                     "eager_call_us_p10_p50_p90": spread(call_each)},
         "cpu_baseline": cpu,
     }
     return line
@@ -644,6 +673,7 @@ def main():
                            "traffic": r["traffic"], "call_traffic": r["call_traffic"],
                            "status_flags": o["config"]["status_flags"]})
         line["other_workloads"] = others
+    line["environment"] = environment()
     print(json.dumps(line), flush=True)
 
 
