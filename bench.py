@@ -179,6 +179,29 @@ def environment():
     return env
 
 
+def launch_floor(reps=64):
+    """Event-timed duration of the library's read kernel over one 4 KiB tile
+    (one workgroup, one load): what any kernel timed the way the bench times
+    its kernels costs at the least, in us (median over reps)."""
+    import numpy as np
+    import torch
+
+    import smc_resampling_amd as smcsd
+
+    a = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(64, dtype=torch.int32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    st = torch.cuda.current_stream()
+    for pair in ev:
+        for e_ in pair:
+            e_.record(st)  # creates the event handles the library attaches
+    torch.cuda.synchronize()
+    for pair in ev:
+        smcsd.read_ceiling(a, None, sink=sink, start=pair[0], stop=pair[1], stream=st.cuda_stream)
+    torch.cuda.synchronize()
+    return float(np.median([p[0].elapsed_time(p[1]) for p in ev])) * 1e3
+
+
 def host_description():
     """CPU model and the cores this process may use."""
     model = "unknown"
@@ -674,6 +697,7 @@ def main():
                            "status_flags": o["config"]["status_flags"]})
         line["other_workloads"] = others
     line["environment"] = environment()
+    line["environment"]["launch_floor_us"] = launch_floor()
     print(json.dumps(line), flush=True)
 
 
