@@ -161,6 +161,67 @@ def traffic_from_profiles(workload):
     return get("traffic_bytes_per_call k_stream"), get("traffic_bytes_per_call decision")
 
 
+STAMP_CALLS = 8  # calls whose decision-kernel stamps a phase summary pools
+STAMP_CLOCK_MHZ = 100.0  # s_memrealtime
+
+
+def phase_name(code):
+    """What ended at a stamp with this code (the codes of the library's launch.h)."""
+    fixed = {1: "statistics merged, token logits gathered", 2: "accept tests", 3: "bonus draw (all accepted)",
+             4: "residual pass over the rejected row pair", 5: "residual draw: tile located",
+             6: "residual draw: search in the tile", 7: "zero-residual draw from p_n",
+             10: "parents read, statistics merged", 11: "draft rows ranked, token logits gathered",
+             300: "step to a leaf", 400: "final draw"}
+    if code in fixed:
+        return fixed[code]
+    if 100 <= code < 200:
+        return f"level: child accepted after {code - 100} rejections"
+    if 200 <= code < 300:
+        return f"level: all {code - 200} children rejected"
+    return f"code {code}"
+
+
+def phase_summary(calls, stream):
+    """Replay `calls` one at a time on a measurement build and pool the
+    decision kernel's phase stamps: per phase (named by its end) the count and
+    the median and 90th percentile of its duration in us, and each workgroup's
+    span from its start to its last stamp."""
+    import numpy as np
+    import torch
+
+    import smc_resampling_amd as smcsd
+
+    torch.cuda.synchronize()
+    try:
+        smcsd.phase_stamps(clear=True)
+    except smcsd.SmcsdError:
+        sys.exit("--phase-stamps needs a library built with -DSMCSD_PHASE_STAMPS=1, named by SMCSD_LIBRARY")
+    phases, spans, kernel = {}, [], []
+    for c in calls:
+        with torch.cuda.stream(stream):
+            c()
+        torch.cuda.synchronize()
+        st = smcsd.phase_stamps(clear=True).astype(np.int64)
+        t, code = st[:, :, 0], st[:, :, 1]
+        live = np.nonzero(t[:, 0])[0]
+        if not len(live):
+            continue
+        for g in live:
+            n = int(np.count_nonzero(t[g]))
+            for k in range(1, n):
+                phases.setdefault(int(code[g, k]), []).append((t[g, k] - t[g, k - 1]) / STAMP_CLOCK_MHZ)
+            spans.append((t[g, n - 1] - t[g, 0]) / STAMP_CLOCK_MHZ)
+        ends = [t[g, int(np.count_nonzero(t[g])) - 1] for g in live]
+        kernel.append((max(ends) - t[live, 0].min()) / STAMP_CLOCK_MHZ)
+    if not spans:
+        return {"note": "no stamps: the workload's decision kernel records none, or the library was built without"}
+    q = lambda x: [round(float(v), 3) for v in np.percentile(x, [50, 90])]  # noqa: E731
+    return {"calls": len(calls), "workgroups": len(spans),
+            "phases_us_count_p50_p90": {phase_name(k): [len(v)] + q(v) for k, v in sorted(phases.items())},
+            "workgroup_span_us_p50_p90_max": q(spans) + [round(float(max(spans)), 3)],
+            "first_start_to_last_stamp_us_p50": round(float(np.median(kernel)), 3)}
+
+
 def environment():
     """The GPU and software the line was measured on."""
     import torch
@@ -249,6 +310,9 @@ def parse():
                     help="also run a plain device copy of this many bytes (scales rocprofv3 byte counters)")
     ap.add_argument("--summarize", nargs="+", default=None,
                     help="print a summary of these rocprofv3 output directories and exit")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="SD and tree workloads, with a library built with -DSMCSD_PHASE_STAMPS=1 (named by "
+                         "SMCSD_LIBRARY): add the decision kernel's phase durations to the line")
     return ap.parse_args()
 
 
@@ -579,6 +643,8 @@ def run_workload(args, config, steps_arg, with_cpu):
         f"{bytes_total / steps / (ms_per_step / 1e3) / 1e9:.0f} GB/s per call; k_stream {stream_ms * 1e3:.2f} us "
         f"({achieved:.0f} GB/s), decision kernel {tail_ms * 1e3:.2f} us, flags={flags}")
 
+    stamps = phase_summary(calls[W:W + STAMP_CALLS], run_stream) if args.phase_stamps else None
+
     # ---------------- the plain-read ceiling at the call's byte count -------------
     # The library's read-only kernel (the streaming kernel's loads, no
     # arithmetic) over the same batches, in the same order, with events on
@@ -665,6 +731,8 @@ def run_workload(args, config, steps_arg, with_cpu):
                      "eager_call_us_p10_p50_p90": spread(call_each)},
         "cpu_baseline": cpu,
     }
+    if stamps is not None:
+        line["phase_stamps"] = stamps
     return line
 
 

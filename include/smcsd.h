@@ -124,6 +124,9 @@ enum {
 #define SMCSD_WORKSPACE_ALIGN 256
 /* Size of the static scratch of smc_reweight_resample_noalloc (one per GPU). */
 #define SMCSD_NOALLOC_SCRATCH_BYTES (32u << 20)
+/* Layout of the phase timestamps of a measurement build (smcsd_phase_stamps). */
+#define SMCSD_STAMP_WGS 4096
+#define SMCSD_STAMP_EVENTS 16
 
 /* ABI version of the loaded library (SMCSD_ABI_VERSION it was built with). */
 int32_t smcsd_abi_version(void);
@@ -164,6 +167,24 @@ void smcsd_time_next_call(void* stream_start, void* stream_stop, void* tail_star
  */
 int32_t smcsd_read_ceiling(const void* a, size_t a_bytes, const void* b, size_t b_bytes, uint32_t* sink,
                            void* start_event, void* stop_event, void* stream);
+
+/*
+ * Measurement aid: phase timestamps of the decision kernels of sd_verify and
+ * tree_verify, recorded only by a build with -DSMCSD_PHASE_STAMPS=1 (the
+ * library's own build records nothing and returns SMCSD_ERR_UNSUPPORTED).
+ * Thread 0 of decision workgroup g < SMCSD_STAMP_WGS (a sequence or a tree)
+ * records at its k-th event (k < SMCSD_STAMP_EVENTS) the GPU's constant
+ * 100 MHz clock and a code naming the phase that just ended (0: the
+ * workgroup's start).  The stamps persist on the device, one set per process,
+ * until cleared; later calls overwrite the workgroups they run.
+ *   host_dst   NULL, or host memory receiving the first `bytes` bytes of the
+ *              uint64 array [SMCSD_STAMP_WGS][SMCSD_STAMP_EVENTS][2] (clock,
+ *              code); unwritten events read 0.
+ *   clear      nonzero: zero every stamp after the copy.
+ * Synchronous: call it when the timed calls have finished (after a device
+ * synchronisation).  Returns SMCSD_ERR_HIP when a copy fails.
+ */
+int32_t smcsd_phase_stamps(void* host_dst, size_t bytes, int32_t clear);
 
 /*
  * Workspace bytes sd_verify needs for these sizes (0 when B == 0).

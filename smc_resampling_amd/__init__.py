@@ -22,7 +22,7 @@ __all__ = [
     "new_workspace", "time_next_call", "smc_pages_workspace_bytes", "smc_pages_append", "smc_pages_resample",
     "draft_sample_workspace_bytes", "prepare_draft_sample", "draft_sample", "pacer_lengths",
     "tree_verify_workspace_bytes", "prepare_tree_verify", "tree_verify", "TREE_MAX_NODES", "read_ceiling",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "phase_stamps", "STAMP_WGS", "STAMP_EVENTS",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +37,7 @@ FLAG_PAGES_FULL, FLAG_PAGES_EXHAUSTED = 32, 64
 WORKSPACE_ALIGN = 256
 TREE_MAX_NODES = 256
 NOALLOC_SCRATCH_BYTES = 32 << 20
+STAMP_WGS, STAMP_EVENTS = 4096, 16
 
 _P, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -45,6 +46,7 @@ _SIGNATURES = {
     "smcsd_status_string": ([_I32], ctypes.c_char_p),
     "smcsd_time_next_call": ([_P, _P, _P, _P], None),
     "smcsd_read_ceiling": ([_P, _SZ, _P, _SZ, _P, _P, _P, _P], _I32),
+    "smcsd_phase_stamps": ([_P, _SZ, _I32], _I32),
     "sd_verify_workspace_bytes": ([_I32, _I32, _I32, _I32, _I64], _SZ),
     "sd_verify": ([_I32, _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
     "smc_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32], _SZ),
@@ -117,6 +119,19 @@ def read_ceiling(a, b=None, *, sink=None, start=None, stop=None, stream=None):
                                    None if start is None else start.cuda_event,
                                    None if stop is None else stop.cuda_event, st))
     return sink
+
+
+def phase_stamps(clear: bool = False):
+    """The decision kernels' phase timestamps of a measurement build
+    (``smcsd_phase_stamps``): uint64 numpy array [STAMP_WGS, STAMP_EVENTS, 2]
+    of (100 MHz clock, phase code), 0 where nothing was recorded; ``clear``
+    zeroes them after the copy.  Raises SmcsdError on the library's own build,
+    which records none."""
+    import numpy as np
+
+    out = np.zeros((STAMP_WGS, STAMP_EVENTS, 2), dtype=np.uint64)
+    _check(_lib.smcsd_phase_stamps(out.ctypes.data, out.nbytes, 1 if clear else 0))
+    return out
 
 
 def status_string(code: int) -> str:

@@ -117,6 +117,11 @@ extern "C" {
 
 int32_t smcsd_abi_version(void) { return SMCSD_ABI_VERSION; }
 
+int32_t smcsd_phase_stamps(void* host_dst, size_t bytes, int32_t clear) {
+  const hipError_t e = smcsd::phase_stamps(host_dst, bytes, clear != 0);
+  return e == hipSuccess ? SMCSD_OK : e == hipErrorNotSupported ? SMCSD_ERR_UNSUPPORTED : SMCSD_ERR_HIP;
+}
+
 void smcsd_time_next_call(void* stream_start, void* stream_stop, void* tail_start, void* tail_stop) {
   t_timers = {static_cast<hipEvent_t>(stream_start), static_cast<hipEvent_t>(stream_stop),
               static_cast<hipEvent_t>(tail_start), static_cast<hipEvent_t>(tail_stop)};

@@ -47,6 +47,27 @@ namespace smcsd {
 #define SMCSD_TEMPORAL_ROWS 0
 #endif
 
+// Phase timestamps of the decision kernels, for measurement builds only
+// (-DSMCSD_PHASE_STAMPS=1; the library's build compiles every stamp away).
+// Thread 0 of workgroup g < SMCSD_STAMP_WGS records, at its k-th event, the
+// 100 MHz s_memrealtime clock and a code naming the phase that just ended
+// (STAMP_* in launch.h); smcsd_phase_stamps copies them out.
+#ifndef SMCSD_PHASE_STAMPS
+#define SMCSD_PHASE_STAMPS 0
+#endif
+#if SMCSD_PHASE_STAMPS
+__device__ unsigned long long g_stamps[SMCSD_STAMP_WGS * SMCSD_STAMP_EVENTS * 2];
+__device__ __forceinline__ void stamp(int k, unsigned code) {
+  if (threadIdx.x == 0 && blockIdx.x < SMCSD_STAMP_WGS && k < SMCSD_STAMP_EVENTS) {
+    const size_t i = ((size_t)blockIdx.x * SMCSD_STAMP_EVENTS + k) * 2;
+    g_stamps[i] = __builtin_amdgcn_s_memrealtime();
+    g_stamps[i + 1] = code;
+  }
+}
+#else
+__device__ __forceinline__ void stamp(int, unsigned) {}
+#endif
+
 constexpr int MAXR = 2 * SMCSD_MAX_K + 1;  // rows per group
 constexpr int MAX_TILES = 256;             // tiles per row (V <= 524288)
 
@@ -783,6 +804,8 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   const int64_t b = blockIdx.x;
   const int ntiles = s.ntiles;
   const Group G = group_of(b, s.K, s.offsets, s.rows_d);
+  int ev = 0;
+  stamp(ev++, 0);
   if (s.offsets && threadIdx.x == 0) {
     uint32_t bad = G.ok ? 0u : FLAG_BAD_INPUT;
     if (b == 0 && s.offsets[0] != 0) bad = FLAG_BAD_INPUT;
@@ -808,6 +831,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   const float z = token_logit<DT, SD_BLOCK>(s, G, b, xt, &ok);
   store_tokens<SD_BLOCK>(z, ok, uj, kb, L);
   __syncthreads();
+  stamp(ev++, STAMP_SD_MERGED);
   uint32_t fl = 0;
   // accept test up to the first rejection
   if (wave == 0) {
@@ -835,6 +859,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     if (lane == 0) L.n = n;
   }
   __syncthreads();
+  stamp(ev++, STAMP_SD_TESTED);
   const int n = L.n;
   const raw* trow = group_row<raw>(s, G, b, n);
   int y;
@@ -843,6 +868,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     const RowStat sk = stat_of(L, kb);
     if (!sk.ok) fl |= FLAG_NONFINITE;
     y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, sk.M, (double)ufin, bnp, bper, L, fl);
+    stamp(ev++, STAMP_SD_BONUS_DRAWN);
   } else {
     // residual max(0, p_n - q_n): each wavefront weighs its tiles and keeps
     // the weights of the last one in registers for the search
@@ -863,6 +889,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
       if (lane == 0) L.W[t] = (double)m;
     }
     __syncthreads();
+    stamp(ev++, STAMP_SD_RESIDUAL_PASS);
     if (wave == 0) {
       auto wt = [&](int k) -> double { return L.W[k]; };
       double before = 0.0, target = 0.0, total = 0.0;
@@ -881,6 +908,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
       }
     }
     __syncthreads();
+    stamp(ev++, STAMP_SD_LOCATED);
     const int tt = L.sel;
     if (tt >= 0) {
       // the wavefront that weighed tile tt draws inside it
@@ -903,6 +931,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
         if (lane == 0) L.y = tt * TILE + idx;
       }
       __syncthreads();
+      stamp(ev++, STAMP_SD_RESIDUAL_DRAWN);
       y = L.y;
     } else {
       // p_n and q_n agree to rounding: draw from p_n with the same uniform
@@ -910,6 +939,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
       stage_partials<SD_BLOCK>(pg + (int64_t)n * s.nseg, s.nseg, L);
       __syncthreads();
       y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, st.M, (double)ufin, s.nseg, s.seg, L, fl);
+      stamp(ev++, STAMP_SD_FALLBACK_DRAWN);
     }
   }
   or_flags(fl, L);
@@ -1094,6 +1124,8 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int ntiles = s.ntiles;
+  int ev = 0;
+  stamp(ev++, 0);
   const int64_t n0 = a.node_off[b], d0 = a.draft_off[b];
   const int64_t M64 = a.node_off[b + 1] - n0, D64 = a.draft_off[b + 1] - d0;
   // offsets that do not describe a tree inside the buffers: nothing is read
@@ -1128,6 +1160,7 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     L.ut[tid] = un;
   }
   __syncthreads();
+  stamp(ev++, STAMP_TREE_MERGED);
   // tree order: the root's parent is -1, every other parent comes earlier;
   // mark the nodes that have children
   bool badn = false;
@@ -1172,6 +1205,7 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     L.xok[tid] = xv;
   }
   __syncthreads();
+  stamp(ev++, STAMP_TREE_GATHERED);
   uint32_t fl = 0;
   const double ufin = (double)L.ut[0];
   int u = 0, depth = 0, y = 0;
@@ -1188,9 +1222,11 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
       // a leaf: the bonus token from p_u (its tile or segment partials)
       int bnp, bper;
       const float2* bp = bonus_partials(s, n0 + u, n0 + u, 0, &bnp, &bper);
+      stamp(ev++, STAMP_TREE_LEAF);
       stage_partials<TREE_BLOCK>(bp, bnp, L.t);
       __syncthreads();
       y = draw_softmax<DT, VL, TREE_WAVES>(trow, s, s.c, st.M, ufin, bnp, bper, L.t, fl);
+      stamp(ev++, STAMP_TREE_DRAWN);
       break;
     }
     const RowStat sd = stat_at(L.Md, L.Sd, L.lSd, dr);
@@ -1290,6 +1326,7 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
         nrej++;
       }
     }
+    stamp(ev++, (next >= 0 ? STAMP_TREE_ACCEPTED : STAMP_TREE_REJECTED) + (unsigned)min(nrej, 99));
     if (next >= 0) {
       u = next;
       depth++;
@@ -1343,6 +1380,7 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     }
     lds_barrier();
     y = L.t.y;
+    stamp(ev++, STAMP_TREE_DRAWN);
     break;
   }
   or_flags(fl, L.t);
@@ -1703,6 +1741,27 @@ hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipS
 template <typename DT, bool VL>
 static const void* tree_tail_kernel() {
   return kptr(&k_tree_tail<DT, VL>);
+}
+
+hipError_t phase_stamps(void* dst, size_t bytes, bool clear) {
+#if SMCSD_PHASE_STAMPS
+  constexpr size_t kBytes = sizeof(g_stamps);
+  if (dst) {
+    hipError_t e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_stamps), bytes < kBytes ? bytes : kBytes, 0,
+                                       hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+  }
+  if (clear) {
+    static const unsigned long long zeros[SMCSD_STAMP_WGS * SMCSD_STAMP_EVENTS * 2] = {};
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_stamps), zeros, kBytes, 0, hipMemcpyHostToDevice);
+  }
+  return hipSuccess;
+#else
+  (void)dst;
+  (void)bytes;
+  (void)clear;
+  return hipErrorNotSupported;
+#endif
 }
 
 hipError_t launch_tree(const TreeArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {

@@ -93,6 +93,25 @@ struct KernelTimers {
 hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, bool pw, Plan* p);
 // Each launches the streaming kernel, then the tail kernel; with timers, the
 // launches carry the events.
+// Phase codes of the measurement build's timestamps (each names the phase that
+// ends at its stamp; 0 marks a workgroup's start).
+enum : unsigned {
+  STAMP_SD_MERGED = 1,          // statistics merged, token logits gathered
+  STAMP_SD_TESTED = 2,          // accept tests up to the first rejection
+  STAMP_SD_BONUS_DRAWN = 3,     // every draft accepted: the bonus draw
+  STAMP_SD_RESIDUAL_PASS = 4,   // a rejection: the residual pass over the row pair
+  STAMP_SD_LOCATED = 5,         // the residual draw's tile located
+  STAMP_SD_RESIDUAL_DRAWN = 6,  // the search inside that tile
+  STAMP_SD_FALLBACK_DRAWN = 7,  // zero residual: the draw from p_n
+  STAMP_TREE_MERGED = 10,       // parents read, statistics merged
+  STAMP_TREE_GATHERED = 11,     // draft rows ranked, token logits gathered
+  STAMP_TREE_ACCEPTED = 100,    // + r: a level whose child was accepted after r rejections
+  STAMP_TREE_REJECTED = 200,    // + r: a level whose r children were all rejected
+  STAMP_TREE_LEAF = 300,        // a leaf reached
+  STAMP_TREE_DRAWN = 400,       // the final draw (at a leaf, or from the last residual)
+};
+hipError_t phase_stamps(void* dst, size_t bytes, bool clear);
+
 hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);
 hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);
 hipError_t launch_tree(const TreeArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t);

@@ -136,6 +136,18 @@ def test_csr_call_needs_k(s):
         s.prepare_sd_verify(t, d, torch.zeros(3, dtype=torch.int32), torch.zeros(5), 1.0, draft_offsets=off)
 
 
+def test_phase_stamps_are_absent_from_the_library_build(s):
+    """The library's own build records no phase timestamps: the measurement
+    aid answers SMCSD_ERR_UNSUPPORTED and touches nothing."""
+    L = s.lib()
+    assert L.smcsd_phase_stamps(None, 0, 1) == s.SMCSD_ERR_UNSUPPORTED
+    buf = (ctypes.c_uint64 * 4)(7, 7, 7, 7)
+    assert L.smcsd_phase_stamps(ctypes.addressof(buf), ctypes.sizeof(buf), 0) == s.SMCSD_ERR_UNSUPPORTED
+    assert list(buf) == [7, 7, 7, 7]
+    with pytest.raises(s.SmcsdError):
+        s.phase_stamps()
+
+
 def test_read_ceiling_rejects_bad_buffers(s):
     L = s.lib()
     sink = ctypes.c_void_p(1 << 40)
