@@ -43,14 +43,42 @@ KERNEL_SOURCES = [os.path.join(ROOT, "include", "smcsd.h")] + sorted(
                                                                                           "csrc")))
 
 
+def strip_c_comments(text: str) -> str:
+    """C/C++ source without its comments (string and character literals kept
+    whole) and without trailing blanks and empty lines: what the compiler sees
+    of the code, so that editing a comment leaves it unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":  # a literal: copy it through its closing quote
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (l.rstrip() for l in "".join(out).split("\n"))
+    return "\n".join(l for l in lines if l)
+
+
 def kernel_sources_hash() -> str:
-    """sha256 of the library's kernel sources (the header and csrc/*)."""
+    """sha256 of the library's kernel sources (the header and csrc/*), comments
+    left out: a code change changes it, a comment edit does not."""
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + strip_c_comments(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -101,9 +101,10 @@ __device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait until every memory operation this wavefront issued has completed.  A
-// workgroup barrier orders LDS only: the counters other wavefronts read after
-// one must have reached the cache first.
+// Wait until every memory operation this wavefront issued has completed: the
+// count updates are device-scope atomics performed at the L2, and the
+// __syncthreads that follows each use (a workgroup-scope release and acquire
+// around the barrier) then orders them before the other wavefronts' reads.
 __device__ __forceinline__ void mem_done() {
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
