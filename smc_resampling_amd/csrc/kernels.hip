@@ -993,18 +993,28 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_draw_tail(SdArgs a) {
 // node u, child c is accepted iff u_c < r(x_c) / q_u(x_c) with r the running
 // distribution (p_u, then max(0, r - q_u) / Z after each rejected child).  A
 // rejection costs one pass of the whole workgroup over u's row pair: the
-// residual chain is rebuilt elementwise from p_u and q_u with the masses Z of
-// the earlier rejections, and the tile masses of max(0, r - q_u) give the new
-// Z.  The walk ends at a leaf (bonus draw from p_leaf, as in sd_verify) or
-// when every child of u is rejected (inverse-CDF draw from the last pass's
-// weights: the tile is located from the pass's tile masses, then reloaded and
-// searched).
+// first rebuilds max(0, p_u - q_u) elementwise, a later one continues from
+// the previous pass's weights (held in LDS where they fit, else rebuilt from
+// p_u and q_u with the masses Z of the earlier rejections), and the tile
+// masses of max(0, r - q_u) give the new Z.  The walk ends at a leaf (bonus
+// draw from p_leaf, as in sd_verify) or when every child of u is rejected
+// (inverse-CDF draw from the last pass's weights: the tile is located from
+// the pass's tile masses, then searched).
 // ---------------------------------------------------------------------------
 constexpr int TREE_MAX = SMCSD_TREE_MAX_NODES;
 // 8 wavefronts: with 2 waves per SIMD the walk keeps its state in registers
 // (no scratch spills, whose stores every barrier would wait for)
 constexpr int TREE_WAVES = 8;
 constexpr int TREE_BLOCK = TREE_WAVES * WAVE;
+// Tiles whose residual weights a node's passes keep in LDS (bf16 with 16-byte
+// loads: 16 tiles, 128 KiB, every tile up to V = 32768; the walk's one
+// workgroup per CU leaves that LDS unused): the node's next pass continues the
+// residual chain from them (one exponential a logit pair, no target-row
+// loads), and the final draw reads its tile's weights there.
+template <typename DT, bool VL>
+constexpr int tree_held_tiles() {
+  return DT::VEC == 8 && VL ? 16 : 0;
+}
 
 struct TreeLds {
   TailLds t;  // draw scratch: staged partials, tile masses, located tile
@@ -1118,7 +1128,12 @@ __device__ __forceinline__ void tree_weights(const Raw<DT>& rt, const Raw<DT>& r
 template <typename DT, bool VL>
 __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
   using raw = typename DT::raw;
+  constexpr int HT = tree_held_tiles<DT, VL>();
   __shared__ TreeLds L;
+  // residual weights of the node's last pass, tiles < HT, four elements a
+  // 16-byte slot: [tile][element / 4][lane]
+  constexpr int Q4 = PER_LANE / 4;
+  __shared__ float4 HW[HT > 0 ? HT * Q4 * WAVE : 1];
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   const int tid = threadIdx.x;
@@ -1247,6 +1262,46 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
       m = wave_sum(m);
       if (lane == 0) L.t.W[t] = (double)m;
     };
+    // The weights of tile t in a pass with nr earlier rejections (sub:
+    // max(0, r - q), else r).  A sub pass whose previous rejection left mass
+    // (Z > 0) continues from that pass's weights W held in LDS: r = W / Z,
+    // w = max(0, r - q), the same operations as the chain rebuilt from p and
+    // q, with one exponential a logit pair instead of two.  Every sub pass
+    // stores its weights of the held tiles for the next.  Tile t is always weighed by wavefront
+    // t % TREE_WAVES, so its LDS slice needs no barrier.
+    auto weigh = [&](int t, Raw<DT>& rt, Raw<DT>& rd, bool cont, int nr, bool sub, float (&w)[PER_LANE]) {
+      mask_tail<DT>(rd, s.V, t, lane);
+      if (cont) {
+        const float z = L.iz[nr - 1];
+#pragma unroll
+        for (int i = 0; i < Q4; i++) {
+          const float4 h = HW[(t * Q4 + i) * WAVE + lane];
+          w[4 * i] = h.x;
+          w[4 * i + 1] = h.y;
+          w[4 * i + 2] = h.z;
+          w[4 * i + 3] = h.w;
+        }
+#pragma unroll
+        for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
+          float q[DT::VEC];
+          unpack<DT>(rd, ch, q);
+#pragma unroll
+          for (int k = 0; k < DT::VEC; k++) {
+            const int e = ch * DT::VEC + k;
+            const float qk = __builtin_amdgcn_exp2f(fmaf(q[k], s.c, -Ad));
+            w[e] = fmaxf(w[e] * z - qk, 0.0f);
+          }
+        }
+      } else {
+        mask_tail<DT>(rt, s.V, t, lane);
+        tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, nr, sub, w);
+      }
+      if (HT > 0 && sub && t < HT) {
+#pragma unroll
+        for (int i = 0; i < Q4; i++)
+          HW[(t * Q4 + i) * WAVE + lane] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+      }
+    };
     // one pass over u's row pair: every tile's mass into L.t.W; with bf16
     // 16-byte loads (registers to spare) a wavefront issues the loads of two
     // of its tiles before weighing either, so a 16-tile pair costs one round
@@ -1261,22 +1316,23 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
         }
         return;
       }
+      const bool cont = HT > 0 && sub && nr > 0 && L.iz[nr - 1] > 0.0f;
       for (int t0 = wave; t0 < ntiles; t0 += 2 * TREE_WAVES) {
         const int t1 = t0 + TREE_WAVES;
         const int t1c = min(t1, ntiles - 1);  // a tile of the row either way
+        const bool c0 = cont && t0 < HT, c1 = cont && t1 < HT;
+        // both rows' tiles are loaded even where the weights continue from
+        // LDS: the loads stay one unconditional batch (measured faster than
+        // skipping the target row's, which comes from cache then)
         Raw<DT> rt0 = load_raw<DT, VL, 0>(trow, s.V, t0, lane);
         Raw<DT> rd0 = load_raw<DT, VL, 0>(drw, s.V, t0, lane);
         Raw<DT> rt1 = load_raw<DT, VL, 0>(trow, s.V, t1c, lane);
         Raw<DT> rd1 = load_raw<DT, VL, 0>(drw, s.V, t1c, lane);
         float w[PER_LANE];
-        mask_tail<DT>(rt0, s.V, t0, lane);
-        mask_tail<DT>(rd0, s.V, t0, lane);
-        tree_weights<DT>(rt0, rd0, At, Ad, s.c, L.iz, nr, sub, w);
+        weigh(t0, rt0, rd0, c0, nr, sub, w);
         store_mass(t0, w);
         if (t1 < ntiles) {
-          mask_tail<DT>(rt1, s.V, t1, lane);
-          mask_tail<DT>(rd1, s.V, t1, lane);
-          tree_weights<DT>(rt1, rd1, At, Ad, s.c, L.iz, nr, sub, w);
+          weigh(t1, rt1, rd1, c1, nr, sub, w);
           store_mass(t1, w);
         }
       }
@@ -1362,10 +1418,22 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     lds_barrier();
     const int tt = L.t.sel;
     if (wave == tt % TREE_WAVES) {
-      // the located tile's weights, recomputed exactly as its pass did (the
-      // wavefront that weighed it reads it again, likely from its cache)
+      // the located tile's weights as its pass weighed them (held in LDS, or
+      // recomputed the same way by the wavefront that weighed it, which reads
+      // the tile again, likely from its cache)
       float w[PER_LANE];
-      tile_w(tt, last, !zero, w);
+      if (HT > 0 && !zero && tt < HT) {
+#pragma unroll
+        for (int i = 0; i < Q4; i++) {
+          const float4 h = HW[(tt * Q4 + i) * WAVE + lane];
+          w[4 * i] = h.x;
+          w[4 * i + 1] = h.y;
+          w[4 * i + 2] = h.z;
+          w[4 * i + 3] = h.w;
+        }
+      } else {
+        tile_w(tt, last, !zero, w);
+      }
       auto wfn = [&](int ch, float (&x)[DT::VEC]) {
 #pragma unroll
         for (int k = 0; k < DT::VEC; k++) x[k] = w[ch * DT::VEC + k];
