@@ -12,7 +12,11 @@ a gap in the pins unless it is equivalent to the original (for example an
 allocation guard `n > 0 ? n : 1` turned into `n >= 0`) or only reads out of
 bounds.
 
-Usage: python tests/oracle_mutation_sweep.py [--jobs 8] [--timeout 120]
+With --sanitize each mutant is built with gcc -fsanitize=address,undefined
+and run with the AddressSanitizer runtime preloaded, so a mutant that reads
+or writes out of bounds fails even where the values it reads would pass.
+
+Usage: python tests/oracle_mutation_sweep.py [--jobs 8] [--timeout 120] [--sanitize]
 Not collected by pytest: a full sweep takes several minutes on 8 cores.
 """
 import argparse
@@ -65,7 +69,7 @@ def mutants(lines):
     return out
 
 
-def run_one(lines, site, timeout):
+def run_one(lines, site, timeout, asan_rt=None):
     i, _, new = site
     mutated = list(lines)
     mutated[i] = new
@@ -75,15 +79,21 @@ def run_one(lines, site, timeout):
         with open(src, "w") as f:
             f.write("\n".join(mutated))
         # the oracle's own build line (gcc -O2 -std=c99, IEEE semantics), quiet
-        cc = subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-w", "-o", so, src, "-lm"],
+        san = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"] if asan_rt else ["-O2"]
+        cc = subprocess.run(["gcc", *san, "-std=c99", "-fPIC", "-shared", "-w", "-o", so, src, "-lm"],
                             capture_output=True)
         if cc.returncode:
             return "nocompile"
+        env = dict(os.environ)
+        if asan_rt:
+            env.update(LD_PRELOAD=asan_rt, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1")
         try:
             r = subprocess.run([sys.executable, os.path.join(HERE, "mutant_runner.py"), so], capture_output=True,
-                               text=True, timeout=timeout)
+                               text=True, timeout=timeout, env=env)
         except subprocess.TimeoutExpired:
             return "timeout"
+        if "Sanitizer" in r.stderr:
+            return "sanitizer"
     if r.returncode == 0:
         return "survived"
     return "caught" if "caught" in r.stdout else f"crash({r.returncode})"
@@ -93,13 +103,17 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("--timeout", type=int, default=120)
+    ap.add_argument("--sanitize", action="store_true")
     args = ap.parse_args()
+    asan_rt = None
+    if args.sanitize:
+        asan_rt = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
     with open(oracle.SRC) as f:
         lines = f.read().split("\n")
     sites = mutants(lines)
     print(f"{len(sites)} mutants of {os.path.basename(oracle.SRC)}", flush=True)
     with ThreadPoolExecutor(args.jobs) as ex:
-        results = list(ex.map(lambda s: run_one(lines, s, args.timeout), sites))
+        results = list(ex.map(lambda s: run_one(lines, s, args.timeout, asan_rt), sites))
     print(dict(collections.Counter(results)))
     for (i, pat, new), res in zip(sites, results):
         if res == "survived":
