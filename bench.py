@@ -38,47 +38,66 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = [os.path.join(ROOT, "include", "smcsd.h")] + sorted(
-    os.path.join(ROOT, "smc_resampling_amd", "csrc", f) for f in os.listdir(os.path.join(ROOT, "smc_resampling_amd",
-                                                                                          "csrc")))
+def _elf_sections(d: bytes) -> dict:
+    """name -> (offset, size) of the sections of a 64-bit little-endian ELF image."""
+    import struct
+
+    if d[:4] != b"\x7fELF" or d[4] != 2 or d[5] != 1:
+        raise ValueError("not a 64-bit little-endian ELF image")
+    shoff, = struct.unpack_from("<Q", d, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", d, 0x3A)
+    entry = lambda i: struct.unpack_from("<IIQQQQ", d, shoff + i * shentsize)  # noqa: E731
+    strtab = entry(shstrndx)[4]
+    out = {}
+    for i in range(shnum):
+        name, _, _, _, off, size = entry(i)
+        end = d.index(b"\0", strtab + name)
+        out[d[strtab + name:end].decode()] = (off, size)
+    return out
 
 
-def strip_c_comments(text: str) -> str:
-    """C/C++ source without its comments (string and character literals kept
-    whole) and without trailing blanks and empty lines: what the compiler sees
-    of the code, so that editing a comment leaves it unchanged."""
-    out, i, n = [], 0, len(text)
-    while i < n:
-        c = text[i]
-        if c in "\"'":  # a literal: copy it through its closing quote
-            j = i + 1
-            while j < n and text[j] != c:
-                j += 2 if text[j] == "\\" else 1
-            out.append(text[i:j + 1])
-            i = j + 1
-        elif text.startswith("//", i):
-            j = text.find("\n", i)
-            i = n if j < 0 else j
-        elif text.startswith("/*", i):
-            j = text.find("*/", i + 2)
-            out.append(" ")
-            i = n if j < 0 else j + 2
-        else:
-            out.append(c)
-            i += 1
-    lines = (l.rstrip() for l in "".join(out).split("\n"))
-    return "\n".join(l for l in lines if l)
-
-
-def kernel_sources_hash() -> str:
-    """sha256 of the library's kernel sources (the header and csrc/*), comments
-    left out: a code change changes it, a comment edit does not."""
+def kernel_code_hash(lib_path: str = None) -> str:
+    """sha256 of the device code a build of the library holds: for each
+    amdgcn code object of its offload bundles (section .hip_fatbin, one bundle
+    per translation unit), its target and its .text, .rodata (kernel
+    descriptors) and .note (kernel metadata: registers, LDS, ...) sections.  A change to any kernel's instructions,
+    descriptor or resources changes it; comments, host code and the names the
+    compiler makes up per build do not."""
     import hashlib
+    import struct
 
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, encoding="utf-8") as fh:
-            h.update(os.path.basename(f).encode() + b"\0" + strip_c_comments(fh.read()).encode())
+    if lib_path is None:
+        lib_path = os.environ.get("SMCSD_LIBRARY") or os.path.join(ROOT, "smc_resampling_amd", "libsmcsd.so")
+    with open(lib_path, "rb") as f:
+        d = f.read()
+    off, size = _elf_sections(d)[".hip_fatbin"]
+    fat = d[off:off + size]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    if not fat.startswith(magic):
+        raise ValueError("unexpected offload bundle format")
+    h, nobj = hashlib.sha256(), 0
+    start = 0
+    while start >= 0:  # one bundle per translation unit, one after another
+        b = fat[start:]
+        n, = struct.unpack_from("<Q", b, len(magic))
+        pos, end = len(magic) + 8, 0
+        for _ in range(n):
+            eoff, esize, tlen = struct.unpack_from("<QQQ", b, pos)
+            triple = b[pos + 24:pos + 24 + tlen]
+            pos += 24 + tlen
+            end = max(end, eoff + esize)
+            if b"amdgcn" not in triple or esize == 0:
+                continue
+            elf = b[eoff:eoff + esize]
+            secs = _elf_sections(elf)
+            h.update(triple + b"\0")
+            for name in (".text", ".rodata", ".note"):
+                so, ss = secs.get(name, (0, 0))
+                h.update(name.encode() + b"\0" + elf[so:so + ss])
+            nobj += 1
+        start = fat.find(magic, start + max(end, len(magic)))
+    if nobj == 0:
+        raise ValueError("no amdgcn code object in the offload bundles")
     return h.hexdigest()
 
 
@@ -111,7 +130,7 @@ def summarize(dirs, copy_bytes=None):
     (--pmc), with HBM traffic per call of the streaming kernel and of the
     decision path (CALL_KERNELS) when the directories hold FETCH_SIZE /
     WRITE_SIZE and a copy of `copy_bytes` calibrates them."""
-    out = [f"kernel_sources_sha256: {kernel_sources_hash()}"]
+    out = [f"kernel_code_sha256: {kernel_code_hash()}"]
     avg = {}  # (kernel, counter) -> KiB per dispatch
     peak = {}  # (kernel, counter) -> largest single dispatch
     for d in dirs:
@@ -183,7 +202,7 @@ def traffic_from_profiles(workload):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_sources_sha256") != kernel_sources_hash():
+    if fields.get("kernel_code_sha256") != kernel_code_hash():
         return None, None
     get = lambda k: float(fields[k]) if k in fields else None  # noqa: E731
     return get("traffic_bytes_per_call k_stream"), get("traffic_bytes_per_call decision")
@@ -256,7 +275,7 @@ def environment():
 
     p = torch.cuda.get_device_properties(0)
     env = {"device": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
-           "hip": torch.version.hip, "torch": torch.__version__}
+           "hip": torch.version.hip, "torch": torch.__version__, "kernel_code_sha256": kernel_code_hash()}
     try:  # the shader clock the runtime reports (kHz)
         lib = ctypes.CDLL("libamdhip64.so")
         for key, attr in (("clock_mhz", 5), ("memory_clock_mhz", 60)):  # hipDeviceAttribute{,Memory}ClockRate

@@ -1400,15 +1400,9 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     }
     if (wave == 0) {
       auto wt = [&](int k) -> double { return L.t.W[k]; };
-      double bef = 0.0, target = 0.0, tot = 0.0;
+      double bef = 0.0, target = 0.0;
       int lastk = -1;
-      const int k = locate(
-          ntiles, wt, 0.0,
-          [&](double tt) {
-            tot = tt;
-            return ufin * tt;
-          },
-          lane, &bef, &target, &lastk);
+      const int k = locate(ntiles, wt, 0.0, [&](double tt) { return ufin * tt; }, lane, &bef, &target, &lastk);
       if (lane == 0) {
         L.t.sel = k >= 0 ? k : (lastk >= 0 ? lastk : 0);
         L.t.clamp = k < 0;

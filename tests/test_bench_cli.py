@@ -1,4 +1,4 @@
-"""bench.py on the CPU: the one-GPU refusal and the hash tying profiles to the kernel sources."""
+"""bench.py on the CPU: the one-GPU refusal and the hash tying profiles to the built kernels."""
 import json
 import os
 import subprocess
@@ -16,15 +16,39 @@ def test_more_than_one_gpu_is_refused():
         assert "one GPU" in msg["error"]
 
 
-def test_source_hash_ignores_comments_only():
-    """The hash that ties a profile to the kernel sources follows the code:
-    comments (line and block) and blank lines drop out, literals stay whole."""
+def _tiny_library(tmp_path, name, kernel_body, host_comment=""):
+    """Two translation units, each with a kernel, the second's body given."""
+    first = tmp_path / f"{name}_1.hip"
+    first.write_text("#include <hip/hip_runtime.h>\n"
+                     "__global__ void k1(float* x) { x[threadIdx.x] += 1.0f; }\n")
+    second = tmp_path / f"{name}_2.hip"
+    second.write_text("#include <hip/hip_runtime.h>\n"
+                      f"// {host_comment}\n"
+                      f"__global__ void k2(float* x) {{ {kernel_body} }}\n"
+                      'extern "C" int host_entry(int v) { return v + 1; }\n')
+    so = str(tmp_path / f"lib{name}.so")
+    subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", str(first), str(second), "-o",
+                           so], stderr=subprocess.DEVNULL)
+    return so
+
+
+def test_kernel_code_hash_follows_the_device_code(tmp_path):
+    """The hash that ties a profile to the kernels is taken over the built
+    device code (.text, .rodata, .note of every amdgcn code object, one bundle
+    per translation unit): two builds of the same sources agree although the
+    bundles' bytes differ, a comment or host-code edit leaves it alone, and a
+    change to a kernel in any translation unit moves it."""
+    import shutil
+
+    if shutil.which("hipcc") is None:
+        import pytest
+
+        pytest.skip("hipcc is not installed")
     sys.path.insert(0, ROOT)
     import bench
 
-    code = 'int f(int x) {\n  return x + 1;  // one\n}\nconst char* s = "a // b /* c */";\nchar q = \'"\';\n'
-    commented = '/* header\n   block */\nint f(int x) {  // f\n\n  return x + 1;  // another note\n}\n' \
-                'const char* s = "a // b /* c */";\nchar q = \'"\';  /* q */\n'
-    assert bench.strip_c_comments(code) == bench.strip_c_comments(commented)
-    assert "a // b /* c */" in bench.strip_c_comments(code)
-    assert bench.strip_c_comments(code) != bench.strip_c_comments(code.replace("x + 1", "x + 2"))
+    body = "x[threadIdx.x] *= 2.0f;"
+    a = bench.kernel_code_hash(_tiny_library(tmp_path, "a", body))
+    b = bench.kernel_code_hash(_tiny_library(tmp_path, "b", body, host_comment="another comment"))
+    c = bench.kernel_code_hash(_tiny_library(tmp_path, "c", "x[threadIdx.x] *= 3.0f;"))
+    assert a == b and a != c and len(a) == 64
