@@ -228,12 +228,42 @@ def phase_name(code):
     return f"code {code}"
 
 
+def pool_stamps(stamp_sets, ncalls):
+    """Pool the phase stamps of several calls (each a uint64 array [workgroups,
+    events, 2] of (100 MHz clock, code), 0 where nothing was recorded): per
+    phase, named by the code of the stamp that ends it, the count and the
+    median and 90th percentile of its duration in us; each workgroup's span
+    from its first stamp to its last; and each call's span from its first
+    workgroup's start to its last stamp (median)."""
+    import numpy as np
+
+    phases, spans, kernel = {}, [], []
+    for st in stamp_sets:
+        st = np.asarray(st).astype(np.int64)
+        t, code = st[:, :, 0], st[:, :, 1]
+        live = np.nonzero(t[:, 0])[0]
+        if not len(live):
+            continue
+        ends = []
+        for g in live:
+            n = int(np.count_nonzero(t[g]))
+            for k in range(1, n):
+                phases.setdefault(int(code[g, k]), []).append((t[g, k] - t[g, k - 1]) / STAMP_CLOCK_MHZ)
+            spans.append((t[g, n - 1] - t[g, 0]) / STAMP_CLOCK_MHZ)
+            ends.append(t[g, n - 1])
+        kernel.append((max(ends) - t[live, 0].min()) / STAMP_CLOCK_MHZ)
+    if not spans:
+        return {"note": "no stamps: the workload's decision kernel records none, or the library was built without"}
+    q = lambda x: [round(float(v), 3) for v in np.percentile(x, [50, 90])]  # noqa: E731
+    return {"calls": ncalls, "workgroups": len(spans),
+            "phases_us_count_p50_p90": {phase_name(k): [len(v)] + q(v) for k, v in sorted(phases.items())},
+            "workgroup_span_us_p50_p90_max": q(spans) + [round(float(max(spans)), 3)],
+            "first_start_to_last_stamp_us_p50": round(float(np.median(kernel)), 3)}
+
+
 def phase_summary(calls, stream):
     """Replay `calls` one at a time on a measurement build and pool the
-    decision kernel's phase stamps: per phase (named by its end) the count and
-    the median and 90th percentile of its duration in us, and each workgroup's
-    span from its start to its last stamp."""
-    import numpy as np
+    decision kernel's phase stamps (pool_stamps)."""
     import torch
 
     import smc_resampling_amd as smcsd
@@ -243,30 +273,13 @@ def phase_summary(calls, stream):
         smcsd.phase_stamps(clear=True)
     except smcsd.SmcsdError:
         sys.exit("--phase-stamps needs a library built with -DSMCSD_PHASE_STAMPS=1, named by SMCSD_LIBRARY")
-    phases, spans, kernel = {}, [], []
+    sets = []
     for c in calls:
         with torch.cuda.stream(stream):
             c()
         torch.cuda.synchronize()
-        st = smcsd.phase_stamps(clear=True).astype(np.int64)
-        t, code = st[:, :, 0], st[:, :, 1]
-        live = np.nonzero(t[:, 0])[0]
-        if not len(live):
-            continue
-        for g in live:
-            n = int(np.count_nonzero(t[g]))
-            for k in range(1, n):
-                phases.setdefault(int(code[g, k]), []).append((t[g, k] - t[g, k - 1]) / STAMP_CLOCK_MHZ)
-            spans.append((t[g, n - 1] - t[g, 0]) / STAMP_CLOCK_MHZ)
-        ends = [t[g, int(np.count_nonzero(t[g])) - 1] for g in live]
-        kernel.append((max(ends) - t[live, 0].min()) / STAMP_CLOCK_MHZ)
-    if not spans:
-        return {"note": "no stamps: the workload's decision kernel records none, or the library was built without"}
-    q = lambda x: [round(float(v), 3) for v in np.percentile(x, [50, 90])]  # noqa: E731
-    return {"calls": len(calls), "workgroups": len(spans),
-            "phases_us_count_p50_p90": {phase_name(k): [len(v)] + q(v) for k, v in sorted(phases.items())},
-            "workgroup_span_us_p50_p90_max": q(spans) + [round(float(max(spans)), 3)],
-            "first_start_to_last_stamp_us_p50": round(float(np.median(kernel)), 3)}
+        sets.append(smcsd.phase_stamps(clear=True))
+    return pool_stamps(sets, len(calls))
 
 
 def environment():

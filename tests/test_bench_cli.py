@@ -52,3 +52,29 @@ def test_kernel_code_hash_follows_the_device_code(tmp_path):
     b = bench.kernel_code_hash(_tiny_library(tmp_path, "b", body, host_comment="another comment"))
     c = bench.kernel_code_hash(_tiny_library(tmp_path, "c", "x[threadIdx.x] *= 3.0f;"))
     assert a == b and a != c and len(a) == 64
+
+
+def test_phase_stamps_pool():
+    """The phase summary of --phase-stamps on a hand-made stamp set: durations
+    are the gaps between a workgroup's consecutive stamps (100 MHz clock),
+    named by the later stamp's code; unwritten events and workgroups drop out."""
+    import numpy as np
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    st = np.zeros((4, 16, 2), dtype=np.uint64)
+    # workgroup 0: start at 1000, merged (+200 = 2 us), tested (+50), bonus draw (+300)
+    st[0, :4] = [[1000, 0], [1200, 1], [1250, 2], [1550, 3]]
+    # workgroup 2: start at 1100, merged (+400 = 4 us), tested (+50), residual pass (+500)
+    st[2, :4] = [[1100, 0], [1500, 1], [1550, 2], [2050, 4]]
+    r = bench.pool_stamps([st], 1)
+    ph = r["phases_us_count_p50_p90"]
+    assert r["workgroups"] == 2 and r["calls"] == 1
+    assert ph[bench.phase_name(1)][0] == 2 and ph[bench.phase_name(1)][1] == 3.0  # median of 2 and 4 us
+    assert ph[bench.phase_name(2)] == [2, 0.5, 0.5]
+    assert ph[bench.phase_name(3)][:2] == [1, 3.0] and ph[bench.phase_name(4)][:2] == [1, 5.0]
+    assert r["workgroup_span_us_p50_p90_max"][2] == 9.5  # workgroup 2: 1100 -> 2050
+    assert r["first_start_to_last_stamp_us_p50"] == 10.5  # 1000 -> 2050
+    assert "note" in bench.pool_stamps([np.zeros((4, 16, 2), dtype=np.uint64)], 1)
+    assert bench.phase_name(102).endswith("after 2 rejections") and bench.phase_name(201).startswith("level: all 1")
