@@ -282,6 +282,37 @@ def phase_summary(calls, stream):
     return pool_stamps(sets, len(calls))
 
 
+def decision_stats(cfg, calls, outs, batches, W, nb, stream, reps=16):
+    """What the method decided on up to `reps` of the timed steps, replayed one
+    at a time after the timing: for SD and trees, the mean accepted draft
+    tokens and tokens emitted per sequence per step (accepted + the residual or
+    bonus token), and for linear SD the accepted fraction of draft positions;
+    for SMC, the fraction of prompts that resampled and the mean ESS over N."""
+    import numpy as np
+    import torch
+
+    n = min(reps, len(calls) - W)
+    acc, kb, ess, res = [], [], [], []
+    for s in range(W, W + n):
+        with torch.cuda.stream(stream):
+            calls[s]()
+        torch.cuda.synchronize()
+        if cfg.kind == "smc":
+            ess.append(outs["ess"].cpu().numpy())
+            res.append(outs["resampled"].cpu().numpy())
+        else:
+            acc.append(outs["num_accepted"].cpu().numpy().astype(np.int64))
+            kb.append(np.asarray(batches[s % nb].get("Kb", np.full(len(acc[-1]), cfg.K))))
+    if cfg.kind == "smc":
+        return {"steps": n, "resample_rate": float(np.mean(np.concatenate(res) != 0)),
+                "mean_ess_over_n": float(np.mean(np.concatenate(ess)) / cfg.N)}
+    a = np.concatenate(acc)
+    d = {"steps": n, "mean_accepted": float(a.mean()), "tokens_per_step": float(a.mean() + 1)}
+    if cfg.kind != "tree":
+        d["accepted_fraction"] = float(a.sum() / np.concatenate(kb).sum())
+    return d
+
+
 def environment():
     """The GPU and software the line was measured on."""
     import torch
@@ -704,6 +735,8 @@ def run_workload(args, config, steps_arg, with_cpu):
         f"({achieved:.0f} GB/s), decision kernel {tail_ms * 1e3:.2f} us, flags={flags}")
 
     stamps = phase_summary(calls[W:W + STAMP_CALLS], run_stream) if args.phase_stamps else None
+    decisions = (None if args.draft_sample or args.with_pages
+                 else decision_stats(cfg, calls, outs, batches, W, nb, run_stream))
 
     # ---------------- the plain-read ceiling at the call's byte count -------------
     # The library's read-only kernel (the streaming kernel's loads, no
@@ -790,6 +823,7 @@ def run_workload(args, config, steps_arg, with_cpu):
                      "decision_kernel_us_p10_p50_p90": spread(tail_each),
                      "eager_call_us_p10_p50_p90": spread(call_each)},
         "cpu_baseline": cpu,
+        "decisions": decisions,
     }
     if stamps is not None:
         line["phase_stamps"] = stamps
@@ -822,7 +856,7 @@ def main():
                            "frac_of_read_ceiling": r["frac_of_read_ceiling"],
                            "decision_kernel_us": r["decision_kernel_us"], "call_frac": r["call_frac"],
                            "traffic": r["traffic"], "call_traffic": r["call_traffic"],
-                           "status_flags": o["config"]["status_flags"]})
+                           "status_flags": o["config"]["status_flags"], "decisions": o["decisions"]})
         line["other_workloads"] = others
     line["environment"] = environment()
     line["environment"]["launch_floor_us"] = launch_floor()
