@@ -325,6 +325,8 @@ int32_t smc_reweight_resample_power(int32_t dtype, int32_t P, int32_t N, int32_t
  *   P, N, K, V) > SMCSD_NOALLOC_SCRATCH_BYTES) returns SMCSD_ERR_UNSUPPORTED
  *   before anything is enqueued; the 32-prompt x 64-particle step at K = 8,
  *   V = 151936 needs 23.4 MB.
+ *   The first call on a GPU looks up that GPU's array address (no allocation);
+ *   it may already be made under graph capture.
  *   Every call on one GPU shares that GPU's array, which keeps the last call's
  *   contents (nothing in it has to start at zero): calls that overlap on one
  *   GPU (two streams, two threads) race.  Calls in order on one stream do not.

@@ -58,3 +58,19 @@ def test_noalloc_refuses_calls_beyond_its_scratch():
                                                  f.data_ptr(), f.data_ptr(), f.data_ptr(), None, None, 0,
                                                  i.data_ptr(), i.data_ptr(), f.data_ptr(), i.data_ptr(), None, None)
     assert code == 2  # SMCSD_ERR_UNSUPPORTED
+
+
+def test_noalloc_first_call_under_graph_capture():
+    """A caller that captures from the start: in a fresh process, the entry
+    point's first call (which looks up the scratch's device address) is made
+    under graph capture; two replays equal the workspace call."""
+    import os
+    import subprocess
+    import sys
+
+    from gpu_util import say
+
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "noalloc_capture_child.py")
+    r = subprocess.run([sys.executable, "-u", child], capture_output=True, text=True, timeout=300)
+    say(r.stdout.strip().replace("\n", "; "))
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), (r.stdout + r.stderr)[-3000:]
