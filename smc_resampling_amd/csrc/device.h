@@ -318,7 +318,8 @@ __device__ __forceinline__ void unpack(const Raw<DT>& r, int c, float (&v)[DT::V
 // row statistics
 // ---------------------------------------------------------------------------
 struct RowStat {
-  float M;    // max over the row of z * c (log2 domain, c = log2(e) / T)
+  float M;    // offset of the row's z * c (log2 domain, c = log2(e) / T): at most
+              // the row's largest z c, and within 64 of it
   double S;   // sum over the row of 2^(z c - M)
   double lS;  // natural log of S
   bool ok;    // M finite and S finite and >= 1 (up to rounding)

@@ -9,8 +9,8 @@
 // segments of `seg` consecutive 2048-logit tiles; a unit is one (row,
 // segment).  Wavefront w of W streams units [U w / W, U (w+1) / W) with the
 // next tiles' loads in flight across unit, row and group boundaries, keeps
-// per-lane running softmax statistics over a unit and stores the unit's (max,
-// sum of exponentials).  A unit's partial depends on its logits alone, so
+// per-lane running softmax statistics over a unit and stores the unit's
+// (offset, sum of exponentials at that offset).  A unit's partial depends on its logits alone, so
 // equal rows get bitwise-equal statistics however the work is spread.  The
 // kernel holds nothing else, so it runs at high occupancy.
 //
@@ -122,38 +122,80 @@ __device__ __forceinline__ const raw* group_row(const StepArgs& a, const Group& 
 // ---------------------------------------------------------------------------
 // softmax partials
 // ---------------------------------------------------------------------------
-// Per-lane running statistics over a unit's tiles: m = max of z c (log2
-// domain), s = sum 2^(z c - m), rescaled when the lane's maximum grows.
+// Per-lane running statistics over a unit's tiles: s = sum 2^(z c - m) in the
+// log2 domain, with the offset m never above the largest z c folded so far
+// (so a row's sum is at least 1).
+//
+// lane_fold_tile_at_max folds a tile at the running maximum: m is the
+// largest z c so far, and s is rescaled when it grows.
 template <typename DT>
-__device__ __forceinline__ void lane_fold_tile(const Raw<DT>& cur, float c, float& m, float& s) {
-  float v[PER_LANE];
+__device__ __forceinline__ void lane_fold_tile_at_max(const Raw<DT>& cur, float c, float& m, float& s) {
+  // the values are unpacked from the raw tile where used (the raw registers
+  // stay live for the whole fold; 32 unpacked values would not fit beside them)
+  constexpr int CH = Raw<DT>::CHUNKS, VEC = DT::VEC;
+  float w[VEC];
+  float tm = -INFINITY;
+  bool nan = false;
 #pragma unroll
-  for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) {
-    float w[DT::VEC];
+  for (int ch = 0; ch < CH; ch++) {
     unpack<DT>(cur, ch, w);
 #pragma unroll
-    for (int k = 0; k < DT::VEC; k++) v[ch * DT::VEC + k] = w[k];
+    for (int k = 0; k < VEC; k++) {
+      tm = fmaxf(tm, w[k]);
+      nan |= w[k] != w[k];
+    }
   }
-  float tm = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < PER_LANE; e++) tm = fmaxf(tm, v[e]);
   const float mn = fmaxf(m, tm * c);
   if (mn > -INFINITY) {
     float acc = s * __builtin_amdgcn_exp2f(m - mn);  // 0 while m is -inf (NaN stays NaN)
 #pragma unroll
-    for (int e = 0; e < PER_LANE; e++) acc += __builtin_amdgcn_exp2f(fmaf(v[e], c, -mn));
+    for (int ch = 0; ch < CH; ch++) {
+      unpack<DT>(cur, ch, w);
+#pragma unroll
+      for (int k = 0; k < VEC; k++) acc += __builtin_amdgcn_exp2f(fmaf(w[k], c, -mn));
+    }
     s = acc;
     m = mn;
-  } else {
+  } else if (nan) {
     // every value so far is -inf or NaN: keep a NaN visible
-    bool nan = false;
-#pragma unroll
-    for (int e = 0; e < PER_LANE; e++) nan |= v[e] != v[e];
-    if (nan) s = __builtin_nanf("");
+    s = __builtin_nanf("");
   }
 }
 
-// Merge per-lane statistics (m2, s2) into (m, s).  A -inf maximum contributes
+// lane_fold_tile keeps the offset where it is while every term stays at most
+// kFoldCeil: the tile is folded at the current offset (unpack, fma, exp, add
+// per logit: no maximum, no rescale), and the fold stands if the sum stays at
+// most kFoldCeil.  A lane whose offset is still -inf (a unit's first tile)
+// offsets at the largest value of its first chunk.  Otherwise (a value more
+// than 64 above the offset in the log2 domain, a NaN or +inf, a first chunk of
+// -inf) the tile is folded again at the running maximum.
+constexpr float kFoldCeil = 18446744073709551616.0f;  // 2^64
+
+template <typename DT>
+__device__ __forceinline__ void lane_fold_tile(const Raw<DT>& cur, float c, float& m, float& s) {
+  constexpr int CH = Raw<DT>::CHUNKS, VEC = DT::VEC;
+  float w[VEC];
+  unpack<DT>(cur, 0, w);
+  float m0 = w[0];
+#pragma unroll
+  for (int k = 1; k < VEC; k++) m0 = fmaxf(m0, w[k]);
+  const float mo = m > -INFINITY ? m : m0 * c;
+  float acc = s;  // 0, or NaN, while m is -inf
+#pragma unroll
+  for (int ch = 0; ch < CH; ch++) {
+    if (ch) unpack<DT>(cur, ch, w);
+#pragma unroll
+    for (int k = 0; k < VEC; k++) acc += __builtin_amdgcn_exp2f(fmaf(w[k], c, -mo));
+  }
+  if (acc <= kFoldCeil) {  // false for NaN and +inf
+    s = acc;
+    m = mo;
+  } else {
+    lane_fold_tile_at_max<DT>(cur, c, m, s);
+  }
+}
+
+// Merge per-lane statistics (m2, s2) into (m, s).  A -inf offset contributes
 // its sum times 0, so a NaN sum stays NaN.
 __device__ __forceinline__ void lane_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
@@ -166,7 +208,8 @@ __device__ __forceinline__ void lane_merge(float& m, float& s, float m2, float s
   }
 }
 
-// The wavefront's (MC, S) from per-lane (m, s): MC = max m, S = sum s 2^(m - MC).
+// The wavefront's (MC, S) from per-lane (m, s): MC = the largest offset m,
+// S = sum s 2^(m - MC).
 // All -inf gives (-inf, 0); a NaN s stays NaN.
 __device__ __forceinline__ float2 wave_partial(float m, float s) {
   const float M = wave_max_nonnan(m);  // m comes from fmaxf: never NaN
@@ -438,7 +481,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(6, 6))) v
 struct TailLds {
   // per row of the group (and, for a power target, the bonus row at the
   // plain scale as row 2K+1)
-  float M[MAXR + 1];         // row max of z c (log2 domain)
+  float M[MAXR + 1];         // row offset of z c (log2 domain; at most the row maximum, within 64 of it)
   double S[MAXR + 1];        // row sum of 2^(z c - M)
   double lS[MAXR + 1];       // log S
   float z[2 * SMCSD_MAX_K];  // logits of the draft tokens: target rows, then draft rows
@@ -466,9 +509,9 @@ __device__ __forceinline__ RowStat stat_of(const TailLds& L, int r) {
   return rs;
 }
 
-// Fold partial (pm, ps) into running statistics (m, s): log2-domain maxima,
+// Fold partial (pm, ps) into running statistics (m, s): log2-domain offsets,
 // fp64 sums.  The rescaling factor 2^(smaller - larger) <= 1 comes from the
-// fp32 exponential (relative error about 1e-7); a factor of a -inf maximum is 0
+// fp32 exponential (relative error about 1e-7); a factor of a -inf offset is 0
 // and keeps a NaN sum NaN.
 __device__ __forceinline__ void fold(float& m, double& s, float pm, double ps) {
   if (pm > m) {
@@ -613,7 +656,7 @@ __device__ __forceinline__ int locate(int n, WFN weight, double base, TFN target
 template <typename DT>
 __device__ __forceinline__ float2 tile_partial_of(const Raw<DT>& r, float c) {
   float m = -INFINITY, s = 0.0f;
-  lane_fold_tile<DT>(r, c, m, s);
+  lane_fold_tile_at_max<DT>(r, c, m, s);
   return wave_partial(m, s);
 }
 
@@ -621,7 +664,7 @@ struct NoIdleWork {
   __device__ void operator()() const {}
 };
 
-// Inverse-CDF draw from softmax(z c) of `row` (row maximum M, log2 domain)
+// Inverse-CDF draw from softmax(z c) of `row` (row offset M, log2 domain)
 // with uniform u.  L.P holds np partials of the row, each over `per` tiles (a
 // bonus row's own tile partials, or segment partials).  Whole workgroup;
 // every thread gets the token.  While wavefront 0 reloads and searches the
@@ -1018,7 +1061,7 @@ constexpr int tree_held_tiles() {
 
 struct TreeLds {
   TailLds t;  // draw scratch: staged partials, tile masses, located tile
-  float Mt[TREE_MAX], Md[TREE_MAX];      // row maxima (log2 domain): target row of node n, local draft row k
+  float Mt[TREE_MAX], Md[TREE_MAX];      // row offsets (log2 domain): target row of node n, local draft row k
   double St[TREE_MAX], Sd[TREE_MAX];     // row sums of 2^(z c - M)
   double lSt[TREE_MAX], lSd[TREE_MAX];   // their natural logs
   int par[TREE_MAX];                     // local parent of node n (-1 at the root)
