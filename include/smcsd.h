@@ -54,11 +54,13 @@
  *   streams every logit once and one that turns the row statistics into
  *   decisions (for smc_reweight_resample a third, one workgroup per prompt,
  *   for the effective sample size, the resampling and the page tables).
- *   Outputs are valid once the stream reaches that point.  No workgroup ever
- *   waits for another, so a call completes however much of the device it
- *   gets; what one kernel reads from other workgroups the kernel before it
- *   wrote.  Calls on one workspace must not overlap (on one stream they never
- *   do).
+ *   Outputs are valid once the stream reaches that point.  What one kernel
+ *   reads from other workgroups the kernel before it wrote, with one
+ *   exception: tree_verify's decision kernel may run each tree on up to four
+ *   workgroups that exchange single tagged words (see there), only when the
+ *   whole grid fits on the device at once.  No other workgroup ever waits for
+ *   another, so those calls complete however much of the device they get.
+ *   Calls on one workspace must not overlap (on one stream they never do).
  *
  * Workspace:
  *   Caller-owned device scratch of at least the size the *_workspace_bytes()
@@ -113,11 +115,14 @@ enum {
                                    the page bookkeeping, a state it rejects           */
   SMCSD_FLAG_PAGES_FULL = 32,   /* smc_pages_append: a row would exceed its L pages;
                                    nothing changed                                    */
-  SMCSD_FLAG_PAGES_EXHAUSTED = 64 /* smc_pages_append: fewer free pages than the step
+  SMCSD_FLAG_PAGES_EXHAUSTED = 64, /* smc_pages_append: fewer free pages than the step
                                    needs; nothing changed                             */
+  SMCSD_FLAG_WAIT_EXPIRED = 128 /* tree_verify: the workgroups sharing a tree did not
+                                   all run within 0.1 s of each other (other work held
+                                   the device); outputs of that tree unspecified      */
 };
 
-#define SMCSD_ABI_VERSION 2
+#define SMCSD_ABI_VERSION 3
 #define SMCSD_MAX_K 128    /* largest draft length per sequence / particle      */
 #define SMCSD_MAX_N 1024   /* largest particle count per prompt                 */
 #define SMCSD_MAX_V 524288 /* largest vocabulary                                 */
@@ -480,6 +485,15 @@ int32_t pacer_lengths(int32_t B, int32_t block, int32_t max_blocks, double t0, d
  *   token drawn from p_leaf) or at a node whose children were all rejected
  *   (final token drawn from the last max(0, r - q_u)).  A chain of K+1 nodes
  *   is sd_verify with K draft tokens, decision for decision.
+ * Execution: when few trees leave most of the device idle (B <= 64 trees of
+ *   two or more tiles on a 256-CU device), the decision kernel runs each tree
+ *   on up to four workgroups: each walks the whole tree, weighs every fourth
+ *   tile of a rejection pass and reads the other tiles' masses from the other
+ *   workgroups through tagged words in the workspace (one relaxed device-scope
+ *   64-bit atomic per value; the streaming kernel of the same call zeroes
+ *   them).  The decisions are bit-identical to a single workgroup's.  A
+ *   workgroup waits at most 0.1 s for the others; past that it raises
+ *   SMCSD_FLAG_WAIT_EXPIRED.
  * Layout (all device memory, caller-owned):
  *   node_offsets   int32 [B+1]: tree b owns nodes node_offsets[b] ..
  *                  node_offsets[b+1]-1 (1 <= M_b <= SMCSD_TREE_MAX_NODES),

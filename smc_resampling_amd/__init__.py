@@ -18,7 +18,7 @@ __all__ = [
     "sd_verify", "smc_reweight_resample", "sd_verify_workspace_bytes", "smc_workspace_bytes",
     "prepare_sd_verify", "prepare_smc_reweight_resample", "status_string", "abi_version", "lib", "SmcsdError",
     "FLAG_NONFINITE", "FLAG_ZERO_RESIDUAL", "FLAG_ZERO_WEIGHTS", "FLAG_CDF_CLAMP", "FLAG_BAD_INPUT",
-    "FLAG_PAGES_FULL", "FLAG_PAGES_EXHAUSTED",
+    "FLAG_PAGES_FULL", "FLAG_PAGES_EXHAUSTED", "FLAG_WAIT_EXPIRED",
     "new_workspace", "time_next_call", "smc_pages_workspace_bytes", "smc_pages_append", "smc_pages_resample",
     "draft_sample_workspace_bytes", "prepare_draft_sample", "draft_sample", "pacer_lengths",
     "tree_verify_workspace_bytes", "prepare_tree_verify", "tree_verify", "TREE_MAX_NODES", "read_ceiling",
@@ -33,7 +33,7 @@ LIB_PATH = os.environ.get("SMCSD_LIBRARY") or os.path.join(HERE, "libsmcsd.so")
 SMCSD_OK, SMCSD_ERR_INVALID_ARG, SMCSD_ERR_UNSUPPORTED, SMCSD_ERR_WORKSPACE, SMCSD_ERR_HIP = range(5)
 SMCSD_F32, SMCSD_BF16 = 0, 1
 FLAG_NONFINITE, FLAG_ZERO_RESIDUAL, FLAG_ZERO_WEIGHTS, FLAG_CDF_CLAMP, FLAG_BAD_INPUT = 1, 2, 4, 8, 16
-FLAG_PAGES_FULL, FLAG_PAGES_EXHAUSTED = 32, 64
+FLAG_PAGES_FULL, FLAG_PAGES_EXHAUSTED, FLAG_WAIT_EXPIRED = 32, 64, 128
 WORKSPACE_ALIGN = 256
 TREE_MAX_NODES = 256
 NOALLOC_SCRATCH_BYTES = 32 << 20

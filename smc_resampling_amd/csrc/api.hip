@@ -45,13 +45,20 @@ SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
 }
 
 // Token trees: every target row (node) and draft row is a group of its own,
-// so each has segment partials and, with multi-tile segments, tile partials.
-SdLayout tree_layout(int64_t rows, int64_t V) {
+// so each has segment partials and, with multi-tile segments, tile partials;
+// then the words through which the workgroups sharing a tree exchange tile
+// masses (two banks of one word per tile, per tree).
+struct TreeLayout {
+  size_t part, tpart, xchg, total;
+};
+
+TreeLayout tree_layout(int32_t B, int64_t rows, int64_t V) {
   const int nt = ntiles_of(V);
-  SdLayout l;
+  TreeLayout l;
   l.part = 0;
   l.tpart = align_up(l.part + sizeof(float2) * (size_t)(rows * nt));
-  l.total = align_up(l.tpart + sizeof(float2) * (size_t)(rows * nt));
+  l.xchg = align_up(l.tpart + sizeof(float2) * (size_t)(rows * nt));
+  l.total = align_up(l.xchg + sizeof(uint64_t) * (size_t)((int64_t)B * 2 * nt));
   return l;
 }
 
@@ -105,6 +112,8 @@ void fill_step(smcsd::StepArgs* s, const smcsd::Plan& plan, const void* target, 
   s->cb = s->c;
   s->part = reinterpret_cast<float2*>(ws + part_off);
   s->part1 = nullptr;
+  s->xz = nullptr;
+  s->xzn = 0;
   s->tpart = reinterpret_cast<float2*>(ws + tpart_off);
   s->flags = flags;
   s->flat = 0;
@@ -219,7 +228,7 @@ int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, con
 size_t tree_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t V, int64_t num_nodes, int64_t num_draft_rows) {
   (void)dtype;
   if (B <= 0 || V <= 0 || num_nodes < B || num_draft_rows < 0) return 0;
-  return tree_layout(num_nodes + num_draft_rows, V).total;
+  return tree_layout(B, num_nodes + num_draft_rows, V).total;
 }
 
 int32_t tree_verify(int32_t dtype, int32_t B, int32_t V, float temperature, const int32_t* node_offsets,
@@ -240,7 +249,7 @@ int32_t tree_verify(int32_t dtype, int32_t B, int32_t V, float temperature, cons
     return SMCSD_ERR_INVALID_ARG;
   if (num_draft_rows > 0 && !draft_logits) return SMCSD_ERR_INVALID_ARG;
   const int64_t rows = num_nodes + num_draft_rows;
-  const SdLayout l = tree_layout(rows, V);
+  const TreeLayout l = tree_layout(B, rows, V);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
   const bool bf16 = dtype == SMCSD_BF16;
@@ -262,6 +271,8 @@ int32_t tree_verify(int32_t dtype, int32_t B, int32_t V, float temperature, cons
   a.last_node = last_node;
   a.final_token = final_token;
   a.B = B;
+  a.split = 1;
+  a.xchg = reinterpret_cast<uint64_t*>(ws + l.xchg);
   return smcsd::launch_tree(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;

@@ -23,7 +23,7 @@ constexpr int TILE = 2048;
 constexpr int PER_LANE = TILE / WAVE;  // 32 values per lane
 
 constexpr uint32_t FLAG_NONFINITE = 1, FLAG_ZERO_RESIDUAL = 2, FLAG_ZERO_WEIGHTS = 4,
-                   FLAG_CDF_CLAMP = 8, FLAG_BAD_INPUT = 16;
+                   FLAG_CDF_CLAMP = 8, FLAG_BAD_INPUT = 16, FLAG_WAIT_EXPIRED = 128;
 
 // Index of the calling wavefront in its workgroup, as a value the compiler
 // knows to be the same across the wavefront (so branches on it stay scalar).
@@ -128,6 +128,43 @@ __device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
   const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
   return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// ---------------------------------------------------------------------------
+// tagged words: values exchanged between the workgroups of one decision
+// ---------------------------------------------------------------------------
+// A value travels together with its tag in one 64-bit word (tag in the high
+// half, the fp32 value's bits in the low half), stored and loaded with
+// relaxed device-scope atomics.  Nothing else is communicated through the
+// word's arrival, so no release or acquire is needed: a reader only relies
+// on seeing, eventually, the one store that carries the tag it waits for.
+// Tags are never 0, and the words start at 0 (an earlier kernel zeroes them).
+__device__ __forceinline__ void tagged_put(uint64_t* w, uint32_t tag, float v) {
+  __hip_atomic_store(w, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Ticks of the 100 MHz constant clock a reader waits for a word: 0.1 s, far
+// beyond any exchange of workgroups that run together (about 1 us), so that
+// a decision whose workgroups cannot all run (other work holding the device)
+// still ends.
+constexpr uint64_t TAG_WAIT_TICKS = 10000000;
+
+// Waits for word w to carry `tag` and returns its value in *v; false (and
+// *v = 0) when the wait bound passes first.
+__device__ __forceinline__ bool tagged_get(uint64_t* w, uint32_t tag, float* v) {
+  const uint64_t t0 = wall_clock64();
+  for (;;) {
+    const uint64_t x = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(x >> 32) == tag) {
+      *v = __uint_as_float((uint32_t)x);
+      return true;
+    }
+    if (wall_clock64() - t0 > TAG_WAIT_TICKS) {
+      *v = 0.0f;
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 // OR of a small flag word over the 64 lanes (one ballot per bit).

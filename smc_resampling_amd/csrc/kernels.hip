@@ -57,16 +57,17 @@ namespace smcsd {
 #endif
 #if SMCSD_PHASE_STAMPS
 __device__ unsigned long long g_stamps[SMCSD_STAMP_WGS * SMCSD_STAMP_EVENTS * 2];
-__device__ __forceinline__ void stamp(int k, unsigned code) {
-  if (threadIdx.x == 0 && blockIdx.x < SMCSD_STAMP_WGS && k < SMCSD_STAMP_EVENTS) {
-    const size_t i = ((size_t)blockIdx.x * SMCSD_STAMP_EVENTS + k) * 2;
+__device__ __forceinline__ void stamp_wg(int64_t g, int k, unsigned code) {
+  if (threadIdx.x == 0 && g < SMCSD_STAMP_WGS && k < SMCSD_STAMP_EVENTS) {
+    const size_t i = ((size_t)g * SMCSD_STAMP_EVENTS + k) * 2;
     g_stamps[i] = __builtin_amdgcn_s_memrealtime();
     g_stamps[i + 1] = code;
   }
 }
 #else
-__device__ __forceinline__ void stamp(int, unsigned) {}
+__device__ __forceinline__ void stamp_wg(int64_t, int, unsigned) {}
 #endif
+__device__ __forceinline__ void stamp(int k, unsigned code) { stamp_wg(blockIdx.x, k, code); }
 
 constexpr int MAXR = 2 * SMCSD_MAX_K + 1;  // rows per group
 constexpr int MAX_TILES = 256;             // tiles per row (V <= 524288)
@@ -288,6 +289,9 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   const int64_t w = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wave_id();
   const int64_t W = (int64_t)gridDim.x * WAVES_PER_BLOCK;
   const int64_t u0 = a.units * w / W, u1 = a.units * (w + 1) / W;
+  // the words the decision kernel after this one exchanges values through
+  // start at 0 (plain stores: the kernel boundary orders them before it)
+  for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < a.xzn; i += (int64_t)gridDim.x * BLOCK) a.xz[i] = 0;
   if (u0 >= u1) return;
   const int nseg = a.nseg, seg = a.seg, ntiles = a.ntiles;
   const float c = a.c;
@@ -1074,6 +1078,7 @@ struct TreeLds {
   double Z[TREE_MAX];                    // masses of the current node's rejections
   float iz[TREE_MAX];                    // 1 / Z (0: that rejection left r unchanged)
   int bad, accept;
+  int lost;  // a wait for another member's tile mass ran out: wait no more
 };
 
 // Row statistics of the RA rows at partA (into Mt/St/lSt) and the RB rows at
@@ -1180,10 +1185,27 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
+  // workgroup -> (tree b, member k of S).  The S members of a tree are 8
+  // workgroup indices apart, so that, with workgroups dealt to the 8 XCDs in
+  // turn, they share one L2; indices past the last tree have nothing to do.
+  // Every member walks the whole tree (the same loads and arithmetic, so the
+  // same decisions); a rejection pass is shared: member k weighs the tiles
+  // t = k (mod S) and the members exchange their tiles' masses.
+  const int S = a.split;
+  int b = blockIdx.x, k = 0;
+  if (S > 1) {
+    const int x = (int)blockIdx.x % 8, r = (int)blockIdx.x / 8;
+    k = r % S;
+    b = x + 8 * (r / S);
+    if (b >= a.B) return;
+  }
   const int ntiles = s.ntiles;
   int ev = 0;
-  stamp(ev++, 0);
+  auto tstamp = [&](unsigned code) {
+    if (k == 0) stamp_wg(b, ev, code);
+    ev++;
+  };
+  tstamp(0);
   const int64_t n0 = a.node_off[b], d0 = a.draft_off[b];
   const int64_t M64 = a.node_off[b + 1] - n0, D64 = a.draft_off[b + 1] - d0;
   // offsets that do not describe a tree inside the buffers: nothing is read
@@ -1199,6 +1221,7 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
   if (tid == 0) {
     L.t.fl = 0;
     L.bad = 0;
+    L.lost = 0;
   }
   // parents, tokens and uniforms, one thread per node
   int pn = -1;
@@ -1218,7 +1241,7 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     L.ut[tid] = un;
   }
   __syncthreads();
-  stamp(ev++, STAMP_TREE_MERGED);
+  tstamp(STAMP_TREE_MERGED);
   // tree order: the root's parent is -1, every other parent comes earlier;
   // mark the nodes that have children
   bool badn = false;
@@ -1263,10 +1286,12 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     L.xok[tid] = xv;
   }
   __syncthreads();
-  stamp(ev++, STAMP_TREE_GATHERED);
+  tstamp(STAMP_TREE_GATHERED);
   uint32_t fl = 0;
   const double ufin = (double)L.ut[0];
   int u = 0, depth = 0, y = 0;
+  int owner = 0;        // the member that draws the final token
+  uint32_t npass = 0;   // passes so far: the tag of a pass's exchanged masses
   for (;;) {
     // the children of u, as bits of node indices (M <= TREE_MAX = 4 wavefronts of nodes)
     const uint64_t kb = __ballot(tid < M && L.par[tid] == u);
@@ -1277,14 +1302,17 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     if (!st.ok) fl |= FLAG_NONFINITE;
     const raw* trow = static_cast<const raw*>(s.target) + (n0 + u) * s.V;
     if (dr < 0) {
-      // a leaf: the bonus token from p_u (its tile or segment partials)
-      int bnp, bper;
-      const float2* bp = bonus_partials(s, n0 + u, n0 + u, 0, &bnp, &bper);
-      stamp(ev++, STAMP_TREE_LEAF);
-      stage_partials<TREE_BLOCK>(bp, bnp, L.t);
-      __syncthreads();
-      y = draw_softmax<DT, VL, TREE_WAVES>(trow, s, s.c, st.M, ufin, bnp, bper, L.t, fl);
-      stamp(ev++, STAMP_TREE_DRAWN);
+      // a leaf: the bonus token from p_u (its tile or segment partials),
+      // drawn by member 0
+      if (k == 0) {
+        int bnp, bper;
+        const float2* bp = bonus_partials(s, n0 + u, n0 + u, 0, &bnp, &bper);
+        tstamp(STAMP_TREE_LEAF);
+        stage_partials<TREE_BLOCK>(bp, bnp, L.t);
+        __syncthreads();
+        y = draw_softmax<DT, VL, TREE_WAVES>(trow, s, s.c, st.M, ufin, bnp, bper, L.t, fl);
+        tstamp(STAMP_TREE_DRAWN);
+      }
       break;
     }
     const RowStat sd = stat_at(L.Md, L.Sd, L.lSd, dr);
@@ -1298,27 +1326,34 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
       const Raw<DT> rd = load_tile<DT, VL, 0>(drw, s.V, t, lane);
       tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, nr, sub, w);
     };
-    auto store_mass = [&](int t, const float (&w)[PER_LANE]) {
+    // the word through which tile t's mass of the pass tagged `tag` travels
+    auto xslot = [&](uint32_t tag, int t) { return a.xchg + ((int64_t)b * 2 + (tag & 1u)) * ntiles + t; };
+    auto store_mass = [&](int t, const float (&w)[PER_LANE], uint32_t tag) {
       float m = 0.0f;
 #pragma unroll
       for (int e = 0; e < PER_LANE; e++) m += w[e];
       m = wave_sum(m);
-      if (lane == 0) L.t.W[t] = (double)m;
+      if (lane == 0) {
+        L.t.W[t] = (double)m;
+        if (S > 1) tagged_put(xslot(tag, t), tag, m);
+      }
     };
     // The weights of tile t in a pass with nr earlier rejections (sub:
     // max(0, r - q), else r).  A sub pass whose previous rejection left mass
     // (Z > 0) continues from that pass's weights W held in LDS: r = W / Z,
     // w = max(0, r - q), the same operations as the chain rebuilt from p and
     // q, with one exponential a logit pair instead of two.  Every sub pass
-    // stores its weights of the held tiles for the next.  Tile t is always weighed by wavefront
-    // t % TREE_WAVES, so its LDS slice needs no barrier.
+    // stores its weights of the held tiles for the next.  Tile t = k + S j is
+    // always weighed by wavefront j % TREE_WAVES and held in slot j < HT, so
+    // its LDS slice needs no barrier.
     auto weigh = [&](int t, Raw<DT>& rt, Raw<DT>& rd, bool cont, int nr, bool sub, float (&w)[PER_LANE]) {
       mask_tail<DT>(rd, s.V, t, lane);
+      const int hj = t / S;
       if (cont) {
         const float z = L.iz[nr - 1];
 #pragma unroll
         for (int i = 0; i < Q4; i++) {
-          const float4 h = HW[(t * Q4 + i) * WAVE + lane];
+          const float4 h = HW[(hj * Q4 + i) * WAVE + lane];
           w[4 * i] = h.x;
           w[4 * i + 1] = h.y;
           w[4 * i + 2] = h.z;
@@ -1339,44 +1374,60 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
         mask_tail<DT>(rt, s.V, t, lane);
         tree_weights<DT>(rt, rd, At, Ad, s.c, L.iz, nr, sub, w);
       }
-      if (HT > 0 && sub && t < HT) {
+      if (HT > 0 && sub && hj < HT) {
 #pragma unroll
         for (int i = 0; i < Q4; i++)
-          HW[(t * Q4 + i) * WAVE + lane] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+          HW[(hj * Q4 + i) * WAVE + lane] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
       }
     };
-    // one pass over u's row pair: every tile's mass into L.t.W; with bf16
-    // 16-byte loads (registers to spare) a wavefront issues the loads of two
-    // of its tiles before weighing either, so a 16-tile pair costs one round
-    // trip to memory, not two
+    // one pass over u's row pair: every tile's mass into L.t.W, this
+    // member's tiles weighed here and the others' masses read from their
+    // words; with bf16 16-byte loads (registers to spare) a wavefront issues
+    // the loads of two of its tiles before weighing either, so a 16-tile pair
+    // costs one round trip to memory, not two.  A member writes a bank of
+    // words again two passes later, which it reaches only after every member
+    // has published the pass in between, hence read this bank: two banks
+    // (by the pass's parity) keep every word until all have read it.
     constexpr bool PAIR = DT::VEC == 8 && VL;
     auto pass = [&](int nr, bool sub) {
+      const uint32_t tag = ++npass;
       if constexpr (!PAIR) {
-        for (int t = wave; t < ntiles; t += TREE_WAVES) {
+        for (int t = k + S * wave; t < ntiles; t += S * TREE_WAVES) {
           float w[PER_LANE];
           tile_w(t, nr, sub, w);
-          store_mass(t, w);
+          store_mass(t, w, tag);
         }
-        return;
+      } else {
+        const bool cont = HT > 0 && sub && nr > 0 && L.iz[nr - 1] > 0.0f;
+        for (int t0 = k + S * wave; t0 < ntiles; t0 += 2 * S * TREE_WAVES) {
+          const int t1 = t0 + S * TREE_WAVES;
+          const int t1c = t1 < ntiles ? t1 : t0;  // a tile of the row either way
+          const bool c0 = cont && t0 / S < HT, c1 = cont && t1 / S < HT;
+          // both rows' tiles are loaded even where the weights continue from
+          // LDS: the loads stay one unconditional batch (measured faster than
+          // skipping the target row's, which comes from cache then)
+          Raw<DT> rt0 = load_raw<DT, VL, 0>(trow, s.V, t0, lane);
+          Raw<DT> rd0 = load_raw<DT, VL, 0>(drw, s.V, t0, lane);
+          Raw<DT> rt1 = load_raw<DT, VL, 0>(trow, s.V, t1c, lane);
+          Raw<DT> rd1 = load_raw<DT, VL, 0>(drw, s.V, t1c, lane);
+          float w[PER_LANE];
+          weigh(t0, rt0, rd0, c0, nr, sub, w);
+          store_mass(t0, w, tag);
+          if (t1 < ntiles) {
+            weigh(t1, rt1, rd1, c1, nr, sub, w);
+            store_mass(t1, w, tag);
+          }
+        }
       }
-      const bool cont = HT > 0 && sub && nr > 0 && L.iz[nr - 1] > 0.0f;
-      for (int t0 = wave; t0 < ntiles; t0 += 2 * TREE_WAVES) {
-        const int t1 = t0 + TREE_WAVES;
-        const int t1c = min(t1, ntiles - 1);  // a tile of the row either way
-        const bool c0 = cont && t0 < HT, c1 = cont && t1 < HT;
-        // both rows' tiles are loaded even where the weights continue from
-        // LDS: the loads stay one unconditional batch (measured faster than
-        // skipping the target row's, which comes from cache then)
-        Raw<DT> rt0 = load_raw<DT, VL, 0>(trow, s.V, t0, lane);
-        Raw<DT> rd0 = load_raw<DT, VL, 0>(drw, s.V, t0, lane);
-        Raw<DT> rt1 = load_raw<DT, VL, 0>(trow, s.V, t1c, lane);
-        Raw<DT> rd1 = load_raw<DT, VL, 0>(drw, s.V, t1c, lane);
-        float w[PER_LANE];
-        weigh(t0, rt0, rd0, c0, nr, sub, w);
-        store_mass(t0, w);
-        if (t1 < ntiles) {
-          weigh(t1, rt1, rd1, c1, nr, sub, w);
-          store_mass(t1, w);
+      if (S > 1) {
+        for (int t = tid; t < ntiles; t += TREE_BLOCK) {
+          if (t % S == k) continue;
+          float v = 0.0f;
+          if (!L.lost && !tagged_get(xslot(tag, t), tag, &v)) {
+            fl |= FLAG_WAIT_EXPIRED;  // this tree's outputs are unspecified
+            L.lost = 1;
+          }
+          L.t.W[t] = (double)v;
         }
       }
     };
@@ -1425,7 +1476,7 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
         nrej++;
       }
     }
-    stamp(ev++, (next >= 0 ? STAMP_TREE_ACCEPTED : STAMP_TREE_REJECTED) + (unsigned)min(nrej, 99));
+    tstamp((next >= 0 ? STAMP_TREE_ACCEPTED : STAMP_TREE_REJECTED) + (unsigned)min(nrej, 99));
     if (next >= 0) {
       u = next;
       depth++;
@@ -1454,15 +1505,16 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     }
     lds_barrier();
     const int tt = L.t.sel;
-    if (wave == tt % TREE_WAVES) {
+    owner = tt % S;
+    if (k == owner && wave == (tt / S) % TREE_WAVES) {
       // the located tile's weights as its pass weighed them (held in LDS, or
       // recomputed the same way by the wavefront that weighed it, which reads
       // the tile again, likely from its cache)
       float w[PER_LANE];
-      if (HT > 0 && !zero && tt < HT) {
+      if (HT > 0 && !zero && tt / S < HT) {
 #pragma unroll
         for (int i = 0; i < Q4; i++) {
-          const float4 h = HW[(tt * Q4 + i) * WAVE + lane];
+          const float4 h = HW[(tt / S * Q4 + i) * WAVE + lane];
           w[4 * i] = h.x;
           w[4 * i + 1] = h.y;
           w[4 * i + 2] = h.z;
@@ -1485,15 +1537,17 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     }
     lds_barrier();
     y = L.t.y;
-    stamp(ev++, STAMP_TREE_DRAWN);
+    tstamp(STAMP_TREE_DRAWN);
     break;
   }
   or_flags(fl, L.t);
   __syncthreads();
   if (tid == 0) {
-    a.num_accepted[b] = depth;
-    a.last_node[b] = u;
-    a.final_token[b] = y;
+    if (k == 0) {
+      a.num_accepted[b] = depth;
+      a.last_node[b] = u;
+    }
+    if (k == owner) a.final_token[b] = y;
     raise_flags(s.flags, L.t.fl);
   }
 }
@@ -1869,13 +1923,36 @@ hipError_t phase_stamps(void* dst, size_t bytes, bool clear) {
 #endif
 }
 
-hipError_t launch_tree(const TreeArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
+// Members per tree: 4, else 2, while the 8 S ceil(B / 8) workgroups of the
+// split grid all fit on the device at once (members wait for each other's
+// tile masses) and every member has a tile to weigh; else 1 (no exchange).
+static int tree_split(int B, int ntiles, const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, TREE_BLOCK, 0) != hipSuccess)
+    return 1;
+  const int64_t held = (int64_t)cus * per_cu;
+  for (int S = 4; S > 1; S /= 2)
+    if (S <= ntiles && 8LL * S * ((B + 7) / 8) <= held) return S;
+  return 1;
+}
+
+hipError_t launch_tree(const TreeArgs& args, const Plan& p, bool bf16, bool vec, hipStream_t s,
+                       const KernelTimers& t) {
+  const void* k = bf16 ? (vec ? tree_tail_kernel<Bf16, true>() : tree_tail_kernel<Bf16, false>())
+                       : (vec ? tree_tail_kernel<F32, true>() : tree_tail_kernel<F32, false>());
+  TreeArgs a = args;
+  a.split = tree_split(a.B, a.s.ntiles, k);
+  if (a.split > 1) {
+    a.s.xz = a.xchg;  // the streaming kernel zeroes the exchange words
+    a.s.xzn = (int64_t)a.B * 2 * a.s.ntiles;
+  }
   hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide, p.pw), (unsigned)p.grid, BLOCK, a.s, s,
                         t.stream_start, t.stream_stop);
   if (e != hipSuccess) return e;
-  const void* k = bf16 ? (vec ? tree_tail_kernel<Bf16, true>() : tree_tail_kernel<Bf16, false>())
-                       : (vec ? tree_tail_kernel<F32, true>() : tree_tail_kernel<F32, false>());
-  return launch(k, (unsigned)a.B, TREE_BLOCK, a, s, t.tail_start, t.tail_stop);
+  const int64_t grid = a.split > 1 ? 8LL * a.split * ((a.B + 7) / 8) : a.B;
+  return launch(k, (unsigned)grid, TREE_BLOCK, a, s, t.tail_start, t.tail_stop);
 }
 
 }  // namespace smcsd

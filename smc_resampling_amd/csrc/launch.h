@@ -32,6 +32,8 @@ struct StepArgs {
   uint32_t* flags;
   int flat;       // 1: every row is a group of its own, the target rows then the draft rows (K = 0)
   float2* part1;  // power target: [ngroups * nseg] segment partials of each group's bonus row at scale c
+  uint64_t* xz;   // [xzn] words the streaming kernel zeroes for the decision kernel after it (or null)
+  int64_t xzn;
 };
 
 struct SdArgs {
@@ -72,6 +74,12 @@ struct TreeArgs {
   int32_t* last_node;
   int32_t* final_token;
   int B;
+  // Members per tree (1, 2 or 4): the workgroups that share each rejection
+  // pass of a tree, each weighing every split-th tile, and exchanging tile
+  // masses through xchg: [B][2][ntiles] tagged words, zeroed by the streaming
+  // kernel of the same call.  Set by launch_tree.
+  int split;
+  uint64_t* xchg;
 };
 
 // Segment length and streaming grid of a call.

@@ -221,3 +221,42 @@ def test_tree_deterministic():
     b = run_tree_gpu(c)
     for x, y in zip(a, b):
         assert np.array_equal(np.asarray(x), np.asarray(y))
+
+
+def _concat_tree_cases(a, b):
+    """One call's inputs holding the trees of case a, then those of case b."""
+    na, da = int(a["node_off"][-1]), int(a["draft_off"][-1])
+    out = dict(T=a["T"], dtype=a["dtype"])
+    out["target"] = np.concatenate([a["target"], b["target"]])
+    out["draft"] = np.concatenate([a["draft"], b["draft"]])
+    out["node_off"] = np.concatenate([a["node_off"], b["node_off"][1:] + na]).astype(np.int32)
+    out["draft_off"] = np.concatenate([a["draft_off"], b["draft_off"][1:] + da]).astype(np.int32)
+    for k in ("parent", "tokens", "uniforms"):
+        out[k] = np.concatenate([a[k], b[k]])
+    return out
+
+
+@pytest.mark.parametrize("B,V,dtype", [(1, 32768, "bf16"), (13, 32768, "bf16"), (64, 32768, "bf16"),
+                                       (65, 6000, "f32"), (128, 2049, "bf16"), (8, 151936, "bf16"),
+                                       (40, 20000, "f32")])
+def test_tree_split_members_match_one_workgroup(B, V, dtype):
+    """Calls of few trees run each tree on several workgroups that share its
+    rejection passes (4 members up to 64 trees, 2 up to 128, fewer when a
+    row has fewer tiles); the same trees in a call of 300 trees run on one
+    workgroup each.  Both must decide bit for bit alike, and match the
+    oracle."""
+    from gpu_util import check_tree, run_tree_gpu
+
+    rng = np.random.default_rng(B * 7 + V)
+    shapes = [tree_parents("full", width=2, depth=3), tree_parents("star", M=6), tree_parents("chain", M=5),
+              tree_parents("random", rng, M=40), tree_parents("full", width=3, depth=2)]
+    trees = [shapes[i % len(shapes)] for i in range(B)]
+    small = tree_case(B * 31 + 5, trees, V, T=0.8, delta=np.array([(0.5, 1.0, 2.0)[b % 3] for b in range(B)]),
+                      dtype=dtype)
+    check_tree(small, f"split call B={B} V={V} {dtype}")
+    pad = tree_case(B * 31 + 6, [tree_parents("root")] * (300 - B), V, T=0.8, delta=1.0, dtype=dtype)
+    big = _concat_tree_cases(small, pad)
+    na_s, ln_s, ft_s, fl_s = run_tree_gpu(small)
+    na_b, ln_b, ft_b, fl_b = run_tree_gpu(big)
+    assert np.array_equal(na_s, na_b[:B]) and np.array_equal(ln_s, ln_b[:B]) and np.array_equal(ft_s, ft_b[:B])
+    assert (fl_s & 128) == 0 and (fl_b & 128) == 0
