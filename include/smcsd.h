@@ -56,11 +56,12 @@
  *   for the effective sample size, the resampling and the page tables).
  *   Outputs are valid once the stream reaches that point.  What one kernel
  *   reads from other workgroups the kernel before it wrote, with one
- *   exception: tree_verify's decision kernel may run each tree on up to four
- *   workgroups that exchange single tagged words (see there), only when the
- *   whole grid fits on the device at once.  No other workgroup ever waits for
- *   another, so those calls complete however much of the device they get.
- *   Calls on one workspace must not overlap (on one stream they never do).
+ *   exception: the decision kernels of sd_verify and tree_verify may run each
+ *   sequence or tree on up to four workgroups that exchange single tagged
+ *   words (see tree_verify), only when the whole grid fits on the device at
+ *   once.  No other workgroup ever waits for another, so the other calls
+ *   complete however much of the device they get.  Calls on one workspace
+ *   must not overlap (on one stream they never do).
  *
  * Workspace:
  *   Caller-owned device scratch of at least the size the *_workspace_bytes()
@@ -117,9 +118,10 @@ enum {
                                    nothing changed                                    */
   SMCSD_FLAG_PAGES_EXHAUSTED = 64, /* smc_pages_append: fewer free pages than the step
                                    needs; nothing changed                             */
-  SMCSD_FLAG_WAIT_EXPIRED = 128 /* tree_verify: the workgroups sharing a tree did not
-                                   all run within 0.1 s of each other (other work held
-                                   the device); outputs of that tree unspecified      */
+  SMCSD_FLAG_WAIT_EXPIRED = 128 /* sd_verify, tree_verify: the workgroups sharing a
+                                   sequence or tree did not all run within 0.1 s of
+                                   each other (other work held the device); its
+                                   outputs are unspecified                            */
 };
 
 #define SMCSD_ABI_VERSION 3
@@ -230,6 +232,11 @@ size_t sd_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t K, int32_t V,
  *                    aligned to SMCSD_WORKSPACE_ALIGN (any contents; see
  *                    Workspace above).
  *   stream           hipStream_t.
+ * Execution: with few sequences (B <= 64 on a 256-CU device, rows of four or
+ * more tiles of 2048 logits; up to 128 with two), the residual pass of each
+ * sequence is shared by four (two) workgroups exchanging tile masses through
+ * tagged words in the workspace, as tree_verify's passes; the decisions are
+ * bit-identical to one workgroup's.
  */
 int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperature,
                   const void* target_logits, const void* draft_logits,

@@ -31,16 +31,20 @@ bool vec_ok(int32_t dtype, int64_t V, const void* a, const void* b) {
 // most a call can use), the tile partials of each group's bonus row and, for
 // SMC, the reweighted log-weights.
 
+// sd_verify's layout also holds the words through which the workgroups
+// sharing a sequence's residual pass exchange tile masses (one per tile, per
+// sequence); draft_sample's draws need none.
 struct SdLayout {
-  size_t part, tpart, total;
+  size_t part, tpart, xchg, total;
 };
 
-SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d) {
+SdLayout sd_layout(int32_t B, int64_t V, int64_t rows_d, bool exchange) {
   const int nt = ntiles_of(V);
   SdLayout l;
   l.part = 0;
   l.tpart = align_up(l.part + sizeof(float2) * (size_t)((2 * rows_d + B) * nt));
-  l.total = align_up(l.tpart + sizeof(float2) * (size_t)((int64_t)B * nt));
+  l.xchg = align_up(l.tpart + sizeof(float2) * (size_t)((int64_t)B * nt));
+  l.total = align_up(l.xchg + (exchange ? sizeof(uint64_t) * (size_t)((int64_t)B * nt) : 0));
   return l;
 }
 
@@ -152,7 +156,7 @@ size_t sd_verify_workspace_bytes(int32_t dtype, int32_t B, int32_t K, int32_t V,
   (void)dtype;
   (void)K;
   if (B <= 0 || V <= 0 || total_draft_rows < 0) return 0;
-  return sd_layout(B, V, total_draft_rows).total;
+  return sd_layout(B, V, total_draft_rows, true).total;
 }
 
 int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperature,
@@ -170,7 +174,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   if (B == 0) return SMCSD_OK;
   if (!target_logits || !uniforms || !num_accepted || !final_token) return SMCSD_ERR_INVALID_ARG;
   if (total_draft_rows > 0 && (!draft_logits || !draft_tokens)) return SMCSD_ERR_INVALID_ARG;
-  const SdLayout l = sd_layout(B, V, total_draft_rows);
+  const SdLayout l = sd_layout(B, V, total_draft_rows, true);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
   const bool bf16 = dtype == SMCSD_BF16;
@@ -185,6 +189,8 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   a.uniforms = uniforms;
   a.num_accepted = num_accepted;
   a.final_token = final_token;
+  a.split = 1;
+  a.xchg = reinterpret_cast<uint64_t*>(ws + l.xchg);
   return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;
@@ -193,7 +199,7 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
 size_t draft_sample_workspace_bytes(int32_t dtype, int32_t R, int32_t V) {
   (void)dtype;
   if (R <= 0 || V <= 0) return 0;
-  return sd_layout(R, V, 0).total;
+  return sd_layout(R, V, 0, false).total;
 }
 
 // One draw per row: the verify step's final draw with no draft tokens (each
@@ -206,7 +212,7 @@ int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, con
   if (V > SMCSD_MAX_V) return SMCSD_ERR_UNSUPPORTED;
   if (R == 0) return SMCSD_OK;
   if (!logits || !uniforms || !tokens) return SMCSD_ERR_INVALID_ARG;
-  const SdLayout l = sd_layout(R, V, 0);
+  const SdLayout l = sd_layout(R, V, 0, false);
   if (!workspace || workspace_bytes < l.total || ((uintptr_t)workspace % kAlign) != 0)
     return SMCSD_ERR_WORKSPACE;
   const bool bf16 = dtype == SMCSD_BF16;
@@ -220,6 +226,8 @@ int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, con
   a.uniforms = uniforms;
   a.num_accepted = nullptr;
   a.final_token = tokens;
+  a.split = 1;
+  a.xchg = nullptr;
   return smcsd::launch_sd(a, plan, bf16, vec, static_cast<hipStream_t>(stream), take_timers()) == hipSuccess
              ? SMCSD_OK
              : SMCSD_ERR_HIP;

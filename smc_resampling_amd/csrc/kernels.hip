@@ -848,11 +848,28 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   __shared__ TailLds L;
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
-  const int64_t b = blockIdx.x;
+  // workgroup -> (sequence b, member k of S), as for token trees: the S
+  // members of a sequence are 8 workgroup indices apart (one L2 when
+  // workgroups are dealt to the 8 XCDs in turn), each decides the whole
+  // sequence alike, and they share the residual pass, member k weighing the
+  // tiles t = k (mod S) and reading the others' masses from their words.
+  const int S = a.split;
+  int64_t b = blockIdx.x;
+  int k = 0;
+  if (S > 1) {
+    const int x = (int)blockIdx.x % 8, r = (int)blockIdx.x / 8;
+    k = r % S;
+    b = x + 8 * (r / S);
+    if (b >= s.ngroups) return;
+  }
   const int ntiles = s.ntiles;
   const Group G = group_of(b, s.K, s.offsets, s.rows_d);
   int ev = 0;
-  stamp(ev++, 0);
+  auto sstamp = [&](unsigned code) {
+    if (k == 0) stamp_wg(b, ev, code);
+    ev++;
+  };
+  sstamp(0);
   if (s.offsets && threadIdx.x == 0) {
     uint32_t bad = G.ok ? 0u : FLAG_BAD_INPUT;
     if (b == 0 && s.offsets[0] != 0) bad = FLAG_BAD_INPUT;
@@ -878,7 +895,7 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
   const float z = token_logit<DT, SD_BLOCK>(s, G, b, xt, &ok);
   store_tokens<SD_BLOCK>(z, ok, uj, kb, L);
   __syncthreads();
-  stamp(ev++, STAMP_SD_MERGED);
+  sstamp(STAMP_SD_MERGED);
   uint32_t fl = 0;
   // accept test up to the first rejection
   if (wave == 0) {
@@ -906,16 +923,17 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     if (lane == 0) L.n = n;
   }
   __syncthreads();
-  stamp(ev++, STAMP_SD_TESTED);
+  sstamp(STAMP_SD_TESTED);
   const int n = L.n;
   const raw* trow = group_row<raw>(s, G, b, n);
-  int y;
+  int y = 0;
+  int owner = 0;  // the member that draws the final token
   if (n == kb) {
-    // every draft accepted: the bonus token from p_{K_b}
+    // every draft accepted: the bonus token from p_{K_b}, drawn by member 0
     const RowStat sk = stat_of(L, kb);
     if (!sk.ok) fl |= FLAG_NONFINITE;
-    y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, sk.M, (double)ufin, bnp, bper, L, fl);
-    stamp(ev++, STAMP_SD_BONUS_DRAWN);
+    if (k == 0) y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, sk.M, (double)ufin, bnp, bper, L, fl);
+    sstamp(STAMP_SD_BONUS_DRAWN);
   } else {
     // residual max(0, p_n - q_n): each wavefront weighs its tiles and keeps
     // the weights of the last one in registers for the search
@@ -924,7 +942,8 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
     const float At = log2_norm(st), Ad = log2_norm(sd);
     float w[PER_LANE];
     int held = -1;
-    for (int t = wave; t < ntiles; t += SD_WAVES) {
+    uint64_t* xw = a.xchg + b * ntiles;  // this sequence's words (tag 1)
+    for (int t = k + S * wave; t < ntiles; t += S * SD_WAVES) {
       const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, t, lane);
       const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, t, lane);
       residual_weights<DT>(rt, rd, At, Ad, s.c, w);
@@ -933,10 +952,22 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
 #pragma unroll
       for (int e = 0; e < PER_LANE; e++) m += w[e];
       m = wave_sum(m);
-      if (lane == 0) L.W[t] = (double)m;
+      if (lane == 0) {
+        L.W[t] = (double)m;
+        if (S > 1) tagged_put(xw + t, 1u, m);
+      }
+    }
+    if (S > 1) {
+      // the other members' tile masses
+      for (int t = threadIdx.x; t < ntiles; t += SD_BLOCK) {
+        if (t % S == k) continue;
+        float v = 0.0f;
+        if (!tagged_get(xw + t, 1u, &v)) fl |= FLAG_WAIT_EXPIRED;  // outputs unspecified
+        L.W[t] = (double)v;
+      }
     }
     __syncthreads();
-    stamp(ev++, STAMP_SD_RESIDUAL_PASS);
+    sstamp(STAMP_SD_RESIDUAL_PASS);
     if (wave == 0) {
       auto wt = [&](int k) -> double { return L.W[k]; };
       double before = 0.0, target = 0.0, total = 0.0;
@@ -955,11 +986,12 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
       }
     }
     __syncthreads();
-    stamp(ev++, STAMP_SD_LOCATED);
+    sstamp(STAMP_SD_LOCATED);
     const int tt = L.sel;
     if (tt >= 0) {
       // the wavefront that weighed tile tt draws inside it
-      if (wave == tt % SD_WAVES) {
+      owner = tt % S;
+      if (k == owner && wave == (tt / S) % SD_WAVES) {
         if (held != tt) {
           const Raw<DT> rt = load_tile<DT, VL>(trow, s.V, tt, lane);
           const Raw<DT> rd = load_tile<DT, VL>(drow, s.V, tt, lane);
@@ -978,22 +1010,25 @@ __global__ __launch_bounds__(SD_BLOCK) void k_sd_tail(SdArgs a) {
         if (lane == 0) L.y = tt * TILE + idx;
       }
       __syncthreads();
-      stamp(ev++, STAMP_SD_RESIDUAL_DRAWN);
+      sstamp(STAMP_SD_RESIDUAL_DRAWN);
       y = L.y;
     } else {
       // p_n and q_n agree to rounding: draw from p_n with the same uniform
+      // (member 0)
       fl |= FLAG_ZERO_RESIDUAL;
-      stage_partials<SD_BLOCK>(pg + (int64_t)n * s.nseg, s.nseg, L);
-      __syncthreads();
-      y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, st.M, (double)ufin, s.nseg, s.seg, L, fl);
-      stamp(ev++, STAMP_SD_FALLBACK_DRAWN);
+      if (k == 0) {
+        stage_partials<SD_BLOCK>(pg + (int64_t)n * s.nseg, s.nseg, L);
+        __syncthreads();
+        y = draw_softmax<DT, VL, SD_WAVES>(trow, s, s.c, st.M, (double)ufin, s.nseg, s.seg, L, fl);
+      }
+      sstamp(STAMP_SD_FALLBACK_DRAWN);
     }
   }
   or_flags(fl, L);
   __syncthreads();
   if (threadIdx.x == 0) {
-    if (a.num_accepted) a.num_accepted[b] = n;  // absent for a plain draw (no draft tokens)
-    a.final_token[b] = y;
+    if (k == 0 && a.num_accepted) a.num_accepted[b] = n;  // absent for a plain draw (no draft tokens)
+    if (k == owner) a.final_token[b] = y;
     raise_flags(s.flags, L.fl);
   }
 }
@@ -1872,18 +1907,44 @@ static const void* smc_tail_kernel() {
   return kptr(&k_smc_tail<DT, VL>);
 }
 
-hipError_t launch_sd(const SdArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
+// Members per decision (a sequence or a tree): 4, else 2, while the
+// 8 S ceil(n / 8) workgroups of the split grid all fit on the device at once
+// (members wait for each other's tile masses) and every member has a tile to
+// weigh; else 1 (no exchange).
+static int member_split(int64_t n, int ntiles, const void* kernel, int block) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
+    return 1;
+  const int64_t held = (int64_t)cus * per_cu;
+  for (int S = 4; S > 1; S /= 2)
+    if (S <= ntiles && 8LL * S * ((n + 7) / 8) <= held) return S;
+  return 1;
+}
+
+// The decision kernel's grid: one workgroup per decision, or for S members
+// 8 S ceil(n / 8) (member k of decision b at index b % 8 + 8 (k + S (b / 8))).
+static unsigned member_grid(int64_t n, int S) { return (unsigned)(S > 1 ? 8LL * S * ((n + 7) / 8) : n); }
+
+hipError_t launch_sd(const SdArgs& args, const Plan& p, bool bf16, bool vec, hipStream_t s,
+                     const KernelTimers& t) {
+  SdArgs a = args;
+  const bool draws = a.s.K == 0 && !a.s.offsets;  // draws only
+  const void* k = draws ? (bf16 ? (vec ? draw_tail_kernel<Bf16, true>() : draw_tail_kernel<Bf16, false>())
+                                : (vec ? draw_tail_kernel<F32, true>() : draw_tail_kernel<F32, false>()))
+                        : (bf16 ? (vec ? sd_tail_kernel<Bf16, true>() : sd_tail_kernel<Bf16, false>())
+                                : (vec ? sd_tail_kernel<F32, true>() : sd_tail_kernel<F32, false>()));
+  a.split = draws || !a.xchg ? 1 : member_split(a.s.ngroups, a.s.ntiles, k, SD_BLOCK);
+  if (a.split > 1) {
+    a.s.xz = a.xchg;  // the streaming kernel zeroes the exchange words
+    a.s.xzn = a.s.ngroups * a.s.ntiles;
+  }
   hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide, p.pw), (unsigned)p.grid, BLOCK, a.s, s,
                         t.stream_start, t.stream_stop);
   if (e != hipSuccess) return e;
-  if (a.s.K == 0 && !a.s.offsets) {  // draws only
-    const void* k = bf16 ? (vec ? draw_tail_kernel<Bf16, true>() : draw_tail_kernel<Bf16, false>())
-                         : (vec ? draw_tail_kernel<F32, true>() : draw_tail_kernel<F32, false>());
-    return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
-  }
-  const void* k = bf16 ? (vec ? sd_tail_kernel<Bf16, true>() : sd_tail_kernel<Bf16, false>())
-                       : (vec ? sd_tail_kernel<F32, true>() : sd_tail_kernel<F32, false>());
-  return launch(k, (unsigned)a.s.ngroups, SD_BLOCK, a, s, t.tail_start, t.tail_stop);
+  if (draws) return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
+  return launch(k, member_grid(a.s.ngroups, a.split), SD_BLOCK, a, s, t.tail_start, t.tail_stop);
 }
 
 hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
@@ -1923,27 +1984,12 @@ hipError_t phase_stamps(void* dst, size_t bytes, bool clear) {
 #endif
 }
 
-// Members per tree: 4, else 2, while the 8 S ceil(B / 8) workgroups of the
-// split grid all fit on the device at once (members wait for each other's
-// tile masses) and every member has a tile to weigh; else 1 (no exchange).
-static int tree_split(int B, int ntiles, const void* kernel) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, TREE_BLOCK, 0) != hipSuccess)
-    return 1;
-  const int64_t held = (int64_t)cus * per_cu;
-  for (int S = 4; S > 1; S /= 2)
-    if (S <= ntiles && 8LL * S * ((B + 7) / 8) <= held) return S;
-  return 1;
-}
-
 hipError_t launch_tree(const TreeArgs& args, const Plan& p, bool bf16, bool vec, hipStream_t s,
                        const KernelTimers& t) {
   const void* k = bf16 ? (vec ? tree_tail_kernel<Bf16, true>() : tree_tail_kernel<Bf16, false>())
                        : (vec ? tree_tail_kernel<F32, true>() : tree_tail_kernel<F32, false>());
   TreeArgs a = args;
-  a.split = tree_split(a.B, a.s.ntiles, k);
+  a.split = member_split(a.B, a.s.ntiles, k, TREE_BLOCK);
   if (a.split > 1) {
     a.s.xz = a.xchg;  // the streaming kernel zeroes the exchange words
     a.s.xzn = (int64_t)a.B * 2 * a.s.ntiles;
@@ -1951,8 +1997,7 @@ hipError_t launch_tree(const TreeArgs& args, const Plan& p, bool bf16, bool vec,
   hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide, p.pw), (unsigned)p.grid, BLOCK, a.s, s,
                         t.stream_start, t.stream_stop);
   if (e != hipSuccess) return e;
-  const int64_t grid = a.split > 1 ? 8LL * a.split * ((a.B + 7) / 8) : a.B;
-  return launch(k, (unsigned)grid, TREE_BLOCK, a, s, t.tail_start, t.tail_stop);
+  return launch(k, member_grid(a.B, a.split), TREE_BLOCK, a, s, t.tail_start, t.tail_stop);
 }
 
 }  // namespace smcsd

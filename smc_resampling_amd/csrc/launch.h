@@ -41,6 +41,12 @@ struct SdArgs {
   const float* uniforms;
   int32_t* num_accepted;
   int32_t* final_token;
+  // Members per sequence (1, 2 or 4): the workgroups that share a sequence's
+  // residual pass, each weighing every split-th tile, and exchanging tile
+  // masses through xchg: [B][ntiles] tagged words, zeroed by the streaming
+  // kernel of the same call.  Set by launch_sd.
+  int split;
+  uint64_t* xchg;
 };
 
 struct SmcArgs {

@@ -273,3 +273,43 @@ def test_sd_decisions_do_not_depend_on_segmentation():
     differ = (naR[0] != na1) | (ftR[0] != ft1)
     assert not (differ & ~near).any(), np.nonzero(differ & ~near)
     assert int(flR.item()) & ~8 == 0
+
+
+def _concat_sd_cases(a, b):
+    """One call's inputs holding the sequences of case a, then those of b
+    (fixed K in both, or CSR offsets in both)."""
+    out = dict(T=a["T"], dtype=a["dtype"], K=max(a["K"], b["K"]))
+    for k in ("target", "draft", "tokens", "uniforms"):
+        out[k] = np.concatenate([a[k], b[k]])
+    if a.get("offsets") is not None:
+        out["offsets"] = np.concatenate([a["offsets"], b["offsets"][1:] + a["offsets"][-1]]).astype(np.int32)
+    return out
+
+
+@pytest.mark.parametrize("B,V,K,dtype,ragged", [(64, 32768, 4, "bf16", False), (1, 32000, 2, "f32", False),
+                                                (13, 2049, 3, "bf16", False), (100, 6000, 5, "f32", False),
+                                                (40, 20000, 6, "bf16", True), (8, 151936, 8, "bf16", True)])
+def test_sd_split_members_match_one_workgroup(B, V, K, dtype, ragged):
+    """Calls of few sequences share each sequence's residual pass among
+    several workgroups (4 up to 64 sequences, 2 up to 128, fewer when a row
+    has fewer tiles); the same sequences in a call of 300 run on one
+    workgroup each.  Both must decide bit for bit alike, and match the
+    oracle."""
+    from gpu_util import check_sd, run_sd_gpu
+    from synth.small import sd_case
+
+    rng = np.random.default_rng(B * 11 + V)
+    delta = np.array([(0.5, 1.0, 2.0)[b % 3] for b in range(B)])
+    if ragged:
+        lens = rng.integers(0, K + 1, B)
+        small = sd_case(B * 17 + 1, B, V, T=0.9, lengths=lens, delta=delta, dtype=dtype)
+        pad = sd_case(B * 17 + 2, 300 - B, V, T=0.9, lengths=np.zeros(300 - B, np.int32), dtype=dtype)
+    else:
+        small = sd_case(B * 17 + 1, B, V, T=0.9, K=K, delta=delta, dtype=dtype)
+        pad = sd_case(B * 17 + 2, 300 - B, V, T=0.9, K=K, dtype=dtype)
+    check_sd(small, f"split call B={B} V={V} K={K} {dtype} ragged={ragged}")
+    big = _concat_sd_cases(small, pad)
+    na_s, ft_s, fl_s = run_sd_gpu(small)
+    na_b, ft_b, fl_b = run_sd_gpu(big)
+    assert np.array_equal(na_s, na_b[:B]) and np.array_equal(ft_s, ft_b[:B])
+    assert (fl_s & 128) == 0 and (fl_b & 128) == 0
