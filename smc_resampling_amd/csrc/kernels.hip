@@ -1466,50 +1466,61 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
         }
       }
     };
-    int nrej = 0, next = -1;
-    for (int kw = 0; kw < TREE_MAX / WAVE && next < 0; kw++) {
-      uint64_t bits = L.kids[kw];
-      while (bits && next < 0) {
-        const int cnode = kw * WAVE + __builtin_ctzll(bits);
-        bits &= bits - 1;
-        if (tid == 0) {
-          // the ratio r(x) / q(x) of this child's token
-          bool acc = false;
-          if (!L.xok[cnode]) {
-            fl |= FLAG_BAD_INPUT;
-          } else {
-            // p(x) / q(x) as in sd_verify (the fp32 exponential of the fp64
-            // log difference); each earlier rejection j turns r(x) / q(x)
-            // into max(0, r(x) / q(x) - 1) / Z_j
-            const double lp = log_prob(L.zt[cnode], st, s.c), lq = log_prob(L.zd[cnode], sd, s.c);
-            double ratio = (double)__builtin_amdgcn_exp2f((float)((lp - lq) * 1.4426950408889634));
-            for (int j = 0; j < nrej; j++)
-              if (L.Z[j] > 0.0) ratio = fmax(ratio - 1.0, 0.0) / L.Z[j];
-            acc = (double)L.ut[cnode] < ratio;
-          }
-          L.accept = acc;
-        }
-        lds_barrier();
-        if (L.accept) {
-          next = cnode;
-          break;
-        }
-        // rejected: one pass for the mass of max(0, r - q)
-        pass(nrej, true);
-        lds_barrier();
-        if (wave == 0) {
-          double z = 0.0;
-          for (int t = lane; t < ntiles; t += WAVE) z += L.t.W[t];
-          z = wave_sum_f64(z);
-          if (lane == 0) {
-            L.Z[nrej] = z;
-            L.iz[nrej] = z > 0.0 ? (float)(1.0 / z) : 0.0f;
-            if (!(z > 0.0)) fl |= FLAG_ZERO_RESIDUAL;  // r and q agree: r stays
-          }
-        }
-        lds_barrier();
-        nrej++;
+    // thread 0's acceptance test of child c after nr rejections at u: the
+    // ratio r(x) / q(x) of its token
+    auto accepts = [&](int c, int nr) -> bool {
+      if (!L.xok[c]) {
+        fl |= FLAG_BAD_INPUT;
+        return false;
       }
+      // p(x) / q(x) as in sd_verify (the fp32 exponential of the fp64 log
+      // difference); each earlier rejection j turns r(x) / q(x) into
+      // max(0, r(x) / q(x) - 1) / Z_j
+      const double lp = log_prob(L.zt[c], st, s.c), lq = log_prob(L.zd[c], sd, s.c);
+      double ratio = (double)__builtin_amdgcn_exp2f((float)((lp - lq) * 1.4426950408889634));
+      for (int j = 0; j < nr; j++)
+        if (L.Z[j] > 0.0) ratio = fmax(ratio - 1.0, 0.0) / L.Z[j];
+      return (double)L.ut[c] < ratio;
+    };
+    // the children of u in node order
+    int kw = 0;
+    uint64_t bits = L.kids[0];
+    auto next_child = [&]() -> int {
+      while (!bits && ++kw < TREE_MAX / WAVE) bits = L.kids[kw];
+      if (!bits) return -1;
+      const int c = kw * WAVE + __builtin_ctzll(bits);
+      bits &= bits - 1;
+      return c;
+    };
+    int nrej = 0, next = -1;
+    int cnode = next_child();  // u has children: a node without is a leaf
+    if (tid == 0) L.accept = accepts(cnode, 0);
+    lds_barrier();
+    for (;;) {
+      if (L.accept) {
+        next = cnode;
+        break;
+      }
+      // rejected: one pass for the mass of max(0, r - q); wavefront 0 then
+      // forms its total and thread 0 tests the next child right away
+      pass(nrej, true);
+      lds_barrier();
+      const int cn = next_child();
+      if (wave == 0) {
+        double z = 0.0;
+        for (int t = lane; t < ntiles; t += WAVE) z += L.t.W[t];
+        z = wave_sum_f64(z);
+        if (lane == 0) {
+          L.Z[nrej] = z;
+          L.iz[nrej] = z > 0.0 ? (float)(1.0 / z) : 0.0f;
+          if (!(z > 0.0)) fl |= FLAG_ZERO_RESIDUAL;  // r and q agree: r stays
+          if (cn >= 0) L.accept = accepts(cn, nrej + 1);
+        }
+      }
+      lds_barrier();
+      nrej++;
+      if (cn < 0) break;  // every child rejected
+      cnode = cn;
     }
     tstamp((next >= 0 ? STAMP_TREE_ACCEPTED : STAMP_TREE_REJECTED) + (unsigned)min(nrej, 99));
     if (next >= 0) {
