@@ -33,5 +33,16 @@ def build(out: str = LIB, extra_flags=()) -> str:
     return out
 
 
+# A test build whose member workgroups never wait for each other's tile
+# masses (tests/test_wait_expiry.py: calls still end, and raise
+# SMCSD_FLAG_WAIT_EXPIRED or decide correctly).
+NOWAIT_LIB = os.path.join(HERE, "libsmcsd_nowait.so")
+
+
+def build_nowait(out: str = NOWAIT_LIB) -> str:
+    return build(out, ["-DSMCSD_TAG_WAIT_TICKS=0"])
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_nowait())

@@ -146,8 +146,11 @@ __device__ __forceinline__ void tagged_put(uint64_t* w, uint32_t tag, float v) {
 // Ticks of the 100 MHz constant clock a reader waits for a word: 0.1 s, far
 // beyond any exchange of workgroups that run together (about 1 us), so that
 // a decision whose workgroups cannot all run (other work holding the device)
-// still ends.
-constexpr uint64_t TAG_WAIT_TICKS = 10000000;
+// still ends.  A test build sets 0, so that the waits run out at once.
+#ifndef SMCSD_TAG_WAIT_TICKS
+#define SMCSD_TAG_WAIT_TICKS 10000000
+#endif
+constexpr uint64_t TAG_WAIT_TICKS = SMCSD_TAG_WAIT_TICKS;
 
 // Waits for word w to carry `tag` and returns its value in *v; false (and
 // *v = 0) when the wait bound passes first.
