@@ -218,6 +218,8 @@ def phase_name(code):
              4: "residual pass over the rejected row pair", 5: "residual draw: tile located",
              6: "residual draw: search in the tile", 7: "zero-residual draw from p_n",
              10: "parents read, statistics merged", 11: "draft rows ranked, token logits gathered",
+             12: "pass: child tested, up to the pass", 13: "pass: own tiles weighed (thread 0's wavefront)",
+             14: "pass: other members' masses read",
              300: "step to a leaf", 400: "final draw"}
     if code in fixed:
         return fixed[code]

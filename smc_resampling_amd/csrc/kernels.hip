@@ -46,6 +46,11 @@ namespace smcsd {
 #ifndef SMCSD_TEMPORAL_ROWS
 #define SMCSD_TEMPORAL_ROWS 0
 #endif
+// Measurement knob, 4 in the library's build: the most member workgroups a
+// decision may be shared by (1: one workgroup per sequence or tree).
+#ifndef SMCSD_MAX_MEMBERS
+#define SMCSD_MAX_MEMBERS 4
+#endif
 
 // Phase timestamps of the decision kernels, for measurement builds only
 // (-DSMCSD_PHASE_STAMPS=1; the library's build compiles every stamp away).
@@ -1426,6 +1431,9 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
     constexpr bool PAIR = DT::VEC == 8 && VL;
     auto pass = [&](int nr, bool sub) {
       const uint32_t tag = ++npass;
+#if SMCSD_PHASE_STAMPS >= 2
+      tstamp(STAMP_TREE_PASS_START);
+#endif
       if constexpr (!PAIR) {
         for (int t = k + S * wave; t < ntiles; t += S * TREE_WAVES) {
           float w[PER_LANE];
@@ -1454,6 +1462,9 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
           }
         }
       }
+#if SMCSD_PHASE_STAMPS >= 2
+      if (tid == 0) tstamp(STAMP_TREE_PASS_WEIGHED);
+#endif
       if (S > 1) {
         for (int t = tid; t < ntiles; t += TREE_BLOCK) {
           if (t % S == k) continue;
@@ -1505,6 +1516,9 @@ __global__ __launch_bounds__(TREE_BLOCK) void k_tree_tail(TreeArgs a) {
       // forms its total and thread 0 tests the next child right away
       pass(nrej, true);
       lds_barrier();
+#if SMCSD_PHASE_STAMPS >= 2
+      tstamp(STAMP_TREE_PASS_GATHERED);
+#endif
       const int cn = next_child();
       if (wave == 0) {
         double z = 0.0;
@@ -1929,7 +1943,7 @@ static int member_split(int64_t n, int ntiles, const void* kernel, int block) {
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess)
     return 1;
   const int64_t held = (int64_t)cus * per_cu;
-  for (int S = 4; S > 1; S /= 2)
+  for (int S = SMCSD_MAX_MEMBERS; S > 1; S /= 2)
     if (S <= ntiles && 8LL * S * ((n + 7) / 8) <= held) return S;
   return 1;
 }

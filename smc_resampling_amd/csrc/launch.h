@@ -123,6 +123,11 @@ enum : unsigned {
   STAMP_TREE_REJECTED = 200,    // + r: a level whose r children were all rejected
   STAMP_TREE_LEAF = 300,        // a leaf reached
   STAMP_TREE_DRAWN = 400,       // the final draw (at a leaf, or from the last residual)
+  // -DSMCSD_PHASE_STAMPS=2 also splits each rejection pass of the tree walk
+  // (then the level phases above end at the pass's last stamp):
+  STAMP_TREE_PASS_START = 12,     // the child's test and its barrier, up to the pass
+  STAMP_TREE_PASS_WEIGHED = 13,   // thread 0's wavefront has weighed its tiles (round trip, arithmetic)
+  STAMP_TREE_PASS_GATHERED = 14,  // the other members' masses read, barrier passed
 };
 hipError_t phase_stamps(void* dst, size_t bytes, bool clear);
 
