@@ -356,6 +356,37 @@ def launch_floor(reps=64):
     return float(np.median([p[0].elapsed_time(p[1]) for p in ev])) * 1e3
 
 
+def graph_launch(reps=256):
+    """Per-kernel time of a replayed graph of `reps` launches of the library's
+    read kernel over one 4 KiB tile: what each kernel of a call costs at the
+    least when the calls are replayed as the bench times them, in us (median
+    of three replays)."""
+    import numpy as np
+    import torch
+
+    import smc_resampling_amd as smcsd
+
+    a = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(64, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(reps):
+            smcsd.read_ceiling(a, None, sink=sink, stream=side.cuda_stream)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            ev0.record(side)
+            graph.replay()
+            ev1.record(side)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) * 1e3 / reps)
+    return float(np.median(times))
+
+
 def host_description():
     """CPU model and the cores this process may use."""
     model = "unknown"
@@ -862,6 +893,7 @@ def main():
         line["other_workloads"] = others
     line["environment"] = environment()
     line["environment"]["launch_floor_us"] = launch_floor()
+    line["environment"]["graph_kernel_floor_us"] = graph_launch()
     print(json.dumps(line), flush=True)
 
 
