@@ -67,7 +67,7 @@ TreeLayout tree_layout(int32_t B, int64_t rows, int64_t V) {
 }
 
 struct SmcLayout {
-  size_t ws_logw, part, tpart, total;
+  size_t ws_logw, part, tpart, lwords, total;
 };
 
 SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
@@ -79,7 +79,9 @@ SmcLayout smc_layout(int32_t P, int32_t N, int32_t K, int64_t V) {
   // the segment partials of every row, then (power target) those of each
   // particle's bonus row at the plain scale: 2K+2 rows per particle
   l.tpart = align_up(l.part + sizeof(float2) * (size_t)(PN * (2 * K + 2) * nt));
-  l.total = align_up(l.tpart + sizeof(float2) * (size_t)(PN * nt));
+  // the tagged words of the reweighted log-weights (one per particle)
+  l.lwords = align_up(l.tpart + sizeof(float2) * (size_t)(PN * nt));
+  l.total = align_up(l.lwords + sizeof(uint64_t) * (size_t)PN);
   return l;
 }
 
@@ -350,6 +352,7 @@ static int32_t smc_step(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t 
   a.resample_u = resample_uniforms;
   a.logw = log_weights;
   a.ws_logw = reinterpret_cast<float*>(ws + l.ws_logw);
+  a.lwords = reinterpret_cast<uint64_t*>(ws + l.lwords);
   a.pt_in = page_table_in;
   a.pt_out = page_table_out;
   a.bonus_token = bonus_token;

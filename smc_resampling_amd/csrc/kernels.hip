@@ -1659,7 +1659,17 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
   const int64_t base = p * N;
   uint32_t fl = 0;
   const float ru = a.resample_u[p];  // issued early: nothing below waits on it until the slot ranges
-  for (int k = threadIdx.x; k < N; k += BLOCK) Q.lw[k] = a.ws_logw[base + k];
+  if (a.lwords) {
+    // from the particles' tagged words (this workgroup is the prompt's last
+    // particle's: see k_smc_tail)
+    for (int k = threadIdx.x; k < N; k += BLOCK) {
+      float v = 0.0f;
+      if (!tagged_get(a.lwords + base + k, 1u, &v)) raise_flags(s.flags, FLAG_WAIT_EXPIRED);
+      Q.lw[k] = v;
+    }
+  } else {
+    for (int k = threadIdx.x; k < N; k += BLOCK) Q.lw[k] = a.ws_logw[base + k];
+  }
   __syncthreads();
   if (wave == 0) {
     float mf = -INFINITY;
@@ -1756,7 +1766,13 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
 template <typename DT, bool VL>
 __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   using raw = typename DT::raw;
-  __shared__ TailLds L;
+  // the particle's work in L; the prompt's, in the prompt's last particle's
+  // workgroup, in Q over the same LDS
+  __shared__ union {
+    TailLds L;
+    PromptLds Q;
+  } U;
+  TailLds& L = U.L;
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   const int64_t i = blockIdx.x;
@@ -1810,7 +1826,10 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   const RowStat sk = stat_of(L, K);
   if (!sk.ok) fl |= FLAG_NONFINITE;
   auto store_lw = [&]() {
-    if (wave == 1 && lane == 0) a.ws_logw[i] = lw;
+    if (wave == 1 && lane == 0) {
+      if (a.lwords) tagged_put(a.lwords + i, 1u, lw);
+      else a.ws_logw[i] = lw;
+    }
   };
   // the bonus row's statistics and draw are at its own scale (beta / T)
   const int y = draw_softmax<DT, VL>(group_row<raw>(s, G, i, K), s, s.cb, sk.M, (double)ub, bnp, bper, L, fl,
@@ -1820,6 +1839,14 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
   if (threadIdx.x == 0) {
     a.bonus_token[i] = y;
     raise_flags(s.flags, L.fl);
+  }
+  // The prompt's ESS, resampling and page gather, by its last particle's
+  // workgroup once every particle's log-weight word has arrived (the planner
+  // takes this path only when every workgroup of the call fits on the device
+  // at once, so the ones it waits for are running).
+  if (a.lwords && i % a.N == a.N - 1) {
+    __syncthreads();  // L's last reads, before Q reuses its LDS
+    smc_prompt_tail(a, i / a.N, U.Q);
   }
 }
 
@@ -1972,12 +1999,28 @@ hipError_t launch_sd(const SdArgs& args, const Plan& p, bool bf16, bool vec, hip
   return launch(k, member_grid(a.s.ngroups, a.split), SD_BLOCK, a, s, t.tail_start, t.tail_stop);
 }
 
-hipError_t launch_smc(const SmcArgs& a, const Plan& p, bool bf16, bool vec, hipStream_t s, const KernelTimers& t) {
+constexpr int64_t SMC_MERGED_MAX = 512;
+
+hipError_t launch_smc(const SmcArgs& args, const Plan& p, bool bf16, bool vec, hipStream_t s,
+                      const KernelTimers& t) {
+  SmcArgs a = args;
+  const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())
+                       : (vec ? smc_tail_kernel<F32, true>() : smc_tail_kernel<F32, false>());
+  // the prompts' work inside the particle kernel on calls of at most
+  // SMC_MERGED_MAX particles whose workgroups all fit on the device at once
+  // (each prompt's last particle waits for the others' log-weights), else a
+  // prompt kernel after it (measured: 20.0 -> 18.8 us on 16 particles, 1576
+  // -> 1588 us on 2048, where the prompt kernel's own grid does the gathers
+  // sooner than the last particles can)
+  if (a.lwords && (a.s.ngroups > SMC_MERGED_MAX || resident_blocks(k) < a.s.ngroups)) a.lwords = nullptr;
+  if (a.lwords) {
+    a.s.xz = a.lwords;  // the streaming kernel zeroes the words
+    a.s.xzn = a.s.ngroups;
+  }
   hipError_t e = launch(stream_kernel(bf16, vec, p.tp, p.wide, p.pw), (unsigned)p.grid, BLOCK, a.s, s,
                         t.stream_start, t.stream_stop);
   if (e != hipSuccess) return e;
-  const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())
-                       : (vec ? smc_tail_kernel<F32, true>() : smc_tail_kernel<F32, false>());
+  if (a.lwords) return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
   e = launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, nullptr);
   if (e != hipSuccess) return e;
   return launch(kptr(&k_smc_prompt), (unsigned)(a.s.ngroups / a.N), BLOCK, a, s, nullptr, t.tail_stop);

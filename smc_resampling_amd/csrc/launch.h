@@ -65,6 +65,12 @@ struct SmcArgs {
   int32_t* ancestors;
   float* ess;
   int32_t* resampled;
+  // [P*N] tagged words of the reweighted log-weights (tag 1), zeroed by the
+  // streaming kernel, through which each prompt's last particle workgroup
+  // collects its prompt's log-weights and then does the prompt's work itself;
+  // null: a separate prompt kernel (the whole grid does not fit at once).
+  // Set by launch_smc.
+  uint64_t* lwords;
 };
 
 // Token trees: one workgroup per tree decides by walking it (the streaming

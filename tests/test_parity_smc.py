@@ -276,3 +276,41 @@ def test_smc_many_small_prompts():
     check_smc_steps(c, steps=2, ess_frac=0.9, label="1024x2")
     c = smc_case(4601, 300, 7, 3, 1500, T=0.8, dtype="f32", L=5, logw_scale=3.0)
     check_smc_steps(c, steps=2, ess_frac=1.0, label="300x7")
+
+
+def _concat_smc_cases(a, b):
+    """One call's inputs holding the prompts of case a, then those of b (same N, K, V)."""
+    out = dict(a)
+    for k in ("target", "draft", "tokens", "bonus_u", "resample_u", "logw", "pt"):
+        out[k] = np.concatenate([a[k], b[k]])
+    out["P"] = a["P"] + b["P"]
+    return out
+
+
+@pytest.mark.parametrize("P,N,K,V,dtype", [(1, 16, 4, 20000, "bf16"), (4, 64, 3, 4096, "bf16"),
+                                           (3, 7, 2, 3001, "f32"), (1, 512, 1, 2048, "bf16")])
+def test_smc_prompt_work_in_particle_kernel_matches_prompt_kernel(P, N, K, V, dtype):
+    """Calls of at most 512 particles (whose workgroups all fit on the
+    device) do each prompt's ESS, resampling and page gather in the prompt's
+    last particle's workgroup (log-weights through tagged words); larger calls
+    use a prompt kernel.  The same prompts decided both ways (alone, then
+    padded to more than 2048 particles) must agree bit for bit, and the small
+    call must match the oracle."""
+    from gpu_util import check_smc_steps, run_smc_gpu
+    from synth.small import smc_case
+
+    small = smc_case(P * 100 + N, P, N, K, V, dtype=dtype, L=8, logw_scale=2.0)
+    check_smc_steps(small, steps=1, ess_frac=0.9, label=f"prompt work in the particle kernel P={P} N={N}")
+    pad_p = (2100 + N - 1) // N
+    pad = smc_case(P * 100 + N + 1, pad_p, N, K, V, dtype=dtype, L=8, logw_scale=2.0)
+    pad["pt"] = pad["pt"] + small["pt"].size  # page ids of their own
+    big = _concat_smc_cases(small, pad)
+    a = run_smc_gpu(small, small["logw"], small["pt"], ess_frac=0.9)
+    b = run_smc_gpu(big, big["logw"], big["pt"], ess_frac=0.9)
+    PN = P * N
+    for k in ("bonus", "ancestors", "logw"):
+        assert np.array_equal(a[k], b[k][:PN]), k
+    for k in ("ess", "resampled"):
+        assert np.array_equal(a[k], b[k][:P]), k
+    assert np.array_equal(a["pt_out"], b["pt_out"][:PN])
+    assert (a["flags"] & 128) == 0 and (b["flags"] & 128) == 0
