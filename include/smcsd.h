@@ -53,14 +53,18 @@
  *   `stream` (a hipStream_t; NULL is the default stream) and returns: one that
  *   streams every logit once and one that turns the row statistics into
  *   decisions (for smc_reweight_resample a third, one workgroup per prompt,
- *   for the effective sample size, the resampling and the page tables).
- *   Outputs are valid once the stream reaches that point.  What one kernel
- *   reads from other workgroups the kernel before it wrote, with one
- *   exception: the decision kernels of sd_verify and tree_verify may run each
- *   sequence or tree on up to four workgroups that exchange single tagged
- *   words (see tree_verify), only when the whole grid fits on the device at
- *   once.  No other workgroup ever waits for another, so the other calls
- *   complete however much of the device they get.  Calls on one workspace
+ *   for the effective sample size, the resampling and the page tables, except
+ *   on the calls described below).  Outputs are valid once the stream reaches
+ *   that point.  What one kernel reads from other workgroups the kernel
+ *   before it wrote, with two exceptions, both taken only when the whole grid
+ *   fits on the device at once: the decision kernels of sd_verify and
+ *   tree_verify may run each sequence or tree on up to four workgroups that
+ *   exchange single tagged words (see tree_verify), and on a
+ *   smc_reweight_resample call of at most 512 particles the workgroup of each
+ *   prompt's last particle collects the prompt's new log-weights as tagged
+ *   words and does the prompt's work itself (no third kernel).  No other
+ *   workgroup ever waits for another, so the other calls complete however
+ *   much of the device they get.  Calls on one workspace
  *   must not overlap (on one stream they never do).
  *
  * Workspace:
@@ -121,7 +125,9 @@ enum {
   SMCSD_FLAG_WAIT_EXPIRED = 128 /* sd_verify, tree_verify: the workgroups sharing a
                                    sequence or tree did not all run within 0.1 s of
                                    each other (other work held the device); its
-                                   outputs are unspecified                            */
+                                   outputs are unspecified.  smc_reweight_resample:
+                                   the same for a prompt's particles on a call whose
+                                   prompt work runs in the particle kernel            */
 };
 
 #define SMCSD_ABI_VERSION 3

@@ -1,8 +1,9 @@
 """The bounded wait of member workgroups, forced from the host: a test build
 of the library whose waits run out at once (-DSMCSD_TAG_WAIT_TICKS=0, built by
-__graft_entry__.build()) runs SD and tree calls in a child process.  Every call
-must end; shared decisions either raise SMCSD_FLAG_WAIT_EXPIRED or match the
-oracle, and unshared ones match the oracle."""
+__graft_entry__.build()) runs SD, tree and SMC calls in a child process.  Every
+call must end; shared decisions (and SMC prompts whose work runs in a particle's
+workgroup) either raise SMCSD_FLAG_WAIT_EXPIRED or match the oracle, and the
+others match the oracle."""
 import os
 import subprocess
 import sys

@@ -1,10 +1,11 @@
 """Child process of test_wait_expiry.py, run with SMCSD_LIBRARY naming the
 test build whose member workgroups never wait for each other's tile masses
 (-DSMCSD_TAG_WAIT_TICKS=0).  Calls whose decisions are shared by member
-workgroups must still end, and each must either raise SMCSD_FLAG_WAIT_EXPIRED
-or decide as the oracle does; calls on one workgroup per decision (no waits)
-must decide as the oracle does and raise no such flag.  Prints one line per
-call, then OK."""
+workgroups, and SMC calls whose prompt work runs in a particle's workgroup
+(log-weights collected as tagged words), must still end, and each must either
+raise SMCSD_FLAG_WAIT_EXPIRED or decide as the oracle does; calls with no
+waits (one workgroup per decision, a prompt kernel) must decide as the oracle
+does and raise no such flag.  Prints one line per call, then OK."""
 import os
 import sys
 
@@ -15,9 +16,9 @@ import numpy as np  # noqa: E402
 
 import oracle  # noqa: E402
 import smc_resampling_amd as s  # noqa: E402
-from compare import compare_sd, compare_tree  # noqa: E402
-from gpu_util import run_sd_gpu, run_tree_gpu  # noqa: E402
-from synth.small import sd_case, tree_case, tree_parents  # noqa: E402
+from compare import compare_sd, compare_smc, compare_tree  # noqa: E402
+from gpu_util import run_sd_gpu, run_smc_gpu, run_tree_gpu  # noqa: E402
+from synth.small import sd_case, smc_case, tree_case, tree_parents  # noqa: E402
 
 EXPIRED = s.FLAG_WAIT_EXPIRED
 
@@ -50,6 +51,20 @@ def main():
         ref = oracle.sd_verify(c["target"], c["draft"], c["tokens"], c["uniforms"], c["T"], K=c["K"])
         compare_sd(c, ref, na, ft, label).assert_ok()
         print(f"{label}: equal to the oracle (flags {fl})", flush=True)
+    # at most 512 particles: the prompt's work in its last particle's workgroup
+    for label, P, N, waits in (("smc, 1x16 particles", 1, 16, True), ("smc, 8x64 particles", 8, 64, True),
+                               ("smc, 9x64 particles (prompt kernel)", 9, 64, False)):
+        c = smc_case(7200 + P * N, P, N, 3, 4096, dtype="bf16", L=8, logw_scale=2.0)
+        g = run_smc_gpu(c, c["logw"], c["pt"], ess_frac=0.9)
+        if g["flags"] & EXPIRED:
+            assert waits, (label, g["flags"])
+            expired += 1
+            print(f"{label}: wait expired (flags {g['flags']})", flush=True)
+            continue
+        ref = oracle.smc_step(c["target"], c["draft"], c["tokens"], c["bonus_u"], c["resample_u"], c["logw"], c["T"],
+                              0.9, P, N, c["K"], pt_in=c["pt"])
+        compare_smc(c, ref, g, c["logw"], c["pt"], label).assert_ok()
+        print(f"{label}: equal to the oracle (flags {g['flags']})", flush=True)
     print(f"calls whose waits ran out: {expired}", flush=True)
     print("OK", flush=True)
 
