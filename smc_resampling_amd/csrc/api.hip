@@ -183,7 +183,8 @@ int32_t sd_verify(int32_t dtype, int32_t B, int32_t K, int32_t V, float temperat
   const bool vec = vec_ok(dtype, V, target_logits, draft_logits);
   const int64_t rows = 2 * total_draft_rows + B;
   smcsd::Plan plan;
-  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, false, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  if (const hipError_t pe = smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, false, &plan); pe != hipSuccess)
+    return pe == hipErrorNotSupported ? SMCSD_ERR_UNSUPPORTED : SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::SdArgs a;
   fill_step(&a.s, plan, target_logits, draft_logits, draft_offsets, draft_tokens, B, total_draft_rows + B,
@@ -220,7 +221,8 @@ int32_t draft_sample(int32_t dtype, int32_t R, int32_t V, float temperature, con
   const bool bf16 = dtype == SMCSD_BF16;
   const bool vec = vec_ok(dtype, V, logits, nullptr);
   smcsd::Plan plan;
-  if (smcsd::plan_stream(R, ntiles_of(V), bf16, vec, false, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  if (const hipError_t pe = smcsd::plan_stream(R, ntiles_of(V), bf16, vec, false, &plan); pe != hipSuccess)
+    return pe == hipErrorNotSupported ? SMCSD_ERR_UNSUPPORTED : SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::SdArgs a;
   fill_step(&a.s, plan, logits, nullptr, nullptr, nullptr, R, R, 0, V, 0, temperature, ws, l.part, l.tpart,
@@ -265,7 +267,8 @@ int32_t tree_verify(int32_t dtype, int32_t B, int32_t V, float temperature, cons
   const bool bf16 = dtype == SMCSD_BF16;
   const bool vec = vec_ok(dtype, V, target_logits, num_draft_rows > 0 ? draft_logits : nullptr);
   smcsd::Plan plan;
-  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, false, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  if (const hipError_t pe = smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, false, &plan); pe != hipSuccess)
+    return pe == hipErrorNotSupported ? SMCSD_ERR_UNSUPPORTED : SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::TreeArgs a;
   // flat streaming: group g is target row g, then draft row g - num_nodes
@@ -336,7 +339,8 @@ static int32_t smc_step(int32_t dtype, int32_t P, int32_t N, int32_t K, int32_t 
   const bool power = beta != 1.0f;
   smcsd::Plan plan;
   const int64_t rows = PN * (2 * K + 1);
-  if (smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, power, &plan) != hipSuccess) return SMCSD_ERR_HIP;
+  if (const hipError_t pe = smcsd::plan_stream(rows, ntiles_of(V), bf16, vec, power, &plan); pe != hipSuccess)
+    return pe == hipErrorNotSupported ? SMCSD_ERR_UNSUPPORTED : SMCSD_ERR_HIP;
   char* ws = static_cast<char*>(workspace);
   smcsd::SmcArgs a;
   fill_step(&a.s, plan, target_logits, draft_logits, nullptr, draft_tokens, PN, PN * (K + 1), PN * K, V, K,

@@ -168,6 +168,15 @@ __device__ __forceinline__ void lane_fold_tile_at_max(const Raw<DT>& cur, float 
   }
 }
 
+// Hides from the compiler that a tile's raw registers still hold the bits a
+// loop unpacked from them, so that the unpacked values are not kept live for a
+// later loop (which unpacks again).
+template <typename DT>
+__device__ __forceinline__ void hide_bits(Raw<DT>& r) {
+#pragma unroll
+  for (int ch = 0; ch < Raw<DT>::CHUNKS; ch++) asm volatile("" : "+v"(r.q[ch]));
+}
+
 // lane_fold_tile keeps the offset where it is while every term stays at most
 // kFoldCeil: the tile is folded at the current offset (unpack, fma, exp, add
 // per logit: no maximum, no rescale), and the fold stands if the sum stays at
@@ -178,7 +187,7 @@ __device__ __forceinline__ void lane_fold_tile_at_max(const Raw<DT>& cur, float 
 constexpr float kFoldCeil = 18446744073709551616.0f;  // 2^64
 
 template <typename DT>
-__device__ __forceinline__ void lane_fold_tile(const Raw<DT>& cur, float c, float& m, float& s) {
+__device__ __forceinline__ void lane_fold_tile(Raw<DT>& cur, float c, float& m, float& s) {
   constexpr int CH = Raw<DT>::CHUNKS, VEC = DT::VEC;
   float w[VEC];
   unpack<DT>(cur, 0, w);
@@ -197,6 +206,11 @@ __device__ __forceinline__ void lane_fold_tile(const Raw<DT>& cur, float c, floa
     s = acc;
     m = mo;
   } else {
+    // The second fold unpacks the tile again, so the first fold's unpacked
+    // values die as they are used instead of staying live for this rare branch
+    // (32 values per lane against the tile's 16 raw registers, which stay live
+    // until the slot's next load anyway).
+    hide_bits<DT>(cur);
     lane_fold_tile_at_max<DT>(cur, c, m, s);
   }
 }
@@ -229,10 +243,16 @@ __device__ __forceinline__ float2 wave_partial(float m, float s) {
 // The group of the rows a wavefront streams.  With CSR offsets the wavefront
 // keeps offsets[g0 + l] in lane l, so moving to the next group needs no load
 // (a load inside the streaming loop would wait for every tile in flight).
+// Indices are 32-bit (the planner rejects calls of more than INT32_MAX
+// tiles, so every row, group and tile index fits): the streaming loop's
+// scalar state then fits in scalar registers.
 struct GroupCursor {
-  int64_t g;
-  Group G;
-  int64_t g0;   // base of the offsets window
+  int32_t g;
+  int32_t d0, kb;  // the group's first draft row and draft length
+  int32_t fr0;     // its first row in the group-major order
+  int32_t fr1;     // one past its last row
+  bool ok;
+  int32_t g0;   // base of the offsets window
   int32_t win;  // offsets[g0 + lane]
 };
 
@@ -257,16 +277,26 @@ __device__ __forceinline__ int64_t find_group_wave(int64_t fr, const StepArgs& a
   return lo;
 }
 
-__device__ __forceinline__ void cursor_set(GroupCursor& cu, int64_t g, const StepArgs& a, int lane) {
+__device__ __forceinline__ void cursor_take(GroupCursor& cu, const Group& G) {
+  cu.d0 = (int32_t)G.d0;
+  cu.kb = G.kb;
+  cu.ok = G.ok;
+  // a malformed group (not ok) is never read; its row range only has to stay
+  // finite, so that the cursor moves on
+  cu.fr0 = G.ok ? (int32_t)G.fr0 : 0;
+  cu.fr1 = G.ok ? (int32_t)(G.fr0 + 2 * (int64_t)G.kb + 1) : 0;
+}
+
+__device__ __forceinline__ void cursor_set(GroupCursor& cu, int32_t g, const StepArgs& a, int lane) {
   cu.g = g;
   if (!a.offsets) {
-    cu.G = make_group(g, g * a.K, (g + 1) * a.K, a.K, a.rows_d);
+    cursor_take(cu, make_group(g, (int64_t)g * a.K, (int64_t)(g + 1) * a.K, a.K, a.rows_d));
     return;
   }
   int32_t o0, o1;
   if (g + 1 - cu.g0 >= WAVE || g < cu.g0) {  // refill the window
     cu.g0 = g;
-    cu.win = a.offsets[min(g + lane, a.ngroups)];
+    cu.win = a.offsets[min((int64_t)g + lane, a.ngroups)];
     // read it here: the wait for the load (and for every tile load issued
     // before it) then stays in this rare branch instead of following every
     // group change (the empty asm keeps the reads from being merged with the
@@ -279,7 +309,18 @@ __device__ __forceinline__ void cursor_set(GroupCursor& cu, int64_t g, const Ste
     o0 = __builtin_amdgcn_readlane(cu.win, i);
     o1 = __builtin_amdgcn_readlane(cu.win, i + 1);
   }
-  cu.G = make_group(g, o0, o1, a.K, a.rows_d);
+  cursor_take(cu, make_group(g, o0, o1, a.K, a.rows_d));
+}
+
+// Row rr of the cursor's group (null outside the buffers).
+template <typename raw>
+__device__ __forceinline__ const raw* cursor_row(const StepArgs& a, const GroupCursor& cu, int32_t rr) {
+  Group G;
+  G.d0 = cu.d0;
+  G.kb = cu.kb;
+  G.fr0 = cu.fr0;
+  G.ok = cu.ok;
+  return group_row<raw>(a, G, cu.g, rr);
 }
 
 // TP: the call's segments span several tiles, so each group's bonus row also
@@ -293,7 +334,7 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   const int lane = threadIdx.x % WAVE;
   const int64_t w = (int64_t)blockIdx.x * WAVES_PER_BLOCK + wave_id();
   const int64_t W = (int64_t)gridDim.x * WAVES_PER_BLOCK;
-  const int64_t u0 = a.units * w / W, u1 = a.units * (w + 1) / W;
+  const int32_t u0 = (int32_t)(a.units * w / W), u1 = (int32_t)(a.units * (w + 1) / W);
   // the words the decision kernel after this one exchanges values through
   // start at 0 (plain stores: the kernel boundary orders them before it)
   for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < a.xzn; i += (int64_t)gridDim.x * BLOCK) a.xz[i] = 0;
@@ -302,29 +343,29 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   const float c = a.c;
   uint32_t bad = 0;
   // load cursor: unit lu of row lfr, tile lt of [.., lte)
-  int64_t lu = u0, lfr = u0 / nseg;
-  int lsg = (int)(u0 - lfr * nseg);
+  int32_t lu = u0, lfr = u0 / nseg;
+  int lsg = lu - lfr * nseg;
   int lt = lsg * seg, lte = min(ntiles, lt + seg);
   GroupCursor gc;
   gc.g0 = -WAVE;
   gc.win = 0;
-  cursor_set(gc, find_group_wave(lfr, a, lane), a, lane);
-  const raw* lrow = group_row<raw>(a, gc.G, gc.g, lfr - gc.G.fr0);
+  cursor_set(gc, (int32_t)find_group_wave(lfr, a, lane), a, lane);
+  const raw* lrow = cursor_row<raw>(a, gc, lfr - gc.fr0);
   if (!lrow) bad = FLAG_BAD_INPUT;
   // tiles of a group's last target row (its bonus row) also get a partial of
   // their own, at tpart[lbon + tile]; lbon < 0 for every other row
-  auto bonus_base = [&]() -> int64_t { return TP && lrow && lfr - gc.G.fr0 == gc.G.kb ? gc.g * ntiles : -1; };
-  int64_t lbon = bonus_base();
+  auto bonus_base = [&]() -> int32_t { return TP && lrow && lfr - gc.fr0 == gc.kb ? gc.g * ntiles : -1; };
+  int32_t lbon = bonus_base();
   // Issues the loads of the next tile.  A row outside the buffers (malformed
   // offsets) is read as row 0 of the target, and its partials are not used.
-  auto fetch = [&](int64_t& dst) {
+  auto fetch = [&](int32_t& dst) {
 #if SMCSD_TEMPORAL_ROWS > 0
     // build-time measurement knob: SD rows at the first draft positions
     // (target and draft row j < SMCSD_TEMPORAL_ROWS) loaded with the temporal
     // policy, so that a rejection's re-read might find them cached
-    const int64_t rr = lfr - gc.G.fr0;
+    const int32_t rr = lfr - gc.fr0;
     const bool keep = !a.flat && a.cb == a.c &&
-                      ((rr < SMCSD_TEMPORAL_ROWS) || (rr > gc.G.kb && rr <= gc.G.kb + SMCSD_TEMPORAL_ROWS));
+                      ((rr < SMCSD_TEMPORAL_ROWS) || (rr > gc.kb && rr <= gc.kb + SMCSD_TEMPORAL_ROWS));
     Raw<DT> x;
     if (keep) x = load_raw<DT, VL, 0>(lrow ? lrow : static_cast<const raw*>(a.target), a.V, lt, lane);
     else x = load_raw<DT, VL>(lrow ? lrow : static_cast<const raw*>(a.target), a.V, lt, lane);
@@ -337,8 +378,8 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
         if (++lsg == nseg) {
           lsg = 0;
           lfr++;
-          if (lfr >= gc.G.fr0 + 2 * (int64_t)gc.G.kb + 1) cursor_set(gc, gc.g + 1, a, lane);
-          lrow = group_row<raw>(a, gc.G, gc.g, lfr - gc.G.fr0);
+          if (lfr >= gc.fr1) cursor_set(gc, gc.g + 1, a, lane);
+          lrow = cursor_row<raw>(a, gc, lfr - gc.fr0);
           if (!lrow) bad = FLAG_BAD_INPUT;
           lbon = bonus_base();
         }
@@ -350,27 +391,27 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   };
   // tiles in [u0, u1): seg per unit, fewer in a row's last segment
   const int last_seg = ntiles - (nseg - 1) * seg;
-  const int64_t T = (u1 - u0) * seg - (u1 / nseg - u0 / nseg) * (int64_t)(seg - last_seg);
+  const int32_t T = (u1 - u0) * seg - (u1 / nseg - u0 / nseg) * (seg - last_seg);
   // reduce cursor: tile ct of [.., cte) of the current unit.  Finished units'
   // partials wait in lanes (unit pbase + l in lane l) and are stored 64 at a
   // time: a store is a memory operation the loads' wait counter also counts.
-  int csg = (int)(u0 % nseg);
+  int csg = u0 % nseg;
   int ct = csg * seg, cte = min(ntiles, ct + seg);
   // the scale of the row being reduced: c, or cb for a group's bonus row when
   // the call gives that row its own (SMC with a power target, whose groups are
   // all 2K+1 rows: the row within its group is the row index modulo 2K+1)
   const bool split = PW || a.cb != c;
   const int grows = 2 * a.K + 1;
-  int crr = split ? (int)((u0 / nseg) % grows) : 0;
+  int crr = split ? (u0 / nseg) % grows : 0;
   float cc = split && crr == a.K ? a.cb : c;
   float m = -INFINITY, s = 0.0f;
   // PW: the group of the row being reduced, and the bonus row's unit at scale c
-  int64_t cgrp = PW ? (u0 / nseg) / grows : 0;
+  int32_t cgrp = PW ? (u0 / nseg) / grows : 0;
   float m1 = -INFINITY, s1 = 0.0f;
   float2 pb = make_float2(0.0f, 0.0f);
-  int64_t pbase = u0;
+  int32_t pbase = u0;
   int pn = 0;
-  auto reduce = [&](Raw<DT>& x, int64_t dst) {
+  auto reduce = [&](Raw<DT>& x, int32_t dst) {
     mask_tail<DT>(x, a.V, ct, lane);
     // a bonus-row tile is folded on its own first, then into the unit's statistics
     const float pm = m, ps = s;
@@ -424,11 +465,11 @@ __device__ __forceinline__ void stream_body(const StepArgs& a) {
   // every slot is refilled unconditionally, so a reduction waits only for its
   // own tile.
   Raw<DT> q[NS];
-  int64_t qd[NS];
+  int32_t qd[NS];
   if (T >= 2 * NS) {
 #pragma unroll
     for (int i = 0; i < NS; i++) q[i] = fetch(qd[i]);
-    int64_t left = T;
+    int32_t left = T;
     do {
 #pragma unroll
       for (int i = 0; i < NS; i++) {
@@ -1915,6 +1956,9 @@ hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, bool pw, P
   if (resident <= 0) return hipErrorInvalidDevice;
   const int64_t waves = (int64_t)resident * WAVES_PER_BLOCK;
   const int64_t tiles = rows * ntiles;
+  // the streaming kernel's indices are 32-bit (more tiles than this would be
+  // 8.8 TB of bf16 logits)
+  if (tiles > INT32_MAX) return hipErrorNotSupported;
   int64_t seg = tiles / (32 * waves);
   if (seg >= LONG_SEG) seg = tiles / (16 * waves);
   seg = seg < SEG_MIN ? SEG_MIN : seg;
