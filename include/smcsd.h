@@ -52,8 +52,8 @@
  *   allocates, frees or synchronises; each call enqueues its kernels on
  *   `stream` (a hipStream_t; NULL is the default stream) and returns: one that
  *   streams every logit once and one that turns the row statistics into
- *   decisions (for smc_reweight_resample a third, one workgroup per prompt,
- *   for the effective sample size, the resampling and the page tables, except
+ *   decisions (for smc_reweight_resample a third, one to eight workgroups per
+ *   prompt, for the effective sample size, the resampling and the page tables, except
  *   on the calls described below).  Outputs are valid once the stream reaches
  *   that point.  What one kernel reads from other workgroups the kernel
  *   before it wrote, with two exceptions, both taken only when the whole grid

@@ -25,9 +25,10 @@
 // k_smc_tail (smc_reweight_resample; same page, sec. 2 steps 3-4): one
 // workgroup per particle computes the log-weight increment
 // sum_j log p_j(x_j) - log q_j(x_j) (and, for a power target, the bonus
-// token's weight) and draws the (K+1)-th token.  k_smc_prompt, one workgroup
-// per prompt, then computes the Kish ESS, resamples systematically when it is
-// below the threshold and gathers the page-table rows by ancestor (sec. 3).
+// token's weight) and draws the (K+1)-th token.  k_smc_prompt, one to eight
+// workgroups per prompt, then computes the Kish ESS, resamples systematically
+// when it is below the threshold and gathers the page-table rows by ancestor
+// (sec. 3).
 //
 // k_tree_tail (tree_verify): one workgroup per token tree walks it from the
 // root.  k_draw_tail (draft_sample): one workgroup per row draws its token.
@@ -1693,7 +1694,10 @@ __device__ __forceinline__ void gather_rows(const E* src, E* dst, int N, int64_t
   }
 }
 
-__device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
+// Prompt p's work; with parts > 1 the prompt is shared by that many
+// workgroups: each forms the ESS and the ancestors itself (the same values),
+// part 0 stores them, and each gathers its own share of the page-table rows.
+__device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q, int part = 0, int parts = 1) {
   const StepArgs& s = a.s;
   const int lane = threadIdx.x % WAVE, wave = wave_id();
   const int N = a.N;
@@ -1764,15 +1768,15 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
       carry = __builtin_amdgcn_readlane(hi, WAVE - 1);
       if (ii < N) {
         Q.hi[ii] = hi;
-        a.logw[base + ii] = do_res ? 0.0f : Q.lw[ii];
+        if (part == 0) a.logw[base + ii] = do_res ? 0.0f : Q.lw[ii];
       }
     }
-    if (lane == 0) {
+    if (lane == 0 && part == 0) {
       a.ess[p] = (float)E;
       a.resampled[p] = do_res ? 1 : 0;
     }
     fl = wave_or_flags(fl);
-    if (lane == 0) raise_flags(s.flags, fl);
+    if (lane == 0 && part == 0) raise_flags(s.flags, fl);
   }
   __syncthreads();
   // slot k's ancestor: the first particle whose range ends past k (the range
@@ -1785,19 +1789,21 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q) {
       if (Q.hi[mid] > k) hi = mid;
       else lo = mid + 1;
     }
-    a.ancestors[base + k] = lo;
+    if (part == 0) a.ancestors[base + k] = lo;
     Q.anc[k] = lo;
   }
   __syncthreads();
-  // page-table rows by ancestor (the identity when the prompt kept its particles)
-  if (a.pt_in && a.L > 0) {
+  // page-table rows by ancestor (the identity when the prompt kept its
+  // particles): this part's rows r0 .. r1-1
+  const int r0 = (int)((int64_t)N * part / parts), r1 = (int)((int64_t)N * (part + 1) / parts);
+  if (a.pt_in && a.L > 0 && r0 < r1) {
     const int64_t L = a.L;
     const int32_t* __restrict__ src = a.pt_in + base * L;
-    int32_t* __restrict__ dst = a.pt_out + base * L;
+    int32_t* __restrict__ dst = a.pt_out + (base + r0) * L;
     if ((L % 4) == 0 && (((uintptr_t)src | (uintptr_t)dst) & 15) == 0)
-      gather_rows(reinterpret_cast<const i32x4*>(src), reinterpret_cast<i32x4*>(dst), N, L / 4, Q.anc);
+      gather_rows(reinterpret_cast<const i32x4*>(src), reinterpret_cast<i32x4*>(dst), r1 - r0, L / 4, Q.anc + r0);
     else
-      gather_rows(src, dst, N, L, Q.anc);
+      gather_rows(src, dst, r1 - r0, L, Q.anc + r0);
   }
 }
 
@@ -1895,7 +1901,8 @@ __global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
 // kernel boundary orders them): ESS, systematic resampling, page-table gather.
 __global__ __launch_bounds__(BLOCK) void k_smc_prompt(SmcArgs a) {
   __shared__ PromptLds Q;
-  smc_prompt_tail(a, blockIdx.x, Q);
+  const int parts = (int)(gridDim.x / (a.s.ngroups / a.N));  // workgroups per prompt
+  smc_prompt_tail(a, blockIdx.x / parts, Q, (int)(blockIdx.x % parts), parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -2067,7 +2074,12 @@ hipError_t launch_smc(const SmcArgs& args, const Plan& p, bool bf16, bool vec, h
   if (a.lwords) return launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, t.tail_stop);
   e = launch(k, (unsigned)a.s.ngroups, BLOCK, a, s, t.tail_start, nullptr);
   if (e != hipSuccess) return e;
-  return launch(kptr(&k_smc_prompt), (unsigned)(a.s.ngroups / a.N), BLOCK, a, s, nullptr, t.tail_stop);
+  // a prompt's page-table rows are shared by up to 8 workgroups, about 16 KiB
+  // of rows each, so that large tables are copied by more than one CU a prompt
+  int64_t parts = a.pt_in && a.L > 0 ? (int64_t)a.N * a.L / 4096 : 1;
+  parts = parts < 1 ? 1 : parts > 8 ? 8 : parts;
+  if (parts > a.N) parts = a.N;
+  return launch(kptr(&k_smc_prompt), (unsigned)(a.s.ngroups / a.N * parts), BLOCK, a, s, nullptr, t.tail_stop);
 }
 
 template <typename DT, bool VL>
