@@ -314,3 +314,17 @@ def test_smc_prompt_work_in_particle_kernel_matches_prompt_kernel(P, N, K, V, dt
         assert np.array_equal(a[k], b[k][:P]), k
     assert np.array_equal(a["pt_out"], b["pt_out"][:PN])
     assert (a["flags"] & 128) == 0 and (b["flags"] & 128) == 0
+
+
+@pytest.mark.parametrize("P,N,L", [(40, 13, 1000), (40, 13, 999), (9, 64, 300), (33, 16, 2048)])
+def test_smc_prompt_shared_by_workgroups(P, N, L):
+    """More than 512 particles with large page tables: each prompt's work is
+    shared by up to eight workgroups, each gathering its share of the rows
+    (3 parts of 13 rows, 4 of 64, 8 of 16; 16-byte and element copies).  Every
+    output, the page table included, must match the oracle, with resampling
+    forced (ess_frac 2) and left to the threshold."""
+    from gpu_util import check_smc_steps
+
+    c = smc_case(P * 1000 + N + L, P, N, 2, 2048, dtype="bf16", L=L, logw_scale=2.0)
+    check_smc_steps(c, steps=1, ess_frac=2.0, label=f"shared prompt P={P} N={N} L={L} forced")
+    check_smc_steps(c, steps=1, ess_frac=0.9, label=f"shared prompt P={P} N={N} L={L}")
