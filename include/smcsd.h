@@ -79,7 +79,9 @@
  *
  * Errors:
  *   Argument errors are found on the host and returned before anything is
- *   enqueued.  A launch failure returns SMCSD_ERR_HIP.  Conditions that
+ *   enqueued.  A call whose logits span more than INT32_MAX tiles of 2048
+ *   (8.8 TB of bf16, more than any device holds) returns
+ *   SMCSD_ERR_UNSUPPORTED.  A launch failure returns SMCSD_ERR_HIP.  Conditions that
  *   depend on the data are OR-ed as SMCSD_FLAG_* bits into *status_flags
  *   (device memory, optional, never cleared by the library).  Uniforms must
  *   lie in [0, 1); this is not checked.
