@@ -1959,13 +1959,14 @@ static const void* stream_kernel(bool bf16, bool vec, bool tp, bool wide, bool p
 constexpr int SEG_MIN = 1, TP_MIN_SEG = 2, LONG_SEG = 8;
 
 hipError_t plan_stream(int64_t rows, int ntiles, bool bf16, bool vec, bool pw, Plan* p) {
+  const int64_t tiles = rows * ntiles;
+  // the streaming kernel's indices are 32-bit (more tiles than this would be
+  // 8.8 TB of bf16 logits); checked before anything asks the device
+  if (tiles > INT32_MAX) return hipErrorNotSupported;
   const int resident = resident_blocks(stream_kernel(bf16, vec, false, false, pw));
   if (resident <= 0) return hipErrorInvalidDevice;
   const int64_t waves = (int64_t)resident * WAVES_PER_BLOCK;
-  const int64_t tiles = rows * ntiles;
-  // the streaming kernel's indices are 32-bit (more tiles than this would be
-  // 8.8 TB of bf16 logits)
-  if (tiles > INT32_MAX) return hipErrorNotSupported;
+
   int64_t seg = tiles / (32 * waves);
   if (seg >= LONG_SEG) seg = tiles / (16 * waves);
   seg = seg < SEG_MIN ? SEG_MIN : seg;

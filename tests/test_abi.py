@@ -74,7 +74,9 @@ def _sd(s, **kw):
     (dict(V=0), 1), (dict(B=-1), 1), (dict(K=-1), 1), (dict(K=300, rows_d=1200), 2), (dict(rows_d=7), 1),
     (dict(rows_d=9), 1), (dict(tgt=None), 1), (dict(u=None), 1), (dict(drf=None), 1), (dict(na=None), 1),
     (dict(ws=None), 3), (dict(wsb=16), 3), (dict(ws=FAKE + 8), 3), (dict(off=FAKE, rows_d=9), 1),
-    (dict(B=0, rows_d=0, tgt=None, drf=None), 0)])
+    (dict(B=0, rows_d=0, tgt=None, drf=None), 0),
+    # more than INT32_MAX tiles of 2048 logits
+    (dict(B=70000, K=128, V=1 << 19, rows_d=70000 * 128, wsb=1 << 62), 2)])
 def test_sd_verify_host_validation(s, kw, code):
     assert _sd(s, **kw) == code
 
@@ -93,7 +95,8 @@ def _smc(s, **kw):
     (dict(dtype=5), 1), (dict(N=0), 1), (dict(P=-1), 1), (dict(T=0.0), 1), (dict(ess=-0.1), 1),
     (dict(ess=math.nan), 1), (dict(N=2000), 2), (dict(K=257), 2), (dict(lw=None), 1), (dict(ur=None), 1),
     (dict(pti=FAKE, pto=FAKE + 64, L=4), 1), (dict(pti=FAKE, pto=None, L=4), 1), (dict(ws=None), 3),
-    (dict(wsb=100), 3), (dict(P=0, tgt=None), 0), (dict(L=-1), 1)])
+    (dict(wsb=100), 3), (dict(P=0, tgt=None), 0), (dict(L=-1), 1),
+    (dict(P=300, N=1024, K=128, V=1 << 19, wsb=1 << 62), 2)])
 def test_smc_host_validation(s, kw, code):
     assert _smc(s, **kw) == code
 
