@@ -1807,11 +1807,15 @@ __device__ void smc_prompt_tail(const SmcArgs& a, int64_t p, PromptLds& Q, int p
   }
 }
 
-// With vector loads, at most 64 VGPRs (8 wavefronts per SIMD), so that 8
-// workgroups fit on a compute unit and a launch of 2048 particles is resident
-// at once (the element-wise loads need more registers than that).
-template <typename DT, bool VL>
-__global__ __launch_bounds__(BLOCK, VL ? 8 : 1) void k_smc_tail(SmcArgs a) {
+// With vector loads, the form followed by a prompt kernel keeps at most 64
+// VGPRs (8 wavefronts per SIMD), so that 8 workgroups fit on a compute unit
+// and 2048 particles run at once; the form that also does the prompts' work
+// (MERGED: calls of at most 512 particles) takes up to 80, 6 workgroups a
+// compute unit, with half the scalar spills (16 particles: 18.75 -> 18.2 us a
+// call; the 64 cap is the faster one on 2048 particles, 20.6 against 23.0 us
+// of decisions).  The element-wise loads need more registers than either.
+template <typename DT, bool VL, bool MERGED>
+__global__ __launch_bounds__(BLOCK, VL ? (MERGED ? 6 : 8) : 1) void k_smc_tail(SmcArgs a) {
   using raw = typename DT::raw;
   // the particle's work in L; the prompt's, in the prompt's last particle's
   // workgroup, in Q over the same LDS
@@ -2007,8 +2011,8 @@ static const void* draw_tail_kernel() {
 }
 
 template <typename DT, bool VL>
-static const void* smc_tail_kernel() {
-  return kptr(&k_smc_tail<DT, VL>);
+static const void* smc_tail_kernel(bool merged) {
+  return merged ? kptr(&k_smc_tail<DT, VL, true>) : kptr(&k_smc_tail<DT, VL, false>);
 }
 
 // Members per decision (a sequence or a tree): 4, else 2, while the
@@ -2056,15 +2060,19 @@ constexpr int64_t SMC_MERGED_MAX = 512;
 hipError_t launch_smc(const SmcArgs& args, const Plan& p, bool bf16, bool vec, hipStream_t s,
                       const KernelTimers& t) {
   SmcArgs a = args;
-  const void* k = bf16 ? (vec ? smc_tail_kernel<Bf16, true>() : smc_tail_kernel<Bf16, false>())
-                       : (vec ? smc_tail_kernel<F32, true>() : smc_tail_kernel<F32, false>());
+  auto tail_kernel = [&](bool merged) {
+    return bf16 ? (vec ? smc_tail_kernel<Bf16, true>(merged) : smc_tail_kernel<Bf16, false>(merged))
+                : (vec ? smc_tail_kernel<F32, true>(merged) : smc_tail_kernel<F32, false>(merged));
+  };
   // the prompts' work inside the particle kernel on calls of at most
   // SMC_MERGED_MAX particles whose workgroups all fit on the device at once
   // (each prompt's last particle waits for the others' log-weights), else a
   // prompt kernel after it (measured: 20.0 -> 18.8 us on 16 particles, 1576
   // -> 1588 us on 2048, where the prompt kernel's own grid does the gathers
   // sooner than the last particles can)
-  if (a.lwords && (a.s.ngroups > SMC_MERGED_MAX || resident_blocks(k) < a.s.ngroups)) a.lwords = nullptr;
+  if (a.lwords && (a.s.ngroups > SMC_MERGED_MAX || resident_blocks(tail_kernel(true)) < a.s.ngroups))
+    a.lwords = nullptr;
+  const void* k = tail_kernel(a.lwords != nullptr);
   if (a.lwords) {
     a.s.xz = a.lwords;  // the streaming kernel zeroes the words
     a.s.xzn = a.s.ngroups;
